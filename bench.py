@@ -1,0 +1,303 @@
+"""Benchmark of one cluster-routed sparse attention layer on one MI355X.
+
+A step is one pass of the whole layer over one batch of synthetic input:
+query clustering, multi-stage key clustering with statistics and the
+cluster-order permutations, Quest scoring with selection, and the
+block-sparse attention (the four C entry points, in the order ac_layer runs
+them).  Inputs are resident in HBM before the timed region.
+
+Prints ONE JSON line.  ``value`` is the dense-equivalent throughput
+4*B*H*L^2*d / layer time in TFLOP/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def workload_params(name: str, variant: str, compensate: int):
+    """Layer hyperparameters of each workload (see csa_inputs for the data)."""
+    import clustered_sparse_attention_amd as nm  # enum values (AC_*)
+    base = dict(nq=65, iters=10, iters_warm=3, init_sample=32, seed=0, compensate=compensate)
+    if name == "tiny":
+        base.update(nq=16, m0=32, nmax=64, tau_rule=nm.AC_TAU_INF, tau_param=0.0, sel_mode=nm.AC_SEL_TOPK, topk=8,
+                    sel_param=0.0, init_sample=0)
+    elif name == "cogvideox":
+        base.update(m0=200, nmax=1000, tau_rule=nm.AC_TAU_PCTL, tau_param=0.95, sel_mode=nm.AC_SEL_DENSITY, sel_param=0.10)
+    elif name == "hunyuan":
+        base.update(m0=100, nmax=1500, tau_rule=nm.AC_TAU_MEAN_X, tau_param=1.5, sel_mode=nm.AC_SEL_TOPK, topk=64,
+                    sel_param=0.0)
+    elif name == "wan":
+        base.update(m0=200, nmax=1500, tau_rule=nm.AC_TAU_MEAN_X, tau_param=1.5, sel_mode=nm.AC_SEL_DENSITY, sel_param=0.15)
+        if variant == "topp":
+            base.update(sel_mode=nm.AC_SEL_TOPP, sel_param=0.9)
+    elif name == "long":
+        base.update(m0=200, nmax=1500, tau_rule=nm.AC_TAU_MEAN_X, tau_param=1.5, sel_mode=nm.AC_SEL_DENSITY, sel_param=0.08)
+    else:
+        raise ValueError(name)
+    if variant == "dense":
+        base.update(sel_mode=nm.AC_SEL_DENSE)
+    return base
+
+
+def _abi(kw):
+    import clustered_sparse_attention_amd as ac
+    kw = dict(kw)
+    kw.setdefault("topk", 8)
+    kw.setdefault("score_mode", 0)
+    kw.setdefault("scale", 0.0)
+    return ac.params_default(**{k: v for k, v in kw.items()})
+
+
+class Layer:
+    """Device buffers of one layer and the four entry points."""
+
+    def __init__(self, Qd, Kd, Vd, shape, params):
+        import torch
+        import clustered_sparse_attention_amd as ac
+        self.ac = ac
+        B, H, L, d = shape
+        self.shape = ac.Shape(B, H, L, d)
+        self.p = params
+        self.ncap, self.ws_bytes = ac.ac_sizes(self.shape, params)
+        BH = B * H
+        dev = torch.device("cuda")
+        nq = min(params.nq, L)
+        self.Q, self.K, self.V = Qd, Kd, Vd
+        self.ws = ac.workspace(self.ws_bytes, dev)
+        self.q = ac.Clusters(BH, L, nq, d, dev, rho=True)
+        self.k = ac.Clusters(BH, L, self.ncap, d, dev, rho=False)
+        self.st = ac.KStats(BH, self.ncap, d, dev)
+        self.sel = ac.Selection(BH, nq, self.ncap, dev, score=False)
+        self.O = torch.empty_like(Qd)
+
+    def step(self, ev=None):
+        ac = self.ac
+        if ev: ev[0].record()
+        ac.ac_cluster_q(self.shape, self.p, self.Q, None, self.q, self.ws)
+        if ev: ev[1].record()
+        ac.ac_cluster_k(self.shape, self.p, self.K, self.V, None, self.k, self.st, self.ws)
+        if ev: ev[2].record()
+        ac.ac_score_select(self.shape, self.p, self.q, self.k, self.st, self.sel, self.ws)
+        if ev: ev[3].record()
+        ac.ac_sparse_attn(self.shape, self.p, self.Q, self.K, self.V, self.q, self.k, self.st, self.sel, self.O,
+                          None, self.ws)
+        if ev: ev[4].record()
+
+    def attn_only(self):
+        self.ac.ac_sparse_attn(self.shape, self.p, self.Q, self.K, self.V, self.q, self.k, self.st, self.sel, self.O,
+                               None, self.ws)
+
+
+def pairs_of(layer):
+    """Query-key pairs the attention computed (dense heads: L*L)."""
+    L = layer.shape.L
+    seg_q = layer.q.seg.cpu().numpy()
+    cnt_q = np.diff(seg_q, axis=1)
+    seg_k = layer.k.seg.cpu().numpy()
+    cnt_k = np.diff(seg_k, axis=1)
+    lst = layer.sel.list.cpu().numpy()
+    n = layer.sel.n.cpu().numpy()
+    fb = layer.st.fallback.cpu().numpy()
+    dense_all = layer.p.sel_mode == 3
+    tot = 0
+    per_head = []
+    for h in range(cnt_q.shape[0]):
+        if dense_all or fb[h]:
+            ph = L * L
+        else:
+            ph = 0
+            for r in range(cnt_q.shape[1]):
+                if cnt_q[h, r]:
+                    ph += int(cnt_q[h, r]) * int(cnt_k[h][lst[h, r, :n[h, r]]].sum())
+        per_head.append(ph)
+        tot += ph
+    return tot, per_head
+
+
+def cpu_baseline(w, Q, K, V, kw, max_rows=2048):
+    """The oracle, timed on this host on one head (full clustering, scoring,
+    selection, and attention for a seeded sample of query rows), extrapolated
+    to the whole layer."""
+    from oracle import numerics as nm, kmeans as okm, multistage as oms, stats as ost, score as osc
+    from oracle import attention as oat
+    import csa_inputs as gen
+    p = nm.Params(**{k: v for k, v in kw.items() if k in nm.Params.__dataclass_fields__})
+    p.tau_param = float(np.float32(p.tau_param))
+    p.sel_param = float(np.float32(p.sel_param))
+    Qb, Kb, Vb = Q[0, 0], K[0, 0], V[0, 0]
+    L, d = Qb.shape
+    t0 = time.perf_counter()
+    qc = okm.cluster_queries(Qb, p, 0)
+    kc = oms.cluster_keys(Kb, p, 0)
+    kst = ost.key_stats(Kb, Vb, kc["labels"], kc["cent"])
+    S = osc.scores(p, qc["cent"], kst)
+    sel = osc.select(S, kst["count"], qc["rho"], L, d, p)
+    t1 = time.perf_counter()
+    rows = gen.row_sample(L, max_rows, 9004)
+    Qx, Kx, Vx = (nm.bf16_to_f64(x) for x in (Qb, Kb, Vb))
+    if kc["fallback"] or p.sel_mode == nm.SEL_DENSE:
+        oat.dense_rows(Qx, Kx, Vx, rows, p.attn_scale(d))
+    else:
+        oat.sparse_rows(Qx, Kx, Vx, rows, qc["labels"], kc["labels"], sel, p.attn_scale(d), bool(p.compensate),
+                        kst["count"], kst["kmean"], kst["vmean"])
+    t2 = time.perf_counter()
+    per_head = (t1 - t0) + (t2 - t1) * (L / rows.size)
+    layer_s = per_head * w.BH
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return dict(value=w.dense_flops / layer_s / 1e12, unit="TFLOP/s (dense-equivalent)", cores=cores, kind="oracle",
+                sample=f"head 0 of {w.BH}: full clustering/scoring/selection ({t1 - t0:.1f} s) + attention for "
+                       f"{rows.size} of {L} query rows ({t2 - t1:.1f} s), extrapolated x{L / rows.size:.1f} rows "
+                       f"and x{w.BH} heads to {layer_s:.0f} s per layer",
+                measured_s=round(t2 - t0, 2), layer_s_extrapolated=round(layer_s, 1))
+
+
+def sdpa_ms(Qd, Kd, Vd, reps=3):
+    """torch scaled_dot_product_attention restricted to the flash backend."""
+    import torch
+    try:
+        from torch.nn.attention import sdpa_kernel, SDPBackend
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            torch.nn.functional.scaled_dot_product_attention(Qd, Kd, Vd)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                torch.nn.functional.scaled_dot_product_attention(Qd, Kd, Vd)
+            e1.record()
+            torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+    except Exception as e:  # backend not available on this build
+        print(f"[bench] sdpa flash backend unavailable: {e}", file=sys.stderr)
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="wan", choices=["tiny", "cogvideox", "hunyuan", "wan", "long"])
+    ap.add_argument("--variant", default="density", choices=["density", "topp", "dense"])
+    ap.add_argument("--compensate", type=int, default=0)
+    ap.add_argument("--heads", type=int, default=0, help="run only this many heads (0 = all)")
+    ap.add_argument("--no-baselines", action="store_true", help="skip dense baselines and the CPU oracle")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (heads shard across GPUs by design "
+              "only); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import csa_inputs as gen
+    import clustered_sparse_attention_amd as ac
+    ac.load()
+
+    w = gen.get_workload(args.workload)
+    if args.heads:
+        w = gen.get_workload(args.workload, H=args.heads)
+    t0 = time.perf_counter()
+    Q, K, V = gen.generate(w)
+    print(f"[bench] generated {w.name} B={w.B} H={w.H} L={w.L} d={w.d} in {time.perf_counter() - t0:.1f} s",
+          file=sys.stderr, flush=True)
+
+    def dev(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+
+    Qd, Kd, Vd = dev(Q), dev(K), dev(V)
+    kw = workload_params(args.workload, args.variant, args.compensate)
+    params = _abi(kw)
+    layer = Layer(Qd, Kd, Vd, (w.B, w.H, w.L, w.d), params)
+
+    for _ in range(args.warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        layer.step(evs[s])
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_step = (t_end - t_start) * 1e3 / args.steps
+    phase = np.array([[evs[s][i].elapsed_time(evs[s][i + 1]) for i in range(4)] for s in range(args.steps)])
+    phase_ms = phase.mean(axis=0)
+    print(f"[bench] timed {args.steps} steps: {ms_step:.2f} ms/step", file=sys.stderr, flush=True)
+
+    pairs, _ = pairs_of(layer)
+    attn_flops = 4.0 * w.d * pairs
+    attn_ms = float(phase_ms[3])
+    achieved = attn_flops / (attn_ms * 1e-3) / 1e12
+    fb = layer.st.fallback.cpu().numpy()
+    ncl = layer.k.ncl.cpu().numpy()
+    stages = layer.st.stages.cpu().numpy()
+
+    out = {
+        "metric": "sparse-attn layer ms + dense-equiv TFLOP/s at L=75.6K,d=128; MFMA util %",
+        "value": round(w.dense_flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s (dense-equivalent)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.description, "B": w.B, "H": w.H, "L": w.L, "d": w.d,
+                   "selection": args.variant, "compensate": args.compensate,
+                   "params": {k: (round(v, 6) if isinstance(v, float) else v) for k, v in kw.items()}},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "k_attn (block-sparse attention)",
+                     "algorithmic_flops_per_launch": attn_flops, "avg_launch_ms": round(attn_ms, 4)},
+        "phase_ms": {"cluster_q": round(float(phase_ms[0]), 3), "cluster_k": round(float(phase_ms[1]), 3),
+                     "score_select": round(float(phase_ms[2]), 3), "sparse_attn": round(attn_ms, 3)},
+        "layer": {"density_pairs": round(pairs / (w.BH * float(w.L) ** 2), 4), "fallback_heads": int(fb.sum()),
+                  "key_clusters_min_max": [int(ncl.min()), int(ncl.max())],
+                  "stages_max": int(stages.max())},
+    }
+    if not args.no_baselines:
+        dense_kw = workload_params(args.workload, "dense", 0)
+        dl = Layer(Qd, Kd, Vd, (w.B, w.H, w.L, w.d), _abi(dense_kw))
+        dl.step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            dl.attn_only()
+        e1.record()
+        torch.cuda.synchronize()
+        own_dense = e0.elapsed_time(e1) / 3
+        del dl
+        sd = sdpa_ms(Qd, Kd, Vd)
+        best = min(x for x in (own_dense, sd) if x is not None)
+        out["dense_baseline"] = {"own_dense_attn_ms": round(own_dense, 3), "sdpa_flash_ms": None if sd is None else round(sd, 3),
+                                 "speedup_layer_vs_best_dense": round(best / ms_step, 3),
+                                 "own_dense_tflops": round(w.dense_flops / (own_dense * 1e-3) / 1e12, 2)}
+    if not args.no_cpu and not args.no_baselines:
+        out["cpu_baseline"] = cpu_baseline(w, Q, K, V, kw)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

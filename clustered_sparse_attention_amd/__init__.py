@@ -1,0 +1,274 @@
+"""Python binding of the cluster-routed sparse attention library (libac.so).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+of ``libac.so``.  PyTorch provides device memory and the stream.  The
+functions carry the names of the C entry points declared in
+``include/ac.h`` and raise ``ACError`` on a non-OK status.  There is no
+fallback path: if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libac.so")
+
+# enums (values of include/ac.h)
+AC_OK, AC_E_ARG, AC_E_SHAPE, AC_E_WORKSPACE, AC_E_UNSUPPORTED, AC_E_DEVICE = range(6)
+AC_TAU_MEAN_X, AC_TAU_PCTL, AC_TAU_ABS, AC_TAU_INF = range(4)
+AC_SCORE_QUEST, AC_SCORE_MEAN = range(2)
+AC_SEL_TOPK, AC_SEL_DENSITY, AC_SEL_TOPP, AC_SEL_DENSE = range(4)
+
+ENTRY_POINTS = ("ac_params_default", "ac_sizes", "ac_cluster_q", "ac_cluster_k", "ac_score_select",
+                "ac_sparse_attn", "ac_layer", "ac_status_str", "ac_last_error")
+
+
+class ACError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"status {status}: {msg}")
+        self.status = status
+
+
+# ---------------------------------------------------------------- C structs
+P = ctypes.c_void_p
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32), ("d", ctypes.c_int32)]
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("nq", ctypes.c_int32), ("iters", ctypes.c_int32), ("iters_warm", ctypes.c_int32),
+                ("m0", ctypes.c_int32), ("nmax", ctypes.c_int32), ("tau_rule", ctypes.c_int32),
+                ("tau_param", ctypes.c_float), ("score_mode", ctypes.c_int32), ("sel_mode", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("sel_param", ctypes.c_float), ("compensate", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("init_sample", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+
+
+class CClusters(ctypes.Structure):
+    _fields_ = [("ncap", ctypes.c_int32), ("labels", P), ("perm", P), ("seg", P), ("cent", P), ("ncl", P),
+                ("rho", P)]
+
+
+class CKStats(ctypes.Structure):
+    _fields_ = [("kmax", P), ("kmin", P), ("kmean", P), ("vmean", P), ("fallback", P), ("tau", P), ("mse", P),
+                ("stages", P)]
+
+
+class CSelection(ctypes.Structure):
+    _fields_ = [("ncap_k", ctypes.c_int32), ("list", P), ("n", P), ("mask", P), ("score", P)]
+
+
+class CState(ctypes.Structure):
+    _fields_ = [("cent_q", P), ("cent_k", P), ("ncl_k", P), ("fallback", P), ("tau", P), ("valid", ctypes.c_int32)]
+
+
+class CLayerStats(ctypes.Structure):
+    _fields_ = [("ncl_k", P), ("fallback", P), ("tau", P), ("mse", P), ("stages", P), ("pairs", P)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libac.so (built by ``clustered_sparse_attention_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m clustered_sparse_attention_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    st = ctypes.c_int
+    vp = ctypes.c_void_p
+    lib.ac_params_default.argtypes = [ctypes.POINTER(Params)]
+    lib.ac_params_default.restype = st
+    lib.ac_sizes.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), ctypes.POINTER(ctypes.c_int32),
+                             ctypes.POINTER(ctypes.c_size_t)]
+    lib.ac_sizes.restype = st
+    lib.ac_cluster_q.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), vp, vp, ctypes.POINTER(CClusters),
+                                 vp, ctypes.c_size_t, vp]
+    lib.ac_cluster_q.restype = st
+    lib.ac_cluster_k.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), vp, vp, ctypes.POINTER(CState),
+                                 ctypes.POINTER(CClusters), ctypes.POINTER(CKStats), vp, ctypes.c_size_t, vp]
+    lib.ac_cluster_k.restype = st
+    lib.ac_score_select.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), ctypes.POINTER(CClusters),
+                                    ctypes.POINTER(CClusters), ctypes.POINTER(CKStats), ctypes.POINTER(CSelection),
+                                    vp, ctypes.c_size_t, vp]
+    lib.ac_score_select.restype = st
+    lib.ac_sparse_attn.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), vp, vp, vp,
+                                   ctypes.POINTER(CClusters), ctypes.POINTER(CClusters), ctypes.POINTER(CKStats),
+                                   ctypes.POINTER(CSelection), vp, vp, vp, ctypes.c_size_t, vp]
+    lib.ac_sparse_attn.restype = st
+    lib.ac_layer.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), vp, vp, vp, ctypes.POINTER(CState), vp,
+                             ctypes.POINTER(CLayerStats), vp, ctypes.c_size_t, vp]
+    lib.ac_layer.restype = st
+    lib.ac_status_str.argtypes = [st]
+    lib.ac_status_str.restype = ctypes.c_char_p
+    lib.ac_last_error.argtypes = []
+    lib.ac_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != AC_OK:
+        lib = load()
+        raise ACError(status, f"{lib.ac_status_str(status).decode()}: {lib.ac_last_error().decode()}")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libac must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ---------------------------------------------------------------- parameter helpers
+def params_default(**kw) -> Params:
+    p = Params()
+    _check(load().ac_params_default(ctypes.byref(p)))
+    for k, v in kw.items():
+        if not hasattr(p, k):
+            raise AttributeError(k)
+        setattr(p, k, v)
+    return p
+
+
+def ac_sizes(shape: Shape, params: Params):
+    """(ncap_k, workspace bytes) for this shape and these parameters."""
+    ncap = ctypes.c_int32()
+    ws = ctypes.c_size_t()
+    _check(load().ac_sizes(ctypes.byref(shape), ctypes.byref(params), ctypes.byref(ncap), ctypes.byref(ws)))
+    return ncap.value, ws.value
+
+
+# ---------------------------------------------------------------- device buffers (torch)
+class Clusters:
+    """Device arrays of one side's clusters (see ac_clusters)."""
+
+    def __init__(self, BH: int, L: int, ncap: int, d: int, device, rho: bool):
+        import torch
+        i32 = torch.int32
+        self.ncap = ncap
+        self.labels = torch.empty((BH, L), dtype=i32, device=device)
+        self.perm = torch.empty((BH, L), dtype=i32, device=device)
+        self.seg = torch.empty((BH, ncap + 1), dtype=i32, device=device)
+        self.cent = torch.zeros((BH, ncap, d), dtype=torch.float32, device=device)
+        self.ncl = torch.empty((BH,), dtype=i32, device=device)
+        self.rho = torch.empty((BH, ncap), dtype=torch.float32, device=device) if rho else None
+
+    def c(self) -> CClusters:
+        return CClusters(self.ncap, _ptr(self.labels), _ptr(self.perm), _ptr(self.seg), _ptr(self.cent),
+                         _ptr(self.ncl), _ptr(self.rho))
+
+
+class KStats:
+    def __init__(self, BH: int, ncap: int, d: int, device):
+        import torch
+        self.kmax = torch.empty((BH, ncap, d), dtype=torch.bfloat16, device=device)
+        self.kmin = torch.empty((BH, ncap, d), dtype=torch.bfloat16, device=device)
+        self.kmean = torch.empty((BH, ncap, d), dtype=torch.float32, device=device)
+        self.vmean = torch.empty((BH, ncap, d), dtype=torch.float32, device=device)
+        self.fallback = torch.empty((BH,), dtype=torch.uint8, device=device)
+        self.tau = torch.empty((BH,), dtype=torch.float32, device=device)
+        self.mse = torch.empty((BH,), dtype=torch.float32, device=device)
+        self.stages = torch.empty((BH,), dtype=torch.int32, device=device)
+
+    def c(self) -> CKStats:
+        return CKStats(_ptr(self.kmax), _ptr(self.kmin), _ptr(self.kmean), _ptr(self.vmean), _ptr(self.fallback),
+                       _ptr(self.tau), _ptr(self.mse), _ptr(self.stages))
+
+
+class Selection:
+    def __init__(self, BH: int, nq: int, ncap_k: int, device, score: bool = True):
+        import torch
+        self.ncap_k = ncap_k
+        self.list = torch.empty((BH, nq, ncap_k), dtype=torch.int32, device=device)
+        self.n = torch.empty((BH, nq), dtype=torch.int32, device=device)
+        self.mask = torch.empty((BH, nq, (ncap_k + 31) // 32), dtype=torch.int32, device=device)
+        self.score = torch.empty((BH, nq, ncap_k), dtype=torch.float32, device=device) if score else None
+
+    def c(self) -> CSelection:
+        return CSelection(self.ncap_k, _ptr(self.list), _ptr(self.n), _ptr(self.mask), _ptr(self.score))
+
+
+class State:
+    """Centres and flags carried from one denoising step to the next."""
+
+    def __init__(self, BH: int, nq: int, ncap_k: int, d: int, device):
+        import torch
+        self.cent_q = torch.zeros((BH, nq, d), dtype=torch.float32, device=device)
+        self.cent_k = torch.zeros((BH, ncap_k, d), dtype=torch.float32, device=device)
+        self.ncl_k = torch.zeros((BH,), dtype=torch.int32, device=device)
+        self.fallback = torch.zeros((BH,), dtype=torch.uint8, device=device)
+        self.tau = torch.zeros((BH,), dtype=torch.float32, device=device)
+        self.valid = 0
+        self._c = None
+
+    def c(self) -> CState:
+        self._c = CState(_ptr(self.cent_q), _ptr(self.cent_k), _ptr(self.ncl_k), _ptr(self.fallback),
+                         _ptr(self.tau), self.valid)
+        return self._c
+
+
+def workspace(nbytes: int, device):
+    """A 256-byte aligned device byte buffer of at least nbytes."""
+    import torch
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + nbytes]
+
+
+# ---------------------------------------------------------------- entry points
+def ac_cluster_q(shape, params, Q, warm_cent, q_out: Clusters, ws, stream=None):
+    _check(load().ac_cluster_q(ctypes.byref(shape), ctypes.byref(params), _ptr(Q), _ptr(warm_cent),
+                               ctypes.byref(q_out.c()), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def ac_cluster_k(shape, params, K, V, warm: Optional[State], k_out: Clusters, stats: KStats, ws, stream=None):
+    wc = ctypes.byref(warm.c()) if warm is not None else None
+    _check(load().ac_cluster_k(ctypes.byref(shape), ctypes.byref(params), _ptr(K), _ptr(V), wc,
+                               ctypes.byref(k_out.c()), ctypes.byref(stats.c()), _ptr(ws), ws.numel(),
+                               _stream(stream)))
+
+
+def ac_score_select(shape, params, q: Clusters, k: Clusters, stats: KStats, sel: Selection, ws, stream=None):
+    _check(load().ac_score_select(ctypes.byref(shape), ctypes.byref(params), ctypes.byref(q.c()),
+                                  ctypes.byref(k.c()), ctypes.byref(stats.c()), ctypes.byref(sel.c()), _ptr(ws),
+                                  ws.numel(), _stream(stream)))
+
+
+def ac_sparse_attn(shape, params, Q, K, V, q: Clusters, k: Clusters, stats: KStats, sel: Selection, O, lse=None,
+                   ws=None, stream=None):
+    _check(load().ac_sparse_attn(ctypes.byref(shape), ctypes.byref(params), _ptr(Q), _ptr(K), _ptr(V),
+                                 ctypes.byref(q.c()), ctypes.byref(k.c()), ctypes.byref(stats.c()),
+                                 ctypes.byref(sel.c()), _ptr(O), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def ac_layer(shape, params, Q, K, V, state: State, O, ws, host_stats: bool = False, stream=None):
+    """Run the whole layer.  Returns a dict of per-head numpy arrays when
+    host_stats is set (the call then waits for the stream), else None."""
+    import numpy as np
+    BH = shape.B * shape.H
+    hs = None
+    arrs = None
+    if host_stats:
+        arrs = dict(ncl_k=np.zeros(BH, np.int32), fallback=np.zeros(BH, np.uint8), tau=np.zeros(BH, np.float32),
+                    mse=np.zeros(BH, np.float32), stages=np.zeros(BH, np.int32), pairs=np.zeros(BH, np.int64))
+        hs = CLayerStats(*(a.ctypes.data for a in arrs.values()))
+    cs = state.c()
+    _check(load().ac_layer(ctypes.byref(shape), ctypes.byref(params), _ptr(Q), _ptr(K), _ptr(V), ctypes.byref(cs),
+                           _ptr(O), ctypes.byref(hs) if hs is not None else None, _ptr(ws), ws.numel(),
+                           _stream(stream)))
+    state.valid = cs.valid
+    return arrs

@@ -1,0 +1,660 @@
+// Host side of the C ABI declared in include/ac.h: argument validation,
+// workspace planning and the launch order of each entry point, including
+// the host-driven stage loop of AdaCluster Algorithm 1.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "../../include/ac.h"
+#include "internal.h"
+
+#define AC_API extern "C" __attribute__((visibility("default")))
+
+namespace ac {
+namespace {
+
+thread_local char g_err[512] = "";
+
+ac_status fail(ac_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+#define AC_HIP(call)                                                                       \
+  do {                                                                                     \
+    hipError_t e_ = (call);                                                                \
+    if (e_ != hipSuccess) return fail(AC_E_DEVICE, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+#define AC_CHECK_LAUNCH()                                                                       \
+  do {                                                                                          \
+    hipError_t e_ = hipGetLastError();                                                          \
+    if (e_ != hipSuccess) return fail(AC_E_DEVICE, "kernel launch: %s", hipGetErrorString(e_)); \
+  } while (0)
+
+#define AC_TRY(expr)                 \
+  do {                               \
+    ac_status s_ = (expr);           \
+    if (s_ != AC_OK) return s_;      \
+  } while (0)
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------------------
+// validation
+ac_status check_shape(const ac_shape *s) {
+  if (!s) return fail(AC_E_ARG, "shape is NULL");
+  if (s->B <= 0 || s->H <= 0 || s->L <= 0 || s->d <= 0)
+    return fail(AC_E_SHAPE, "B, H, L, d must be positive (got %d %d %d %d)", s->B, s->H, s->L, s->d);
+  if (s->d != 64 && s->d != 128) return fail(AC_E_UNSUPPORTED, "d = %d: only 64 and 128 are supported", s->d);
+  if ((int64_t)s->B * s->H > (1 << 20)) return fail(AC_E_SHAPE, "B*H too large");
+  if ((int64_t)s->L > (1 << 26)) return fail(AC_E_SHAPE, "L too large");
+  return AC_OK;
+}
+
+ac_status check_params(const ac_shape *s, const ac_params *p) {
+  if (!p) return fail(AC_E_ARG, "params is NULL");
+  if (p->nq <= 0) return fail(AC_E_ARG, "nq must be positive");
+  if (p->iters < 0 || p->iters_warm < 0) return fail(AC_E_ARG, "iteration counts must be >= 0");
+  if (p->m0 <= 0 || p->nmax <= 0) return fail(AC_E_ARG, "m0 and nmax must be positive");
+  if (p->tau_rule < AC_TAU_MEAN_X || p->tau_rule > AC_TAU_INF) return fail(AC_E_ARG, "tau_rule out of range");
+  if (p->tau_rule == AC_TAU_PCTL && !(p->tau_param > 0.f && p->tau_param <= 1.f))
+    return fail(AC_E_ARG, "percentile tau_param must be in (0, 1]");
+  if ((p->tau_rule == AC_TAU_MEAN_X || p->tau_rule == AC_TAU_ABS) && !(p->tau_param >= 0.f && std::isfinite(p->tau_param)))
+    return fail(AC_E_ARG, "tau_param must be finite and >= 0");
+  if (p->score_mode != AC_SCORE_QUEST && p->score_mode != AC_SCORE_MEAN) return fail(AC_E_ARG, "score_mode out of range");
+  if (p->sel_mode < AC_SEL_TOPK || p->sel_mode > AC_SEL_DENSE) return fail(AC_E_ARG, "sel_mode out of range");
+  if (p->sel_mode == AC_SEL_TOPK && p->topk <= 0) return fail(AC_E_ARG, "topk must be positive");
+  if (p->sel_mode == AC_SEL_DENSITY && !(p->sel_param > 0.f && p->sel_param <= 1.f))
+    return fail(AC_E_ARG, "density must be in (0, 1]");
+  if (p->sel_mode == AC_SEL_TOPP && !(p->sel_param > 0.f && p->sel_param <= 1.f))
+    return fail(AC_E_ARG, "top-p must be in (0, 1]");
+  if (p->compensate != 0 && p->compensate != 1) return fail(AC_E_ARG, "compensate must be 0 or 1");
+  if (!(p->scale >= 0.f) || !std::isfinite(p->scale)) return fail(AC_E_ARG, "scale must be finite and >= 0");
+  if (p->init_sample < 0) return fail(AC_E_ARG, "init_sample must be >= 0");
+  const int64_t ncap = (int64_t)p->nmax - 1 + p->m0;
+  if (ncap > SEL_MAXN) return fail(AC_E_UNSUPPORTED, "nmax - 1 + m0 = %lld exceeds %d key clusters", (long long)ncap, SEL_MAXN);
+  const int64_t mmax = std::max<int64_t>(std::min<int64_t>(p->nq, s->L), std::min<int64_t>(p->m0, s->L));
+  const int64_t smax = p->init_sample > 0 ? std::min<int64_t>(s->L, (int64_t)p->init_sample * mmax) : s->L;
+  if (smax > KPP_SMAX)
+    return fail(AC_E_UNSUPPORTED, "k-means++ subsample of %lld points exceeds %d (lower init_sample)", (long long)smax, KPP_SMAX);
+  return AC_OK;
+}
+
+// ---------------------------------------------------------------------------
+// workspace plan: every region any entry point uses, at fixed offsets
+struct Plan {
+  int BH, L, D, nq, ncapk, mcap, max_tiles, nq_pad, ncap_pad, mwords;
+  size_t total = 0;
+  // scratch
+  size_t qhat, qn, lab, lperm, lseg, thist, ops_hi, ops_lo, ops_norm, d2buf, hn, hm, hcoff, hnew;
+  size_t uidx0, uidx1, dist, flag, rstate, rhist, msepart;
+  size_t scoreA, scoreB, S, seltok, kc, vc, lb, tile_off, pairs;
+  // ac_layer persistent
+  size_t q_labels, q_perm, q_seg, q_cent, q_ncl, q_rho;
+  size_t k_labels, k_perm, k_seg, k_cent, k_ncl;
+  size_t kmax, kmin, kmean, vmean, fb, tau, mse, stages;
+  size_t sel_list, sel_n, sel_mask, sel_score;
+};
+
+Plan make_plan(const ac_shape *s, const ac_params *p) {
+  Plan P;
+  P.BH = s->B * s->H;
+  P.L = s->L;
+  P.D = s->d;
+  P.nq = std::min(p->nq, s->L);
+  P.ncapk = p->nmax - 1 + p->m0;
+  P.mcap = std::max({P.ncapk, P.nq, 2});
+  P.max_tiles = (int)cdiv(P.L, SORT_TILE);
+  P.nq_pad = (int)cdiv(P.nq, 16) * 16;
+  P.ncap_pad = (int)cdiv(P.ncapk, 16) * 16;
+  P.mwords = (int)cdiv(P.ncapk, 32);
+  const size_t BH = P.BH, L = P.L, D = P.D;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + std::max<size_t>(bytes, 1));
+    return o;
+  };
+  P.qhat = take(BH * L * D * 2);
+  P.qn = take(BH * L * 4);
+  P.lab = take(BH * L * 4);
+  P.lperm = take(BH * L * 4);
+  P.lseg = take(BH * (P.mcap + 1) * 4);
+  P.thist = take(BH * P.max_tiles * (size_t)P.mcap * 4);
+  P.ops_hi = take(BH * P.mcap * D * 2);
+  P.ops_lo = take(BH * P.mcap * D * 2);
+  P.ops_norm = take(BH * P.mcap * 4);
+  P.d2buf = take(BH * (size_t)KPP_SMAX * 8);
+  P.hn = take(BH * 4);
+  P.hm = take(BH * 4);
+  P.hcoff = take(BH * 4);
+  P.hnew = take(BH * 4);
+  P.uidx0 = take(BH * L * 4);
+  P.uidx1 = take(BH * L * 4);
+  P.dist = take(BH * L * 4);
+  P.flag = take(BH * L * 4);
+  P.rstate = take(BH * 2 * 4);
+  P.rhist = take(BH * 256 * 4);
+  P.msepart = take(BH * P.ncapk * 8);
+  P.scoreA = take(BH * P.nq_pad * 6 * D * 2);
+  P.scoreB = take(BH * P.ncap_pad * 6 * D * 2);
+  P.S = take(BH * P.nq * (size_t)P.ncapk * 4);
+  P.seltok = take(BH * P.nq * 4);
+  P.kc = take(BH * P.ncapk * D * 2);
+  P.vc = take(BH * P.ncapk * D * 2);
+  P.lb = take(BH * P.ncapk * 4);
+  P.tile_off = take(BH * (P.nq + 1) * 4);
+  P.pairs = take(BH * 8);
+  P.q_labels = take(BH * L * 4);
+  P.q_perm = take(BH * L * 4);
+  P.q_seg = take(BH * (P.nq + 1) * 4);
+  P.q_cent = take(BH * P.nq * D * 4);
+  P.q_ncl = take(BH * 4);
+  P.q_rho = take(BH * P.nq * 4);
+  P.k_labels = take(BH * L * 4);
+  P.k_perm = take(BH * L * 4);
+  P.k_seg = take(BH * (P.ncapk + 1) * 4);
+  P.k_cent = take(BH * P.ncapk * D * 4);
+  P.k_ncl = take(BH * 4);
+  P.kmax = take(BH * P.ncapk * D * 2);
+  P.kmin = take(BH * P.ncapk * D * 2);
+  P.kmean = take(BH * P.ncapk * D * 4);
+  P.vmean = take(BH * P.ncapk * D * 4);
+  P.fb = take(BH);
+  P.tau = take(BH * 4);
+  P.mse = take(BH * 4);
+  P.stages = take(BH * 4);
+  P.sel_list = take(BH * P.nq * (size_t)P.ncapk * 4);
+  P.sel_n = take(BH * P.nq * 4);
+  P.sel_mask = take(BH * P.nq * (size_t)P.mwords * 4);
+  P.sel_score = take(BH * P.nq * (size_t)P.ncapk * 4);
+  P.total = off + 256;  // slack for aligning the base pointer
+  return P;
+}
+
+template <typename T>
+T *at(void *base, size_t off) {
+  return reinterpret_cast<T *>(reinterpret_cast<char *>(base) + off);
+}
+
+ac_status check_ws(const Plan &P, void *ws, size_t ws_bytes) {
+  if (!ws) return fail(AC_E_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(AC_E_ARG, "workspace must be 256-byte aligned");
+  if (ws_bytes < P.total)
+    return fail(AC_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes required", ws_bytes, P.total);
+  return AC_OK;
+}
+
+ac_status check_device() {
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || n <= 0)
+    return fail(AC_E_DEVICE, "no HIP device available (%s)", e == hipSuccess ? "count 0" : hipGetErrorString(e));
+  return AC_OK;
+}
+
+float attn_scale(const ac_params *p, int D) { return p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)D); }
+
+// ---------------------------------------------------------------------------
+// the k-means engine: optional k-means++ seeding, iters Lloyd iterations,
+// and a final assignment into labels_out.
+struct Engine {
+  const Plan &P;
+  void *ws;
+  hipStream_t st;
+  int *n() { return at<int>(ws, P.hn); }
+  int *m() { return at<int>(ws, P.hm); }
+  int *coff() { return at<int>(ws, P.hcoff); }
+  CentOps ops() { return CentOps{at<uint16_t>(ws, P.ops_hi), at<uint16_t>(ws, P.ops_lo), at<float>(ws, P.ops_norm), P.mcap}; }
+  SortArgs sort_args(const int *labels, int *perm, int *seg, int segcap, int mcap_used) {
+    SortArgs s;
+    s.labels = labels;
+    s.lab_hs = P.L;
+    s.n = n();
+    s.m = m();
+    s.tile_hist = at<int>(ws, P.thist);
+    s.max_tiles = P.max_tiles;
+    s.mcap = std::max(mcap_used, 2);
+    s.perm = perm;
+    s.perm_hs = P.L;
+    s.seg = seg;
+    s.seg_hs = segcap + 1;
+    s.segcap = segcap;
+    return s;
+  }
+  // mmax: bound on m over heads (grid size); npts: bound on n.
+  ac_status run(const KmArgs &a, int mmax, int npts, bool seed_init, int iters, const ac_params *p, int role,
+                int stage, int *labels_out) {
+    const int D = P.D;
+    if (seed_init) {
+      launch_kpp_init(D, a, P.BH, at<double>(ws, P.d2buf), p->init_sample, p->seed, role, stage, st);
+      AC_CHECK_LAUNCH();
+    }
+    CentOps op = ops();
+    launch_cent_prep(D, a, op, P.BH, mmax, st);
+    AC_CHECK_LAUNCH();
+    int *lab = at<int>(ws, P.lab);
+    for (int it = 0; it < iters; ++it) {
+      launch_assign(D, a, op, P.BH, npts, lab, P.L, st);
+      SortArgs s = sort_args(lab, at<int>(ws, P.lperm), at<int>(ws, P.lseg), P.mcap, mmax);
+      launch_sort(s, P.BH, npts, st);
+      launch_update(D, a, s, op, P.BH, mmax, st);
+      AC_CHECK_LAUNCH();
+    }
+    launch_assign(D, a, op, P.BH, npts, labels_out, P.L, st);
+    AC_CHECK_LAUNCH();
+    return AC_OK;
+  }
+};
+
+// ---------------------------------------------------------------------------
+ac_status do_cluster_q(const Plan &P, const ac_params *p, const uint16_t *Q, const float *warm_cent,
+                       ac_clusters *q, void *ws, hipStream_t st) {
+  const int BH = P.BH, L = P.L, D = P.D;
+  Engine E{P, ws, st};
+  uint16_t *qhat = at<uint16_t>(ws, P.qhat);
+  float *qn = at<float>(ws, P.qn);
+  launch_qnorm(D, Q, qhat, qn, (int64_t)BH * L, st);
+  launch_fill_i32(E.n(), BH, L, st);
+  launch_fill_i32(E.m(), BH, P.nq, st);
+  launch_fill_i32(E.coff(), BH, 0, st);
+  launch_fill_i32(q->ncl, BH, P.nq, st);
+  AC_CHECK_LAUNCH();
+  if (warm_cent) {
+    // centres beyond nq (if ncap > nq) are left as they are
+    for (int h = 0; h < BH; ++h)
+      AC_HIP(hipMemcpyAsync(q->cent + (size_t)h * q->ncap * D, warm_cent + (size_t)h * q->ncap * D,
+                            (size_t)P.nq * D * 4, hipMemcpyDeviceToDevice, st));
+  }
+  KmArgs a{qhat, (int64_t)L * D, nullptr, 0, E.n(), E.m(), E.coff(), q->cent, (int64_t)q->ncap * D};
+  AC_TRY(E.run(a, P.nq, L, warm_cent == nullptr, warm_cent ? p->iters_warm : p->iters, p, 0, 0, q->labels));
+  SortArgs s = E.sort_args(q->labels, q->perm, q->seg, q->ncap, P.nq);
+  launch_sort(s, BH, L, st);
+  launch_seg_mean(qn, q->perm, q->seg, L, q->ncap, q->ncl, q->rho, BH, st);
+  AC_CHECK_LAUNCH();
+  return AC_OK;
+}
+
+ac_status finish_keys(const Plan &P, const uint16_t *K, const uint16_t *V, ac_clusters *k, ac_kstats *stats,
+                      void *ws, hipStream_t st, int mmax) {
+  // final assignment of every key over all centres, counting sort, statistics
+  const int BH = P.BH, L = P.L, D = P.D;
+  Engine E{P, ws, st};
+  launch_fill_i32(E.n(), BH, L, st);
+  launch_copy_i32(k->ncl, E.m(), BH, st);
+  launch_fill_i32(E.coff(), BH, 0, st);
+  KmArgs a{K, (int64_t)L * D, nullptr, 0, E.n(), E.m(), E.coff(), k->cent, (int64_t)k->ncap * D};
+  CentOps op = E.ops();
+  launch_cent_prep(D, a, op, BH, mmax, st);
+  launch_assign(D, a, op, BH, L, k->labels, L, st);
+  SortArgs s = E.sort_args(k->labels, k->perm, k->seg, k->ncap, mmax);
+  launch_sort(s, BH, L, st);
+  KStatsArgs ks{K, V, k->perm, k->seg, k->ncl, k->cent, stats->kmax, stats->kmin, stats->kmean, stats->vmean,
+                at<double>(ws, P.msepart), stats->mse, L, k->ncap};
+  launch_kstats(D, ks, BH, st);
+  AC_CHECK_LAUNCH();
+  return AC_OK;
+}
+
+ac_status do_cluster_k_cold(const Plan &P, const ac_params *p, const uint16_t *K, const uint16_t *V,
+                            ac_clusters *k, ac_kstats *stats, void *ws, hipStream_t st) {
+  const int BH = P.BH, L = P.L, D = P.D;
+  Engine E{P, ws, st};
+  std::vector<int> nU(BH, L), nC(BH, 0), done(BH, 0), F(BH, 0), stg(BH, 0), hn(BH), hm(BH), hc(BH);
+  int *uidx[2] = {at<int>(ws, P.uidx0), at<int>(ws, P.uidx1)};
+  int cur = 0;
+  float *dist = at<float>(ws, P.dist);
+  int *flag = at<int>(ws, P.flag);
+  for (int t = 0;; ++t) {
+    int active = 0, mmax = 0, nmaxpts = 0;
+    for (int h = 0; h < BH; ++h) {
+      if (!done[h] && nC[h] >= p->nmax) { F[h] = 1; done[h] = 1; }
+      if (done[h]) { hn[h] = 0; hm[h] = 0; hc[h] = nC[h]; continue; }
+      hn[h] = nU[h];
+      hm[h] = std::min(nU[h], p->m0);
+      hc[h] = nC[h];
+      active++;
+      mmax = std::max(mmax, hm[h]);
+      nmaxpts = std::max(nmaxpts, hn[h]);
+    }
+    if (!active) break;
+    AC_HIP(hipMemcpyAsync(E.n(), hn.data(), BH * 4, hipMemcpyHostToDevice, st));
+    AC_HIP(hipMemcpyAsync(E.m(), hm.data(), BH * 4, hipMemcpyHostToDevice, st));
+    AC_HIP(hipMemcpyAsync(E.coff(), hc.data(), BH * 4, hipMemcpyHostToDevice, st));
+    KmArgs a{K, (int64_t)L * D, t == 0 ? nullptr : uidx[cur], L, E.n(), E.m(), E.coff(), k->cent,
+             (int64_t)k->ncap * D};
+    int *lab = at<int>(ws, P.lab);
+    AC_TRY(E.run(a, mmax, nmaxpts, true, p->iters, p, 1, t, lab));
+    launch_stage_dist(D, a, BH, nmaxpts, lab, L, dist, L, st);
+    if (t == 0)
+      launch_tau(dist, L, E.n(), BH, nmaxpts, p->tau_rule, p->tau_param, stats->tau, at<uint32_t>(ws, P.rstate),
+                 at<uint32_t>(ws, P.rhist), st);
+    launch_flag_removed(dist, L, E.n(), stats->tau, flag, L, BH, nmaxpts, st);
+    // stable compaction: label 0 (kept) first
+    launch_fill_i32(E.m(), BH, 2, st);
+    SortArgs s = E.sort_args(flag, at<int>(ws, P.lperm), at<int>(ws, P.lseg), 1, 2);
+    launch_sort(s, BH, nmaxpts, st);
+    launch_compact_gather(t == 0 ? nullptr : uidx[cur], L, at<int>(ws, P.lperm), L, at<int>(ws, P.lseg), 2,
+                          uidx[cur ^ 1], at<int>(ws, P.hnew), BH, nmaxpts, st);
+    AC_CHECK_LAUNCH();
+    std::vector<int> nnew(BH);
+    AC_HIP(hipMemcpyAsync(nnew.data(), at<int>(ws, P.hnew), BH * 4, hipMemcpyDeviceToHost, st));
+    AC_HIP(hipStreamSynchronize(st));
+    for (int h = 0; h < BH; ++h) {
+      if (done[h]) continue;
+      nC[h] += hm[h];
+      stg[h] = t + 1;
+      nU[h] = hn[h] > 0 ? nnew[h] : 0;
+      if (nU[h] == 0) done[h] = 1;
+    }
+    cur ^= 1;
+  }
+  std::vector<uint8_t> fb(BH);
+  int mmax = 1;
+  for (int h = 0; h < BH; ++h) {
+    fb[h] = (uint8_t)F[h];
+    mmax = std::max(mmax, nC[h]);
+  }
+  AC_HIP(hipMemcpyAsync(k->ncl, nC.data(), BH * 4, hipMemcpyHostToDevice, st));
+  AC_HIP(hipMemcpyAsync(stats->fallback, fb.data(), BH, hipMemcpyHostToDevice, st));
+  AC_HIP(hipMemcpyAsync(stats->stages, stg.data(), BH * 4, hipMemcpyHostToDevice, st));
+  AC_TRY(finish_keys(P, K, V, k, stats, ws, st, mmax));
+  // the host vectors above must outlive the copies
+  AC_HIP(hipStreamSynchronize(st));
+  return AC_OK;
+}
+
+ac_status do_cluster_k_warm(const Plan &P, const ac_params *p, const uint16_t *K, const uint16_t *V,
+                            const ac_state *w, ac_clusters *k, ac_kstats *stats, void *ws, hipStream_t st) {
+  const int BH = P.BH, L = P.L, D = P.D;
+  Engine E{P, ws, st};
+  AC_HIP(hipMemcpyAsync(k->cent, w->cent_k, (size_t)BH * k->ncap * D * 4, hipMemcpyDeviceToDevice, st));
+  launch_copy_i32(w->ncl_k, k->ncl, BH, st);
+  launch_copy_u8(w->fallback, stats->fallback, BH, st);
+  launch_copy_f32(w->tau, stats->tau, BH, st);
+  launch_fill_i32(stats->stages, BH, 0, st);
+  launch_fill_i32(E.n(), BH, L, st);
+  launch_copy_i32(w->ncl_k, E.m(), BH, st);
+  launch_fill_i32(E.coff(), BH, 0, st);
+  AC_CHECK_LAUNCH();
+  KmArgs a{K, (int64_t)L * D, nullptr, 0, E.n(), E.m(), E.coff(), k->cent, (int64_t)k->ncap * D};
+  AC_TRY(E.run(a, k->ncap, L, false, p->iters_warm, p, 1, 0, k->labels));
+  // finish_keys repeats the final assignment; harmless and keeps one code path
+  return finish_keys(P, K, V, k, stats, ws, st, k->ncap);
+}
+
+ac_status do_score_select(const Plan &P, const ac_params *p, const ac_clusters *q, const ac_clusters *k,
+                          const ac_kstats *stats, ac_selection *sel, void *ws, hipStream_t st) {
+  const int BH = P.BH, D = P.D;
+  float *S = sel->score ? sel->score : at<float>(ws, P.S);
+  ScoreArgs sa;
+  sa.cq = q->cent;
+  sa.nqcap = q->ncap;
+  sa.nq = P.nq;
+  sa.kmax = stats->kmax;
+  sa.kmin = stats->kmin;
+  sa.kmean = stats->kmean;
+  sa.seg_k = k->seg;
+  sa.ncl_k = k->ncl;
+  sa.ncap = k->ncap;
+  sa.mode = p->score_mode;
+  sa.A = at<uint16_t>(ws, P.scoreA);
+  sa.Bm = at<uint16_t>(ws, P.scoreB);
+  sa.nq_pad = P.nq_pad;
+  sa.ncap_pad = P.ncap_pad;
+  sa.S = S;
+  // S rows are q->ncap wide in clusters but the kernels index [nqcap][ncap]
+  launch_score(D, sa, BH, st);
+  AC_CHECK_LAUNCH();
+  SelectArgs se;
+  se.S = S;
+  se.seg_k = k->seg;
+  se.ncl_k = k->ncl;
+  se.rho = q->rho;
+  se.ncl_q = q->ncl;
+  se.nqcap = q->ncap;
+  se.ncap = k->ncap;
+  se.L = P.L;
+  se.D = D;
+  se.mode = p->sel_mode;
+  se.topk = p->topk;
+  se.param = p->sel_param;
+  se.scale = attn_scale(p, D);
+  se.list = sel->list;
+  se.nsel = sel->n;
+  se.mask = sel->mask;
+  se.mwords = P.mwords;
+  se.seltok = at<int>(ws, P.seltok);
+  launch_select(se, BH, st);
+  AC_CHECK_LAUNCH();
+  return AC_OK;
+}
+
+ac_status do_attn(const Plan &P, const ac_params *p, const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                  const ac_clusters *q, const ac_clusters *k, const ac_kstats *stats, const ac_selection *sel,
+                  uint16_t *O, float *lse, void *ws, hipStream_t st) {
+  const int BH = P.BH, D = P.D;
+  AttnArgs a;
+  a.Q = Q; a.K = K; a.V = V;
+  a.perm_q = q->perm; a.seg_q = q->seg; a.ncl_q = q->ncl; a.nqcap = q->ncap;
+  a.perm_k = k->perm; a.seg_k = k->seg; a.ncl_k = k->ncl; a.ncap = k->ncap;
+  a.list = sel->list; a.nsel = sel->n; a.mask = sel->mask; a.mwords = P.mwords;
+  a.fallback = stats->fallback;
+  a.all_dense = p->sel_mode == AC_SEL_DENSE;
+  a.compensate = p->compensate;
+  a.kc = at<uint16_t>(ws, P.kc);
+  a.vc = at<uint16_t>(ws, P.vc);
+  a.lb = at<float>(ws, P.lb);
+  a.tile_off = at<int>(ws, P.tile_off);
+  a.O = O;
+  a.lse = lse;
+  a.L = P.L;
+  a.scale_log2 = attn_scale(p, D) * 1.44269504088896340736f;
+  launch_attn_prep(D, a, stats->kmean, stats->vmean, at<uint16_t>(ws, P.kc), at<uint16_t>(ws, P.vc), at<float>(ws, P.lb),
+                   at<int>(ws, P.tile_off), at<int>(ws, P.seltok), at<long long>(ws, P.pairs), BH, st);
+  AC_CHECK_LAUNCH();
+  const int max_blocks = (int)cdiv(P.L, ATT_QT) + q->ncap;
+  launch_attn(D, a, BH, max_blocks, st);
+  AC_CHECK_LAUNCH();
+  return AC_OK;
+}
+
+// pointer checks for the public structs
+ac_status check_clusters(const ac_clusters *c, const char *what, int need_cap, bool need_rho) {
+  if (!c) return fail(AC_E_ARG, "%s clusters is NULL", what);
+  if (!c->labels || !c->perm || !c->seg || !c->cent || !c->ncl) return fail(AC_E_ARG, "%s clusters has a NULL array", what);
+  if (need_rho && !c->rho) return fail(AC_E_ARG, "%s clusters needs rho", what);
+  if (c->ncap < need_cap) return fail(AC_E_ARG, "%s clusters capacity %d is below %d", what, c->ncap, need_cap);
+  return AC_OK;
+}
+ac_status check_kstats(const ac_kstats *s) {
+  if (!s) return fail(AC_E_ARG, "kstats is NULL");
+  if (!s->kmax || !s->kmin || !s->kmean || !s->vmean || !s->fallback || !s->tau || !s->mse || !s->stages)
+    return fail(AC_E_ARG, "kstats has a NULL array");
+  return AC_OK;
+}
+ac_status check_sel(const ac_selection *s, int ncapk) {
+  if (!s) return fail(AC_E_ARG, "selection is NULL");
+  if (!s->list || !s->n || !s->mask) return fail(AC_E_ARG, "selection has a NULL array");
+  if (s->ncap_k != ncapk) return fail(AC_E_ARG, "selection ncap_k %d differs from the key capacity %d", s->ncap_k, ncapk);
+  return AC_OK;
+}
+
+}  // namespace
+}  // namespace ac
+
+using namespace ac;
+
+AC_API ac_status ac_params_default(ac_params *p) {
+  if (!p) return fail(AC_E_ARG, "params is NULL");
+  std::memset(p, 0, sizeof(*p));
+  p->nq = 65;
+  p->iters = 10;
+  p->iters_warm = 3;
+  p->m0 = 200;
+  p->nmax = 1500;
+  p->tau_rule = AC_TAU_MEAN_X;
+  p->tau_param = 1.5f;
+  p->score_mode = AC_SCORE_QUEST;
+  p->sel_mode = AC_SEL_DENSITY;
+  p->topk = 8;
+  p->sel_param = 0.15f;
+  p->compensate = 0;
+  p->scale = 0.f;
+  p->init_sample = 32;
+  p->seed = 0;
+  return AC_OK;
+}
+
+AC_API ac_status ac_sizes(const ac_shape *s, const ac_params *p, int32_t *ncap_k, size_t *ws_bytes) {
+  AC_TRY(check_shape(s));
+  AC_TRY(check_params(s, p));
+  if (!ncap_k || !ws_bytes) return fail(AC_E_ARG, "output pointer is NULL");
+  Plan P = make_plan(s, p);
+  *ncap_k = P.ncapk;
+  *ws_bytes = P.total;
+  return AC_OK;
+}
+
+AC_API ac_status ac_cluster_q(const ac_shape *s, const ac_params *p, const uint16_t *Q, const float *warm_cent,
+                              ac_clusters *q_out, void *ws, size_t ws_bytes, ac_stream_t stream) {
+  AC_TRY(check_shape(s));
+  AC_TRY(check_params(s, p));
+  if (!Q) return fail(AC_E_ARG, "Q is NULL");
+  Plan P = make_plan(s, p);
+  AC_TRY(check_clusters(q_out, "query", P.nq, true));
+  if (q_out->ncap != P.nq) return fail(AC_E_ARG, "query clusters ncap must be min(nq, L) = %d", P.nq);
+  AC_TRY(check_ws(P, ws, ws_bytes));
+  AC_TRY(check_device());
+  return do_cluster_q(P, p, Q, warm_cent, q_out, ws, (hipStream_t)stream);
+}
+
+AC_API ac_status ac_cluster_k(const ac_shape *s, const ac_params *p, const uint16_t *K, const uint16_t *V,
+                              const ac_state *warm, ac_clusters *k_out, ac_kstats *stats, void *ws, size_t ws_bytes,
+                              ac_stream_t stream) {
+  AC_TRY(check_shape(s));
+  AC_TRY(check_params(s, p));
+  if (!K || !V) return fail(AC_E_ARG, "K or V is NULL");
+  Plan P = make_plan(s, p);
+  AC_TRY(check_clusters(k_out, "key", P.ncapk, false));
+  if (k_out->ncap != P.ncapk) return fail(AC_E_ARG, "key clusters ncap must be %d", P.ncapk);
+  AC_TRY(check_kstats(stats));
+  const bool is_warm = warm && warm->valid;
+  if (is_warm && (!warm->cent_k || !warm->ncl_k || !warm->fallback || !warm->tau))
+    return fail(AC_E_ARG, "warm state has a NULL array");
+  AC_TRY(check_ws(P, ws, ws_bytes));
+  AC_TRY(check_device());
+  if (is_warm) return do_cluster_k_warm(P, p, K, V, warm, k_out, stats, ws, (hipStream_t)stream);
+  return do_cluster_k_cold(P, p, K, V, k_out, stats, ws, (hipStream_t)stream);
+}
+
+AC_API ac_status ac_score_select(const ac_shape *s, const ac_params *p, const ac_clusters *q, const ac_clusters *k,
+                                 const ac_kstats *stats, ac_selection *sel, void *ws, size_t ws_bytes,
+                                 ac_stream_t stream) {
+  AC_TRY(check_shape(s));
+  AC_TRY(check_params(s, p));
+  Plan P = make_plan(s, p);
+  AC_TRY(check_clusters(q, "query", P.nq, true));
+  if (q->ncap != P.nq) return fail(AC_E_ARG, "query clusters ncap must be min(nq, L) = %d", P.nq);
+  AC_TRY(check_clusters(k, "key", P.ncapk, false));
+  if (k->ncap != P.ncapk) return fail(AC_E_ARG, "key clusters ncap must be %d", P.ncapk);
+  AC_TRY(check_kstats(stats));
+  AC_TRY(check_sel(sel, P.ncapk));
+  AC_TRY(check_ws(P, ws, ws_bytes));
+  AC_TRY(check_device());
+  return do_score_select(P, p, q, k, stats, sel, ws, (hipStream_t)stream);
+}
+
+AC_API ac_status ac_sparse_attn(const ac_shape *s, const ac_params *p, const uint16_t *Q, const uint16_t *K,
+                                const uint16_t *V, const ac_clusters *q, const ac_clusters *k, const ac_kstats *stats,
+                                const ac_selection *sel, uint16_t *O, float *lse, void *ws, size_t ws_bytes,
+                                ac_stream_t stream) {
+  AC_TRY(check_shape(s));
+  AC_TRY(check_params(s, p));
+  if (!Q || !K || !V || !O) return fail(AC_E_ARG, "Q, K, V or O is NULL");
+  Plan P = make_plan(s, p);
+  AC_TRY(check_clusters(q, "query", P.nq, false));
+  if (q->ncap != P.nq) return fail(AC_E_ARG, "query clusters ncap must be min(nq, L) = %d", P.nq);
+  AC_TRY(check_clusters(k, "key", P.ncapk, false));
+  if (k->ncap != P.ncapk) return fail(AC_E_ARG, "key clusters ncap must be %d", P.ncapk);
+  AC_TRY(check_kstats(stats));
+  AC_TRY(check_sel(sel, P.ncapk));
+  AC_TRY(check_ws(P, ws, ws_bytes));
+  AC_TRY(check_device());
+  return do_attn(P, p, Q, K, V, q, k, stats, sel, O, lse, ws, (hipStream_t)stream);
+}
+
+AC_API ac_status ac_layer(const ac_shape *s, const ac_params *p, const uint16_t *Q, const uint16_t *K,
+                          const uint16_t *V, ac_state *state, uint16_t *O, ac_layer_stats *host_stats, void *ws,
+                          size_t ws_bytes, ac_stream_t stream) {
+  AC_TRY(check_shape(s));
+  AC_TRY(check_params(s, p));
+  if (!Q || !K || !V || !O) return fail(AC_E_ARG, "Q, K, V or O is NULL");
+  if (!state || !state->cent_q || !state->cent_k || !state->ncl_k || !state->fallback || !state->tau)
+    return fail(AC_E_ARG, "state is NULL or has a NULL array");
+  Plan P = make_plan(s, p);
+  AC_TRY(check_ws(P, ws, ws_bytes));
+  AC_TRY(check_device());
+  hipStream_t st = (hipStream_t)stream;
+  const int BH = P.BH, D = P.D;
+  ac_clusters q{P.nq, at<int>(ws, P.q_labels), at<int>(ws, P.q_perm), at<int>(ws, P.q_seg), at<float>(ws, P.q_cent),
+                at<int>(ws, P.q_ncl), at<float>(ws, P.q_rho)};
+  ac_clusters k{P.ncapk, at<int>(ws, P.k_labels), at<int>(ws, P.k_perm), at<int>(ws, P.k_seg), at<float>(ws, P.k_cent),
+                at<int>(ws, P.k_ncl), nullptr};
+  ac_kstats ks{at<uint16_t>(ws, P.kmax), at<uint16_t>(ws, P.kmin), at<float>(ws, P.kmean), at<float>(ws, P.vmean),
+               at<uint8_t>(ws, P.fb), at<float>(ws, P.tau), at<float>(ws, P.mse), at<int>(ws, P.stages)};
+  ac_selection sel{P.ncapk, at<int>(ws, P.sel_list), at<int>(ws, P.sel_n), at<uint32_t>(ws, P.sel_mask),
+                   at<float>(ws, P.sel_score)};
+  const bool warm = state->valid != 0;
+  AC_TRY(do_cluster_q(P, p, Q, warm ? state->cent_q : nullptr, &q, ws, st));
+  if (warm)
+    AC_TRY(do_cluster_k_warm(P, p, K, V, state, &k, &ks, ws, st));
+  else
+    AC_TRY(do_cluster_k_cold(P, p, K, V, &k, &ks, ws, st));
+  AC_TRY(do_score_select(P, p, &q, &k, &ks, &sel, ws, st));
+  AC_TRY(do_attn(P, p, Q, K, V, &q, &k, &ks, &sel, O, nullptr, ws, st));
+  // carry the centres (and, after a cold step, counts, flags and tau) to the next step
+  AC_HIP(hipMemcpyAsync(state->cent_q, q.cent, (size_t)BH * P.nq * D * 4, hipMemcpyDeviceToDevice, st));
+  AC_HIP(hipMemcpyAsync(state->cent_k, k.cent, (size_t)BH * P.ncapk * D * 4, hipMemcpyDeviceToDevice, st));
+  if (!warm) {
+    launch_copy_i32(k.ncl, state->ncl_k, BH, st);
+    launch_copy_u8(ks.fallback, state->fallback, BH, st);
+    launch_copy_f32(ks.tau, state->tau, BH, st);
+    AC_CHECK_LAUNCH();
+    state->valid = 1;
+  }
+  if (host_stats) {
+    AC_HIP(hipStreamSynchronize(st));
+    if (host_stats->ncl_k) AC_HIP(hipMemcpy(host_stats->ncl_k, k.ncl, BH * 4, hipMemcpyDeviceToHost));
+    if (host_stats->fallback) AC_HIP(hipMemcpy(host_stats->fallback, ks.fallback, BH, hipMemcpyDeviceToHost));
+    if (host_stats->tau) AC_HIP(hipMemcpy(host_stats->tau, ks.tau, BH * 4, hipMemcpyDeviceToHost));
+    if (host_stats->mse) AC_HIP(hipMemcpy(host_stats->mse, ks.mse, BH * 4, hipMemcpyDeviceToHost));
+    if (host_stats->stages) AC_HIP(hipMemcpy(host_stats->stages, ks.stages, BH * 4, hipMemcpyDeviceToHost));
+    if (host_stats->pairs) AC_HIP(hipMemcpy(host_stats->pairs, at<long long>(ws, P.pairs), BH * 8, hipMemcpyDeviceToHost));
+  }
+  return AC_OK;
+}
+
+AC_API const char *ac_status_str(ac_status st) {
+  switch (st) {
+    case AC_OK: return "ok";
+    case AC_E_ARG: return "invalid argument";
+    case AC_E_SHAPE: return "invalid shape";
+    case AC_E_WORKSPACE: return "workspace too small";
+    case AC_E_UNSUPPORTED: return "unsupported configuration";
+    case AC_E_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+AC_API const char *ac_last_error(void) { return g_err; }

@@ -1,0 +1,317 @@
+// Cluster-routed block-sparse flash attention for gfx950.
+//
+// A block takes ATT_QT = 128 queries of one query cluster (4 waves x 32) and
+// walks the concatenation of the key clusters selected for that cluster in
+// tiles of 64 keys.  Tiles may span cluster boundaries, so each (query tile,
+// selection) has a single ragged tail however small the clusters are.  Rows
+// are gathered through the counting-sort permutations inside the kernel; the
+// output is scattered back to original token order.  With compensation the
+// non-empty excluded clusters follow as pseudo-keys (key mean, value mean,
+// logit bias log2 n_c in base-2 units); fallback heads attend to all keys.
+//
+// MFMA layout (v_mfma_f32_32x32x16_bf16, 64 lanes, g = lane / 32):
+//   S^T = K . Q^T: A = K rows (lane -> key slot), B = Q (lane -> query),
+//   accumulator lane l holds query l % 32 and 16 keys of each 32-key block,
+//   register j <-> key 16*(j/8) + 8*g + (j%8) (the K rows are loaded in that
+//   order).  Those 8-register halves are exactly the B operand of
+//   O^T = V^T . P^T for 16 contiguous keys, and V^T comes from a transposed
+//   LDS tile with one 16-byte read per lane and k-step.
+#include "common.h"
+#include "internal.h"
+
+namespace ac {
+
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_prep(AttnArgs a, const float *__restrict__ kmean,
+                                                   const float *__restrict__ vmean, uint16_t *__restrict__ kc,
+                                                   uint16_t *__restrict__ vc, float *__restrict__ lb,
+                                                   int *__restrict__ tile_off, const int *__restrict__ seltok,
+                                                   long long *__restrict__ pairs) {
+  const int h = blockIdx.y, c = blockIdx.x;
+  if (c < a.ncap && a.compensate) {
+    const int64_t o = ((int64_t)h * a.ncap + c) * D;
+    for (int dd = threadIdx.x; dd < D; dd += 256) {
+      kc[o + dd] = f2bf(kmean[o + dd]);
+      vc[o + dd] = f2bf(vmean[o + dd]);
+    }
+    if (threadIdx.x == 0) {
+      const int *seg = a.seg_k + (int64_t)h * (a.ncap + 1);
+      const int cnt = c < a.ncl_k[h] ? seg[c + 1] - seg[c] : 0;
+      lb[(int64_t)h * a.ncap + c] = cnt > 0 ? log2f((float)cnt) : -__builtin_inff();
+    }
+  }
+  if (c == 0 && threadIdx.x == 0) {
+    const int *sq = a.seg_q + (int64_t)h * (a.nqcap + 1);
+    int *to = tile_off + (int64_t)h * (a.nqcap + 1);
+    const int nq = a.ncl_q[h];
+    const bool dense = a.all_dense || (a.fallback != nullptr && a.fallback[h] != 0);
+    int run = 0;
+    long long pr = 0;
+    for (int r = 0; r <= a.nqcap; ++r) {
+      to[r] = run;
+      if (r < nq) {
+        const int cnt = sq[r + 1] - sq[r];
+        run += (cnt + ATT_QT - 1) / ATT_QT;
+        pr += (long long)cnt * (dense ? (long long)a.L : (long long)seltok[(int64_t)h * a.nqcap + r]);
+      }
+    }
+    pairs[h] = pr;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
+  constexpr int KSQ = D / 16;        // k-steps of the QK product
+  constexpr int DB = D / 32;         // 32-dim blocks of O
+  constexpr int KROW = D + 8;        // padded K row (bf16)
+  constexpr int VROW = ATT_KT + 8;   // padded V^T row (keys)
+  const int h = blockIdx.y;
+  const int blk = blockIdx.x;
+  const int nq = a.ncl_q[h];
+  const int *toff = a.tile_off + (int64_t)h * (a.nqcap + 1);
+  if (nq <= 0 || blk >= toff[nq]) return;
+  int lo = 0, hi = nq;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (toff[mid] <= blk) lo = mid; else hi = mid;
+  }
+  const int r = lo;
+  const int *segq = a.seg_q + (int64_t)h * (a.nqcap + 1);
+  const int qbeg = segq[r] + (blk - toff[r]) * ATT_QT;
+  const int qend = segq[r + 1];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  __shared__ uint16_t Ks[ATT_KT * KROW];
+  __shared__ uint16_t Vt[D * VROW];
+  __shared__ int rowidx[ATT_KT];
+  __shared__ float sbias[ATT_KT];
+  extern __shared__ int dyn[];
+  int *s_cum = dyn;                       // [ncap + 1]
+  int *s_start = dyn + (a.ncap + 1);      // [ncap]
+  uint32_t *s_mask = (uint32_t *)(dyn + 2 * a.ncap + 1);  // [mwords]
+
+  const bool dense = a.all_dense || (a.fallback != nullptr && a.fallback[h] != 0);
+  const int64_t rowi = (int64_t)h * a.nqcap + r;
+  int nsel = 0;
+  int T;
+  if (!dense) {
+    nsel = a.nsel[rowi];
+    const int *lst = a.list + rowi * a.ncap;
+    const int *segk = a.seg_k + (int64_t)h * (a.ncap + 1);
+    const int per = (nsel + 255) / 256;
+    const int ib = min(nsel, tid * per), ie = min(nsel, ib + per);
+    int loc = 0;
+    for (int i = ib; i < ie; ++i) {
+      int c = lst[i];
+      int s0 = segk[c];
+      s_start[i] = s0;
+      s_cum[i] = segk[c + 1] - s0;  // length for now
+      loc += s_cum[i];
+    }
+    __shared__ int scan[256];
+    scan[tid] = loc;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      int v = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    int run = scan[tid] - loc;
+    for (int i = ib; i < ie; ++i) {
+      int len = s_cum[i];
+      s_cum[i] = run;
+      run += len;
+    }
+    if (tid == 255) s_cum[nsel] = scan[255];
+    if (a.compensate)
+      for (int w = tid; w < a.mwords; w += 256) s_mask[w] = a.mask[rowi * a.mwords + w];
+    __syncthreads();
+    T = s_cum[nsel];
+  } else {
+    T = a.L;
+  }
+
+  // Q fragments of this wave's 32 queries (B operand of S^T = K Q^T)
+  const int qi = qbeg + wave * 32 + l32;
+  const bool qvalid = qi < qend;
+  const int64_t qrow = qvalid ? (int64_t)a.perm_q[(int64_t)h * a.L + qi] : 0;
+  bf16x8_t qf[KSQ];
+  {
+    const uint16_t *qr = a.Q + ((int64_t)h * a.L + qrow) * D;
+#pragma unroll
+    for (int ks = 0; ks < KSQ; ++ks)
+      qf[ks] = qvalid ? *(const bf16x8_t *)&qr[ks * 16 + g * 8] : (bf16x8_t){};
+  }
+
+  f32x16_t acc_o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc_o[db] = (f32x16_t){};
+  float m_i = -__builtin_inff();
+  float l_i = 0.f;
+  const float sl2 = a.scale_log2;
+
+  const uint16_t *Kh = a.K + (int64_t)h * a.L * D;
+  const uint16_t *Vh = a.V + (int64_t)h * a.L * D;
+  const int *permk = a.perm_k + (int64_t)h * a.L;
+  const int ncl_k = a.ncl_k[h];
+  const int phases = (!dense && a.compensate) ? 2 : 1;
+
+  for (int phase = 0; phase < phases; ++phase) {
+    const int total = phase == 0 ? T : ncl_k;
+    const uint16_t *Kp = phase == 0 ? Kh : a.kc + (int64_t)h * a.ncap * D;
+    const uint16_t *Vp = phase == 0 ? Vh : a.vc + (int64_t)h * a.ncap * D;
+    for (int k0 = 0; k0 < total; k0 += ATT_KT) {
+      __syncthreads();  // previous tile fully consumed
+      if (tid < ATT_KT) {
+        const int o = k0 + tid;
+        int rw = -1;
+        float bias = 0.f;
+        if (o < total) {
+          if (phase == 1) {
+            rw = o;
+            const bool selected = (s_mask[o >> 5] >> (o & 31)) & 1u;
+            bias = selected ? -__builtin_inff() : a.lb[(int64_t)h * a.ncap + o];
+          } else if (dense) {
+            rw = o;
+          } else {
+            int lo2 = 0, hi2 = nsel;  // s_cum[lo2] <= o < s_cum[hi2]
+            while (hi2 - lo2 > 1) {
+              int mid = (lo2 + hi2) >> 1;
+              if (s_cum[mid] <= o) lo2 = mid; else hi2 = mid;
+            }
+            rw = permk[s_start[lo2] + (o - s_cum[lo2])];
+          }
+        } else {
+          bias = -__builtin_inff();
+        }
+        rowidx[tid] = rw;
+        sbias[tid] = bias;
+      }
+      __syncthreads();
+      // K tile -> Ks (row-major), V tile -> Vt (transposed)
+#pragma unroll
+      for (int it = 0; it < (ATT_KT * D / 8) / 256; ++it) {
+        const int q = tid + it * 256;
+        const int rr = q / (D / 8), cc = (q % (D / 8)) * 8;
+        const int rw = rowidx[rr];
+        u32x4_t v = {0, 0, 0, 0};
+        if (rw >= 0) v = *(const u32x4_t *)&Kp[(int64_t)rw * D + cc];
+        *(u32x4_t *)&Ks[rr * KROW + cc] = v;
+      }
+#pragma unroll
+      for (int it = 0; it < (ATT_KT / 2 * D / 8) / 256; ++it) {
+        const int q = tid + it * 256;
+        const int kp = q % (ATT_KT / 2), dc = q / (ATT_KT / 2);
+        const int r0 = rowidx[2 * kp], r1 = rowidx[2 * kp + 1];
+        u32x4_t v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
+        if (r0 >= 0) v0 = *(const u32x4_t *)&Vp[(int64_t)r0 * D + dc * 8];
+        if (r1 >= 0) v1 = *(const u32x4_t *)&Vp[(int64_t)r1 * D + dc * 8];
+        const uint16_t *e0 = (const uint16_t *)&v0;
+        const uint16_t *e1 = (const uint16_t *)&v1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          *(uint32_t *)&Vt[(dc * 8 + i) * VROW + 2 * kp] = (uint32_t)e0[i] | ((uint32_t)e1[i] << 16);
+      }
+      __syncthreads();
+
+      // S^T for two 32-key blocks
+      f32x16_t acc_s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        acc_s[kb] = (f32x16_t){};
+        // key slot l32 -> tile key 32*kb + 16*(a/2) + 8*gg + 4*(a%2) + b, with l32 = 8a + 4gg + b
+        const int aa = l32 >> 3, gg = (l32 >> 2) & 1, bb = l32 & 3;
+        const int key = 32 * kb + 16 * (aa >> 1) + 8 * gg + 4 * (aa & 1) + bb;
+#pragma unroll
+        for (int ks = 0; ks < KSQ; ++ks) {
+          bf16x8_t kf = *(const bf16x8_t *)&Ks[key * KROW + ks * 16 + g * 8];
+          acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], acc_s[kb], 0, 0, 0);
+        }
+      }
+      // scores in base-2 units, masked / biased
+      float mt = -__builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = 32 * kb + 16 * (j >> 3) + 8 * g + (j & 7);
+          float sv = acc_s[kb][j] * sl2 + sbias[key];
+          acc_s[kb][j] = sv;
+          mt = fmaxf(mt, sv);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m_i, mt);
+      const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
+      const float alpha = exp2f(m_i - m_use);
+      float psum = 0.f;
+      bf16x8_t pb[4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          bf16x8_t t;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            float p = exp2f(acc_s[kb][half * 8 + i] - m_use);
+            psum += p;
+            t[i] = (__bf16)p;
+          }
+          pb[kb * 2 + half] = t;
+        }
+      l_i = l_i * alpha + psum;
+      m_i = m_new;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc_o[db][j] *= alpha;
+      // O^T += V^T P^T over 4 k-steps of 16 keys
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int kbase = 16 * s + 8 * g;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          bf16x8_t vf = *(const bf16x8_t *)&Vt[(32 * db + l32) * VROW + kbase];
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[s], acc_o[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  const float lsum = l_i + __shfl_xor(l_i, 32, 64);
+  if (!qvalid) return;
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  uint16_t *orow = a.O + ((int64_t)h * a.L + qrow) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      const int d0 = 32 * db + 8 * jq + 4 * g;
+      uint32_t w0 = (uint32_t)f2bf(acc_o[db][jq * 4 + 0] * inv) | ((uint32_t)f2bf(acc_o[db][jq * 4 + 1] * inv) << 16);
+      uint32_t w1 = (uint32_t)f2bf(acc_o[db][jq * 4 + 2] * inv) | ((uint32_t)f2bf(acc_o[db][jq * 4 + 3] * inv) << 16);
+      *(u32x2_t *)&orow[d0] = (u32x2_t){w0, w1};
+    }
+  if (a.lse != nullptr && g == 0)
+    a.lse[(int64_t)h * a.L + qrow] = lsum > 0.f ? (m_i + log2f(lsum)) * 0.69314718055994530942f : -__builtin_inff();
+}
+
+void launch_attn_prep(int D, const AttnArgs &a, const float *kmean, const float *vmean, uint16_t *kc, uint16_t *vc,
+                      float *lb, int *tile_off, const int *seltok, long long *pairs, int BH, hipStream_t st) {
+  dim3 grid(a.compensate ? a.ncap : 1, BH);
+  if (D == 64)
+    hipLaunchKernelGGL(k_attn_prep<64>, grid, dim3(256), 0, st, a, kmean, vmean, kc, vc, lb, tile_off, seltok, pairs);
+  else
+    hipLaunchKernelGGL(k_attn_prep<128>, grid, dim3(256), 0, st, a, kmean, vmean, kc, vc, lb, tile_off, seltok, pairs);
+}
+
+void launch_attn(int D, const AttnArgs &a, int BH, int max_blocks, hipStream_t st) {
+  size_t dyn = (size_t)(2 * a.ncap + 1 + a.mwords) * sizeof(int);
+  if (D == 64)
+    hipLaunchKernelGGL(k_attn<64>, dim3(max_blocks, BH), dim3(256), dyn, st, a);
+  else
+    hipLaunchKernelGGL(k_attn<128>, dim3(max_blocks, BH), dim3(256), dyn, st, a);
+}
+
+}  // namespace ac

@@ -1,0 +1,91 @@
+// Device-side helpers shared by the gfx950 kernels of the layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define AC_DEV __device__ __forceinline__
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+namespace ac {
+
+constexpr int kWave = 64;
+
+// bf16 bit pattern -> fp32 (exact).
+AC_DEV float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// fp32 -> bf16 bit pattern, round to nearest even (finite inputs).
+AC_DEV uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// fp64 -> bf16 bit pattern with a single rounding to 8 significant bits
+// (nearest, ties to even), for values in the bf16 normal range or zero:
+// round the binary64 significand at bit 45, then narrow exactly to fp32.
+AC_DEV uint16_t d2bf(double x) {
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  u += 0x00000FFFFFFFFFFFull + ((u >> 45) & 1ull);
+  u &= ~0x00001FFFFFFFFFFFull;
+  float f = (float)__longlong_as_double((long long)u);  // exact: <= 8 significant bits
+  return (uint16_t)(__float_as_uint(f) >> 16);
+}
+
+// Split an fp32 value into bf16 parts whose sum reproduces it: hi = bf16(x),
+// mid = bf16(x - hi), lo = bf16(x - hi - mid).  The differences are exact in fp32.
+AC_DEV void split3(float x, uint16_t &hi, uint16_t &mid, uint16_t &lo) {
+  hi = f2bf(x);
+  float r1 = x - bf2f(hi);
+  mid = f2bf(r1);
+  float r2 = r1 - bf2f(mid);
+  lo = f2bf(r2);
+}
+
+// Order-preserving map of fp32 to uint32 (larger float -> larger integer).
+AC_DEV uint32_t f2ord(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// SplitMix64 step from state z (Steele, Lea and Flood 2014): add the golden
+// gamma, then the xor-shift-multiply finaliser.
+AC_DEV uint64_t splitmix64(uint64_t z) {
+  z += 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Counter-based uniform in [0, 1) for (seed, stream, counter).
+AC_DEV double uniform01(uint64_t seed, uint64_t stream, uint64_t counter) {
+  uint64_t x = splitmix64(seed);
+  x = splitmix64(x ^ stream);
+  x = splitmix64(x ^ counter);
+  return (double)(x >> 11) * (1.0 / 9007199254740992.0);
+}
+
+// Random stream of one k-means++ run: head, role (0 queries, 1 keys), stage.
+AC_DEV uint64_t stream_id(uint64_t bh, uint32_t role, uint32_t stage) {
+  return ((bh & ((1ull << 44) - 1)) << 20) | ((uint64_t)(role & 0xF) << 16) | (stage & 0xFFFF);
+}
+
+template <typename T>
+AC_DEV T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+AC_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace ac

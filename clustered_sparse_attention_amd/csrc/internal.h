@@ -1,0 +1,156 @@
+// Internal interfaces between the host library and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ac {
+
+constexpr int KPP_SMAX = 16384;  // most points a k-means++ subsample may hold
+constexpr int SORT_TILE = 512;   // points per counting-sort tile (one wave)
+constexpr int ATT_QT = 128;      // query rows per attention block
+constexpr int ATT_KT = 64;       // keys per attention tile
+constexpr int SEL_MAXN = 4096;   // most key clusters the select kernel sorts
+
+enum { TAU_RULE_MEAN_X = 0, TAU_RULE_PCTL = 1, TAU_RULE_ABS = 2, TAU_RULE_INF = 3 };
+
+// One batched k-means job (see kmeans.hip).
+struct KmArgs {
+  const uint16_t *X;  // [BH] heads of rows, head stride x_hs elements, rows of D bf16
+  int64_t x_hs;
+  const int *idx;     // [BH, idx_hs] point -> row, or NULL (point i is row i)
+  int64_t idx_hs;
+  const int *n;       // [BH] points per head
+  const int *m;       // [BH] centres per head
+  const int *coff;    // [BH] first centre of the job in cent
+  float *cent;        // [BH, cent_hs] fp32 centres (rows of D)
+  int64_t cent_hs;
+};
+
+// GEMM operands of the job's centres, indexed by local centre id.
+struct CentOps {
+  uint16_t *hi;  // [BH, cap, D]
+  uint16_t *lo;  // [BH, cap, D]
+  float *norm;   // [BH, cap]
+  int cap;
+};
+
+struct SortArgs {
+  const int *labels;  // [BH, lab_hs]
+  int64_t lab_hs;
+  const int *n;       // [BH]
+  const int *m;       // [BH]
+  int *tile_hist;     // [BH, max_tiles, mcap]
+  int max_tiles;
+  int mcap;
+  int *perm;          // [BH, perm_hs]
+  int64_t perm_hs;
+  int *seg;           // [BH, seg_hs], entries 0..segcap written
+  int64_t seg_hs;
+  int segcap;
+};
+
+struct KStatsArgs {
+  const uint16_t *K, *V;  // [BH, L, D]
+  const int *perm, *seg;  // [BH, L], [BH, ncap + 1]
+  const int *ncl;         // [BH]
+  const float *cent;      // [BH, ncap, D]
+  uint16_t *kmax, *kmin;  // [BH, ncap, D]
+  float *kmean, *vmean;   // [BH, ncap, D]
+  double *msepart;        // [BH, ncap]
+  float *mse;             // [BH]
+  int L, ncap;
+};
+
+struct ScoreArgs {
+  const float *cq;        // [BH, nqcap, D] query-cluster centres
+  int nqcap;              // rows per head of cq / S
+  int nq;                 // rows used
+  const uint16_t *kmax, *kmin;
+  const float *kmean;
+  const int *seg_k;       // [BH, ncap + 1]
+  const int *ncl_k;       // [BH]
+  int ncap;               // key-cluster capacity
+  int mode;               // 0 QUEST, 1 MEAN
+  uint16_t *A;            // [BH, nq_pad, 6D]
+  uint16_t *Bm;           // [BH, ncap_pad, 6D]
+  int nq_pad, ncap_pad;
+  float *S;               // [BH, nqcap, ncap]
+};
+
+struct SelectArgs {
+  const float *S;         // [BH, nqcap, ncap]
+  const int *seg_k;       // [BH, ncap + 1]
+  const int *ncl_k;       // [BH]
+  const float *rho;       // [BH, nqcap]
+  const int *ncl_q;       // [BH]
+  int nqcap, ncap, L, D;
+  int mode, topk;
+  float param, scale;
+  int *list;              // [BH, nqcap, ncap]
+  int *nsel;              // [BH, nqcap]
+  uint32_t *mask;         // [BH, nqcap, mwords]
+  int mwords;
+  int *seltok;            // [BH, nqcap] selected key tokens
+};
+
+struct AttnArgs {
+  const uint16_t *Q, *K, *V;  // [BH, L, D]
+  const int *perm_q, *seg_q;  // [BH, L], [BH, nqcap + 1]
+  const int *ncl_q;           // [BH]
+  int nqcap;
+  const int *perm_k, *seg_k;  // [BH, L], [BH, ncap + 1]
+  const int *ncl_k;
+  int ncap;
+  const int *list, *nsel;     // [BH, nqcap, ncap], [BH, nqcap]
+  const uint32_t *mask;       // [BH, nqcap, mwords]
+  int mwords;
+  const uint8_t *fallback;    // [BH] or NULL
+  int all_dense;
+  int compensate;
+  const uint16_t *kc, *vc;    // [BH, ncap, D] bf16 pseudo-keys / values
+  const float *lb;            // [BH, ncap] log2(n_c) or -inf
+  const int *tile_off;        // [BH, nqcap + 1] first block of each query cluster
+  uint16_t *O;                // [BH, L, D]
+  float *lse;                 // [BH, L] or NULL
+  int L;
+  float scale_log2;           // scale * log2(e)
+};
+
+// kmeans.hip
+void launch_qnorm(int D, const uint16_t *Q, uint16_t *Qh, float *qn, int64_t rows, hipStream_t st);
+void launch_kpp_init(int D, const KmArgs &a, int BH, double *d2buf, int init_sample, uint64_t seed, int role,
+                     int stage, hipStream_t st);
+void launch_cent_prep(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, hipStream_t st);
+void launch_assign(int D, const KmArgs &a, const CentOps &op, int BH, int nmax_pts, int *labels, int64_t lab_hs,
+                   hipStream_t st);
+void launch_sort(const SortArgs &s, int BH, int nmax_pts, hipStream_t st);
+void launch_update(int D, const KmArgs &a, const SortArgs &s, const CentOps &op, int BH, int mmax, hipStream_t st);
+void launch_stage_dist(int D, const KmArgs &a, int BH, int nmax_pts, const int *labels, int64_t lab_hs, float *dist,
+                       int64_t dist_hs, hipStream_t st);
+void launch_tau(const float *dist, int64_t dist_hs, const int *n_arr, int BH, int nmax_pts, int rule, float param,
+                float *tau, uint32_t *radix_state, uint32_t *radix_hist, hipStream_t st);
+void launch_flag_removed(const float *dist, int64_t dist_hs, const int *n_arr, const float *tau, int *flag,
+                         int64_t flag_hs, int BH, int nmax_pts, hipStream_t st);
+void launch_compact_gather(const int *idx_old, int64_t idx_hs, const int *perm, int64_t perm_hs, const int *seg,
+                           int64_t seg_hs, int *idx_new, int *n_new, int BH, int nmax_pts, hipStream_t st);
+void launch_kstats(int D, const KStatsArgs &s, int BH, hipStream_t st);
+void launch_seg_mean(const float *val, const int *perm, const int *seg, int L, int ncap, const int *ncl, float *out,
+                     int BH, hipStream_t st);
+void launch_fill_i32(int *p, int64_t n, int v, hipStream_t st);
+void launch_fill_u8(uint8_t *p, int64_t n, uint8_t v, hipStream_t st);
+void launch_copy_i32(const int *s, int *d, int64_t n, hipStream_t st);
+void launch_copy_f32(const float *s, float *d, int64_t n, hipStream_t st);
+void launch_copy_u8(const uint8_t *s, uint8_t *d, int64_t n, hipStream_t st);
+void launch_set_m_min(int *m, const int *n, int v, int BH, hipStream_t st);
+
+// select.hip
+void launch_score(int D, const ScoreArgs &a, int BH, hipStream_t st);
+void launch_select(const SelectArgs &a, int BH, hipStream_t st);
+
+// attn.hip
+void launch_attn_prep(int D, const AttnArgs &a, const float *kmean, const float *vmean, uint16_t *kc, uint16_t *vc,
+                      float *lb, int *tile_off, const int *seltok, long long *pairs, int BH, hipStream_t st);
+void launch_attn(int D, const AttnArgs &a, int BH, int max_blocks, hipStream_t st);
+
+}  // namespace ac

@@ -1,0 +1,831 @@
+// Clustering kernels for gfx950: query normalisation, batched k-means
+// (k-means++ seeding, MFMA distance GEMM with a fused argmin, counting-sort
+// based centre update), the per-stage distance / threshold / compaction steps
+// of AdaCluster Algorithm 1, and the per-cluster key statistics.
+//
+// A "job" runs one k-means per head over that head's point list: point i of
+// head h is row idx[h][i] (or row i when idx is NULL) of X[h], there are n[h]
+// points and m[h] centres, stored at cent[h][coff[h] + c].  Heads with n = 0
+// or m = 0 are idle.  Every launch covers all heads (grid.y = head).
+#include "common.h"
+#include "internal.h"
+
+namespace ac {
+
+// ---------------------------------------------------------------------------
+// Query normalisation (AdaCluster §3.1): q_hat = bf16(q / ||q||), ||q|| fp32.
+// Eight lanes per row; the norm and quotient are fp64, rounded once to bf16.
+template <int D>
+__global__ __launch_bounds__(256) void k_qnorm(const uint16_t *__restrict__ Q, uint16_t *__restrict__ Qh,
+                                               float *__restrict__ qn, int64_t rows) {
+  constexpr int PER = D / 8;  // dims per lane
+  int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 8;
+  int sub = threadIdx.x & 7;
+  if (row >= rows) return;  // whole 8-lane groups exit together
+  const uint16_t *src = Q + row * D + sub * PER;
+  uint16_t v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; i += 8) *(u32x4_t *)&v[i] = *(const u32x4_t *)&src[i];
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    double x = (double)bf2f(v[i]);
+    ss += x * x;
+  }
+  ss += __shfl_xor(ss, 1, 64);
+  ss += __shfl_xor(ss, 2, 64);
+  ss += __shfl_xor(ss, 4, 64);
+  double nrm = sqrt(ss);
+  uint16_t o[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) o[i] = nrm > 0.0 ? d2bf((double)bf2f(v[i]) / nrm) : (uint16_t)0;
+  uint16_t *dst = Qh + row * D + sub * PER;
+#pragma unroll
+  for (int i = 0; i < PER; i += 8) *(u32x4_t *)&dst[i] = *(const u32x4_t *)&o[i];
+  if (sub == 0) qn[row] = (float)nrm;
+}
+
+// ---------------------------------------------------------------------------
+// k-means++ seeding (Arthur and Vassilvitskii 2007) on the strided subsample
+// {floor(j*n/s)}, one block per head.  D^2 is exact fp64 over bf16 points
+// and lives in a global scratch row of SMAX doubles per head.
+template <int D>
+__global__ __launch_bounds__(1024) void k_kpp_init(KmArgs a, double *__restrict__ d2buf, int init_sample,
+                                                  uint64_t seed, int role, int stage) {
+  const int h = blockIdx.y;
+  const int n = a.n[h], m = a.m[h];
+  if (n <= 0 || m <= 0) return;
+  const int s = init_sample > 0 ? min(n, init_sample * m) : n;  // host guarantees s <= SMAX
+  double *D2 = d2buf + (int64_t)h * KPP_SMAX;
+  float *cent = a.cent + (int64_t)h * a.cent_hs + (int64_t)a.coff[h] * D;
+  const uint16_t *X = a.X + (int64_t)h * a.x_hs;
+  const int *idx = a.idx ? a.idx + (int64_t)h * a.idx_hs : nullptr;
+  const uint64_t sid = stream_id((uint64_t)h, role, stage);
+
+  __shared__ float c_sh[D];
+  __shared__ double red[1024 / 64];
+  __shared__ double scan_sh[1024];
+  __shared__ int pick_sh;
+
+  const int tid = threadIdx.x;
+  const int chunk = (s + 1023) / 1024;
+  const int jb = min(s, tid * chunk), je = min(s, jb + chunk);
+
+  auto row_of = [&](int j) -> int64_t {
+    int li = (int)(((int64_t)j * n) / s);
+    return idx ? (int64_t)idx[li] : (int64_t)li;
+  };
+
+  for (int t = 0; t < m; ++t) {
+    double u = uniform01(seed, sid, (uint64_t)t);
+    if (t == 0) {
+      if (tid == 0) pick_sh = min(s - 1, (int)(u * (double)s));
+    } else {
+      // total and the thread-chunk prefix of D^2
+      double loc = 0.0;
+      for (int j = jb; j < je; ++j) loc += D2[j];
+      scan_sh[tid] = loc;
+      __syncthreads();
+      // inclusive Hillis-Steele scan over 1024 partial sums
+      for (int off = 1; off < 1024; off <<= 1) {
+        double v = tid >= off ? scan_sh[tid - off] : 0.0;
+        __syncthreads();
+        scan_sh[tid] += v;
+        __syncthreads();
+      }
+      double total = scan_sh[1023];
+      if (tid == 0) pick_sh = -1;
+      __syncthreads();
+      if (total > 0.0) {
+        double target = u * total;
+        double excl = tid > 0 ? scan_sh[tid - 1] : 0.0;
+        if (excl <= target && target < scan_sh[tid] && je > jb) {
+          double run = excl;
+          int pj = je - 1;
+          for (int j = jb; j < je; ++j) {
+            run += D2[j];
+            if (run > target) { pj = j; break; }
+          }
+          pick_sh = pj;  // exactly one thread satisfies the range test
+        }
+        __syncthreads();
+        if (tid == 0 && pick_sh < 0) pick_sh = s - 1;
+      } else {
+        if (tid == 0) pick_sh = min(s - 1, (int)(u * (double)s));
+      }
+    }
+    __syncthreads();
+    const int pj = pick_sh;
+    const int64_t prow = row_of(pj);
+    for (int dd = tid; dd < D; dd += 1024) {
+      float v = bf2f(X[prow * D + dd]);
+      c_sh[dd] = v;
+      cent[(int64_t)t * D + dd] = v;
+    }
+    __syncthreads();
+    // D^2 update with the new centre
+    for (int j = tid; j < s; j += 1024) {
+      const uint16_t *xr = X + row_of(j) * D;
+      double acc = 0.0;
+#pragma unroll 8
+      for (int dd = 0; dd < D; dd += 8) {
+        u32x4_t w = *(const u32x4_t *)&xr[dd];
+        const uint16_t *e = (const uint16_t *)&w;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          double df = (double)bf2f(e[i]) - (double)c_sh[dd + i];
+          acc += df * df;
+        }
+      }
+      D2[j] = (t == 0) ? acc : fmin(D2[j], acc);
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Centre operands for the distance GEMM: hi = bf16(c), lo = bf16(c - hi),
+// and ||c||^2 (fp64 sum, stored fp32).  One wave per centre.
+template <int D>
+__global__ __launch_bounds__(256) void k_cent_prep(KmArgs a, CentOps op) {
+  const int h = blockIdx.y;
+  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (c >= a.m[h]) return;
+  const float *cr = a.cent + (int64_t)h * a.cent_hs + (int64_t)(a.coff[h] + c) * D;
+  uint16_t *hi = op.hi + ((int64_t)h * op.cap + c) * D;
+  uint16_t *lo = op.lo + ((int64_t)h * op.cap + c) * D;
+  double ss = 0.0;
+  for (int dd = lane; dd < D; dd += 64) {
+    float v = cr[dd];
+    uint16_t bh = f2bf(v);
+    hi[dd] = bh;
+    lo[dd] = f2bf(v - bf2f(bh));
+    ss += (double)v * (double)v;
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) op.norm[(int64_t)h * op.cap + c] = (float)ss;
+}
+
+// ---------------------------------------------------------------------------
+// Nearest centre of every point: argmin_c ||c||^2 - 2 x.c on bf16 MFMA
+// (16x16x32, fp32 accumulation; x.c = x.hi + x.lo).  A block holds 256
+// points (4 waves x 64); centre operands stream through LDS in chunks of 64.
+// Ties go to the lower centre index.
+template <int D>
+__global__ __launch_bounds__(256) void k_assign(KmArgs a, CentOps op, int *__restrict__ labels,
+                                                int64_t lab_hs) {
+  constexpr int KS = D / 32;   // k-steps of 32 dims
+  constexpr int CH = 64;       // centres per LDS chunk
+  constexpr int LDSROW = D + 8;  // padded row (bf16 elements)
+  const int h = blockIdx.y;
+  const int n = a.n[h], m = a.m[h];
+  const int base = blockIdx.x * 256;
+  if (n <= 0 || m <= 0 || base >= n) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l16 = lane & 15, g = lane >> 4;
+
+  __shared__ uint16_t s_hi[CH * LDSROW];
+  __shared__ uint16_t s_lo[CH * LDSROW];
+  __shared__ float s_norm[CH];
+
+  const uint16_t *X = a.X + (int64_t)h * a.x_hs;
+  const int *idx = a.idx ? a.idx + (int64_t)h * a.idx_hs : nullptr;
+
+  // A fragments: 4 row tiles of 16 points, KS k-steps, 8 bf16 each.
+  bf16x8_t af[4][KS];
+  const int wbase = base + wave * 64;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    int i = wbase + rt * 16 + l16;
+    if (i < n) {
+      int64_t row = idx ? (int64_t)idx[i] : (int64_t)i;
+      const uint16_t *xr = X + row * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) af[rt][ks] = *(const bf16x8_t *)&xr[ks * 32 + g * 8];
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) af[rt][ks] = (bf16x8_t){};
+    }
+  }
+
+  float best[4][4];
+  int bidx[4][4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { best[rt][j] = __builtin_inff(); bidx[rt][j] = 0x7fffffff; }
+
+  const uint16_t *ghi = op.hi + (int64_t)h * op.cap * D;
+  const uint16_t *glo = op.lo + (int64_t)h * op.cap * D;
+  const float *gnorm = op.norm + (int64_t)h * op.cap;
+
+  for (int c0 = 0; c0 < m; c0 += CH) {
+    const int cn = min(CH, m - c0);
+    __syncthreads();
+    // stage the chunk: cn rows of D bf16 (hi and lo), 16-byte pieces
+    for (int q = threadIdx.x; q < CH * (D / 8); q += 256) {
+      int r = q / (D / 8), cc = (q % (D / 8)) * 8;
+      u32x4_t vh = {0, 0, 0, 0}, vl = {0, 0, 0, 0};
+      if (r < cn) {
+        vh = *(const u32x4_t *)&ghi[(int64_t)(c0 + r) * D + cc];
+        vl = *(const u32x4_t *)&glo[(int64_t)(c0 + r) * D + cc];
+      }
+      *(u32x4_t *)&s_hi[r * LDSROW + cc] = vh;
+      *(u32x4_t *)&s_lo[r * LDSROW + cc] = vl;
+    }
+    if (threadIdx.x < CH) s_norm[threadIdx.x] = threadIdx.x < cn ? gnorm[c0 + threadIdx.x] : 0.f;
+    __syncthreads();
+#pragma unroll 1
+    for (int ct = 0; ct < CH / 16; ++ct) {
+      if (ct * 16 >= cn) break;
+      f32x4_t acc[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[rt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      const int crow = ct * 16 + l16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8_t bh = *(const bf16x8_t *)&s_hi[crow * LDSROW + ks * 32 + g * 8];
+        bf16x8_t bl = *(const bf16x8_t *)&s_lo[crow * LDSROW + ks * 32 + g * 8];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt][ks], bh, acc[rt], 0, 0, 0);
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt][ks], bl, acc[rt], 0, 0, 0);
+        }
+      }
+      // D layout: lane holds column (centre) l16, rows 4*g + j.
+      const int cidx = c0 + ct * 16 + l16;
+      const bool cvalid = (ct * 16 + l16) < cn;
+      const float cn2 = s_norm[ct * 16 + l16];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float dv = cvalid ? fmaf(-2.f, acc[rt][j], cn2) : __builtin_inff();
+          if (dv < best[rt][j]) { best[rt][j] = dv; bidx[rt][j] = cidx; }
+        }
+    }
+  }
+  // reduce over the 16 lanes that share g (same rows, different centres)
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float bv = best[rt][j];
+      int bi = bidx[rt][j];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        float ov = __shfl_xor(bv, o, 64);
+        int oi = __shfl_xor(bi, o, 64);
+        if (ov < bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      }
+      int i = wbase + rt * 16 + g * 4 + j;
+      if (l16 == 0 && i < n) labels[(int64_t)h * lab_hs + i] = bi == 0x7fffffff ? 0 : bi;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Stable counting sort of per-head labels in [0, m): tile histograms, a scan
+// over tiles and labels, then an in-order scatter of each tile by one wave.
+// perm[h][p] = local index of the p-th point in label order; seg[h][c] the
+// first position of label c, seg[h][c] = n for m <= c <= segcap.
+__global__ __launch_bounds__(64) void k_sort_hist(SortArgs s) {
+  const int h = blockIdx.y, tile = blockIdx.x;
+  const int n = s.n[h], m = s.m[h];
+  const int beg = tile * SORT_TILE;
+  if (beg >= n || m <= 0) return;
+  extern __shared__ int sh_hist[];
+  for (int c = threadIdx.x; c < m; c += 64) sh_hist[c] = 0;
+  __syncthreads();
+  const int *lab = s.labels + (int64_t)h * s.lab_hs;
+  const int end = min(n, beg + SORT_TILE);
+  for (int i = beg + threadIdx.x; i < end; i += 64) atomicAdd(&sh_hist[lab[i]], 1);
+  __syncthreads();
+  int *th = s.tile_hist + ((int64_t)h * s.max_tiles + tile) * s.mcap;
+  for (int c = threadIdx.x; c < m; c += 64) th[c] = sh_hist[c];
+}
+
+__global__ __launch_bounds__(1024) void k_sort_scan(SortArgs s) {
+  const int h = blockIdx.x;
+  const int n = s.n[h], m = s.m[h];
+  int *seg = s.seg + (int64_t)h * s.seg_hs;
+  const int nt = (n + SORT_TILE - 1) / SORT_TILE;
+  __shared__ int part[1024];
+  // per label: exclusive scan over tiles (in place) and the label total
+  const int per = (m + 1023) / 1024;
+  const int cb = min(m, (int)threadIdx.x * per), ce = min(m, cb + per);
+  int tot_local = 0;
+  for (int c = cb; c < ce; ++c) {
+    int run = 0;
+    for (int t = 0; t < nt; ++t) {
+      int *p = s.tile_hist + ((int64_t)h * s.max_tiles + t) * s.mcap + c;
+      int v = *p;
+      *p = run;
+      run += v;
+    }
+    seg[c] = run;  // count for now
+    tot_local += run;
+  }
+  part[threadIdx.x] = tot_local;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int run = part[threadIdx.x] - tot_local;
+  for (int c = cb; c < ce; ++c) {
+    int v = seg[c];
+    seg[c] = run;
+    run += v;
+  }
+  for (int c = m + threadIdx.x; c <= s.segcap; c += 1024) seg[c] = max(n, 0);
+  if (n <= 0)
+    for (int c = threadIdx.x; c <= s.segcap; c += 1024) seg[c] = 0;
+}
+
+__global__ __launch_bounds__(64) void k_sort_scatter(SortArgs s) {
+  const int h = blockIdx.y, tile = blockIdx.x;
+  const int n = s.n[h], m = s.m[h];
+  const int beg = tile * SORT_TILE;
+  if (beg >= n || m <= 0) return;
+  extern __shared__ int sh_base[];
+  const int *seg = s.seg + (int64_t)h * s.seg_hs;
+  const int *th = s.tile_hist + ((int64_t)h * s.max_tiles + tile) * s.mcap;
+  for (int c = threadIdx.x; c < m; c += 64) sh_base[c] = seg[c] + th[c];
+  __syncthreads();
+  const int *lab = s.labels + (int64_t)h * s.lab_hs;
+  int *perm = s.perm + (int64_t)h * s.perm_hs;
+  const int end = min(n, beg + SORT_TILE);
+  const int lane = threadIdx.x;
+  for (int i0 = beg; i0 < end; i0 += 64) {
+    const int i = i0 + lane;
+    const bool valid = i < end;
+    const int lb = valid ? lab[i] : -1;
+    uint64_t remaining = __ballot(valid);
+    int pos = 0;
+    while (remaining) {
+      const int leader = __ffsll((long long)remaining) - 1;
+      const int ll = __shfl(lb, leader, 64);
+      const uint64_t same = __ballot(lb == ll) & remaining;
+      const int basev = sh_base[ll];
+      if (lb == ll && valid) {
+        uint64_t lt = lane == 0 ? 0ull : (same & ((1ull << lane) - 1ull));
+        pos = basev + __popcll(lt);
+      }
+      __syncthreads();  // single-wave block: orders the LDS read before the update
+      if (lane == leader) sh_base[ll] = basev + __popcll(same);
+      __syncthreads();
+      remaining &= ~same;
+    }
+    if (valid) perm[pos] = i;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Lloyd update: each centre becomes the fp64 mean of its members (read in
+// counting-sort order); an empty cluster keeps its centre.  The new centre's
+// GEMM operands are written in the same pass.  One block per (centre, head).
+template <int D>
+__global__ __launch_bounds__(256) void k_update(KmArgs a, SortArgs s, CentOps op) {
+  const int h = blockIdx.y, c = blockIdx.x;
+  if (c >= a.m[h] || a.n[h] <= 0) return;
+  const int *seg = s.seg + (int64_t)h * s.seg_hs;
+  const int *perm = s.perm + (int64_t)h * s.perm_hs;
+  const int beg = seg[c], end = seg[c + 1];
+  const uint16_t *X = a.X + (int64_t)h * a.x_hs;
+  const int *idx = a.idx ? a.idx + (int64_t)h * a.idx_hs : nullptr;
+  float *cr = a.cent + (int64_t)h * a.cent_hs + (int64_t)(a.coff[h] + c) * D;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int PL = D / 64;  // dims per lane (1 or 2)
+  __shared__ double sh[4][D];
+  __shared__ float newc[D];
+  double acc[PL];
+#pragma unroll
+  for (int k = 0; k < PL; ++k) acc[k] = 0.0;
+  for (int p = beg + wave; p < end; p += 4) {
+    int li = perm[p];
+    int64_t row = idx ? (int64_t)idx[li] : (int64_t)li;
+    const uint16_t *xr = X + row * D + lane * PL;
+    if (PL == 2) {
+      uint32_t w = *(const uint32_t *)xr;
+      acc[0] += (double)bf2f((uint16_t)(w & 0xFFFF));
+      acc[PL - 1] += (double)bf2f((uint16_t)(w >> 16));
+    } else {
+      acc[0] += (double)bf2f(xr[0]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PL; ++k) sh[wave][lane * PL + k] = acc[k];
+  __syncthreads();
+  const int cnt = end - beg;
+  if (threadIdx.x < D) {
+    const int dd = threadIdx.x;
+    float v;
+    if (cnt > 0) {
+      double sum = ((sh[0][dd] + sh[1][dd]) + sh[2][dd]) + sh[3][dd];
+      v = (float)(sum / (double)cnt);
+      cr[dd] = v;
+    } else {
+      v = cr[dd];
+    }
+    newc[dd] = v;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint16_t *hi = op.hi + ((int64_t)h * op.cap + c) * D;
+    uint16_t *lo = op.lo + ((int64_t)h * op.cap + c) * D;
+    double ss = 0.0;
+    for (int dd = lane; dd < D; dd += 64) {
+      float v = newc[dd];
+      uint16_t bh = f2bf(v);
+      hi[dd] = bh;
+      lo[dd] = f2bf(v - bf2f(bh));
+      ss += (double)v * (double)v;
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) op.norm[(int64_t)h * op.cap + c] = (float)ss;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Distance of each point of a stage to its own centre, ||x - c(x)|| (fp64
+// accumulation, stored fp32).  One wave per point.
+template <int D>
+__global__ __launch_bounds__(256) void k_stage_dist(KmArgs a, const int *__restrict__ labels, int64_t lab_hs,
+                                                    float *__restrict__ dist, int64_t dist_hs) {
+  const int h = blockIdx.y;
+  const int n = a.n[h];
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= n || a.m[h] <= 0) return;
+  const uint16_t *X = a.X + (int64_t)h * a.x_hs;
+  const int *idx = a.idx ? a.idx + (int64_t)h * a.idx_hs : nullptr;
+  int64_t row = idx ? (int64_t)idx[i] : (int64_t)i;
+  const int c = labels[(int64_t)h * lab_hs + i];
+  const float *cr = a.cent + (int64_t)h * a.cent_hs + (int64_t)(a.coff[h] + c) * D;
+  double acc = 0.0;
+  for (int dd = lane; dd < D; dd += 64) {
+    double df = (double)bf2f(X[row * D + dd]) - (double)cr[dd];
+    acc += df * df;
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) dist[(int64_t)h * dist_hs + i] = (float)sqrt(acc);
+}
+
+// ---------------------------------------------------------------------------
+// tau of the first stage.  MEAN_X / ABS / INF directly; PCTL by a radix
+// select over the fp32 bit patterns (non-negative values order as integers).
+__global__ __launch_bounds__(1024) void k_tau_direct(const float *__restrict__ dist, int64_t dist_hs,
+                                                     const int *__restrict__ n_arr, int rule, float param,
+                                                     float *__restrict__ tau) {
+  const int h = blockIdx.x;
+  const int n = n_arr[h];
+  if (rule == TAU_RULE_ABS) { if (threadIdx.x == 0) tau[h] = param; return; }
+  if (rule == TAU_RULE_INF) { if (threadIdx.x == 0) tau[h] = __builtin_inff(); return; }
+  // MEAN_X: fixed-order fp64 sum
+  __shared__ double part[1024];
+  double loc = 0.0;
+  const float *d = dist + (int64_t)h * dist_hs;
+  for (int i = threadIdx.x; i < n; i += 1024) loc += (double)d[i];
+  part[threadIdx.x] = loc;
+  __syncthreads();
+  for (int off = 512; off > 0; off >>= 1) {
+    if (threadIdx.x < off) part[threadIdx.x] += part[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) tau[h] = n > 0 ? (float)((double)param * (part[0] / (double)n)) : 0.f;
+}
+
+// radix-select state per head: {prefix bits, remaining rank (1-based)}
+__global__ __launch_bounds__(256) void k_radix_init(const int *__restrict__ n_arr, float param,
+                                                    uint32_t *__restrict__ state, uint32_t *__restrict__ ghist) {
+  const int h = blockIdx.x;
+  for (int b = threadIdx.x; b < 256; b += 256) ghist[h * 256 + b] = 0;
+  if (threadIdx.x == 0) {
+    int n = n_arr[h];
+    double r = ceil((double)param * (double)n);
+    int rk = (int)r;
+    rk = rk < 1 ? 1 : (rk > n ? n : rk);
+    state[h * 2 + 0] = 0;
+    state[h * 2 + 1] = (uint32_t)rk;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_radix_hist(const float *__restrict__ dist, int64_t dist_hs,
+                                                    const int *__restrict__ n_arr, const uint32_t *__restrict__ state,
+                                                    uint32_t *__restrict__ ghist, int shift) {
+  const int h = blockIdx.y;
+  const int n = n_arr[h];
+  __shared__ uint32_t hs[256];
+  hs[threadIdx.x] = 0;
+  __syncthreads();
+  const uint32_t prefix = state[h * 2];
+  const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+  const float *d = dist + (int64_t)h * dist_hs;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+    uint32_t b = __float_as_uint(d[i]);
+    if ((b & hmask) == prefix) atomicAdd(&hs[(b >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  if (hs[threadIdx.x]) atomicAdd(&ghist[h * 256 + threadIdx.x], hs[threadIdx.x]);
+}
+
+__global__ __launch_bounds__(64) void k_radix_pick(uint32_t *__restrict__ state, uint32_t *__restrict__ ghist,
+                                                   int shift, float *__restrict__ tau) {
+  const int h = blockIdx.x;
+  if (threadIdx.x == 0) {
+    uint32_t rk = state[h * 2 + 1];
+    uint32_t run = 0;
+    int bin = 255;
+    for (int b = 0; b < 256; ++b) {
+      uint32_t v = ghist[h * 256 + b];
+      if (run + v >= rk) { bin = b; break; }
+      run += v;
+    }
+    state[h * 2 + 0] |= ((uint32_t)bin << shift);
+    state[h * 2 + 1] = rk - run;
+    if (shift == 0) tau[h] = __uint_as_float(state[h * 2 + 0]);
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < 256; b += 64) ghist[h * 256 + b] = 0;
+}
+
+// keep flag for compaction: label 0 = stays in U (d >= tau), 1 = removed.
+__global__ __launch_bounds__(256) void k_flag_removed(const float *__restrict__ dist, int64_t dist_hs,
+                                                      const int *__restrict__ n_arr, const float *__restrict__ tau,
+                                                      int *__restrict__ flag, int64_t flag_hs) {
+  const int h = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_arr[h]) return;
+  flag[(int64_t)h * flag_hs + i] = dist[(int64_t)h * dist_hs + i] < tau[h] ? 1 : 0;
+}
+
+// new U list = old U entries that stayed, in order: out[p] = idx[perm[p]]
+// for p < seg[1]; also the new size.
+__global__ __launch_bounds__(256) void k_compact_gather(const int *__restrict__ idx_old, int64_t idx_hs,
+                                                        const int *__restrict__ perm, int64_t perm_hs,
+                                                        const int *__restrict__ seg, int64_t seg_hs,
+                                                        int *__restrict__ idx_new, int *__restrict__ n_new) {
+  const int h = blockIdx.y;
+  const int keep = seg[(int64_t)h * seg_hs + 1];
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (blockIdx.x == 0 && threadIdx.x == 0) n_new[h] = keep;
+  if (p >= keep) return;
+  int li = perm[(int64_t)h * perm_hs + p];
+  idx_new[(int64_t)h * idx_hs + p] = idx_old ? idx_old[(int64_t)h * idx_hs + li] : li;
+}
+
+// ---------------------------------------------------------------------------
+// Statistics of the final key clusters, one block per (cluster, head):
+// count, fp64 means of K and V, per-dimension max / min of K (exact bf16),
+// and the cluster's share of sum ||k - c(k)||^2 (fp64).
+template <int D>
+__global__ __launch_bounds__(256) void k_kstats(KStatsArgs s) {
+  const int h = blockIdx.y, c = blockIdx.x;
+  const int ncl = s.ncl[h];
+  const int64_t cb = ((int64_t)h * s.ncap + c);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (c >= ncl) {
+    if (c < s.ncap) {
+      for (int dd = threadIdx.x; dd < D; dd += 256) {
+        s.kmax[cb * D + dd] = 0; s.kmin[cb * D + dd] = 0;
+        s.kmean[cb * D + dd] = 0.f; s.vmean[cb * D + dd] = 0.f;
+      }
+      if (threadIdx.x == 0) s.msepart[cb] = 0.0;
+    }
+    return;
+  }
+  const int *seg = s.seg + (int64_t)h * (s.ncap + 1);
+  const int *perm = s.perm + (int64_t)h * s.L;
+  const int beg = seg[c], end = seg[c + 1];
+  const uint16_t *K = s.K + (int64_t)h * s.L * D;
+  const uint16_t *V = s.V + (int64_t)h * s.L * D;
+  const float *cent = s.cent + cb * D;
+  constexpr int PL = D / 64;
+  double sk[PL], sv[PL], se = 0.0;
+  float mx[PL], mn[PL], cc[PL];
+#pragma unroll
+  for (int k = 0; k < PL; ++k) {
+    sk[k] = 0.0; sv[k] = 0.0; mx[k] = -__builtin_inff(); mn[k] = __builtin_inff();
+    cc[k] = cent[lane * PL + k];
+  }
+  for (int p = beg + wave; p < end; p += 4) {
+    int64_t row = perm[p];
+    const uint16_t *kr = K + row * D + lane * PL;
+    const uint16_t *vr = V + row * D + lane * PL;
+#pragma unroll
+    for (int k = 0; k < PL; ++k) {
+      float kv = bf2f(kr[k]), vv = bf2f(vr[k]);
+      sk[k] += (double)kv;
+      sv[k] += (double)vv;
+      mx[k] = fmaxf(mx[k], kv);
+      mn[k] = fminf(mn[k], kv);
+      double df = (double)kv - (double)cc[k];
+      se += df * df;
+    }
+  }
+  __shared__ double shk[4][D], shv[4][D];
+  __shared__ float shx[4][D], shn[4][D];
+  __shared__ double she[4];
+#pragma unroll
+  for (int k = 0; k < PL; ++k) {
+    shk[wave][lane * PL + k] = sk[k];
+    shv[wave][lane * PL + k] = sv[k];
+    shx[wave][lane * PL + k] = mx[k];
+    shn[wave][lane * PL + k] = mn[k];
+  }
+  se = wave_sum(se);
+  if (lane == 0) she[wave] = se;
+  __syncthreads();
+  const int cnt = end - beg;
+  if (threadIdx.x < D) {
+    const int dd = threadIdx.x;
+    if (cnt > 0) {
+      double a = ((shk[0][dd] + shk[1][dd]) + shk[2][dd]) + shk[3][dd];
+      double b = ((shv[0][dd] + shv[1][dd]) + shv[2][dd]) + shv[3][dd];
+      s.kmean[cb * D + dd] = (float)(a / cnt);
+      s.vmean[cb * D + dd] = (float)(b / cnt);
+      float x = fmaxf(fmaxf(shx[0][dd], shx[1][dd]), fmaxf(shx[2][dd], shx[3][dd]));
+      float y = fminf(fminf(shn[0][dd], shn[1][dd]), fminf(shn[2][dd], shn[3][dd]));
+      s.kmax[cb * D + dd] = (uint16_t)(__float_as_uint(x) >> 16);
+      s.kmin[cb * D + dd] = (uint16_t)(__float_as_uint(y) >> 16);
+    } else {
+      s.kmean[cb * D + dd] = 0.f; s.vmean[cb * D + dd] = 0.f;
+      s.kmax[cb * D + dd] = 0; s.kmin[cb * D + dd] = 0;
+    }
+  }
+  if (threadIdx.x == 0) s.msepart[cb] = ((she[0] + she[1]) + she[2]) + she[3];
+}
+
+__global__ __launch_bounds__(256) void k_mse_reduce(const double *__restrict__ msepart, int ncap,
+                                                    const int *__restrict__ ncl, int L, float *__restrict__ mse) {
+  const int h = blockIdx.x;
+  __shared__ double part[256];
+  double loc = 0.0;
+  for (int c = threadIdx.x; c < ncl[h]; c += 256) loc += msepart[(int64_t)h * ncap + c];
+  part[threadIdx.x] = loc;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) part[threadIdx.x] += part[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) mse[h] = (float)(part[0] / (double)L);
+}
+
+// mean of a per-token scalar over each cluster's members (rho of the query
+// clusters: mean ||q||), fp64 sum in counting-sort order.
+__global__ __launch_bounds__(256) void k_seg_mean(const float *__restrict__ val, const int *__restrict__ perm,
+                                                  const int *__restrict__ seg, int L, int ncap,
+                                                  const int *__restrict__ ncl, float *__restrict__ out) {
+  const int h = blockIdx.y, c = blockIdx.x;
+  if (c >= ncap) return;
+  const int *sg = seg + (int64_t)h * (ncap + 1);
+  const int beg = c < ncl[h] ? sg[c] : 0, end = c < ncl[h] ? sg[c + 1] : 0;
+  __shared__ double part[256];
+  double loc = 0.0;
+  for (int p = beg + threadIdx.x; p < end; p += 256) loc += (double)val[(int64_t)h * L + perm[(int64_t)h * L + p]];
+  part[threadIdx.x] = loc;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) part[threadIdx.x] += part[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[(int64_t)h * ncap + c] = end > beg ? (float)(part[0] / (double)(end - beg)) : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// small per-head bookkeeping kernels
+__global__ void k_fill_i32(int *__restrict__ p, int64_t n, int v) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+__global__ void k_copy_i32(const int *__restrict__ src, int *__restrict__ dst, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+__global__ void k_copy_f32(const float *__restrict__ src, float *__restrict__ dst, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+__global__ void k_copy_u8(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+__global__ void k_fill_u8(uint8_t *__restrict__ p, int64_t n, uint8_t v) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+// m[h] = min(v, n[h]) clipped below at 0
+__global__ void k_set_m_min(int *__restrict__ m, const int *__restrict__ n, int v, int BH) {
+  int h = blockIdx.x * 256 + threadIdx.x;
+  if (h < BH) m[h] = max(0, min(v, n[h]));
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+static inline dim3 g2(int64_t x, int y) { return dim3((unsigned)(x > 0 ? x : 1), (unsigned)y); }
+
+#define AC_D_DISPATCH(D, ...)            \
+  do {                                   \
+    if ((D) == 64) { constexpr int DD = 64; __VA_ARGS__; } \
+    else { constexpr int DD = 128; __VA_ARGS__; }           \
+  } while (0)
+
+void launch_qnorm(int D, const uint16_t *Q, uint16_t *Qh, float *qn, int64_t rows, hipStream_t st) {
+  int64_t blocks = (rows * 8 + 255) / 256;
+  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_qnorm<DD>, dim3((unsigned)blocks), dim3(256), 0, st, Q, Qh, qn, rows));
+}
+
+void launch_kpp_init(int D, const KmArgs &a, int BH, double *d2buf, int init_sample, uint64_t seed, int role,
+                     int stage, hipStream_t st) {
+  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_kpp_init<DD>, dim3(1, BH), dim3(1024), 0, st, a, d2buf, init_sample, seed,
+                                      role, stage));
+}
+
+void launch_cent_prep(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, hipStream_t st) {
+  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_cent_prep<DD>, g2((mmax + 3) / 4, BH), dim3(256), 0, st, a, op));
+}
+
+void launch_assign(int D, const KmArgs &a, const CentOps &op, int BH, int nmax_pts, int *labels, int64_t lab_hs,
+                   hipStream_t st) {
+  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_assign<DD>, g2((nmax_pts + 255) / 256, BH), dim3(256), 0, st, a, op, labels,
+                                      lab_hs));
+}
+
+void launch_sort(const SortArgs &s, int BH, int nmax_pts, hipStream_t st) {
+  int tiles = (nmax_pts + SORT_TILE - 1) / SORT_TILE;
+  size_t sh = (size_t)s.mcap * sizeof(int);
+  hipLaunchKernelGGL(k_sort_hist, g2(tiles, BH), dim3(64), sh, st, s);
+  hipLaunchKernelGGL(k_sort_scan, dim3(BH), dim3(1024), 0, st, s);
+  hipLaunchKernelGGL(k_sort_scatter, g2(tiles, BH), dim3(64), sh, st, s);
+}
+
+void launch_update(int D, const KmArgs &a, const SortArgs &s, const CentOps &op, int BH, int mmax, hipStream_t st) {
+  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_update<DD>, g2(mmax, BH), dim3(256), 0, st, a, s, op));
+}
+
+void launch_stage_dist(int D, const KmArgs &a, int BH, int nmax_pts, const int *labels, int64_t lab_hs, float *dist,
+                       int64_t dist_hs, hipStream_t st) {
+  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_stage_dist<DD>, g2((nmax_pts + 3) / 4, BH), dim3(256), 0, st, a, labels,
+                                      lab_hs, dist, dist_hs));
+}
+
+void launch_tau(const float *dist, int64_t dist_hs, const int *n_arr, int BH, int nmax_pts, int rule, float param,
+                float *tau, uint32_t *radix_state, uint32_t *radix_hist, hipStream_t st) {
+  if (rule != TAU_RULE_PCTL) {
+    hipLaunchKernelGGL(k_tau_direct, dim3(BH), dim3(1024), 0, st, dist, dist_hs, n_arr, rule, param, tau);
+    return;
+  }
+  hipLaunchKernelGGL(k_radix_init, dim3(BH), dim3(256), 0, st, n_arr, param, radix_state, radix_hist);
+  int blocks = (nmax_pts + 4095) / 4096;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hipLaunchKernelGGL(k_radix_hist, g2(blocks, BH), dim3(256), 0, st, dist, dist_hs, n_arr, radix_state, radix_hist,
+                       shift);
+    hipLaunchKernelGGL(k_radix_pick, dim3(BH), dim3(64), 0, st, radix_state, radix_hist, shift, tau);
+  }
+}
+
+void launch_flag_removed(const float *dist, int64_t dist_hs, const int *n_arr, const float *tau, int *flag,
+                         int64_t flag_hs, int BH, int nmax_pts, hipStream_t st) {
+  hipLaunchKernelGGL(k_flag_removed, g2((nmax_pts + 255) / 256, BH), dim3(256), 0, st, dist, dist_hs, n_arr, tau,
+                     flag, flag_hs);
+}
+
+void launch_compact_gather(const int *idx_old, int64_t idx_hs, const int *perm, int64_t perm_hs, const int *seg,
+                           int64_t seg_hs, int *idx_new, int *n_new, int BH, int nmax_pts, hipStream_t st) {
+  hipLaunchKernelGGL(k_compact_gather, g2((nmax_pts + 255) / 256, BH), dim3(256), 0, st, idx_old, idx_hs, perm,
+                     perm_hs, seg, seg_hs, idx_new, n_new);
+}
+
+void launch_kstats(int D, const KStatsArgs &s, int BH, hipStream_t st) {
+  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_kstats<DD>, g2(s.ncap, BH), dim3(256), 0, st, s));
+  hipLaunchKernelGGL(k_mse_reduce, dim3(BH), dim3(256), 0, st, s.msepart, s.ncap, s.ncl, s.L, s.mse);
+}
+
+void launch_seg_mean(const float *val, const int *perm, const int *seg, int L, int ncap, const int *ncl, float *out,
+                     int BH, hipStream_t st) {
+  hipLaunchKernelGGL(k_seg_mean, g2(ncap, BH), dim3(256), 0, st, val, perm, seg, L, ncap, ncl, out);
+}
+
+void launch_fill_i32(int *p, int64_t n, int v, hipStream_t st) {
+  if (n > 0) hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n, v);
+}
+void launch_fill_u8(uint8_t *p, int64_t n, uint8_t v, hipStream_t st) {
+  if (n > 0) hipLaunchKernelGGL(k_fill_u8, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n, v);
+}
+void launch_copy_i32(const int *s, int *d, int64_t n, hipStream_t st) {
+  if (n > 0) hipLaunchKernelGGL(k_copy_i32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, s, d, n);
+}
+void launch_copy_f32(const float *s, float *d, int64_t n, hipStream_t st) {
+  if (n > 0) hipLaunchKernelGGL(k_copy_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, s, d, n);
+}
+void launch_copy_u8(const uint8_t *s, uint8_t *d, int64_t n, hipStream_t st) {
+  if (n > 0) hipLaunchKernelGGL(k_copy_u8, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, s, d, n);
+}
+void launch_set_m_min(int *m, const int *n, int v, int BH, hipStream_t st) {
+  hipLaunchKernelGGL(k_set_m_min, dim3((BH + 255) / 256), dim3(256), 0, st, m, n, v, BH);
+}
+
+}  // namespace ac

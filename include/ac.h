@@ -1,0 +1,226 @@
+/*
+ * ac.h - C ABI of the cluster-routed sparse attention layer for MI355X (gfx950).
+ *
+ * One attention layer of a video diffusion transformer, made sparse the way
+ * AdaCluster (arXiv 2604.18348, "AdaCluster: Adaptive Query-Key Clustering for
+ * Sparse Attention in Video Generation") describes it, with the optional
+ * stripe-mean compensation of ClusterAttention (arXiv 2608.26965, §1.2):
+ *
+ *   ac_cluster_q     angular k-means on L2-normalised queries   (AdaCluster §3.1, Algorithm 3 "KMeans(Normalize(Q))")
+ *   ac_cluster_k     multi-stage key k-means with dense fallback (AdaCluster §3.2.2, Algorithm 1) + per-cluster statistics
+ *   ac_score_select  Quest bound per (query cluster, key cluster) and top-K / density / top-p selection
+ *                    (AdaCluster §3.2.3 eq. (1), Algorithm 2, Algorithm 3 "argtopk")
+ *   ac_sparse_attn   attention of each query over the keys of its cluster's selected key clusters, with
+ *                    optional centroid compensation, or dense attention for fallback heads
+ *                    (AdaCluster Algorithm 3; ClusterAttention §1.2 eqs. (2), (5))
+ *   ac_layer         the whole layer, cold (first denoising step) or warm (later steps reuse the cluster
+ *                    counts and centres: AdaCluster §3.2.2 "Efficient initialization")
+ *
+ * Conventions (all entry points)
+ * ------------------------------
+ * Layout    Q, K, V, O are contiguous row-major [B, H, L, d] bfloat16, passed as uint16_t bit patterns.
+ *           "BH" below is B*H; every per-head array is indexed by the flattened head b*H + h.
+ *           d must be 64 or 128 (AC_E_UNSUPPORTED otherwise).  Self-attention: queries and keys share L.
+ * Pointers  Every array pointer is a DEVICE pointer owned by the caller, except the arrays inside
+ *           ac_layer_stats, which are HOST pointers.  The library never allocates caller-visible
+ *           memory, never frees, and keeps no pointer after a call returns.  Scratch memory is the
+ *           caller's workspace `ws` of `ws_bytes` bytes (device memory, 256-byte aligned), sized by
+ *           ac_sizes(); its contents are undefined between calls.
+ * Streams   Every call enqueues its work on `stream` (a hipStream_t) and returns without waiting,
+ *           except: a cold ac_cluster_k / cold ac_layer waits on the stream once per stage of
+ *           Algorithm 1 (it reads the size of the unassigned set), and ac_layer waits at its end when
+ *           host_stats is not NULL.  Calls on different streams with different buffers are independent.
+ * Errors    Every entry point returns an ac_status.  Argument errors (NULL pointers, bad shapes or
+ *           parameters, a workspace that is too small) are detected before any device work is
+ *           enqueued, so outputs are untouched.  AC_E_DEVICE reports a HIP runtime error; the text of
+ *           the last error on the calling thread is returned by ac_last_error().  The dense fallback of
+ *           a head (Algorithm 1's flag F) is a result, not an error.  No C++ exception crosses the ABI.
+ * Precision Inputs bf16; k-means distances on bf16 MFMA with fp32 accumulation (centres split into a
+ *           bf16 high and low part); statistics accumulate in fp64; attention on bf16 MFMA with fp32
+ *           accumulation and an fp32 online softmax; O is rounded to bf16.
+ */
+#ifndef AC_H_
+#define AC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *ac_stream_t; /* a hipStream_t; NULL = the default stream */
+
+typedef enum ac_status {
+  AC_OK = 0,
+  AC_E_ARG = 1,         /* NULL pointer or invalid parameter value */
+  AC_E_SHAPE = 2,       /* invalid B, H, L or d */
+  AC_E_WORKSPACE = 3,   /* ws_bytes smaller than ac_sizes() asks for */
+  AC_E_UNSUPPORTED = 4, /* valid but not supported by these kernels (e.g. d not in {64, 128}) */
+  AC_E_DEVICE = 5       /* HIP runtime error (no device, launch failure, ...) */
+} ac_status;
+
+/* Rule for the distance threshold tau of Algorithm 1, taken per head from the stage-0 distances
+ * ||k_i - c(k_i)|| (AdaCluster §4.1: 1.5x the mean token-to-centre distance of the first step). */
+enum { AC_TAU_MEAN_X = 0, /* tau = tau_param * mean distance */
+       AC_TAU_PCTL = 1,   /* tau = nearest-rank percentile: the ceil(tau_param * n)-th smallest distance */
+       AC_TAU_ABS = 2,    /* tau = tau_param */
+       AC_TAU_INF = 3 };  /* tau = +inf: a single stage */
+
+/* Cluster score (AdaCluster §3.2.3 eq. (1); MEAN is the "w/o Quest" ablation of §4.4). */
+enum { AC_SCORE_QUEST = 0, AC_SCORE_MEAN = 1 };
+
+/* Key-cluster selection per query cluster, in order of score (desc), ties by cluster index (asc).
+ * Empty clusters are never selected; at least one cluster always is. */
+enum { AC_SEL_TOPK = 0,    /* the first min(topk, non-empty) clusters (Algorithm 3 argtopk) */
+       AC_SEL_DENSITY = 1, /* clusters until their summed sizes reach ceil(sel_param * L) keys */
+       AC_SEL_TOPP = 2,    /* shortest prefix whose softmax mass reaches sel_param, with
+                              pi_c = softmax_c(rho_r * S_rc * scale + ln n_c) */
+       AC_SEL_DENSE = 3 }; /* every head dense (the dense baseline) */
+
+typedef struct ac_shape {
+  int32_t B, H, L, d;
+} ac_shape;
+
+typedef struct ac_params {
+  int32_t nq;          /* query clusters (65); min(nq, L) are used */
+  int32_t iters;       /* Lloyd iterations of a cold k-means (10) */
+  int32_t iters_warm;  /* Lloyd iterations of a warm step (3) */
+  int32_t m0;          /* key clusters per stage of Algorithm 1 (200); each stage uses min(|U|, m0) */
+  int32_t nmax;        /* N_max: a head falls back to dense attention when a stage would start with
+                          at least nmax centres and keys are left (1500) */
+  int32_t tau_rule;    /* AC_TAU_* (AC_TAU_MEAN_X) */
+  float tau_param;     /* 1.5 */
+  int32_t score_mode;  /* AC_SCORE_* (AC_SCORE_QUEST) */
+  int32_t sel_mode;    /* AC_SEL_* (AC_SEL_DENSITY) */
+  int32_t topk;        /* K of AC_SEL_TOPK (8) */
+  float sel_param;     /* density of AC_SEL_DENSITY or p of AC_SEL_TOPP (0.15) */
+  int32_t compensate;  /* 1: add every non-empty excluded key cluster as one pseudo-key (key mean,
+                          value mean, logit bias ln n_c): ClusterAttention §1.2 eq. (5) (0) */
+  float scale;         /* softmax scale; 0 means 1/sqrt(d) (0) */
+  int32_t init_sample; /* k-means++ runs on a strided subsample of min(n, init_sample * m) points;
+                          0 = every point (32).  The subsample may hold at most 16384 points. */
+  uint64_t seed;       /* seed of the counter-based SplitMix64 stream of k-means++ (0) */
+} ac_params;
+
+/* Clusters of one side (queries or keys), per head.  All pointers are device pointers. */
+typedef struct ac_clusters {
+  int32_t ncap;    /* capacity of the per-cluster arrays per head: nq for queries,
+                      nmax - 1 + m0 for keys (ac_sizes returns it) */
+  int32_t *labels; /* [BH, L]      cluster of each token (original token order) */
+  int32_t *perm;   /* [BH, L]      perm[p] = original index of the p-th token in cluster order (stable) */
+  int32_t *seg;    /* [BH, ncap+1] first position of each cluster in perm; seg[ncl] = L, and
+                      seg[c] = L for ncl <= c <= ncap */
+  float *cent;     /* [BH, ncap, d] centres (fp32) after the last Lloyd update */
+  int32_t *ncl;    /* [BH]         clusters in use */
+  float *rho;      /* [BH, ncap]   queries: mean ||q|| of each cluster's members (0 if empty);
+                      may be NULL for keys */
+} ac_clusters;
+
+/* Statistics of the final key clusters (device pointers). */
+typedef struct ac_kstats {
+  uint16_t *kmax;    /* [BH, ncap, d] bf16 per-dimension max of member keys (Quest's max(K^d)) */
+  uint16_t *kmin;    /* [BH, ncap, d] bf16 per-dimension min */
+  float *kmean;      /* [BH, ncap, d] mean member key   (ClusterAttention's key centroid) */
+  float *vmean;      /* [BH, ncap, d] mean member value (its value centroid) */
+  uint8_t *fallback; /* [BH] Algorithm 1's F: 1 = the head runs dense attention */
+  float *tau;        /* [BH] distance threshold of the head */
+  float *mse;        /* [BH] (1/L) sum_i ||k_i - c(k_i)||^2 (AdaCluster §3.2.1); compactness = 1/mse */
+  int32_t *stages;   /* [BH] stages Algorithm 1 ran (0 on a warm step) */
+} ac_kstats;
+
+/* Selected key clusters per (head, query cluster) (device pointers). */
+typedef struct ac_selection {
+  int32_t ncap_k;  /* capacity of the key-cluster axis (= the key ac_clusters.ncap) */
+  int32_t *list;   /* [BH, nq, ncap_k] selected cluster ids in selection order; the rest undefined */
+  int32_t *n;      /* [BH, nq] number selected */
+  uint32_t *mask;  /* [BH, nq, ceil(ncap_k/32)] bit c set iff cluster c is selected */
+  float *score;    /* [BH, nq, ncap_k] scores (-inf for empty / unused clusters); may be NULL */
+} ac_selection;
+
+/* State carried from one denoising step to the next (device pointers, caller-owned).
+ * A cold ac_layer fills it and sets valid = 1; a call with valid = 1 runs warm. */
+typedef struct ac_state {
+  float *cent_q;     /* [BH, nq, d] */
+  float *cent_k;     /* [BH, ncap_k, d] */
+  int32_t *ncl_k;    /* [BH] */
+  uint8_t *fallback; /* [BH] */
+  float *tau;        /* [BH] */
+  int32_t valid;
+} ac_state;
+
+/* Optional per-head summary of ac_layer (HOST pointers, each [BH]; any may be NULL). */
+typedef struct ac_layer_stats {
+  int32_t *ncl_k;
+  uint8_t *fallback;
+  float *tau;
+  float *mse;
+  int32_t *stages;
+  int64_t *pairs; /* query-key pairs attended (dense heads: L*L), compensation pseudo-keys excluded */
+} ac_layer_stats;
+
+/* Fill *p with the defaults listed in ac_params.  Returns AC_E_ARG if p is NULL. */
+ac_status ac_params_default(ac_params *p);
+
+/* Validate shape and parameters and size the workspace.  *ncap_k receives the key-cluster
+ * capacity (nmax - 1 + m0, at most L) and *ws_bytes the workspace that every entry point accepts
+ * for this shape and these parameters.  Host-only: touches no device. */
+ac_status ac_sizes(const ac_shape *s, const ac_params *p, int32_t *ncap_k, size_t *ws_bytes);
+
+/* AdaCluster Algorithm 3, "A_q, C_q <- KMeans(Normalize(Q))" (§3.1): each query is divided by its
+ * L2 norm and rounded to bf16, then clustered by Euclidean k-means into min(nq, L) clusters
+ * (k-means++ seeding and p->iters Lloyd iterations, or p->iters_warm iterations from warm_cent when
+ * warm_cent is not NULL), then finally assigned.  Fills q_out (ncap must be >= min(nq, L); rho is
+ * required).  Q: [B,H,L,d] bf16; warm_cent: NULL or [BH, q_out->ncap, d] fp32. */
+ac_status ac_cluster_q(const ac_shape *s, const ac_params *p, const uint16_t *Q, const float *warm_cent,
+                       ac_clusters *q_out, void *ws, size_t ws_bytes, ac_stream_t stream);
+
+/* AdaCluster Algorithm 1 (MultiStageClustering, §3.2.2) on each head's keys, then the statistics
+ * of the final clusters.  Cold (warm == NULL): stages of k-means with min(|U|, m0) clusters; keys
+ * closer than tau to their stage centre leave U; a head whose centre count reaches nmax with keys
+ * left falls back (F = 1); finally every key goes to its nearest centre over all stages.  Warm
+ * (warm != NULL and warm->valid): p->iters_warm Lloyd iterations over all keys from warm->cent_k with
+ * warm->ncl_k centres; F and tau are copied from warm.  V only feeds vmean.  k_out->ncap must be
+ * ac_sizes' ncap_k; k_out->rho may be NULL. */
+ac_status ac_cluster_k(const ac_shape *s, const ac_params *p, const uint16_t *K, const uint16_t *V,
+                       const ac_state *warm, ac_clusters *k_out, ac_kstats *stats, void *ws,
+                       size_t ws_bytes, ac_stream_t stream);
+
+/* Scores of every (query cluster r, key cluster c) pair and the selection of key clusters for
+ * each query cluster.  QUEST: S_rc = sum_d max(cq_r[d] kmax_c[d], cq_r[d] kmin_c[d]) (AdaCluster
+ * eq. (1)), evaluated as the single product [cq+, cq-] . [kmax; kmin] on MFMA (the exact form of
+ * eq. (2) with per-cluster max/min vectors); MEAN: S_rc = cq_r . kmean_c.  cq_r is the query
+ * cluster centre.  Empty clusters score -inf.  Selection per p->sel_mode (see AC_SEL_*). */
+ac_status ac_score_select(const ac_shape *s, const ac_params *p, const ac_clusters *q,
+                          const ac_clusters *k, const ac_kstats *stats, ac_selection *sel, void *ws,
+                          size_t ws_bytes, ac_stream_t stream);
+
+/* AdaCluster Algorithm 3 lines "K* <- K[Index], V* <- V[Index], Attention(Q, K*, V*)": every query
+ * of query cluster r attends, with scale p->scale (0: 1/sqrt(d)), to the keys of the key clusters
+ * selected for r, softmax-normalised over that set (ClusterAttention §1.2 eq. (2)).  With
+ * p->compensate every non-empty excluded cluster enters as one pseudo-key (kmean_c, vmean_c, logit
+ * bias ln n_c; ClusterAttention eq. (5)).  Heads with fallback = 1, or every head when p->sel_mode is
+ * AC_SEL_DENSE, attend densely to all L keys.  Rows are gathered through q->perm and k->perm inside
+ * the kernel; O [B,H,L,d] bf16 is written in original token order; lse [BH, L] (natural log of the
+ * softmax denominator of the scaled logits) may be NULL. */
+ac_status ac_sparse_attn(const ac_shape *s, const ac_params *p, const uint16_t *Q, const uint16_t *K,
+                         const uint16_t *V, const ac_clusters *q, const ac_clusters *k,
+                         const ac_kstats *stats, const ac_selection *sel, uint16_t *O, float *lse,
+                         void *ws, size_t ws_bytes, ac_stream_t stream);
+
+/* The whole layer (AdaCluster Algorithm 3 with the optional compensation): ac_cluster_q,
+ * ac_cluster_k, ac_score_select and ac_sparse_attn on buffers carved from the workspace.  Cold when
+ * !state->valid (fills the state and sets valid = 1), warm otherwise.  host_stats may be NULL. */
+ac_status ac_layer(const ac_shape *s, const ac_params *p, const uint16_t *Q, const uint16_t *K,
+                   const uint16_t *V, ac_state *state, uint16_t *O, ac_layer_stats *host_stats,
+                   void *ws, size_t ws_bytes, ac_stream_t stream);
+
+/* Static description of a status code. */
+const char *ac_status_str(ac_status st);
+/* Text of the last error reported on the calling thread ("" if none). */
+const char *ac_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AC_H_ */

@@ -1,0 +1,130 @@
+"""The C-ABI library loads, exports every symbol include/ac.h declares, and
+rejects bad arguments before touching any device.  CPU only."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import clustered_sparse_attention_amd as ac
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ac.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ac_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ac.load()
+    names = _declared()
+    assert set(names) == set(ac.ENTRY_POINTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_sizes_match_c_layout():
+    assert ctypes.sizeof(ac.Shape) == 16
+    assert ctypes.sizeof(ac.Params) == 64
+    assert ctypes.sizeof(ac.CClusters) == 56
+    assert ctypes.sizeof(ac.CKStats) == 64
+    assert ctypes.sizeof(ac.CSelection) == 40
+    assert ctypes.sizeof(ac.CState) == 48
+
+
+def test_defaults_and_status_strings():
+    p = ac.params_default()
+    assert (p.nq, p.iters, p.m0, p.nmax, p.tau_rule, p.sel_mode) == (65, 10, 200, 1500, ac.AC_TAU_MEAN_X,
+                                                                    ac.AC_SEL_DENSITY)
+    assert abs(p.tau_param - 1.5) < 1e-7 and abs(p.sel_param - 0.15) < 1e-7
+    lib = ac.load()
+    assert lib.ac_status_str(ac.AC_E_WORKSPACE) == b"workspace too small"
+
+
+def test_sizes_validation():
+    p = ac.params_default()
+    ncap, ws = ac.ac_sizes(ac.Shape(1, 40, 75600, 128), p)
+    assert ncap == 1699 and ws > 40 * 75600 * 128 * 2
+    for bad_shape, code in [((1, 2, 4096, 96), ac.AC_E_UNSUPPORTED), ((0, 2, 4096, 64), ac.AC_E_SHAPE),
+                            ((1, 2, -5, 64), ac.AC_E_SHAPE)]:
+        with pytest.raises(ac.ACError) as e:
+            ac.ac_sizes(ac.Shape(*bad_shape), p)
+        assert e.value.status == code
+    for kw in [dict(nq=0), dict(tau_rule=9), dict(sel_mode=7), dict(sel_mode=ac.AC_SEL_DENSITY, sel_param=1.5),
+               dict(compensate=2), dict(tau_rule=ac.AC_TAU_PCTL, tau_param=0.0), dict(sel_mode=ac.AC_SEL_TOPK, topk=0)]:
+        with pytest.raises(ac.ACError) as e:
+            ac.ac_sizes(ac.Shape(1, 2, 4096, 64), ac.params_default(**kw))
+        assert e.value.status == ac.AC_E_ARG, kw
+    with pytest.raises(ac.ACError) as e:
+        ac.ac_sizes(ac.Shape(1, 2, 4096, 64), ac.params_default(nmax=5000))
+    assert e.value.status == ac.AC_E_UNSUPPORTED
+    with pytest.raises(ac.ACError) as e:
+        ac.ac_sizes(ac.Shape(1, 2, 100000, 64), ac.params_default(init_sample=0))
+    assert e.value.status == ac.AC_E_UNSUPPORTED
+
+
+def _fake_clusters(ncap):
+    # aligned non-NULL addresses that are never dereferenced: every call below fails validation first
+    a = 1 << 20
+    return ac.CClusters(ncap, a, a, a, a, a, a)
+
+
+def test_entry_points_reject_bad_arguments_before_any_device_work():
+    lib = ac.load()
+    shape = ac.Shape(1, 2, 4096, 64)
+    p = ac.params_default(nq=16, m0=32, nmax=64)
+    ncap, wsb = ac.ac_sizes(shape, p)
+    q = _fake_clusters(16)
+    k = _fake_clusters(ncap)
+    ws = 1 << 24
+    # NULL Q
+    assert lib.ac_cluster_q(ctypes.byref(shape), ctypes.byref(p), None, None, ctypes.byref(q), ws, wsb, None) == ac.AC_E_ARG
+    # workspace too small
+    assert lib.ac_cluster_q(ctypes.byref(shape), ctypes.byref(p), 1 << 20, None, ctypes.byref(q), ws, wsb - 1,
+                            None) == ac.AC_E_WORKSPACE
+    # misaligned workspace
+    assert lib.ac_cluster_q(ctypes.byref(shape), ctypes.byref(p), 1 << 20, None, ctypes.byref(q), ws + 8, wsb,
+                            None) == ac.AC_E_ARG
+    # wrong query capacity
+    q_bad = _fake_clusters(15)
+    assert lib.ac_cluster_q(ctypes.byref(shape), ctypes.byref(p), 1 << 20, None, ctypes.byref(q_bad), ws, wsb,
+                            None) == ac.AC_E_ARG
+    # key capacity must equal nmax - 1 + m0
+    st = ac.CKStats(*([1 << 20] * 8))
+    k_bad = _fake_clusters(ncap - 1)
+    assert lib.ac_cluster_k(ctypes.byref(shape), ctypes.byref(p), 1 << 20, 1 << 20, None, ctypes.byref(k_bad),
+                            ctypes.byref(st), ws, wsb, None) == ac.AC_E_ARG
+    # NULL stats array
+    st_bad = ac.CKStats(*([1 << 20] * 7 + [0]))
+    assert lib.ac_cluster_k(ctypes.byref(shape), ctypes.byref(p), 1 << 20, 1 << 20, None, ctypes.byref(k),
+                            ctypes.byref(st_bad), ws, wsb, None) == ac.AC_E_ARG
+    # selection capacity mismatch
+    sel = ac.CSelection(ncap + 1, 1 << 20, 1 << 20, 1 << 20, 0)
+    assert lib.ac_score_select(ctypes.byref(shape), ctypes.byref(p), ctypes.byref(q), ctypes.byref(k),
+                               ctypes.byref(st), ctypes.byref(sel), ws, wsb, None) == ac.AC_E_ARG
+    assert b"ncap_k" in lib.ac_last_error()
+    # NULL O
+    sel_ok = ac.CSelection(ncap, 1 << 20, 1 << 20, 1 << 20, 0)
+    assert lib.ac_sparse_attn(ctypes.byref(shape), ctypes.byref(p), 1 << 20, 1 << 20, 1 << 20, ctypes.byref(q),
+                              ctypes.byref(k), ctypes.byref(st), ctypes.byref(sel_ok), None, None, ws, wsb,
+                              None) == ac.AC_E_ARG
+    # NULL state
+    assert lib.ac_layer(ctypes.byref(shape), ctypes.byref(p), 1 << 20, 1 << 20, 1 << 20, None, 1 << 20, None, ws, wsb,
+                        None) == ac.AC_E_ARG
+
+
+def test_valid_arguments_without_device_report_device_error():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; this checks the no-device path")
+    lib = ac.load()
+    shape = ac.Shape(1, 2, 4096, 64)
+    p = ac.params_default(nq=16, m0=32, nmax=64)
+    ncap, wsb = ac.ac_sizes(shape, p)
+    q = _fake_clusters(16)
+    assert lib.ac_cluster_q(ctypes.byref(shape), ctypes.byref(p), 1 << 20, None, ctypes.byref(q), 1 << 24, wsb,
+                            None) == ac.AC_E_DEVICE
+    assert len(lib.ac_last_error()) > 0
