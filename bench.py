@@ -30,7 +30,7 @@ PEAK_HBM_GBS = 8000.0
 def workload_params(name: str, variant: str, compensate: int):
     """Layer hyperparameters of each workload (see csa_inputs for the data)."""
     import clustered_sparse_attention_amd as nm  # enum values (AC_*)
-    base = dict(nq=65, iters=10, iters_warm=3, init_sample=32, seed=0, compensate=compensate)
+    base = dict(nq=65, iters=10, iters_warm=3, init_sample=8, seed=0, compensate=compensate)
     if name == "tiny":
         base.update(nq=16, m0=32, nmax=64, tau_rule=nm.AC_TAU_INF, tau_param=0.0, sel_mode=nm.AC_SEL_TOPK, topk=8,
                     sel_param=0.0, init_sample=0)

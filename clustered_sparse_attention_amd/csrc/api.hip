@@ -97,7 +97,9 @@ struct Plan {
   size_t total = 0;
   // scratch
   size_t qhat, qn, lab, lperm, lseg, thist, ops_hi, ops_lo, ops_norm, d2buf, hn, hm, hcoff, hnew;
-  size_t uidx0, uidx1, dist, flag, rstate, rhist, msepart;
+  size_t uidx0, uidx1, dist, flag, rstate, rhist, msepart, chunk_off, upd_part, kpp_nx, kpp_G;
+  int kpp_smax;
+  int upd_items;
   size_t scoreA, scoreB, S, seltok, kc, vc, lb, tile_off, pairs;
   // ac_layer persistent
   size_t q_labels, q_perm, q_seg, q_cent, q_ncl, q_rho;
@@ -146,6 +148,16 @@ Plan make_plan(const ac_shape *s, const ac_params *p) {
   P.rstate = take(BH * 2 * 4);
   P.rhist = take(BH * 256 * 4);
   P.msepart = take(BH * P.ncapk * 8);
+  P.chunk_off = take(BH * (P.mcap + 1) * 4);
+  P.upd_items = (int)cdiv(P.L, UPD_CHUNK) + P.mcap;
+  {
+    const int mm = std::max(P.nq, std::min(p->m0, P.L));
+    P.kpp_smax = p->init_sample > 0 ? (int)std::min<int64_t>(P.L, (int64_t)p->init_sample * mm) : P.L;
+    const bool gram = P.kpp_smax <= KPP_GRAM_MAX;
+    P.kpp_nx = take(gram ? BH * (size_t)P.kpp_smax * 8 : 0);
+    P.kpp_G = take(gram ? BH * (size_t)P.kpp_smax * P.kpp_smax * 8 : 0);
+  }
+  P.upd_part = take(BH * (size_t)P.upd_items * D * 8);
   P.scoreA = take(BH * P.nq_pad * 6 * D * 2);
   P.scoreB = take(BH * P.ncap_pad * 6 * D * 2);
   P.S = take(BH * P.nq * (size_t)P.ncapk * 4);
@@ -237,7 +249,11 @@ struct Engine {
                 int stage, int *labels_out) {
     const int D = P.D;
     if (seed_init) {
-      launch_kpp_init(D, a, P.BH, at<double>(ws, P.d2buf), p->init_sample, p->seed, role, stage, st);
+      if (P.kpp_smax <= KPP_GRAM_MAX)
+        launch_kpp_gram(D, a, P.BH, P.kpp_smax, at<double>(ws, P.kpp_nx), at<double>(ws, P.kpp_G), p->init_sample,
+                        p->seed, role, stage, st);
+      else
+        launch_kpp(D, a, P.BH, at<double>(ws, P.d2buf), p->init_sample, p->seed, role, stage, st);
       AC_CHECK_LAUNCH();
     }
     CentOps op = ops();
@@ -248,7 +264,8 @@ struct Engine {
       launch_assign(D, a, op, P.BH, npts, lab, P.L, st);
       SortArgs s = sort_args(lab, at<int>(ws, P.lperm), at<int>(ws, P.lseg), P.mcap, mmax);
       launch_sort(s, P.BH, npts, st);
-      launch_update(D, a, s, op, P.BH, mmax, st);
+      launch_update(D, a, s, op, P.BH, mmax, npts, at<int>(ws, P.chunk_off), P.mcap + 1, at<double>(ws, P.upd_part),
+                    (int64_t)P.upd_items * D, st);
       AC_CHECK_LAUNCH();
     }
     launch_assign(D, a, op, P.BH, npts, labels_out, P.L, st);
@@ -511,7 +528,7 @@ AC_API ac_status ac_params_default(ac_params *p) {
   p->sel_param = 0.15f;
   p->compensate = 0;
   p->scale = 0.f;
-  p->init_sample = 32;
+  p->init_sample = 8;
   p->seed = 0;
   return AC_OK;
 }

@@ -85,8 +85,8 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
 
   __shared__ uint16_t Ks[ATT_KT * KROW];
   __shared__ uint16_t Vt[D * VROW];
-  __shared__ int rowidx[ATT_KT];
-  __shared__ float sbias[ATT_KT];
+  __shared__ int rowidx[3][ATT_KT];
+  __shared__ float sbias[3][ATT_KT];
   extern __shared__ int dyn[];
   int *s_cum = dyn;                       // [ncap + 1]
   int *s_start = dyn + (a.ncap + 1);      // [ncap]
@@ -155,127 +155,163 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
 
   const uint16_t *Kh = a.K + (int64_t)h * a.L * D;
   const uint16_t *Vh = a.V + (int64_t)h * a.L * D;
+  const uint16_t *Kc = a.kc + (int64_t)h * a.ncap * D;
+  const uint16_t *Vc = a.vc + (int64_t)h * a.ncap * D;
   const int *permk = a.perm_k + (int64_t)h * a.L;
   const int ncl_k = a.ncl_k[h];
-  const int phases = (!dense && a.compensate) ? 2 : 1;
+  const bool comp = !dense && a.compensate;
+  // tiles 0..nt0-1 walk the selected keys, nt0..ntiles-1 the pseudo-keys
+  const int nt0 = (T + ATT_KT - 1) / ATT_KT;
+  const int ntiles = nt0 + (comp ? (ncl_k + ATT_KT - 1) / ATT_KT : 0);
 
-  for (int phase = 0; phase < phases; ++phase) {
-    const int total = phase == 0 ? T : ncl_k;
-    const uint16_t *Kp = phase == 0 ? Kh : a.kc + (int64_t)h * a.ncap * D;
-    const uint16_t *Vp = phase == 0 ? Vh : a.vc + (int64_t)h * a.ncap * D;
-    for (int k0 = 0; k0 < total; k0 += ATT_KT) {
-      __syncthreads();  // previous tile fully consumed
-      if (tid < ATT_KT) {
-        const int o = k0 + tid;
-        int rw = -1;
-        float bias = 0.f;
-        if (o < total) {
-          if (phase == 1) {
-            rw = o;
-            const bool selected = (s_mask[o >> 5] >> (o & 31)) & 1u;
-            bias = selected ? -__builtin_inff() : a.lb[(int64_t)h * a.ncap + o];
-          } else if (dense) {
-            rw = o;
-          } else {
-            int lo2 = 0, hi2 = nsel;  // s_cum[lo2] <= o < s_cum[hi2]
-            while (hi2 - lo2 > 1) {
-              int mid = (lo2 + hi2) >> 1;
-              if (s_cum[mid] <= o) lo2 = mid; else hi2 = mid;
-            }
-            rw = permk[s_start[lo2] + (o - s_cum[lo2])];
-          }
-        } else {
-          bias = -__builtin_inff();
+  // row index and logit bias of every key of tile tt (threads 0..63)
+  auto tile_index = [&](int tt) {
+    const bool ph1 = tt >= nt0;
+    const int o = (ph1 ? tt - nt0 : tt) * ATT_KT + tid;
+    const int total = ph1 ? ncl_k : T;
+    int rw = -1;
+    float bias = -__builtin_inff();
+    if (o < total) {
+      bias = 0.f;
+      if (ph1) {
+        rw = o;
+        const bool selected = (s_mask[o >> 5] >> (o & 31)) & 1u;
+        bias = selected ? -__builtin_inff() : a.lb[(int64_t)h * a.ncap + o];
+      } else if (dense) {
+        rw = o;
+      } else {
+        int lo2 = 0, hi2 = nsel;  // s_cum[lo2] <= o < s_cum[hi2]
+        while (hi2 - lo2 > 1) {
+          const int mid = (lo2 + hi2) >> 1;
+          if (s_cum[mid] <= o) lo2 = mid; else hi2 = mid;
         }
-        rowidx[tid] = rw;
-        sbias[tid] = bias;
+        rw = permk[s_start[lo2] + (o - s_cum[lo2])];
       }
-      __syncthreads();
-      // K tile -> Ks (row-major), V tile -> Vt (transposed)
-#pragma unroll
-      for (int it = 0; it < (ATT_KT * D / 8) / 256; ++it) {
-        const int q = tid + it * 256;
-        const int rr = q / (D / 8), cc = (q % (D / 8)) * 8;
-        const int rw = rowidx[rr];
-        u32x4_t v = {0, 0, 0, 0};
-        if (rw >= 0) v = *(const u32x4_t *)&Kp[(int64_t)rw * D + cc];
-        *(u32x4_t *)&Ks[rr * KROW + cc] = v;
-      }
-#pragma unroll
-      for (int it = 0; it < (ATT_KT / 2 * D / 8) / 256; ++it) {
-        const int q = tid + it * 256;
-        const int kp = q % (ATT_KT / 2), dc = q / (ATT_KT / 2);
-        const int r0 = rowidx[2 * kp], r1 = rowidx[2 * kp + 1];
-        u32x4_t v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
-        if (r0 >= 0) v0 = *(const u32x4_t *)&Vp[(int64_t)r0 * D + dc * 8];
-        if (r1 >= 0) v1 = *(const u32x4_t *)&Vp[(int64_t)r1 * D + dc * 8];
-        const uint16_t *e0 = (const uint16_t *)&v0;
-        const uint16_t *e1 = (const uint16_t *)&v1;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          *(uint32_t *)&Vt[(dc * 8 + i) * VROW + 2 * kp] = (uint32_t)e0[i] | ((uint32_t)e1[i] << 16);
-      }
-      __syncthreads();
+    }
+    rowidx[tt % 3][tid] = rw;
+    sbias[tt % 3][tid] = bias;
+  };
 
-      // S^T for two 32-key blocks
-      f32x16_t acc_s[2];
+  constexpr int KCH = (ATT_KT * D / 8) / 256;      // 16-byte K pieces per thread
+  constexpr int VCH = (ATT_KT / 2 * D / 8) / 256;  // V key pairs x 8 dims per thread
+  u32x4_t kreg[KCH], vreg[VCH][2];
+  auto load_tile = [&](int tt) {
+    const bool ph1 = tt >= nt0;
+    const uint16_t *Kp = ph1 ? Kc : Kh;
+    const uint16_t *Vp = ph1 ? Vc : Vh;
+    const int *ri = rowidx[tt % 3];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        acc_s[kb] = (f32x16_t){};
-        // key slot l32 -> tile key 32*kb + 16*(a/2) + 8*gg + 4*(a%2) + b, with l32 = 8a + 4gg + b
-        const int aa = l32 >> 3, gg = (l32 >> 2) & 1, bb = l32 & 3;
-        const int key = 32 * kb + 16 * (aa >> 1) + 8 * gg + 4 * (aa & 1) + bb;
+    for (int it = 0; it < KCH; ++it) {
+      const int q = tid + it * 256;
+      const int rr = q / (D / 8), cc = (q % (D / 8)) * 8;
+      const int rw = ri[rr];
+      kreg[it] = rw >= 0 ? *(const u32x4_t *)&Kp[(int64_t)rw * D + cc] : (u32x4_t){0, 0, 0, 0};
+    }
 #pragma unroll
-        for (int ks = 0; ks < KSQ; ++ks) {
-          bf16x8_t kf = *(const bf16x8_t *)&Ks[key * KROW + ks * 16 + g * 8];
-          acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], acc_s[kb], 0, 0, 0);
-        }
+    for (int it = 0; it < VCH; ++it) {
+      const int q = tid + it * 256;
+      const int kp = q % (ATT_KT / 2), dc = q / (ATT_KT / 2);
+      const int r0 = ri[2 * kp], r1 = ri[2 * kp + 1];
+      vreg[it][0] = r0 >= 0 ? *(const u32x4_t *)&Vp[(int64_t)r0 * D + dc * 8] : (u32x4_t){0, 0, 0, 0};
+      vreg[it][1] = r1 >= 0 ? *(const u32x4_t *)&Vp[(int64_t)r1 * D + dc * 8] : (u32x4_t){0, 0, 0, 0};
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int it = 0; it < KCH; ++it) {
+      const int q = tid + it * 256;
+      const int rr = q / (D / 8), cc = (q % (D / 8)) * 8;
+      *(u32x4_t *)&Ks[rr * KROW + cc] = kreg[it];
+    }
+#pragma unroll
+    for (int it = 0; it < VCH; ++it) {
+      const int q = tid + it * 256;
+      const int kp = q % (ATT_KT / 2), dc = q / (ATT_KT / 2);
+      const uint16_t *e0 = (const uint16_t *)&vreg[it][0];
+      const uint16_t *e1 = (const uint16_t *)&vreg[it][1];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *(uint32_t *)&Vt[(dc * 8 + i) * VROW + 2 * kp] = (uint32_t)e0[i] | ((uint32_t)e1[i] << 16);
+    }
+  };
+
+  if (tid < ATT_KT) {
+    if (ntiles > 0) tile_index(0);
+    if (ntiles > 1) tile_index(1);
+  }
+  __syncthreads();
+  if (ntiles > 0) load_tile(0);
+
+  // key slot l32 of each 32-key block holds tile key 16*(a/2) + 8*gg + 4*(a%2) + b, l32 = 8a + 4gg + b
+  const int kslot = 16 * ((l32 >> 3) >> 1) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
+
+  for (int tt = 0; tt < ntiles; ++tt) {
+    __syncthreads();  // the previous tile is consumed; this tile's row indices are visible
+    store_tile();
+    __syncthreads();
+    if (tt + 1 < ntiles) load_tile(tt + 1);  // in flight during this tile's MFMAs
+    if (tid < ATT_KT && tt + 2 < ntiles) tile_index(tt + 2);
+
+    // S^T for two 32-key blocks
+    f32x16_t acc_s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      acc_s[kb] = (f32x16_t){};
+      const int key = 32 * kb + kslot;
+#pragma unroll
+      for (int ks = 0; ks < KSQ; ++ks) {
+        const bf16x8_t kf = *(const bf16x8_t *)&Ks[key * KROW + ks * 16 + g * 8];
+        acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], acc_s[kb], 0, 0, 0);
       }
-      // scores in base-2 units, masked / biased
-      float mt = -__builtin_inff();
+    }
+    // scores in base-2 units; the bias (mask, ln n_c) only on tail and pseudo-key tiles
+    const bool need_bias = tt >= nt0 - 1;
+    const float *bz = sbias[tt % 3];
+    float mt = -__builtin_inff();
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = 32 * kb + 16 * (j >> 3) + 8 * g + (j & 7);
-          float sv = acc_s[kb][j] * sl2 + sbias[key];
-          acc_s[kb][j] = sv;
-          mt = fmaxf(mt, sv);
+      for (int j = 0; j < 16; ++j) {
+        float sv = acc_s[kb][j] * sl2;
+        if (need_bias) sv += bz[32 * kb + 16 * (j >> 3) + 8 * g + (j & 7)];
+        acc_s[kb][j] = sv;
+        mt = fmaxf(mt, sv);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_i, mt);
+    const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
+    const float alpha = exp2f(m_i - m_use);
+    float psum = 0.f;
+    bf16x8_t pb[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        bf16x8_t t;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float pv = exp2f(acc_s[kb][half * 8 + i] - m_use);
+          psum += pv;
+          t[i] = (__bf16)pv;
         }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_i, mt);
-      const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
-      const float alpha = exp2f(m_i - m_use);
-      float psum = 0.f;
-      bf16x8_t pb[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          bf16x8_t t;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            float p = exp2f(acc_s[kb][half * 8 + i] - m_use);
-            psum += p;
-            t[i] = (__bf16)p;
-          }
-          pb[kb * 2 + half] = t;
-        }
-      l_i = l_i * alpha + psum;
-      m_i = m_new;
+        pb[kb * 2 + half] = t;
+      }
+    l_i = l_i * alpha + psum;
+    m_i = m_new;
+    if (__ballot(alpha != 1.f)) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc_o[db][j] *= alpha;
-      // O^T += V^T P^T over 4 k-steps of 16 keys
+    }
+    // O^T += V^T P^T over 4 k-steps of 16 keys
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int kbase = 16 * s + 8 * g;
+    for (int s = 0; s < 4; ++s) {
+      const int kbase = 16 * s + 8 * g;
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          bf16x8_t vf = *(const bf16x8_t *)&Vt[(32 * db + l32) * VROW + kbase];
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[s], acc_o[db], 0, 0, 0);
-        }
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8_t vf = *(const bf16x8_t *)&Vt[(32 * db + l32) * VROW + kbase];
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[s], acc_o[db], 0, 0, 0);
       }
     }
   }

@@ -7,10 +7,12 @@
 namespace ac {
 
 constexpr int KPP_SMAX = 16384;  // most points a k-means++ subsample may hold
+constexpr int KPP_GRAM_MAX = 2048;  // subsamples up to this size seed from a distance matrix
 constexpr int SORT_TILE = 512;   // points per counting-sort tile (one wave)
 constexpr int ATT_QT = 128;      // query rows per attention block
 constexpr int ATT_KT = 64;       // keys per attention tile
 constexpr int SEL_MAXN = 4096;   // most key clusters the select kernel sorts
+constexpr int UPD_CHUNK = 256;   // members per block in the centre update
 
 enum { TAU_RULE_MEAN_X = 0, TAU_RULE_PCTL = 1, TAU_RULE_ABS = 2, TAU_RULE_INF = 3 };
 
@@ -119,13 +121,16 @@ struct AttnArgs {
 
 // kmeans.hip
 void launch_qnorm(int D, const uint16_t *Q, uint16_t *Qh, float *qn, int64_t rows, hipStream_t st);
-void launch_kpp_init(int D, const KmArgs &a, int BH, double *d2buf, int init_sample, uint64_t seed, int role,
-                     int stage, hipStream_t st);
+void launch_kpp(int D, const KmArgs &a, int BH, double *d2buf, int init_sample, uint64_t seed, int role, int stage,
+                hipStream_t st);
+void launch_kpp_gram(int D, const KmArgs &a, int BH, int smax, double *nx, double *G, int init_sample, uint64_t seed,
+                     int role, int stage, hipStream_t st);
 void launch_cent_prep(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, hipStream_t st);
 void launch_assign(int D, const KmArgs &a, const CentOps &op, int BH, int nmax_pts, int *labels, int64_t lab_hs,
                    hipStream_t st);
 void launch_sort(const SortArgs &s, int BH, int nmax_pts, hipStream_t st);
-void launch_update(int D, const KmArgs &a, const SortArgs &s, const CentOps &op, int BH, int mmax, hipStream_t st);
+void launch_update(int D, const KmArgs &a, const SortArgs &s, const CentOps &op, int BH, int mmax, int npts,
+                   int *chunk_off, int64_t co_hs, double *partial, int64_t part_hs, hipStream_t st);
 void launch_stage_dist(int D, const KmArgs &a, int BH, int nmax_pts, const int *labels, int64_t lab_hs, float *dist,
                        int64_t dist_hs, hipStream_t st);
 void launch_tau(const float *dist, int64_t dist_hs, const int *n_arr, int BH, int nmax_pts, int rule, float param,

@@ -46,104 +46,6 @@ __global__ __launch_bounds__(256) void k_qnorm(const uint16_t *__restrict__ Q, u
 }
 
 // ---------------------------------------------------------------------------
-// k-means++ seeding (Arthur and Vassilvitskii 2007) on the strided subsample
-// {floor(j*n/s)}, one block per head.  D^2 is exact fp64 over bf16 points
-// and lives in a global scratch row of SMAX doubles per head.
-template <int D>
-__global__ __launch_bounds__(1024) void k_kpp_init(KmArgs a, double *__restrict__ d2buf, int init_sample,
-                                                  uint64_t seed, int role, int stage) {
-  const int h = blockIdx.y;
-  const int n = a.n[h], m = a.m[h];
-  if (n <= 0 || m <= 0) return;
-  const int s = init_sample > 0 ? min(n, init_sample * m) : n;  // host guarantees s <= SMAX
-  double *D2 = d2buf + (int64_t)h * KPP_SMAX;
-  float *cent = a.cent + (int64_t)h * a.cent_hs + (int64_t)a.coff[h] * D;
-  const uint16_t *X = a.X + (int64_t)h * a.x_hs;
-  const int *idx = a.idx ? a.idx + (int64_t)h * a.idx_hs : nullptr;
-  const uint64_t sid = stream_id((uint64_t)h, role, stage);
-
-  __shared__ float c_sh[D];
-  __shared__ double red[1024 / 64];
-  __shared__ double scan_sh[1024];
-  __shared__ int pick_sh;
-
-  const int tid = threadIdx.x;
-  const int chunk = (s + 1023) / 1024;
-  const int jb = min(s, tid * chunk), je = min(s, jb + chunk);
-
-  auto row_of = [&](int j) -> int64_t {
-    int li = (int)(((int64_t)j * n) / s);
-    return idx ? (int64_t)idx[li] : (int64_t)li;
-  };
-
-  for (int t = 0; t < m; ++t) {
-    double u = uniform01(seed, sid, (uint64_t)t);
-    if (t == 0) {
-      if (tid == 0) pick_sh = min(s - 1, (int)(u * (double)s));
-    } else {
-      // total and the thread-chunk prefix of D^2
-      double loc = 0.0;
-      for (int j = jb; j < je; ++j) loc += D2[j];
-      scan_sh[tid] = loc;
-      __syncthreads();
-      // inclusive Hillis-Steele scan over 1024 partial sums
-      for (int off = 1; off < 1024; off <<= 1) {
-        double v = tid >= off ? scan_sh[tid - off] : 0.0;
-        __syncthreads();
-        scan_sh[tid] += v;
-        __syncthreads();
-      }
-      double total = scan_sh[1023];
-      if (tid == 0) pick_sh = -1;
-      __syncthreads();
-      if (total > 0.0) {
-        double target = u * total;
-        double excl = tid > 0 ? scan_sh[tid - 1] : 0.0;
-        if (excl <= target && target < scan_sh[tid] && je > jb) {
-          double run = excl;
-          int pj = je - 1;
-          for (int j = jb; j < je; ++j) {
-            run += D2[j];
-            if (run > target) { pj = j; break; }
-          }
-          pick_sh = pj;  // exactly one thread satisfies the range test
-        }
-        __syncthreads();
-        if (tid == 0 && pick_sh < 0) pick_sh = s - 1;
-      } else {
-        if (tid == 0) pick_sh = min(s - 1, (int)(u * (double)s));
-      }
-    }
-    __syncthreads();
-    const int pj = pick_sh;
-    const int64_t prow = row_of(pj);
-    for (int dd = tid; dd < D; dd += 1024) {
-      float v = bf2f(X[prow * D + dd]);
-      c_sh[dd] = v;
-      cent[(int64_t)t * D + dd] = v;
-    }
-    __syncthreads();
-    // D^2 update with the new centre
-    for (int j = tid; j < s; j += 1024) {
-      const uint16_t *xr = X + row_of(j) * D;
-      double acc = 0.0;
-#pragma unroll 8
-      for (int dd = 0; dd < D; dd += 8) {
-        u32x4_t w = *(const u32x4_t *)&xr[dd];
-        const uint16_t *e = (const uint16_t *)&w;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          double df = (double)bf2f(e[i]) - (double)c_sh[dd + i];
-          acc += df * df;
-        }
-      }
-      D2[j] = (t == 0) ? acc : fmin(D2[j], acc);
-    }
-    __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Centre operands for the distance GEMM: hi = bf16(c), lo = bf16(c - hi),
 // and ||c||^2 (fp64 sum, stored fp32).  One wave per centre.
 template <int D>
@@ -384,69 +286,115 @@ __global__ __launch_bounds__(64) void k_sort_scatter(SortArgs s) {
 }
 
 // ---------------------------------------------------------------------------
-// Lloyd update: each centre becomes the fp64 mean of its members (read in
-// counting-sort order); an empty cluster keeps its centre.  The new centre's
-// GEMM operands are written in the same pass.  One block per (centre, head).
+// Lloyd update as a chunked segmented reduction over the counting-sort order:
+// every cluster is cut into chunks of UPD_CHUNK members; one block sums one
+// chunk in fp64 (16 lanes per row, fixed order), a second kernel adds a
+// cluster's chunk sums in order and divides.  An empty cluster keeps its
+// centre.  The new centre's GEMM operands are written in the same pass.
+__global__ __launch_bounds__(1024) void k_chunk_scan(SortArgs s, int *__restrict__ chunk_off, int64_t co_hs) {
+  const int h = blockIdx.x;
+  const int m = s.m[h];
+  const int *seg = s.seg + (int64_t)h * s.seg_hs;
+  int *co = chunk_off + (int64_t)h * co_hs;
+  __shared__ int part[1024];
+  const int per = (m + 1023) / 1024;
+  const int cb = min(m, (int)threadIdx.x * per), ce = min(m, cb + per);
+  int loc = 0;
+  for (int c = cb; c < ce; ++c) loc += (seg[c + 1] - seg[c] + UPD_CHUNK - 1) / UPD_CHUNK;
+  part[threadIdx.x] = loc;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int run = part[threadIdx.x] - loc;
+  for (int c = cb; c < ce; ++c) {
+    co[c] = run;
+    run += (seg[c + 1] - seg[c] + UPD_CHUNK - 1) / UPD_CHUNK;
+  }
+  if (threadIdx.x == 1023) co[max(m, 0)] = part[1023];
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void k_update(KmArgs a, SortArgs s, CentOps op) {
-  const int h = blockIdx.y, c = blockIdx.x;
-  if (c >= a.m[h] || a.n[h] <= 0) return;
+__global__ __launch_bounds__(256) void k_update_partial(KmArgs a, SortArgs s, const int *__restrict__ chunk_off,
+                                                        int64_t co_hs, double *__restrict__ partial, int64_t part_hs) {
+  constexpr int PL = D / 16;
+  const int h = blockIdx.y, item = blockIdx.x;
+  const int m = a.m[h];
+  if (m <= 0 || a.n[h] <= 0) return;
+  const int *co = chunk_off + (int64_t)h * co_hs;
+  if (item >= co[m]) return;
+  int lo = 0, hi = m;  // co[lo] <= item < co[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (co[mid] <= item) lo = mid; else hi = mid;
+  }
+  const int c = lo;
   const int *seg = s.seg + (int64_t)h * s.seg_hs;
   const int *perm = s.perm + (int64_t)h * s.perm_hs;
-  const int beg = seg[c], end = seg[c + 1];
+  const int beg = seg[c] + (item - co[c]) * UPD_CHUNK;
+  const int end = min(seg[c + 1], beg + UPD_CHUNK);
   const uint16_t *X = a.X + (int64_t)h * a.x_hs;
   const int *idx = a.idx ? a.idx + (int64_t)h * a.idx_hs : nullptr;
-  float *cr = a.cent + (int64_t)h * a.cent_hs + (int64_t)(a.coff[h] + c) * D;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  constexpr int PL = D / 64;  // dims per lane (1 or 2)
-  __shared__ double sh[4][D];
-  __shared__ float newc[D];
+  const int grp = threadIdx.x >> 4, sub = threadIdx.x & 15;
   double acc[PL];
 #pragma unroll
   for (int k = 0; k < PL; ++k) acc[k] = 0.0;
-  for (int p = beg + wave; p < end; p += 4) {
-    int li = perm[p];
-    int64_t row = idx ? (int64_t)idx[li] : (int64_t)li;
-    const uint16_t *xr = X + row * D + lane * PL;
-    if (PL == 2) {
-      uint32_t w = *(const uint32_t *)xr;
-      acc[0] += (double)bf2f((uint16_t)(w & 0xFFFF));
-      acc[PL - 1] += (double)bf2f((uint16_t)(w >> 16));
-    } else {
-      acc[0] += (double)bf2f(xr[0]);
-    }
-  }
+  for (int p = beg + grp; p < end; p += 16) {
+    const int li = perm[p];
+    const int64_t row = idx ? (int64_t)idx[li] : (int64_t)li;
+    const uint16_t *xr = X + row * D + sub * PL;
+    uint16_t xv[PL];
+    if (PL == 8) *(u32x4_t *)xv = *(const u32x4_t *)xr;
+    else *(u32x2_t *)xv = *(const u32x2_t *)xr;
 #pragma unroll
-  for (int k = 0; k < PL; ++k) sh[wave][lane * PL + k] = acc[k];
+    for (int k = 0; k < PL; ++k) acc[k] += (double)bf2f(xv[k]);
+  }
+  __shared__ double sh[16][D];
+#pragma unroll
+  for (int k = 0; k < PL; ++k) sh[grp][sub * PL + k] = acc[k];
   __syncthreads();
-  const int cnt = end - beg;
   if (threadIdx.x < D) {
-    const int dd = threadIdx.x;
+    double t = 0.0;
+#pragma unroll
+    for (int gg = 0; gg < 16; ++gg) t += sh[gg][threadIdx.x];
+    partial[(int64_t)h * part_hs + (int64_t)item * D + threadIdx.x] = t;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(128) void k_update_final(KmArgs a, SortArgs s, const int *__restrict__ chunk_off,
+                                                      int64_t co_hs, const double *__restrict__ partial,
+                                                      int64_t part_hs, CentOps op) {
+  const int h = blockIdx.y, c = blockIdx.x;
+  if (c >= a.m[h] || a.n[h] <= 0) return;
+  const int *seg = s.seg + (int64_t)h * s.seg_hs;
+  const int *co = chunk_off + (int64_t)h * co_hs;
+  const int cnt = seg[c + 1] - seg[c];
+  float *cr = a.cent + (int64_t)h * a.cent_hs + (int64_t)(a.coff[h] + c) * D;
+  __shared__ double red[2];
+  double ss = 0.0;
+  for (int dd = threadIdx.x; dd < D; dd += 128) {
     float v;
     if (cnt > 0) {
-      double sum = ((sh[0][dd] + sh[1][dd]) + sh[2][dd]) + sh[3][dd];
-      v = (float)(sum / (double)cnt);
+      double t = 0.0;
+      for (int it = co[c]; it < co[c + 1]; ++it) t += partial[(int64_t)h * part_hs + (int64_t)it * D + dd];
+      v = (float)(t / (double)cnt);
       cr[dd] = v;
     } else {
       v = cr[dd];
     }
-    newc[dd] = v;
+    const uint16_t bh = f2bf(v);
+    op.hi[((int64_t)h * op.cap + c) * D + dd] = bh;
+    op.lo[((int64_t)h * op.cap + c) * D + dd] = f2bf(v - bf2f(bh));
+    ss += (double)v * (double)v;
   }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  if (wave == 0) {
-    uint16_t *hi = op.hi + ((int64_t)h * op.cap + c) * D;
-    uint16_t *lo = op.lo + ((int64_t)h * op.cap + c) * D;
-    double ss = 0.0;
-    for (int dd = lane; dd < D; dd += 64) {
-      float v = newc[dd];
-      uint16_t bh = f2bf(v);
-      hi[dd] = bh;
-      lo[dd] = f2bf(v - bf2f(bh));
-      ss += (double)v * (double)v;
-    }
-    ss = wave_sum(ss);
-    if (lane == 0) op.norm[(int64_t)h * op.cap + c] = (float)ss;
-  }
+  if (threadIdx.x == 0) op.norm[(int64_t)h * op.cap + c] = (float)(red[0] + red[1]);
 }
 
 // ---------------------------------------------------------------------------
@@ -738,12 +686,6 @@ void launch_qnorm(int D, const uint16_t *Q, uint16_t *Qh, float *qn, int64_t row
   AC_D_DISPATCH(D, hipLaunchKernelGGL(k_qnorm<DD>, dim3((unsigned)blocks), dim3(256), 0, st, Q, Qh, qn, rows));
 }
 
-void launch_kpp_init(int D, const KmArgs &a, int BH, double *d2buf, int init_sample, uint64_t seed, int role,
-                     int stage, hipStream_t st) {
-  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_kpp_init<DD>, dim3(1, BH), dim3(1024), 0, st, a, d2buf, init_sample, seed,
-                                      role, stage));
-}
-
 void launch_cent_prep(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, hipStream_t st) {
   AC_D_DISPATCH(D, hipLaunchKernelGGL(k_cent_prep<DD>, g2((mmax + 3) / 4, BH), dim3(256), 0, st, a, op));
 }
@@ -762,8 +704,14 @@ void launch_sort(const SortArgs &s, int BH, int nmax_pts, hipStream_t st) {
   hipLaunchKernelGGL(k_sort_scatter, g2(tiles, BH), dim3(64), sh, st, s);
 }
 
-void launch_update(int D, const KmArgs &a, const SortArgs &s, const CentOps &op, int BH, int mmax, hipStream_t st) {
-  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_update<DD>, g2(mmax, BH), dim3(256), 0, st, a, s, op));
+void launch_update(int D, const KmArgs &a, const SortArgs &s, const CentOps &op, int BH, int mmax, int npts,
+                   int *chunk_off, int64_t co_hs, double *partial, int64_t part_hs, hipStream_t st) {
+  hipLaunchKernelGGL(k_chunk_scan, dim3(BH), dim3(1024), 0, st, s, chunk_off, co_hs);
+  const int items = (npts + UPD_CHUNK - 1) / UPD_CHUNK + mmax;
+  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_update_partial<DD>, g2(items, BH), dim3(256), 0, st, a, s, chunk_off, co_hs,
+                                      partial, part_hs));
+  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_update_final<DD>, g2(mmax, BH), dim3(128), 0, st, a, s, chunk_off, co_hs,
+                                      partial, part_hs, op));
 }
 
 void launch_stage_dist(int D, const KmArgs &a, int BH, int nmax_pts, const int *labels, int64_t lab_hs, float *dist,

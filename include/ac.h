@@ -99,7 +99,7 @@ typedef struct ac_params {
                           value mean, logit bias ln n_c): ClusterAttention §1.2 eq. (5) (0) */
   float scale;         /* softmax scale; 0 means 1/sqrt(d) (0) */
   int32_t init_sample; /* k-means++ runs on a strided subsample of min(n, init_sample * m) points;
-                          0 = every point (32).  The subsample may hold at most 16384 points. */
+                          0 = every point (8).  The subsample may hold at most 16384 points. */
   uint64_t seed;       /* seed of the counter-based SplitMix64 stream of k-means++ (0) */
 } ac_params;
 

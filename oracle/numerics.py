@@ -41,7 +41,7 @@ class Params:
     sel_param: float = 0.15
     compensate: int = 0
     scale: float = 0.0          # 0 -> 1/sqrt(d)
-    init_sample: int = 32       # k-means++ subsample factor; 0 -> every point
+    init_sample: int = 8        # k-means++ subsample factor; 0 -> every point
     seed: int = 0
 
     def attn_scale(self, d: int) -> float:

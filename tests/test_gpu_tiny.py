@@ -44,15 +44,18 @@ def _bits(x, bh):
 
 # ---------------------------------------------------------------- queries
 
-def test_query_seeding_bit_exact(tiny):
+@pytest.mark.parametrize("init_sample", [0, 8])
+def test_query_seeding_bit_exact(tiny, init_sample):
+    """k-means++ picks equal the oracle's: the streamed path (every point,
+    s = 4096) and the distance-matrix path (s = 8 * 16 = 128)."""
     Q, K, V = tiny
-    p = P(iters=0)
+    p = P(iters=0, init_sample=init_sample)
     r = Run(Q, K, V, p)
     r.cluster_q()
     cent = np_(r.q.cent)
     for bh in range(r.BH):
         X = nm.bf16_to_f64(okm.normalize_queries(_bits(Q, bh)))
-        C0, _ = okm.kmeanspp_init(X, 16, p.seed, nm.stream_id(bh, 0, 0), 0)
+        C0, _ = okm.kmeanspp_init(X, 16, p.seed, nm.stream_id(bh, 0, 0), init_sample)
         assert np.array_equal(cent[bh].astype(np.float64), C0), f"head {bh}"
 
 
@@ -96,15 +99,16 @@ def test_query_perm_seg_rho(tiny):
 
 # ---------------------------------------------------------------- keys
 
-def test_key_seeding_and_single_stage(tiny):
+@pytest.mark.parametrize("init_sample", [0, 8, 64])
+def test_key_seeding_and_single_stage(tiny, init_sample):
     Q, K, V = tiny
-    p0 = P(iters=0)
+    p0 = P(iters=0, init_sample=init_sample)
     r0 = Run(Q, K, V, p0)
     r0.cluster_k()
     c0 = np_(r0.k.cent).astype(np.float64)
     for bh in range(r0.BH):
         Kx = nm.bf16_to_f64(_bits(K, bh))
-        C0, _ = okm.kmeanspp_init(Kx, 32, p0.seed, nm.stream_id(bh, 1, 0), 0)
+        C0, _ = okm.kmeanspp_init(Kx, 32, p0.seed, nm.stream_id(bh, 1, 0), init_sample)
         assert np.array_equal(c0[bh, :32], C0), bh
     p = P()
     r = Run(Q, K, V, p)
@@ -140,10 +144,11 @@ def test_key_stats(tiny):
         assert abs(mse[bh] - st["mse"]) <= 1e-4 * st["mse"]
 
 
-@pytest.mark.parametrize("rule,param", [(nm.TAU_MEAN_X, 1.5), (nm.TAU_PCTL, 0.95)])
-def test_key_multistage_matches_oracle(tiny, rule, param):
+@pytest.mark.parametrize("rule,param,init_sample", [(nm.TAU_MEAN_X, 1.5, 0), (nm.TAU_PCTL, 0.95, 0),
+                                                    (nm.TAU_MEAN_X, 1.5, 8)])
+def test_key_multistage_matches_oracle(tiny, rule, param, init_sample):
     Q, K, V = tiny
-    p = P(m0=16, nmax=64, tau_rule=rule, tau_param=param)
+    p = P(m0=16, nmax=64, tau_rule=rule, tau_param=param, init_sample=init_sample)
     r = Run(Q, K, V, p)
     r.cluster_k()
     ncl, fb, stages, tau = np_(r.k.ncl), np_(r.st.fallback), np_(r.st.stages), np_(r.st.tau)
