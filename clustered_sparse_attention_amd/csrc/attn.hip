@@ -164,13 +164,14 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   const int nt0 = (T + ATT_KT - 1) / ATT_KT;
   const int ntiles = nt0 + (comp ? (ncl_k + ATT_KT - 1) / ATT_KT : 0);
 
-  // row index and logit bias of every key of tile tt (threads 0..63)
-  auto tile_index = [&](int tt) {
+  // row index and logit bias of every key of tile tt (threads 0..63), in two
+  // halves so that the dependent permutation load is in flight across the MFMAs
+  auto tile_index_issue = [&](int tt, float &bias) -> int {
     const bool ph1 = tt >= nt0;
     const int o = (ph1 ? tt - nt0 : tt) * ATT_KT + tid;
     const int total = ph1 ? ncl_k : T;
     int rw = -1;
-    float bias = -__builtin_inff();
+    bias = -__builtin_inff();
     if (o < total) {
       bias = 0.f;
       if (ph1) {
@@ -188,6 +189,9 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         rw = permk[s_start[lo2] + (o - s_cum[lo2])];
       }
     }
+    return rw;
+  };
+  auto tile_index_commit = [&](int tt, int rw, float bias) {
     rowidx[tt % 3][tid] = rw;
     sbias[tt % 3][tid] = bias;
   };
@@ -204,16 +208,16 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     for (int it = 0; it < KCH; ++it) {
       const int q = tid + it * 256;
       const int rr = q / (D / 8), cc = (q % (D / 8)) * 8;
-      const int rw = ri[rr];
-      kreg[it] = rw >= 0 ? *(const u32x4_t *)&Kp[(int64_t)rw * D + cc] : (u32x4_t){0, 0, 0, 0};
+      const int rw = max(ri[rr], 0);  // masked keys (-1) read row 0: their logit bias is -inf
+      kreg[it] = *(const u32x4_t *)&Kp[(int64_t)rw * D + cc];
     }
 #pragma unroll
     for (int it = 0; it < VCH; ++it) {
       const int q = tid + it * 256;
       const int kp = q % (ATT_KT / 2), dc = q / (ATT_KT / 2);
-      const int r0 = ri[2 * kp], r1 = ri[2 * kp + 1];
-      vreg[it][0] = r0 >= 0 ? *(const u32x4_t *)&Vp[(int64_t)r0 * D + dc * 8] : (u32x4_t){0, 0, 0, 0};
-      vreg[it][1] = r1 >= 0 ? *(const u32x4_t *)&Vp[(int64_t)r1 * D + dc * 8] : (u32x4_t){0, 0, 0, 0};
+      const int r0 = max(ri[2 * kp], 0), r1 = max(ri[2 * kp + 1], 0);
+      vreg[it][0] = *(const u32x4_t *)&Vp[(int64_t)r0 * D + dc * 8];
+      vreg[it][1] = *(const u32x4_t *)&Vp[(int64_t)r1 * D + dc * 8];
     }
   };
   auto store_tile = [&]() {
@@ -236,8 +240,11 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   };
 
   if (tid < ATT_KT) {
-    if (ntiles > 0) tile_index(0);
-    if (ntiles > 1) tile_index(1);
+    for (int tt = 0; tt < 2 && tt < ntiles; ++tt) {
+      float b;
+      const int rw = tile_index_issue(tt, b);
+      tile_index_commit(tt, rw, b);
+    }
   }
   __syncthreads();
   if (ntiles > 0) load_tile(0);
@@ -250,7 +257,10 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     store_tile();
     __syncthreads();
     if (tt + 1 < ntiles) load_tile(tt + 1);  // in flight during this tile's MFMAs
-    if (tid < ATT_KT && tt + 2 < ntiles) tile_index(tt + 2);
+    const bool idx_next = tid < ATT_KT && tt + 2 < ntiles;
+    int pend_rw = -1;
+    float pend_b = 0.f;
+    if (idx_next) pend_rw = tile_index_issue(tt + 2, pend_b);
 
     // S^T for two 32-key blocks
     f32x16_t acc_s[2];
@@ -264,23 +274,37 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], acc_s[kb], 0, 0, 0);
       }
     }
-    // scores in base-2 units; the bias (mask, ln n_c) only on tail and pseudo-key tiles
-    const bool need_bias = tt >= nt0 - 1;
+    // scores in base-2 units: s * scale * log2(e) + bias (0, -inf for masked
+    // keys, log2 n_c for pseudo-keys)
     const float *bz = sbias[tt % 3];
     float mt = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float sv = acc_s[kb][j] * sl2;
-        if (need_bias) sv += bz[32 * kb + 16 * (j >> 3) + 8 * g + (j & 7)];
-        acc_s[kb][j] = sv;
-        mt = fmaxf(mt, sv);
+      for (int half = 0; half < 2; ++half) {
+        const f32x4_t b0 = *(const f32x4_t *)&bz[32 * kb + 16 * half + 8 * g];
+        const f32x4_t b1 = *(const f32x4_t *)&bz[32 * kb + 16 * half + 8 * g + 4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float sv = fmaf(acc_s[kb][half * 8 + i], sl2, i < 4 ? b0[i] : b1[i - 4]);
+          acc_s[kb][half * 8 + i] = sv;
+          mt = fmaxf(mt, sv);
+        }
       }
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_i, mt);
-    const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
-    const float alpha = exp2f(m_i - m_use);
+    // lazy rescale: the reference max m_i may trail the running max by up to
+    // 2^8, so p <= 256; O and l are rescaled only when a row outgrows that
+    if (__ballot(mt > m_i + 8.f)) {
+      const float m_new = fmaxf(m_i, mt);
+      const float alpha = m_i == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_i - m_new);
+      l_i *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc_o[db][j] *= alpha;
+      m_i = m_new;
+    }
+    const float m_use = m_i == -__builtin_inff() ? 0.f : m_i;
     float psum = 0.f;
     bf16x8_t pb[4];
 #pragma unroll
@@ -290,20 +314,13 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         bf16x8_t t;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float pv = exp2f(acc_s[kb][half * 8 + i] - m_use);
+          const float pv = __builtin_amdgcn_exp2f(acc_s[kb][half * 8 + i] - m_use);
           psum += pv;
           t[i] = (__bf16)pv;
         }
         pb[kb * 2 + half] = t;
       }
-    l_i = l_i * alpha + psum;
-    m_i = m_new;
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc_o[db][j] *= alpha;
-    }
+    l_i += psum;
     // O^T += V^T P^T over 4 k-steps of 16 keys
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -314,6 +331,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[s], acc_o[db], 0, 0, 0);
       }
     }
+    if (idx_next) tile_index_commit(tt + 2, pend_rw, pend_b);
   }
 
   const float lsum = l_i + __shfl_xor(l_i, 32, 64);
