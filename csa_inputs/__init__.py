@@ -95,9 +95,10 @@ WORKLOADS = {
     # Wan2.1-14B-like: 21x60x60 grid, 500 components with Zipf(1.1) sizes.
     "wan": _w("wan", 1, 40, 21 * 60 * 60, 128, 104, 500, [0.3] * 40, "zipf1.1", "", 0.0, (), (), 100,
               "Wan2.1-14B-like H=40 L=75600 d=128"),
-    # Long stress: 80% from 1000 components (weights j^-0.62), 20% Student-t(3) with per-head scale.
+    # Long stress: 80% from 1000 components (weights j^-0.62), 20% Student-t(3) with per-head
+    # scale in [0.15, 0.75]; the widest heads cannot be covered by N_max centres and fall back.
     "long": _w("long", 1, 24, 180000, 128, 105, 1000, [0.3] * 24, "pow0.62", "student3", 0.20,
-               np.linspace(0.5, 2.0, 24), range(24), 100, "long-sequence H=24 L=180000 d=128"),
+               np.linspace(0.15, 0.75, 24), range(24), 100, "long-sequence H=24 L=180000 d=128"),
 }
 
 

@@ -120,3 +120,132 @@ def attn_error(O_gpu: np.ndarray, O_ref: np.ndarray):
 
 ATTN_MAX_ABS = 2e-2
 ATTN_REL_L2 = 5e-3
+
+
+# ---------------------------------------------------------------- full-size sampled checks
+
+def workload_oracle_params(name: str, variant: str = "density", compensate: int = 0) -> nm.Params:
+    """The parameters bench.py times for a workload, as an oracle Params."""
+    import bench
+    kw = bench.workload_params(name, variant, compensate)
+    kw = {k: v for k, v in kw.items() if k in nm.Params.__dataclass_fields__}
+    return oracle_params(**kw)
+
+
+def check_clusters_sampled(r: "Run", Qb, Kb, Vb, rows_seed: int, nrows: int = 2048, tau_invariant: bool = True):
+    """Stage-wise checks of the clustering outputs of every head, given the
+    GPU's own earlier stages.  Returns a summary dict; raises on a failure."""
+    from oracle import kmeans as okm
+    from oracle import stats as ost
+    B, H, L, d = Qb.shape
+    BH = B * H
+    Qf, Kf, Vf = (x.reshape(BH, L, d) for x in (Qb, Kb, Vb))
+    qlab, qperm, qseg, qcent = (np_(t) for t in (r.q.labels, r.q.perm, r.q.seg, r.q.cent))
+    klab, kperm, kseg, kcent, ncl = (np_(t) for t in (r.k.labels, r.k.perm, r.k.seg, r.k.cent, r.k.ncl))
+    fb, tau, mse = np_(r.st.fallback), np_(r.st.tau), np_(r.st.mse)
+    kmax, kmin = bf16_dev_to_f64(r.st.kmax), bf16_dev_to_f64(r.st.kmin)
+    kmean, vmean = np_(r.st.kmean), np_(r.st.vmean)
+    rows = gen.row_sample(L, nrows, rows_seed)
+    out = dict(label_flips=0, label_ties=0, fallback=int(fb.sum()), ncl=ncl.tolist())
+    for h in range(BH):
+        nk = int(ncl[h])
+        assert 1 <= nk <= r.ncap_k
+        # query labels: nearest centre of the sampled rows (normalised queries)
+        Xq = nm.bf16_to_f64(okm.normalize_queries(Qf[h][rows]))
+        bad, flips, ties = near_tie_flips(Xq, qcent[h].astype(np.float64), qlab[h][rows])
+        assert bad == 0, (h, "query labels", bad)
+        out["label_flips"] += flips
+        out["label_ties"] += ties
+        # key labels: nearest over all of C
+        Xk = nm.bf16_to_f64(Kf[h][rows])
+        C = kcent[h, :nk].astype(np.float64)
+        bad, flips, ties = near_tie_flips(Xk, C, klab[h][rows])
+        assert bad == 0, (h, "key labels", bad)
+        out["label_flips"] += flips
+        out["label_ties"] += ties
+        # Algorithm 1 invariant: without fallback every key is within tau of a centre
+        if tau_invariant and not fb[h]:
+            dmin = np.sqrt(np.min(okm.sq_dist(Xk, C), axis=1))
+            assert np.all(dmin < tau[h] * (1 + 1e-5)), (h, "tau invariant")
+        elif fb[h]:
+            assert nk >= r.p.nmax
+        # permutations and segments: bit-exact
+        for lab, perm, seg, m in ((qlab[h], qperm[h], qseg[h], r.nq), (klab[h], kperm[h], kseg[h], nk)):
+            perm_o, seg_o = ost.counting_sort(lab, m)
+            assert np.array_equal(perm, perm_o), (h, "perm")
+            assert np.array_equal(seg[:m + 1], seg_o), (h, "seg")
+        # statistics of every key cluster
+        st = ost.key_stats(Kf[h], Vf[h], klab[h], C)
+        assert np.array_equal(kmax[h, :nk], st["kmax"]) and np.array_equal(kmin[h, :nk], st["kmin"]), (h, "max/min")
+        scale_k = max(1.0, float(np.max(np.abs(st["kmean"]))))
+        assert np.max(np.abs(kmean[h, :nk] - st["kmean"])) <= 1e-5 * scale_k, (h, "kmean")
+        assert np.max(np.abs(vmean[h, :nk] - st["vmean"])) <= 1e-5 * max(1.0, float(np.max(np.abs(st["vmean"])))), h
+        assert abs(mse[h] - st["mse"]) <= 1e-4 * st["mse"], (h, "mse")
+    assert out["label_flips"] <= 0.001 * 2 * BH * rows.size
+    return out
+
+
+def check_scores_selection(r: "Run", p: nm.Params):
+    """Scores against the oracle's eq. (1) from the GPU's centres and
+    statistics; selections against the oracle's selection from the GPU's
+    scores (differences only between near-equal scores / masses)."""
+    from oracle import score as osc
+    BH = r.BH
+    cq = np_(r.q.cent).astype(np.float64)
+    kmax, kmin = bf16_dev_to_f64(r.st.kmax), bf16_dev_to_f64(r.st.kmin)
+    kmean = np_(r.st.kmean).astype(np.float64)
+    kseg, ncl, rho = np_(r.k.seg), np_(r.k.ncl), np_(r.q.rho)
+    S = np_(r.sel.score)
+    lst, n = np_(r.sel.list), np_(r.sel.n)
+    ties = 0
+    for h in range(BH):
+        nk = int(ncl[h])
+        count = np.diff(kseg[h])[:nk]
+        if p.score_mode == nm.SCORE_QUEST:
+            So = osc.quest_scores(cq[h], kmax[h, :nk], kmin[h, :nk], count)
+        else:
+            So = osc.mean_scores(cq[h], kmean[h, :nk], count)
+        fin = np.isfinite(So)
+        assert np.array_equal(fin, np.isfinite(S[h, :, :nk])), h
+        amax = np.max(np.abs(So[fin]))
+        assert np.max(np.abs(S[h, :, :nk][fin] - So[fin])) <= 1e-5 * amax, h
+        for q in range(r.nq):
+            g = lst[h, q, :n[h, q]].tolist()
+            o = osc.select_row(S[h, q, :nk].astype(np.float64), count, float(rho[h, q]), r.L, r.d, p).tolist()
+            if g != o:
+                diff = set(g) ^ set(o)
+                cut = S[h, q, o[-1]]
+                near = all(abs(S[h, q, c] - cut) < 1e-5 * amax for c in diff)
+                assert near or p.sel_mode == nm.SEL_TOPP, (h, q, "selection")
+                ties += 1
+    return ties
+
+
+def check_attention_sampled(r: "Run", Qb, Kb, Vb, p: nm.Params, rows_seed: int, nrows: int = 2048):
+    """Attention of a seeded sample of query rows per head against the fp64
+    oracle given the GPU's clusters and selection."""
+    from oracle import stats as ost
+    from oracle import attention as oat
+    B, H, L, d = Qb.shape
+    BH = B * H
+    Qf, Kf, Vf = (x.reshape(BH, L, d) for x in (Qb, Kb, Vb))
+    O = bf16_dev_to_f64(r.O).reshape(BH, L, d)
+    qlab, klab, ncl, fb = np_(r.q.labels), np_(r.k.labels), np_(r.k.ncl), np_(r.st.fallback)
+    lst, n = np_(r.sel.list), np_(r.sel.n)
+    rows = gen.row_sample(L, nrows, rows_seed)
+    worst = (0.0, 0.0)
+    for h in range(BH):
+        Qx, Kx, Vx = (nm.bf16_to_f64(x[h]) for x in (Qf, Kf, Vf))
+        if fb[h] or p.sel_mode == nm.SEL_DENSE:
+            Oo = np.concatenate([oat.dense_rows(Qx, Kx, Vx, rows[i:i + 256], p.attn_scale(d))[0]
+                                 for i in range(0, rows.size, 256)])
+        else:
+            nk = int(ncl[h])
+            st = ost.key_stats(Kf[h], Vf[h], klab[h], np.zeros((nk, d)))
+            sel = [lst[h, q, :n[h, q]] for q in range(r.nq)]
+            Oo, _ = oat.sparse_rows(Qx, Kx, Vx, rows, qlab[h], klab[h], sel, p.attn_scale(d), bool(p.compensate),
+                                    st["count"], st["kmean"], st["vmean"])
+        mx, rl2 = attn_error(O[h][rows], Oo)
+        assert mx <= ATTN_MAX_ABS and rl2 <= ATTN_REL_L2, (h, mx, rl2)
+        worst = (max(worst[0], mx), max(worst[1], rl2))
+    return worst
