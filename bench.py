@@ -187,6 +187,44 @@ def sdpa_ms(Qd, Kd, Vd, reps=3):
         return None
 
 
+ATTN_SRC = os.path.join(ROOT, "clustered_sparse_attention_amd", "csrc", "attn.hip")
+TRAFFIC = os.path.join(ROOT, "profiles", "k_attn_wan_traffic.json")
+
+
+def attn_source_hash() -> str:
+    import hashlib
+    return hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+
+
+def measured_traffic(workload: str, variant: str, compensate: int):
+    """HBM bytes per k_attn launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's
+    reading for a plain copy of known size), or None when the summary is for
+    another workload or the kernel source changed since it was taken."""
+    try:
+        t = json.load(open(TRAFFIC))
+    except (OSError, ValueError):
+        return None
+    if t.get("attn_source_sha256") != attn_source_hash():
+        return None
+    if (t.get("workload"), t.get("variant"), t.get("compensate")) != (workload, variant, compensate):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def copy_probe(nbytes: int):
+    """A plain device copy of nbytes (torch), for calibrating the HBM byte
+    counters: its FETCH_SIZE / WRITE_SIZE should read nbytes each."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -198,7 +236,11 @@ def main():
     ap.add_argument("--heads", type=int, default=0, help="run only this many heads (0 = all)")
     ap.add_argument("--no-baselines", action="store_true", help="skip dense baselines and the CPU oracle")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, help="only run a plain copy of this many bytes")
     args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (heads shard across GPUs by design "
               "only); run with --gpus 1", file=sys.stderr)
@@ -267,7 +309,8 @@ def main():
                    "selection": args.variant, "compensate": args.compensate,
                    "params": {k: (round(v, 6) if isinstance(v, float) else v) for k, v in kw.items()}},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(args.workload, args.variant, args.compensate),
                      "kernel": "k_attn (block-sparse attention)",
                      "algorithmic_flops_per_launch": attn_flops, "avg_launch_ms": round(attn_ms, 4)},
         "phase_ms": {"cluster_q": round(float(phase_ms[0]), 3), "cluster_k": round(float(phase_ms[1]), 3),

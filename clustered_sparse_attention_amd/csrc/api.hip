@@ -93,10 +93,10 @@ ac_status check_params(const ac_shape *s, const ac_params *p) {
 // ---------------------------------------------------------------------------
 // workspace plan: every region any entry point uses, at fixed offsets
 struct Plan {
-  int BH, L, D, nq, ncapk, mcap, max_tiles, nq_pad, ncap_pad, mwords;
+  int BH, L, D, nq, ncapk, mcap, max_tiles, max_groups, nq_pad, ncap_pad, mwords;
   size_t total = 0;
   // scratch
-  size_t qhat, qn, lab, lperm, lseg, thist, ops_hi, ops_lo, ops_norm, d2buf, hn, hm, hcoff, hnew;
+  size_t qhat, qn, lab, lperm, lseg, thist, tgrp, ops_hi, ops_lo, ops_norm, d2buf, hn, hm, hcoff, hnew;
   size_t uidx0, uidx1, dist, flag, rstate, rhist, msepart, chunk_off, upd_part, kpp_nx, kpp_G;
   int kpp_smax;
   int upd_items;
@@ -117,6 +117,7 @@ Plan make_plan(const ac_shape *s, const ac_params *p) {
   P.ncapk = p->nmax - 1 + p->m0;
   P.mcap = std::max({P.ncapk, P.nq, 2});
   P.max_tiles = (int)cdiv(P.L, SORT_TILE);
+  P.max_groups = (int)cdiv(P.max_tiles, SORT_GROUP);
   P.nq_pad = (int)cdiv(P.nq, 16) * 16;
   P.ncap_pad = (int)cdiv(P.ncapk, 16) * 16;
   P.mwords = (int)cdiv(P.ncapk, 32);
@@ -133,6 +134,7 @@ Plan make_plan(const ac_shape *s, const ac_params *p) {
   P.lperm = take(BH * L * 4);
   P.lseg = take(BH * (P.mcap + 1) * 4);
   P.thist = take(BH * P.max_tiles * (size_t)P.mcap * 4);
+  P.tgrp = take(BH * P.max_groups * (size_t)P.mcap * 4);
   P.ops_hi = take(BH * P.mcap * D * 2);
   P.ops_lo = take(BH * P.mcap * D * 2);
   P.ops_norm = take(BH * P.mcap * 4);
@@ -236,6 +238,8 @@ struct Engine {
     s.m = m();
     s.tile_hist = at<int>(ws, P.thist);
     s.max_tiles = P.max_tiles;
+    s.grp = at<int>(ws, P.tgrp);
+    s.max_groups = P.max_groups;
     s.mcap = std::max(mcap_used, 2);
     s.perm = perm;
     s.perm_hs = P.L;
@@ -261,14 +265,14 @@ struct Engine {
     AC_CHECK_LAUNCH();
     int *lab = at<int>(ws, P.lab);
     for (int it = 0; it < iters; ++it) {
-      launch_assign(D, a, op, P.BH, npts, lab, P.L, st);
+      launch_assign(D, a, op, P.BH, mmax, npts, lab, P.L, st);
       SortArgs s = sort_args(lab, at<int>(ws, P.lperm), at<int>(ws, P.lseg), P.mcap, mmax);
       launch_sort(s, P.BH, npts, st);
       launch_update(D, a, s, op, P.BH, mmax, npts, at<int>(ws, P.chunk_off), P.mcap + 1, at<double>(ws, P.upd_part),
                     (int64_t)P.upd_items * D, st);
       AC_CHECK_LAUNCH();
     }
-    launch_assign(D, a, op, P.BH, npts, labels_out, P.L, st);
+    launch_assign(D, a, op, P.BH, mmax, npts, labels_out, P.L, st);
     AC_CHECK_LAUNCH();
     return AC_OK;
   }
@@ -313,7 +317,7 @@ ac_status finish_keys(const Plan &P, const uint16_t *K, const uint16_t *V, ac_cl
   KmArgs a{K, (int64_t)L * D, nullptr, 0, E.n(), E.m(), E.coff(), k->cent, (int64_t)k->ncap * D};
   CentOps op = E.ops();
   launch_cent_prep(D, a, op, BH, mmax, st);
-  launch_assign(D, a, op, BH, L, k->labels, L, st);
+  launch_assign(D, a, op, BH, mmax, L, k->labels, L, st);
   SortArgs s = E.sort_args(k->labels, k->perm, k->seg, k->ncap, mmax);
   launch_sort(s, BH, L, st);
   KStatsArgs ks{K, V, k->perm, k->seg, k->ncl, k->cent, stats->kmax, stats->kmin, stats->kmean, stats->vmean,

@@ -65,8 +65,15 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   constexpr int DB = D / 32;         // 32-dim blocks of O
   constexpr int KROW = D + 8;        // padded K row (bf16)
   constexpr int VROW = ATT_KT + 8;   // padded V^T row (keys)
-  const int h = blockIdx.y;
-  const int blk = blockIdx.x;
+  // XCD-aware order: the hardware deals consecutive block ids round-robin to
+  // the 8 XCDs, so id -> work item w = (id % 8) * (N / 8) + id / 8 hands each
+  // XCD a contiguous run of work items; the query tiles of one query cluster
+  // (which stream the same key list) then share that XCD's L2.
+  const int nper = gridDim.x / 8;
+  const int w = (int)(blockIdx.x % 8) * nper + (int)(blockIdx.x / 8);
+  const int h = w / a.blocks_per_head;
+  const int blk = w % a.blocks_per_head;
+  if (h >= a.BH) return;
   const int nq = a.ncl_q[h];
   const int *toff = a.tile_off + (int64_t)h * (a.nqcap + 1);
   if (nq <= 0 || blk >= toff[nq]) return;
@@ -85,8 +92,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
 
   __shared__ uint16_t Ks[ATT_KT * KROW];
   __shared__ uint16_t Vt[D * VROW];
-  __shared__ int rowidx[3][ATT_KT];
-  __shared__ float sbias[3][ATT_KT];
+  __shared__ __align__(16) float sbias[4][3][ATT_KT];
   extern __shared__ int dyn[];
   int *s_cum = dyn;                       // [ncap + 1]
   int *s_start = dyn + (a.ncap + 1);      // [ncap]
@@ -164,58 +170,64 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   const int nt0 = (T + ATT_KT - 1) / ATT_KT;
   const int ntiles = nt0 + (comp ? (ncl_k + ATT_KT - 1) / ATT_KT : 0);
 
-  // row index and logit bias of every key of tile tt (threads 0..63), in two
-  // halves so that the dependent permutation load is in flight across the MFMAs
-  auto tile_index_issue = [&](int tt, float &bias) -> int {
+  // Key index pipeline, run by every wave for itself: lane l finds the row
+  // of key l of a tile (and its logit bias) two tiles ahead.  The loads it
+  // needs are unconditional and their results are first used at the end of
+  // the iteration, so their latency hides behind the tile's MFMAs.  Tiles
+  // advance monotonically through the selection, so a cursor replaces a
+  // search: the cluster holding a key is found by stepping forward from the
+  // cluster that held the previous tile's last key.
+  int cur = 0;
+  auto index_issue = [&](int tt, int &raw, float &braw) {
     const bool ph1 = tt >= nt0;
-    const int o = (ph1 ? tt - nt0 : tt) * ATT_KT + tid;
-    const int total = ph1 ? ncl_k : T;
-    int rw = -1;
-    bias = -__builtin_inff();
-    if (o < total) {
-      bias = 0.f;
-      if (ph1) {
-        rw = o;
-        const bool selected = (s_mask[o >> 5] >> (o & 31)) & 1u;
-        bias = selected ? -__builtin_inff() : a.lb[(int64_t)h * a.ncap + o];
-      } else if (dense) {
-        rw = o;
-      } else {
-        int lo2 = 0, hi2 = nsel;  // s_cum[lo2] <= o < s_cum[hi2]
-        while (hi2 - lo2 > 1) {
-          const int mid = (lo2 + hi2) >> 1;
-          if (s_cum[mid] <= o) lo2 = mid; else hi2 = mid;
-        }
-        rw = permk[s_start[lo2] + (o - s_cum[lo2])];
-      }
+    const int o = (ph1 ? tt - nt0 : tt) * ATT_KT + lane;
+    int pos = min(o, a.L - 1);
+    if (!ph1 && !dense) {
+      const int oc = min(o, T - 1);
+      int c = cur;
+      while (c + 1 < nsel && s_cum[c + 1] <= oc) ++c;
+      pos = s_start[c] + (oc - s_cum[c]);
+      cur = __shfl(c, 63, 64);
     }
-    return rw;
+    raw = permk[pos];
+    braw = comp ? a.lb[(int64_t)h * a.ncap + min(o, a.ncap - 1)] : 0.f;
   };
-  auto tile_index_commit = [&](int tt, int rw, float bias) {
-    rowidx[tt % 3][tid] = rw;
-    sbias[tt % 3][tid] = bias;
+  // final row (-1: masked) and bias of key `lane` of tile tt
+  auto index_commit = [&](int tt, int raw, float braw, float *bias_dst) -> int {
+    const bool ph1 = tt >= nt0;
+    const int o = (ph1 ? tt - nt0 : tt) * ATT_KT + lane;
+    const int total = ph1 ? ncl_k : T;
+    int rw = ph1 ? o : (dense ? o : raw);
+    float bias = 0.f;
+    if (ph1) {
+      const bool selected = (s_mask[min(o, a.ncap - 1) >> 5] >> (o & 31)) & 1u;
+      bias = selected ? -__builtin_inff() : braw;
+    }
+    if (o >= total) { rw = -1; bias = -__builtin_inff(); }
+    bias_dst[lane] = bias;
+    return rw;
   };
 
   constexpr int KCH = (ATT_KT * D / 8) / 256;      // 16-byte K pieces per thread
   constexpr int VCH = (ATT_KT / 2 * D / 8) / 256;  // V key pairs x 8 dims per thread
   u32x4_t kreg[KCH], vreg[VCH][2];
-  auto load_tile = [&](int tt) {
+  // rows come from lane (key) of this wave's index registers
+  auto load_tile = [&](int tt, int rwv) {
     const bool ph1 = tt >= nt0;
     const uint16_t *Kp = ph1 ? Kc : Kh;
     const uint16_t *Vp = ph1 ? Vc : Vh;
-    const int *ri = rowidx[tt % 3];
 #pragma unroll
     for (int it = 0; it < KCH; ++it) {
       const int q = tid + it * 256;
       const int rr = q / (D / 8), cc = (q % (D / 8)) * 8;
-      const int rw = max(ri[rr], 0);  // masked keys (-1) read row 0: their logit bias is -inf
+      const int rw = max(__shfl(rwv, rr, 64), 0);  // masked keys (-1) read row 0: their bias is -inf
       kreg[it] = *(const u32x4_t *)&Kp[(int64_t)rw * D + cc];
     }
 #pragma unroll
     for (int it = 0; it < VCH; ++it) {
       const int q = tid + it * 256;
       const int kp = q % (ATT_KT / 2), dc = q / (ATT_KT / 2);
-      const int r0 = max(ri[2 * kp], 0), r1 = max(ri[2 * kp + 1], 0);
+      const int r0 = max(__shfl(rwv, 2 * kp, 64), 0), r1 = max(__shfl(rwv, 2 * kp + 1, 64), 0);
       vreg[it][0] = *(const u32x4_t *)&Vp[(int64_t)r0 * D + dc * 8];
       vreg[it][1] = *(const u32x4_t *)&Vp[(int64_t)r1 * D + dc * 8];
     }
@@ -239,58 +251,73 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     }
   };
 
-  if (tid < ATT_KT) {
-    for (int tt = 0; tt < 2 && tt < ntiles; ++tt) {
-      float b;
-      const int rw = tile_index_issue(tt, b);
-      tile_index_commit(tt, rw, b);
+  float *sbw = &sbias[wave][0][0];  // this wave's bias rows, one per tile mod 3
+  int rw_next = -1;                 // row of key `lane` of tile tt + 1
+  if (ntiles > 0) {
+    int raw;
+    float braw;
+    index_issue(0, raw, braw);
+    const int rw0 = index_commit(0, raw, braw, sbw);
+    if (ntiles > 1) {
+      index_issue(1, raw, braw);
+      rw_next = index_commit(1, raw, braw, sbw + ATT_KT);
     }
+    load_tile(0, rw0);
   }
-  __syncthreads();
-  if (ntiles > 0) load_tile(0);
 
   // key slot l32 of each 32-key block holds tile key 16*(a/2) + 8*gg + 4*(a%2) + b, l32 = 8a + 4gg + b
   const int kslot = 16 * ((l32 >> 3) >> 1) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
 
   for (int tt = 0; tt < ntiles; ++tt) {
-    __syncthreads();  // the previous tile is consumed; this tile's row indices are visible
+    __syncthreads();  // the previous tile is consumed
     store_tile();
     __syncthreads();
-    if (tt + 1 < ntiles) load_tile(tt + 1);  // in flight during this tile's MFMAs
-    const bool idx_next = tid < ATT_KT && tt + 2 < ntiles;
-    int pend_rw = -1;
+    if (tt + 1 < ntiles) load_tile(tt + 1, rw_next);  // in flight during this tile's MFMAs
+    const bool idx_next = tt + 2 < ntiles;
+    int pend_raw = 0;
     float pend_b = 0.f;
-    if (idx_next) pend_rw = tile_index_issue(tt + 2, pend_b);
+    if (idx_next) index_issue(tt + 2, pend_raw, pend_b);
 
-    // S^T for two 32-key blocks
+    // S^T for two 32-key blocks (the two accumulation chains interleaved)
     f32x16_t acc_s[2];
+    acc_s[0] = (f32x16_t){};
+    acc_s[1] = (f32x16_t){};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      acc_s[kb] = (f32x16_t){};
-      const int key = 32 * kb + kslot;
+    for (int ks = 0; ks < KSQ; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < KSQ; ++ks) {
-        const bf16x8_t kf = *(const bf16x8_t *)&Ks[key * KROW + ks * 16 + g * 8];
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8_t kf = *(const bf16x8_t *)&Ks[(32 * kb + kslot) * KROW + ks * 16 + g * 8];
         acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], acc_s[kb], 0, 0, 0);
       }
     }
-    // scores in base-2 units: s * scale * log2(e) + bias (0, -inf for masked
-    // keys, log2 n_c for pseudo-keys)
-    const float *bz = sbias[tt % 3];
+    // scores in base-2 units: s * scale * log2(e) + bias.  Full tiles of
+    // selected keys carry no bias: the row max is taken on the raw products
+    // and the scale and max subtraction fold into one FMA per score.
+    // Tail and pseudo-key tiles add the bias (-inf masked, log2 n_c).
+    const bool biased = tt >= nt0 - 1;
     float mt = -__builtin_inff();
+    if (biased) {
+      const float *bz = sbw + (tt % 3) * ATT_KT;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const f32x4_t b0 = *(const f32x4_t *)&bz[32 * kb + 16 * half + 8 * g];
-        const f32x4_t b1 = *(const f32x4_t *)&bz[32 * kb + 16 * half + 8 * g + 4];
+        for (int half = 0; half < 2; ++half) {
+          const f32x4_t b0 = *(const f32x4_t *)&bz[32 * kb + 16 * half + 8 * g];
+          const f32x4_t b1 = *(const f32x4_t *)&bz[32 * kb + 16 * half + 8 * g + 4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float sv = fmaf(acc_s[kb][half * 8 + i], sl2, i < 4 ? b0[i] : b1[i - 4]);
-          acc_s[kb][half * 8 + i] = sv;
-          mt = fmaxf(mt, sv);
+          for (int i = 0; i < 8; ++i) {
+            const float sv = fmaf(acc_s[kb][half * 8 + i], sl2, i < 4 ? b0[i] : b1[i - 4]);
+            acc_s[kb][half * 8 + i] = sv;
+            mt = fmaxf(mt, sv);
+          }
         }
-      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mt = fmaxf(mt, acc_s[kb][j]);
+      mt *= sl2;
+    }
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     // lazy rescale: the reference max m_i may trail the running max by up to
     // 2^8, so p <= 256; O and l are rescaled only when a row outgrows that
@@ -305,6 +332,8 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
       m_i = m_new;
     }
     const float m_use = m_i == -__builtin_inff() ? 0.f : m_i;
+    // biased: exp2(s - m); unbiased: exp2(acc * sl2 - m) as one FMA
+    const float mul = biased ? 1.f : sl2;
     float psum = 0.f;
     bf16x8_t pb[4];
 #pragma unroll
@@ -314,7 +343,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         bf16x8_t t;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(acc_s[kb][half * 8 + i] - m_use);
+          const float pv = __builtin_amdgcn_exp2f(fmaf(acc_s[kb][half * 8 + i], mul, -m_use));
           psum += pv;
           t[i] = (__bf16)pv;
         }
@@ -331,7 +360,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[s], acc_o[db], 0, 0, 0);
       }
     }
-    if (idx_next) tile_index_commit(tt + 2, pend_rw, pend_b);
+    if (idx_next) rw_next = index_commit(tt + 2, pend_raw, pend_b, sbw + ((tt + 2) % 3) * ATT_KT);
   }
 
   const float lsum = l_i + __shfl_xor(l_i, 32, 64);
@@ -362,10 +391,14 @@ void launch_attn_prep(int D, const AttnArgs &a, const float *kmean, const float 
 
 void launch_attn(int D, const AttnArgs &a, int BH, int max_blocks, hipStream_t st) {
   size_t dyn = (size_t)(2 * a.ncap + 1 + a.mwords) * sizeof(int);
+  AttnArgs aa = a;
+  aa.blocks_per_head = max_blocks;
+  aa.BH = BH;
+  const long long total = ((long long)max_blocks * BH + 7) / 8 * 8;  // a multiple of the 8 XCDs
   if (D == 64)
-    hipLaunchKernelGGL(k_attn<64>, dim3(max_blocks, BH), dim3(256), dyn, st, a);
+    hipLaunchKernelGGL(k_attn<64>, dim3((unsigned)total), dim3(256), dyn, st, aa);
   else
-    hipLaunchKernelGGL(k_attn<128>, dim3(max_blocks, BH), dim3(256), dyn, st, a);
+    hipLaunchKernelGGL(k_attn<128>, dim3((unsigned)total), dim3(256), dyn, st, aa);
 }
 
 }  // namespace ac

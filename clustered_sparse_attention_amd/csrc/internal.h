@@ -8,10 +8,12 @@ namespace ac {
 
 constexpr int KPP_SMAX = 16384;  // most points a k-means++ subsample may hold
 constexpr int KPP_GRAM_MAX = 2048;  // subsamples up to this size seed from a distance matrix
-constexpr int SORT_TILE = 512;   // points per counting-sort tile (one wave)
+constexpr int SORT_TILE = 128;   // points per counting-sort tile (one wave)
+constexpr int SORT_GROUP = 32;   // tiles per group in the two-level scan over tiles
 constexpr int ATT_QT = 128;      // query rows per attention block
 constexpr int ATT_KT = 64;       // keys per attention tile
 constexpr int SEL_MAXN = 4096;   // most key clusters the select kernel sorts
+constexpr int ASSIGN_RES_MAX = 224;  // most centres the LDS-resident assignment holds
 constexpr int UPD_CHUNK = 256;   // members per block in the centre update
 
 enum { TAU_RULE_MEAN_X = 0, TAU_RULE_PCTL = 1, TAU_RULE_ABS = 2, TAU_RULE_INF = 3 };
@@ -45,6 +47,8 @@ struct SortArgs {
   int *tile_hist;     // [BH, max_tiles, mcap]
   int max_tiles;
   int mcap;
+  int *grp;           // [BH, max_groups, mcap] per-group label offsets
+  int max_groups;
   int *perm;          // [BH, perm_hs]
   int64_t perm_hs;
   int *seg;           // [BH, seg_hs], entries 0..segcap written
@@ -117,6 +121,8 @@ struct AttnArgs {
   float *lse;                 // [BH, L] or NULL
   int L;
   float scale_log2;           // scale * log2(e)
+  int blocks_per_head;        // grid layout (set by the launcher)
+  int BH;
 };
 
 // kmeans.hip
@@ -126,7 +132,7 @@ void launch_kpp(int D, const KmArgs &a, int BH, double *d2buf, int init_sample, 
 void launch_kpp_gram(int D, const KmArgs &a, int BH, int smax, double *nx, double *G, int init_sample, uint64_t seed,
                      int role, int stage, hipStream_t st);
 void launch_cent_prep(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, hipStream_t st);
-void launch_assign(int D, const KmArgs &a, const CentOps &op, int BH, int nmax_pts, int *labels, int64_t lab_hs,
+void launch_assign(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, int nmax_pts, int *labels, int64_t lab_hs,
                    hipStream_t st);
 void launch_sort(const SortArgs &s, int BH, int nmax_pts, hipStream_t st);
 void launch_update(int D, const KmArgs &a, const SortArgs &s, const CentOps &op, int BH, int mmax, int npts,

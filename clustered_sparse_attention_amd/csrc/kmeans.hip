@@ -7,6 +7,8 @@
 // head h is row idx[h][i] (or row i when idx is NULL) of X[h], there are n[h]
 // points and m[h] centres, stored at cent[h][coff[h] + c].  Heads with n = 0
 // or m = 0 are idle.  Every launch covers all heads (grid.y = head).
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -186,11 +188,129 @@ __global__ __launch_bounds__(256) void k_assign(KmArgs a, CentOps op, int *__res
     }
 }
 
+// Same result as k_assign for m <= ASSIGN_RES_MAX, organised for HBM rate:
+// every head's centres stay resident in LDS while a block walks a contiguous
+// range of the flattened (head, 64-point sub-tile) list, one sub-tile per
+// wave at a time.  Blocks are sized to one per compute unit, so there is no
+// per-tile barrier and each wave's point loads overlap the other waves'
+// MFMA work.
+template <int D>
+__global__ __launch_bounds__(1024) void k_assign_res(KmArgs a, CentOps op, int *__restrict__ labels, int64_t lab_hs,
+                                                     int BH) {
+  constexpr int KS = D / 32;
+  constexpr int LDSROW = D + 8;
+  __shared__ uint16_t s_hi[ASSIGN_RES_MAX * LDSROW];
+  __shared__ uint16_t s_lo[ASSIGN_RES_MAX * LDSROW];
+  __shared__ __align__(16) float s_norm[ASSIGN_RES_MAX];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l16 = lane & 15, g = lane >> 4;
+  // this block's share of the flattened sub-tile list
+  int64_t total = 0;
+  for (int h = 0; h < BH; ++h) total += (a.n[h] > 0 && a.m[h] > 0) ? (a.n[h] + 63) / 64 : 0;
+  const int64_t per = (total + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * per, hi = min(total, lo + per);
+  if (lo >= hi) return;
+  int64_t hb = 0;  // first flattened sub-tile of head h
+  for (int h = 0; h < BH && hb < hi; ++h) {
+    const int n = a.n[h], m = a.m[h];
+    const int nsub = (n > 0 && m > 0) ? (n + 63) / 64 : 0;
+    const int64_t he = hb + nsub;
+    const int64_t r0 = max(lo, hb), r1 = min(hi, he);
+    if (r0 < r1) {
+      const int mp = (m + 15) & ~15;
+      const uint16_t *ghi = op.hi + (int64_t)h * op.cap * D;
+      const uint16_t *glo = op.lo + (int64_t)h * op.cap * D;
+      const float *gnorm = op.norm + (int64_t)h * op.cap;
+      __syncthreads();  // previous head's centres no longer read
+      for (int q = threadIdx.x; q < mp * (D / 8); q += 1024) {
+        const int r = q / (D / 8), cc = (q % (D / 8)) * 8;
+        u32x4_t vh = {0, 0, 0, 0}, vl = {0, 0, 0, 0};
+        if (r < m) {
+          vh = *(const u32x4_t *)&ghi[(int64_t)r * D + cc];
+          vl = *(const u32x4_t *)&glo[(int64_t)r * D + cc];
+        }
+        *(u32x4_t *)&s_hi[r * LDSROW + cc] = vh;
+        *(u32x4_t *)&s_lo[r * LDSROW + cc] = vl;
+      }
+      for (int c = threadIdx.x; c < mp; c += 1024) s_norm[c] = c < m ? gnorm[c] : 0.f;
+      __syncthreads();
+      const uint16_t *X = a.X + (int64_t)h * a.x_hs;
+      const int *idx = a.idx ? a.idx + (int64_t)h * a.idx_hs : nullptr;
+      for (int64_t t = r0 + wave; t < r1; t += 16) {
+        const int wbase = (int)(t - hb) * 64;
+        bf16x8_t af[4][KS];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const int i = wbase + rt * 16 + l16;
+          if (i < n) {
+            const int64_t row = idx ? (int64_t)idx[i] : (int64_t)i;
+            const uint16_t *xr = X + row * D;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) af[rt][ks] = *(const bf16x8_t *)&xr[ks * 32 + g * 8];
+          } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) af[rt][ks] = (bf16x8_t){};
+          }
+        }
+        // centres in the A slot, points in B: lane holds point l16 of each
+        // row tile and centres 4g..4g+3 of the centre tile, so the running
+        // argmin is one value per row tile and lane.
+        float best[4];
+        int bidx[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) { best[rt] = __builtin_inff(); bidx[rt] = 0x7fffffff; }
+#pragma unroll 1
+        for (int ct = 0; ct < mp / 16; ++ct) {
+          f32x4_t acc[4];
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) acc[rt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+          const int crow = ct * 16 + l16;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8_t bh = *(const bf16x8_t *)&s_hi[crow * LDSROW + ks * 32 + g * 8];
+            const bf16x8_t bl = *(const bf16x8_t *)&s_lo[crow * LDSROW + ks * 32 + g * 8];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+              acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh, af[rt][ks], acc[rt], 0, 0, 0);
+              acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl, af[rt][ks], acc[rt], 0, 0, 0);
+            }
+          }
+          const int c0 = ct * 16 + 4 * g;
+          const f32x4_t cn2 = *(const f32x4_t *)&s_norm[c0];
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float dv = (c0 + j < m) ? fmaf(-2.f, acc[rt][j], cn2[j]) : __builtin_inff();
+              if (dv < best[rt]) { best[rt] = dv; bidx[rt] = c0 + j; }
+            }
+        }
+        // reduce over the four lane groups that hold the same point
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          float bv = best[rt];
+          int bi = bidx[rt];
+#pragma unroll
+          for (int o = 16; o < 64; o <<= 1) {
+            const float ov = __shfl_xor(bv, o, 64);
+            const int oi = __shfl_xor(bi, o, 64);
+            if (ov < bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+          }
+          const int i = wbase + rt * 16 + l16;
+          if (g == 0 && i < n) labels[(int64_t)h * lab_hs + i] = bi == 0x7fffffff ? 0 : bi;
+        }
+      }
+    }
+    hb = he;
+  }
+}
+
 // ---------------------------------------------------------------------------
-// Stable counting sort of per-head labels in [0, m): tile histograms, a scan
-// over tiles and labels, then an in-order scatter of each tile by one wave.
-// perm[h][p] = local index of the p-th point in label order; seg[h][c] the
-// first position of label c, seg[h][c] = n for m <= c <= segcap.
+// Stable counting sort of per-head labels in [0, m): tile histograms, a
+// two-level scan (tiles within groups of SORT_GROUP, then groups and labels),
+// and an in-order scatter of each tile by one wave.  perm[h][p] = local index
+// of the p-th point in label order; seg[h][c] the first position of label c,
+// seg[h][c] = n for m <= c <= segcap.
 __global__ __launch_bounds__(64) void k_sort_hist(SortArgs s) {
   const int h = blockIdx.y, tile = blockIdx.x;
   const int n = s.n[h], m = s.m[h];
@@ -207,22 +327,48 @@ __global__ __launch_bounds__(64) void k_sort_hist(SortArgs s) {
   for (int c = threadIdx.x; c < m; c += 64) th[c] = sh_hist[c];
 }
 
+// Exclusive scan of each label's counts over the tiles of one group (in
+// place); the group's total goes to grp.  One thread per (group, label).
+__global__ __launch_bounds__(256) void k_sort_gscan(SortArgs s) {
+  const int g = blockIdx.x, h = blockIdx.y;
+  const int c = blockIdx.z * 256 + threadIdx.x;
+  const int n = s.n[h], m = s.m[h];
+  const int nt = (n + SORT_TILE - 1) / SORT_TILE;
+  const int t0 = g * SORT_GROUP;
+  if (c >= m || t0 >= nt) return;
+  const int t1 = min(nt, t0 + SORT_GROUP);
+  int *p = s.tile_hist + ((int64_t)h * s.max_tiles + t0) * s.mcap + c;
+  int v[SORT_GROUP];
+#pragma unroll
+  for (int t = 0; t < SORT_GROUP; ++t) v[t] = (t0 + t < t1) ? p[(int64_t)t * s.mcap] : 0;
+  int run = 0;
+#pragma unroll
+  for (int t = 0; t < SORT_GROUP; ++t) {
+    if (t0 + t < t1) p[(int64_t)t * s.mcap] = run;
+    run += v[t];
+  }
+  s.grp[((int64_t)h * s.max_groups + g) * s.mcap + c] = run;
+}
+
+// Per head: scan each label over the groups, then the label totals; grp
+// ends up holding the first output position of (group, label).
 __global__ __launch_bounds__(1024) void k_sort_scan(SortArgs s) {
   const int h = blockIdx.x;
   const int n = s.n[h], m = s.m[h];
   int *seg = s.seg + (int64_t)h * s.seg_hs;
   const int nt = (n + SORT_TILE - 1) / SORT_TILE;
+  const int ng = (nt + SORT_GROUP - 1) / SORT_GROUP;
+  int *grp = s.grp + (int64_t)h * s.max_groups * s.mcap;
   __shared__ int part[1024];
-  // per label: exclusive scan over tiles (in place) and the label total
   const int per = (m + 1023) / 1024;
   const int cb = min(m, (int)threadIdx.x * per), ce = min(m, cb + per);
   int tot_local = 0;
   for (int c = cb; c < ce; ++c) {
     int run = 0;
-    for (int t = 0; t < nt; ++t) {
-      int *p = s.tile_hist + ((int64_t)h * s.max_tiles + t) * s.mcap + c;
-      int v = *p;
-      *p = run;
+    for (int g = 0; g < ng; ++g) {
+      int *q = grp + (int64_t)g * s.mcap + c;
+      const int v = *q;
+      *q = run;
       run += v;
     }
     seg[c] = run;  // count for now
@@ -238,8 +384,9 @@ __global__ __launch_bounds__(1024) void k_sort_scan(SortArgs s) {
   }
   int run = part[threadIdx.x] - tot_local;
   for (int c = cb; c < ce; ++c) {
-    int v = seg[c];
+    const int v = seg[c];
     seg[c] = run;
+    for (int g = 0; g < ng; ++g) grp[(int64_t)g * s.mcap + c] += run;
     run += v;
   }
   for (int c = m + threadIdx.x; c <= s.segcap; c += 1024) seg[c] = max(n, 0);
@@ -247,41 +394,41 @@ __global__ __launch_bounds__(1024) void k_sort_scan(SortArgs s) {
     for (int c = threadIdx.x; c <= s.segcap; c += 1024) seg[c] = 0;
 }
 
+// One wave per tile.  Lanes holding the same label are found with one
+// ballot per label bit; each lane's rank among them is a popcount, and the
+// lowest such lane advances the label's cursor.  A wave's LDS operations
+// complete in program order, so no barrier is needed between batches.
 __global__ __launch_bounds__(64) void k_sort_scatter(SortArgs s) {
   const int h = blockIdx.y, tile = blockIdx.x;
   const int n = s.n[h], m = s.m[h];
   const int beg = tile * SORT_TILE;
   if (beg >= n || m <= 0) return;
   extern __shared__ int sh_base[];
-  const int *seg = s.seg + (int64_t)h * s.seg_hs;
+  const int *gb = s.grp + ((int64_t)h * s.max_groups + tile / SORT_GROUP) * s.mcap;
   const int *th = s.tile_hist + ((int64_t)h * s.max_tiles + tile) * s.mcap;
-  for (int c = threadIdx.x; c < m; c += 64) sh_base[c] = seg[c] + th[c];
+  for (int c = threadIdx.x; c < m; c += 64) sh_base[c] = gb[c] + th[c];
   __syncthreads();
   const int *lab = s.labels + (int64_t)h * s.lab_hs;
   int *perm = s.perm + (int64_t)h * s.perm_hs;
   const int end = min(n, beg + SORT_TILE);
   const int lane = threadIdx.x;
+  const int nb = m > 1 ? 32 - __builtin_clz((unsigned)(m - 1)) : 0;
   for (int i0 = beg; i0 < end; i0 += 64) {
     const int i = i0 + lane;
     const bool valid = i < end;
-    const int lb = valid ? lab[i] : -1;
-    uint64_t remaining = __ballot(valid);
-    int pos = 0;
-    while (remaining) {
-      const int leader = __ffsll((long long)remaining) - 1;
-      const int ll = __shfl(lb, leader, 64);
-      const uint64_t same = __ballot(lb == ll) & remaining;
-      const int basev = sh_base[ll];
-      if (lb == ll && valid) {
-        uint64_t lt = lane == 0 ? 0ull : (same & ((1ull << lane) - 1ull));
-        pos = basev + __popcll(lt);
-      }
-      __syncthreads();  // single-wave block: orders the LDS read before the update
-      if (lane == leader) sh_base[ll] = basev + __popcll(same);
-      __syncthreads();
-      remaining &= ~same;
+    const int lb = valid ? lab[i] : 0;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < nb; ++b) {
+      const bool bit = (lb >> b) & 1;
+      const uint64_t bb = __ballot(bit);
+      same &= bit ? bb : ~bb;
     }
-    if (valid) perm[pos] = i;
+    const uint64_t below = same & ((1ull << lane) - 1ull);
+    if (valid) {
+      const int basev = sh_base[lb];
+      perm[basev + __popcll(below)] = i;
+      if (below == 0) sh_base[lb] = basev + __popcll(same);
+    }
   }
 }
 
@@ -342,15 +489,31 @@ __global__ __launch_bounds__(256) void k_update_partial(KmArgs a, SortArgs s, co
   double acc[PL];
 #pragma unroll
   for (int k = 0; k < PL; ++k) acc[k] = 0.0;
-  for (int p = beg + grp; p < end; p += 16) {
-    const int li = perm[p];
-    const int64_t row = idx ? (int64_t)idx[li] : (int64_t)li;
-    const uint16_t *xr = X + row * D + sub * PL;
-    uint16_t xv[PL];
-    if (PL == 8) *(u32x4_t *)xv = *(const u32x4_t *)xr;
-    else *(u32x2_t *)xv = *(const u32x2_t *)xr;
+  typedef uint32_t pw_t __attribute__((ext_vector_type(PL / 2)));
+  // four rows per lane in flight; rows are still added in member order
+  for (int p0 = beg + grp; p0 < end; p0 += 64) {
+    int li[4];
 #pragma unroll
-    for (int k = 0; k < PL; ++k) acc[k] += (double)bf2f(xv[k]);
+    for (int j = 0; j < 4; ++j) li[j] = (p0 + 16 * j < end) ? perm[p0 + 16 * j] : -1;
+    pw_t xv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (li[j] >= 0) {
+        const int64_t row = idx ? (int64_t)idx[li[j]] : (int64_t)li[j];
+        xv[j] = *(const pw_t *)(X + row * D + sub * PL);
+      } else {
+        xv[j] = (pw_t){};
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (li[j] < 0) break;
+#pragma unroll
+      for (int k = 0; k < PL; ++k) {
+        const uint32_t w = xv[j][k >> 1];
+        acc[k] += (double)bf2f((uint16_t)((k & 1) ? (w >> 16) : (w & 0xFFFFu)));
+      }
+    }
   }
   __shared__ double sh[16][D];
 #pragma unroll
@@ -399,27 +562,36 @@ __global__ __launch_bounds__(128) void k_update_final(KmArgs a, SortArgs s, cons
 
 // ---------------------------------------------------------------------------
 // Distance of each point of a stage to its own centre, ||x - c(x)|| (fp64
-// accumulation, stored fp32).  One wave per point.
+// accumulation, stored fp32).  16 lanes per point, 16 points per block.
 template <int D>
 __global__ __launch_bounds__(256) void k_stage_dist(KmArgs a, const int *__restrict__ labels, int64_t lab_hs,
                                                     float *__restrict__ dist, int64_t dist_hs) {
+  constexpr int PL = D / 16;
+  typedef uint32_t pw_t __attribute__((ext_vector_type(PL / 2)));
   const int h = blockIdx.y;
   const int n = a.n[h];
-  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (i >= n || a.m[h] <= 0) return;
-  const uint16_t *X = a.X + (int64_t)h * a.x_hs;
-  const int *idx = a.idx ? a.idx + (int64_t)h * a.idx_hs : nullptr;
-  int64_t row = idx ? (int64_t)idx[i] : (int64_t)i;
-  const int c = labels[(int64_t)h * lab_hs + i];
-  const float *cr = a.cent + (int64_t)h * a.cent_hs + (int64_t)(a.coff[h] + c) * D;
+  const int i = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  if (blockIdx.x * 16 >= n || a.m[h] <= 0) return;
   double acc = 0.0;
-  for (int dd = lane; dd < D; dd += 64) {
-    double df = (double)bf2f(X[row * D + dd]) - (double)cr[dd];
-    acc += df * df;
+  if (i < n) {
+    const uint16_t *X = a.X + (int64_t)h * a.x_hs;
+    const int64_t row = a.idx ? (int64_t)a.idx[(int64_t)h * a.idx_hs + i] : (int64_t)i;
+    const int c = labels[(int64_t)h * lab_hs + i];
+    const float *cr = a.cent + (int64_t)h * a.cent_hs + (int64_t)(a.coff[h] + c) * D + sub * PL;
+    const pw_t xv = *(const pw_t *)(X + row * D + sub * PL);
+#pragma unroll
+    for (int q = 0; q < PL; ++q) {
+      const uint32_t w = xv[q >> 1];
+      const double df = (double)bf2f((uint16_t)((q & 1) ? (w >> 16) : (w & 0xFFFFu))) - (double)cr[q];
+      acc = fma(df, df, acc);
+    }
   }
-  acc = wave_sum(acc);
-  if (lane == 0) dist[(int64_t)h * dist_hs + i] = (float)sqrt(acc);
+  acc += __shfl_xor(acc, 1, 64);
+  acc += __shfl_xor(acc, 2, 64);
+  acc += __shfl_xor(acc, 4, 64);
+  acc += __shfl_xor(acc, 8, 64);
+  if (i < n && sub == 0) dist[(int64_t)h * dist_hs + i] = (float)sqrt(acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -531,10 +703,12 @@ __global__ __launch_bounds__(256) void k_compact_gather(const int *__restrict__ 
 // and the cluster's share of sum ||k - c(k)||^2 (fp64).
 template <int D>
 __global__ __launch_bounds__(256) void k_kstats(KStatsArgs s) {
+  constexpr int PL = D / 16;  // dims per lane, 16 lanes per row
+  typedef uint32_t pw_t __attribute__((ext_vector_type(PL / 2)));
   const int h = blockIdx.y, c = blockIdx.x;
   const int ncl = s.ncl[h];
   const int64_t cb = ((int64_t)h * s.ncap + c);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int grp = threadIdx.x >> 4, sub = threadIdx.x & 15;
   if (c >= ncl) {
     if (c < s.ncap) {
       for (int dd = threadIdx.x; dd < D; dd += 256) {
@@ -551,52 +725,57 @@ __global__ __launch_bounds__(256) void k_kstats(KStatsArgs s) {
   const uint16_t *K = s.K + (int64_t)h * s.L * D;
   const uint16_t *V = s.V + (int64_t)h * s.L * D;
   const float *cent = s.cent + cb * D;
-  constexpr int PL = D / 64;
   double sk[PL], sv[PL], se = 0.0;
   float mx[PL], mn[PL], cc[PL];
 #pragma unroll
   for (int k = 0; k < PL; ++k) {
     sk[k] = 0.0; sv[k] = 0.0; mx[k] = -__builtin_inff(); mn[k] = __builtin_inff();
-    cc[k] = cent[lane * PL + k];
+    cc[k] = cent[sub * PL + k];
   }
-  for (int p = beg + wave; p < end; p += 4) {
-    int64_t row = perm[p];
-    const uint16_t *kr = K + row * D + lane * PL;
-    const uint16_t *vr = V + row * D + lane * PL;
+  for (int p = beg + grp; p < end; p += 16) {
+    const int64_t row = perm[p];
+    const pw_t kw = *(const pw_t *)(K + row * D + sub * PL);
+    const pw_t vw = *(const pw_t *)(V + row * D + sub * PL);
 #pragma unroll
     for (int k = 0; k < PL; ++k) {
-      float kv = bf2f(kr[k]), vv = bf2f(vr[k]);
+      const uint32_t a1 = kw[k >> 1], b1 = vw[k >> 1];
+      const float kv = bf2f((uint16_t)((k & 1) ? (a1 >> 16) : (a1 & 0xFFFFu)));
+      const float vv = bf2f((uint16_t)((k & 1) ? (b1 >> 16) : (b1 & 0xFFFFu)));
       sk[k] += (double)kv;
       sv[k] += (double)vv;
       mx[k] = fmaxf(mx[k], kv);
       mn[k] = fminf(mn[k], kv);
-      double df = (double)kv - (double)cc[k];
-      se += df * df;
+      const double df = (double)kv - (double)cc[k];
+      se = fma(df, df, se);
     }
   }
-  __shared__ double shk[4][D], shv[4][D];
-  __shared__ float shx[4][D], shn[4][D];
-  __shared__ double she[4];
+  __shared__ double shk[16][D], shv[16][D];
+  __shared__ float shx[16][D], shn[16][D];
+  __shared__ double she[256];
 #pragma unroll
   for (int k = 0; k < PL; ++k) {
-    shk[wave][lane * PL + k] = sk[k];
-    shv[wave][lane * PL + k] = sv[k];
-    shx[wave][lane * PL + k] = mx[k];
-    shn[wave][lane * PL + k] = mn[k];
+    shk[grp][sub * PL + k] = sk[k];
+    shv[grp][sub * PL + k] = sv[k];
+    shx[grp][sub * PL + k] = mx[k];
+    shn[grp][sub * PL + k] = mn[k];
   }
-  se = wave_sum(se);
-  if (lane == 0) she[wave] = se;
+  she[threadIdx.x] = se;
   __syncthreads();
   const int cnt = end - beg;
   if (threadIdx.x < D) {
     const int dd = threadIdx.x;
     if (cnt > 0) {
-      double a = ((shk[0][dd] + shk[1][dd]) + shk[2][dd]) + shk[3][dd];
-      double b = ((shv[0][dd] + shv[1][dd]) + shv[2][dd]) + shv[3][dd];
+      double a = 0.0, b = 0.0;
+      float x = -__builtin_inff(), y = __builtin_inff();
+#pragma unroll
+      for (int gg = 0; gg < 16; ++gg) {
+        a += shk[gg][dd];
+        b += shv[gg][dd];
+        x = fmaxf(x, shx[gg][dd]);
+        y = fminf(y, shn[gg][dd]);
+      }
       s.kmean[cb * D + dd] = (float)(a / cnt);
       s.vmean[cb * D + dd] = (float)(b / cnt);
-      float x = fmaxf(fmaxf(shx[0][dd], shx[1][dd]), fmaxf(shx[2][dd], shx[3][dd]));
-      float y = fminf(fminf(shn[0][dd], shn[1][dd]), fminf(shn[2][dd], shn[3][dd]));
       s.kmax[cb * D + dd] = (uint16_t)(__float_as_uint(x) >> 16);
       s.kmin[cb * D + dd] = (uint16_t)(__float_as_uint(y) >> 16);
     } else {
@@ -604,7 +783,11 @@ __global__ __launch_bounds__(256) void k_kstats(KStatsArgs s) {
       s.kmax[cb * D + dd] = 0; s.kmin[cb * D + dd] = 0;
     }
   }
-  if (threadIdx.x == 0) s.msepart[cb] = ((she[0] + she[1]) + she[2]) + she[3];
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int k = 0; k < 256; ++k) t += she[k];
+    s.msepart[cb] = t;
+  }
 }
 
 __global__ __launch_bounds__(256) void k_mse_reduce(const double *__restrict__ msepart, int ncap,
@@ -690,8 +873,26 @@ void launch_cent_prep(int D, const KmArgs &a, const CentOps &op, int BH, int mma
   AC_D_DISPATCH(D, hipLaunchKernelGGL(k_cent_prep<DD>, g2((mmax + 3) / 4, BH), dim3(256), 0, st, a, op));
 }
 
-void launch_assign(int D, const KmArgs &a, const CentOps &op, int BH, int nmax_pts, int *labels, int64_t lab_hs,
-                   hipStream_t st) {
+static int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+void launch_assign(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, int nmax_pts, int *labels,
+                   int64_t lab_hs, hipStream_t st) {
+  if (mmax <= ASSIGN_RES_MAX) {
+    const int64_t subs = (int64_t)BH * ((nmax_pts + 63) / 64);
+    const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(device_cus(), (subs + 15) / 16));
+    AC_D_DISPATCH(D, hipLaunchKernelGGL(k_assign_res<DD>, dim3(blocks), dim3(1024), 0, st, a, op, labels, lab_hs, BH));
+    return;
+  }
   AC_D_DISPATCH(D, hipLaunchKernelGGL(k_assign<DD>, g2((nmax_pts + 255) / 256, BH), dim3(256), 0, st, a, op, labels,
                                       lab_hs));
 }
@@ -699,7 +900,10 @@ void launch_assign(int D, const KmArgs &a, const CentOps &op, int BH, int nmax_p
 void launch_sort(const SortArgs &s, int BH, int nmax_pts, hipStream_t st) {
   int tiles = (nmax_pts + SORT_TILE - 1) / SORT_TILE;
   size_t sh = (size_t)s.mcap * sizeof(int);
+  const int groups = (tiles + SORT_GROUP - 1) / SORT_GROUP;
   hipLaunchKernelGGL(k_sort_hist, g2(tiles, BH), dim3(64), sh, st, s);
+  hipLaunchKernelGGL(k_sort_gscan, dim3((unsigned)groups, (unsigned)BH, (unsigned)((s.mcap + 255) / 256)), dim3(256), 0,
+                     st, s);
   hipLaunchKernelGGL(k_sort_scan, dim3(BH), dim3(1024), 0, st, s);
   hipLaunchKernelGGL(k_sort_scatter, g2(tiles, BH), dim3(64), sh, st, s);
 }
@@ -716,7 +920,7 @@ void launch_update(int D, const KmArgs &a, const SortArgs &s, const CentOps &op,
 
 void launch_stage_dist(int D, const KmArgs &a, int BH, int nmax_pts, const int *labels, int64_t lab_hs, float *dist,
                        int64_t dist_hs, hipStream_t st) {
-  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_stage_dist<DD>, g2((nmax_pts + 3) / 4, BH), dim3(256), 0, st, a, labels,
+  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_stage_dist<DD>, g2((nmax_pts + 15) / 16, BH), dim3(256), 0, st, a, labels,
                                       lab_hs, dist, dist_hs));
 }
 
