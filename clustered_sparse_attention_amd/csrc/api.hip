@@ -100,7 +100,7 @@ struct Plan {
   size_t uidx0, uidx1, dist, flag, rstate, rhist, msepart, chunk_off, upd_part, kpp_nx, kpp_G;
   int kpp_smax;
   int upd_items;
-  size_t scoreA, scoreB, S, seltok, kc, vc, lb, tile_off, pairs;
+  size_t scoreA, scoreB, S, seltok, kc, vc, rows, rows_T, pbias, tile_off, pairs;
   // ac_layer persistent
   size_t q_labels, q_perm, q_seg, q_cent, q_ncl, q_rho;
   size_t k_labels, k_perm, k_seg, k_cent, k_ncl;
@@ -166,7 +166,9 @@ Plan make_plan(const ac_shape *s, const ac_params *p) {
   P.seltok = take(BH * P.nq * 4);
   P.kc = take(BH * P.ncapk * D * 2);
   P.vc = take(BH * P.ncapk * D * 2);
-  P.lb = take(BH * P.ncapk * 4);
+  P.rows = take(BH * (size_t)P.nq * L * 4);
+  P.rows_T = take(BH * (size_t)P.nq * 4);
+  P.pbias = take(BH * (size_t)P.nq * P.ncapk * 4);
   P.tile_off = take(BH * (P.nq + 1) * 4);
   P.pairs = take(BH * 8);
   P.q_labels = take(BH * L * 4);
@@ -475,14 +477,16 @@ ac_status do_attn(const Plan &P, const ac_params *p, const uint16_t *Q, const ui
   a.compensate = p->compensate;
   a.kc = at<uint16_t>(ws, P.kc);
   a.vc = at<uint16_t>(ws, P.vc);
-  a.lb = at<float>(ws, P.lb);
+  a.rows = at<int>(ws, P.rows);
+  a.rows_T = at<int>(ws, P.rows_T);
+  a.pbias = at<float>(ws, P.pbias);
   a.tile_off = at<int>(ws, P.tile_off);
   a.O = O;
   a.lse = lse;
   a.L = P.L;
   a.scale_log2 = attn_scale(p, D) * 1.44269504088896340736f;
-  launch_attn_prep(D, a, stats->kmean, stats->vmean, at<uint16_t>(ws, P.kc), at<uint16_t>(ws, P.vc), at<float>(ws, P.lb),
-                   at<int>(ws, P.tile_off), at<int>(ws, P.seltok), at<long long>(ws, P.pairs), BH, st);
+  launch_attn_prep(D, a, stats->kmean, stats->vmean, at<uint16_t>(ws, P.kc), at<uint16_t>(ws, P.vc),
+                   at<int>(ws, P.tile_off), at<long long>(ws, P.pairs), BH, st);
   AC_CHECK_LAUNCH();
   const int max_blocks = (int)cdiv(P.L, ATT_QT) + q->ncap;
   launch_attn(D, a, BH, max_blocks, st);

@@ -21,11 +21,77 @@
 
 namespace ac {
 
+// Per (head, query cluster): the key rows of its selection, concatenated in
+// selection order (each cluster's members in counting-sort order), their
+// count, and with compensation the logit bias of every key cluster's
+// pseudo-key (log2 n_c for an excluded non-empty cluster, -inf otherwise).
+// Fallback heads attend to every key and need no list.
+__global__ __launch_bounds__(256) void k_attn_rows(AttnArgs a) {
+  const int h = blockIdx.y, r = blockIdx.x;
+  if (r >= a.ncl_q[h]) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const bool dense = a.all_dense || (a.fallback != nullptr && a.fallback[h] != 0);
+  const int64_t rowi = (int64_t)h * a.nqcap + r;
+  const int *segk = a.seg_k + (int64_t)h * (a.ncap + 1);
+  if (dense) {
+    if (tid == 0) a.rows_T[rowi] = a.L;
+    return;
+  }
+  if (a.compensate) {
+    const int ncl_k = a.ncl_k[h];
+    for (int c = tid; c < ncl_k; c += 256) {
+      const bool sel = (a.mask[rowi * a.mwords + (c >> 5)] >> (c & 31)) & 1u;
+      const int cnt = segk[c + 1] - segk[c];
+      a.pbias[rowi * a.ncap + c] = (sel || cnt <= 0) ? -__builtin_inff() : log2f((float)cnt);
+    }
+  }
+  extern __shared__ int s_off[];  // [ncap + 1] first output position of each selected cluster
+  __shared__ int scan[256];
+  const int nsel = a.nsel[rowi];
+  const int *lst = a.list + rowi * a.ncap;
+  const int per = (nsel + 255) / 256;
+  const int ib = min(nsel, tid * per), ie = min(nsel, ib + per);
+  int loc = 0;
+  for (int i = ib; i < ie; ++i) {
+    const int c = lst[i];
+    const int len = segk[c + 1] - segk[c];
+    s_off[i] = len;
+    loc += len;
+  }
+  scan[tid] = loc;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  int run = scan[tid] - loc;
+  for (int i = ib; i < ie; ++i) {
+    const int len = s_off[i];
+    s_off[i] = run;
+    run += len;
+  }
+  if (tid == 255) {
+    s_off[nsel] = scan[255];
+    a.rows_T[rowi] = scan[255];
+  }
+  __syncthreads();
+  int *dst = a.rows + rowi * a.L;
+  const int *permk = a.perm_k + (int64_t)h * a.L;
+  for (int i = wave; i < nsel; i += 4) {
+    const int c = lst[i];
+    const int s0 = segk[c], len = segk[c + 1] - s0, o0 = s_off[i];
+    for (int j = lane; j < len; j += 64) dst[o0 + j] = permk[s0 + j];
+  }
+}
+
+// bf16 pseudo-keys / values, the first block of every query cluster, and the
+// number of (query, key) pairs each head evaluates.
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_prep(AttnArgs a, const float *__restrict__ kmean,
                                                    const float *__restrict__ vmean, uint16_t *__restrict__ kc,
-                                                   uint16_t *__restrict__ vc, float *__restrict__ lb,
-                                                   int *__restrict__ tile_off, const int *__restrict__ seltok,
+                                                   uint16_t *__restrict__ vc, int *__restrict__ tile_off,
                                                    long long *__restrict__ pairs) {
   const int h = blockIdx.y, c = blockIdx.x;
   if (c < a.ncap && a.compensate) {
@@ -34,17 +100,11 @@ __global__ __launch_bounds__(256) void k_attn_prep(AttnArgs a, const float *__re
       kc[o + dd] = f2bf(kmean[o + dd]);
       vc[o + dd] = f2bf(vmean[o + dd]);
     }
-    if (threadIdx.x == 0) {
-      const int *seg = a.seg_k + (int64_t)h * (a.ncap + 1);
-      const int cnt = c < a.ncl_k[h] ? seg[c + 1] - seg[c] : 0;
-      lb[(int64_t)h * a.ncap + c] = cnt > 0 ? log2f((float)cnt) : -__builtin_inff();
-    }
   }
   if (c == 0 && threadIdx.x == 0) {
     const int *sq = a.seg_q + (int64_t)h * (a.nqcap + 1);
     int *to = tile_off + (int64_t)h * (a.nqcap + 1);
     const int nq = a.ncl_q[h];
-    const bool dense = a.all_dense || (a.fallback != nullptr && a.fallback[h] != 0);
     int run = 0;
     long long pr = 0;
     for (int r = 0; r <= a.nqcap; ++r) {
@@ -52,19 +112,47 @@ __global__ __launch_bounds__(256) void k_attn_prep(AttnArgs a, const float *__re
       if (r < nq) {
         const int cnt = sq[r + 1] - sq[r];
         run += (cnt + ATT_QT - 1) / ATT_QT;
-        pr += (long long)cnt * (dense ? (long long)a.L : (long long)seltok[(int64_t)h * a.nqcap + r]);
+        pr += (long long)cnt * (long long)a.rows_T[(int64_t)h * a.nqcap + r];
       }
     }
     pairs[h] = pr;
   }
 }
 
+// LDS tile layouts.  K and V tiles are written by direct global->LDS loads
+// (16 bytes per lane, lane i at base + 16 i), so rows are unpadded; the
+// 16-byte chunks of each row are XOR-permuted instead, chunk c of row R at
+// slot c ^ swz(R), which makes the MFMA operand reads conflict-free:
+//  K (row-major, read 16 bytes per lane, 16 rows x one chunk per quarter
+//    wave): swz = R mod 16 (D = 128) or (R / 2) mod 8 (D = 64);
+//  V (row-major, read transposed with ds_read_b64_tr_b16, 4 rows x 4 chunks
+//    per half wave): swz = 4 (R mod 4) (D = 128) or 4 ((R / 2) mod 2) (D = 64).
+template <int D> AC_DEV int kswz(int R) { return D == 128 ? (R & 15) : ((R >> 1) & 7); }
+template <int D> AC_DEV int vswz(int R) { return D == 128 ? 4 * (R & 3) : 4 * ((R >> 1) & 1); }
+
+// One 16-byte-per-lane global->LDS load (lane i lands at lds + 16 i).  It is
+// issued from inline assembly so that the compiler does not tie every later
+// LDS read to its completion: the kernel waits for these loads itself, at
+// the end of each tile, before the barrier that publishes the buffer.
+AC_DEV void dma16(const uint16_t *src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(src) : "memory", "m0");
+}
+AC_DEV uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void *)p);
+}
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+#define AC_LDS(T, p) ((__attribute__((address_space(3))) T *)(p))
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
-  constexpr int KSQ = D / 16;        // k-steps of the QK product
-  constexpr int DB = D / 32;         // 32-dim blocks of O
-  constexpr int KROW = D + 8;        // padded K row (bf16)
-  constexpr int VROW = ATT_KT + 8;   // padded V^T row (keys)
+  constexpr int KSQ = D / 16;         // k-steps of the QK product
+  constexpr int DB = D / 32;          // 32-dim blocks of O
+  constexpr int NC = D / 8;           // 16-byte chunks per row
+  constexpr int RPI = 64 / NC;        // rows per 64-lane global->LDS load
+  constexpr int IPW = ATT_KT / RPI / 4;  // such loads per wave, per tensor and tile
+  constexpr int TILE = ATT_KT * D;    // elements per tile
   // XCD-aware order: the hardware deals consecutive block ids round-robin to
   // the 8 XCDs, so id -> work item w = (id % 8) * (N / 8) + id / 8 hands each
   // XCD a contiguous run of work items; the query tiles of one query cluster
@@ -87,58 +175,23 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   const int qbeg = segq[r] + (blk - toff[r]) * ATT_QT;
   const int qend = segq[r + 1];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
 
-  __shared__ uint16_t Ks[ATT_KT * KROW];
-  __shared__ uint16_t Vt[D * VROW];
+  __shared__ __align__(1024) uint16_t Kb0[TILE], Kb1[TILE], Vb0[TILE], Vb1[TILE];
   __shared__ __align__(16) float sbias[4][3][ATT_KT];
-  extern __shared__ int dyn[];
-  int *s_cum = dyn;                       // [ncap + 1]
-  int *s_start = dyn + (a.ncap + 1);      // [ncap]
-  uint32_t *s_mask = (uint32_t *)(dyn + 2 * a.ncap + 1);  // [mwords]
 
   const bool dense = a.all_dense || (a.fallback != nullptr && a.fallback[h] != 0);
   const int64_t rowi = (int64_t)h * a.nqcap + r;
-  int nsel = 0;
-  int T;
-  if (!dense) {
-    nsel = a.nsel[rowi];
-    const int *lst = a.list + rowi * a.ncap;
-    const int *segk = a.seg_k + (int64_t)h * (a.ncap + 1);
-    const int per = (nsel + 255) / 256;
-    const int ib = min(nsel, tid * per), ie = min(nsel, ib + per);
-    int loc = 0;
-    for (int i = ib; i < ie; ++i) {
-      int c = lst[i];
-      int s0 = segk[c];
-      s_start[i] = s0;
-      s_cum[i] = segk[c + 1] - s0;  // length for now
-      loc += s_cum[i];
-    }
-    __shared__ int scan[256];
-    scan[tid] = loc;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      int v = tid >= off ? scan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
-    }
-    int run = scan[tid] - loc;
-    for (int i = ib; i < ie; ++i) {
-      int len = s_cum[i];
-      s_cum[i] = run;
-      run += len;
-    }
-    if (tid == 255) s_cum[nsel] = scan[255];
-    if (a.compensate)
-      for (int w = tid; w < a.mwords; w += 256) s_mask[w] = a.mask[rowi * a.mwords + w];
-    __syncthreads();
-    T = s_cum[nsel];
-  } else {
-    T = a.L;
-  }
+  const int T = dense ? a.L : a.rows_T[rowi];
+  const int *rl = a.rows + rowi * a.L;
+  const bool comp = !dense && a.compensate;
+  const int ncl_k = a.ncl_k[h];
+  const float *pbr = a.pbias + rowi * a.ncap;
+  // tiles 0..nt0-1 walk the selected keys, nt0..ntiles-1 the pseudo-keys
+  const int nt0 = (T + ATT_KT - 1) / ATT_KT;
+  const int ntiles = nt0 + (comp ? (ncl_k + ATT_KT - 1) / ATT_KT : 0);
 
   // Q fragments of this wave's 32 queries (B operand of S^T = K Q^T)
   const int qi = qbeg + wave * 32 + l32;
@@ -163,91 +216,41 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   const uint16_t *Vh = a.V + (int64_t)h * a.L * D;
   const uint16_t *Kc = a.kc + (int64_t)h * a.ncap * D;
   const uint16_t *Vc = a.vc + (int64_t)h * a.ncap * D;
-  const int *permk = a.perm_k + (int64_t)h * a.L;
-  const int ncl_k = a.ncl_k[h];
-  const bool comp = !dense && a.compensate;
-  // tiles 0..nt0-1 walk the selected keys, nt0..ntiles-1 the pseudo-keys
-  const int nt0 = (T + ATT_KT - 1) / ATT_KT;
-  const int ntiles = nt0 + (comp ? (ncl_k + ATT_KT - 1) / ATT_KT : 0);
 
-  // Key index pipeline, run by every wave for itself: lane l finds the row
-  // of key l of a tile (and its logit bias) two tiles ahead.  The loads it
-  // needs are unconditional and their results are first used at the end of
-  // the iteration, so their latency hides behind the tile's MFMAs.  Tiles
-  // advance monotonically through the selection, so a cursor replaces a
-  // search: the cluster holding a key is found by stepping forward from the
-  // cluster that held the previous tile's last key.
-  int cur = 0;
+  // Key index pipeline, run by every wave for itself: lane l loads the row
+  // of key l of a tile (and its pseudo-key bias) two tiles ahead; the loads
+  // are unconditional and first used at the end of the iteration.
   auto index_issue = [&](int tt, int &raw, float &braw) {
     const bool ph1 = tt >= nt0;
     const int o = (ph1 ? tt - nt0 : tt) * ATT_KT + lane;
-    int pos = min(o, a.L - 1);
-    if (!ph1 && !dense) {
-      const int oc = min(o, T - 1);
-      int c = cur;
-      while (c + 1 < nsel && s_cum[c + 1] <= oc) ++c;
-      pos = s_start[c] + (oc - s_cum[c]);
-      cur = __shfl(c, 63, 64);
-    }
-    raw = permk[pos];
-    braw = comp ? a.lb[(int64_t)h * a.ncap + min(o, a.ncap - 1)] : 0.f;
+    raw = rl[max(0, min(o, T - 1))];
+    braw = comp ? pbr[min(o, a.ncap - 1)] : 0.f;
   };
   // final row (-1: masked) and bias of key `lane` of tile tt
   auto index_commit = [&](int tt, int raw, float braw, float *bias_dst) -> int {
     const bool ph1 = tt >= nt0;
     const int o = (ph1 ? tt - nt0 : tt) * ATT_KT + lane;
     const int total = ph1 ? ncl_k : T;
-    int rw = ph1 ? o : (dense ? o : raw);
-    float bias = 0.f;
-    if (ph1) {
-      const bool selected = (s_mask[min(o, a.ncap - 1) >> 5] >> (o & 31)) & 1u;
-      bias = selected ? -__builtin_inff() : braw;
-    }
+    int rw = (ph1 || dense) ? o : raw;
+    float bias = ph1 ? braw : 0.f;
     if (o >= total) { rw = -1; bias = -__builtin_inff(); }
     bias_dst[lane] = bias;
     return rw;
   };
-
-  constexpr int KCH = (ATT_KT * D / 8) / 256;      // 16-byte K pieces per thread
-  constexpr int VCH = (ATT_KT / 2 * D / 8) / 256;  // V key pairs x 8 dims per thread
-  u32x4_t kreg[KCH], vreg[VCH][2];
-  // rows come from lane (key) of this wave's index registers
-  auto load_tile = [&](int tt, int rwv) {
+  // global->LDS loads of tile tt: wave w writes rows [RPI*(4*ii+w), +RPI) of
+  // both tensors; rows come from the wave's index registers by shuffle
+  auto dma_tile = [&](int tt, int rwv, uint16_t *kdst, uint16_t *vdst) {
     const bool ph1 = tt >= nt0;
     const uint16_t *Kp = ph1 ? Kc : Kh;
     const uint16_t *Vp = ph1 ? Vc : Vh;
 #pragma unroll
-    for (int it = 0; it < KCH; ++it) {
-      const int q = tid + it * 256;
-      const int rr = q / (D / 8), cc = (q % (D / 8)) * 8;
-      const int rw = max(__shfl(rwv, rr, 64), 0);  // masked keys (-1) read row 0: their bias is -inf
-      kreg[it] = *(const u32x4_t *)&Kp[(int64_t)rw * D + cc];
-    }
-#pragma unroll
-    for (int it = 0; it < VCH; ++it) {
-      const int q = tid + it * 256;
-      const int kp = q % (ATT_KT / 2), dc = q / (ATT_KT / 2);
-      const int r0 = max(__shfl(rwv, 2 * kp, 64), 0), r1 = max(__shfl(rwv, 2 * kp + 1, 64), 0);
-      vreg[it][0] = *(const u32x4_t *)&Vp[(int64_t)r0 * D + dc * 8];
-      vreg[it][1] = *(const u32x4_t *)&Vp[(int64_t)r1 * D + dc * 8];
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int it = 0; it < KCH; ++it) {
-      const int q = tid + it * 256;
-      const int rr = q / (D / 8), cc = (q % (D / 8)) * 8;
-      *(u32x4_t *)&Ks[rr * KROW + cc] = kreg[it];
-    }
-#pragma unroll
-    for (int it = 0; it < VCH; ++it) {
-      const int q = tid + it * 256;
-      const int kp = q % (ATT_KT / 2), dc = q / (ATT_KT / 2);
-      const uint16_t *e0 = (const uint16_t *)&vreg[it][0];
-      const uint16_t *e1 = (const uint16_t *)&vreg[it][1];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *(uint32_t *)&Vt[(dc * 8 + i) * VROW + 2 * kp] = (uint32_t)e0[i] | ((uint32_t)e1[i] << 16);
+    for (int ii = 0; ii < IPW; ++ii) {
+      const int I = ii * 4 + wave;
+      const int R = I * RPI + lane / NC;
+      const int p = lane % NC;
+      const int64_t rw = (int64_t)max(__shfl(rwv, R, 64), 0);  // masked keys read row 0; their bias is -inf
+      dma16(Kp + rw * D + (p ^ kswz<D>(R)) * 8, lds_addr(kdst + I * 512));
+      dma16(Vp + rw * D + (p ^ vswz<D>(R)) * 8, lds_addr(vdst + I * 512));
     }
   };
 
@@ -262,21 +265,32 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
       index_issue(1, raw, braw);
       rw_next = index_commit(1, raw, braw, sbw + ATT_KT);
     }
-    load_tile(0, rw0);
+    dma_tile(0, rw0, Kb0, Vb0);
   }
+  __builtin_amdgcn_s_waitcnt(0);  // tile 0, the Q fragments and the index loads have landed
+  __syncthreads();
 
   // key slot l32 of each 32-key block holds tile key 16*(a/2) + 8*gg + 4*(a%2) + b, l32 = 8a + 4gg + b
   const int kslot = 16 * ((l32 >> 3) >> 1) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
+  const int kx = kswz<D>(kslot);  // the same for kslot + 32
+  // transposed V reads: lane (i = lane % 16, half hd of the 32 dims, key half g)
+  const int vi = lane & 15, vhd = (lane >> 4) & 1;
+  const int vrow = 8 * g + (vi >> 2);                   // + 16 s + 4 u
+  const int vxq = vswz<D>(vrow) >> 2;                   // row-dependent chunk flip (bits 2-3)
+  const int vc2 = 2 * vhd + ((vi & 3) >> 1);            // chunk within the 4-chunk (32-dim) group
+  const int vhalf = 4 * (vi & 1);
 
   for (int tt = 0; tt < ntiles; ++tt) {
-    __syncthreads();  // the previous tile is consumed
-    store_tile();
-    __syncthreads();
-    if (tt + 1 < ntiles) load_tile(tt + 1, rw_next);  // in flight during this tile's MFMAs
+    const uint16_t *Ks = (tt & 1) ? Kb1 : Kb0;
+    const uint16_t *Vs = (tt & 1) ? Vb1 : Vb0;
     const bool idx_next = tt + 2 < ntiles;
     int pend_raw = 0;
     float pend_b = 0.f;
     if (idx_next) index_issue(tt + 2, pend_raw, pend_b);
+    if (tt + 1 < ntiles) {  // in flight during this tile's MFMAs
+      if (tt & 1) dma_tile(tt + 1, rw_next, Kb0, Vb0);
+      else dma_tile(tt + 1, rw_next, Kb1, Vb1);
+    }
 
     // S^T for two 32-key blocks (the two accumulation chains interleaved)
     f32x16_t acc_s[2];
@@ -286,7 +300,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
     for (int ks = 0; ks < KSQ; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8_t kf = *(const bf16x8_t *)&Ks[(32 * kb + kslot) * KROW + ks * 16 + g * 8];
+        const bf16x8_t kf = *(const bf16x8_t *)&Ks[(32 * kb + kslot) * D + (((2 * ks + g) ^ kx) << 3)];
         acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], acc_s[kb], 0, 0, 0);
       }
     }
@@ -332,9 +346,10 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
       m_i = m_new;
     }
     const float m_use = m_i == -__builtin_inff() ? 0.f : m_i;
-    // biased: exp2(s - m); unbiased: exp2(acc * sl2 - m) as one FMA
+    // biased: exp2(s - m); unbiased: exp2(acc * sl2 - m) as one FMA.  The row
+    // sum adds the bf16-rounded weights that the PV product uses, two per
+    // dot instruction.
     const float mul = biased ? 1.f : sl2;
-    float psum = 0.f;
     bf16x8_t pb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -342,25 +357,36 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
       for (int half = 0; half < 2; ++half) {
         bf16x8_t t;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(acc_s[kb][half * 8 + i], mul, -m_use));
-          psum += pv;
-          t[i] = (__bf16)pv;
-        }
+        for (int i = 0; i < 8; ++i)
+          t[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc_s[kb][half * 8 + i], mul, -m_use));
         pb[kb * 2 + half] = t;
       }
-    l_i += psum;
-    // O^T += V^T P^T over 4 k-steps of 16 keys
+    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x2_t pr = {pb[q][2 * i], pb[q][2 * i + 1]};
+        l_i = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_i, false);
+      }
+    // O^T += V^T P^T over 4 k-steps of 16 keys; the V^T operand (8 keys of
+    // one dim per lane) comes from two transposing 4-key reads
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int kbase = 16 * s + 8 * g;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8_t vf = *(const bf16x8_t *)&Vt[(32 * db + l32) * VROW + kbase];
+        const int ch = (4 * (db ^ vxq) + vc2) << 3;
+        const uint16_t *v0 = &Vs[(16 * s + vrow) * D + ch + vhalf];
+        const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(AC_LDS(i16x4_t, v0));
+        const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(AC_LDS(i16x4_t, v0 + 4 * D));
+        const i16x4_t cat[2] = {lo4, hi4};
+        const bf16x8_t vf = *(const bf16x8_t *)cat;
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[s], acc_o[db], 0, 0, 0);
       }
     }
     if (idx_next) rw_next = index_commit(tt + 2, pend_raw, pend_b, sbw + ((tt + 2) % 3) * ATT_KT);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile tt + 1 has landed
+    __syncthreads();                // all of it has; nobody reads tile tt any more
   }
 
   const float lsum = l_i + __shfl_xor(l_i, 32, 64);
@@ -381,24 +407,25 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
 }
 
 void launch_attn_prep(int D, const AttnArgs &a, const float *kmean, const float *vmean, uint16_t *kc, uint16_t *vc,
-                      float *lb, int *tile_off, const int *seltok, long long *pairs, int BH, hipStream_t st) {
+                      int *tile_off, long long *pairs, int BH, hipStream_t st) {
+  hipLaunchKernelGGL(k_attn_rows, dim3((unsigned)a.nqcap, (unsigned)BH), dim3(256), (size_t)(a.ncap + 1) * sizeof(int),
+                     st, a);
   dim3 grid(a.compensate ? a.ncap : 1, BH);
   if (D == 64)
-    hipLaunchKernelGGL(k_attn_prep<64>, grid, dim3(256), 0, st, a, kmean, vmean, kc, vc, lb, tile_off, seltok, pairs);
+    hipLaunchKernelGGL(k_attn_prep<64>, grid, dim3(256), 0, st, a, kmean, vmean, kc, vc, tile_off, pairs);
   else
-    hipLaunchKernelGGL(k_attn_prep<128>, grid, dim3(256), 0, st, a, kmean, vmean, kc, vc, lb, tile_off, seltok, pairs);
+    hipLaunchKernelGGL(k_attn_prep<128>, grid, dim3(256), 0, st, a, kmean, vmean, kc, vc, tile_off, pairs);
 }
 
 void launch_attn(int D, const AttnArgs &a, int BH, int max_blocks, hipStream_t st) {
-  size_t dyn = (size_t)(2 * a.ncap + 1 + a.mwords) * sizeof(int);
   AttnArgs aa = a;
   aa.blocks_per_head = max_blocks;
   aa.BH = BH;
   const long long total = ((long long)max_blocks * BH + 7) / 8 * 8;  // a multiple of the 8 XCDs
   if (D == 64)
-    hipLaunchKernelGGL(k_attn<64>, dim3((unsigned)total), dim3(256), dyn, st, aa);
+    hipLaunchKernelGGL(k_attn<64>, dim3((unsigned)total), dim3(256), 0, st, aa);
   else
-    hipLaunchKernelGGL(k_attn<128>, dim3((unsigned)total), dim3(256), dyn, st, aa);
+    hipLaunchKernelGGL(k_attn<128>, dim3((unsigned)total), dim3(256), 0, st, aa);
 }
 
 }  // namespace ac

@@ -115,7 +115,9 @@ struct AttnArgs {
   int all_dense;
   int compensate;
   const uint16_t *kc, *vc;    // [BH, ncap, D] bf16 pseudo-keys / values
-  const float *lb;            // [BH, ncap] log2(n_c) or -inf
+  int *rows;                  // [BH, nqcap, L] key rows of each selection, concatenated
+  int *rows_T;                // [BH, nqcap] their count (L on fallback heads)
+  float *pbias;               // [BH, nqcap, ncap] pseudo-key logit bias (base 2)
   const int *tile_off;        // [BH, nqcap + 1] first block of each query cluster
   uint16_t *O;                // [BH, L, D]
   float *lse;                 // [BH, L] or NULL
@@ -161,7 +163,7 @@ void launch_select(const SelectArgs &a, int BH, hipStream_t st);
 
 // attn.hip
 void launch_attn_prep(int D, const AttnArgs &a, const float *kmean, const float *vmean, uint16_t *kc, uint16_t *vc,
-                      float *lb, int *tile_off, const int *seltok, long long *pairs, int BH, hipStream_t st);
+                      int *tile_off, long long *pairs, int BH, hipStream_t st);
 void launch_attn(int D, const AttnArgs &a, int BH, int max_blocks, hipStream_t st);
 
 }  // namespace ac
