@@ -82,19 +82,31 @@ class Layer:
         self.st = ac.KStats(BH, self.ncap, d, dev)
         self.sel = ac.Selection(BH, nq, self.ncap, dev, score=False)
         self.O = torch.empty_like(Qd)
+        self.torch = torch
+        self.side = torch.cuda.Stream()  # default priority
 
     def step(self, ev=None):
-        ac = self.ac
-        if ev: ev[0].record()
-        ac.ac_cluster_q(self.shape, self.p, self.Q, None, self.q, self.ws)
-        if ev: ev[1].record()
+        """One layer: the query clustering on a side stream beside the key
+        clustering (the two use disjoint workspace scratch), then scoring,
+        selection and attention.  ev: 7 timing events (start, key clustering
+        done, query clustering start / done on the side stream, both joined,
+        selection done, attention done)."""
+        ac, torch = self.ac, self.torch
+        main = torch.cuda.current_stream()
+        if ev: ev[0].record(main)
+        self.side.wait_stream(main)
+        if ev: ev[2].record(self.side)
+        ac.ac_cluster_q(self.shape, self.p, self.Q, None, self.q, self.ws, stream=self.side.cuda_stream)
+        if ev: ev[3].record(self.side)
         ac.ac_cluster_k(self.shape, self.p, self.K, self.V, None, self.k, self.st, self.ws)
-        if ev: ev[2].record()
+        if ev: ev[1].record(main)
+        main.wait_stream(self.side)
+        if ev: ev[4].record(main)
         ac.ac_score_select(self.shape, self.p, self.q, self.k, self.st, self.sel, self.ws)
-        if ev: ev[3].record()
+        if ev: ev[5].record(main)
         ac.ac_sparse_attn(self.shape, self.p, self.Q, self.K, self.V, self.q, self.k, self.st, self.sel, self.O,
                           None, self.ws)
-        if ev: ev[4].record()
+        if ev: ev[6].record(main)
 
     def attn_only(self):
         self.ac.ac_sparse_attn(self.shape, self.p, self.Q, self.K, self.V, self.q, self.k, self.st, self.sel, self.O,
@@ -212,6 +224,69 @@ def measured_traffic(workload: str, variant: str, compensate: int):
     return t.get("bytes_per_launch")
 
 
+def _counter_kib(csv_path: str, kernel_regex: str):
+    """Per-dispatch sums of one rocprofv3 counter (KiB) for kernels whose
+    name matches kernel_regex, grouped by dispatch id."""
+    import csv
+    import re
+    per = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if re.search(kernel_regex, r["Kernel_Name"]):
+                d = int(r["Dispatch_Id"])
+                per[d] = per.get(d, 0.0) + float(r["Counter_Value"])
+    return per
+
+
+def summarize(args):
+    """Write the committed profile summaries from rocprofv3 output.
+
+    --summarize stats <kernel_stats.csv> <out.md> <command...>
+    --summarize traffic <fetch.csv> <write.csv> <copy_fetch.csv> <copy_write.csv> <copy_bytes>
+                        <dispatches_per_call> <out.json> <command...>
+    """
+    import csv
+    kind, rest = args[0], args[1:]
+    if kind == "stats":
+        src, out, cmd = rest[0], rest[1], " ".join(rest[2:])
+        rows = list(csv.DictReader(open(src)))
+        rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+        lines = [f"# rocprofv3 kernel statistics", "", f"Command: `{cmd}`", "",
+                 "| kernel | calls | total ms | avg us | % |", "|---|---:|---:|---:|---:|"]
+        for r in rows[:30]:
+            name = r["Name"].replace("void ", "").split("(")[0]
+            lines.append(f"| {name} | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+                         f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+        open(out, "w").write("\n".join(lines) + "\n")
+        return
+    if kind == "traffic":
+        f_csv, w_csv, cf_csv, cw_csv = rest[:4]
+        copy_bytes, per_call, out = int(rest[4]), int(rest[5]), rest[6]
+        cmd = " ".join(rest[7:])
+        rx = r"k_attn"
+        fetch = _counter_kib(f_csv, rx)
+        write = _counter_kib(w_csv, rx)
+        cf = max(_counter_kib(cf_csv, r"copy|elementwise|Copy").values())
+        cw = max(_counter_kib(cw_csv, r"copy|elementwise|Copy").values())
+        f_scale = copy_bytes / (cf * 1024.0)
+        w_scale = copy_bytes / (cw * 1024.0)
+        tot_f = sum(fetch.values()) * 1024.0 * f_scale
+        tot_w = sum(write.values()) * 1024.0 * w_scale
+        launches = len(fetch) / per_call
+        res = {"workload": "wan", "variant": "density", "compensate": 0,
+               "kernels": "k_attn_rows + k_attn_prep + k_attn (one ac_sparse_attn call)",
+               "fetch_kib_raw": sum(fetch.values()), "write_kib_raw": sum(write.values()),
+               "dispatches": len(fetch), "entry_point_calls": launches,
+               "copy_probe_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
+               "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+               "bytes_per_launch": (tot_f + tot_w) / launches,
+               "attn_source_sha256": attn_source_hash(), "command": cmd}
+        json.dump(res, open(out, "w"), indent=1)
+        print(json.dumps(res))
+        return
+    raise SystemExit(f"unknown summary kind {kind}")
+
+
 def copy_probe(nbytes: int):
     """A plain device copy of nbytes (torch), for calibrating the HBM byte
     counters: its FETCH_SIZE / WRITE_SIZE should read nbytes each."""
@@ -237,7 +312,11 @@ def main():
     ap.add_argument("--no-baselines", action="store_true", help="skip dense baselines and the CPU oracle")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a plain copy of this many bytes")
+    ap.add_argument("--summarize", nargs="+", help="write a profile summary from rocprofv3 output (no GPU)")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
@@ -272,7 +351,7 @@ def main():
     torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(args.steps):
@@ -280,13 +359,15 @@ def main():
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     ms_step = (t_end - t_start) * 1e3 / args.steps
-    phase = np.array([[evs[s][i].elapsed_time(evs[s][i + 1]) for i in range(4)] for s in range(args.steps)])
+    # cluster_q (side stream), cluster_k, both overlapped, score_select, sparse_attn
+    pairs_ev = [(2, 3), (0, 1), (0, 4), (4, 5), (5, 6)]
+    phase = np.array([[evs[s][a].elapsed_time(evs[s][b]) for a, b in pairs_ev] for s in range(args.steps)])
     phase_ms = phase.mean(axis=0)
     print(f"[bench] timed {args.steps} steps: {ms_step:.2f} ms/step", file=sys.stderr, flush=True)
 
     pairs, _ = pairs_of(layer)
     attn_flops = 4.0 * w.d * pairs
-    attn_ms = float(phase_ms[3])
+    attn_ms = float(phase_ms[4])
     achieved = attn_flops / (attn_ms * 1e-3) / 1e12
     fb = layer.st.fallback.cpu().numpy()
     ncl = layer.k.ncl.cpu().numpy()
@@ -311,10 +392,11 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(args.workload, args.variant, args.compensate),
-                     "kernel": "k_attn (block-sparse attention)",
+                     "kernel": "ac_sparse_attn: k_attn_rows + k_attn_prep + k_attn (block-sparse attention)",
                      "algorithmic_flops_per_launch": attn_flops, "avg_launch_ms": round(attn_ms, 4)},
         "phase_ms": {"cluster_q": round(float(phase_ms[0]), 3), "cluster_k": round(float(phase_ms[1]), 3),
-                     "score_select": round(float(phase_ms[2]), 3), "sparse_attn": round(attn_ms, 3)},
+                     "clustering_q_beside_k": round(float(phase_ms[2]), 3),
+                     "score_select": round(float(phase_ms[3]), 3), "sparse_attn": round(attn_ms, 3)},
         "layer": {"density_pairs": round(pairs / (w.BH * float(w.L) ** 2), 4), "fallback_heads": int(fb.sum()),
                   "key_clusters_min_max": [int(ncl.min()), int(ncl.max())],
                   "stages_max": int(stages.max())},

@@ -92,14 +92,20 @@ ac_status check_params(const ac_shape *s, const ac_params *p) {
 
 // ---------------------------------------------------------------------------
 // workspace plan: every region any entry point uses, at fixed offsets
+// Scratch of one k-means engine.  Query and key clustering each have their
+// own, so the two may run at the same time on different streams.
+struct Scratch {
+  size_t lab, lperm, lseg, thist, tgrp, ops_hi, ops_lo, ops_norm, d2buf, hn, hm, hcoff, chunk_off, upd_part;
+  size_t kpp_nx, kpp_G;
+  int mcap, kpp_smax, upd_items;
+};
+
 struct Plan {
-  int BH, L, D, nq, ncapk, mcap, max_tiles, max_groups, nq_pad, ncap_pad, mwords;
+  int BH, L, D, nq, ncapk, max_tiles, max_groups, nq_pad, ncap_pad, mwords;
   size_t total = 0;
-  // scratch
-  size_t qhat, qn, lab, lperm, lseg, thist, tgrp, ops_hi, ops_lo, ops_norm, d2buf, hn, hm, hcoff, hnew;
-  size_t uidx0, uidx1, dist, flag, rstate, rhist, msepart, chunk_off, upd_part, kpp_nx, kpp_G;
-  int kpp_smax;
-  int upd_items;
+  Scratch sq, sk;  // query / key clustering
+  size_t qhat, qn, hnew;
+  size_t uidx0, uidx1, dist, flag, rstate, rhist, msepart;
   size_t scoreA, scoreB, S, seltok, kc, vc, rows, rows_T, pbias, tile_off, pairs;
   // ac_layer persistent
   size_t q_labels, q_perm, q_seg, q_cent, q_ncl, q_rho;
@@ -108,6 +114,9 @@ struct Plan {
   size_t sel_list, sel_n, sel_mask, sel_score;
 };
 
+// stride of the per-selection key row lists: whole key tiles
+static inline int64_t rows_ld(int64_t n) { return (n + ATT_KT - 1) / ATT_KT * ATT_KT; }
+
 Plan make_plan(const ac_shape *s, const ac_params *p) {
   Plan P;
   P.BH = s->B * s->H;
@@ -115,7 +124,6 @@ Plan make_plan(const ac_shape *s, const ac_params *p) {
   P.D = s->d;
   P.nq = std::min(p->nq, s->L);
   P.ncapk = p->nmax - 1 + p->m0;
-  P.mcap = std::max({P.ncapk, P.nq, 2});
   P.max_tiles = (int)cdiv(P.L, SORT_TILE);
   P.max_groups = (int)cdiv(P.max_tiles, SORT_GROUP);
   P.nq_pad = (int)cdiv(P.nq, 16) * 16;
@@ -128,20 +136,33 @@ Plan make_plan(const ac_shape *s, const ac_params *p) {
     off = align256(off + std::max<size_t>(bytes, 1));
     return o;
   };
+  // mcap: most labels a sort of this engine sees; mm: most centres it seeds
+  auto scratch = [&](Scratch &S, int mcap, int mm) {
+    S.mcap = std::max(mcap, 2);
+    S.lab = take(BH * L * 4);
+    S.lperm = take(BH * L * 4);
+    S.lseg = take(BH * (S.mcap + 1) * 4);
+    S.thist = take(BH * P.max_tiles * (size_t)S.mcap * 4);
+    S.tgrp = take(BH * P.max_groups * (size_t)S.mcap * 4);
+    S.ops_hi = take(BH * S.mcap * D * 2);
+    S.ops_lo = take(BH * S.mcap * D * 2);
+    S.ops_norm = take(BH * S.mcap * 4);
+    S.hn = take(BH * 4);
+    S.hm = take(BH * 4);
+    S.hcoff = take(BH * 4);
+    S.chunk_off = take(BH * (S.mcap + 1) * 4);
+    S.upd_items = (int)cdiv(P.L, UPD_CHUNK) + S.mcap;
+    S.upd_part = take(BH * (size_t)S.upd_items * D * 8);
+    S.kpp_smax = p->init_sample > 0 ? (int)std::min<int64_t>(P.L, (int64_t)p->init_sample * mm) : P.L;
+    const bool gram = S.kpp_smax <= KPP_GRAM_MAX;
+    S.kpp_nx = take(gram ? BH * (size_t)S.kpp_smax * 8 : 0);
+    S.kpp_G = take(gram ? BH * (size_t)S.kpp_smax * S.kpp_smax * 8 : 0);
+    S.d2buf = take(gram ? 0 : BH * (size_t)KPP_SMAX * 8);
+  };
+  scratch(P.sq, P.nq, P.nq);
+  scratch(P.sk, P.ncapk, std::min(p->m0, P.L));
   P.qhat = take(BH * L * D * 2);
   P.qn = take(BH * L * 4);
-  P.lab = take(BH * L * 4);
-  P.lperm = take(BH * L * 4);
-  P.lseg = take(BH * (P.mcap + 1) * 4);
-  P.thist = take(BH * P.max_tiles * (size_t)P.mcap * 4);
-  P.tgrp = take(BH * P.max_groups * (size_t)P.mcap * 4);
-  P.ops_hi = take(BH * P.mcap * D * 2);
-  P.ops_lo = take(BH * P.mcap * D * 2);
-  P.ops_norm = take(BH * P.mcap * 4);
-  P.d2buf = take(BH * (size_t)KPP_SMAX * 8);
-  P.hn = take(BH * 4);
-  P.hm = take(BH * 4);
-  P.hcoff = take(BH * 4);
   P.hnew = take(BH * 4);
   P.uidx0 = take(BH * L * 4);
   P.uidx1 = take(BH * L * 4);
@@ -150,25 +171,15 @@ Plan make_plan(const ac_shape *s, const ac_params *p) {
   P.rstate = take(BH * 2 * 4);
   P.rhist = take(BH * 256 * 4);
   P.msepart = take(BH * P.ncapk * 8);
-  P.chunk_off = take(BH * (P.mcap + 1) * 4);
-  P.upd_items = (int)cdiv(P.L, UPD_CHUNK) + P.mcap;
-  {
-    const int mm = std::max(P.nq, std::min(p->m0, P.L));
-    P.kpp_smax = p->init_sample > 0 ? (int)std::min<int64_t>(P.L, (int64_t)p->init_sample * mm) : P.L;
-    const bool gram = P.kpp_smax <= KPP_GRAM_MAX;
-    P.kpp_nx = take(gram ? BH * (size_t)P.kpp_smax * 8 : 0);
-    P.kpp_G = take(gram ? BH * (size_t)P.kpp_smax * P.kpp_smax * 8 : 0);
-  }
-  P.upd_part = take(BH * (size_t)P.upd_items * D * 8);
   P.scoreA = take(BH * P.nq_pad * 6 * D * 2);
   P.scoreB = take(BH * P.ncap_pad * 6 * D * 2);
   P.S = take(BH * P.nq * (size_t)P.ncapk * 4);
   P.seltok = take(BH * P.nq * 4);
   P.kc = take(BH * P.ncapk * D * 2);
   P.vc = take(BH * P.ncapk * D * 2);
-  P.rows = take(BH * (size_t)P.nq * L * 4);
+  P.rows = take(BH * (size_t)P.nq * rows_ld(L) * 4);
   P.rows_T = take(BH * (size_t)P.nq * 4);
-  P.pbias = take(BH * (size_t)P.nq * P.ncapk * 4);
+  P.pbias = take(BH * (size_t)P.nq * rows_ld(P.ncapk) * 4);
   P.tile_off = take(BH * (P.nq + 1) * 4);
   P.pairs = take(BH * 8);
   P.q_labels = take(BH * L * 4);
@@ -226,21 +237,22 @@ float attn_scale(const ac_params *p, int D) { return p->scale > 0.f ? p->scale :
 // and a final assignment into labels_out.
 struct Engine {
   const Plan &P;
+  const Scratch &S;
   void *ws;
   hipStream_t st;
-  int *n() { return at<int>(ws, P.hn); }
-  int *m() { return at<int>(ws, P.hm); }
-  int *coff() { return at<int>(ws, P.hcoff); }
-  CentOps ops() { return CentOps{at<uint16_t>(ws, P.ops_hi), at<uint16_t>(ws, P.ops_lo), at<float>(ws, P.ops_norm), P.mcap}; }
+  int *n() { return at<int>(ws, S.hn); }
+  int *m() { return at<int>(ws, S.hm); }
+  int *coff() { return at<int>(ws, S.hcoff); }
+  CentOps ops() { return CentOps{at<uint16_t>(ws, S.ops_hi), at<uint16_t>(ws, S.ops_lo), at<float>(ws, S.ops_norm), S.mcap}; }
   SortArgs sort_args(const int *labels, int *perm, int *seg, int segcap, int mcap_used) {
     SortArgs s;
     s.labels = labels;
     s.lab_hs = P.L;
     s.n = n();
     s.m = m();
-    s.tile_hist = at<int>(ws, P.thist);
+    s.tile_hist = at<int>(ws, S.thist);
     s.max_tiles = P.max_tiles;
-    s.grp = at<int>(ws, P.tgrp);
+    s.grp = at<int>(ws, S.tgrp);
     s.max_groups = P.max_groups;
     s.mcap = std::max(mcap_used, 2);
     s.perm = perm;
@@ -255,23 +267,23 @@ struct Engine {
                 int stage, int *labels_out) {
     const int D = P.D;
     if (seed_init) {
-      if (P.kpp_smax <= KPP_GRAM_MAX)
-        launch_kpp_gram(D, a, P.BH, P.kpp_smax, at<double>(ws, P.kpp_nx), at<double>(ws, P.kpp_G), p->init_sample,
+      if (S.kpp_smax <= KPP_GRAM_MAX)
+        launch_kpp_gram(D, a, P.BH, S.kpp_smax, at<double>(ws, S.kpp_nx), at<double>(ws, S.kpp_G), p->init_sample,
                         p->seed, role, stage, st);
       else
-        launch_kpp(D, a, P.BH, at<double>(ws, P.d2buf), p->init_sample, p->seed, role, stage, st);
+        launch_kpp(D, a, P.BH, at<double>(ws, S.d2buf), p->init_sample, p->seed, role, stage, st);
       AC_CHECK_LAUNCH();
     }
     CentOps op = ops();
     launch_cent_prep(D, a, op, P.BH, mmax, st);
     AC_CHECK_LAUNCH();
-    int *lab = at<int>(ws, P.lab);
+    int *lab = at<int>(ws, S.lab);
     for (int it = 0; it < iters; ++it) {
       launch_assign(D, a, op, P.BH, mmax, npts, lab, P.L, st);
-      SortArgs s = sort_args(lab, at<int>(ws, P.lperm), at<int>(ws, P.lseg), P.mcap, mmax);
+      SortArgs s = sort_args(lab, at<int>(ws, S.lperm), at<int>(ws, S.lseg), S.mcap, mmax);
       launch_sort(s, P.BH, npts, st);
-      launch_update(D, a, s, op, P.BH, mmax, npts, at<int>(ws, P.chunk_off), P.mcap + 1, at<double>(ws, P.upd_part),
-                    (int64_t)P.upd_items * D, st);
+      launch_update(D, a, s, op, P.BH, mmax, npts, at<int>(ws, S.chunk_off), S.mcap + 1, at<double>(ws, S.upd_part),
+                    (int64_t)S.upd_items * D, st);
       AC_CHECK_LAUNCH();
     }
     launch_assign(D, a, op, P.BH, mmax, npts, labels_out, P.L, st);
@@ -284,7 +296,7 @@ struct Engine {
 ac_status do_cluster_q(const Plan &P, const ac_params *p, const uint16_t *Q, const float *warm_cent,
                        ac_clusters *q, void *ws, hipStream_t st) {
   const int BH = P.BH, L = P.L, D = P.D;
-  Engine E{P, ws, st};
+  Engine E{P, P.sq, ws, st};
   uint16_t *qhat = at<uint16_t>(ws, P.qhat);
   float *qn = at<float>(ws, P.qn);
   launch_qnorm(D, Q, qhat, qn, (int64_t)BH * L, st);
@@ -312,7 +324,7 @@ ac_status finish_keys(const Plan &P, const uint16_t *K, const uint16_t *V, ac_cl
                       void *ws, hipStream_t st, int mmax) {
   // final assignment of every key over all centres, counting sort, statistics
   const int BH = P.BH, L = P.L, D = P.D;
-  Engine E{P, ws, st};
+  Engine E{P, P.sk, ws, st};
   launch_fill_i32(E.n(), BH, L, st);
   launch_copy_i32(k->ncl, E.m(), BH, st);
   launch_fill_i32(E.coff(), BH, 0, st);
@@ -332,7 +344,7 @@ ac_status finish_keys(const Plan &P, const uint16_t *K, const uint16_t *V, ac_cl
 ac_status do_cluster_k_cold(const Plan &P, const ac_params *p, const uint16_t *K, const uint16_t *V,
                             ac_clusters *k, ac_kstats *stats, void *ws, hipStream_t st) {
   const int BH = P.BH, L = P.L, D = P.D;
-  Engine E{P, ws, st};
+  Engine E{P, P.sk, ws, st};
   std::vector<int> nU(BH, L), nC(BH, 0), done(BH, 0), F(BH, 0), stg(BH, 0), hn(BH), hm(BH), hc(BH);
   int *uidx[2] = {at<int>(ws, P.uidx0), at<int>(ws, P.uidx1)};
   int cur = 0;
@@ -356,7 +368,7 @@ ac_status do_cluster_k_cold(const Plan &P, const ac_params *p, const uint16_t *K
     AC_HIP(hipMemcpyAsync(E.coff(), hc.data(), BH * 4, hipMemcpyHostToDevice, st));
     KmArgs a{K, (int64_t)L * D, t == 0 ? nullptr : uidx[cur], L, E.n(), E.m(), E.coff(), k->cent,
              (int64_t)k->ncap * D};
-    int *lab = at<int>(ws, P.lab);
+    int *lab = at<int>(ws, E.S.lab);
     AC_TRY(E.run(a, mmax, nmaxpts, true, p->iters, p, 1, t, lab));
     launch_stage_dist(D, a, BH, nmaxpts, lab, L, dist, L, st);
     if (t == 0)
@@ -365,9 +377,9 @@ ac_status do_cluster_k_cold(const Plan &P, const ac_params *p, const uint16_t *K
     launch_flag_removed(dist, L, E.n(), stats->tau, flag, L, BH, nmaxpts, st);
     // stable compaction: label 0 (kept) first
     launch_fill_i32(E.m(), BH, 2, st);
-    SortArgs s = E.sort_args(flag, at<int>(ws, P.lperm), at<int>(ws, P.lseg), 1, 2);
+    SortArgs s = E.sort_args(flag, at<int>(ws, E.S.lperm), at<int>(ws, E.S.lseg), 1, 2);
     launch_sort(s, BH, nmaxpts, st);
-    launch_compact_gather(t == 0 ? nullptr : uidx[cur], L, at<int>(ws, P.lperm), L, at<int>(ws, P.lseg), 2,
+    launch_compact_gather(t == 0 ? nullptr : uidx[cur], L, at<int>(ws, E.S.lperm), L, at<int>(ws, E.S.lseg), 2,
                           uidx[cur ^ 1], at<int>(ws, P.hnew), BH, nmaxpts, st);
     AC_CHECK_LAUNCH();
     std::vector<int> nnew(BH);
@@ -400,7 +412,7 @@ ac_status do_cluster_k_cold(const Plan &P, const ac_params *p, const uint16_t *K
 ac_status do_cluster_k_warm(const Plan &P, const ac_params *p, const uint16_t *K, const uint16_t *V,
                             const ac_state *w, ac_clusters *k, ac_kstats *stats, void *ws, hipStream_t st) {
   const int BH = P.BH, L = P.L, D = P.D;
-  Engine E{P, ws, st};
+  Engine E{P, P.sk, ws, st};
   AC_HIP(hipMemcpyAsync(k->cent, w->cent_k, (size_t)BH * k->ncap * D * 4, hipMemcpyDeviceToDevice, st));
   launch_copy_i32(w->ncl_k, k->ncl, BH, st);
   launch_copy_u8(w->fallback, stats->fallback, BH, st);
@@ -478,6 +490,8 @@ ac_status do_attn(const Plan &P, const ac_params *p, const uint16_t *Q, const ui
   a.kc = at<uint16_t>(ws, P.kc);
   a.vc = at<uint16_t>(ws, P.vc);
   a.rows = at<int>(ws, P.rows);
+  a.rows_ld = rows_ld(P.L);
+  a.pb_ld = rows_ld(P.ncapk);
   a.rows_T = at<int>(ws, P.rows_T);
   a.pbias = at<float>(ws, P.pbias);
   a.tile_off = at<int>(ws, P.tile_off);
@@ -619,6 +633,33 @@ AC_API ac_status ac_sparse_attn(const ac_shape *s, const ac_params *p, const uin
   return do_attn(P, p, Q, K, V, q, k, stats, sel, O, lse, ws, (hipStream_t)stream);
 }
 
+namespace ac {
+namespace {
+// A second stream (default priority) per device and host thread, created on
+// first use and kept until the process ends: ac_layer runs the query
+// clustering on it, beside the key clustering, which shares no scratch with
+// it and reads nothing it writes.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+ac_status side_stream(SideStream **out) {
+  static thread_local SideStream tab[64];
+  int dev = 0;
+  AC_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(AC_E_DEVICE, "device ordinal %d out of range", dev);
+  SideStream &x = tab[dev];
+  if (!x.s) {
+    AC_HIP(hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking));
+    AC_HIP(hipEventCreateWithFlags(&x.fork, hipEventDisableTiming));
+    AC_HIP(hipEventCreateWithFlags(&x.join, hipEventDisableTiming));
+  }
+  *out = &x;
+  return AC_OK;
+}
+}  // namespace
+}  // namespace ac
+
 AC_API ac_status ac_layer(const ac_shape *s, const ac_params *p, const uint16_t *Q, const uint16_t *K,
                           const uint16_t *V, ac_state *state, uint16_t *O, ac_layer_stats *host_stats, void *ws,
                           size_t ws_bytes, ac_stream_t stream) {
@@ -641,11 +682,18 @@ AC_API ac_status ac_layer(const ac_shape *s, const ac_params *p, const uint16_t 
   ac_selection sel{P.ncapk, at<int>(ws, P.sel_list), at<int>(ws, P.sel_n), at<uint32_t>(ws, P.sel_mask),
                    at<float>(ws, P.sel_score)};
   const bool warm = state->valid != 0;
-  AC_TRY(do_cluster_q(P, p, Q, warm ? state->cent_q : nullptr, &q, ws, st));
-  if (warm)
-    AC_TRY(do_cluster_k_warm(P, p, K, V, state, &k, &ks, ws, st));
-  else
-    AC_TRY(do_cluster_k_cold(P, p, K, V, &k, &ks, ws, st));
+  // query clustering on the side stream, key clustering on the caller's
+  SideStream *ss = nullptr;
+  AC_TRY(side_stream(&ss));
+  AC_HIP(hipEventRecord(ss->fork, st));
+  AC_HIP(hipStreamWaitEvent(ss->s, ss->fork, 0));
+  const ac_status sq = do_cluster_q(P, p, Q, warm ? state->cent_q : nullptr, &q, ws, ss->s);
+  AC_HIP(hipEventRecord(ss->join, ss->s));
+  const ac_status sk = warm ? do_cluster_k_warm(P, p, K, V, state, &k, &ks, ws, st)
+                            : do_cluster_k_cold(P, p, K, V, &k, &ks, ws, st);
+  AC_HIP(hipStreamWaitEvent(st, ss->join, 0));
+  AC_TRY(sq);
+  AC_TRY(sk);
   AC_TRY(do_score_select(P, p, &q, &k, &ks, &sel, ws, st));
   AC_TRY(do_attn(P, p, Q, K, V, &q, &k, &ks, &sel, O, nullptr, ws, st));
   // carry the centres (and, after a cold step, counts, flags and tau) to the next step

@@ -16,6 +16,8 @@
 //   order).  Those 8-register halves are exactly the B operand of
 //   O^T = V^T . P^T for 16 contiguous keys, and V^T comes from a transposed
 //   LDS tile with one 16-byte read per lane and k-step.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -42,7 +44,7 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnArgs a) {
     for (int c = tid; c < ncl_k; c += 256) {
       const bool sel = (a.mask[rowi * a.mwords + (c >> 5)] >> (c & 31)) & 1u;
       const int cnt = segk[c + 1] - segk[c];
-      a.pbias[rowi * a.ncap + c] = (sel || cnt <= 0) ? -__builtin_inff() : log2f((float)cnt);
+      a.pbias[rowi * a.pb_ld + c] = (sel || cnt <= 0) ? -__builtin_inff() : log2f((float)cnt);
     }
   }
   extern __shared__ int s_off[];  // [ncap + 1] first output position of each selected cluster
@@ -77,7 +79,7 @@ __global__ __launch_bounds__(256) void k_attn_rows(AttnArgs a) {
     a.rows_T[rowi] = scan[255];
   }
   __syncthreads();
-  int *dst = a.rows + rowi * a.L;
+  int *dst = a.rows + rowi * a.rows_ld;
   const int *permk = a.perm_k + (int64_t)h * a.L;
   for (int i = wave; i < nsel; i += 4) {
     const int c = lst[i];
@@ -137,6 +139,13 @@ template <int D> AC_DEV int vswz(int R) { return D == 128 ? 4 * (R & 3) : 4 * ((
 AC_DEV void dma16(const uint16_t *src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(src) : "memory", "m0");
 }
+// s_waitcnt vmcnt(N) alone: the N most recent vector memory operations may
+// still be in flight (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and
+// lgkmcnt at their maxima).
+template <int N> AC_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 AC_DEV uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void *)p);
 }
@@ -146,13 +155,15 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 #define AC_LDS(T, p) ((__attribute__((address_space(3))) T *)(p))
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
-  constexpr int KSQ = D / 16;         // k-steps of the QK product
-  constexpr int DB = D / 32;          // 32-dim blocks of O
-  constexpr int NC = D / 8;           // 16-byte chunks per row
-  constexpr int RPI = 64 / NC;        // rows per 64-lane global->LDS load
-  constexpr int IPW = ATT_KT / RPI / 4;  // such loads per wave, per tensor and tile
-  constexpr int TILE = ATT_KT * D;    // elements per tile
+__global__ __launch_bounds__(ATT_THREADS, 1) void k_attn(AttnArgs a) {
+  constexpr int KSQ = D / 16;                 // k-steps of the QK product
+  constexpr int DB = D / 32;                  // 32-dim blocks of O
+  constexpr int NC = D / 8;                   // 16-byte chunks per row
+  constexpr int RPI = 64 / NC;                // rows per 64-lane global->LDS load
+  constexpr int NW = ATT_THREADS / 64;        // waves
+  constexpr int IPW = ATT_KT / RPI / NW;      // such loads per wave, per tensor and tile
+  constexpr int TILE = ATT_KT * D;            // elements per tile
+  constexpr int NST = 3;                      // K / V tile buffers
   // XCD-aware order: the hardware deals consecutive block ids round-robin to
   // the 8 XCDs, so id -> work item w = (id % 8) * (N / 8) + id / 8 hands each
   // XCD a contiguous run of work items; the query tiles of one query cluster
@@ -179,23 +190,27 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
 
-  __shared__ __align__(1024) uint16_t Kb0[TILE], Kb1[TILE], Vb0[TILE], Vb1[TILE];
-  __shared__ __align__(16) float sbias[4][3][ATT_KT];
+  __shared__ __align__(1024) uint16_t Kb[NST * TILE], Vb[NST * TILE];
+  __shared__ __align__(16) int ring[4][2 * ATT_KT];      // raw rows and pseudo-key biases of a tile, by tile mod 4
+  __shared__ __align__(16) float sbias[NW][4][ATT_KT];   // per wave: key biases / scale, by tile mod 4
 
   const bool dense = a.all_dense || (a.fallback != nullptr && a.fallback[h] != 0);
   const int64_t rowi = (int64_t)h * a.nqcap + r;
   const int T = dense ? a.L : a.rows_T[rowi];
-  const int *rl = a.rows + rowi * a.L;
   const bool comp = !dense && a.compensate;
   const int ncl_k = a.ncl_k[h];
-  const float *pbr = a.pbias + rowi * a.ncap;
   // tiles 0..nt0-1 walk the selected keys, nt0..ntiles-1 the pseudo-keys
   const int nt0 = (T + ATT_KT - 1) / ATT_KT;
   const int ntiles = nt0 + (comp ? (ncl_k + ATT_KT - 1) / ATT_KT : 0);
+  const int *rl = a.rows + rowi * a.rows_ld;
+  const float *pbr = a.pbias + rowi * a.pb_ld;
+  const int last_row_tile = max(nt0 - 1, 0);
+  const int last_pb_tile = max((a.ncap + ATT_KT - 1) / ATT_KT - 1, 0);
 
   // Q fragments of this wave's 32 queries (B operand of S^T = K Q^T)
   const int qi = qbeg + wave * 32 + l32;
   const bool qvalid = qi < qend;
+  const bool wave_active = qbeg + wave * 32 < qend;
   const int64_t qrow = qvalid ? (int64_t)a.perm_q[(int64_t)h * a.L + qi] : 0;
   bf16x8_t qf[KSQ];
   {
@@ -211,64 +226,61 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   float m_i = -__builtin_inff();
   float l_i = 0.f;
   const float sl2 = a.scale_log2;
+  const float inv_sl2 = 1.f / sl2;
 
-  const uint16_t *Kh = a.K + (int64_t)h * a.L * D;
-  const uint16_t *Vh = a.V + (int64_t)h * a.L * D;
-  const uint16_t *Kc = a.kc + (int64_t)h * a.ncap * D;
-  const uint16_t *Vc = a.vc + (int64_t)h * a.ncap * D;
+  const char *Kh = (const char *)(a.K + (int64_t)h * a.L * D);
+  const char *Vh = (const char *)(a.V + (int64_t)h * a.L * D);
+  const char *Kc = (const char *)(a.kc + (int64_t)h * a.ncap * D);
+  const char *Vc = (const char *)(a.vc + (int64_t)h * a.ncap * D);
 
-  // Key index pipeline, run by every wave for itself: lane l loads the row
-  // of key l of a tile (and its pseudo-key bias) two tiles ahead; the loads
-  // are unconditional and first used at the end of the iteration.
-  auto index_issue = [&](int tt, int &raw, float &braw) {
-    const bool ph1 = tt >= nt0;
-    const int o = (ph1 ? tt - nt0 : tt) * ATT_KT + lane;
-    raw = rl[max(0, min(o, T - 1))];
-    braw = comp ? pbr[min(o, a.ncap - 1)] : 0.f;
+  // Every global->LDS load of the loop is issued from inline assembly and the
+  // loop holds no other global memory access, so the kernel alone decides
+  // when to wait for them.  The row list and pseudo-key biases of a tile go
+  // to a small LDS ring (wave 0, 32 lanes x 16 bytes) four tiles ahead.
+  auto ring_load = [&](int tt) {
+    if (wave == 0 && lane < 32) {
+      const int tr = min(tt, last_row_tile);
+      const int tp = min(max(tt - nt0, 0), last_pb_tile);
+      const int *src = lane < 16 ? rl + tr * ATT_KT + 4 * lane : (const int *)pbr + tp * ATT_KT + 4 * (lane - 16);
+      dma16((const uint16_t *)src, lds_addr(&ring[tt & 3][0]));
+    }
   };
-  // final row (-1: masked) and bias of key `lane` of tile tt
-  auto index_commit = [&](int tt, int raw, float braw, float *bias_dst) -> int {
+  // final row (-1: masked) of key `lane` of tile tt from the ring; its logit
+  // bias, divided by the base-2 score scale so that it adds to the raw
+  // product, goes to this wave's bias rows
+  float *sbw = &sbias[wave][0][0];
+  auto commit = [&](int tt) -> int {
     const bool ph1 = tt >= nt0;
     const int o = (ph1 ? tt - nt0 : tt) * ATT_KT + lane;
     const int total = ph1 ? ncl_k : T;
+    const int raw = ring[tt & 3][lane];
+    const float braw = __int_as_float(ring[tt & 3][ATT_KT + lane]);
     int rw = (ph1 || dense) ? o : raw;
-    float bias = ph1 ? braw : 0.f;
+    float bias = ph1 ? braw * inv_sl2 : 0.f;
     if (o >= total) { rw = -1; bias = -__builtin_inff(); }
-    bias_dst[lane] = bias;
+    sbw[(tt & 3) * ATT_KT + lane] = bias;
     return rw;
   };
-  // global->LDS loads of tile tt: wave w writes rows [RPI*(4*ii+w), +RPI) of
-  // both tensors; rows come from the wave's index registers by shuffle
-  auto dma_tile = [&](int tt, int rwv, uint16_t *kdst, uint16_t *vdst) {
+  // The swizzles depend on the row only modulo 16, and a lane's row moves by
+  // NW * RPI (a multiple of 16) from one load to the next, so its source
+  // chunk byte offset is fixed.
+  const uint32_t koff = 16u * (uint32_t)((lane % NC) ^ kswz<D>(wave * RPI + lane / NC));
+  const uint32_t voff = 16u * (uint32_t)((lane % NC) ^ vswz<D>(wave * RPI + lane / NC));
+  // one tensor of tile tt into buffer `buf`: wave w writes rows
+  // [RPI*(NW*ii+w), +RPI); rows come from the wave's index registers by shuffle
+  auto dma = [&](bool vpart, int tt, int rwv, int buf) {
     const bool ph1 = tt >= nt0;
-    const uint16_t *Kp = ph1 ? Kc : Kh;
-    const uint16_t *Vp = ph1 ? Vc : Vh;
+    const char *src = vpart ? (ph1 ? Vc : Vh) : (ph1 ? Kc : Kh);
+    const uint32_t off = vpart ? voff : koff;
+    const uint16_t *dst = (vpart ? Vb : Kb) + buf * TILE;
 #pragma unroll
     for (int ii = 0; ii < IPW; ++ii) {
-      const int I = ii * 4 + wave;
+      const int I = ii * NW + wave;
       const int R = I * RPI + lane / NC;
-      const int p = lane % NC;
-      const int64_t rw = (int64_t)max(__shfl(rwv, R, 64), 0);  // masked keys read row 0; their bias is -inf
-      dma16(Kp + rw * D + (p ^ kswz<D>(R)) * 8, lds_addr(kdst + I * 512));
-      dma16(Vp + rw * D + (p ^ vswz<D>(R)) * 8, lds_addr(vdst + I * 512));
+      const uint32_t rw = (uint32_t)max(__shfl(rwv, R, 64), 0);  // masked keys read row 0; their bias is -inf
+      dma16((const uint16_t *)(src + (rw * (uint32_t)(2 * D) + off)), lds_addr(dst + I * 512));
     }
   };
-
-  float *sbw = &sbias[wave][0][0];  // this wave's bias rows, one per tile mod 3
-  int rw_next = -1;                 // row of key `lane` of tile tt + 1
-  if (ntiles > 0) {
-    int raw;
-    float braw;
-    index_issue(0, raw, braw);
-    const int rw0 = index_commit(0, raw, braw, sbw);
-    if (ntiles > 1) {
-      index_issue(1, raw, braw);
-      rw_next = index_commit(1, raw, braw, sbw + ATT_KT);
-    }
-    dma_tile(0, rw0, Kb0, Vb0);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // tile 0, the Q fragments and the index loads have landed
-  __syncthreads();
 
   // key slot l32 of each 32-key block holds tile key 16*(a/2) + 8*gg + 4*(a%2) + b, l32 = 8a + 4gg + b
   const int kslot = 16 * ((l32 >> 3) >> 1) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
@@ -280,114 +292,131 @@ __global__ __launch_bounds__(256, 2) void k_attn(AttnArgs a) {
   const int vc2 = 2 * vhd + ((vi & 3) >> 1);            // chunk within the 4-chunk (32-dim) group
   const int vhalf = 4 * (vi & 1);
 
-  for (int tt = 0; tt < ntiles; ++tt) {
-    const uint16_t *Ks = (tt & 1) ? Kb1 : Kb0;
-    const uint16_t *Vs = (tt & 1) ? Vb1 : Vb0;
-    const bool idx_next = tt + 2 < ntiles;
-    int pend_raw = 0;
-    float pend_b = 0.f;
-    if (idx_next) index_issue(tt + 2, pend_raw, pend_b);
-    if (tt + 1 < ntiles) {  // in flight during this tile's MFMAs
-      if (tt & 1) dma_tile(tt + 1, rw_next, Kb0, Vb0);
-      else dma_tile(tt + 1, rw_next, Kb1, Vb1);
-    }
-
-    // S^T for two 32-key blocks (the two accumulation chains interleaved)
-    f32x16_t acc_s[2];
-    acc_s[0] = (f32x16_t){};
-    acc_s[1] = (f32x16_t){};
+  // S^T = K Q^T for one tile: two 32-key blocks, chains interleaved
+  auto qk = [&](const uint16_t *Ks, f32x16_t *acc) {
+    acc[0] = (f32x16_t){};
+    acc[1] = (f32x16_t){};
 #pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks) {
+    for (int ks = 0; ks < KSQ; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8_t kf = *(const bf16x8_t *)&Ks[(32 * kb + kslot) * D + (((2 * ks + g) ^ kx) << 3)];
-        acc_s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], acc_s[kb], 0, 0, 0);
+        acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], acc[kb], 0, 0, 0);
       }
-    }
-    // scores in base-2 units: s * scale * log2(e) + bias.  Full tiles of
-    // selected keys carry no bias: the row max is taken on the raw products
-    // and the scale and max subtraction fold into one FMA per score.
-    // Tail and pseudo-key tiles add the bias (-inf masked, log2 n_c).
-    const bool biased = tt >= nt0 - 1;
+  };
+  // add the tile's scaled biases (0 for selected keys) and return the row
+  // max in base-2 units
+  auto bias_max = [&](f32x16_t *acc, const float *bz) -> float {
     float mt = -__builtin_inff();
-    if (biased) {
-      const float *bz = sbw + (tt % 3) * ATT_KT;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const f32x4_t b0 = *(const f32x4_t *)&bz[32 * kb + 16 * half + 8 * g];
-          const f32x4_t b1 = *(const f32x4_t *)&bz[32 * kb + 16 * half + 8 * g + 4];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float sv = fmaf(acc_s[kb][half * 8 + i], sl2, i < 4 ? b0[i] : b1[i - 4]);
-            acc_s[kb][half * 8 + i] = sv;
-            mt = fmaxf(mt, sv);
-          }
-        }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) mt = fmaxf(mt, acc_s[kb][j]);
-      mt *= sl2;
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    // lazy rescale: the reference max m_i may trail the running max by up to
-    // 2^8, so p <= 256; O and l are rescaled only when a row outgrows that
-    if (__ballot(mt > m_i + 8.f)) {
-      const float m_new = fmaxf(m_i, mt);
-      const float alpha = m_i == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_i - m_new);
-      l_i *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc_o[db][j] *= alpha;
-      m_i = m_new;
-    }
-    const float m_use = m_i == -__builtin_inff() ? 0.f : m_i;
-    // biased: exp2(s - m); unbiased: exp2(acc * sl2 - m) as one FMA.  The row
-    // sum adds the bf16-rounded weights that the PV product uses, two per
-    // dot instruction.
-    const float mul = biased ? 1.f : sl2;
-    bf16x8_t pb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        bf16x8_t t;
+        const f32x4_t b0 = *(const f32x4_t *)&bz[32 * kb + 16 * half + 8 * g];
+        const f32x4_t b1 = *(const f32x4_t *)&bz[32 * kb + 16 * half + 8 * g + 4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          t[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(acc_s[kb][half * 8 + i], mul, -m_use));
-        pb[kb * 2 + half] = t;
+        for (int i = 0; i < 8; ++i) {
+          const float sv = acc[kb][half * 8 + i] + (i < 4 ? b0[i] : b1[i - 4]);
+          acc[kb][half * 8 + i] = sv;
+          mt = fmaxf(mt, sv);
+        }
       }
-    const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+    mt *= sl2;
+    return fmaxf(mt, __shfl_xor(mt, 32, 64));
+  };
+
+  // Pipeline.  K and V of tile t + 2 are loaded while tile t is computed,
+  // into three buffers each, so every load has about two iterations to land;
+  // the row ring runs three tiles ahead.  Tiles past the end are loaded from
+  // clamped, in-bounds rows and never used, which keeps the number of loads
+  // per iteration fixed.
+  ring_load(0);
+  ring_load(1);
+  ring_load(2);
+  __builtin_amdgcn_s_waitcnt(0);  // the ring, the Q fragments and the scalars above have landed
+  __syncthreads();
+  {
+    const int rw0 = commit(0);
+    const int rw1 = commit(1);
+    dma(false, 0, rw0, 0);
+    dma(true, 0, rw0, 0);
+    dma(false, 1, rw1, 1);
+    dma(true, 1, rw1, 1);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+
+  int b0 = 0;  // buffer of tile tt; tile tt + 2 goes to the one after the next
+  for (int tt = 0; tt < ntiles; ++tt) {
+    const int b2 = b0 == 0 ? 2 : b0 - 1;
+    const int rw = commit(tt + 2);  // its ring slot landed by the last barrier
+    ring_load(tt + 3);
+    dma(false, tt + 2, rw, b2);     // buffers of tile tt - 1, read last iteration
+    dma(true, tt + 2, rw, b2);
+    if (wave_active) {
+      f32x16_t sc[2];
+      qk(Kb + b0 * TILE, sc);
+      const float mt = bias_max(sc, sbw + (tt & 3) * ATT_KT);
+      // lazy rescale: the reference max m_i may trail the running max by up
+      // to 2^8, so p <= 256; O and l are rescaled only when a row outgrows it
+      if (__ballot(mt > m_i + 8.f)) {
+        const float m_new = fmaxf(m_i, mt);
+        const float alpha = m_i == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_i - m_new);
+        l_i *= alpha;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x2_t pr = {pb[q][2 * i], pb[q][2 * i + 1]};
-        l_i = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_i, false);
+          for (int j = 0; j < 16; ++j) acc_o[db][j] *= alpha;
+        m_i = m_new;
       }
-    // O^T += V^T P^T over 4 k-steps of 16 keys; the V^T operand (8 keys of
-    // one dim per lane) comes from two transposing 4-key reads
+      const float m_use = m_i == -__builtin_inff() ? 0.f : m_i;
+      // p = exp2(s * scale * log2 e + bias - m)
+      bf16x8_t pb[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int ch = (4 * (db ^ vxq) + vc2) << 3;
-        const uint16_t *v0 = &Vs[(16 * s + vrow) * D + ch + vhalf];
-        const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(AC_LDS(i16x4_t, v0));
-        const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(AC_LDS(i16x4_t, v0 + 4 * D));
-        const i16x4_t cat[2] = {lo4, hi4};
-        const bf16x8_t vf = *(const bf16x8_t *)cat;
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[s], acc_o[db], 0, 0, 0);
+        for (int half = 0; half < 2; ++half) {
+          bf16x8_t t;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            t[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[kb][half * 8 + i], sl2, -m_use));
+          pb[kb * 2 + half] = t;
+        }
+      // the row sum adds the bf16 weights that the PV product uses, two per
+      // dot instruction
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        l_i = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[q], pb[q], 0, 1), ones, l_i, false);
+        l_i = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[q], pb[q], 2, 3), ones, l_i, false);
+        l_i = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[q], pb[q], 4, 5), ones, l_i, false);
+        l_i = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[q], pb[q], 6, 7), ones, l_i, false);
+      }
+      // O^T += V^T P^T over 4 k-steps of 16 keys; the V^T operand (8 keys of
+      // one dim per lane) comes from two transposing 4-key reads
+      const uint16_t *Vs = Vb + b0 * TILE;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int ch = (4 * (db ^ vxq) + vc2) << 3;
+          const uint16_t *v0 = &Vs[(16 * s + vrow) * D + ch + vhalf];
+          const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(AC_LDS(i16x4_t, v0));
+          const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(AC_LDS(i16x4_t, v0 + 4 * D));
+          const i16x4_t cat[2] = {lo4, hi4};
+          const bf16x8_t vf = *(const bf16x8_t *)cat;
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[s], acc_o[db], 0, 0, 0);
+        }
       }
     }
-    if (idx_next) rw_next = index_commit(tt + 2, pend_raw, pend_b, sbw + ((tt + 2) % 3) * ATT_KT);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of tile tt + 1 has landed
-    __syncthreads();                // all of it has; nobody reads tile tt any more
+    // All but this iteration's K and V loads have landed (the ring load of
+    // tile tt + 3 was issued before them); the barrier makes tile tt + 1 and
+    // the ring visible and frees the buffers of tile tt.
+    wait_vmcnt<2 * IPW>();
+    __syncthreads();
+    b0 = b0 == 2 ? 0 : b0 + 1;
   }
+  __builtin_amdgcn_s_waitcnt(0);  // no load may still write LDS when the block ends
 
   const float lsum = l_i + __shfl_xor(l_i, 32, 64);
   if (!qvalid) return;
@@ -423,9 +452,9 @@ void launch_attn(int D, const AttnArgs &a, int BH, int max_blocks, hipStream_t s
   aa.BH = BH;
   const long long total = ((long long)max_blocks * BH + 7) / 8 * 8;  // a multiple of the 8 XCDs
   if (D == 64)
-    hipLaunchKernelGGL(k_attn<64>, dim3((unsigned)total), dim3(256), 0, st, aa);
+    hipLaunchKernelGGL(k_attn<64>, dim3((unsigned)total), dim3(ATT_THREADS), 0, st, aa);
   else
-    hipLaunchKernelGGL(k_attn<128>, dim3((unsigned)total), dim3(256), 0, st, aa);
+    hipLaunchKernelGGL(k_attn<128>, dim3((unsigned)total), dim3(ATT_THREADS), 0, st, aa);
 }
 
 }  // namespace ac

@@ -10,7 +10,8 @@ constexpr int KPP_SMAX = 16384;  // most points a k-means++ subsample may hold
 constexpr int KPP_GRAM_MAX = 2048;  // subsamples up to this size seed from a distance matrix
 constexpr int SORT_TILE = 128;   // points per counting-sort tile (one wave)
 constexpr int SORT_GROUP = 32;   // tiles per group in the two-level scan over tiles
-constexpr int ATT_QT = 128;      // query rows per attention block
+constexpr int ATT_QT = 256;      // query rows per attention block (8 waves x 32)
+constexpr int ATT_THREADS = 512;
 constexpr int ATT_KT = 64;       // keys per attention tile
 constexpr int SEL_MAXN = 4096;   // most key clusters the select kernel sorts
 constexpr int ASSIGN_RES_MAX = 224;  // most centres the LDS-resident assignment holds
@@ -115,9 +116,10 @@ struct AttnArgs {
   int all_dense;
   int compensate;
   const uint16_t *kc, *vc;    // [BH, ncap, D] bf16 pseudo-keys / values
-  int *rows;                  // [BH, nqcap, L] key rows of each selection, concatenated
+  int *rows;                  // [BH, nqcap, rows_ld] key rows of each selection, concatenated
   int *rows_T;                // [BH, nqcap] their count (L on fallback heads)
-  float *pbias;               // [BH, nqcap, ncap] pseudo-key logit bias (base 2)
+  float *pbias;               // [BH, nqcap, pb_ld] pseudo-key logit bias (base 2)
+  int64_t rows_ld, pb_ld;     // row strides, multiples of the key tile
   const int *tile_off;        // [BH, nqcap + 1] first block of each query cluster
   uint16_t *O;                // [BH, L, D]
   float *lse;                 // [BH, L] or NULL

@@ -30,6 +30,12 @@
  *           except: a cold ac_cluster_k / cold ac_layer waits on the stream once per stage of
  *           Algorithm 1 (it reads the size of the unassigned set), and ac_layer waits at its end when
  *           host_stats is not NULL.  Calls on different streams with different buffers are independent.
+ *           ac_cluster_q and ac_cluster_k use disjoint parts of the workspace, so the two may run at
+ *           the same time on two streams that share one workspace (every other pair of calls that
+ *           share a workspace must be ordered).  ac_layer does so itself: it runs the query
+ *           clustering on a second stream of its own (created on first use, one per device and host
+ *           thread, default priority, kept until the process ends) and joins it before returning
+ *           control of `stream` to the caller's later work.
  * Errors    Every entry point returns an ac_status.  Argument errors (NULL pointers, bad shapes or
  *           parameters, a workspace that is too small) are detected before any device work is
  *           enqueued, so outputs are untouched.  AC_E_DEVICE reports a HIP runtime error; the text of
@@ -163,7 +169,7 @@ typedef struct ac_layer_stats {
 ac_status ac_params_default(ac_params *p);
 
 /* Validate shape and parameters and size the workspace.  *ncap_k receives the key-cluster
- * capacity (nmax - 1 + m0, at most L) and *ws_bytes the workspace that every entry point accepts
+ * capacity (nmax - 1 + m0) and *ws_bytes the workspace that every entry point accepts
  * for this shape and these parameters.  Host-only: touches no device. */
 ac_status ac_sizes(const ac_shape *s, const ac_params *p, int32_t *ncap_k, size_t *ws_bytes);
 

@@ -270,3 +270,32 @@ def test_layer_end_to_end_against_independent_oracle(tiny):
         mx, rl2 = attn_error(Og[bh], ref[bh]["O"])
         assert mx <= ATTN_MAX_ABS and rl2 <= ATTN_REL_L2, (bh, mx, rl2)
         assert hs["pairs"][bh] > 0
+
+
+def test_query_and_key_clustering_side_by_side_share_a_workspace(tiny):
+    """ac_cluster_q on a second stream beside ac_cluster_k, both on one
+    workspace, gives bit-identical clusters, statistics and attention to the
+    same calls made one after the other (the two use disjoint scratch)."""
+    import torch
+    import clustered_sparse_attention_amd as ac
+    Q, K, V = tiny
+    p = P(tau_rule=nm.TAU_MEAN_X, tau_param=1.5, m0=16, nmax=48, init_sample=8)
+    seq = Run(Q, K, V, p).all()
+    par = Run(Q, K, V, p)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    for _ in range(2):  # the second round reuses the workspace left by the first
+        side.wait_stream(main)
+        ac.ac_cluster_q(par.shape, par.cp, par.Q, None, par.q, par.ws, stream=side.cuda_stream)
+        par.cluster_k()
+        main.wait_stream(side)
+        par.score_select()
+        par.attn()
+    torch.cuda.synchronize()
+    for name in ("labels", "perm", "seg", "cent", "ncl", "rho"):
+        assert torch.equal(getattr(seq.q, name), getattr(par.q, name)), f"q.{name}"
+    for name in ("labels", "perm", "seg", "cent", "ncl"):
+        assert torch.equal(getattr(seq.k, name), getattr(par.k, name)), f"k.{name}"
+    for name in ("kmax", "kmin", "kmean", "vmean", "fallback", "tau", "stages"):
+        assert torch.equal(getattr(seq.st, name), getattr(par.st, name)), f"stats.{name}"
+    assert torch.equal(seq.O, par.O)
