@@ -194,14 +194,17 @@ __global__ __launch_bounds__(256) void k_assign(KmArgs a, CentOps op, int *__res
 // wave at a time.  Blocks are sized to one per compute unit, so there is no
 // per-tile barrier and each wave's point loads overlap the other waves'
 // MFMA work.
-template <int D>
-__global__ __launch_bounds__(1024) void k_assign_res(KmArgs a, CentOps op, int *__restrict__ labels, int64_t lab_hs,
-                                                     int BH) {
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void k_assign_res(KmArgs a, CentOps op, int *__restrict__ labels, int64_t lab_hs,
+                                                   int BH, int mpmax) {
   constexpr int KS = D / 32;
   constexpr int LDSROW = D + 8;
-  __shared__ uint16_t s_hi[ASSIGN_RES_MAX * LDSROW];
-  __shared__ uint16_t s_lo[ASSIGN_RES_MAX * LDSROW];
-  __shared__ __align__(16) float s_norm[ASSIGN_RES_MAX];
+  constexpr int NW = NT / 64;
+  // LDS sized for the largest centre count of the launch: hi and lo rows, norms
+  extern __shared__ __align__(16) uint16_t lds_res[];
+  uint16_t *s_hi = lds_res;
+  uint16_t *s_lo = lds_res + mpmax * LDSROW;
+  float *s_norm = (float *)(lds_res + 2 * mpmax * LDSROW);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int l16 = lane & 15, g = lane >> 4;
   // this block's share of the flattened sub-tile list
@@ -222,7 +225,7 @@ __global__ __launch_bounds__(1024) void k_assign_res(KmArgs a, CentOps op, int *
       const uint16_t *glo = op.lo + (int64_t)h * op.cap * D;
       const float *gnorm = op.norm + (int64_t)h * op.cap;
       __syncthreads();  // previous head's centres no longer read
-      for (int q = threadIdx.x; q < mp * (D / 8); q += 1024) {
+      for (int q = threadIdx.x; q < mp * (D / 8); q += NT) {
         const int r = q / (D / 8), cc = (q % (D / 8)) * 8;
         u32x4_t vh = {0, 0, 0, 0}, vl = {0, 0, 0, 0};
         if (r < m) {
@@ -232,11 +235,11 @@ __global__ __launch_bounds__(1024) void k_assign_res(KmArgs a, CentOps op, int *
         *(u32x4_t *)&s_hi[r * LDSROW + cc] = vh;
         *(u32x4_t *)&s_lo[r * LDSROW + cc] = vl;
       }
-      for (int c = threadIdx.x; c < mp; c += 1024) s_norm[c] = c < m ? gnorm[c] : 0.f;
+      for (int c = threadIdx.x; c < mp; c += NT) s_norm[c] = c < m ? gnorm[c] : 0.f;
       __syncthreads();
       const uint16_t *X = a.X + (int64_t)h * a.x_hs;
       const int *idx = a.idx ? a.idx + (int64_t)h * a.idx_hs : nullptr;
-      for (int64_t t = r0 + wave; t < r1; t += 16) {
+      for (int64_t t = r0 + wave; t < r1; t += NW) {
         const int wbase = (int)(t - hb) * 64;
         bf16x8_t af[4][KS];
 #pragma unroll
@@ -888,9 +891,21 @@ static int device_cus() {
 void launch_assign(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, int nmax_pts, int *labels,
                    int64_t lab_hs, hipStream_t st) {
   if (mmax <= ASSIGN_RES_MAX) {
+    // 512 threads and LDS for this launch's centres only, one block per CU:
+    // half of each CU's registers stay free for work on other streams
+    constexpr int NT = 512;
+    const int mpmax = (mmax + 15) & ~15;
+    const size_t lds = (size_t)mpmax * (D + 8) * 2 * 2 + (size_t)mpmax * 4;
     const int64_t subs = (int64_t)BH * ((nmax_pts + 63) / 64);
-    const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(device_cus(), (subs + 15) / 16));
-    AC_D_DISPATCH(D, hipLaunchKernelGGL(k_assign_res<DD>, dim3(blocks), dim3(1024), 0, st, a, op, labels, lab_hs, BH));
+    const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(device_cus(), (subs + NT / 64 - 1) / (NT / 64)));
+    AC_D_DISPATCH(D, {
+      static bool lds_ok = hipFuncSetAttribute((const void *)k_assign_res<DD, NT>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)((size_t)ASSIGN_RES_MAX * (DD + 8) * 4 + ASSIGN_RES_MAX * 4)) ==
+                           hipSuccess;
+      (void)lds_ok;  // a refusal shows up as a launch error
+      hipLaunchKernelGGL((k_assign_res<DD, NT>), dim3(blocks), dim3(NT), lds, st, a, op, labels, lab_hs, BH, mpmax);
+    });
     return;
   }
   AC_D_DISPATCH(D, hipLaunchKernelGGL(k_assign<DD>, g2((nmax_pts + 255) / 256, BH), dim3(256), 0, st, a, op, labels,

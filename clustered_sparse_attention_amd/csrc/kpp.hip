@@ -155,23 +155,56 @@ __global__ __launch_bounds__(KPP_THREADS) void k_kpp(KmArgs a, double *__restric
 // included) accumulated by the same sequential fp64 fma chain over d, so
 // identical rows give exactly 0; the sequential part then reads one G row per
 // round instead of the whole subsample.
+// Distance matrix of the seeding subsample on fp64 matrix cores
+// (v_mfma_f64_16x16x4_f64).  In k-step ks, lane group g = lane / 16 holds
+// dimension g * D/4 + ks of its row, so each lane reads one contiguous run of
+// D/4 values of its row once.  A dot product is the same sequence of MFMA
+// accumulations wherever its pair sits, and the squared norms are the
+// diagonal of the same product, so G = (|x_j|^2 + |x_k|^2) - 2 x_j.x_k is
+// exactly 0 for identical rows.
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
 template <int D>
-__global__ __launch_bounds__(256) void k_kpp_norms(KmArgs a, int init_sample, double *__restrict__ nx, int smax) {
+AC_DEV void kpp_rows(const KmArgs &a, int h, int n, int s, int r0, u32x4_t (&v)[D / 32]) {
+  // lane's run: row r0 + lane % 16 of the subsample, dims [g * D/4, (g + 1) * D/4)
+  const int lane = threadIdx.x & 63, j = r0 + (lane & 15), g = lane >> 4;
+  if (j < s) {
+    const int li = (int)(((int64_t)j * n) / s);
+    const int64_t row = a.idx ? (int64_t)a.idx[(int64_t)h * a.idx_hs + li] : (int64_t)li;
+    const u32x4_t *src = (const u32x4_t *)(a.X + (int64_t)h * a.x_hs + row * D + g * (D / 4));
+#pragma unroll
+    for (int q = 0; q < D / 32; ++q) v[q] = src[q];
+  } else {
+#pragma unroll
+    for (int q = 0; q < D / 32; ++q) v[q] = (u32x4_t){0, 0, 0, 0};
+  }
+}
+template <int D> AC_DEV double kpp_elem(const u32x4_t (&v)[D / 32], int ks) {
+  const uint32_t w = v[ks >> 3][(ks >> 1) & 3];
+  return (double)bf2f((uint16_t)((ks & 1) ? (w >> 16) : (w & 0xFFFFu)));
+}
+
+// |x_j|^2 as the diagonal of a 16 x 16 block product of the rows with themselves
+template <int D>
+__global__ __launch_bounds__(64) void k_kpp_norms(KmArgs a, int init_sample, double *__restrict__ nx, int smax) {
   const int h = blockIdx.y;
   const int n = a.n[h], m = a.m[h];
   if (n <= 0 || m <= 0) return;
   const int s = init_sample > 0 ? min(n, init_sample * m) : n;
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= s) return;
-  const int li = (int)(((int64_t)j * n) / s);
-  const int64_t row = a.idx ? (int64_t)a.idx[(int64_t)h * a.idx_hs + li] : (int64_t)li;
-  const uint16_t *xr = a.X + (int64_t)h * a.x_hs + row * D;
-  double acc = 0.0;
-  for (int d = 0; d < D; ++d) {
-    const double x = (double)bf2f(xr[d]);
-    acc = fma(x, x, acc);
+  const int r0 = blockIdx.x * 16;
+  if (r0 >= s) return;
+  u32x4_t v[D / 32];
+  kpp_rows<D>(a, h, n, s, r0, v);
+  f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int ks = 0; ks < D / 4; ++ks) {
+    const double x = kpp_elem<D>(v, ks);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(x, x, acc, 0, 0, 0);
   }
-  nx[(int64_t)h * smax + j] = acc;
+  // lane holds column lane % 16 and rows lane / 16 + 4 p: the diagonal entry of
+  // column c sits in lane c + 16 (c % 4), p = c / 4
+  const int lane = threadIdx.x, col = lane & 15, g = lane >> 4;
+  if ((col & 3) == g && r0 + col < s) nx[(int64_t)h * smax + r0 + col] = acc[col >> 2];
 }
 
 template <int D>
@@ -184,63 +217,57 @@ __global__ __launch_bounds__(256) void k_kpp_gram(KmArgs a, int init_sample, con
   const int nt = (s + 63) / 64;
   const int tj = blockIdx.x / ((smax + 63) / 64), tk = blockIdx.x % ((smax + 63) / 64);
   if (tj >= nt || tk >= nt || tk < tj) return;
-  // tiles transposed in LDS: xs[d][row] so 4 consecutive rows are one 8-byte read
-  __shared__ uint16_t xj[D][64 + 4], xk[D][64 + 4];
-  const int *idx = a.idx ? a.idx + (int64_t)h * a.idx_hs : nullptr;
-  const uint16_t *X = a.X + (int64_t)h * a.x_hs;
-  for (int q = threadIdx.x; q < 64 * (D / 8); q += 256) {
-    const int r = q / (D / 8), c8 = (q % (D / 8)) * 8;
-    u32x4_t vj = {0, 0, 0, 0}, vk = {0, 0, 0, 0};
-    const int j = tj * 64 + r, k = tk * 64 + r;
-    if (j < s) {
-      const int li = (int)(((int64_t)j * n) / s);
-      vj = *(const u32x4_t *)&X[(idx ? (int64_t)idx[li] : (int64_t)li) * D + c8];
-    }
-    if (k < s) {
-      const int li = (int)(((int64_t)k * n) / s);
-      vk = *(const u32x4_t *)&X[(idx ? (int64_t)idx[li] : (int64_t)li) * D + c8];
-    }
-    const uint16_t *ej = (const uint16_t *)&vj, *ek = (const uint16_t *)&vk;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave: 32 x 32 block (rows j0 + [0, 32), columns k0 + [0, 32)) as 2 x 2 MFMA tiles
+  const int j0 = tj * 64 + (wave >> 1) * 32, k0 = tk * 64 + (wave & 1) * 32;
+  u32x4_t vj[2][D / 32], vk[2][D / 32];
+  kpp_rows<D>(a, h, n, s, j0, vj[0]);
+  kpp_rows<D>(a, h, n, s, j0 + 16, vj[1]);
+  kpp_rows<D>(a, h, n, s, k0, vk[0]);
+  kpp_rows<D>(a, h, n, s, k0 + 16, vk[1]);
+  f64x4_t acc[2][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      xj[c8 + i][r] = ej[i];
-      xk[c8 + i][r] = ek[i];
-    }
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int w = 0; w < 2; ++w) acc[u][w] = (f64x4_t){0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int ks = 0; ks < D / 4; ++ks) {
+    const double x0 = kpp_elem<D>(vj[0], ks), x1 = kpp_elem<D>(vj[1], ks);
+    const double y0 = kpp_elem<D>(vk[0], ks), y1 = kpp_elem<D>(vk[1], ks);
+    acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(x0, y0, acc[0][0], 0, 0, 0);
+    acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(x0, y1, acc[0][1], 0, 0, 0);
+    acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(x1, y0, acc[1][0], 0, 0, 0);
+    acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(x1, y1, acc[1][1], 0, 0, 0);
   }
-  __syncthreads();
-  const int rj = (threadIdx.x >> 4) * 4, rk = (threadIdx.x & 15) * 4;
-  double acc[4][4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) acc[u][v] = 0.0;
-  for (int d = 0; d < D; ++d) {
-    const u32x2_t wj = *(const u32x2_t *)&xj[d][rj];
-    const u32x2_t wk = *(const u32x2_t *)&xk[d][rk];
-    double aj[4], ak[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      aj[u] = (double)bf2f((uint16_t)(u & 1 ? wj[u >> 1] >> 16 : wj[u >> 1] & 0xFFFFu));
-      ak[u] = (double)bf2f((uint16_t)(u & 1 ? wk[u >> 1] >> 16 : wk[u >> 1] & 0xFFFFu));
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[u][v] = fma(aj[u], ak[v], acc[u][v]);
-  }
+  // lane holds column k = k0 + 16 w + lane % 16 and rows j = j0 + 16 u + lane / 16 + 4 p
   double *Gh = G + (int64_t)h * smax * smax;
   const double *nxh = nx + (int64_t)h * smax;
+  __shared__ double tr[4][32][33];  // this wave's block, for the transposed (symmetric) write
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int j = tj * 64 + rj + u, k = tk * 64 + rk + v;
-      if (j < s && k < s) {
-        const double g = fmax((nxh[j] + nxh[k]) - 2.0 * acc[u][v], 0.0);
-        Gh[(int64_t)j * smax + k] = g;
-        Gh[(int64_t)k * smax + j] = g;
+    for (int w = 0; w < 2; ++w) {
+      const int kl = 16 * w + (lane & 15);
+      const int k = k0 + kl;
+      const double nk = k < s ? nxh[k] : 0.0;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int jl = 16 * u + (lane >> 4) + 4 * p;
+        const int j = j0 + jl;
+        const double nj = j < s ? nxh[j] : 0.0;
+        const double g = fmax((nj + nk) - 2.0 * acc[u][w][p], 0.0);
+        tr[wave][jl][kl] = g;
+        if (j < s && k < s) Gh[(int64_t)j * smax + k] = g;
       }
     }
+  if (tk == tj) return;  // diagonal tiles hold both halves already
+  __syncthreads();
+  // G[k][j] = G[j][k]: lanes run along j, so the writes are coalesced
+  for (int q = lane; q < 32 * 32; q += 64) {
+    const int kl = q >> 5, jl = q & 31;
+    const int j = j0 + jl, k = k0 + kl;
+    if (j < s && k < s) Gh[(int64_t)k * smax + j] = tr[wave][jl][kl];
+  }
 }
 
 template <int D>
@@ -312,11 +339,11 @@ void launch_kpp_gram(int D, const KmArgs &a, int BH, int smax, double *nx, doubl
                      int role, int stage, hipStream_t st) {
   const int nt = (smax + 63) / 64;
   if (D == 64) {
-    hipLaunchKernelGGL(k_kpp_norms<64>, dim3((smax + 255) / 256, BH), dim3(256), 0, st, a, init_sample, nx, smax);
+    hipLaunchKernelGGL(k_kpp_norms<64>, dim3((smax + 15) / 16, BH), dim3(64), 0, st, a, init_sample, nx, smax);
     hipLaunchKernelGGL(k_kpp_gram<64>, dim3(nt * nt, BH), dim3(256), 0, st, a, init_sample, nx, G, smax);
     hipLaunchKernelGGL(k_kpp_seq<64>, dim3(BH), dim3(KPP_THREADS), 0, st, a, G, smax, init_sample, seed, role, stage);
   } else {
-    hipLaunchKernelGGL(k_kpp_norms<128>, dim3((smax + 255) / 256, BH), dim3(256), 0, st, a, init_sample, nx, smax);
+    hipLaunchKernelGGL(k_kpp_norms<128>, dim3((smax + 15) / 16, BH), dim3(64), 0, st, a, init_sample, nx, smax);
     hipLaunchKernelGGL(k_kpp_gram<128>, dim3(nt * nt, BH), dim3(256), 0, st, a, init_sample, nx, G, smax);
     hipLaunchKernelGGL(k_kpp_seq<128>, dim3(BH), dim3(KPP_THREADS), 0, st, a, G, smax, init_sample, seed, role, stage);
   }
