@@ -64,7 +64,7 @@ def _abi(kw):
 class Layer:
     """Device buffers of one layer and the four entry points."""
 
-    def __init__(self, Qd, Kd, Vd, shape, params):
+    def __init__(self, Qd, Kd, Vd, shape, params, tail_block=0):
         import torch
         import clustered_sparse_attention_amd as ac
         self.ac = ac
@@ -82,6 +82,10 @@ class Layer:
         self.st = ac.KStats(BH, self.ncap, d, dev)
         self.sel = ac.Selection(BH, nq, self.ncap, dev, score=False)
         self.O = torch.empty_like(Qd)
+        self.tail_block = tail_block
+        if tail_block:
+            self.qm = ac.Clusters(BH, L, nq, d, dev, rho=False)
+            self.selm = ac.Selection(BH, nq, self.ncap, dev, score=False)
         self.torch = torch
         self.side = torch.cuda.Stream()  # default priority
 
@@ -103,25 +107,35 @@ class Layer:
         main.wait_stream(self.side)
         if ev: ev[4].record(main)
         ac.ac_score_select(self.shape, self.p, self.q, self.k, self.st, self.sel, self.ws)
+        if self.tail_block:
+            ac.ac_tail_merge(self.shape, self.p, self.tail_block, self.q, self.sel, self.qm, self.selm, self.ws)
         if ev: ev[5].record(main)
-        ac.ac_sparse_attn(self.shape, self.p, self.Q, self.K, self.V, self.q, self.k, self.st, self.sel, self.O,
-                          None, self.ws)
+        self.attn_only()
         if ev: ev[6].record(main)
 
     def attn_only(self):
-        self.ac.ac_sparse_attn(self.shape, self.p, self.Q, self.K, self.V, self.q, self.k, self.st, self.sel, self.O,
+        q, sel = (self.qm, self.selm) if self.tail_block else (self.q, self.sel)
+        self.ac.ac_sparse_attn(self.shape, self.p, self.Q, self.K, self.V, q, self.k, self.st, sel, self.O,
                                None, self.ws)
+
+    def query_blocks(self, block):
+        """Query blocks of `block` rows the attention runs, before and after the
+        tail merge (equal when it is off)."""
+        b0 = np.diff(self.q.seg.cpu().numpy(), axis=1)
+        b1 = np.diff(self.qm.seg.cpu().numpy(), axis=1) if self.tail_block else b0
+        return int(((b0 + block - 1) // block).sum()), int(((b1 + block - 1) // block).sum())
 
 
 def pairs_of(layer):
     """Query-key pairs the attention computed (dense heads: L*L)."""
     L = layer.shape.L
-    seg_q = layer.q.seg.cpu().numpy()
+    q, sel = (layer.qm, layer.selm) if layer.tail_block else (layer.q, layer.sel)
+    seg_q = q.seg.cpu().numpy()
     cnt_q = np.diff(seg_q, axis=1)
     seg_k = layer.k.seg.cpu().numpy()
     cnt_k = np.diff(seg_k, axis=1)
-    lst = layer.sel.list.cpu().numpy()
-    n = layer.sel.n.cpu().numpy()
+    lst = sel.list.cpu().numpy()
+    n = sel.n.cpu().numpy()
     fb = layer.st.fallback.cpu().numpy()
     dense_all = layer.p.sel_mode == 3
     tot = 0
@@ -309,6 +323,9 @@ def main():
     ap.add_argument("--variant", default="density", choices=["density", "topp", "dense"])
     ap.add_argument("--compensate", type=int, default=0)
     ap.add_argument("--heads", type=int, default=0, help="run only this many heads (0 = all)")
+    ap.add_argument("--tail-block", type=int, default=0,
+                    help="merge query-cluster tails for attention blocks of this many rows before the attention "
+                         "(iCATS tail merging; 0 = off)")
     ap.add_argument("--no-baselines", action="store_true", help="skip dense baselines and the CPU oracle")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a plain copy of this many bytes")
@@ -344,7 +361,7 @@ def main():
     Qd, Kd, Vd = dev(Q), dev(K), dev(V)
     kw = workload_params(args.workload, args.variant, args.compensate)
     params = _abi(kw)
-    layer = Layer(Qd, Kd, Vd, (w.B, w.H, w.L, w.d), params)
+    layer = Layer(Qd, Kd, Vd, (w.B, w.H, w.L, w.d), params, tail_block=args.tail_block)
 
     for _ in range(args.warmup):
         layer.step()
@@ -397,6 +414,10 @@ def main():
         "phase_ms": {"cluster_q": round(float(phase_ms[0]), 3), "cluster_k": round(float(phase_ms[1]), 3),
                      "clustering_q_beside_k": round(float(phase_ms[2]), 3),
                      "score_select": round(float(phase_ms[3]), 3), "sparse_attn": round(attn_ms, 3)},
+        "_phase_note": "score_select includes ac_tail_merge when tail merging is on",
+        "tail_merge": None if not args.tail_block else dict(
+            zip(("block", "query_blocks_before", "query_blocks_after"),
+                (args.tail_block,) + layer.query_blocks(args.tail_block))),
         "layer": {"density_pairs": round(pairs / (w.BH * float(w.L) ** 2), 4), "fallback_heads": int(fb.sum()),
                   "key_clusters_min_max": [int(ncl.min()), int(ncl.max())],
                   "stages_max": int(stages.max())},

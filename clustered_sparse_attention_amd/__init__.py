@@ -22,7 +22,7 @@ AC_SCORE_QUEST, AC_SCORE_MEAN = range(2)
 AC_SEL_TOPK, AC_SEL_DENSITY, AC_SEL_TOPP, AC_SEL_DENSE = range(4)
 
 ENTRY_POINTS = ("ac_params_default", "ac_sizes", "ac_cluster_q", "ac_cluster_k", "ac_score_select",
-                "ac_sparse_attn", "ac_layer", "ac_status_str", "ac_last_error")
+                "ac_sparse_attn", "ac_tail_merge", "ac_layer", "ac_status_str", "ac_last_error")
 
 
 class ACError(RuntimeError):
@@ -44,7 +44,8 @@ class Params(ctypes.Structure):
                 ("m0", ctypes.c_int32), ("nmax", ctypes.c_int32), ("tau_rule", ctypes.c_int32),
                 ("tau_param", ctypes.c_float), ("score_mode", ctypes.c_int32), ("sel_mode", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("sel_param", ctypes.c_float), ("compensate", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("init_sample", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+                ("scale", ctypes.c_float), ("init_sample", ctypes.c_int32), ("tail_block", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32), ("seed", ctypes.c_uint64)]
 
 
 class CClusters(ctypes.Structure):
@@ -101,6 +102,10 @@ def load() -> ctypes.CDLL:
                                    ctypes.POINTER(CClusters), ctypes.POINTER(CClusters), ctypes.POINTER(CKStats),
                                    ctypes.POINTER(CSelection), vp, vp, vp, ctypes.c_size_t, vp]
     lib.ac_sparse_attn.restype = st
+    lib.ac_tail_merge.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), ctypes.c_int32,
+                                  ctypes.POINTER(CClusters), ctypes.POINTER(CSelection), ctypes.POINTER(CClusters),
+                                  ctypes.POINTER(CSelection), vp, ctypes.c_size_t, vp]
+    lib.ac_tail_merge.restype = st
     lib.ac_layer.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), vp, vp, vp, ctypes.POINTER(CState), vp,
                              ctypes.POINTER(CLayerStats), vp, ctypes.c_size_t, vp]
     lib.ac_layer.restype = st
@@ -253,6 +258,13 @@ def ac_sparse_attn(shape, params, Q, K, V, q: Clusters, k: Clusters, stats: KSta
     _check(load().ac_sparse_attn(ctypes.byref(shape), ctypes.byref(params), _ptr(Q), _ptr(K), _ptr(V),
                                  ctypes.byref(q.c()), ctypes.byref(k.c()), ctypes.byref(stats.c()),
                                  ctypes.byref(sel.c()), _ptr(O), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def ac_tail_merge(shape, params, block: int, q_in: Clusters, sel_in: Selection, q_out: Clusters,
+                  sel_out: Selection, ws, stream=None):
+    _check(load().ac_tail_merge(ctypes.byref(shape), ctypes.byref(params), int(block), ctypes.byref(q_in.c()),
+                                ctypes.byref(sel_in.c()), ctypes.byref(q_out.c()), ctypes.byref(sel_out.c()),
+                                _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def ac_layer(shape, params, Q, K, V, state: State, O, ws, host_stats: bool = False, stream=None):

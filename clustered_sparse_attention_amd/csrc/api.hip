@@ -81,6 +81,8 @@ ac_status check_params(const ac_shape *s, const ac_params *p) {
   if (p->compensate != 0 && p->compensate != 1) return fail(AC_E_ARG, "compensate must be 0 or 1");
   if (!(p->scale >= 0.f) || !std::isfinite(p->scale)) return fail(AC_E_ARG, "scale must be finite and >= 0");
   if (p->init_sample < 0) return fail(AC_E_ARG, "init_sample must be >= 0");
+  if (p->tail_block < 0) return fail(AC_E_ARG, "tail_block must be >= 0");
+  if (p->reserved0 != 0) return fail(AC_E_ARG, "reserved0 must be 0");
   const int64_t ncap = (int64_t)p->nmax - 1 + p->m0;
   if (ncap > SEL_MAXN) return fail(AC_E_UNSUPPORTED, "nmax - 1 + m0 = %lld exceeds %d key clusters", (long long)ncap, SEL_MAXN);
   const int64_t mmax = std::max<int64_t>(std::min<int64_t>(p->nq, s->L), std::min<int64_t>(p->m0, s->L));
@@ -112,6 +114,8 @@ struct Plan {
   size_t k_labels, k_perm, k_seg, k_cent, k_ncl;
   size_t kmax, kmin, kmean, vmean, fb, tau, mse, stages;
   size_t sel_list, sel_n, sel_mask, sel_score;
+  // tail merging: its plan, and ac_layer's merged clusters and selection
+  size_t tm_plan, m_labels, m_perm, m_seg, m_list, m_n, m_mask;
 };
 
 // stride of the per-selection key row lists: whole key tiles
@@ -205,6 +209,13 @@ Plan make_plan(const ac_shape *s, const ac_params *p) {
   P.sel_n = take(BH * P.nq * 4);
   P.sel_mask = take(BH * P.nq * (size_t)P.mwords * 4);
   P.sel_score = take(BH * P.nq * (size_t)P.ncapk * 4);
+  P.tm_plan = take(BH * 8 * (size_t)(P.nq + 1) * 4);
+  P.m_labels = take(BH * L * 4);
+  P.m_perm = take(BH * L * 4);
+  P.m_seg = take(BH * (P.nq + 1) * 4);
+  P.m_list = take(BH * P.nq * (size_t)P.ncapk * 4);
+  P.m_n = take(BH * P.nq * 4);
+  P.m_mask = take(BH * P.nq * (size_t)P.mwords * 4);
   P.total = off + 256;  // slack for aligning the base pointer
   return P;
 }
@@ -475,6 +486,33 @@ ac_status do_score_select(const Plan &P, const ac_params *p, const ac_clusters *
   return AC_OK;
 }
 
+ac_status do_tail_merge(const Plan &P, int block, const ac_clusters *qi, const ac_selection *si, ac_clusters *qo,
+                        ac_selection *so, void *ws, hipStream_t st) {
+  TailArgs t;
+  t.seg_in = qi->seg;
+  t.perm_in = qi->perm;
+  t.ncl = qi->ncl;
+  t.list_in = si->list;
+  t.n_in = si->n;
+  t.mask_in = si->mask;
+  t.seg_out = qo->seg;
+  t.perm_out = qo->perm;
+  t.labels_out = qo->labels;
+  t.list_out = so->list;
+  t.n_out = so->n;
+  t.mask_out = so->mask;
+  t.plan = at<int>(ws, P.tm_plan);
+  t.nq = P.nq;
+  t.ncapk = P.ncapk;
+  t.mwords = P.mwords;
+  t.L = P.L;
+  t.block = block > 0 ? block : ATT_QT;
+  launch_tail_merge(t, P.BH, st);
+  launch_copy_i32(qi->ncl, qo->ncl, P.BH, st);
+  AC_CHECK_LAUNCH();
+  return AC_OK;
+}
+
 ac_status do_attn(const Plan &P, const ac_params *p, const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                   const ac_clusters *q, const ac_clusters *k, const ac_kstats *stats, const ac_selection *sel,
                   uint16_t *O, float *lse, void *ws, hipStream_t st) {
@@ -633,6 +671,29 @@ AC_API ac_status ac_sparse_attn(const ac_shape *s, const ac_params *p, const uin
   return do_attn(P, p, Q, K, V, q, k, stats, sel, O, lse, ws, (hipStream_t)stream);
 }
 
+AC_API ac_status ac_tail_merge(const ac_shape *s, const ac_params *p, int32_t block, const ac_clusters *q_in,
+                               const ac_selection *sel_in, ac_clusters *q_out, ac_selection *sel_out, void *ws,
+                               size_t ws_bytes, ac_stream_t stream) {
+  AC_TRY(check_shape(s));
+  AC_TRY(check_params(s, p));
+  if (block < 0) return fail(AC_E_ARG, "block must be >= 0");
+  Plan P = make_plan(s, p);
+  AC_TRY(check_clusters(q_in, "query", P.nq, false));
+  if (q_in->ncap != P.nq) return fail(AC_E_ARG, "query clusters ncap must be min(nq, L) = %d", P.nq);
+  if (!q_out || !q_out->labels || !q_out->perm || !q_out->seg || !q_out->ncl)
+    return fail(AC_E_ARG, "output query clusters is NULL or has a NULL array");
+  if (q_out->ncap != P.nq) return fail(AC_E_ARG, "output query clusters ncap must be min(nq, L) = %d", P.nq);
+  if (q_out->perm == q_in->perm || q_out->seg == q_in->seg || q_out->labels == q_in->labels)
+    return fail(AC_E_ARG, "output query clusters alias the input");
+  AC_TRY(check_sel(sel_in, P.ncapk));
+  AC_TRY(check_sel(sel_out, P.ncapk));
+  if (sel_out->list == sel_in->list || sel_out->n == sel_in->n || sel_out->mask == sel_in->mask)
+    return fail(AC_E_ARG, "output selection aliases the input");
+  AC_TRY(check_ws(P, ws, ws_bytes));
+  AC_TRY(check_device());
+  return do_tail_merge(P, block, q_in, sel_in, q_out, sel_out, ws, (hipStream_t)stream);
+}
+
 namespace ac {
 namespace {
 // A second stream (default priority) per device and host thread, created on
@@ -695,7 +756,14 @@ AC_API ac_status ac_layer(const ac_shape *s, const ac_params *p, const uint16_t 
   AC_TRY(sq);
   AC_TRY(sk);
   AC_TRY(do_score_select(P, p, &q, &k, &ks, &sel, ws, st));
-  AC_TRY(do_attn(P, p, Q, K, V, &q, &k, &ks, &sel, O, nullptr, ws, st));
+  if (p->tail_block > 0) {
+    ac_clusters qm{P.nq, at<int>(ws, P.m_labels), at<int>(ws, P.m_perm), at<int>(ws, P.m_seg), q.cent, q.ncl, q.rho};
+    ac_selection sm{P.ncapk, at<int>(ws, P.m_list), at<int>(ws, P.m_n), at<uint32_t>(ws, P.m_mask), nullptr};
+    AC_TRY(do_tail_merge(P, p->tail_block, &q, &sel, &qm, &sm, ws, st));
+    AC_TRY(do_attn(P, p, Q, K, V, &qm, &k, &ks, &sm, O, nullptr, ws, st));
+  } else {
+    AC_TRY(do_attn(P, p, Q, K, V, &q, &k, &ks, &sel, O, nullptr, ws, st));
+  }
   // carry the centres (and, after a cold step, counts, flags and tau) to the next step
   AC_HIP(hipMemcpyAsync(state->cent_q, q.cent, (size_t)BH * P.nq * D * 4, hipMemcpyDeviceToDevice, st));
   AC_HIP(hipMemcpyAsync(state->cent_k, k.cent, (size_t)BH * P.ncapk * D * 4, hipMemcpyDeviceToDevice, st));

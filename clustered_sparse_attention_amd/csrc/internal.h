@@ -129,6 +129,18 @@ struct AttnArgs {
   int BH;
 };
 
+// Tail merging of query clusters (see merge.hip).
+struct TailArgs {
+  const int *seg_in, *perm_in, *ncl;  // [BH, nq + 1], [BH, L], [BH]
+  const int *list_in, *n_in;          // [BH, nq, ncapk], [BH, nq]
+  const uint32_t *mask_in;            // [BH, nq, mwords]
+  int *seg_out, *perm_out, *labels_out;
+  int *list_out, *n_out;
+  uint32_t *mask_out;
+  int *plan;                          // [BH, 8, nq + 1]
+  int nq, ncapk, mwords, L, block;
+};
+
 // kmeans.hip
 void launch_qnorm(int D, const uint16_t *Q, uint16_t *Qh, float *qn, int64_t rows, hipStream_t st);
 void launch_kpp(int D, const KmArgs &a, int BH, double *d2buf, int init_sample, uint64_t seed, int role, int stage,
@@ -167,5 +179,8 @@ void launch_select(const SelectArgs &a, int BH, hipStream_t st);
 void launch_attn_prep(int D, const AttnArgs &a, const float *kmean, const float *vmean, uint16_t *kc, uint16_t *vc,
                       int *tile_off, long long *pairs, int BH, hipStream_t st);
 void launch_attn(int D, const AttnArgs &a, int BH, int max_blocks, hipStream_t st);
+
+// merge.hip
+void launch_tail_merge(const TailArgs &t, int BH, hipStream_t st);
 
 }  // namespace ac

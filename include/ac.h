@@ -106,6 +106,9 @@ typedef struct ac_params {
   float scale;         /* softmax scale; 0 means 1/sqrt(d) (0) */
   int32_t init_sample; /* k-means++ runs on a strided subsample of min(n, init_sample * m) points;
                           0 = every point (8).  The subsample may hold at most 16384 points. */
+  int32_t tail_block;  /* ac_layer only: > 0 applies ac_tail_merge with this query block before the
+                          attention (iCATS tail merging); 0 = off (0) */
+  int32_t reserved0;   /* must be 0 */
   uint64_t seed;       /* seed of the counter-based SplitMix64 stream of k-means++ (0) */
 } ac_params;
 
@@ -214,8 +217,28 @@ ac_status ac_sparse_attn(const ac_shape *s, const ac_params *p, const uint16_t *
                          const ac_kstats *stats, const ac_selection *sel, uint16_t *O, float *lse,
                          void *ws, size_t ws_bytes, ac_stream_t stream);
 
+/* Tail merging of the query clusters before the attention ("iCATS: Fast Video Generation via
+ * Interaction-Aware Sparse Attention and Timestep-Adaptive Sparsity", method section, tail-merging
+ * design, and its worked example).  The attention processes each query cluster in blocks of `block`
+ * rows (0: the attention kernel's own block, 256), so the last, partial block of every cluster costs a
+ * whole block for every key it attends to.  Per head: (1) query clusters with identical key-cluster
+ * masks merge into the lowest-numbered one (token lists appended in cluster order; no token's key
+ * set changes); (2) among the clusters that still have a tail t = size mod block > 0, each pair that
+ * are each other's nearest neighbour in Hamming distance between masks (ties to the lower index) and
+ * whose tails sum to at most `block` moves the smaller tail (ties: the higher-numbered cluster's) to
+ * the other cluster, whose mask becomes the OR of both and whose selection list gains the donor's
+ * extra clusters in the donor's order.  Empty clusters take part in neither pass.  Every token
+ * attends afterwards to a superset of its original key clusters; the block count never grows.
+ * Writes q_out->labels, perm, seg and ncl (cent and rho are not touched and may alias q_in's), and
+ * sel_out->list, n and mask (score is not touched).  q_out and sel_out must not alias the inputs.
+ * q_in/q_out ncap must be min(nq, L); sel capacities as for ac_score_select. */
+ac_status ac_tail_merge(const ac_shape *s, const ac_params *p, int32_t block, const ac_clusters *q_in,
+                        const ac_selection *sel_in, ac_clusters *q_out, ac_selection *sel_out, void *ws,
+                        size_t ws_bytes, ac_stream_t stream);
+
 /* The whole layer (AdaCluster Algorithm 3 with the optional compensation): ac_cluster_q,
- * ac_cluster_k, ac_score_select and ac_sparse_attn on buffers carved from the workspace.  Cold when
+ * ac_cluster_k, ac_score_select, ac_tail_merge when p->tail_block > 0, and ac_sparse_attn on
+ * buffers carved from the workspace.  Cold when
  * !state->valid (fills the state and sets valid = 1), warm otherwise.  host_stats may be NULL. */
 ac_status ac_layer(const ac_shape *s, const ac_params *p, const uint16_t *Q, const uint16_t *K,
                    const uint16_t *V, ac_state *state, uint16_t *O, ac_layer_stats *host_stats,

@@ -13,6 +13,7 @@ from .multistage import cluster_keys, warm_keys
 from .stats import key_stats, counting_sort
 from .score import scores, select
 from .attention import dense_rows, sparse_rows
+from . import tailmerge
 
 
 def run_head(Qb, Kb, Vb, p, bh: int, rows=None, warm=None):
@@ -44,13 +45,18 @@ def run_head(Qb, Kb, Vb, p, bh: int, rows=None, warm=None):
     Q, K, V = bf16_to_f64(Qb), bf16_to_f64(Kb), bf16_to_f64(Vb)
     scale = p.attn_scale(d)
     dense = bool(kc["fallback"]) or p.sel_mode == SEL_DENSE
+    merged = None
+    q_labels = qc["labels"]
+    if p.tail_block > 0 and not dense:
+        merged = merge_queries(q_labels, len(sel), sel, kst["count"].shape[0], p.tail_block)
+        q_labels, sel = merged["labels"], merged["sel"]
     if dense:
         O, lse = dense_rows(Q, K, V, rows, scale)
     else:
-        O, lse = sparse_rows(Q, K, V, rows, qc["labels"], kc["labels"], sel, scale,
+        O, lse = sparse_rows(Q, K, V, rows, q_labels, kc["labels"], sel, scale,
                              bool(p.compensate), kst["count"], kst["kmean"], kst["vmean"])
     return dict(q=qc, k=kc, kstats=kst, kperm=kperm, kseg=kseg, S=S, sel=sel, O=O, lse=lse,
-                rows=rows, dense=dense,
+                rows=rows, dense=dense, merged=merged,
                 state=dict(cent_q=qc["cent"], cent_k=kc["cent"], fallback=kc["fallback"], tau=kc["tau"]))
 
 
@@ -64,3 +70,21 @@ def run_layer(Q, K, V, p, rows=None, warm=None):
         out.append(run_head(Q[b, h], K[b, h], V[b, h], p, bh, rows,
                             None if warm is None else warm[bh]))
     return out
+
+
+def merge_queries(q_labels, nq, sel, nk, b):
+    """Tail merging (iCATS, tail-merging design) of one head's query
+    clusters: returns the merged clusters' token order (perm, seg), each
+    token's new cluster and the new selections."""
+    perm, seg = counting_sort(q_labels, nq)
+    sizes = np.diff(seg)
+    masks = np.zeros((nq, nk), dtype=bool)
+    for r in range(nq):
+        masks[r, np.asarray(sel[r], dtype=np.int64)] = True
+    pieces, new_masks, new_lists, new_sizes = tailmerge.tail_merge(sizes, masks, sel, b)
+    new_perm, new_seg = tailmerge.apply(perm, seg, pieces)
+    labels = np.empty_like(q_labels)
+    for c in range(nq):
+        labels[new_perm[new_seg[c]:new_seg[c + 1]]] = c
+    return dict(perm=new_perm, seg=new_seg, labels=labels, sel=new_lists, masks=new_masks, sizes=new_sizes,
+                blocks_before=tailmerge.blocks(sizes, b), blocks_after=tailmerge.blocks(new_sizes, b))

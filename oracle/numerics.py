@@ -42,6 +42,7 @@ class Params:
     compensate: int = 0
     scale: float = 0.0          # 0 -> 1/sqrt(d)
     init_sample: int = 8        # k-means++ subsample factor; 0 -> every point
+    tail_block: int = 0         # query block of the tail merge (iCATS); 0 -> no merge
     seed: int = 0
 
     def attn_scale(self, d: int) -> float:

@@ -29,7 +29,7 @@ def abi_params(p: nm.Params):
     return ac.params_default(nq=p.nq, iters=p.iters, iters_warm=p.iters_warm, m0=p.m0, nmax=p.nmax,
                              tau_rule=p.tau_rule, tau_param=p.tau_param, score_mode=p.score_mode,
                              sel_mode=p.sel_mode, topk=p.topk, sel_param=p.sel_param, compensate=p.compensate,
-                             scale=p.scale, init_sample=p.init_sample, seed=p.seed)
+                             scale=p.scale, init_sample=p.init_sample, tail_block=p.tail_block, seed=p.seed)
 
 
 def to_dev(bits: np.ndarray):
@@ -221,17 +221,20 @@ def check_scores_selection(r: "Run", p: nm.Params):
     return ties
 
 
-def check_attention_sampled(r: "Run", Qb, Kb, Vb, p: nm.Params, rows_seed: int, nrows: int = 2048):
+def check_attention_sampled(r: "Run", Qb, Kb, Vb, p: nm.Params, rows_seed: int, nrows: int = 2048, q=None, sel=None):
     """Attention of a seeded sample of query rows per head against the fp64
-    oracle given the GPU's clusters and selection."""
+    oracle given the GPU's clusters and selection (q / sel: other query
+    clusters and selection than the Run's, e.g. tail-merged ones)."""
     from oracle import stats as ost
     from oracle import attention as oat
     B, H, L, d = Qb.shape
     BH = B * H
     Qf, Kf, Vf = (x.reshape(BH, L, d) for x in (Qb, Kb, Vb))
     O = bf16_dev_to_f64(r.O).reshape(BH, L, d)
-    qlab, klab, ncl, fb = np_(r.q.labels), np_(r.k.labels), np_(r.k.ncl), np_(r.st.fallback)
-    lst, n = np_(r.sel.list), np_(r.sel.n)
+    q = r.q if q is None else q
+    sel_ = r.sel if sel is None else sel
+    qlab, klab, ncl, fb = np_(q.labels), np_(r.k.labels), np_(r.k.ncl), np_(r.st.fallback)
+    lst, n = np_(sel_.list), np_(sel_.n)
     rows = gen.row_sample(L, nrows, rows_seed)
     worst = (0.0, 0.0)
     for h in range(BH):
@@ -249,3 +252,47 @@ def check_attention_sampled(r: "Run", Qb, Kb, Vb, p: nm.Params, rows_seed: int, 
         assert mx <= ATTN_MAX_ABS and rl2 <= ATTN_REL_L2, (h, mx, rl2)
         worst = (max(worst[0], mx), max(worst[1], rl2))
     return worst
+
+
+def unpack_masks(words: np.ndarray, nbits: int) -> np.ndarray:
+    """[..., mwords] uint32 bitmasks -> [..., nbits] bool (bit c of word c // 32)."""
+    w = words.astype(np.uint64)
+    bits = (w[..., :, None] >> np.arange(32, dtype=np.uint64)) & np.uint64(1)
+    return bits.reshape(*words.shape[:-1], -1)[..., :nbits].astype(bool)
+
+
+def check_tail_merge(r, block, heads=None):
+    """GPU ac_tail_merge of a Run's query clusters and selection against the
+    oracle's tail_merge on the same inputs, bit for bit: new token order,
+    segments, labels, masks, lists and counts.  Returns (q_out, sel_out,
+    blocks before, blocks after) summed over the checked heads."""
+    import torch
+    import clustered_sparse_attention_amd as ac
+    from oracle import tailmerge as tm
+    dev = torch.device("cuda")
+    qm = ac.Clusters(r.BH, r.L, r.nq, r.d, dev, rho=False)
+    sm = ac.Selection(r.BH, r.nq, r.ncap_k, dev, score=False)
+    ac.ac_tail_merge(r.shape, r.cp, block, r.q, r.sel, qm, sm, r.ws)
+    torch.cuda.synchronize()
+    b = block if block > 0 else 256
+    perm, seg = np_(r.q.perm), np_(r.q.seg)
+    lst, n, mask = np_(r.sel.list), np_(r.sel.n), np_(r.sel.mask).view(np.uint32)
+    mperm, mseg, mlab = np_(qm.perm), np_(qm.seg), np_(qm.labels)
+    mlst, mn, mmask = np_(sm.list), np_(sm.n), np_(sm.mask).view(np.uint32)
+    before = after = 0
+    for bh in (range(r.BH) if heads is None else heads):
+        sizes = np.diff(seg[bh][:r.nq + 1])
+        masks = unpack_masks(mask[bh], r.ncap_k)
+        lists = [lst[bh, c, :n[bh, c]] for c in range(r.nq)]
+        pieces, nmask, nlist, nsize = tm.tail_merge(sizes, masks, lists, b)
+        eperm, eseg = tm.apply(perm[bh], seg[bh], pieces)
+        assert np.array_equal(mseg[bh][:r.nq + 1], eseg), f"head {bh}: segments"
+        assert np.array_equal(mperm[bh], eperm), f"head {bh}: token order"
+        for c in range(r.nq):
+            assert np.all(mlab[bh][eperm[eseg[c]:eseg[c + 1]]] == c), f"head {bh}: labels of {c}"
+            assert mn[bh, c] == len(nlist[c]) and np.array_equal(mlst[bh, c, :mn[bh, c]], nlist[c]), \
+                f"head {bh}: list of {c}"
+        assert np.array_equal(unpack_masks(mmask[bh], r.ncap_k), nmask), f"head {bh}: masks"
+        before += tm.blocks(sizes, b)
+        after += tm.blocks(nsize, b)
+    return qm, sm, before, after

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_sizes_match_c_layout():
     assert ctypes.sizeof(ac.Shape) == 16
-    assert ctypes.sizeof(ac.Params) == 64
+    assert ctypes.sizeof(ac.Params) == 72
     assert ctypes.sizeof(ac.CClusters) == 56
     assert ctypes.sizeof(ac.CKStats) == 64
     assert ctypes.sizeof(ac.CSelection) == 40
@@ -40,6 +40,7 @@ def test_defaults_and_status_strings():
     assert (p.nq, p.iters, p.m0, p.nmax, p.tau_rule, p.sel_mode) == (65, 10, 200, 1500, ac.AC_TAU_MEAN_X,
                                                                     ac.AC_SEL_DENSITY)
     assert abs(p.tau_param - 1.5) < 1e-7 and abs(p.sel_param - 0.15) < 1e-7
+    assert (p.tail_block, p.reserved0) == (0, 0)
     lib = ac.load()
     assert lib.ac_status_str(ac.AC_E_WORKSPACE) == b"workspace too small"
 

@@ -54,6 +54,28 @@ def test_wan_selection_and_attention(wan_run, variant, compensate):
           f"rel-L2 {worst[1]:.3g}")
 
 
+@pytest.mark.parametrize("variant", ["density", "topp"])
+def test_wan_tail_merge(wan_run, variant):
+    """iCATS tail merging at full size: the merged clusters and selections of
+    all 40 heads bit-identical to the oracle's, the query block count never
+    larger, and the attention on the merged layout within tolerance."""
+    import torch
+    import clustered_sparse_attention_amd as ac
+    from abi_helpers import abi_params, check_tail_merge
+    w, Q, K, V, r = wan_run
+    p = workload_oracle_params("wan", variant, 0)
+    r.p, r.cp = p, abi_params(p)
+    r.score_select()
+    torch.cuda.synchronize()
+    qm, sm, before, after = check_tail_merge(r, 0)
+    assert after <= before
+    ac.ac_sparse_attn(r.shape, r.cp, r.Q, r.K, r.V, qm, r.k, r.st, sm, r.O, None, r.ws)
+    torch.cuda.synchronize()
+    worst = check_attention_sampled(r, Q, K, V, p, ROW_SEED["wan"], q=qm, sel=sm)
+    print(f"wan {variant} tail merge (256-row blocks): query blocks {before} -> {after}; worst max-abs "
+          f"{worst[0]:.3g} rel-L2 {worst[1]:.3g}")
+
+
 @pytest.mark.parametrize("name", ["cogvideox", "hunyuan", "long"])
 def test_config_full_size(name):
     import torch

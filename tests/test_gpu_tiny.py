@@ -299,3 +299,52 @@ def test_query_and_key_clustering_side_by_side_share_a_workspace(tiny):
     for name in ("kmax", "kmin", "kmean", "vmean", "fallback", "tau", "stages"):
         assert torch.equal(getattr(seq.st, name), getattr(par.st, name)), f"stats.{name}"
     assert torch.equal(seq.O, par.O)
+
+
+# ---------------------------------------------------------------- tail merging (iCATS)
+
+@pytest.mark.parametrize("block", [0, 64, 100, 1000])
+def test_tail_merge_bit_exact(tiny, block):
+    """ac_tail_merge against the oracle's pass 1 + pass 2 on the GPU's own
+    clusters and selection: token order, segments, labels, masks, lists."""
+    from abi_helpers import check_tail_merge
+    Q, K, V = tiny
+    for mode, extra in ((nm.SEL_TOPK, dict(topk=4)), (nm.SEL_TOPP, dict(sel_param=0.5))):
+        r = Run(Q, K, V, P(sel_mode=mode, **extra)).all()
+        _, _, before, after = check_tail_merge(r, block)
+        assert after <= before
+
+
+def test_attention_after_tail_merge(tiny):
+    """The attention on merged clusters equals the oracle's attention over
+    each token's merged key set; the same layer through ac_layer with
+    tail_block gives the identical output."""
+    import torch
+    import clustered_sparse_attention_amd as ac
+    from abi_helpers import check_tail_merge
+    Q, K, V = tiny
+    block = 64
+    p = P(sel_mode=nm.SEL_TOPK, topk=4, compensate=1)
+    r = Run(Q, K, V, p).all()
+    qm, sm, before, after = check_tail_merge(r, block)
+    O = torch.empty_like(r.Q)
+    ac.ac_sparse_attn(r.shape, r.cp, r.Q, r.K, r.V, qm, r.k, r.st, sm, O, None, r.ws)
+    torch.cuda.synchronize()
+    Og = bf16_dev_to_f64(O).reshape(r.BH, r.L, r.d)
+    mlab, klab = np_(qm.labels), np_(r.k.labels)
+    mlst, mn = np_(sm.list), np_(sm.n)
+    for bh in range(r.BH):
+        Qx, Kx, Vx = (nm.bf16_to_f64(_bits(x, bh)) for x in (Q, K, V))
+        sel = [mlst[bh, c, :mn[bh, c]] for c in range(r.nq)]
+        st = ost.key_stats(_bits(K, bh), _bits(V, bh), klab[bh], np.zeros((r.ncap_k, r.d)))
+        Oo, _ = oat.sparse_rows(Qx, Kx, Vx, np.arange(r.L), mlab[bh], klab[bh], sel, p.attn_scale(r.d), True,
+                                st["count"], st["kmean"], st["vmean"])
+        mx, rl2 = attn_error(Og[bh], Oo)
+        assert mx <= ATTN_MAX_ABS and rl2 <= ATTN_REL_L2, (bh, mx, rl2)
+    pl = P(sel_mode=nm.SEL_TOPK, topk=4, compensate=1, tail_block=block)
+    rl = Run(Q, K, V, pl)
+    state = ac.State(rl.BH, rl.nq, rl.ncap_k, rl.d, torch.device("cuda"))
+    O2 = torch.empty_like(rl.Q)
+    ac.ac_layer(rl.shape, rl.cp, rl.Q, rl.K, rl.V, state, O2, rl.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(O2, O)
