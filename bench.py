@@ -298,6 +298,64 @@ def summarize(args):
         json.dump(res, open(out, "w"), indent=1)
         print(json.dumps(res))
         return
+    if kind == "roofline":
+        # per-kernel roofline of the full-size launches of one layer step, from a
+        # kernel trace of `bench.py --serial` (entry points one after another)
+        src, out, wl, cmd = rest[0], rest[1], rest[2], " ".join(rest[3:])
+        import csa_inputs as gen
+        w = gen.get_workload(wl)
+        kw = workload_params(wl, "density", 0)
+        BH, L, d = w.BH, w.L, w.d
+        nq, m0 = min(kw["nq"], L), min(kw["m0"], L)
+        rows = list(csv.DictReader(open(src)))
+        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+        starts = [i for i, r in enumerate(rows) if "k_qnorm" in r["Kernel_Name"]]
+        steps = [rows[a:b] for a, b in zip(starts, starts[1:] + [len(rows)])][1:]  # drop the warm-up step
+
+        def dur(r):
+            return (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+
+        def nth(step, name, lo, hi):
+            return [r for r in step if name in r["Kernel_Name"]][lo:hi]
+
+        x_bytes = BH * L * d * 2.0
+        table = []  # (kernel, launches, what, work, unit, peak)
+        pad = lambda m: (m + 15) // 16 * 16
+        specs = [
+            ("k_qnorm", "k_qnorm", 0, 1, "read Q + write q-hat (bf16) and norms", 2 * x_bytes + BH * L * 4, "hbm"),
+            ("k_assign_res, queries (n = L, m = %d)" % nq, "k_assign_res", 0, 11,
+             "read X once (the argmin GEMM: %.2f TFLOP incl. hi/lo)" % (4.0 * BH * L * pad(nq) * d / 1e12),
+             x_bytes, "hbm"),
+            ("k_assign_res, key stage 1 (n = L, m = %d)" % m0, "k_assign_res", 11, 22,
+             "bf16 MFMA, centres split hi + lo, m padded to 16", 4.0 * BH * L * pad(m0) * d, "mfma"),
+            ("k_update_partial, queries + key stage 1", "k_update_partial", 0, 20,
+             "gather X in cluster order (bf16) + perm", x_bytes + BH * L * 4, "hbm"),
+            ("k_sort_scatter, full-size", "k_sort_scatter", 0, 22, "read labels, write perm", BH * L * 8.0, "hbm"),
+            ("k_kstats", "k_kstats", 0, 1, "read K and V in cluster order", 2 * x_bytes, "hbm"),
+            ("k_attn (density 0.15)", "k_attn<", 0, 1, "see the bench line (algorithmic pairs x 4d)", None, "mfma"),
+        ]
+        peaks = {"hbm": (PEAK_HBM_GBS, "GB/s", 1e9), "mfma": (PEAK_BF16_TFLOPS, "TFLOP/s", 1e12)}
+        lines = [f"# Per-kernel roofline, {w.description}", "", f"Command: `{cmd}`", "",
+                 "Full-size launches of the timed layer steps (the entry points run one after another); "
+                 "work is algorithmic (what the step must move or compute), time is the kernel's own.", "",
+                 "| kernel | launches/step | work per launch | avg time | achieved | peak | fraction |",
+                 "|---|---:|---|---:|---:|---:|---:|"]
+        for label, name, lo, hi, what, work, bound in specs:
+            ds = [dur(r) for st in steps for r in nth(st, name, lo, hi)]
+            if not ds:
+                continue
+            t = float(np.mean(ds))
+            peak, unit, scale = peaks[bound]
+            if work is None:
+                lines.append(f"| {label} | {hi - lo} | {what} | {t * 1e3:.3f} ms | — | {peak:.0f} {unit} | — |")
+                continue
+            ach = work / t / scale
+            wtxt = f"{work / 1e9:.3f} GB" if bound == "hbm" else f"{work / 1e12:.3f} TFLOP"
+            lines.append(f"| {label} | {hi - lo} | {wtxt}: {what} | {t * 1e3:.3f} ms | {ach:.0f} {unit} | "
+                         f"{peak:.0f} {unit} | {ach / peak:.2f} |")
+        open(out, "w").write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return
     raise SystemExit(f"unknown summary kind {kind}")
 
 
@@ -323,6 +381,8 @@ def main():
     ap.add_argument("--variant", default="density", choices=["density", "topp", "dense"])
     ap.add_argument("--compensate", type=int, default=0)
     ap.add_argument("--heads", type=int, default=0, help="run only this many heads (0 = all)")
+    ap.add_argument("--serial", action="store_true",
+                    help="run the query clustering on the main stream too (for per-kernel profiles)")
     ap.add_argument("--tail-block", type=int, default=0,
                     help="merge query-cluster tails for attention blocks of this many rows before the attention "
                          "(iCATS tail merging; 0 = off)")
@@ -362,6 +422,8 @@ def main():
     kw = workload_params(args.workload, args.variant, args.compensate)
     params = _abi(kw)
     layer = Layer(Qd, Kd, Vd, (w.B, w.H, w.L, w.d), params, tail_block=args.tail_block)
+    if args.serial:
+        layer.side = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
         layer.step()

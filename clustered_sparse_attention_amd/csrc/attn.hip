@@ -165,11 +165,13 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn(AttnArgs a) {
   constexpr int TILE = ATT_KT * D;            // elements per tile
   constexpr int NST = 3;                      // K / V tile buffers
   // XCD-aware order: the hardware deals consecutive block ids round-robin to
-  // the 8 XCDs, so id -> work item w = (id % 8) * (N / 8) + id / 8 hands each
-  // XCD a contiguous run of work items; the query tiles of one query cluster
-  // (which stream the same key list) then share that XCD's L2.
-  const int nper = gridDim.x / 8;
-  const int w = (int)(blockIdx.x % 8) * nper + (int)(blockIdx.x / 8);
+  // the 8 XCDs.  Work items (head-major query tiles) are cut into chunks of
+  // ATT_XCD_CHUNK and chunk k goes to XCD k % 8, so the few query tiles of a
+  // query cluster (which stream the same key list) mostly share one XCD's
+  // L2, while every XCD gets an even share of every head (heads can differ
+  // in cost by the density factor when some fall back to dense).
+  const int x = (int)(blockIdx.x % 8), j = (int)(blockIdx.x / 8);
+  const int w = ((j / ATT_XCD_CHUNK) * 8 + x) * ATT_XCD_CHUNK + j % ATT_XCD_CHUNK;
   const int h = w / a.blocks_per_head;
   const int blk = w % a.blocks_per_head;
   if (h >= a.BH) return;
@@ -450,7 +452,8 @@ void launch_attn(int D, const AttnArgs &a, int BH, int max_blocks, hipStream_t s
   AttnArgs aa = a;
   aa.blocks_per_head = max_blocks;
   aa.BH = BH;
-  const long long total = ((long long)max_blocks * BH + 7) / 8 * 8;  // a multiple of the 8 XCDs
+  const long long total = ((long long)max_blocks * BH + 8 * ATT_XCD_CHUNK - 1) / (8 * ATT_XCD_CHUNK) *
+                          (8 * ATT_XCD_CHUNK);  // whole chunks on all 8 XCDs
   if (D == 64)
     hipLaunchKernelGGL(k_attn<64>, dim3((unsigned)total), dim3(ATT_THREADS), 0, st, aa);
   else

@@ -12,6 +12,7 @@ constexpr int SORT_TILE = 128;   // points per counting-sort tile (one wave)
 constexpr int SORT_GROUP = 32;   // tiles per group in the two-level scan over tiles
 constexpr int ATT_QT = 256;      // query rows per attention block (8 waves x 32)
 constexpr int ATT_THREADS = 512;
+constexpr int ATT_XCD_CHUNK = 4;  // consecutive query tiles kept on one XCD
 constexpr int ATT_KT = 64;       // keys per attention tile
 constexpr int SEL_MAXN = 4096;   // most key clusters the select kernel sorts
 constexpr int ASSIGN_RES_MAX = 224;  // most centres the LDS-resident assignment holds

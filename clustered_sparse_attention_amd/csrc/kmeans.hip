@@ -735,21 +735,37 @@ __global__ __launch_bounds__(256) void k_kstats(KStatsArgs s) {
     sk[k] = 0.0; sv[k] = 0.0; mx[k] = -__builtin_inff(); mn[k] = __builtin_inff();
     cc[k] = cent[sub * PL + k];
   }
-  for (int p = beg + grp; p < end; p += 16) {
-    const int64_t row = perm[p];
-    const pw_t kw = *(const pw_t *)(K + row * D + sub * PL);
-    const pw_t vw = *(const pw_t *)(V + row * D + sub * PL);
+  // four member rows per lane in flight; rows are still added in member order
+  for (int p0 = beg + grp; p0 < end; p0 += 64) {
+    int64_t row[4];
 #pragma unroll
-    for (int k = 0; k < PL; ++k) {
-      const uint32_t a1 = kw[k >> 1], b1 = vw[k >> 1];
-      const float kv = bf2f((uint16_t)((k & 1) ? (a1 >> 16) : (a1 & 0xFFFFu)));
-      const float vv = bf2f((uint16_t)((k & 1) ? (b1 >> 16) : (b1 & 0xFFFFu)));
-      sk[k] += (double)kv;
-      sv[k] += (double)vv;
-      mx[k] = fmaxf(mx[k], kv);
-      mn[k] = fminf(mn[k], kv);
-      const double df = (double)kv - (double)cc[k];
-      se = fma(df, df, se);
+    for (int j = 0; j < 4; ++j) row[j] = (p0 + 16 * j < end) ? (int64_t)perm[p0 + 16 * j] : -1;
+    pw_t kw[4], vw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (row[j] >= 0) {
+        kw[j] = *(const pw_t *)(K + row[j] * D + sub * PL);
+        vw[j] = *(const pw_t *)(V + row[j] * D + sub * PL);
+      } else {
+        kw[j] = (pw_t){};
+        vw[j] = (pw_t){};
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (row[j] < 0) break;
+#pragma unroll
+      for (int k = 0; k < PL; ++k) {
+        const uint32_t a1 = kw[j][k >> 1], b1 = vw[j][k >> 1];
+        const float kv = bf2f((uint16_t)((k & 1) ? (a1 >> 16) : (a1 & 0xFFFFu)));
+        const float vv = bf2f((uint16_t)((k & 1) ? (b1 >> 16) : (b1 & 0xFFFFu)));
+        sk[k] += (double)kv;
+        sv[k] += (double)vv;
+        mx[k] = fmaxf(mx[k], kv);
+        mn[k] = fminf(mn[k], kv);
+        const double df = (double)kv - (double)cc[k];
+        se = fma(df, df, se);
+      }
     }
   }
   __shared__ double shk[16][D], shv[16][D];
