@@ -36,6 +36,22 @@ def quest_scores_split(cq: np.ndarray, kmax: np.ndarray, kmin: np.ndarray) -> np
     return qp @ kmax.T + qm @ kmin.T
 
 
+def token_quest_scores(q_tokens: np.ndarray, kmax: np.ndarray, kmin: np.ndarray, count: np.ndarray,
+                       chunk: int = 64) -> np.ndarray:
+    """Quest bound of every query token against every key cluster: AdaCluster
+    Algorithm 2 in its literal shape (one score per query row and key
+    column, here per key cluster: [L_q, N_k]), each entry eq. (1):
+    S[i, c] = sum_d max(q_i[d] * max(K_c^d), q_i[d] * min(K_c^d)).
+
+    q_tokens are the layer's query rows as they enter attention (not
+    normalised).  Empty clusters score -inf.  Rows are processed in chunks
+    only to bound memory; each entry is the same per-dimension sum."""
+    out = np.empty((q_tokens.shape[0], kmax.shape[0]))
+    for i in range(0, q_tokens.shape[0], chunk):
+        out[i:i + chunk] = quest_scores(q_tokens[i:i + chunk], kmax, kmin, count)
+    return out
+
+
 def mean_scores(cq: np.ndarray, kmean: np.ndarray, count: np.ndarray) -> np.ndarray:
     """Mean-based cluster score (the "w/o Quest" ablation of AdaCluster
     §4.4): S[r, c] = c_r . mean(K_c)."""
