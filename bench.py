@@ -356,7 +356,117 @@ def summarize(args):
         open(out, "w").write("\n".join(lines) + "\n")
         print("\n".join(lines))
         return
+    if kind == "quest":
+        # per-token Quest engines: bench --quest-compare lines + kernel-trace durations
+        src, lines_json, out, cmd = rest[0], rest[1], rest[2], " ".join(rest[3:])
+        res = [json.loads(l) for l in open(lines_json) if l.startswith("{")]
+        tr = list(csv.DictReader(open(src)))
+        dur = {}
+        for r in tr:
+            name = r["Kernel_Name"]
+            if "k_tq_" not in name:
+                continue
+            eng = "mfma" if "k_tq_mfma" in name else "valu"
+            per_block = 512 if eng == "mfma" else 256
+            toks = 256
+            blocks_x = int(r["Grid_Size_X"]) // per_block
+            dur.setdefault((eng, blocks_x * toks), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-6)
+        lines = ["# Per-token Quest scores: TensorQuest (MFMA) against eq. (1) on the vector ALUs", "",
+                 f"Command: `{cmd}`", "",
+                 "Every query token of every head against every key cluster of the head (the keys clustered by "
+                 "the workload's Algorithm 1 at each length); S is [H, L, ld] fp32 with ld the largest cluster "
+                 "count rounded up to 32. MFMA work: write S + read Q (HBM-bound, peak 8000 GB/s); VALU work: "
+                 "4 fp32 operations per (token, cluster, dimension) against 39.3 T lane-ops/s (256 CUs x 4 SIMDs "
+                 "x 16 lanes x 2.4 GHz). Event time per call; kernel-trace average of the same launches beside it.",
+                 "",
+                 "| L | key clusters (mean, ld) | TensorQuest ms (trace) | GB/s | HBM frac | Quest VALU ms (trace) | "
+                 "Tops/s | ALU frac | speedup | torch fill of S, GB/s |",
+                 "|---:|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+        for r in res:
+            Lp = (r["L"] + 255) // 256 * 256
+            tm = np.mean(dur.get(("mfma", Lp), [float("nan")]))
+            tv = np.mean(dur.get(("valu", Lp), [float("nan")]))
+            lines.append(f"| {r['L']} | {r['key_clusters_mean']}, {r['ld']} | {r['tensorquest_mfma_ms']} ({tm:.4f}) | "
+                         f"{r['mfma_hbm_gbs']} | {r['mfma_hbm_frac']} | {r['quest_valu_ms']} ({tv:.3f}) | "
+                         f"{r['valu_tops']} | {r['valu_alu_frac']} | {r['speedup']}x | {r['fill_gbs']} |")
+        open(out, "w").write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return
     raise SystemExit(f"unknown summary kind {kind}")
+
+
+PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12  # fp32 VALU lane-ops/s, unpacked: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+
+
+def quest_compare(args):
+    """Per-token Quest scores (every query token against every key cluster)
+    on MFMA (TensorQuest) and on the vector ALUs (eq. (1) as written), on
+    the workload's head count and clustering at several sequence lengths.
+    One JSON line per length, then a markdown table on stderr."""
+    import torch
+    import csa_inputs as gen
+    import clustered_sparse_attention_amd as ac
+    base = gen.get_workload(args.workload)
+    kw = workload_params(args.workload, "density", 0)
+    rows = []
+    for frac in (0.125, 0.25, 0.5, 1.0):
+        L = int(round(base.L * frac))
+        w = gen.get_workload(args.workload, L=L, H=args.heads or base.H)
+        Q, K, V = gen.generate(w)
+        dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        Qd, Kd, Vd = dev(Q), dev(K), dev(V)
+        shape = ac.Shape(w.B, w.H, w.L, w.d)
+        params = _abi(kw)
+        ncap, wsb = ac.ac_sizes(shape, params)
+        ws = ac.workspace(wsb, Qd.device)
+        kcl = ac.Clusters(w.BH, w.L, ncap, w.d, Qd.device, rho=False)
+        st = ac.KStats(w.BH, ncap, w.d, Qd.device)
+        ac.ac_cluster_k(shape, params, Kd, Vd, None, kcl, st, ws)
+        ncl = kcl.ncl.cpu().numpy()
+        ld = (int(ncl.max()) + 31) // 32 * 32  # rows of whole 128-byte lines
+        S = torch.empty((w.BH, w.L, ld), dtype=torch.float32, device=Qd.device)
+        res = {"L": w.L, "H": w.H, "d": w.d, "ld": ld, "key_clusters_mean": round(float(ncl.mean()), 1)}
+        # what a plain write of the same bytes reaches (torch fill), for scale
+        S.fill_(0.0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            S.fill_(0.0)
+        e1.record()
+        torch.cuda.synchronize()
+        res["fill_gbs"] = round(S.numel() * 4.0 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        for eng, name, reps in ((ac.AC_QUEST_MFMA, "tensorquest_mfma", 10), (ac.AC_QUEST_VALU, "quest_valu", 3)):
+            ac.ac_score_tokens(shape, params, Qd, kcl, st, eng, S, ld)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                ac.ac_score_tokens(shape, params, Qd, kcl, st, eng, S, ld)
+            e1.record()
+            torch.cuda.synchronize()
+            res[name + "_ms"] = round(e0.elapsed_time(e1) / reps, 4)
+        t_m, t_v = res["tensorquest_mfma_ms"] * 1e-3, res["quest_valu_ms"] * 1e-3
+        pairs = float(w.L) * float(ncl.sum())
+        hbm = w.BH * w.L * (ld * 4.0 + w.d * 2.0) + float(ncl.sum()) * 4.0 * w.d
+        res["speedup"] = round(t_v / t_m, 2)
+        res["mfma_hbm_gbs"] = round(hbm / t_m / 1e9, 1)
+        res["mfma_hbm_frac"] = round(hbm / t_m / 1e9 / PEAK_HBM_GBS, 3)
+        res["mfma_tflops"] = round(pairs * 4.0 * w.d / t_m / 1e12, 1)
+        res["valu_tops"] = round(pairs * 4.0 * w.d / t_v / 1e12, 2)
+        res["valu_alu_frac"] = round(pairs * 4.0 * w.d / t_v / 1e12 / PEAK_VALU_TOPS, 3)
+        print(json.dumps(res), flush=True)
+        rows.append(res)
+        del S, ws, kcl, st, Qd, Kd, Vd
+        torch.cuda.empty_cache()
+    print("| L | key clusters (mean, ld) | TensorQuest MFMA ms | HBM GB/s (frac) | torch fill of S, GB/s | "
+          "Quest VALU ms | VALU Tops/s (frac) | speedup |", file=sys.stderr)
+    print("|---:|---|---:|---:|---:|---:|---:|---:|", file=sys.stderr)
+    for r in rows:
+        print(f"| {r['L']} | {r['key_clusters_mean']}, {r['ld']} | {r['tensorquest_mfma_ms']} | {r['mfma_hbm_gbs']} "
+              f"({r['mfma_hbm_frac']}) | {r['fill_gbs']} | {r['quest_valu_ms']} | {r['valu_tops']} "
+              f"({r['valu_alu_frac']}) | {r['speedup']}x |", file=sys.stderr)
 
 
 def copy_probe(nbytes: int):
@@ -390,6 +500,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a plain copy of this many bytes")
     ap.add_argument("--summarize", nargs="+", help="write a profile summary from rocprofv3 output (no GPU)")
+    ap.add_argument("--quest-compare", action="store_true",
+                    help="only time per-token Quest scores, TensorQuest (MFMA) against eq. (1) on the vector ALUs")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize)
@@ -406,6 +518,10 @@ def main():
     import csa_inputs as gen
     import clustered_sparse_attention_amd as ac
     ac.load()
+    if args.quest_compare:
+        quest_compare(args)
+        return
+
 
     w = gen.get_workload(args.workload)
     if args.heads:

@@ -20,9 +20,10 @@ AC_OK, AC_E_ARG, AC_E_SHAPE, AC_E_WORKSPACE, AC_E_UNSUPPORTED, AC_E_DEVICE = ran
 AC_TAU_MEAN_X, AC_TAU_PCTL, AC_TAU_ABS, AC_TAU_INF = range(4)
 AC_SCORE_QUEST, AC_SCORE_MEAN = range(2)
 AC_SEL_TOPK, AC_SEL_DENSITY, AC_SEL_TOPP, AC_SEL_DENSE = range(4)
+AC_QUEST_MFMA, AC_QUEST_VALU = range(2)
 
 ENTRY_POINTS = ("ac_params_default", "ac_sizes", "ac_cluster_q", "ac_cluster_k", "ac_score_select",
-                "ac_sparse_attn", "ac_tail_merge", "ac_layer", "ac_status_str", "ac_last_error")
+                "ac_sparse_attn", "ac_tail_merge", "ac_score_tokens", "ac_layer", "ac_status_str", "ac_last_error")
 
 
 class ACError(RuntimeError):
@@ -106,6 +107,9 @@ def load() -> ctypes.CDLL:
                                   ctypes.POINTER(CClusters), ctypes.POINTER(CSelection), ctypes.POINTER(CClusters),
                                   ctypes.POINTER(CSelection), vp, ctypes.c_size_t, vp]
     lib.ac_tail_merge.restype = st
+    lib.ac_score_tokens.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), vp, ctypes.POINTER(CClusters),
+                                    ctypes.POINTER(CKStats), ctypes.c_int32, vp, ctypes.c_int32, vp]
+    lib.ac_score_tokens.restype = st
     lib.ac_layer.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), vp, vp, vp, ctypes.POINTER(CState), vp,
                              ctypes.POINTER(CLayerStats), vp, ctypes.c_size_t, vp]
     lib.ac_layer.restype = st
@@ -265,6 +269,12 @@ def ac_tail_merge(shape, params, block: int, q_in: Clusters, sel_in: Selection, 
     _check(load().ac_tail_merge(ctypes.byref(shape), ctypes.byref(params), int(block), ctypes.byref(q_in.c()),
                                 ctypes.byref(sel_in.c()), ctypes.byref(q_out.c()), ctypes.byref(sel_out.c()),
                                 _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def ac_score_tokens(shape, params, Q, k: Clusters, stats: KStats, engine: int, S, ld: int, stream=None):
+    """Per-token Quest scores into S ([BH, L, ld] float32)."""
+    _check(load().ac_score_tokens(ctypes.byref(shape), ctypes.byref(params), _ptr(Q), ctypes.byref(k.c()),
+                                  ctypes.byref(stats.c()), int(engine), _ptr(S), int(ld), _stream(stream)))
 
 
 def ac_layer(shape, params, Q, K, V, state: State, O, ws, host_stats: bool = False, stream=None):

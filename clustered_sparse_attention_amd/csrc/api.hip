@@ -694,6 +694,33 @@ AC_API ac_status ac_tail_merge(const ac_shape *s, const ac_params *p, int32_t bl
   return do_tail_merge(P, block, q_in, sel_in, q_out, sel_out, ws, (hipStream_t)stream);
 }
 
+AC_API ac_status ac_score_tokens(const ac_shape *s, const ac_params *p, const uint16_t *Q, const ac_clusters *k,
+                                 const ac_kstats *stats, int32_t engine, float *S, int32_t ld, ac_stream_t stream) {
+  AC_TRY(check_shape(s));
+  AC_TRY(check_params(s, p));
+  if (!Q || !S) return fail(AC_E_ARG, "Q or S is NULL");
+  if (engine != AC_QUEST_MFMA && engine != AC_QUEST_VALU) return fail(AC_E_ARG, "engine %d is not AC_QUEST_*", engine);
+  if (ld < 1) return fail(AC_E_ARG, "ld must be >= 1 (got %d)", ld);
+  Plan P = make_plan(s, p);
+  if (!k || !k->seg || !k->ncl) return fail(AC_E_ARG, "key clusters is NULL or has a NULL seg / ncl");
+  if (k->ncap != P.ncapk) return fail(AC_E_ARG, "key clusters ncap must be %d", P.ncapk);
+  if (!stats || !stats->kmax || !stats->kmin) return fail(AC_E_ARG, "kstats is NULL or has a NULL kmax / kmin");
+  AC_TRY(check_device());
+  TokQuestArgs a;
+  a.Q = Q;
+  a.kmax = stats->kmax;
+  a.kmin = stats->kmin;
+  a.seg = k->seg;
+  a.ncl = k->ncl;
+  a.ncap = P.ncapk;
+  a.S = S;
+  a.ld = ld;
+  a.L = P.L;
+  launch_token_quest(P.D, a, engine, P.BH, (hipStream_t)stream);
+  AC_CHECK_LAUNCH();
+  return AC_OK;
+}
+
 namespace ac {
 namespace {
 // A second stream (default priority) per device and host thread, created on

@@ -142,6 +142,17 @@ struct TailArgs {
   int nq, ncapk, mwords, L, block;
 };
 
+// Per-token Quest scores (see quest.hip).
+struct TokQuestArgs {
+  const uint16_t *Q;            // [BH, L, D] bf16 query rows
+  const uint16_t *kmax, *kmin;  // [BH, ncap, D] bf16
+  const int *seg, *ncl;         // [BH, ncap + 1], [BH]
+  int ncap;
+  float *S;                     // [BH, L, ld]
+  int ld;
+  int L;
+};
+
 // kmeans.hip
 void launch_qnorm(int D, const uint16_t *Q, uint16_t *Qh, float *qn, int64_t rows, hipStream_t st);
 void launch_kpp(int D, const KmArgs &a, int BH, double *d2buf, int init_sample, uint64_t seed, int role, int stage,
@@ -183,5 +194,8 @@ void launch_attn(int D, const AttnArgs &a, int BH, int max_blocks, hipStream_t s
 
 // merge.hip
 void launch_tail_merge(const TailArgs &t, int BH, hipStream_t st);
+
+// quest.hip (engine 0: MFMA, 1: vector ALU)
+void launch_token_quest(int D, const TokQuestArgs &a, int engine, int BH, hipStream_t st);
 
 }  // namespace ac

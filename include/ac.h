@@ -13,6 +13,9 @@
  *   ac_sparse_attn   attention of each query over the keys of its cluster's selected key clusters, with
  *                    optional centroid compensation, or dense attention for fallback heads
  *                    (AdaCluster Algorithm 3; ClusterAttention §1.2 eqs. (2), (5))
+ *   ac_score_tokens  Quest bound of every query token against every key cluster (Algorithm 2's literal shape),
+ *                    on MFMA (TensorQuest) or on the vector ALUs (eq. (1) as written)
+ *   ac_tail_merge    iCATS tail merging of the query clusters before the attention
  *   ac_layer         the whole layer, cold (first denoising step) or warm (later steps reuse the cluster
  *                    counts and centres: AdaCluster §3.2.2 "Efficient initialization")
  *
@@ -75,6 +78,10 @@ enum { AC_TAU_MEAN_X = 0, /* tau = tau_param * mean distance */
 
 /* Cluster score (AdaCluster §3.2.3 eq. (1); MEAN is the "w/o Quest" ablation of §4.4). */
 enum { AC_SCORE_QUEST = 0, AC_SCORE_MEAN = 1 };
+
+/* Engine of ac_score_tokens. */
+enum { AC_QUEST_MFMA = 0, /* TensorQuest: [q+, q-] . [kmax; kmin] as one bf16 MFMA product (eq. (2)) */
+       AC_QUEST_VALU = 1  /* eq. (1) per dimension on the vector ALUs (two products, a max, an add) */ };
 
 /* Key-cluster selection per query cluster, in order of score (desc), ties by cluster index (asc).
  * Empty clusters are never selected; at least one cluster always is. */
@@ -235,6 +242,20 @@ ac_status ac_sparse_attn(const ac_shape *s, const ac_params *p, const uint16_t *
 ac_status ac_tail_merge(const ac_shape *s, const ac_params *p, int32_t block, const ac_clusters *q_in,
                         const ac_selection *sel_in, ac_clusters *q_out, ac_selection *sel_out, void *ws,
                         size_t ws_bytes, ac_stream_t stream);
+
+/* Quest bound of every query token against every key cluster: AdaCluster Algorithm 2 in its literal
+ * shape (one score per query row and key column, the keys reduced to their clusters), each entry
+ * eq. (1): S[bh, i, c] = sum_d max(Q[bh, i, d] kmax_c[d], Q[bh, i, d] kmin_c[d]) for the query rows as
+ * given (not normalised).  engine AC_QUEST_MFMA evaluates it as TensorQuest, the product
+ * [q+, q-] . [kmax; kmin] on bf16 MFMA (q+ = max(q, 0), q- = min(q, 0); every product is exact, the sum
+ * accumulates in fp32); AC_QUEST_VALU evaluates eq. (1) per dimension on the vector ALUs, the form
+ * §3.2.3 calls too slow (fp32, summed over d in order).  Q: [B,H,L,d] bf16; k and stats as filled by
+ * ac_cluster_k (only k->seg, k->ncl, stats->kmax and stats->kmin are read; k->ncap must be ac_sizes'
+ * ncap_k).  S: [BH, L, ld] fp32, row-major with leading dimension ld >= 1; columns c < ld are written:
+ * the score for a non-empty cluster c < ncl_k[bh], -inf otherwise.  Clusters c >= ld get no score, so
+ * pass ld >= the largest ncl_k to score them all.  Needs no workspace. */
+ac_status ac_score_tokens(const ac_shape *s, const ac_params *p, const uint16_t *Q, const ac_clusters *k,
+                          const ac_kstats *stats, int32_t engine, float *S, int32_t ld, ac_stream_t stream);
 
 /* The whole layer (AdaCluster Algorithm 3 with the optional compensation): ac_cluster_q,
  * ac_cluster_k, ac_score_select, ac_tail_merge when p->tail_block > 0, and ac_sparse_attn on

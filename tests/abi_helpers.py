@@ -296,3 +296,47 @@ def check_tail_merge(r, block, heads=None):
         before += tm.blocks(sizes, b)
         after += tm.blocks(nsize, b)
     return qm, sm, before, after
+
+
+def check_token_quest(r, Qb, Kb, Vb, ld, rows=None, engines=(0, 1)):
+    """ac_score_tokens (each engine) against the oracle's per-token Quest
+    scores (eq. (1) in fp64, key max / min from the oracle's statistics of
+    the GPU's key labels) on every head, on all query rows or a sample.
+    Entries for non-empty clusters within 4 d 2^-24 sum_d |q_d| max(|kmax_d|,
+    |kmin_d|) (fp32 summation of exact products); every other column of
+    the ld written ones -inf.  Returns the largest error relative to that
+    bound, per engine."""
+    import torch
+    import clustered_sparse_attention_amd as ac
+    from oracle import stats as ost
+    from oracle import score as osc
+    B, H, L, d = Qb.shape
+    BH = B * H
+    Qf, Kf, Vf = (x.reshape(BH, L, d) for x in (Qb, Kb, Vb))
+    klab, ncl = np_(r.k.labels), np_(r.k.ncl)
+    rows = np.arange(L) if rows is None else rows
+    S = torch.empty((BH, L, ld), dtype=torch.float32, device="cuda")
+    worst = {}
+    outs = {}
+    for eng in engines:
+        S.fill_(float("nan"))
+        ac.ac_score_tokens(r.shape, r.cp, r.Q, r.k, r.st, eng, S, ld)
+        torch.cuda.synchronize()
+        outs[eng] = S[:, rows, :].cpu().numpy()
+        worst[eng] = 0.0
+    for h in range(BH):
+        nk = int(ncl[h])
+        st = ost.key_stats(Kf[h], Vf[h], klab[h], np.zeros((nk, d)))
+        Qx = nm.bf16_to_f64(Qf[h][rows])
+        So = osc.token_quest_scores(Qx, st["kmax"], st["kmin"], st["count"])
+        bound = 4 * d * 2.0 ** -24 * (np.abs(Qx) @ np.maximum(np.abs(st["kmax"]), np.abs(st["kmin"])).T) + 1e-30
+        m = min(nk, ld)
+        live = np.zeros(ld, bool)
+        live[:m] = st["count"][:m] > 0
+        for eng in engines:
+            Sg = outs[eng][h]
+            assert np.all(np.isneginf(Sg[:, ~live])), (h, eng, "dead columns")
+            err = np.abs(Sg[:, :m][:, live[:m]] - So[:, :m][:, live[:m]]) / bound[:, :m][:, live[:m]]
+            assert err.size == 0 or np.max(err) <= 1.0, (h, eng, float(np.max(err)))
+            worst[eng] = max(worst[eng], float(np.max(err)) if err.size else 0.0)
+    return worst

@@ -112,6 +112,11 @@ def test_entry_points_reject_bad_arguments_before_any_device_work():
     assert lib.ac_sparse_attn(ctypes.byref(shape), ctypes.byref(p), 1 << 20, 1 << 20, 1 << 20, ctypes.byref(q),
                               ctypes.byref(k), ctypes.byref(st), ctypes.byref(sel_ok), None, None, ws, wsb,
                               None) == ac.AC_E_ARG
+    # per-token scores: bad engine, ld < 1, NULL S, key capacity
+    for eng, ld, S, kk in [(2, 64, 1 << 20, k), (ac.AC_QUEST_MFMA, 0, 1 << 20, k), (ac.AC_QUEST_VALU, 64, None, k),
+                           (ac.AC_QUEST_MFMA, 64, 1 << 20, k_bad)]:
+        assert lib.ac_score_tokens(ctypes.byref(shape), ctypes.byref(p), 1 << 20, ctypes.byref(kk), ctypes.byref(st),
+                                   eng, S, ld, None) == ac.AC_E_ARG, (eng, ld, S)
     # NULL state
     assert lib.ac_layer(ctypes.byref(shape), ctypes.byref(p), 1 << 20, 1 << 20, 1 << 20, None, 1 << 20, None, ws, wsb,
                         None) == ac.AC_E_ARG

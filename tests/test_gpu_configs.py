@@ -76,6 +76,18 @@ def test_wan_tail_merge(wan_run, variant):
           f"{worst[0]:.3g} rel-L2 {worst[1]:.3g}")
 
 
+def test_wan_token_quest(wan_run):
+    """Per-token Quest scores at full size (40 heads x 75,600 tokens against
+    every key cluster), both engines, on a seeded sample of 256 query rows
+    per head against the oracle's eq. (1)."""
+    from abi_helpers import check_token_quest
+    w, Q, K, V, r = wan_run
+    ld = int(np_(r.k.ncl).max())
+    rows = gen.row_sample(w.L, 256, ROW_SEED["wan"])
+    worst = check_token_quest(r, Q, K, V, ld, rows=rows)
+    print(f"wan token quest ld={ld}: max error / bound {worst}")
+
+
 @pytest.mark.parametrize("name", ["cogvideox", "hunyuan", "long"])
 def test_config_full_size(name):
     import torch

@@ -348,3 +348,24 @@ def test_attention_after_tail_merge(tiny):
     ac.ac_layer(rl.shape, rl.cp, rl.Q, rl.K, rl.V, state, O2, rl.ws)
     torch.cuda.synchronize()
     assert torch.equal(O2, O)
+
+
+# ---------------------------------------------------------------- per-token Quest (Algorithm 2's literal shape)
+
+@pytest.mark.parametrize("shape", [None, (3, 1000, 128)])
+def test_token_quest_both_engines(tiny, shape):
+    """ac_score_tokens on MFMA (TensorQuest) and on the vector ALUs against
+    the oracle's eq. (1) for every query token: on the tiny layer, and on a
+    ragged one (L = 1000, not a multiple of the 256-token block, d = 128);
+    with ld past the last cluster (-inf fill) and ld cutting the clusters."""
+    from abi_helpers import check_token_quest
+    if shape is None:
+        Q, K, V = tiny
+    else:
+        H, L, d = shape
+        Q, K, V = gen.generate(gen.get_workload("tiny", H=H, L=L, d=d))
+    r = Run(Q, K, V, P())
+    r.cluster_k()
+    for ld in (r.ncap_k + 5, 7):
+        worst = check_token_quest(r, Q, K, V, ld)
+        print(f"token quest shape={shape} ld={ld}: max error / bound {worst}")
