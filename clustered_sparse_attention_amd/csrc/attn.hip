@@ -154,16 +154,21 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 #define AC_LDS(T, p) ((__attribute__((address_space(3))) T *)(p))
 
-template <int D>
-__global__ __launch_bounds__(ATT_THREADS, 1) void k_attn(AttnArgs a) {
+// One block: ATT_QT queries of one query cluster, NW waves of QG groups of
+// 32 queries.  Every K or V fragment a wave reads from LDS feeds QG
+// products, so LDS traffic per product falls with QG.
+template <int D, int QG>
+__global__ __launch_bounds__(64 * ATT_QT / (32 * QG), 1) void k_attn(AttnArgs a) {
   constexpr int KSQ = D / 16;                 // k-steps of the QK product
   constexpr int DB = D / 32;                  // 32-dim blocks of O
   constexpr int NC = D / 8;                   // 16-byte chunks per row
   constexpr int RPI = 64 / NC;                // rows per 64-lane global->LDS load
-  constexpr int NW = ATT_THREADS / 64;        // waves
+  constexpr int NW = ATT_QT / (32 * QG);      // waves
   constexpr int IPW = ATT_KT / RPI / NW;      // such loads per wave, per tensor and tile
   constexpr int TILE = ATT_KT * D;            // elements per tile
-  constexpr int NST = 3;                      // K / V tile buffers
+  constexpr int NST = 4;                      // K / V tile buffers
+  constexpr int VPM = 8 / DB;                 // weights computed after each PV product
+  static_assert(IPW >= 1 && IPW * RPI * NW == ATT_KT, "tile load split");
   // XCD-aware order: the hardware deals consecutive block ids round-robin to
   // the 8 XCDs.  Work items (head-major query tiles) are cut into chunks of
   // ATT_XCD_CHUNK and chunk k goes to XCD k % 8, so the few query tiles of a
@@ -193,7 +198,7 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn(AttnArgs a) {
   const int l32 = lane & 31, g = lane >> 5;
 
   __shared__ __align__(1024) uint16_t Kb[NST * TILE], Vb[NST * TILE];
-  __shared__ __align__(16) int ring[4][2 * ATT_KT];      // raw rows and pseudo-key biases of a tile, by tile mod 4
+  __shared__ __align__(16) int ring[8][2 * ATT_KT];      // raw rows and pseudo-key biases of a tile, by tile mod 8
   __shared__ __align__(16) float sbias[NW][4][ATT_KT];   // per wave: key biases / scale, by tile mod 4
 
   const bool dense = a.all_dense || (a.fallback != nullptr && a.fallback[h] != 0);
@@ -209,24 +214,32 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn(AttnArgs a) {
   const int last_row_tile = max(nt0 - 1, 0);
   const int last_pb_tile = max((a.ncap + ATT_KT - 1) / ATT_KT - 1, 0);
 
-  // Q fragments of this wave's 32 queries (B operand of S^T = K Q^T)
-  const int qi = qbeg + wave * 32 + l32;
-  const bool qvalid = qi < qend;
-  const bool wave_active = qbeg + wave * 32 < qend;
-  const int64_t qrow = qvalid ? (int64_t)a.perm_q[(int64_t)h * a.L + qi] : 0;
-  bf16x8_t qf[KSQ];
-  {
-    const uint16_t *qr = a.Q + ((int64_t)h * a.L + qrow) * D;
+  // Q fragments of this wave's QG x 32 queries (B operands of S^T = K Q^T)
+  const bool wave_active = qbeg + wave * 32 * QG < qend;
+  bool qvalid[QG];
+  int64_t qrow[QG];
+  bf16x8_t qf[QG][KSQ];
+#pragma unroll
+  for (int gq = 0; gq < QG; ++gq) {
+    const int qi = qbeg + (wave * QG + gq) * 32 + l32;
+    qvalid[gq] = qi < qend;
+    qrow[gq] = qvalid[gq] ? (int64_t)a.perm_q[(int64_t)h * a.L + qi] : 0;
+    const uint16_t *qr = a.Q + ((int64_t)h * a.L + qrow[gq]) * D;
 #pragma unroll
     for (int ks = 0; ks < KSQ; ++ks)
-      qf[ks] = qvalid ? *(const bf16x8_t *)&qr[ks * 16 + g * 8] : (bf16x8_t){};
+      qf[gq][ks] = qvalid[gq] ? *(const bf16x8_t *)&qr[ks * 16 + g * 8] : (bf16x8_t){};
   }
 
-  f32x16_t acc_o[DB];
+  f32x16_t acc_o[QG][DB];
+  float m_i[QG], l_i[QG], alpha[QG];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc_o[db] = (f32x16_t){};
-  float m_i = -__builtin_inff();
-  float l_i = 0.f;
+  for (int gq = 0; gq < QG; ++gq) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc_o[gq][db] = (f32x16_t){};
+    m_i[gq] = -__builtin_inff();
+    l_i[gq] = 0.f;
+    alpha[gq] = 1.f;  // rescale of O still to apply before the next PV product
+  }
   const float sl2 = a.scale_log2;
   const float inv_sl2 = 1.f / sl2;
 
@@ -238,13 +251,13 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn(AttnArgs a) {
   // Every global->LDS load of the loop is issued from inline assembly and the
   // loop holds no other global memory access, so the kernel alone decides
   // when to wait for them.  The row list and pseudo-key biases of a tile go
-  // to a small LDS ring (wave 0, 32 lanes x 16 bytes) four tiles ahead.
+  // to a small LDS ring (wave 0, 32 lanes x 16 bytes) five tiles ahead.
   auto ring_load = [&](int tt) {
     if (wave == 0 && lane < 32) {
       const int tr = min(tt, last_row_tile);
       const int tp = min(max(tt - nt0, 0), last_pb_tile);
       const int *src = lane < 16 ? rl + tr * ATT_KT + 4 * lane : (const int *)pbr + tp * ATT_KT + 4 * (lane - 16);
-      dma16((const uint16_t *)src, lds_addr(&ring[tt & 3][0]));
+      dma16((const uint16_t *)src, lds_addr(&ring[tt & 7][0]));
     }
   };
   // final row (-1: masked) of key `lane` of tile tt from the ring; its logit
@@ -255,8 +268,8 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn(AttnArgs a) {
     const bool ph1 = tt >= nt0;
     const int o = (ph1 ? tt - nt0 : tt) * ATT_KT + lane;
     const int total = ph1 ? ncl_k : T;
-    const int raw = ring[tt & 3][lane];
-    const float braw = __int_as_float(ring[tt & 3][ATT_KT + lane]);
+    const int raw = ring[tt & 7][lane];
+    const float braw = __int_as_float(ring[tt & 7][ATT_KT + lane]);
     int rw = (ph1 || dense) ? o : raw;
     float bias = ph1 ? braw * inv_sl2 : 0.f;
     if (o >= total) { rw = -1; bias = -__builtin_inff(); }
@@ -266,6 +279,7 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn(AttnArgs a) {
   // The swizzles depend on the row only modulo 16, and a lane's row moves by
   // NW * RPI (a multiple of 16) from one load to the next, so its source
   // chunk byte offset is fixed.
+  static_assert((NW * RPI) % 16 == 0, "swizzle period");
   const uint32_t koff = 16u * (uint32_t)((lane % NC) ^ kswz<D>(wave * RPI + lane / NC));
   const uint32_t voff = 16u * (uint32_t)((lane % NC) ^ vswz<D>(wave * RPI + lane / NC));
   // one tensor of tile tt into buffer `buf`: wave w writes rows
@@ -294,20 +308,26 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn(AttnArgs a) {
   const int vc2 = 2 * vhd + ((vi & 3) >> 1);            // chunk within the 4-chunk (32-dim) group
   const int vhalf = 4 * (vi & 1);
 
-  // S^T = K Q^T for one tile: two 32-key blocks, chains interleaved
-  auto qk = [&](const uint16_t *Ks, f32x16_t *acc) {
-    acc[0] = (f32x16_t){};
-    acc[1] = (f32x16_t){};
+  // S^T = K Q^T for one tile: two 32-key blocks per query group; each K
+  // fragment feeds the QG groups
+  auto qk = [&](const uint16_t *Ks, f32x16_t (*acc)[2]) {
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq) {
+      acc[gq][0] = (f32x16_t){};
+      acc[gq][1] = (f32x16_t){};
+    }
 #pragma unroll
     for (int ks = 0; ks < KSQ; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8_t kf = *(const bf16x8_t *)&Ks[(32 * kb + kslot) * D + (((2 * ks + g) ^ kx) << 3)];
-        acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], acc[kb], 0, 0, 0);
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq)
+          acc[gq][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[gq][ks], acc[gq][kb], 0, 0, 0);
       }
   };
-  // add the tile's scaled biases (0 for selected keys) and return the row
-  // max in base-2 units
+  // row max of a tile in base-2 units, after adding the tile's scaled biases
+  // (0 for selected keys, -inf for masked ones, ln n_c / scale for pseudo-keys)
   auto bias_max = [&](f32x16_t *acc, const float *bz) -> float {
     float mt = -__builtin_inff();
 #pragma unroll
@@ -326,115 +346,196 @@ __global__ __launch_bounds__(ATT_THREADS, 1) void k_attn(AttnArgs a) {
     mt *= sl2;
     return fmaxf(mt, __shfl_xor(mt, 32, 64));
   };
+  // the same for a tile of selected keys only (no biases)
+  auto plain_max = [&](const f32x16_t *acc) -> float {
+    float mt = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, acc[kb][i]);
+    mt *= sl2;
+    return fmaxf(mt, __shfl_xor(mt, 32, 64));
+  };
+  // the V^T operands of k-step s of a tile, one per 32-dim block
+  auto v_frags = [&](const uint16_t *Vs, int s, bf16x8_t *vf) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int ch = (4 * (db ^ vxq) + vc2) << 3;
+      const uint16_t *v0 = &Vs[(16 * s + vrow) * D + ch + vhalf];
+      const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(AC_LDS(i16x4_t, v0));
+      const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(AC_LDS(i16x4_t, v0 + 4 * D));
+      const i16x4_t cat[2] = {lo4, hi4};
+      vf[db] = *(const bf16x8_t *)cat;
+    }
+  };
+  const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+  // O^T += V^T P^T for every query group over the 4 k-steps of a tile
+  auto pv_all = [&](const uint16_t *Vs, const bf16x8_t (*pw)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bf16x8_t vf[DB];
+      v_frags(Vs, q, vf);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq)
+          acc_o[gq][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pw[gq][q], acc_o[gq][db], 0, 0, 0);
+    }
+  };
 
-  // Pipeline.  K and V of tile t + 2 are loaded while tile t is computed,
-  // into three buffers each, so every load has about two iterations to land;
-  // the row ring runs three tiles ahead.  Tiles past the end are loaded from
-  // clamped, in-bounds rows and never used, which keeps the number of loads
-  // per iteration fixed.
-  ring_load(0);
-  ring_load(1);
-  ring_load(2);
+  // Pipeline.  K of tile t + 3 and V of tile t + 2 are loaded while tile t
+  // is computed, into four buffers each (buffer t mod 4): K_t is read in
+  // iteration t and V_t in iteration t + 1, so every load has two to three
+  // iterations to land.  The row ring runs five tiles ahead.  Tiles past the
+  // end are loaded from clamped, in-bounds rows and never used, which keeps
+  // the number of loads per iteration fixed.  Each wave runs the PV product
+  // one tile behind the scores: iteration t computes S_t = K_t Q^T and its
+  // row max, then alternates the PV steps of tile t - 1 with the weights of
+  // S_t, so the softmax's vector work issues while the products run.
+#pragma unroll
+  for (int i = 0; i < 5; ++i) ring_load(i);
+  // V buffer 3 stands for "tile -1" in the first iteration: zeros (times
+  // zero weights), never uninitialised LDS
+  for (int e = tid; e < TILE / 8; e += 64 * NW) *(u32x4_t *)&Vb[3 * TILE + 8 * e] = (u32x4_t){0u, 0u, 0u, 0u};
   __builtin_amdgcn_s_waitcnt(0);  // the ring, the Q fragments and the scalars above have landed
   __syncthreads();
+  int rw_next;  // rows of tile tt + 2, committed one iteration earlier (its K load went then)
   {
     const int rw0 = commit(0);
     const int rw1 = commit(1);
+    rw_next = commit(2);
     dma(false, 0, rw0, 0);
     dma(true, 0, rw0, 0);
     dma(false, 1, rw1, 1);
     dma(true, 1, rw1, 1);
+    dma(false, 2, rw_next, 2);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
 
-  int b0 = 0;  // buffer of tile tt; tile tt + 2 goes to the one after the next
+  bf16x8_t pb[QG][4];  // weights of the previous tile, the B operands of its PV steps
+#pragma unroll
+  for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pb[gq][q] = (bf16x8_t){};
   for (int tt = 0; tt < ntiles; ++tt) {
-    const int b2 = b0 == 0 ? 2 : b0 - 1;
-    const int rw = commit(tt + 2);  // its ring slot landed by the last barrier
-    ring_load(tt + 3);
-    dma(false, tt + 2, rw, b2);     // buffers of tile tt - 1, read last iteration
-    dma(true, tt + 2, rw, b2);
+    const int b0 = tt & 3;
+    const int rw = commit(tt + 3);  // its ring slot landed by the last barrier
+    ring_load(tt + 5);
+    dma(false, tt + 3, rw, (tt + 3) & 3);      // K buffer of tile tt - 1, read last iteration
+    dma(true, tt + 2, rw_next, (tt + 2) & 3);  // V buffer of tile tt - 2, read last iteration
+    rw_next = rw;
     if (wave_active) {
-      f32x16_t sc[2];
+      bool any = false;
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq) any = any || alpha[gq] != 1.f;
+      if (__ballot(any)) {  // O follows the reference max set last iteration (rare)
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) acc_o[gq][db][jj] *= alpha[gq];
+      }
+      f32x16_t sc[QG][2];
       qk(Kb + b0 * TILE, sc);
-      const float mt = bias_max(sc, sbw + (tt & 3) * ATT_KT);
       // lazy rescale: the reference max m_i may trail the running max by up
-      // to 2^8, so p <= 256; O and l are rescaled only when a row outgrows it
-      if (__ballot(mt > m_i + 8.f)) {
-        const float m_new = fmaxf(m_i, mt);
-        const float alpha = m_i == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_i - m_new);
-        l_i *= alpha;
+      // to 2^8, so p <= 256; it moves only when a row outgrows it.  Tiles
+      // before the last selected one hold selected keys only: no biases.
+      float m_new[QG], m_use[QG];
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq) {
+        const float mt = tt < nt0 - 1 ? plain_max(sc[gq]) : bias_max(sc[gq], sbw + (tt & 3) * ATT_KT);
+        m_new[gq] = mt > m_i[gq] + 8.f ? mt : m_i[gq];
+        m_use[gq] = m_new[gq] == -__builtin_inff() ? 0.f : m_new[gq];
+      }
+      // the PV steps of the previous tile (zero weights before the first)
+      // alternate with the weights of this one: after each product, VPM
+      // weights of the same step, so the vector work issues while the
+      // products run.  The V^T operands of a step are read one step ahead.
+      const uint16_t *Vp = Vb + ((tt - 1) & 3) * TILE;
+      float lt[QG];
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq) lt[gq] = 0.f;
+      bf16x8_t vcur[DB], vnext[DB];
+      v_frags(Vp, 0, vcur);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (q + 1 < 4) v_frags(Vp, q + 1, vnext);
+        bf16x8_t t[QG];
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) acc_o[db][j] *= alpha;
-        m_i = m_new;
-      }
-      const float m_use = m_i == -__builtin_inff() ? 0.f : m_i;
-      // p = exp2(s * scale * log2 e + bias - m)
-      bf16x8_t pb[4];
+          for (int gq = 0; gq < QG; ++gq) {
+            acc_o[gq][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[db], pb[gq][q], acc_o[gq][db], 0, 0, 0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+            for (int u = 0; u < VPM; ++u) {
+              const int i = db * VPM + u;
+              t[gq][i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[gq][q >> 1][(q & 1) * 8 + i], sl2, -m_use[gq]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          bf16x8_t t;
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            t[i] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sc[kb][half * 8 + i], sl2, -m_use));
-          pb[kb * 2 + half] = t;
+        for (int gq = 0; gq < QG; ++gq) {
+          lt[gq] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(t[gq], t[gq], 0, 1), ones, lt[gq], false);
+          lt[gq] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(t[gq], t[gq], 2, 3), ones, lt[gq], false);
+          lt[gq] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(t[gq], t[gq], 4, 5), ones, lt[gq], false);
+          lt[gq] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(t[gq], t[gq], 6, 7), ones, lt[gq], false);
+          pb[gq][q] = t[gq];
         }
-      // the row sum adds the bf16 weights that the PV product uses, two per
-      // dot instruction
+        if (q + 1 < 4)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        l_i = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[q], pb[q], 0, 1), ones, l_i, false);
-        l_i = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[q], pb[q], 2, 3), ones, l_i, false);
-        l_i = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[q], pb[q], 4, 5), ones, l_i, false);
-        l_i = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[q], pb[q], 6, 7), ones, l_i, false);
+          for (int db = 0; db < DB; ++db) vcur[db] = vnext[db];
       }
-      // O^T += V^T P^T over 4 k-steps of 16 keys; the V^T operand (8 keys of
-      // one dim per lane) comes from two transposing 4-key reads
-      const uint16_t *Vs = Vb + b0 * TILE;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int ch = (4 * (db ^ vxq) + vc2) << 3;
-          const uint16_t *v0 = &Vs[(16 * s + vrow) * D + ch + vhalf];
-          const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(AC_LDS(i16x4_t, v0));
-          const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(AC_LDS(i16x4_t, v0 + 4 * D));
-          const i16x4_t cat[2] = {lo4, hi4};
-          const bf16x8_t vf = *(const bf16x8_t *)cat;
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[s], acc_o[db], 0, 0, 0);
-        }
+      for (int gq = 0; gq < QG; ++gq) {
+        alpha[gq] = m_i[gq] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_i[gq] - m_new[gq]);
+        l_i[gq] = fmaf(l_i[gq], alpha[gq], lt[gq]);
+        m_i[gq] = m_new[gq];
       }
     }
-    // All but this iteration's K and V loads have landed (the ring load of
-    // tile tt + 3 was issued before them); the barrier makes tile tt + 1 and
-    // the ring visible and frees the buffers of tile tt.
-    wait_vmcnt<2 * IPW>();
+    // K of tile tt + 1 and V of tile tt (issued two iterations ago) and the
+    // ring slot of tile tt + 4 (wave 0, last iteration) have landed; the loads
+    // issued after that ring load may still be in flight.  The barrier makes
+    // them visible and frees the K buffer of tile tt and the V buffer of
+    // tile tt - 1.
+    if (wave == 0) wait_vmcnt<4 * IPW + 1>();
+    else wait_vmcnt<4 * IPW>();
     __syncthreads();
-    b0 = b0 == 2 ? 0 : b0 + 1;
+  }
+  // the last tile's PV product; no load targets its buffer
+  if (wave_active && ntiles > 0) {
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) acc_o[gq][db][jj] *= alpha[gq];
+    pv_all(Vb + ((ntiles - 1) & 3) * TILE, pb);
   }
   __builtin_amdgcn_s_waitcnt(0);  // no load may still write LDS when the block ends
 
-  const float lsum = l_i + __shfl_xor(l_i, 32, 64);
-  if (!qvalid) return;
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  uint16_t *orow = a.O + ((int64_t)h * a.L + qrow) * D;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int gq = 0; gq < QG; ++gq) {
+    const float lsum = l_i[gq] + __shfl_xor(l_i[gq], 32, 64);
+    if (!qvalid[gq]) continue;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    uint16_t *orow = a.O + ((int64_t)h * a.L + qrow[gq]) * D;
 #pragma unroll
-    for (int jq = 0; jq < 4; ++jq) {
-      const int d0 = 32 * db + 8 * jq + 4 * g;
-      uint32_t w0 = (uint32_t)f2bf(acc_o[db][jq * 4 + 0] * inv) | ((uint32_t)f2bf(acc_o[db][jq * 4 + 1] * inv) << 16);
-      uint32_t w1 = (uint32_t)f2bf(acc_o[db][jq * 4 + 2] * inv) | ((uint32_t)f2bf(acc_o[db][jq * 4 + 3] * inv) << 16);
-      *(u32x2_t *)&orow[d0] = (u32x2_t){w0, w1};
-    }
-  if (a.lse != nullptr && g == 0)
-    a.lse[(int64_t)h * a.L + qrow] = lsum > 0.f ? (m_i + log2f(lsum)) * 0.69314718055994530942f : -__builtin_inff();
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const int d0 = 32 * db + 8 * jq + 4 * g;
+        uint32_t w0 = (uint32_t)f2bf(acc_o[gq][db][jq * 4 + 0] * inv) |
+                      ((uint32_t)f2bf(acc_o[gq][db][jq * 4 + 1] * inv) << 16);
+        uint32_t w1 = (uint32_t)f2bf(acc_o[gq][db][jq * 4 + 2] * inv) |
+                      ((uint32_t)f2bf(acc_o[gq][db][jq * 4 + 3] * inv) << 16);
+        *(u32x2_t *)&orow[d0] = (u32x2_t){w0, w1};
+      }
+    if (a.lse != nullptr && g == 0)
+      a.lse[(int64_t)h * a.L + qrow[gq]] =
+          lsum > 0.f ? (m_i[gq] + log2f(lsum)) * 0.69314718055994530942f : -__builtin_inff();
+  }
 }
 
 void launch_attn_prep(int D, const AttnArgs &a, const float *kmean, const float *vmean, uint16_t *kc, uint16_t *vc,
@@ -455,9 +556,9 @@ void launch_attn(int D, const AttnArgs &a, int BH, int max_blocks, hipStream_t s
   const long long total = ((long long)max_blocks * BH + 8 * ATT_XCD_CHUNK - 1) / (8 * ATT_XCD_CHUNK) *
                           (8 * ATT_XCD_CHUNK);  // whole chunks on all 8 XCDs
   if (D == 64)
-    hipLaunchKernelGGL(k_attn<64>, dim3((unsigned)total), dim3(ATT_THREADS), 0, st, aa);
+    hipLaunchKernelGGL((k_attn<64, ATT_QG>), dim3((unsigned)total), dim3(ATT_THREADS), 0, st, aa);
   else
-    hipLaunchKernelGGL(k_attn<128>, dim3((unsigned)total), dim3(ATT_THREADS), 0, st, aa);
+    hipLaunchKernelGGL((k_attn<128, ATT_QG>), dim3((unsigned)total), dim3(ATT_THREADS), 0, st, aa);
 }
 
 }  // namespace ac

@@ -10,8 +10,9 @@ constexpr int KPP_SMAX = 16384;  // most points a k-means++ subsample may hold
 constexpr int KPP_GRAM_MAX = 2048;  // subsamples up to this size seed from a distance matrix
 constexpr int SORT_TILE = 128;   // points per counting-sort tile (one wave)
 constexpr int SORT_GROUP = 32;   // tiles per group in the two-level scan over tiles
-constexpr int ATT_QT = 256;      // query rows per attention block (8 waves x 32)
-constexpr int ATT_THREADS = 512;
+constexpr int ATT_QT = 256;      // query rows per attention block
+constexpr int ATT_QG = 1;        // groups of 32 queries per attention wave
+constexpr int ATT_THREADS = 64 * ATT_QT / (32 * ATT_QG);
 constexpr int ATT_XCD_CHUNK = 4;  // consecutive query tiles kept on one XCD
 constexpr int ATT_KT = 64;       // keys per attention tile
 constexpr int SEL_MAXN = 4096;   // most key clusters the select kernel sorts
