@@ -469,6 +469,95 @@ def quest_compare(args):
               f"({r['valu_alu_frac']}) | {r['speedup']}x |", file=sys.stderr)
 
 
+def flow_log_snr(T: int, shift: float = 5.0):
+    """log SNR of a shifted flow-matching sampler (x_t = (1 - s) x_0 + s eps)
+    over T steps: a synthetic stand-in for a video DiT's sampling schedule."""
+    t = np.linspace(1.0, 0.0, T + 1)[:-1]
+    s = np.clip(shift * t / (1.0 + (shift - 1.0) * t), 1e-4, 1 - 1e-4)
+    return np.log(((1.0 - s) / s) ** 2)
+
+
+def denoise(args):
+    """T denoising steps of the workload's layer under the multi-step policy:
+    dense warm-up steps, k_max calibrated on an uncapped first sparse step
+    (untimed) so that a fraction of the heads falls back, the first sparse
+    step cold, the rest warm; optionally the SNR-guided top-p per step.
+    Each step's Q and K are a 2% perturbation of the previous step's (drawn
+    on the device).  One JSON line with per-step times."""
+    import torch
+    import csa_inputs as gen
+    import clustered_sparse_attention_amd as ac
+    w = gen.get_workload(args.workload, **({"H": args.heads} if args.heads else {}))
+    Q, K, V = gen.generate(w)
+    dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    Qd, Kd, Vd = dev(Q), dev(K), dev(V)
+    del Q, K, V
+    kw = workload_params(args.workload, args.variant, args.compensate)
+    base = _abi(kw)
+    shape = ac.Shape(w.B, w.H, w.L, w.d)
+    T, warm_steps = args.denoise, args.warmup_steps
+    # calibration: the first sparse step with a cap no head reaches
+    cal = ac.params_default(**{f: getattr(base, f) for f, _ in ac.Params._fields_})
+    cal.nmax = 3000
+    _, wsb = ac.ac_sizes(shape, cal)
+    ws = ac.workspace(wsb, Qd.device)
+    nq = min(base.nq, w.L)
+    st = ac.State(w.BH, nq, cal.nmax - 1 + cal.m0, w.d, Qd.device)
+    O = torch.empty_like(Qd)
+    hs = ac.ac_layer(shape, cal, Qd, Kd, Vd, st, O, ws, host_stats=True)
+    kmax = ac.ac_kmax_calibrate(hs["ncl_k"], args.dense_frac)
+    del st, ws
+    topp = ac.ac_topp_schedule(flow_log_snr(T), warm_steps, args.p_min, args.tau_sat) if args.topp_schedule else None
+    sch = ac.Schedule(warmup_steps=warm_steps, warmup_layers=0, nmax=kmax, topp=topp)
+    sparse_p = ac.ac_step_params(base, sch, T - 1, 0)
+    ncap, wsb = ac.ac_sizes(shape, sparse_p)
+    _, wsb_d = ac.ac_sizes(shape, ac.ac_step_params(base, sch, 0, 0))
+    ws = ac.workspace(max(wsb, wsb_d), Qd.device)
+    st = ac.State(w.BH, nq, ncap, w.d, Qd.device)
+    gen_t = torch.Generator(device="cuda")
+    gen_t.manual_seed(1103)
+
+    def perturb(x):
+        xf = x.float()
+        rms = xf.pow(2).mean(dim=(2, 3), keepdim=True).sqrt()
+        eps = torch.randn(xf.shape, generator=gen_t, device=xf.device, dtype=torch.float32)
+        return (xf + 0.02 * rms * eps).to(torch.bfloat16)
+
+    steps = []
+    for step in range(T):
+        if step > 0:
+            Qd, Kd = perturb(Qd), perturb(Kd)
+        p = ac.ac_step_params(base, sch, step, 0)
+        mode = "dense" if p.sel_mode == ac.AC_SEL_DENSE else ("cold" if not st.valid else "warm")
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ac.ac_layer(shape, p, Qd, Kd, Vd, st, O, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        rec = {"step": step, "mode": mode, "ms": round(e0.elapsed_time(e1), 3)}
+        if mode != "dense":
+            rec["sel_param"] = round(float(p.sel_param), 4)
+        steps.append(rec)
+        print(f"[bench] step {step} {mode}: {rec['ms']} ms", file=sys.stderr, flush=True)
+    fb = int(st.fallback.cpu().numpy().sum())
+    sd = sdpa_ms(Qd, Kd, Vd)
+    dense_ms = float(np.mean([r["ms"] for r in steps if r["mode"] == "dense"])) if warm_steps else None
+    total = sum(r["ms"] for r in steps)
+    warm = [r["ms"] for r in steps if r["mode"] == "warm"]
+    cold = [r["ms"] for r in steps if r["mode"] == "cold"]
+    out = {"metric": f"{T}-step denoising run of one layer: total ms", "value": round(total, 2), "unit": "ms",
+           "higher_is_better": False, "workload": w.description, "steps": T, "warmup_steps": warm_steps,
+           "kmax": kmax, "dense_frac_target": args.dense_frac, "fallback_heads": fb, "heads": w.BH,
+           "topp_schedule": None if topp is None else [round(float(x), 4) for x in topp],
+           "per_step": steps, "cold_ms": cold[0] if cold else None,
+           "warm_ms_mean": round(float(np.mean(warm)), 3) if warm else None,
+           "own_dense_ms": None if dense_ms is None else round(dense_ms, 3),
+           "sdpa_flash_ms": None if sd is None else round(sd, 3),
+           "speedup_vs_sdpa_flash_all_steps": None if sd is None else round(sd * T / total, 3)}
+    print(json.dumps(out), flush=True)
+
+
 def copy_probe(nbytes: int):
     """A plain device copy of nbytes (torch), for calibrating the HBM byte
     counters: its FETCH_SIZE / WRITE_SIZE should read nbytes each."""
@@ -500,6 +589,14 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a plain copy of this many bytes")
     ap.add_argument("--summarize", nargs="+", help="write a profile summary from rocprofv3 output (no GPU)")
+    ap.add_argument("--denoise", type=int, default=0,
+                    help="only run this many denoising steps under the multi-step policy (dense warm-up, calibrated "
+                         "k_max, cold then warm steps)")
+    ap.add_argument("--warmup-steps", type=int, default=2, help="dense warm-up steps of --denoise")
+    ap.add_argument("--dense-frac", type=float, default=0.15, help="heads targeted for dense attention by k_max")
+    ap.add_argument("--topp-schedule", action="store_true", help="--denoise: SNR-guided top-p per step")
+    ap.add_argument("--p-min", type=float, default=0.7)
+    ap.add_argument("--tau-sat", type=float, default=0.999)
     ap.add_argument("--quest-compare", action="store_true",
                     help="only time per-token Quest scores, TensorQuest (MFMA) against eq. (1) on the vector ALUs")
     args = ap.parse_args()
@@ -520,6 +617,9 @@ def main():
     ac.load()
     if args.quest_compare:
         quest_compare(args)
+        return
+    if args.denoise:
+        denoise(args)
         return
 
 

@@ -23,7 +23,8 @@ AC_SEL_TOPK, AC_SEL_DENSITY, AC_SEL_TOPP, AC_SEL_DENSE = range(4)
 AC_QUEST_MFMA, AC_QUEST_VALU = range(2)
 
 ENTRY_POINTS = ("ac_params_default", "ac_sizes", "ac_cluster_q", "ac_cluster_k", "ac_score_select",
-                "ac_sparse_attn", "ac_tail_merge", "ac_score_tokens", "ac_layer", "ac_status_str", "ac_last_error")
+                "ac_sparse_attn", "ac_tail_merge", "ac_score_tokens", "ac_layer", "ac_topp_schedule",
+                "ac_kmax_calibrate", "ac_step_params", "ac_status_str", "ac_last_error")
 
 
 class ACError(RuntimeError):
@@ -65,6 +66,11 @@ class CSelection(ctypes.Structure):
 
 class CState(ctypes.Structure):
     _fields_ = [("cent_q", P), ("cent_k", P), ("ncl_k", P), ("fallback", P), ("tau", P), ("valid", ctypes.c_int32)]
+
+
+class CSchedule(ctypes.Structure):
+    _fields_ = [("warmup_steps", ctypes.c_int32), ("warmup_layers", ctypes.c_int32), ("nmax", ctypes.c_int32),
+                ("steps", ctypes.c_int32), ("topp", P)]
 
 
 class CLayerStats(ctypes.Structure):
@@ -113,6 +119,14 @@ def load() -> ctypes.CDLL:
     lib.ac_layer.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), vp, vp, vp, ctypes.POINTER(CState), vp,
                              ctypes.POINTER(CLayerStats), vp, ctypes.c_size_t, vp]
     lib.ac_layer.restype = st
+    lib.ac_topp_schedule.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_double,
+                                     ctypes.c_int32, vp]
+    lib.ac_topp_schedule.restype = st
+    lib.ac_kmax_calibrate.argtypes = [vp, ctypes.c_int32, ctypes.c_double, ctypes.POINTER(ctypes.c_int32)]
+    lib.ac_kmax_calibrate.restype = st
+    lib.ac_step_params.argtypes = [ctypes.POINTER(Params), ctypes.POINTER(CSchedule), ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.POINTER(Params)]
+    lib.ac_step_params.restype = st
     lib.ac_status_str.argtypes = [st]
     lib.ac_status_str.restype = ctypes.c_char_p
     lib.ac_last_error.argtypes = []
@@ -294,3 +308,38 @@ def ac_layer(shape, params, Q, K, V, state: State, O, ws, host_stats: bool = Fal
                            _stream(stream)))
     state.valid = cs.valid
     return arrs
+
+
+# ---------------------------------------------------------------- multi-step policy (host only)
+def ac_topp_schedule(log_snr, warmup_steps: int, p_min: float, tau: float, t_pivot: int = -1):
+    """Per-step top-p (numpy float32 array) of the SNR-guided schedule."""
+    import numpy as np
+    ell = np.ascontiguousarray(log_snr, dtype=np.float64)
+    out = np.empty(ell.size, dtype=np.float32)
+    _check(load().ac_topp_schedule(ell.ctypes.data, ell.size, int(warmup_steps), float(p_min), float(tau),
+                                   int(t_pivot), out.ctypes.data))
+    return out
+
+
+def ac_kmax_calibrate(ncl, frac: float) -> int:
+    import numpy as np
+    n = np.ascontiguousarray(ncl, dtype=np.int32)
+    k = ctypes.c_int32(0)
+    _check(load().ac_kmax_calibrate(n.ctypes.data, n.size, float(frac), ctypes.byref(k)))
+    return int(k.value)
+
+
+class Schedule:
+    """Holds an ac_schedule and the host array its topp points to."""
+
+    def __init__(self, warmup_steps: int = 0, warmup_layers: int = 0, nmax: int = 0, topp=None):
+        import numpy as np
+        self.topp = None if topp is None else np.ascontiguousarray(topp, dtype=np.float32)
+        self.s = CSchedule(warmup_steps, warmup_layers, nmax, 0 if self.topp is None else self.topp.size,
+                           None if self.topp is None else self.topp.ctypes.data)
+
+
+def ac_step_params(base: Params, sch: Schedule, step: int, layer: int) -> Params:
+    out = Params()
+    _check(load().ac_step_params(ctypes.byref(base), ctypes.byref(sch.s), int(step), int(layer), ctypes.byref(out)))
+    return out

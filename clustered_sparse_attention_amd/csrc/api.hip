@@ -769,6 +769,28 @@ AC_API ac_status ac_layer(const ac_shape *s, const ac_params *p, const uint16_t 
                at<uint8_t>(ws, P.fb), at<float>(ws, P.tau), at<float>(ws, P.mse), at<int>(ws, P.stages)};
   ac_selection sel{P.ncapk, at<int>(ws, P.sel_list), at<int>(ws, P.sel_n), at<uint32_t>(ws, P.sel_mask),
                    at<float>(ws, P.sel_score)};
+  if (p->sel_mode == AC_SEL_DENSE) {
+    // dense attention only: no clustering, one query "cluster" of all tokens
+    // per head, the state untouched (the next sparse call starts cold if it
+    // is not valid)
+    launch_identity_clusters(q.perm, q.seg, q.ncl, P.L, P.nq, BH, st);
+    launch_fill_i32(k.ncl, BH, 0, st);
+    launch_fill_u8(ks.fallback, BH, 0, st);
+    AC_CHECK_LAUNCH();
+    AC_TRY(do_attn(P, p, Q, K, V, &q, &k, &ks, &sel, O, nullptr, ws, st));
+    if (host_stats) {
+      AC_HIP(hipStreamSynchronize(st));
+      for (int h = 0; h < BH; ++h) {
+        if (host_stats->ncl_k) host_stats->ncl_k[h] = 0;
+        if (host_stats->fallback) host_stats->fallback[h] = 0;
+        if (host_stats->tau) host_stats->tau[h] = 0.f;
+        if (host_stats->mse) host_stats->mse[h] = 0.f;
+        if (host_stats->stages) host_stats->stages[h] = 0;
+        if (host_stats->pairs) host_stats->pairs[h] = (int64_t)P.L * P.L;
+      }
+    }
+    return AC_OK;
+  }
   const bool warm = state->valid != 0;
   // query clustering on the side stream, key clustering on the caller's
   SideStream *ss = nullptr;
@@ -810,6 +832,78 @@ AC_API ac_status ac_layer(const ac_shape *s, const ac_params *p, const uint16_t 
     if (host_stats->stages) AC_HIP(hipMemcpy(host_stats->stages, ks.stages, BH * 4, hipMemcpyDeviceToHost));
     if (host_stats->pairs) AC_HIP(hipMemcpy(host_stats->pairs, at<long long>(ws, P.pairs), BH * 8, hipMemcpyDeviceToHost));
   }
+  return AC_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Multi-step policy (host only).
+
+AC_API ac_status ac_topp_schedule(const double *log_snr, int32_t steps, int32_t warmup_steps, double p_min, double tau,
+                                  int32_t t_pivot, float *topp) {
+  if (!log_snr || !topp) return fail(AC_E_ARG, "log_snr or topp is NULL");
+  if (steps < 2 || warmup_steps < 0 || warmup_steps >= steps - 1)
+    return fail(AC_E_ARG, "need steps >= 2 and 0 <= warmup_steps < steps - 1 (got %d, %d)", steps, warmup_steps);
+  if (!(p_min > 0.0 && p_min <= 1.0) || !(tau > 0.5 && tau < 1.0))
+    return fail(AC_E_ARG, "need 0 < p_min <= 1 and 0.5 < tau < 1");
+  for (int t = 0; t < steps; ++t)
+    if (!std::isfinite(log_snr[t])) return fail(AC_E_ARG, "log_snr[%d] is not finite", t);
+  if (t_pivot < 0) {
+    // the sparse step where log SNR changes least
+    double best = INFINITY;
+    for (int t = warmup_steps; t < steps; ++t) {
+      const double d = t + 1 < steps ? std::fabs(log_snr[t + 1] - log_snr[t]) : std::fabs(log_snr[t] - log_snr[t - 1]);
+      if (d < best) { best = d; t_pivot = t; }
+    }
+  } else if (t_pivot < warmup_steps || t_pivot >= steps) {
+    return fail(AC_E_ARG, "t_pivot %d outside the sparse steps", t_pivot);
+  }
+  const double span = log_snr[steps - 1] - log_snr[t_pivot];
+  if (!(span > 0.0)) return fail(AC_E_ARG, "log SNR must grow from the pivot step to the last step");
+  // sigmoid(k x_last) = tau
+  const double k = std::log(tau / (1.0 - tau)) / span;
+  for (int t = 0; t < steps; ++t) {
+    if (t < warmup_steps) {
+      topp[t] = 1.f;
+      continue;
+    }
+    const double x = log_snr[t] - log_snr[t_pivot];
+    topp[t] = (float)(p_min + (1.0 - p_min) * (1.0 - 1.0 / (1.0 + std::exp(-k * x))));
+  }
+  return AC_OK;
+}
+
+AC_API ac_status ac_kmax_calibrate(const int32_t *ncl, int32_t units, double frac, int32_t *kmax) {
+  if (!ncl || !kmax) return fail(AC_E_ARG, "ncl or kmax is NULL");
+  if (units < 1 || !(frac >= 0.0 && frac <= 1.0)) return fail(AC_E_ARG, "need units >= 1 and 0 <= frac <= 1");
+  const int nd = (int)std::ceil(frac * units - 1e-9);
+  if (nd <= 0) {
+    *kmax = 0;
+    return AC_OK;
+  }
+  std::vector<int32_t> v(ncl, ncl + units);
+  std::sort(v.begin(), v.end(), [](int32_t a, int32_t b) { return a > b; });
+  *kmax = v[std::min(nd, units) - 1];
+  return AC_OK;
+}
+
+AC_API ac_status ac_step_params(const ac_params *base, const ac_schedule *sch, int32_t step, int32_t layer,
+                                ac_params *out) {
+  if (!base || !sch || !out) return fail(AC_E_ARG, "base, schedule or out is NULL");
+  if (step < 0 || layer < 0) return fail(AC_E_ARG, "step and layer must be >= 0");
+  if (sch->warmup_steps < 0 || sch->warmup_layers < 0 || sch->nmax < 0)
+    return fail(AC_E_ARG, "schedule counts must be >= 0");
+  if (sch->topp && step >= sch->steps) return fail(AC_E_ARG, "step %d beyond the %d scheduled steps", step, sch->steps);
+  ac_params p = *base;
+  if (step < sch->warmup_steps || layer < sch->warmup_layers) {
+    p.sel_mode = AC_SEL_DENSE;
+  } else {
+    if (sch->nmax > 0) p.nmax = sch->nmax;
+    if (sch->topp) {
+      p.sel_mode = AC_SEL_TOPP;
+      p.sel_param = sch->topp[step];
+    }
+  }
+  *out = p;
   return AC_OK;
 }
 

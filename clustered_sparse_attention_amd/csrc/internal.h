@@ -179,6 +179,7 @@ void launch_seg_mean(const float *val, const int *perm, const int *seg, int L, i
                      int BH, hipStream_t st);
 void launch_fill_i32(int *p, int64_t n, int v, hipStream_t st);
 void launch_fill_u8(uint8_t *p, int64_t n, uint8_t v, hipStream_t st);
+void launch_identity_clusters(int *perm, int *seg, int *ncl, int L, int segcap, int BH, hipStream_t st);
 void launch_copy_i32(const int *s, int *d, int64_t n, hipStream_t st);
 void launch_copy_f32(const float *s, float *d, int64_t n, hipStream_t st);
 void launch_copy_u8(const uint8_t *s, uint8_t *d, int64_t n, hipStream_t st);

@@ -851,6 +851,16 @@ __global__ void k_fill_i32(int *__restrict__ p, int64_t n, int v) {
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = v;
 }
+// one cluster per head holding every token in order: perm = 0..L-1,
+// seg = [0, L, L, ...], ncl = 1 (the layout of dense attention)
+__global__ void k_identity_clusters(int *__restrict__ perm, int *__restrict__ seg, int *__restrict__ ncl, int L,
+                                    int segcap) {
+  const int h = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < L) perm[(int64_t)h * L + i] = (int)i;
+  if (i <= segcap) seg[(int64_t)h * (segcap + 1) + i] = i == 0 ? 0 : L;
+  if (i == 0) ncl[h] = 1;
+}
 __global__ void k_copy_i32(const int *__restrict__ src, int *__restrict__ dst, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) dst[i] = src[i];
@@ -994,6 +1004,11 @@ void launch_seg_mean(const float *val, const int *perm, const int *seg, int L, i
 
 void launch_fill_i32(int *p, int64_t n, int v, hipStream_t st) {
   if (n > 0) hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n, v);
+}
+void launch_identity_clusters(int *perm, int *seg, int *ncl, int L, int segcap, int BH, hipStream_t st) {
+  const int64_t n = std::max<int64_t>(L, (int64_t)segcap + 1);
+  hipLaunchKernelGGL(k_identity_clusters, dim3((unsigned)((n + 255) / 256), (unsigned)BH), dim3(256), 0, st, perm, seg,
+                     ncl, L, segcap);
 }
 void launch_fill_u8(uint8_t *p, int64_t n, uint8_t v, hipStream_t st) {
   if (n > 0) hipLaunchKernelGGL(k_fill_u8, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n, v);

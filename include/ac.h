@@ -17,7 +17,9 @@
  *                    on MFMA (TensorQuest) or on the vector ALUs (eq. (1) as written)
  *   ac_tail_merge    iCATS tail merging of the query clusters before the attention
  *   ac_layer         the whole layer, cold (first denoising step) or warm (later steps reuse the cluster
- *                    counts and centres: AdaCluster §3.2.2 "Efficient initialization")
+ *                    counts and centres: AdaCluster §3.2.2 "Efficient initialization"), or dense
+ *   ac_topp_schedule, ac_kmax_calibrate, ac_step_params
+ *                    the multi-step policy: dense warm-up, calibrated k_max, SNR-guided top-p (host only)
  *
  * Conventions (all entry points)
  * ------------------------------
@@ -260,10 +262,52 @@ ac_status ac_score_tokens(const ac_shape *s, const ac_params *p, const uint16_t 
 /* The whole layer (AdaCluster Algorithm 3 with the optional compensation): ac_cluster_q,
  * ac_cluster_k, ac_score_select, ac_tail_merge when p->tail_block > 0, and ac_sparse_attn on
  * buffers carved from the workspace.  Cold when
- * !state->valid (fills the state and sets valid = 1), warm otherwise.  host_stats may be NULL. */
+ * !state->valid (fills the state and sets valid = 1), warm otherwise.  With p->sel_mode AC_SEL_DENSE
+ * it runs dense attention only (no clustering; the state is left as it is; host_stats reports 0
+ * clusters and L*L pairs per head).  host_stats may be NULL. */
 ac_status ac_layer(const ac_shape *s, const ac_params *p, const uint16_t *Q, const uint16_t *K,
                    const uint16_t *V, ac_state *state, uint16_t *O, ac_layer_stats *host_stats,
                    void *ws, size_t ws_bytes, ac_stream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Multi-step, multi-layer policy (host only: no device work, no workspace).
+ * AdaCluster §3.2.2 "Efficient initialization": the multi-stage clustering runs at a layer's first
+ * sparse denoising step (ac_layer with a state that is not valid), later steps start from the
+ * previous centres with the cluster counts kept (ac_layer warm).  AdaCluster §4.1: k_max (N_max)
+ * is set so that the least compact ~15% of attention units use full attention.  iCATS (method
+ * section, SNR-guided sparsity, and its warm-up setting): the first steps and layers stay dense; a
+ * per-step top-p follows an inverse sigmoid of log SNR.  An attention unit is one (layer, head). */
+
+typedef struct ac_schedule {
+  int32_t warmup_steps;  /* steps 0 .. warmup_steps-1 run dense attention */
+  int32_t warmup_layers; /* layers 0 .. warmup_layers-1 run dense attention at every step */
+  int32_t nmax;          /* calibrated k_max (ac_kmax_calibrate) for the sparse units; 0 keeps base->nmax */
+  int32_t steps;         /* entries of topp */
+  const float *topp;     /* [steps] HOST per-step p (ac_topp_schedule): sparse units select with
+                            AC_SEL_TOPP at that p; NULL keeps base->sel_mode and sel_param */
+} ac_schedule;
+
+/* SNR-guided top-p per denoising step: topp[t] = p_min + (1 - p_min) (1 - sigmoid(k x_t)) with
+ * x_t = log_snr[t] - log_snr[t_pivot] and k = logit(tau) / (log_snr[steps-1] - log_snr[t_pivot]),
+ * so the sigmoid is 1/2 at the pivot and tau at the last step; topp[t] = 1 for t < warmup_steps.
+ * t_pivot < 0 picks the sparse step where log SNR changes least (forward difference).  log_snr:
+ * [steps] HOST, log((a_t / b_t)^2) of the sampler (x_t = a_t x_0 + b_t eps), growing from the pivot to
+ * the last step.  Needs steps >= 2, 0 <= warmup_steps < steps - 1, 0 < p_min <= 1, 0.5 < tau < 1. */
+ac_status ac_topp_schedule(const double *log_snr, int32_t steps, int32_t warmup_steps, double p_min, double tau,
+                           int32_t t_pivot, float *topp);
+
+/* k_max from the key-cluster counts ncl[units] of an uncapped first step (ac_layer_stats.ncl_k over
+ * layers and heads, run with the largest nmax): the count of the unit ranked ceil(frac * units)
+ * from the top, 0 when frac * units rounds to no unit.  Run with nmax = k_max, Algorithm 1 decides
+ * the fallback: a unit falls back when a stage would start with k_max centres or more and keys are
+ * left, so at most that many units fall back. */
+ac_status ac_kmax_calibrate(const int32_t *ncl, int32_t units, double frac, int32_t *kmax);
+
+/* The parameters of (step, layer) for ac_layer: base with sel_mode AC_SEL_DENSE during warm-up
+ * (steps < warmup_steps or layers < warmup_layers), otherwise with nmax = sch->nmax (if > 0) and,
+ * when sch->topp is set, sel_mode AC_SEL_TOPP with sel_param = sch->topp[step]. */
+ac_status ac_step_params(const ac_params *base, const ac_schedule *sch, int32_t step, int32_t layer,
+                         ac_params *out);
 
 /* Static description of a status code. */
 const char *ac_status_str(ac_status st);

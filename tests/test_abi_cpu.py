@@ -33,6 +33,7 @@ def test_struct_sizes_match_c_layout():
     assert ctypes.sizeof(ac.CKStats) == 64
     assert ctypes.sizeof(ac.CSelection) == 40
     assert ctypes.sizeof(ac.CState) == 48
+    assert ctypes.sizeof(ac.CSchedule) == 24
 
 
 def test_defaults_and_status_strings():

@@ -369,3 +369,71 @@ def test_token_quest_both_engines(tiny, shape):
     for ld in (r.ncap_k + 5, 7):
         worst = check_token_quest(r, Q, K, V, ld)
         print(f"token quest shape={shape} ld={ld}: max error / bound {worst}")
+
+
+# ---------------------------------------------------------------- multi-step, multi-layer policy
+
+def test_multistep_driver_against_oracle():
+    """Four denoising steps of two layers through ac_step_params and ac_layer:
+    step 0 and layer 0 dense (warm-up), k_max calibrated on an uncapped first
+    sparse step, SNR-guided top-p per step; the first sparse step of layer 1
+    cold (counts and flags equal to the oracle's Algorithm 1 with that cap),
+    later steps warm from the carried state.  Every output against the
+    oracle's run of the same step (warm steps from the carried centres)."""
+    import torch
+    import clustered_sparse_attention_amd as ac
+    from oracle import driver as odr
+    from test_oracle_driver import _ell
+    T, layers = 4, 2
+    base = P(tau_rule=nm.TAU_MEAN_X, tau_param=1.5, m0=16, nmax=200, init_sample=8, sel_mode=nm.SEL_TOPP,
+             sel_param=0.9)
+    inputs = [gen.generate(gen.get_workload("tiny", seed=101 + 10 * l)) for l in range(layers)]
+    topp = ac.ac_topp_schedule(_ell(T), 1, 0.6, 0.95)
+    # calibration: the first sparse step uncapped, over the sparse layers' heads
+    r = Run(*inputs[1], base)
+    cal_state = ac.State(r.BH, r.nq, r.ncap_k, r.d, torch.device("cuda"))
+    O = torch.empty_like(r.Q)
+    hs = ac.ac_layer(r.shape, r.cp, r.Q, r.K, r.V, cal_state, O, r.ws, host_stats=True)
+    kmax = ac.ac_kmax_calibrate(hs["ncl_k"], 0.5)
+    assert kmax == odr.kmax_calibrate(hs["ncl_k"], 0.5) > 0
+    sch = ac.Schedule(warmup_steps=1, warmup_layers=1, nmax=kmax, topp=topp)
+    cbase = r.cp
+    states = {}
+    cur = [list(x) for x in inputs]
+    for step in range(T):
+        if step > 0:  # next-step inputs: 2% perturbations of Q and K
+            for l in range(layers):
+                cur[l][0] = gen.perturb(cur[l][0], 1103 + 7 * step + l)
+                cur[l][1] = gen.perturb(cur[l][1], 2203 + 7 * step + l)
+        for l in range(layers):
+            cp = ac.ac_step_params(cbase, sch, step, l)
+            po = odr.step_params(base, step, l, 1, 1, kmax, topp)
+            assert (cp.sel_mode, cp.nmax) == (po.sel_mode, po.nmax)
+            Qb, Kb, Vb = cur[l]
+            rr = Run(Qb, Kb, Vb, po)
+            # the state is laid out for the sparse steps' key capacity (k_max - 1 + m0)
+            st = states.setdefault(l, ac.State(rr.BH, rr.nq, kmax - 1 + base.m0, rr.d, torch.device("cuda")))
+            was_valid = st.valid
+            prev = None if not was_valid else [dict(cent_q=np_(st.cent_q)[bh].astype(np.float64),
+                                                      cent_k=np_(st.cent_k)[bh, :int(np_(st.ncl_k)[bh])].astype(
+                                                          np.float64),
+                                                      fallback=bool(np_(st.fallback)[bh]), tau=float(np_(st.tau)[bh]))
+                                                 for bh in range(rr.BH)]
+            Og = torch.empty_like(rr.Q)
+            hs = ac.ac_layer(rr.shape, cp, rr.Q, rr.K, rr.V, st, Og, rr.ws, host_stats=True)
+            Og = bf16_dev_to_f64(Og).reshape(rr.BH, rr.L, rr.d)
+            dense = po.sel_mode == nm.SEL_DENSE
+            assert st.valid == (0 if dense and not was_valid else 1)
+            for bh in range(rr.BH):
+                Qh, Kh, Vh = (_bits(x, bh) for x in (Qb, Kb, Vb))
+                if dense:
+                    Qx, Kx, Vx = (nm.bf16_to_f64(x) for x in (Qh, Kh, Vh))
+                    Oo, _ = oat.dense_rows(Qx, Kx, Vx, np.arange(rr.L), po.attn_scale(rr.d))
+                    assert hs["pairs"][bh] == rr.L * rr.L
+                else:
+                    ref = oly.run_head(Qh, Kh, Vh, po, bh, warm=None if prev is None else prev[bh])
+                    Oo = ref["O"]
+                    if prev is None:
+                        assert hs["ncl_k"][bh] == ref["k"]["nk"] and hs["fallback"][bh] == ref["k"]["fallback"]
+                mx, rl2 = attn_error(Og[bh], Oo)
+                assert mx <= ATTN_MAX_ABS and rl2 <= ATTN_REL_L2, (step, l, bh, mx, rl2)
