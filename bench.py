@@ -64,7 +64,7 @@ def _abi(kw):
 class Layer:
     """Device buffers of one layer and the four entry points."""
 
-    def __init__(self, Qd, Kd, Vd, shape, params, tail_block=0):
+    def __init__(self, Qd, Kd, Vd, shape, params, tail_block=0, key_metric=False):
         import torch
         import clustered_sparse_attention_amd as ac
         self.ac = ac
@@ -88,6 +88,9 @@ class Layer:
             self.selm = ac.Selection(BH, nq, self.ncap, dev, score=False)
         self.torch = torch
         self.side = torch.cuda.Stream()  # default priority
+        self.key_metric = key_metric
+        if key_metric:
+            self.M = torch.empty((BH, d, d), dtype=torch.float32, device=dev)
 
     def step(self, ev=None):
         """One layer: the query clustering on a side stream beside the key
@@ -97,15 +100,26 @@ class Layer:
         selection done, attention done)."""
         ac, torch = self.ac, self.torch
         main = torch.cuda.current_stream()
-        if ev: ev[0].record(main)
-        self.side.wait_stream(main)
-        if ev: ev[2].record(self.side)
-        ac.ac_cluster_q(self.shape, self.p, self.Q, None, self.q, self.ws, stream=self.side.cuda_stream)
-        if ev: ev[3].record(self.side)
-        ac.ac_cluster_k(self.shape, self.p, self.K, self.V, None, self.k, self.st, self.ws)
-        if ev: ev[1].record(main)
-        main.wait_stream(self.side)
-        if ev: ev[4].record(main)
+        if self.key_metric:
+            # interaction-aware keys need the query clusters first: one stream
+            if ev: ev[0].record(main)
+            if ev: ev[2].record(main)
+            ac.ac_cluster_q(self.shape, self.p, self.Q, None, self.q, self.ws)
+            if ev: ev[3].record(main)
+            ac.ac_interaction_matrix(self.shape, self.p, self.Q, self.q, self.M, self.ws)
+            ac.ac_cluster_k_metric(self.shape, self.p, self.K, self.V, self.M, self.k, self.st, self.ws)
+            if ev: ev[1].record(main)
+            if ev: ev[4].record(main)
+        else:
+            if ev: ev[0].record(main)
+            self.side.wait_stream(main)
+            if ev: ev[2].record(self.side)
+            ac.ac_cluster_q(self.shape, self.p, self.Q, None, self.q, self.ws, stream=self.side.cuda_stream)
+            if ev: ev[3].record(self.side)
+            ac.ac_cluster_k(self.shape, self.p, self.K, self.V, None, self.k, self.st, self.ws)
+            if ev: ev[1].record(main)
+            main.wait_stream(self.side)
+            if ev: ev[4].record(main)
         ac.ac_score_select(self.shape, self.p, self.q, self.k, self.st, self.sel, self.ws)
         if self.tail_block:
             ac.ac_tail_merge(self.shape, self.p, self.tail_block, self.q, self.sel, self.qm, self.selm, self.ws)
@@ -585,6 +599,9 @@ def main():
     ap.add_argument("--tail-block", type=int, default=0,
                     help="merge query-cluster tails for attention blocks of this many rows before the attention "
                          "(iCATS tail merging; 0 = off)")
+    ap.add_argument("--key-metric", type=int, default=0,
+                    help="cluster the keys interaction-aware (iCATS, metric M_Q from the query clusters) into this "
+                         "many clusters instead of Algorithm 1 (0 = off)")
     ap.add_argument("--no-baselines", action="store_true", help="skip dense baselines and the CPU oracle")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a plain copy of this many bytes")
@@ -636,8 +653,11 @@ def main():
 
     Qd, Kd, Vd = dev(Q), dev(K), dev(V)
     kw = workload_params(args.workload, args.variant, args.compensate)
+    if args.key_metric:
+        kw["m0"] = args.key_metric
     params = _abi(kw)
-    layer = Layer(Qd, Kd, Vd, (w.B, w.H, w.L, w.d), params, tail_block=args.tail_block)
+    layer = Layer(Qd, Kd, Vd, (w.B, w.H, w.L, w.d), params, tail_block=args.tail_block,
+                  key_metric=bool(args.key_metric))
     if args.serial:
         layer.side = torch.cuda.current_stream()
 
@@ -693,6 +713,8 @@ def main():
                      "clustering_q_beside_k": round(float(phase_ms[2]), 3),
                      "score_select": round(float(phase_ms[3]), 3), "sparse_attn": round(attn_ms, 3)},
         "_phase_note": "score_select includes ac_tail_merge when tail merging is on",
+        "key_clustering": "interaction-aware, %d clusters (iCATS)" % args.key_metric if args.key_metric
+                          else "Algorithm 1 (multi-stage)",
         "tail_merge": None if not args.tail_block else dict(
             zip(("block", "query_blocks_before", "query_blocks_after"),
                 (args.tail_block,) + layer.query_blocks(args.tail_block))),

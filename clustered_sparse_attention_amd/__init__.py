@@ -23,7 +23,8 @@ AC_SEL_TOPK, AC_SEL_DENSITY, AC_SEL_TOPP, AC_SEL_DENSE = range(4)
 AC_QUEST_MFMA, AC_QUEST_VALU = range(2)
 
 ENTRY_POINTS = ("ac_params_default", "ac_sizes", "ac_cluster_q", "ac_cluster_k", "ac_score_select",
-                "ac_sparse_attn", "ac_tail_merge", "ac_score_tokens", "ac_layer", "ac_topp_schedule",
+                "ac_sparse_attn", "ac_tail_merge", "ac_score_tokens", "ac_interaction_matrix",
+                "ac_cluster_k_metric", "ac_layer", "ac_topp_schedule",
                 "ac_kmax_calibrate", "ac_step_params", "ac_status_str", "ac_last_error")
 
 
@@ -119,6 +120,12 @@ def load() -> ctypes.CDLL:
     lib.ac_layer.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), vp, vp, vp, ctypes.POINTER(CState), vp,
                              ctypes.POINTER(CLayerStats), vp, ctypes.c_size_t, vp]
     lib.ac_layer.restype = st
+    lib.ac_interaction_matrix.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), vp, ctypes.POINTER(CClusters),
+                                          vp, vp, ctypes.c_size_t, vp]
+    lib.ac_interaction_matrix.restype = st
+    lib.ac_cluster_k_metric.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), vp, vp, vp,
+                                        ctypes.POINTER(CClusters), ctypes.POINTER(CKStats), vp, ctypes.c_size_t, vp]
+    lib.ac_cluster_k_metric.restype = st
     lib.ac_topp_schedule.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_double, ctypes.c_double,
                                      ctypes.c_int32, vp]
     lib.ac_topp_schedule.restype = st
@@ -289,6 +296,18 @@ def ac_score_tokens(shape, params, Q, k: Clusters, stats: KStats, engine: int, S
     """Per-token Quest scores into S ([BH, L, ld] float32)."""
     _check(load().ac_score_tokens(ctypes.byref(shape), ctypes.byref(params), _ptr(Q), ctypes.byref(k.c()),
                                   ctypes.byref(stats.c()), int(engine), _ptr(S), int(ld), _stream(stream)))
+
+
+def ac_interaction_matrix(shape, params, Q, q: Clusters, M, ws, stream=None):
+    """M_Q of every head ([BH, d, d] float32) from the query clusters q."""
+    _check(load().ac_interaction_matrix(ctypes.byref(shape), ctypes.byref(params), _ptr(Q), ctypes.byref(q.c()),
+                                        _ptr(M), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def ac_cluster_k_metric(shape, params, K, V, M, k_out: Clusters, stats: KStats, ws, stream=None):
+    _check(load().ac_cluster_k_metric(ctypes.byref(shape), ctypes.byref(params), _ptr(K), _ptr(V), _ptr(M),
+                                      ctypes.byref(k_out.c()), ctypes.byref(stats.c()), _ptr(ws), ws.numel(),
+                                      _stream(stream)))
 
 
 def ac_layer(shape, params, Q, K, V, state: State, O, ws, host_stats: bool = False, stream=None):

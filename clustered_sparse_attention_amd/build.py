@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libac.so")
 
-SOURCES = ["api.hip", "kmeans.hip", "kpp.hip", "select.hip", "attn.hip", "merge.hip", "quest.hip"]
+SOURCES = ["api.hip", "kmeans.hip", "kpp.hip", "select.hip", "attn.hip", "merge.hip", "quest.hip", "metric.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("AC_OFFLOAD_ARCH", "gfx950")
 

@@ -116,6 +116,8 @@ struct Plan {
   size_t sel_list, sel_n, sel_mask, sel_score;
   // tail merging: its plan, and ac_layer's merged clusters and selection
   size_t tm_plan, m_labels, m_perm, m_seg, m_list, m_n, m_mask;
+  // interaction matrix: raw query sums and counts per query cluster
+  size_t qsum, qcnt;
 };
 
 // stride of the per-selection key row lists: whole key tiles
@@ -216,6 +218,8 @@ Plan make_plan(const ac_shape *s, const ac_params *p) {
   P.m_list = take(BH * P.nq * (size_t)P.ncapk * 4);
   P.m_n = take(BH * P.nq * 4);
   P.m_mask = take(BH * P.nq * (size_t)P.mwords * 4);
+  P.qsum = take(BH * P.nq * D * 8);
+  P.qcnt = take(BH * P.nq * 4);
   P.total = off + 256;  // slack for aligning the base pointer
   return P;
 }
@@ -274,8 +278,10 @@ struct Engine {
     return s;
   }
   // mmax: bound on m over heads (grid size); npts: bound on n.
+  // metric: NULL for Euclidean distances, else [BH, D, D] fp32: the assignment
+  // minimises (x - c) M (x - c)^T (centre operands M c and c M c^T)
   ac_status run(const KmArgs &a, int mmax, int npts, bool seed_init, int iters, const ac_params *p, int role,
-                int stage, int *labels_out) {
+                int stage, int *labels_out, const float *metric = nullptr) {
     const int D = P.D;
     if (seed_init) {
       if (S.kpp_smax <= KPP_GRAM_MAX)
@@ -287,6 +293,7 @@ struct Engine {
     }
     CentOps op = ops();
     launch_cent_prep(D, a, op, P.BH, mmax, st);
+    if (metric) launch_cent_prep_metric(D, a, op, metric, P.BH, mmax, st);
     AC_CHECK_LAUNCH();
     int *lab = at<int>(ws, S.lab);
     for (int it = 0; it < iters; ++it) {
@@ -295,6 +302,7 @@ struct Engine {
       launch_sort(s, P.BH, npts, st);
       launch_update(D, a, s, op, P.BH, mmax, npts, at<int>(ws, S.chunk_off), S.mcap + 1, at<double>(ws, S.upd_part),
                     (int64_t)S.upd_items * D, st);
+      if (metric) launch_cent_prep_metric(D, a, op, metric, P.BH, mmax, st);
       AC_CHECK_LAUNCH();
     }
     launch_assign(D, a, op, P.BH, mmax, npts, labels_out, P.L, st);
@@ -437,6 +445,33 @@ ac_status do_cluster_k_warm(const Plan &P, const ac_params *p, const uint16_t *K
   AC_TRY(E.run(a, k->ncap, L, false, p->iters_warm, p, 1, 0, k->labels));
   // finish_keys repeats the final assignment; harmless and keeps one code path
   return finish_keys(P, K, V, k, stats, ws, st, k->ncap);
+}
+
+// Interaction-aware keys: a fixed count m = min(m0, L) of k-means clusters,
+// Euclidean k-means++ seeding, Lloyd iterations and the final assignment
+// under the metric M, then the order and statistics as for the other keys.
+ac_status do_cluster_k_metric(const Plan &P, const ac_params *p, const uint16_t *K, const uint16_t *V, const float *M,
+                              ac_clusters *k, ac_kstats *stats, void *ws, hipStream_t st) {
+  const int BH = P.BH, L = P.L, D = P.D;
+  const int m = std::min(p->m0, L);
+  Engine E{P, P.sk, ws, st};
+  launch_fill_i32(E.n(), BH, L, st);
+  launch_fill_i32(E.m(), BH, m, st);
+  launch_fill_i32(E.coff(), BH, 0, st);
+  launch_fill_i32(k->ncl, BH, m, st);
+  launch_fill_u8(stats->fallback, BH, 0, st);
+  launch_fill_i32(stats->stages, BH, 1, st);
+  launch_fill_i32((int *)stats->tau, BH, 0, st);  // +0.0f: no distance threshold
+  AC_CHECK_LAUNCH();
+  KmArgs a{K, (int64_t)L * D, nullptr, 0, E.n(), E.m(), E.coff(), k->cent, (int64_t)k->ncap * D};
+  AC_TRY(E.run(a, m, L, true, p->iters, p, 1, 0, k->labels, M));
+  SortArgs s = E.sort_args(k->labels, k->perm, k->seg, k->ncap, m);
+  launch_sort(s, BH, L, st);
+  KStatsArgs ks{K, V, k->perm, k->seg, k->ncl, k->cent, stats->kmax, stats->kmin, stats->kmean, stats->vmean,
+                at<double>(ws, P.msepart), stats->mse, L, k->ncap};
+  launch_kstats(D, ks, BH, st);
+  AC_CHECK_LAUNCH();
+  return AC_OK;
 }
 
 ac_status do_score_select(const Plan &P, const ac_params *p, const ac_clusters *q, const ac_clusters *k,
@@ -719,6 +754,38 @@ AC_API ac_status ac_score_tokens(const ac_shape *s, const ac_params *p, const ui
   launch_token_quest(P.D, a, engine, P.BH, (hipStream_t)stream);
   AC_CHECK_LAUNCH();
   return AC_OK;
+}
+
+AC_API ac_status ac_interaction_matrix(const ac_shape *s, const ac_params *p, const uint16_t *Q, const ac_clusters *q,
+                                       float *M, void *ws, size_t ws_bytes, ac_stream_t stream) {
+  AC_TRY(check_shape(s));
+  AC_TRY(check_params(s, p));
+  if (!Q || !M) return fail(AC_E_ARG, "Q or M is NULL");
+  Plan P = make_plan(s, p);
+  AC_TRY(check_clusters(q, "query", P.nq, false));
+  if (q->ncap != P.nq) return fail(AC_E_ARG, "query clusters ncap must be min(nq, L) = %d", P.nq);
+  AC_TRY(check_ws(P, ws, ws_bytes));
+  AC_TRY(check_device());
+  hipStream_t st = (hipStream_t)stream;
+  launch_interaction_matrix(P.D, Q, q->perm, q->seg, q->ncl, P.L, P.nq, P.nq, at<double>(ws, P.qsum),
+                            at<int>(ws, P.qcnt), M, P.BH, st);
+  AC_CHECK_LAUNCH();
+  return AC_OK;
+}
+
+AC_API ac_status ac_cluster_k_metric(const ac_shape *s, const ac_params *p, const uint16_t *K, const uint16_t *V,
+                                     const float *M, ac_clusters *k_out, ac_kstats *stats, void *ws, size_t ws_bytes,
+                                     ac_stream_t stream) {
+  AC_TRY(check_shape(s));
+  AC_TRY(check_params(s, p));
+  if (!K || !V || !M) return fail(AC_E_ARG, "K, V or M is NULL");
+  Plan P = make_plan(s, p);
+  AC_TRY(check_clusters(k_out, "key", P.ncapk, false));
+  if (k_out->ncap != P.ncapk) return fail(AC_E_ARG, "key clusters ncap must be %d", P.ncapk);
+  AC_TRY(check_kstats(stats));
+  AC_TRY(check_ws(P, ws, ws_bytes));
+  AC_TRY(check_device());
+  return do_cluster_k_metric(P, p, K, V, M, k_out, stats, ws, (hipStream_t)stream);
 }
 
 namespace ac {

@@ -7,7 +7,7 @@
 namespace ac {
 
 constexpr int KPP_SMAX = 16384;  // most points a k-means++ subsample may hold
-constexpr int KPP_GRAM_MAX = 2048;  // subsamples up to this size seed from a distance matrix
+constexpr int KPP_GRAM_MAX = 8192;  // subsamples up to this size seed from a distance matrix
 constexpr int SORT_TILE = 128;   // points per counting-sort tile (one wave)
 constexpr int SORT_GROUP = 32;   // tiles per group in the two-level scan over tiles
 constexpr int ATT_QT = 256;      // query rows per attention block
@@ -196,6 +196,12 @@ void launch_attn(int D, const AttnArgs &a, int BH, int max_blocks, hipStream_t s
 
 // merge.hip
 void launch_tail_merge(const TailArgs &t, int BH, hipStream_t st);
+
+// metric.hip
+void launch_interaction_matrix(int D, const uint16_t *Q, const int *perm, const int *seg, const int *ncl, int L,
+                               int nq, int nqcap, double *qsum, int *qcnt, float *M, int BH, hipStream_t st);
+void launch_cent_prep_metric(int D, const KmArgs &a, const CentOps &op, const float *M, int BH, int mmax,
+                             hipStream_t st);
 
 // quest.hip (engine 0: MFMA, 1: vector ALU)
 void launch_token_quest(int D, const TokQuestArgs &a, int engine, int BH, hipStream_t st);

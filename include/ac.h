@@ -16,6 +16,8 @@
  *   ac_score_tokens  Quest bound of every query token against every key cluster (Algorithm 2's literal shape),
  *                    on MFMA (TensorQuest) or on the vector ALUs (eq. (1) as written)
  *   ac_tail_merge    iCATS tail merging of the query clusters before the attention
+ *   ac_interaction_matrix, ac_cluster_k_metric
+ *                    iCATS interaction-aware key clustering under M_Q from the query clusters
  *   ac_layer         the whole layer, cold (first denoising step) or warm (later steps reuse the cluster
  *                    counts and centres: AdaCluster §3.2.2 "Efficient initialization"), or dense
  *   ac_topp_schedule, ac_kmax_calibrate, ac_step_params
@@ -258,6 +260,27 @@ ac_status ac_tail_merge(const ac_shape *s, const ac_params *p, int32_t block, co
  * pass ld >= the largest ncl_k to score them all.  Needs no workspace. */
 ac_status ac_score_tokens(const ac_shape *s, const ac_params *p, const uint16_t *Q, const ac_clusters *k,
                           const ac_kstats *stats, int32_t engine, float *S, int32_t ld, ac_stream_t stream);
+
+/* Interaction-aware key clustering ("iCATS: Fast Video Generation via Interaction-Aware Sparse
+ * Attention and Timestep-Adaptive Sparsity", method section, interaction-aware clustering).  The error
+ * of the query-key products when a key is replaced by its centre is (k - c) Q^T Q (k - c)^T; the page
+ * approximates Q^T Q by M_Q = sum_r |A_r| mu_r^T mu_r over the query clusters A_r.
+ *
+ * ac_interaction_matrix: M[bh] = M_Q of head bh, with mu_r the mean of the raw member queries of query
+ * cluster r of q (as filled by ac_cluster_q: perm, seg and ncl are read).  Q: [B,H,L,d] bf16;
+ * M: [BH, d, d] fp32 row-major, accumulated in fp64.
+ *
+ * ac_cluster_k_metric: k-means of each head's keys into m = min(p->m0, L) clusters whose assignment
+ * minimises (k - c) M[bh] (k - c)^T: k-means++ seeding as ac_cluster_k's first stage (Euclidean, the
+ * same random stream), p->iters Lloyd iterations (member means, which minimise the form for a positive
+ * semi-definite M) and a final assignment; then perm, seg and the statistics as ac_cluster_k.  No
+ * stages and no fallback: ncl = m, fallback = 0, tau = 0, stages = 1.  k_out->ncap must be ac_sizes'
+ * ncap_k.  The result feeds ac_score_select and ac_sparse_attn like ac_cluster_k's. */
+ac_status ac_interaction_matrix(const ac_shape *s, const ac_params *p, const uint16_t *Q, const ac_clusters *q,
+                                float *M, void *ws, size_t ws_bytes, ac_stream_t stream);
+ac_status ac_cluster_k_metric(const ac_shape *s, const ac_params *p, const uint16_t *K, const uint16_t *V,
+                              const float *M, ac_clusters *k_out, ac_kstats *stats, void *ws, size_t ws_bytes,
+                              ac_stream_t stream);
 
 /* The whole layer (AdaCluster Algorithm 3 with the optional compensation): ac_cluster_q,
  * ac_cluster_k, ac_score_select, ac_tail_merge when p->tail_block > 0, and ac_sparse_attn on

@@ -118,6 +118,15 @@ def test_entry_points_reject_bad_arguments_before_any_device_work():
                            (ac.AC_QUEST_MFMA, 64, 1 << 20, k_bad)]:
         assert lib.ac_score_tokens(ctypes.byref(shape), ctypes.byref(p), 1 << 20, ctypes.byref(kk), ctypes.byref(st),
                                    eng, S, ld, None) == ac.AC_E_ARG, (eng, ld, S)
+    # interaction-aware clustering: NULL M, wrong capacities
+    assert lib.ac_interaction_matrix(ctypes.byref(shape), ctypes.byref(p), 1 << 20, ctypes.byref(q), None, ws, wsb,
+                                     None) == ac.AC_E_ARG
+    assert lib.ac_interaction_matrix(ctypes.byref(shape), ctypes.byref(p), 1 << 20, ctypes.byref(q_bad), 1 << 20, ws,
+                                     wsb, None) == ac.AC_E_ARG
+    assert lib.ac_cluster_k_metric(ctypes.byref(shape), ctypes.byref(p), 1 << 20, 1 << 20, None, ctypes.byref(k),
+                                   ctypes.byref(st), ws, wsb, None) == ac.AC_E_ARG
+    assert lib.ac_cluster_k_metric(ctypes.byref(shape), ctypes.byref(p), 1 << 20, 1 << 20, 1 << 20,
+                                   ctypes.byref(k_bad), ctypes.byref(st), ws, wsb, None) == ac.AC_E_ARG
     # NULL state
     assert lib.ac_layer(ctypes.byref(shape), ctypes.byref(p), 1 << 20, 1 << 20, 1 << 20, None, 1 << 20, None, ws, wsb,
                         None) == ac.AC_E_ARG

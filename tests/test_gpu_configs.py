@@ -8,7 +8,7 @@ import pytest
 import csa_inputs as gen
 from oracle import numerics as nm
 from abi_helpers import (Run, workload_oracle_params, check_clusters_sampled, check_scores_selection,
-                         check_attention_sampled, np_)
+                         check_attention_sampled, np_, bf16_dev_to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +86,58 @@ def test_wan_token_quest(wan_run):
     rows = gen.row_sample(w.L, 256, ROW_SEED["wan"])
     worst = check_token_quest(r, Q, K, V, ld, rows=rows)
     print(f"wan token quest ld={ld}: max error / bound {worst}")
+
+
+def test_wan_interaction_aware_keys(wan_run):
+    """iCATS interaction-aware key clustering at full size: M_Q of all 40
+    heads against the oracle (raw member means of the GPU's query clusters),
+    the metric labels of a sample of keys against the metric argmin for the
+    GPU's centres (up to near ties), the statistics of every cluster, and
+    the layer's selection and attention on these clusters."""
+    import torch
+    import clustered_sparse_attention_amd as ac
+    from abi_helpers import abi_params
+    from oracle import interaction as oia
+    from oracle import stats as ost
+    from test_gpu_tiny import _metric_label_check
+    w, Q, K, V, r = wan_run
+    p = workload_oracle_params("wan")
+    r.p, r.cp = p, abi_params(p)
+    k = ac.Clusters(r.BH, r.L, r.ncap_k, r.d, torch.device("cuda"), rho=False)
+    st = ac.KStats(r.BH, r.ncap_k, r.d, torch.device("cuda"))
+    M = torch.empty((r.BH, r.d, r.d), dtype=torch.float32, device="cuda")
+    ac.ac_interaction_matrix(r.shape, r.cp, r.Q, r.q, M, r.ws)
+    ac.ac_cluster_k_metric(r.shape, r.cp, r.K, r.V, M, k, st, r.ws)
+    torch.cuda.synchronize()
+    Mg = np_(M).astype(np.float64)
+    qlab, lab, cent = np_(r.q.labels), np_(k.labels), np_(k.cent)
+    kmax, kmin = bf16_dev_to_f64(st.kmax), bf16_dev_to_f64(st.kmin)
+    m = min(p.m0, w.L)
+    rows = gen.row_sample(w.L, 512, ROW_SEED["wan"])
+    Qf, Kf, Vf = (x.reshape(r.BH, w.L, w.d) for x in (Q, K, V))
+    flips = 0
+    for h in range(r.BH):
+        Mo = oia.interaction_matrix(Qf[h], qlab[h], r.nq)
+        assert np.max(np.abs(Mg[h] - Mo)) <= 1e-6 * np.max(np.abs(Mo)), h
+        C = cent[h, :m].astype(np.float64)
+        bad, fl = _metric_label_check(nm.bf16_to_f64(Kf[h][rows]), C, Mg[h], lab[h][rows])
+        assert bad == 0, (h, bad)
+        flips += fl
+        sto = ost.key_stats(Kf[h], Vf[h], lab[h], C)
+        assert np.array_equal(kmax[h, :m], sto["kmax"]) and np.array_equal(kmin[h, :m], sto["kmin"]), h
+    assert flips <= 0.001 * r.BH * rows.size
+    # selection and attention on the metric key clusters
+    saved_k, saved_st = r.k, r.st
+    r.k, r.st = k, st
+    try:
+        r.score_select()
+        r.attn()
+        torch.cuda.synchronize()
+        ties = check_scores_selection(r, p)
+        worst = check_attention_sampled(r, Q, K, V, p, ROW_SEED["wan"])
+    finally:
+        r.k, r.st = saved_k, saved_st
+    print(f"wan interaction-aware keys (m = {m}): label flips {flips}, selection ties {ties}, worst {worst}")
 
 
 @pytest.mark.parametrize("name", ["cogvideox", "hunyuan", "long"])

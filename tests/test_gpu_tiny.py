@@ -44,11 +44,12 @@ def _bits(x, bh):
 
 # ---------------------------------------------------------------- queries
 
-@pytest.mark.parametrize("init_sample", [0, 8])
-def test_query_seeding_bit_exact(tiny, init_sample):
-    """k-means++ picks equal the oracle's: the streamed path (every point,
-    s = 4096) and the distance-matrix path (s = 8 * 16 = 128)."""
-    Q, K, V = tiny
+@pytest.mark.parametrize("init_sample,L", [(0, None), (8, None), (0, 10000)])
+def test_query_seeding_bit_exact(tiny, init_sample, L):
+    """k-means++ picks equal the oracle's: the distance-matrix path (every
+    point, s = 4096; s = 8 * 16 = 128) and the streamed path for subsamples
+    above the matrix limit (every point of L = 10000)."""
+    Q, K, V = tiny if L is None else gen.generate(gen.get_workload("tiny", H=1, L=L))
     p = P(iters=0, init_sample=init_sample)
     r = Run(Q, K, V, p)
     r.cluster_q()
@@ -437,3 +438,63 @@ def test_multistep_driver_against_oracle():
                         assert hs["ncl_k"][bh] == ref["k"]["nk"] and hs["fallback"][bh] == ref["k"]["fallback"]
                 mx, rl2 = attn_error(Og[bh], Oo)
                 assert mx <= ATTN_MAX_ABS and rl2 <= ATTN_REL_L2, (step, l, bh, mx, rl2)
+
+
+# ---------------------------------------------------------------- interaction-aware key clustering (iCATS)
+
+def _metric_label_check(X, C, M, lab_gpu):
+    """GPU labels against the metric argmin for the GPU's centres; a mismatch
+    is allowed only where the two best distances are within the rounding of
+    the kernel's operands (x . M c with M c split into two bf16 parts)."""
+    from oracle import interaction as oia
+    Dm = oia.metric_sq_dist(X, C, M)
+    lab_o = np.argmin(Dm, axis=1)
+    srt = np.sort(Dm, axis=1)
+    MC = C @ M  # rows M c (M is symmetric)
+    scale = np.linalg.norm(X, axis=1) * np.max(np.linalg.norm(MC, axis=1)) + np.abs(srt[:, 0])
+    tie = (srt[:, 1] - srt[:, 0]) < 1e-4 * scale
+    bad = (lab_o != lab_gpu) & ~tie
+    return int(bad.sum()), int(((lab_o != lab_gpu) & tie).sum())
+
+
+@pytest.mark.parametrize("iters", [0, 1, 10])
+def test_interaction_aware_key_clustering(tiny, iters):
+    """iCATS interaction-aware clustering: M_Q from the GPU's query clusters
+    against the oracle's (raw member means), then the metric k-means of the
+    keys against the oracle's from the same k-means++ seeds: centres, labels
+    (up to near ties), order and statistics."""
+    import torch
+    import clustered_sparse_attention_amd as ac
+    from oracle import interaction as oia
+    Q, K, V = tiny
+    p = P(iters=iters, m0=24, nmax=64)
+    r = Run(Q, K, V, p)
+    r.cluster_q()
+    M = torch.empty((r.BH, r.d, r.d), dtype=torch.float32, device="cuda")
+    ac.ac_interaction_matrix(r.shape, r.cp, r.Q, r.q, M, r.ws)
+    ac.ac_cluster_k_metric(r.shape, r.cp, r.K, r.V, M, r.k, r.st, r.ws)
+    torch.cuda.synchronize()
+    Mg = np_(M).astype(np.float64)
+    qlab = np_(r.q.labels)
+    cent, lab, perm, seg, ncl = (np_(t) for t in (r.k.cent, r.k.labels, r.k.perm, r.k.seg, r.k.ncl))
+    kmax, kmin = bf16_dev_to_f64(r.st.kmax), bf16_dev_to_f64(r.st.kmin)
+    assert np.all(ncl == 24) and np.all(np_(r.st.fallback) == 0) and np.all(np_(r.st.stages) == 1)
+    for bh in range(r.BH):
+        Mo = oia.interaction_matrix(_bits(Q, bh), qlab[bh], r.nq)
+        assert np.max(np.abs(Mg[bh] - Mo)) <= 1e-6 * np.max(np.abs(Mo)), bh
+        ref = oia.cluster_keys_metric(_bits(K, bh), p, bh, Mg[bh])
+        C = cent[bh, :24].astype(np.float64)
+        assert np.max(np.abs(C - ref["cent"])) <= 1e-5 * max(1.0, np.max(np.abs(ref["cent"]))), bh
+        X = nm.bf16_to_f64(_bits(K, bh))
+        bad, flips = _metric_label_check(X, C, Mg[bh], lab[bh])
+        assert bad == 0 and flips <= 0.001 * r.L, (bh, bad, flips)
+        perm_o, seg_o = ost.counting_sort(lab[bh], 24)
+        assert np.array_equal(perm[bh], perm_o) and np.array_equal(seg[bh, :25], seg_o)
+        st = ost.key_stats(_bits(K, bh), _bits(V, bh), lab[bh], C)
+        assert np.array_equal(kmax[bh, :24], st["kmax"]) and np.array_equal(kmin[bh, :24], st["kmin"])
+    # the metric clusters drive the rest of the layer like Algorithm 1's
+    r.score_select()
+    r.attn()
+    torch.cuda.synchronize()
+    from abi_helpers import check_attention_sampled
+    check_attention_sampled(r, Q, K, V, p, 9001, nrows=512)
