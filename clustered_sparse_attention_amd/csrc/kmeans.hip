@@ -706,12 +706,16 @@ __global__ __launch_bounds__(256) void k_compact_gather(const int *__restrict__ 
 // and the cluster's share of sum ||k - c(k)||^2 (fp64).
 template <int D>
 __global__ __launch_bounds__(256) void k_kstats(KStatsArgs s) {
+  // one block per cluster: 16 row groups of 16 lanes (PL dims each), four
+  // member rows per group in flight; the groups of a wave combine with
+  // shuffles, the four waves through a small LDS table
   constexpr int PL = D / 16;  // dims per lane, 16 lanes per row
   typedef uint32_t pw_t __attribute__((ext_vector_type(PL / 2)));
   const int h = blockIdx.y, c = blockIdx.x;
   const int ncl = s.ncl[h];
   const int64_t cb = ((int64_t)h * s.ncap + c);
   const int grp = threadIdx.x >> 4, sub = threadIdx.x & 15;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (c >= ncl) {
     if (c < s.ncap) {
       for (int dd = threadIdx.x; dd < D; dd += 256) {
@@ -735,7 +739,6 @@ __global__ __launch_bounds__(256) void k_kstats(KStatsArgs s) {
     sk[k] = 0.0; sv[k] = 0.0; mx[k] = -__builtin_inff(); mn[k] = __builtin_inff();
     cc[k] = cent[sub * PL + k];
   }
-  // four member rows per lane in flight; rows are still added in member order
   for (int p0 = beg + grp; p0 < end; p0 += 64) {
     int64_t row[4];
 #pragma unroll
@@ -743,13 +746,9 @@ __global__ __launch_bounds__(256) void k_kstats(KStatsArgs s) {
     pw_t kw[4], vw[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if (row[j] >= 0) {
-        kw[j] = *(const pw_t *)(K + row[j] * D + sub * PL);
-        vw[j] = *(const pw_t *)(V + row[j] * D + sub * PL);
-      } else {
-        kw[j] = (pw_t){};
-        vw[j] = (pw_t){};
-      }
+      const int64_t rr = row[j] >= 0 ? row[j] : row[0];
+      kw[j] = *(const pw_t *)(K + rr * D + sub * PL);
+      vw[j] = *(const pw_t *)(V + rr * D + sub * PL);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -768,17 +767,32 @@ __global__ __launch_bounds__(256) void k_kstats(KStatsArgs s) {
       }
     }
   }
-  __shared__ double shk[16][D], shv[16][D];
-  __shared__ float shx[16][D], shn[16][D];
-  __shared__ double she[256];
+  // the four row groups of a wave (lanes sub, sub + 16, sub + 32, sub + 48)
 #pragma unroll
-  for (int k = 0; k < PL; ++k) {
-    shk[grp][sub * PL + k] = sk[k];
-    shv[grp][sub * PL + k] = sv[k];
-    shx[grp][sub * PL + k] = mx[k];
-    shn[grp][sub * PL + k] = mn[k];
+  for (int o = 16; o < 64; o <<= 1) {
+#pragma unroll
+    for (int k = 0; k < PL; ++k) {
+      sk[k] += __shfl_xor(sk[k], o, 64);
+      sv[k] += __shfl_xor(sv[k], o, 64);
+      mx[k] = fmaxf(mx[k], __shfl_xor(mx[k], o, 64));
+      mn[k] = fminf(mn[k], __shfl_xor(mn[k], o, 64));
+    }
   }
-  she[threadIdx.x] = se;
+  se = wave_sum(se);
+  // then the four waves
+  __shared__ double shk[4][D], shv[4][D];
+  __shared__ float shx[4][D], shn[4][D];
+  __shared__ double she[4];
+  if (lane < 16) {
+#pragma unroll
+    for (int k = 0; k < PL; ++k) {
+      shk[wave][sub * PL + k] = sk[k];
+      shv[wave][sub * PL + k] = sv[k];
+      shx[wave][sub * PL + k] = mx[k];
+      shn[wave][sub * PL + k] = mn[k];
+    }
+  }
+  if (lane == 0) she[wave] = se;
   __syncthreads();
   const int cnt = end - beg;
   if (threadIdx.x < D) {
@@ -787,11 +801,11 @@ __global__ __launch_bounds__(256) void k_kstats(KStatsArgs s) {
       double a = 0.0, b = 0.0;
       float x = -__builtin_inff(), y = __builtin_inff();
 #pragma unroll
-      for (int gg = 0; gg < 16; ++gg) {
-        a += shk[gg][dd];
-        b += shv[gg][dd];
-        x = fmaxf(x, shx[gg][dd]);
-        y = fminf(y, shn[gg][dd]);
+      for (int w = 0; w < 4; ++w) {
+        a += shk[w][dd];
+        b += shv[w][dd];
+        x = fmaxf(x, shx[w][dd]);
+        y = fminf(y, shn[w][dd]);
       }
       s.kmean[cb * D + dd] = (float)(a / cnt);
       s.vmean[cb * D + dd] = (float)(b / cnt);
@@ -802,11 +816,7 @@ __global__ __launch_bounds__(256) void k_kstats(KStatsArgs s) {
       s.kmax[cb * D + dd] = 0; s.kmin[cb * D + dd] = 0;
     }
   }
-  if (threadIdx.x == 0) {
-    double t = 0.0;
-    for (int k = 0; k < 256; ++k) t += she[k];
-    s.msepart[cb] = t;
-  }
+  if (threadIdx.x == 0) s.msepart[cb] = she[0] + she[1] + she[2] + she[3];
 }
 
 __global__ __launch_bounds__(256) void k_mse_reduce(const double *__restrict__ msepart, int ncap,
