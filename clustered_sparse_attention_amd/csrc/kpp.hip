@@ -270,6 +270,15 @@ __global__ __launch_bounds__(256) void k_kpp_gram(KmArgs a, int init_sample, con
   }
 }
 
+// The m sequential rounds from the subsample's distance matrix G, one block
+// per head.  Thread t holds D^2 of the subsample points [t cs, t cs + cs) in
+// registers (cs <= KPP_SEQ_CS), so the draw walks the points in index order:
+// wave scans of the per-thread sums, the wave totals in order through LDS,
+// and the one lane whose range holds u * total finds the point.  Two barriers
+// a round; the row of G of the new centre is then read straight into the
+// registers (each thread its cs contiguous entries).
+constexpr int KPP_SEQ_CS = KPP_GRAM_MAX / KPP_THREADS;
+
 template <int D>
 __global__ __launch_bounds__(KPP_THREADS) void k_kpp_seq(KmArgs a, const double *__restrict__ G, int smax,
                                                         int init_sample, uint64_t seed, int role, int stage) {
@@ -282,48 +291,80 @@ __global__ __launch_bounds__(KPP_THREADS) void k_kpp_seq(KmArgs a, const double 
   const int *idx = a.idx ? a.idx + (int64_t)h * a.idx_hs : nullptr;
   float *cent = a.cent + (int64_t)h * a.cent_hs + (int64_t)a.coff[h] * D;
   const uint64_t sid = stream_id((uint64_t)h, role, stage);
-  const int tid = threadIdx.x;
-  __shared__ double D2[KPP_GRAM_MAX];
-  __shared__ double sh_wt[KPP_WAVES], sh_off[KPP_WAVES + 1];
-  __shared__ int sh_pick;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ double sh_wt[KPP_WAVES];
+  __shared__ int sh_pick[2];
   const int cs = (s + KPP_THREADS - 1) / KPP_THREADS;
-  const int cb = min(s, tid * cs), ce = min(s, cb + cs);
-  for (int t = 0; t < m; ++t) {
-    const double u = uniform01(seed, sid, (uint64_t)t);
-    if (t == 0) {
-      if (tid == 0) sh_pick = min(s - 1, (int)(u * (double)s));
-    } else {
-      double loc = 0.0;
-      for (int j = cb; j < ce; ++j) loc += D2[j];
-      double excl, total;
-      const double incl = block_scan(loc, &excl, &total, sh_wt, sh_off);
-      if (total > 0.0) {
-        const double target = u * total;
-        if (tid == 0) sh_pick = s - 1;
-        __syncthreads();
-        if (ce > cb && excl <= target && target < incl) {
-          double run = excl;
-          int pj = ce - 1;
-          for (int j = cb; j < ce; ++j) {
-            run += D2[j];
-            if (run > target) { pj = j; break; }
-          }
-          sh_pick = pj;
-        }
-      } else if (tid == 0) {
-        sh_pick = min(s - 1, (int)(u * (double)s));
-      }
-    }
-    __syncthreads();
-    const int pj = sh_pick;
+  const int cb = min(s, tid * cs), ne = min(s, cb + cs) - cb;  // this thread's points
+  double d2[KPP_SEQ_CS];
+  auto take_row = [&](int pj, bool first) {
+    const double *gr = Gh + (int64_t)pj * smax + cb;
+#pragma unroll
+    for (int e = 0; e < KPP_SEQ_CS; ++e)
+      if (e < ne) d2[e] = first ? gr[e] : fmin(d2[e], gr[e]);
+  };
+  auto put_centre = [&](int t, int pj) {
     if (tid < D) {
       const int li = (int)(((int64_t)pj * n) / s);
       const int64_t row = idx ? (int64_t)idx[li] : (int64_t)li;
       cent[(int64_t)t * D + tid] = bf2f(X[row * D + tid]);
     }
-    const double *gr = Gh + (int64_t)pj * smax;
-    for (int j = tid; j < s; j += KPP_THREADS) D2[j] = t == 0 ? gr[j] : fmin(D2[j], gr[j]);
+  };
+#pragma unroll
+  for (int e = 0; e < KPP_SEQ_CS; ++e) d2[e] = 0.0;
+  {
+    const double u = uniform01(seed, sid, 0);
+    const int pj = min(s - 1, (int)(u * (double)s));
+    put_centre(0, pj);
+    take_row(pj, true);
+  }
+  for (int t = 1; t < m; ++t) {
+    const double u = uniform01(seed, sid, (uint64_t)t);
+    double loc = 0.0;
+#pragma unroll
+    for (int e = 0; e < KPP_SEQ_CS; ++e)
+      if (e < ne) loc += d2[e];
+    double inc = loc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    const double prev = __shfl_up(inc, 1, 64);  // the previous lane's inclusive sum, bit for bit
+    if (lane == 63) sh_wt[wave] = inc;
+    if (tid == 0) sh_pick[t & 1] = -1;
     __syncthreads();
+    double off = 0.0, total = 0.0;
+#pragma unroll
+    for (int w = 0; w < KPP_WAVES; ++w) {
+      const double v = sh_wt[w];
+      if (w < wave) off += v;
+      total += v;
+    }
+    if (total > 0.0) {
+      const double target = u * total;
+      // the ranges [excl, incl) of consecutive lanes and waves tile [0, total)
+      // exactly: both ends come from the same sums in the same order
+      const double incl = off + inc, excl = lane == 0 ? off : off + prev;
+      if (ne > 0 && excl <= target && target < incl) {
+        double run = excl;
+        int pj = cb + ne - 1;
+#pragma unroll
+        for (int e = 0; e < KPP_SEQ_CS; ++e) {
+          if (e < ne) {
+            run += d2[e];
+            if (run > target) { pj = cb + e; break; }
+          }
+        }
+        sh_pick[t & 1] = pj;
+      }
+    }
+    __syncthreads();
+    int pj = sh_pick[t & 1];
+    if (total <= 0.0) pj = min(s - 1, (int)(u * (double)s));
+    else if (pj < 0) pj = s - 1;  // u * total at the very top (rounding)
+    put_centre(t, pj);
+    take_row(pj, false);
   }
 }
 
