@@ -309,13 +309,25 @@ __global__ __launch_bounds__(64 * ATT_QT / (32 * QG), 1) void k_attn(AttnArgs a)
   const int vhalf = 4 * (vi & 1);
 
   // S^T = K Q^T for one tile: two 32-key blocks per query group; each K
-  // fragment feeds the QG groups
-  auto qk = [&](const uint16_t *Ks, f32x16_t (*acc)[2]) {
+  // fragment feeds the QG groups.  The accumulators start at the keys' logit
+  // biases divided by the base-2 score scale (0 for selected keys, -inf for
+  // masked ones, ln n_c / scale for pseudo-keys), so every tile takes the
+  // same path and the scores need no separate add.
+  auto qk = [&](const uint16_t *Ks, const float *bz, f32x16_t (*acc)[2]) {
 #pragma unroll
-    for (int gq = 0; gq < QG; ++gq) {
-      acc[gq][0] = (f32x16_t){};
-      acc[gq][1] = (f32x16_t){};
-    }
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const f32x4_t b0 = *(const f32x4_t *)&bz[32 * kb + 16 * half + 8 * g];
+        const f32x4_t b1 = *(const f32x4_t *)&bz[32 * kb + 16 * half + 8 * g + 4];
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[gq][kb][half * 8 + i] = b0[i];
+            acc[gq][kb][half * 8 + 4 + i] = b1[i];
+          }
+      }
 #pragma unroll
     for (int ks = 0; ks < KSQ; ++ks)
 #pragma unroll
@@ -325,36 +337,28 @@ __global__ __launch_bounds__(64 * ATT_QT / (32 * QG), 1) void k_attn(AttnArgs a)
         for (int gq = 0; gq < QG; ++gq)
           acc[gq][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[gq][ks], acc[gq][kb], 0, 0, 0);
       }
+    // order: the bias reads and the K reads of two k-steps, then each
+    // k-step's two products followed by the K reads of the step two ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+    for (int ks = 0; ks < KSQ - 2; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * QG, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * QG, 0);
   };
-  // row max of a tile in base-2 units, after adding the tile's scaled biases
-  // (0 for selected keys, -inf for masked ones, ln n_c / scale for pseudo-keys)
-  auto bias_max = [&](f32x16_t *acc, const float *bz) -> float {
-    float mt = -__builtin_inff();
+  // row max of a tile in base-2 units: a tree of three-way maxima, then the
+  // two key halves of the column exchanged between lane halves
+  auto tile_max = [&](const f32x16_t *acc) -> float {
+    float part[2] = {-__builtin_inff(), -__builtin_inff()};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const f32x4_t b0 = *(const f32x4_t *)&bz[32 * kb + 16 * half + 8 * g];
-        const f32x4_t b1 = *(const f32x4_t *)&bz[32 * kb + 16 * half + 8 * g + 4];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float sv = acc[kb][half * 8 + i] + (i < 4 ? b0[i] : b1[i - 4]);
-          acc[kb][half * 8 + i] = sv;
-          mt = fmaxf(mt, sv);
-        }
-      }
-    mt *= sl2;
-    return fmaxf(mt, __shfl_xor(mt, 32, 64));
-  };
-  // the same for a tile of selected keys only (no biases)
-  auto plain_max = [&](const f32x16_t *acc) -> float {
-    float mt = -__builtin_inff();
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, acc[kb][i]);
-    mt *= sl2;
-    return fmaxf(mt, __shfl_xor(mt, 32, 64));
+    for (int i = 0; i < 16; ++i) {
+      part[0] = fmaxf(part[0], acc[0][i]);
+      part[1] = fmaxf(part[1], acc[1][i]);
+    }
+    const float mt = fmaxf(part[0], part[1]) * sl2;
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
   };
   // the V^T operands of k-step s of a tile, one per 32-dim block
   auto v_frags = [&](const uint16_t *Vs, int s, bf16x8_t *vf) {
@@ -438,14 +442,13 @@ __global__ __launch_bounds__(64 * ATT_QT / (32 * QG), 1) void k_attn(AttnArgs a)
             for (int jj = 0; jj < 16; ++jj) acc_o[gq][db][jj] *= alpha[gq];
       }
       f32x16_t sc[QG][2];
-      qk(Kb + b0 * TILE, sc);
+      qk(Kb + b0 * TILE, sbw + (tt & 3) * ATT_KT, sc);
       // lazy rescale: the reference max m_i may trail the running max by up
-      // to 2^8, so p <= 256; it moves only when a row outgrows it.  Tiles
-      // before the last selected one hold selected keys only: no biases.
+      // to 2^8, so p <= 256; it moves only when a row outgrows it.
       float m_new[QG], m_use[QG];
 #pragma unroll
       for (int gq = 0; gq < QG; ++gq) {
-        const float mt = tt < nt0 - 1 ? plain_max(sc[gq]) : bias_max(sc[gq], sbw + (tt & 3) * ATT_KT);
+        const float mt = tile_max(sc[gq]);
         m_new[gq] = mt > m_i[gq] + 8.f ? mt : m_i[gq];
         m_use[gq] = m_new[gq] == -__builtin_inff() ? 0.f : m_new[gq];
       }
