@@ -72,10 +72,12 @@ __global__ __launch_bounds__(256) void k_cent_prep(KmArgs a, CentOps op) {
 }
 
 // ---------------------------------------------------------------------------
-// Nearest centre of every point: argmin_c ||c||^2 - 2 x.c on bf16 MFMA
-// (16x16x32, fp32 accumulation; x.c = x.hi + x.lo).  A block holds 256
-// points (4 waves x 64); centre operands stream through LDS in chunks of 64.
-// Ties go to the lower centre index.
+// Nearest centre of every point: argmin_c ||c||^2 - 2 x.c, taken as
+// argmax_c x.c - ||c||^2 / 2 on bf16 MFMA (16x16x32, fp32 accumulation that
+// starts at -||c||^2 / 2; x.c = x.hi + x.lo), so the products need no
+// separate epilogue arithmetic.  A block holds 256 points (4 waves x 64);
+// centre operands stream through LDS in chunks of 64.  Ties go to the lower
+// centre index; padding centres carry -inf and never win.
 template <int D>
 __global__ __launch_bounds__(256) void k_assign(KmArgs a, CentOps op, int *__restrict__ labels,
                                                 int64_t lab_hs) {
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(256) void k_assign(KmArgs a, CentOps op, int *__res
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) { best[rt][j] = __builtin_inff(); bidx[rt][j] = 0x7fffffff; }
+    for (int j = 0; j < 4; ++j) { best[rt][j] = -__builtin_inff(); bidx[rt][j] = 0x7fffffff; }
 
   const uint16_t *ghi = op.hi + (int64_t)h * op.cap * D;
   const uint16_t *glo = op.lo + (int64_t)h * op.cap * D;
@@ -138,14 +140,15 @@ __global__ __launch_bounds__(256) void k_assign(KmArgs a, CentOps op, int *__res
       *(u32x4_t *)&s_hi[r * LDSROW + cc] = vh;
       *(u32x4_t *)&s_lo[r * LDSROW + cc] = vl;
     }
-    if (threadIdx.x < CH) s_norm[threadIdx.x] = threadIdx.x < cn ? gnorm[c0 + threadIdx.x] : 0.f;
+    if (threadIdx.x < CH) s_norm[threadIdx.x] = threadIdx.x < cn ? -0.5f * gnorm[c0 + threadIdx.x] : -__builtin_inff();
     __syncthreads();
 #pragma unroll 1
     for (int ct = 0; ct < CH / 16; ++ct) {
       if (ct * 16 >= cn) break;
+      // lane holds centre column l16: its accumulators start at -||c||^2 / 2
+      const float nh = s_norm[ct * 16 + l16];
+      const f32x4_t n4 = {nh, nh, nh, nh};
       f32x4_t acc[4];
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) acc[rt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
       const int crow = ct * 16 + l16;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -153,21 +156,17 @@ __global__ __launch_bounds__(256) void k_assign(KmArgs a, CentOps op, int *__res
         bf16x8_t bl = *(const bf16x8_t *)&s_lo[crow * LDSROW + ks * 32 + g * 8];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt][ks], bh, acc[rt], 0, 0, 0);
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt][ks], bh, ks == 0 ? n4 : acc[rt], 0, 0, 0);
           acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt][ks], bl, acc[rt], 0, 0, 0);
         }
       }
       // D layout: lane holds column (centre) l16, rows 4*g + j.
       const int cidx = c0 + ct * 16 + l16;
-      const bool cvalid = (ct * 16 + l16) < cn;
-      const float cn2 = s_norm[ct * 16 + l16];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float dv = cvalid ? fmaf(-2.f, acc[rt][j], cn2) : __builtin_inff();
-          if (dv < best[rt][j]) { best[rt][j] = dv; bidx[rt][j] = cidx; }
-        }
+        for (int j = 0; j < 4; ++j)
+          if (acc[rt][j] > best[rt][j]) { best[rt][j] = acc[rt][j]; bidx[rt][j] = cidx; }
     }
   }
   // reduce over the 16 lanes that share g (same rows, different centres)
@@ -181,7 +180,7 @@ __global__ __launch_bounds__(256) void k_assign(KmArgs a, CentOps op, int *__res
       for (int o = 1; o < 16; o <<= 1) {
         float ov = __shfl_xor(bv, o, 64);
         int oi = __shfl_xor(bi, o, 64);
-        if (ov < bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
       }
       int i = wbase + rt * 16 + g * 4 + j;
       if (l16 == 0 && i < n) labels[(int64_t)h * lab_hs + i] = bi == 0x7fffffff ? 0 : bi;
@@ -235,7 +234,7 @@ __global__ __launch_bounds__(NT) void k_assign_res(KmArgs a, CentOps op, int *__
         *(u32x4_t *)&s_hi[r * LDSROW + cc] = vh;
         *(u32x4_t *)&s_lo[r * LDSROW + cc] = vl;
       }
-      for (int c = threadIdx.x; c < mp; c += NT) s_norm[c] = c < m ? gnorm[c] : 0.f;
+      for (int c = threadIdx.x; c < mp; c += NT) s_norm[c] = c < m ? -0.5f * gnorm[c] : -__builtin_inff();
       __syncthreads();
       const uint16_t *X = a.X + (int64_t)h * a.x_hs;
       const int *idx = a.idx ? a.idx + (int64_t)h * a.idx_hs : nullptr;
@@ -257,16 +256,17 @@ __global__ __launch_bounds__(NT) void k_assign_res(KmArgs a, CentOps op, int *__
         }
         // centres in the A slot, points in B: lane holds point l16 of each
         // row tile and centres 4g..4g+3 of the centre tile, so the running
-        // argmin is one value per row tile and lane.
+        // argmax of x.c - ||c||^2 / 2 is one value per row tile and lane; the
+        // accumulators start at the centres' -||c||^2 / 2 (-inf for padding).
         float best[4];
         int bidx[4];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) { best[rt] = __builtin_inff(); bidx[rt] = 0x7fffffff; }
+        for (int rt = 0; rt < 4; ++rt) { best[rt] = -__builtin_inff(); bidx[rt] = 0x7fffffff; }
 #pragma unroll 1
         for (int ct = 0; ct < mp / 16; ++ct) {
+          const int c0 = ct * 16 + 4 * g;
+          const f32x4_t nh = *(const f32x4_t *)&s_norm[c0];
           f32x4_t acc[4];
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) acc[rt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
           const int crow = ct * 16 + l16;
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
@@ -274,19 +274,15 @@ __global__ __launch_bounds__(NT) void k_assign_res(KmArgs a, CentOps op, int *__
             const bf16x8_t bl = *(const bf16x8_t *)&s_lo[crow * LDSROW + ks * 32 + g * 8];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-              acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh, af[rt][ks], acc[rt], 0, 0, 0);
+              acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh, af[rt][ks], ks == 0 ? nh : acc[rt], 0, 0, 0);
               acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl, af[rt][ks], acc[rt], 0, 0, 0);
             }
           }
-          const int c0 = ct * 16 + 4 * g;
-          const f32x4_t cn2 = *(const f32x4_t *)&s_norm[c0];
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float dv = (c0 + j < m) ? fmaf(-2.f, acc[rt][j], cn2[j]) : __builtin_inff();
-              if (dv < best[rt]) { best[rt] = dv; bidx[rt] = c0 + j; }
-            }
+            for (int j = 0; j < 4; ++j)
+              if (acc[rt][j] > best[rt]) { best[rt] = acc[rt][j]; bidx[rt] = c0 + j; }
         }
         // reduce over the four lane groups that hold the same point
 #pragma unroll
@@ -297,7 +293,7 @@ __global__ __launch_bounds__(NT) void k_assign_res(KmArgs a, CentOps op, int *__
           for (int o = 16; o < 64; o <<= 1) {
             const float ov = __shfl_xor(bv, o, 64);
             const int oi = __shfl_xor(bi, o, 64);
-            if (ov < bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+            if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
           }
           const int i = wbase + rt * 16 + l16;
           if (g == 0 && i < n) labels[(int64_t)h * lab_hs + i] = bi == 0x7fffffff ? 0 : bi;
