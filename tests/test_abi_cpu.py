@@ -51,7 +51,8 @@ def test_sizes_validation():
     ncap, ws = ac.ac_sizes(ac.Shape(1, 40, 75600, 128), p)
     assert ncap == 1699 and ws > 40 * 75600 * 128 * 2
     for bad_shape, code in [((1, 2, 4096, 96), ac.AC_E_UNSUPPORTED), ((0, 2, 4096, 64), ac.AC_E_SHAPE),
-                            ((1, 2, -5, 64), ac.AC_E_SHAPE)]:
+                            ((1, 2, -5, 64), ac.AC_E_SHAPE), ((1, 2, 0, 64), ac.AC_E_SHAPE),
+                            ((1, 0, 4096, 64), ac.AC_E_SHAPE)]:
         with pytest.raises(ac.ACError) as e:
             ac.ac_sizes(ac.Shape(*bad_shape), p)
         assert e.value.status == code

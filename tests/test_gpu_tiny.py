@@ -19,7 +19,7 @@ from oracle import score as osc
 from oracle import attention as oat
 from oracle import layer as oly
 from abi_helpers import (oracle_params, Run, np_, bf16_dev_to_f64, near_tie_flips, attn_error, ATTN_MAX_ABS,
-                         ATTN_REL_L2, to_dev)
+                         ATTN_REL_L2, to_dev, check_clusters_sampled, check_scores_selection, check_attention_sampled)
 
 pytestmark = pytest.mark.gpu
 
@@ -498,3 +498,38 @@ def test_interaction_aware_key_clustering(tiny, iters):
     torch.cuda.synchronize()
     from abi_helpers import check_attention_sampled
     check_attention_sampled(r, Q, K, V, p, 9001, nrows=512)
+
+
+# ---------------------------------------------------------------- small, ragged and degenerate layers
+
+@pytest.mark.parametrize("H,L,d,kw,zero_rows", [
+    (1, 1, 64, {}, 0),
+    (1, 1, 128, dict(sel_mode=nm.SEL_DENSITY, sel_param=0.5, compensate=1), 1),
+    (2, 37, 128, {}, 3),
+    (3, 300, 64, dict(tau_rule=nm.TAU_MEAN_X, tau_param=1.0, nmax=40), 0),
+    (3, 300, 64, dict(tau_rule=nm.TAU_MEAN_X, tau_param=0.8, nmax=70), 2),
+    (2, 513, 64, dict(sel_mode=nm.SEL_TOPP, sel_param=0.9, compensate=1), 0),
+    (1, 700, 128, dict(sel_mode=nm.SEL_DENSITY, sel_param=0.2, compensate=1, tau_rule=nm.TAU_PCTL,
+                       tau_param=0.9), 5),
+])
+def test_small_ragged_and_degenerate_layers(H, L, d, kw, zero_rows):
+    """Layers far from the kernels' tile sizes: a single token (one cluster on
+    each side, the attention returns V), fewer tokens than centres, lengths
+    that are not multiples of any block, rows of zero queries (their
+    normalised query is 0), and multi-stage keys with a low cap so that
+    heads fall back to dense.  Every stage is checked against the oracle
+    given the GPU's earlier stages, the attention on every row."""
+    Q, K, V = gen.generate(gen.get_workload("tiny", H=H, L=L, d=d))
+    if zero_rows:
+        Q = Q.copy()
+        Q[:, :, :zero_rows, :] = 0
+    p = P(**kw)
+    r = Run(Q, K, V, p).all()
+    out = check_clusters_sampled(r, Q, K, V, rows_seed=1, nrows=L)
+    check_scores_selection(r, p)
+    check_attention_sampled(r, Q, K, V, p, rows_seed=2, nrows=L)
+    if L == 1:
+        O = bf16_dev_to_f64(r.O).reshape(r.BH, 1, d)
+        assert np.array_equal(O, nm.bf16_to_f64(V.reshape(r.BH, 1, d)))
+        assert out["ncl"] == [1] * r.BH
+
