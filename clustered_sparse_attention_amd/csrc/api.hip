@@ -541,7 +541,7 @@ ac_status do_tail_merge(const Plan &P, int block, const ac_clusters *qi, const a
   t.ncapk = P.ncapk;
   t.mwords = P.mwords;
   t.L = P.L;
-  t.block = block > 0 ? block : ATT_QT;
+  t.block = block > 0 ? block : att_query_tile(P.D);
   launch_tail_merge(t, P.BH, st);
   launch_copy_i32(qi->ncl, qo->ncl, P.BH, st);
   AC_CHECK_LAUNCH();
@@ -575,7 +575,7 @@ ac_status do_attn(const Plan &P, const ac_params *p, const uint16_t *Q, const ui
   launch_attn_prep(D, a, stats->kmean, stats->vmean, at<uint16_t>(ws, P.kc), at<uint16_t>(ws, P.vc),
                    at<int>(ws, P.tile_off), at<long long>(ws, P.pairs), BH, st);
   AC_CHECK_LAUNCH();
-  const int max_blocks = (int)cdiv(P.L, ATT_QT) + q->ncap;
+  const int max_blocks = (int)cdiv(P.L, att_query_tile(D)) + q->ncap;
   launch_attn(D, a, BH, max_blocks, st);
   AC_CHECK_LAUNCH();
   return AC_OK;

@@ -1,7 +1,8 @@
 // Cluster-routed block-sparse flash attention for gfx950.
 //
-// A block takes ATT_QT = 128 queries of one query cluster (4 waves x 32) and
-// walks the concatenation of the key clusters selected for that cluster in
+// A block takes the query rows of one query cluster, 32 per wave (256 rows
+// in 8 waves at d = 128; 384 in 12 waves at d = 64, whose registers allow
+// three waves per SIMD), and walks the concatenation of the key clusters selected for that cluster in
 // tiles of 64 keys.  Tiles may span cluster boundaries, so each (query tile,
 // selection) has a single ragged tail however small the clusters are.  Rows
 // are gathered through the counting-sort permutations inside the kernel; the
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(256) void k_attn_prep(AttnArgs a, const float *__re
       to[r] = run;
       if (r < nq) {
         const int cnt = sq[r + 1] - sq[r];
-        run += (cnt + ATT_QT - 1) / ATT_QT;
+        run += (cnt + att_qt<D>() - 1) / att_qt<D>();
         pr += (long long)cnt * (long long)a.rows_T[(int64_t)h * a.nqcap + r];
       }
     }
@@ -154,21 +155,24 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 #define AC_LDS(T, p) ((__attribute__((address_space(3))) T *)(p))
 
-// One block: ATT_QT queries of one query cluster, NW waves of QG groups of
-// 32 queries.  Every K or V fragment a wave reads from LDS feeds QG
-// products, so LDS traffic per product falls with QG.
+// One block: QT queries of one query cluster, NW waves of QG groups of 32
+// queries.  Every K or V fragment a wave reads from LDS feeds QG products,
+// so LDS traffic per product falls with QG.  The K and V tiles are loaded by
+// the first LW waves (all of them at d = 128, 8 of 12 at d = 64).
 template <int D, int QG>
-__global__ __launch_bounds__(64 * ATT_QT / (32 * QG), 1) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__(64 * att_qt<D>() / (32 * QG), 1) void k_attn(AttnArgs a) {
+  constexpr int QT = att_qt<D>();             // query rows per block
   constexpr int KSQ = D / 16;                 // k-steps of the QK product
   constexpr int DB = D / 32;                  // 32-dim blocks of O
   constexpr int NC = D / 8;                   // 16-byte chunks per row
   constexpr int RPI = 64 / NC;                // rows per 64-lane global->LDS load
-  constexpr int NW = ATT_QT / (32 * QG);      // waves
-  constexpr int IPW = ATT_KT / RPI / NW;      // such loads per wave, per tensor and tile
+  constexpr int NW = QT / (32 * QG);          // waves
+  constexpr int LW = ATT_KT / RPI < NW ? ATT_KT / RPI : NW;  // waves that load tiles
+  constexpr int IPW = ATT_KT / RPI / LW;      // such loads per loading wave, per tensor and tile
   constexpr int TILE = ATT_KT * D;            // elements per tile
   constexpr int NST = 4;                      // K / V tile buffers
   constexpr int VPM = 8 / DB;                 // weights computed after each PV product
-  static_assert(IPW >= 1 && IPW * RPI * NW == ATT_KT, "tile load split");
+  static_assert(IPW >= 1 && IPW * RPI * LW == ATT_KT, "tile load split");
   // XCD-aware order: the hardware deals consecutive block ids round-robin to
   // the 8 XCDs.  Work items (head-major query tiles) are cut into chunks of
   // ATT_XCD_CHUNK and chunk k goes to XCD k % 8, so the few query tiles of a
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(64 * ATT_QT / (32 * QG), 1) void k_attn(AttnArgs a)
   }
   const int r = lo;
   const int *segq = a.seg_q + (int64_t)h * (a.nqcap + 1);
-  const int qbeg = segq[r] + (blk - toff[r]) * ATT_QT;
+  const int qbeg = segq[r] + (blk - toff[r]) * QT;
   const int qend = segq[r + 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -279,19 +283,20 @@ __global__ __launch_bounds__(64 * ATT_QT / (32 * QG), 1) void k_attn(AttnArgs a)
   // The swizzles depend on the row only modulo 16, and a lane's row moves by
   // NW * RPI (a multiple of 16) from one load to the next, so its source
   // chunk byte offset is fixed.
-  static_assert((NW * RPI) % 16 == 0, "swizzle period");
+  static_assert((LW * RPI) % 16 == 0, "swizzle period");
   const uint32_t koff = 16u * (uint32_t)((lane % NC) ^ kswz<D>(wave * RPI + lane / NC));
   const uint32_t voff = 16u * (uint32_t)((lane % NC) ^ vswz<D>(wave * RPI + lane / NC));
-  // one tensor of tile tt into buffer `buf`: wave w writes rows
-  // [RPI*(NW*ii+w), +RPI); rows come from the wave's index registers by shuffle
+  // one tensor of tile tt into buffer `buf`: loading wave w < LW writes rows
+  // [RPI*(LW*ii+w), +RPI); rows come from the wave's index registers by shuffle
   auto dma = [&](bool vpart, int tt, int rwv, int buf) {
     const bool ph1 = tt >= nt0;
     const char *src = vpart ? (ph1 ? Vc : Vh) : (ph1 ? Kc : Kh);
     const uint32_t off = vpart ? voff : koff;
     const uint16_t *dst = (vpart ? Vb : Kb) + buf * TILE;
+    if (wave >= LW) return;
 #pragma unroll
     for (int ii = 0; ii < IPW; ++ii) {
-      const int I = ii * NW + wave;
+      const int I = ii * LW + wave;
       const int R = I * RPI + lane / NC;
       const uint32_t rw = (uint32_t)max(__shfl(rwv, R, 64), 0);  // masked keys read row 0; their bias is -inf
       dma16((const uint16_t *)(src + (rw * (uint32_t)(2 * D) + off)), lds_addr(dst + I * 512));
@@ -564,9 +569,9 @@ void launch_attn(int D, const AttnArgs &a, int BH, int max_blocks, hipStream_t s
   const long long total = ((long long)max_blocks * BH + 8 * ATT_XCD_CHUNK - 1) / (8 * ATT_XCD_CHUNK) *
                           (8 * ATT_XCD_CHUNK);  // whole chunks on all 8 XCDs
   if (D == 64)
-    hipLaunchKernelGGL((k_attn<64, ATT_QG>), dim3((unsigned)total), dim3(ATT_THREADS), 0, st, aa);
+    hipLaunchKernelGGL((k_attn<64, ATT_QG>), dim3((unsigned)total), dim3(64 * att_qt<64>() / (32 * ATT_QG)), 0, st, aa);
   else
-    hipLaunchKernelGGL((k_attn<128, ATT_QG>), dim3((unsigned)total), dim3(ATT_THREADS), 0, st, aa);
+    hipLaunchKernelGGL((k_attn<128, ATT_QG>), dim3((unsigned)total), dim3(64 * att_qt<128>() / (32 * ATT_QG)), 0, st, aa);
 }
 
 }  // namespace ac

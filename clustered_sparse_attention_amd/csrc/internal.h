@@ -10,9 +10,11 @@ constexpr int KPP_SMAX = 16384;  // most points a k-means++ subsample may hold
 constexpr int KPP_GRAM_MAX = 8192;  // subsamples up to this size seed from a distance matrix
 constexpr int SORT_TILE = 128;   // points per counting-sort tile (one wave)
 constexpr int SORT_GROUP = 32;   // tiles per group in the two-level scan over tiles
-constexpr int ATT_QT = 256;      // query rows per attention block
+constexpr int ATT_QT = 256;      // query rows per attention block at d = 128 (8 waves)
+constexpr int ATT_QT64 = 384;    // at d = 64: 12 waves, three per SIMD fit its registers
 constexpr int ATT_QG = 1;        // groups of 32 queries per attention wave
-constexpr int ATT_THREADS = 64 * ATT_QT / (32 * ATT_QG);
+template <int D> constexpr int att_qt() { return D == 64 ? ATT_QT64 : ATT_QT; }
+inline int att_query_tile(int D) { return D == 64 ? ATT_QT64 : ATT_QT; }
 constexpr int ATT_XCD_CHUNK = 4;  // consecutive query tiles kept on one XCD
 constexpr int ATT_KT = 64;       // keys per attention tile
 constexpr int SEL_MAXN = 4096;   // most key clusters the select kernel sorts

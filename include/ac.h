@@ -231,8 +231,8 @@ ac_status ac_sparse_attn(const ac_shape *s, const ac_params *p, const uint16_t *
 /* Tail merging of the query clusters before the attention ("iCATS: Fast Video Generation via
  * Interaction-Aware Sparse Attention and Timestep-Adaptive Sparsity", method section, tail-merging
  * design, and its worked example).  The attention processes each query cluster in blocks of `block`
- * rows (0: the attention kernel's own block, 256), so the last, partial block of every cluster costs a
- * whole block for every key it attends to.  Per head: (1) query clusters with identical key-cluster
+ * rows (0: the attention kernel's own query block, 256 rows at d = 128 and 384 at d = 64), so the
+ * last, partial block of every cluster costs a whole block for every key it attends to.  Per head: (1) query clusters with identical key-cluster
  * masks merge into the lowest-numbered one (token lists appended in cluster order; no token's key
  * set changes); (2) among the clusters that still have a tail t = size mod block > 0, each pair that
  * are each other's nearest neighbour in Hamming distance between masks (ties to the lower index) and

@@ -274,7 +274,7 @@ def check_tail_merge(r, block, heads=None):
     sm = ac.Selection(r.BH, r.nq, r.ncap_k, dev, score=False)
     ac.ac_tail_merge(r.shape, r.cp, block, r.q, r.sel, qm, sm, r.ws)
     torch.cuda.synchronize()
-    b = block if block > 0 else 256
+    b = block if block > 0 else (384 if r.d == 64 else 256)  # the attention's query block
     perm, seg = np_(r.q.perm), np_(r.q.seg)
     lst, n, mask = np_(r.sel.list), np_(r.sel.n), np_(r.sel.mask).view(np.uint32)
     mperm, mseg, mlab = np_(qm.perm), np_(qm.seg), np_(qm.labels)
