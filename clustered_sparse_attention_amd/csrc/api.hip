@@ -98,6 +98,7 @@ ac_status check_params(const ac_shape *s, const ac_params *p) {
 // own, so the two may run at the same time on different streams.
 struct Scratch {
   size_t lab, lperm, lseg, thist, tgrp, ops_hi, ops_lo, ops_norm, d2buf, hn, hm, hcoff, chunk_off, upd_part;
+  size_t chg, neff;  // Lloyd fixed-point detection: two change counters and the loop's n, per head
   size_t kpp_nx, kpp_G;
   int mcap, kpp_smax, upd_items;
 };
@@ -157,6 +158,8 @@ Plan make_plan(const ac_shape *s, const ac_params *p) {
     S.hm = take(BH * 4);
     S.hcoff = take(BH * 4);
     S.chunk_off = take(BH * (S.mcap + 1) * 4);
+    S.chg = take(2 * BH * 4);
+    S.neff = take(BH * 4);
     S.upd_items = (int)cdiv(P.L, UPD_CHUNK) + S.mcap;
     S.upd_part = take(BH * (size_t)S.upd_items * D * 8);
     S.kpp_smax = p->init_sample > 0 ? (int)std::min<int64_t>(P.L, (int64_t)p->init_sample * mm) : P.L;
@@ -275,6 +278,9 @@ struct Engine {
     s.seg = seg;
     s.seg_hs = segcap + 1;
     s.segcap = segcap;
+    s.neff = nullptr;
+    s.chg_cur = nullptr;
+    s.chg_zero = nullptr;
     return s;
   }
   // mmax: bound on m over heads (grid size); npts: bound on n.
@@ -296,11 +302,29 @@ struct Engine {
     if (metric) launch_cent_prep_metric(D, a, op, metric, P.BH, mmax, st);
     AC_CHECK_LAUNCH();
     int *lab = at<int>(ws, S.lab);
+    // Lloyd iterations.  Once an assignment leaves every label of a head as
+    // it was, the update reproduces that head's centres bit for bit (the
+    // same members, summed in the same order; empty clusters keep theirs),
+    // so every later iteration is a fixed point: the head leaves the loop
+    // (its n in the loop's copy `neff` drops to 0) with exactly the centres
+    // and labels the remaining iterations would give.  Iteration 0 has no
+    // previous labels to compare with.  The final assignment covers every head.
+    int *chg = at<int>(ws, S.chg), *neff = at<int>(ws, S.neff);
+    KmArgs al = a;
+    if (iters > 0) {
+      launch_copy_i32(a.n, neff, P.BH, st);
+      al.n = neff;
+    }
     for (int it = 0; it < iters; ++it) {
-      launch_assign(D, a, op, P.BH, mmax, npts, lab, P.L, st);
+      int *cur = chg + (it & 1) * P.BH, *nxt = chg + ((it + 1) & 1) * P.BH;
+      launch_assign(D, al, op, P.BH, mmax, npts, lab, P.L, st, it > 0 ? cur : nullptr);
       SortArgs s = sort_args(lab, at<int>(ws, S.lperm), at<int>(ws, S.lseg), S.mcap, mmax);
+      s.n = neff;
+      s.neff = neff;
+      s.chg_cur = it > 0 ? cur : nullptr;
+      s.chg_zero = nxt;
       launch_sort(s, P.BH, npts, st);
-      launch_update(D, a, s, op, P.BH, mmax, npts, at<int>(ws, S.chunk_off), S.mcap + 1, at<double>(ws, S.upd_part),
+      launch_update(D, al, s, op, P.BH, mmax, npts, at<int>(ws, S.chunk_off), S.mcap + 1, at<double>(ws, S.upd_part),
                     (int64_t)S.upd_items * D, st);
       if (metric) launch_cent_prep_metric(D, a, op, metric, P.BH, mmax, st);
       AC_CHECK_LAUNCH();

@@ -59,6 +59,12 @@ struct SortArgs {
   int *seg;           // [BH, seg_hs], entries 0..segcap written
   int64_t seg_hs;
   int segcap;
+  // Lloyd fixed-point detection (NULL outside the Lloyd loop): a head whose
+  // assignment did not change (chg_cur[h] == 0) gets neff[h] = 0 (neff is the
+  // n array of the loop), and chg_zero[h] is cleared for the next count
+  int *neff;
+  const int *chg_cur;
+  int *chg_zero;
 };
 
 struct KStatsArgs {
@@ -163,8 +169,10 @@ void launch_kpp(int D, const KmArgs &a, int BH, double *d2buf, int init_sample, 
 void launch_kpp_gram(int D, const KmArgs &a, int BH, int smax, double *nx, double *G, int init_sample, uint64_t seed,
                      int role, int stage, hipStream_t st);
 void launch_cent_prep(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, hipStream_t st);
+// chg (nullable): per-head flag set to 1 when some point's label differs from
+// the one already in `labels` (the caller clears it)
 void launch_assign(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, int nmax_pts, int *labels, int64_t lab_hs,
-                   hipStream_t st);
+                   hipStream_t st, int *chg = nullptr);
 void launch_sort(const SortArgs &s, int BH, int nmax_pts, hipStream_t st);
 void launch_update(int D, const KmArgs &a, const SortArgs &s, const CentOps &op, int BH, int mmax, int npts,
                    int *chunk_off, int64_t co_hs, double *partial, int64_t part_hs, hipStream_t st);

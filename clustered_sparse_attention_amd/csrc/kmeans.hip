@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void k_cent_prep(KmArgs a, CentOps op) {
 // centre index; padding centres carry -inf and never win.
 template <int D>
 __global__ __launch_bounds__(256) void k_assign(KmArgs a, CentOps op, int *__restrict__ labels,
-                                                int64_t lab_hs) {
+                                                int64_t lab_hs, int *__restrict__ chg) {
   constexpr int KS = D / 32;   // k-steps of 32 dims
   constexpr int CH = 64;       // centres per LDS chunk
   constexpr int LDSROW = D + 8;  // padded row (bf16 elements)
@@ -117,10 +117,17 @@ __global__ __launch_bounds__(256) void k_assign(KmArgs a, CentOps op, int *__res
 
   float best[4][4];
   int bidx[4][4];
+  int old[4][4];  // labels already in place for the points this lane writes (when counting changes)
+  bool any_change = false;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) { best[rt][j] = -__builtin_inff(); bidx[rt][j] = 0x7fffffff; }
+    for (int j = 0; j < 4; ++j) {
+      best[rt][j] = -__builtin_inff();
+      bidx[rt][j] = 0x7fffffff;
+      const int i = wbase + rt * 16 + g * 4 + j;
+      old[rt][j] = (chg != nullptr && l16 == 0 && i < n) ? labels[(int64_t)h * lab_hs + i] : 0;
+    }
 
   const uint16_t *ghi = op.hi + (int64_t)h * op.cap * D;
   const uint16_t *glo = op.lo + (int64_t)h * op.cap * D;
@@ -183,8 +190,13 @@ __global__ __launch_bounds__(256) void k_assign(KmArgs a, CentOps op, int *__res
         if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
       }
       int i = wbase + rt * 16 + g * 4 + j;
-      if (l16 == 0 && i < n) labels[(int64_t)h * lab_hs + i] = bi == 0x7fffffff ? 0 : bi;
+      const bool wr = l16 == 0 && i < n;
+      const int nl = bi == 0x7fffffff ? 0 : bi;
+      const bool changed = wr && chg != nullptr && old[rt][j] != nl;
+      if (wr) labels[(int64_t)h * lab_hs + i] = nl;
+      any_change |= __ballot(changed) != 0;
     }
+  if (chg != nullptr && any_change && lane == 0) chg[h] = 1;  // some label of head h changed
 }
 
 // Same result as k_assign for m <= ASSIGN_RES_MAX, organised for HBM rate:
@@ -195,7 +207,7 @@ __global__ __launch_bounds__(256) void k_assign(KmArgs a, CentOps op, int *__res
 // MFMA work.
 template <int D, int NT>
 __global__ __launch_bounds__(NT) void k_assign_res(KmArgs a, CentOps op, int *__restrict__ labels, int64_t lab_hs,
-                                                   int BH, int mpmax) {
+                                                   int BH, int mpmax, int *__restrict__ chg) {
   constexpr int KS = D / 32;
   constexpr int LDSROW = D + 8;
   constexpr int NW = NT / 64;
@@ -238,12 +250,15 @@ __global__ __launch_bounds__(NT) void k_assign_res(KmArgs a, CentOps op, int *__
       __syncthreads();
       const uint16_t *X = a.X + (int64_t)h * a.x_hs;
       const int *idx = a.idx ? a.idx + (int64_t)h * a.idx_hs : nullptr;
+      bool any_change = false;
       for (int64_t t = r0 + wave; t < r1; t += NW) {
         const int wbase = (int)(t - hb) * 64;
         bf16x8_t af[4][KS];
+        int old[4];  // labels already in place (compared when counting changes)
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
           const int i = wbase + rt * 16 + l16;
+          old[rt] = (chg != nullptr && g == 0 && i < n) ? labels[(int64_t)h * lab_hs + i] : 0;
           if (i < n) {
             const int64_t row = idx ? (int64_t)idx[i] : (int64_t)i;
             const uint16_t *xr = X + row * D;
@@ -296,9 +311,14 @@ __global__ __launch_bounds__(NT) void k_assign_res(KmArgs a, CentOps op, int *__
             if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
           }
           const int i = wbase + rt * 16 + l16;
-          if (g == 0 && i < n) labels[(int64_t)h * lab_hs + i] = bi == 0x7fffffff ? 0 : bi;
+          const bool wr = g == 0 && i < n;
+          const int nl = bi == 0x7fffffff ? 0 : bi;
+          const bool changed = wr && chg != nullptr && old[rt] != nl;
+          if (wr) labels[(int64_t)h * lab_hs + i] = nl;
+          any_change |= __ballot(changed) != 0;
         }
       }
+      if (chg != nullptr && any_change && lane == 0) chg[h] = 1;  // some label of head h changed
     }
     hb = he;
   }
@@ -313,6 +333,13 @@ __global__ __launch_bounds__(NT) void k_assign_res(KmArgs a, CentOps op, int *__
 __global__ __launch_bounds__(64) void k_sort_hist(SortArgs s) {
   const int h = blockIdx.y, tile = blockIdx.x;
   const int n = s.n[h], m = s.m[h];
+  if (tile == 0 && threadIdx.x == 0 && s.chg_zero != nullptr) {
+    // Lloyd loop: no label of head h changed in this assignment, so this
+    // update and every later step reproduce the current centres exactly;
+    // the head drops out of the loop (later kernels read neff[h] = 0)
+    if (s.chg_cur != nullptr && s.chg_cur[h] == 0) s.neff[h] = 0;
+    s.chg_zero[h] = 0;
+  }
   const int beg = tile * SORT_TILE;
   if (beg >= n || m <= 0) return;
   extern __shared__ int sh_hist[];
@@ -921,7 +948,7 @@ static int device_cus() {
 }
 
 void launch_assign(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, int nmax_pts, int *labels,
-                   int64_t lab_hs, hipStream_t st) {
+                   int64_t lab_hs, hipStream_t st, int *chg) {
   if (mmax <= ASSIGN_RES_MAX) {
     // 512 threads and LDS for this launch's centres only, one block per CU:
     // half of each CU's registers stay free for work on other streams
@@ -936,12 +963,13 @@ void launch_assign(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, 
                                                (int)((size_t)ASSIGN_RES_MAX * (DD + 8) * 4 + ASSIGN_RES_MAX * 4)) ==
                            hipSuccess;
       (void)lds_ok;  // a refusal shows up as a launch error
-      hipLaunchKernelGGL((k_assign_res<DD, NT>), dim3(blocks), dim3(NT), lds, st, a, op, labels, lab_hs, BH, mpmax);
+      hipLaunchKernelGGL((k_assign_res<DD, NT>), dim3(blocks), dim3(NT), lds, st, a, op, labels, lab_hs, BH, mpmax,
+                         chg);
     });
     return;
   }
   AC_D_DISPATCH(D, hipLaunchKernelGGL(k_assign<DD>, g2((nmax_pts + 255) / 256, BH), dim3(256), 0, st, a, op, labels,
-                                      lab_hs));
+                                      lab_hs, chg));
 }
 
 void launch_sort(const SortArgs &s, int BH, int nmax_pts, hipStream_t st) {
