@@ -341,43 +341,49 @@ def summarize(args):
         def dur(r):
             return (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
 
-        def nth(step, name, lo, hi):
-            return [r for r in step if name in r["Kernel_Name"]][lo:hi]
+        def nth(step, name, idx):
+            hits = [r for r in step if name in r["Kernel_Name"]]
+            return [hits[i] for i in idx if i < len(hits)]
 
         x_bytes = BH * L * d * 2.0
         table = []  # (kernel, launches, what, work, unit, peak)
         pad = lambda m: (m + 15) // 16 * 16
+        # Lloyd launches in which every head still takes part: a head leaves the
+        # loop once an assignment changes none of its labels, so only iteration
+        # 0's update and sort, iterations 0 and 1's assignments and the final
+        # assignment are certain to cover all heads
         specs = [
-            ("k_qnorm", "k_qnorm", 0, 1, "read Q + write q-hat (bf16) and norms", 2 * x_bytes + BH * L * 4, "hbm"),
-            ("k_assign_res, queries (n = L, m = %d)" % nq, "k_assign_res", 0, 11,
+            ("k_qnorm", "k_qnorm", [0], "read Q + write q-hat (bf16) and norms", 2 * x_bytes + BH * L * 4, "hbm"),
+            ("k_assign_res, queries (n = L, m = %d)" % nq, "k_assign_res", [0, 1, 10],
              "read X once (the argmin GEMM: %.2f TFLOP incl. hi/lo)" % (4.0 * BH * L * pad(nq) * d / 1e12),
              x_bytes, "hbm"),
-            ("k_assign_res, key stage 1 (n = L, m = %d)" % m0, "k_assign_res", 11, 22,
+            ("k_assign_res, key stage 1 (n = L, m = %d)" % m0, "k_assign_res", [11, 12, 21],
              "bf16 MFMA, centres split hi + lo, m padded to 16", 4.0 * BH * L * pad(m0) * d, "mfma"),
-            ("k_update_partial, queries + key stage 1", "k_update_partial", 0, 20,
+            ("k_update_partial, queries + key stage 1", "k_update_partial", [0, 10],
              "gather X in cluster order (bf16) + perm", x_bytes + BH * L * 4, "hbm"),
-            ("k_sort_scatter, full-size", "k_sort_scatter", 0, 22, "read labels, write perm", BH * L * 8.0, "hbm"),
-            ("k_kstats", "k_kstats", 0, 1, "read K and V in cluster order", 2 * x_bytes, "hbm"),
-            ("k_attn (density 0.15)", "k_attn<", 0, 1, "see the bench line (algorithmic pairs x 4d)", None, "mfma"),
+            ("k_sort_scatter, full-size", "k_sort_scatter", [0, 11], "read labels, write perm", BH * L * 8.0, "hbm"),
+            ("k_kstats", "k_kstats", [0], "read K and V in cluster order", 2 * x_bytes, "hbm"),
+            ("k_attn (density 0.15)", "k_attn<", [0], "see the bench line (algorithmic pairs x 4d)", None, "mfma"),
         ]
         peaks = {"hbm": (PEAK_HBM_GBS, "GB/s", 1e9), "mfma": (PEAK_BF16_TFLOPS, "TFLOP/s", 1e12)}
         lines = [f"# Per-kernel roofline, {w.description}", "", f"Command: `{cmd}`", "",
-                 "Full-size launches of the timed layer steps (the entry points run one after another); "
-                 "work is algorithmic (what the step must move or compute), time is the kernel's own.", "",
+                 "Full-size launches of the timed layer steps (the entry points run one after another; of the "
+                 "Lloyd loops only the launches in which every head takes part); work is algorithmic (what the "
+                 "step must move or compute), time is the kernel's own.", "",
                  "| kernel | launches/step | work per launch | avg time | achieved | peak | fraction |",
                  "|---|---:|---|---:|---:|---:|---:|"]
-        for label, name, lo, hi, what, work, bound in specs:
-            ds = [dur(r) for st in steps for r in nth(st, name, lo, hi)]
+        for label, name, idx, what, work, bound in specs:
+            ds = [dur(r) for st in steps for r in nth(st, name, idx)]
             if not ds:
                 continue
             t = float(np.mean(ds))
             peak, unit, scale = peaks[bound]
             if work is None:
-                lines.append(f"| {label} | {hi - lo} | {what} | {t * 1e3:.3f} ms | — | {peak:.0f} {unit} | — |")
+                lines.append(f"| {label} | {len(idx)} | {what} | {t * 1e3:.3f} ms | — | {peak:.0f} {unit} | — |")
                 continue
             ach = work / t / scale
             wtxt = f"{work / 1e9:.3f} GB" if bound == "hbm" else f"{work / 1e12:.3f} TFLOP"
-            lines.append(f"| {label} | {hi - lo} | {wtxt}: {what} | {t * 1e3:.3f} ms | {ach:.0f} {unit} | "
+            lines.append(f"| {label} | {len(idx)} | {wtxt}: {what} | {t * 1e3:.3f} ms | {ach:.0f} {unit} | "
                          f"{peak:.0f} {unit} | {ach / peak:.2f} |")
         open(out, "w").write("\n".join(lines) + "\n")
         print("\n".join(lines))
