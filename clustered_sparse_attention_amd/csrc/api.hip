@@ -308,7 +308,9 @@ struct Engine {
     // so every later iteration is a fixed point: the head leaves the loop
     // (its n in the loop's copy `neff` drops to 0) with exactly the centres
     // and labels the remaining iterations would give.  Iteration 0 has no
-    // previous labels to compare with.  The final assignment covers every head.
+    // previous labels to compare with.  The final assignment covers the heads
+    // still in the loop; the others keep the loop's last labels, which it
+    // would repeat.
     int *chg = at<int>(ws, S.chg), *neff = at<int>(ws, S.neff);
     KmArgs al = a;
     if (iters > 0) {
@@ -329,7 +331,12 @@ struct Engine {
       if (metric) launch_cent_prep_metric(D, a, op, metric, P.BH, mmax, st);
       AC_CHECK_LAUNCH();
     }
-    launch_assign(D, a, op, P.BH, mmax, npts, labels_out, P.L, st);
+    if (iters > 0) {
+      launch_assign(D, al, op, P.BH, mmax, npts, labels_out, P.L, st);
+      launch_copy_converged(a.n, neff, lab, labels_out, P.L, npts, P.BH, st);
+    } else {
+      launch_assign(D, a, op, P.BH, mmax, npts, labels_out, P.L, st);
+    }
     AC_CHECK_LAUNCH();
     return AC_OK;
   }

@@ -191,6 +191,8 @@ void launch_fill_i32(int *p, int64_t n, int v, hipStream_t st);
 void launch_fill_u8(uint8_t *p, int64_t n, uint8_t v, hipStream_t st);
 void launch_identity_clusters(int *perm, int *seg, int *ncl, int L, int segcap, int BH, hipStream_t st);
 void launch_copy_i32(const int *s, int *d, int64_t n, hipStream_t st);
+void launch_copy_converged(const int *n, const int *neff, const int *src, int *dst, int64_t hs, int npts, int BH,
+                           hipStream_t st);
 void launch_copy_f32(const float *s, float *d, int64_t n, hipStream_t st);
 void launch_copy_u8(const uint8_t *s, uint8_t *d, int64_t n, hipStream_t st);
 void launch_set_m_min(int *m, const int *n, int v, int BH, hipStream_t st);

@@ -894,6 +894,15 @@ __global__ void k_identity_clusters(int *__restrict__ perm, int *__restrict__ se
   if (i <= segcap) seg[(int64_t)h * (segcap + 1) + i] = i == 0 ? 0 : L;
   if (i == 0) ncl[h] = 1;
 }
+// Labels of the heads that left the Lloyd loop (neff = 0 < n): the loop's last
+// assignment, which the final one would repeat.
+__global__ void k_copy_converged(const int *__restrict__ n, const int *__restrict__ neff, const int *__restrict__ src,
+                                 int *__restrict__ dst, int64_t hs) {
+  const int h = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (neff[h] != 0 || i >= n[h]) return;
+  dst[(int64_t)h * hs + i] = src[(int64_t)h * hs + i];
+}
 __global__ void k_copy_i32(const int *__restrict__ src, int *__restrict__ dst, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) dst[i] = src[i];
@@ -1046,6 +1055,11 @@ void launch_identity_clusters(int *perm, int *seg, int *ncl, int L, int segcap, 
 }
 void launch_fill_u8(uint8_t *p, int64_t n, uint8_t v, hipStream_t st) {
   if (n > 0) hipLaunchKernelGGL(k_fill_u8, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n, v);
+}
+void launch_copy_converged(const int *n, const int *neff, const int *src, int *dst, int64_t hs, int npts, int BH,
+                           hipStream_t st) {
+  if (npts > 0 && BH > 0)
+    hipLaunchKernelGGL(k_copy_converged, g2((npts + 255) / 256, BH), dim3(256), 0, st, n, neff, src, dst, hs);
 }
 void launch_copy_i32(const int *s, int *d, int64_t n, hipStream_t st) {
   if (n > 0) hipLaunchKernelGGL(k_copy_i32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, s, d, n);
