@@ -734,7 +734,8 @@ def main():
                    "params": {k: (round(v, 6) if isinstance(v, float) else v) for k, v in kw.items()}},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(args.workload, args.variant, args.compensate),
+                     "traffic": (measured_traffic(args.workload, args.variant, args.compensate)
+                                 if not args.key_metric and not args.tail_block else None),
                      "kernel": "ac_sparse_attn: k_attn_rows + k_attn_prep + k_attn (block-sparse attention)",
                      "algorithmic_flops_per_launch": attn_flops, "avg_launch_ms": round(attn_ms, 4)},
         "phase_ms": {"cluster_q": round(float(phase_ms[0]), 3), "cluster_k": round(float(phase_ms[1]), 3),
