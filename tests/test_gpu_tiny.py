@@ -502,24 +502,27 @@ def test_interaction_aware_key_clustering(tiny, iters):
 
 # ---------------------------------------------------------------- small, ragged and degenerate layers
 
-@pytest.mark.parametrize("H,L,d,kw,zero_rows", [
-    (1, 1, 64, {}, 0),
-    (1, 1, 128, dict(sel_mode=nm.SEL_DENSITY, sel_param=0.5, compensate=1), 1),
-    (2, 37, 128, {}, 3),
-    (3, 300, 64, dict(tau_rule=nm.TAU_MEAN_X, tau_param=1.0, nmax=40), 0),
-    (3, 300, 64, dict(tau_rule=nm.TAU_MEAN_X, tau_param=0.8, nmax=70), 2),
-    (2, 513, 64, dict(sel_mode=nm.SEL_TOPP, sel_param=0.9, compensate=1), 0),
-    (1, 700, 128, dict(sel_mode=nm.SEL_DENSITY, sel_param=0.2, compensate=1, tau_rule=nm.TAU_PCTL,
-                       tau_param=0.9), 5),
+@pytest.mark.parametrize("B,H,L,d,kw,zero_rows", [
+    (1, 1, 1, 64, {}, 0),
+    (1, 1, 1, 128, dict(sel_mode=nm.SEL_DENSITY, sel_param=0.5, compensate=1), 1),
+    (1, 2, 37, 128, {}, 3),
+    (1, 3, 300, 64, dict(tau_rule=nm.TAU_MEAN_X, tau_param=1.0, nmax=40), 0),
+    (1, 3, 300, 64, dict(tau_rule=nm.TAU_MEAN_X, tau_param=0.8, nmax=70), 2),
+    (1, 2, 513, 64, dict(sel_mode=nm.SEL_TOPP, sel_param=0.9, compensate=1), 0),
+    (1, 1, 700, 128, dict(sel_mode=nm.SEL_DENSITY, sel_param=0.2, compensate=1, tau_rule=nm.TAU_PCTL,
+                          tau_param=0.9), 5),
+    (2, 2, 300, 128, {}, 0),
+    (3, 1, 513, 64, dict(sel_mode=nm.SEL_DENSITY, sel_param=0.2, compensate=1), 4),
 ])
-def test_small_ragged_and_degenerate_layers(H, L, d, kw, zero_rows):
+def test_small_ragged_and_degenerate_layers(B, H, L, d, kw, zero_rows):
     """Layers far from the kernels' tile sizes: a single token (one cluster on
     each side, the attention returns V), fewer tokens than centres, lengths
     that are not multiples of any block, rows of zero queries (their
-    normalised query is 0), and multi-stage keys with a low cap so that
-    heads fall back to dense.  Every stage is checked against the oracle
-    given the GPU's earlier stages, the attention on every row."""
-    Q, K, V = gen.generate(gen.get_workload("tiny", H=H, L=L, d=d))
+    normalised query is 0), multi-stage keys with a low cap so that heads
+    fall back to dense, and batches of several sequences.  Every stage is
+    checked against the oracle given the GPU's earlier stages, the attention
+    on every row."""
+    Q, K, V = gen.generate(gen.get_workload("tiny", B=B, H=H, L=L, d=d))
     if zero_rows:
         Q = Q.copy()
         Q[:, :, :zero_rows, :] = 0
