@@ -150,6 +150,31 @@ def test_lloyd_inertia_non_increasing():
         prev = cur
 
 
+def test_lloyd_fixed_point_once_labels_repeat():
+    """Textbook Lloyd property the GPU loop relies on to let a head leave
+    early: once an assignment equals the previous one, the update returns
+    the same centres bit for bit (same members, same summation order, empty
+    clusters keep theirs), so every later iteration is the same fixed point
+    and stopping there gives exactly the full run's centres and labels."""
+    r = _rng(11)
+    for trial in range(6):
+        n, d, m = int(r.integers(40, 400)), int(r.integers(2, 9)), int(r.integers(3, 25))
+        X = r.standard_normal((n, d)) + r.integers(0, 6, (n, 1)) * 1.5
+        C0, _ = okm.kmeanspp_init(X, min(m, n), trial, 3, 0)
+        C_full, lab_full = okm.lloyd(X, C0, 10)
+        C, prev, stopped = C0.copy(), None, None
+        for it in range(10):
+            lab = okm.assign(X, C)
+            C_new = okm.update(X, lab, C)
+            if prev is not None and np.array_equal(lab, prev):
+                assert np.array_equal(C_new, C)  # the fixed point, exactly
+                stopped = it
+                break
+            prev, C = lab, C_new
+        lab_final = okm.assign(X, C)
+        assert np.array_equal(C, C_full) and np.array_equal(lab_final, lab_full), (trial, stopped)
+
+
 def test_update_empty_cluster_keeps_centre():
     X = np.array([[0.0], [1.0], [2.0]])
     C_prev = np.array([[0.5], [100.0]])
