@@ -281,6 +281,8 @@ struct Engine {
     s.neff = nullptr;
     s.chg_cur = nullptr;
     s.chg_zero = nullptr;
+    s.chunk_off = nullptr;
+    s.co_hs = 0;
     return s;
   }
   // mmax: bound on m over heads (grid size); npts: bound on n.
@@ -325,9 +327,10 @@ struct Engine {
       s.neff = neff;
       s.chg_cur = it > 0 ? cur : nullptr;
       s.chg_zero = nxt;
+      s.chunk_off = at<int>(ws, S.chunk_off);
+      s.co_hs = S.mcap + 1;
       launch_sort(s, P.BH, npts, st);
-      launch_update(D, al, s, op, P.BH, mmax, npts, at<int>(ws, S.chunk_off), S.mcap + 1, at<double>(ws, S.upd_part),
-                    (int64_t)S.upd_items * D, st);
+      launch_update(D, al, s, op, P.BH, mmax, npts, at<double>(ws, S.upd_part), (int64_t)S.upd_items * D, st);
       if (metric) launch_cent_prep_metric(D, a, op, metric, P.BH, mmax, st);
       AC_CHECK_LAUNCH();
     }

@@ -65,6 +65,10 @@ struct SortArgs {
   int *neff;
   const int *chg_cur;
   int *chg_zero;
+  // chunk offsets of the centre update (NULL unless the sort feeds one):
+  // chunk_off[h][c] = number of UPD_CHUNK-member chunks of labels < c, c <= m
+  int *chunk_off;
+  int64_t co_hs;
 };
 
 struct KStatsArgs {
@@ -175,7 +179,7 @@ void launch_assign(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, 
                    hipStream_t st, int *chg = nullptr);
 void launch_sort(const SortArgs &s, int BH, int nmax_pts, hipStream_t st);
 void launch_update(int D, const KmArgs &a, const SortArgs &s, const CentOps &op, int BH, int mmax, int npts,
-                   int *chunk_off, int64_t co_hs, double *partial, int64_t part_hs, hipStream_t st);
+                   double *partial, int64_t part_hs, hipStream_t st);
 void launch_stage_dist(int D, const KmArgs &a, int BH, int nmax_pts, const int *labels, int64_t lab_hs, float *dist,
                        int64_t dist_hs, hipStream_t st);
 void launch_tau(const float *dist, int64_t dist_hs, const int *n_arr, int BH, int nmax_pts, int rule, float param,

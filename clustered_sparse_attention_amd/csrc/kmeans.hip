@@ -377,7 +377,9 @@ __global__ __launch_bounds__(256) void k_sort_gscan(SortArgs s) {
 }
 
 // Per head: scan each label over the groups, then the label totals; grp
-// ends up holding the first output position of (group, label).
+// ends up holding the first output position of (group, label).  With
+// chunk_off set, the chunk counts of the centre update are scanned beside the
+// label totals.
 __global__ __launch_bounds__(1024) void k_sort_scan(SortArgs s) {
   const int h = blockIdx.x;
   const int n = s.n[h], m = s.m[h];
@@ -385,10 +387,10 @@ __global__ __launch_bounds__(1024) void k_sort_scan(SortArgs s) {
   const int nt = (n + SORT_TILE - 1) / SORT_TILE;
   const int ng = (nt + SORT_GROUP - 1) / SORT_GROUP;
   int *grp = s.grp + (int64_t)h * s.max_groups * s.mcap;
-  __shared__ int part[1024];
+  __shared__ int2 part[1024];
   const int per = (m + 1023) / 1024;
   const int cb = min(m, (int)threadIdx.x * per), ce = min(m, cb + per);
-  int tot_local = 0;
+  int tot_local = 0, chunks_local = 0;
   for (int c = cb; c < ce; ++c) {
     int run = 0;
     for (int g = 0; g < ng; ++g) {
@@ -399,22 +401,31 @@ __global__ __launch_bounds__(1024) void k_sort_scan(SortArgs s) {
     }
     seg[c] = run;  // count for now
     tot_local += run;
+    chunks_local += (run + UPD_CHUNK - 1) / UPD_CHUNK;
   }
-  part[threadIdx.x] = tot_local;
+  part[threadIdx.x] = make_int2(tot_local, chunks_local);
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
-    int v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    const int2 v = threadIdx.x >= off ? part[threadIdx.x - off] : make_int2(0, 0);
     __syncthreads();
-    part[threadIdx.x] += v;
+    part[threadIdx.x].x += v.x;
+    part[threadIdx.x].y += v.y;
     __syncthreads();
   }
-  int run = part[threadIdx.x] - tot_local;
+  int run = part[threadIdx.x].x - tot_local;
+  int crun = part[threadIdx.x].y - chunks_local;
+  int *co = s.chunk_off ? s.chunk_off + (int64_t)h * s.co_hs : nullptr;
   for (int c = cb; c < ce; ++c) {
     const int v = seg[c];
     seg[c] = run;
     for (int g = 0; g < ng; ++g) grp[(int64_t)g * s.mcap + c] += run;
     run += v;
+    if (co) {
+      co[c] = crun;
+      crun += (v + UPD_CHUNK - 1) / UPD_CHUNK;
+    }
   }
+  if (co && threadIdx.x == 1023) co[max(m, 0)] = part[1023].y;
   for (int c = m + threadIdx.x; c <= s.segcap; c += 1024) seg[c] = max(n, 0);
   if (n <= 0)
     for (int c = threadIdx.x; c <= s.segcap; c += 1024) seg[c] = 0;
@@ -460,36 +471,11 @@ __global__ __launch_bounds__(64) void k_sort_scatter(SortArgs s) {
 
 // ---------------------------------------------------------------------------
 // Lloyd update as a chunked segmented reduction over the counting-sort order:
-// every cluster is cut into chunks of UPD_CHUNK members; one block sums one
+// every cluster is cut into chunks of UPD_CHUNK members (their offsets come
+// from the sort's label scan); one block sums one
 // chunk in fp64 (16 lanes per row, fixed order), a second kernel adds a
 // cluster's chunk sums in order and divides.  An empty cluster keeps its
 // centre.  The new centre's GEMM operands are written in the same pass.
-__global__ __launch_bounds__(1024) void k_chunk_scan(SortArgs s, int *__restrict__ chunk_off, int64_t co_hs) {
-  const int h = blockIdx.x;
-  const int m = s.m[h];
-  const int *seg = s.seg + (int64_t)h * s.seg_hs;
-  int *co = chunk_off + (int64_t)h * co_hs;
-  __shared__ int part[1024];
-  const int per = (m + 1023) / 1024;
-  const int cb = min(m, (int)threadIdx.x * per), ce = min(m, cb + per);
-  int loc = 0;
-  for (int c = cb; c < ce; ++c) loc += (seg[c + 1] - seg[c] + UPD_CHUNK - 1) / UPD_CHUNK;
-  part[threadIdx.x] = loc;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
-  }
-  int run = part[threadIdx.x] - loc;
-  for (int c = cb; c < ce; ++c) {
-    co[c] = run;
-    run += (seg[c + 1] - seg[c] + UPD_CHUNK - 1) / UPD_CHUNK;
-  }
-  if (threadIdx.x == 1023) co[max(m, 0)] = part[1023];
-}
-
 template <int D>
 __global__ __launch_bounds__(256) void k_update_partial(KmArgs a, SortArgs s, const int *__restrict__ chunk_off,
                                                         int64_t co_hs, double *__restrict__ partial, int64_t part_hs) {
@@ -993,8 +979,9 @@ void launch_sort(const SortArgs &s, int BH, int nmax_pts, hipStream_t st) {
 }
 
 void launch_update(int D, const KmArgs &a, const SortArgs &s, const CentOps &op, int BH, int mmax, int npts,
-                   int *chunk_off, int64_t co_hs, double *partial, int64_t part_hs, hipStream_t st) {
-  hipLaunchKernelGGL(k_chunk_scan, dim3(BH), dim3(1024), 0, st, s, chunk_off, co_hs);
+                   double *partial, int64_t part_hs, hipStream_t st) {
+  const int *chunk_off = s.chunk_off;  // written by the label scan of the sort
+  const int64_t co_hs = s.co_hs;
   const int items = (npts + UPD_CHUNK - 1) / UPD_CHUNK + mmax;
   AC_D_DISPATCH(D, hipLaunchKernelGGL(k_update_partial<DD>, g2(items, BH), dim3(256), 0, st, a, s, chunk_off, co_hs,
                                       partial, part_hs));

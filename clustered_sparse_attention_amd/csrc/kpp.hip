@@ -276,11 +276,19 @@ __global__ __launch_bounds__(256) void k_kpp_gram(KmArgs a, int init_sample, con
 // wave scans of the per-thread sums, the wave totals in order through LDS,
 // and the one lane whose range holds u * total finds the point.  Two barriers
 // a round; the row of G of the new centre is then read straight into the
-// registers (each thread its cs contiguous entries).
-constexpr int KPP_SEQ_CS = KPP_GRAM_MAX / KPP_THREADS;
+// registers (each thread its cs contiguous entries).  A round depends only on
+// the previous pick's row of G, so the picks wait in LDS and their centre
+// rows are copied out by the whole block every KPP_PICK_BUF rounds: the
+// dependent index and point loads of a copy stay off the chain of rounds.
+// 512 threads: fewer waves meet at each barrier than with 1024, while the
+// per-thread runs stay short (16 points at most); 256 and 1024 measured slower.
+constexpr int KPP_SEQ_THREADS = 512;
+constexpr int KPP_SEQ_WAVES = KPP_SEQ_THREADS / 64;
+constexpr int KPP_SEQ_CS = KPP_GRAM_MAX / KPP_SEQ_THREADS;
+constexpr int KPP_PICK_BUF = 1024;
 
 template <int D>
-__global__ __launch_bounds__(KPP_THREADS) void k_kpp_seq(KmArgs a, const double *__restrict__ G, int smax,
+__global__ __launch_bounds__(KPP_SEQ_THREADS) void k_kpp_seq(KmArgs a, const double *__restrict__ G, int smax,
                                                         int init_sample, uint64_t seed, int role, int stage) {
   const int h = blockIdx.x;
   const int n = a.n[h], m = a.m[h];
@@ -292,9 +300,10 @@ __global__ __launch_bounds__(KPP_THREADS) void k_kpp_seq(KmArgs a, const double 
   float *cent = a.cent + (int64_t)h * a.cent_hs + (int64_t)a.coff[h] * D;
   const uint64_t sid = stream_id((uint64_t)h, role, stage);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ double sh_wt[KPP_WAVES];
+  __shared__ double sh_wt[KPP_SEQ_WAVES];
   __shared__ int sh_pick[2];
-  const int cs = (s + KPP_THREADS - 1) / KPP_THREADS;
+  __shared__ int sh_row[KPP_PICK_BUF];  // picks t0 + [0, KPP_PICK_BUF) not yet copied out
+  const int cs = (s + KPP_SEQ_THREADS - 1) / KPP_SEQ_THREADS;
   const int cb = min(s, tid * cs), ne = min(s, cb + cs) - cb;  // this thread's points
   double d2[KPP_SEQ_CS];
   auto take_row = [&](int pj, bool first) {
@@ -303,19 +312,26 @@ __global__ __launch_bounds__(KPP_THREADS) void k_kpp_seq(KmArgs a, const double 
     for (int e = 0; e < KPP_SEQ_CS; ++e)
       if (e < ne) d2[e] = first ? gr[e] : fmin(d2[e], gr[e]);
   };
-  auto put_centre = [&](int t, int pj) {
-    if (tid < D) {
-      const int li = (int)(((int64_t)pj * n) / s);
-      const int64_t row = idx ? (int64_t)idx[li] : (int64_t)li;
-      cent[(int64_t)t * D + tid] = bf2f(X[row * D + tid]);
+  // centres t0 + [0, cnt) from their subsample picks; called by the whole block
+  auto put_centres = [&](int t0, int cnt) {
+    __syncthreads();
+    for (int q = tid; q < cnt; q += KPP_SEQ_THREADS) {
+      const int li = (int)(((int64_t)sh_row[q] * n) / s);
+      sh_row[q] = idx ? idx[li] : li;
     }
+    __syncthreads();
+    for (int q = tid; q < cnt * D; q += KPP_SEQ_THREADS) {
+      const int tt = q / D, e = q % D;
+      cent[(int64_t)(t0 + tt) * D + e] = bf2f(X[(int64_t)sh_row[tt] * D + e]);
+    }
+    __syncthreads();
   };
 #pragma unroll
   for (int e = 0; e < KPP_SEQ_CS; ++e) d2[e] = 0.0;
   {
     const double u = uniform01(seed, sid, 0);
     const int pj = min(s - 1, (int)(u * (double)s));
-    put_centre(0, pj);
+    if (tid == 0) sh_row[0] = pj;
     take_row(pj, true);
   }
   for (int t = 1; t < m; ++t) {
@@ -336,7 +352,7 @@ __global__ __launch_bounds__(KPP_THREADS) void k_kpp_seq(KmArgs a, const double 
     __syncthreads();
     double off = 0.0, total = 0.0;
 #pragma unroll
-    for (int w = 0; w < KPP_WAVES; ++w) {
+    for (int w = 0; w < KPP_SEQ_WAVES; ++w) {
       const double v = sh_wt[w];
       if (w < wave) off += v;
       total += v;
@@ -363,9 +379,11 @@ __global__ __launch_bounds__(KPP_THREADS) void k_kpp_seq(KmArgs a, const double 
     int pj = sh_pick[t & 1];
     if (total <= 0.0) pj = min(s - 1, (int)(u * (double)s));
     else if (pj < 0) pj = s - 1;  // u * total at the very top (rounding)
-    put_centre(t, pj);
+    if (tid == 0) sh_row[t % KPP_PICK_BUF] = pj;
     take_row(pj, false);
+    if ((t + 1) % KPP_PICK_BUF == 0) put_centres(t + 1 - KPP_PICK_BUF, KPP_PICK_BUF);
   }
+  if (m % KPP_PICK_BUF != 0) put_centres(m - m % KPP_PICK_BUF, m % KPP_PICK_BUF);
 }
 
 void launch_kpp(int D, const KmArgs &a, int BH, double *d2buf, int init_sample, uint64_t seed, int role, int stage,
@@ -382,11 +400,11 @@ void launch_kpp_gram(int D, const KmArgs &a, int BH, int smax, double *nx, doubl
   if (D == 64) {
     hipLaunchKernelGGL(k_kpp_norms<64>, dim3((smax + 15) / 16, BH), dim3(64), 0, st, a, init_sample, nx, smax);
     hipLaunchKernelGGL(k_kpp_gram<64>, dim3(nt * nt, BH), dim3(256), 0, st, a, init_sample, nx, G, smax);
-    hipLaunchKernelGGL(k_kpp_seq<64>, dim3(BH), dim3(KPP_THREADS), 0, st, a, G, smax, init_sample, seed, role, stage);
+    hipLaunchKernelGGL(k_kpp_seq<64>, dim3(BH), dim3(KPP_SEQ_THREADS), 0, st, a, G, smax, init_sample, seed, role, stage);
   } else {
     hipLaunchKernelGGL(k_kpp_norms<128>, dim3((smax + 15) / 16, BH), dim3(64), 0, st, a, init_sample, nx, smax);
     hipLaunchKernelGGL(k_kpp_gram<128>, dim3(nt * nt, BH), dim3(256), 0, st, a, init_sample, nx, G, smax);
-    hipLaunchKernelGGL(k_kpp_seq<128>, dim3(BH), dim3(KPP_THREADS), 0, st, a, G, smax, init_sample, seed, role, stage);
+    hipLaunchKernelGGL(k_kpp_seq<128>, dim3(BH), dim3(KPP_SEQ_THREADS), 0, st, a, G, smax, init_sample, seed, role, stage);
   }
 }
 
