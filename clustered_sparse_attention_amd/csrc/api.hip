@@ -154,9 +154,9 @@ Plan make_plan(const ac_shape *s, const ac_params *p) {
     S.ops_hi = take(BH * S.mcap * D * 2);
     S.ops_lo = take(BH * S.mcap * D * 2);
     S.ops_norm = take(BH * S.mcap * 4);
-    S.hn = take(BH * 4);
-    S.hm = take(BH * 4);
-    S.hcoff = take(BH * 4);
+    S.hn = take(3 * (size_t)BH * 4);  // n, m and centre offsets back to back: one copy per stage
+    S.hm = S.hn + BH * 4;
+    S.hcoff = S.hn + 2 * (size_t)BH * 4;
     S.chunk_off = take(BH * (S.mcap + 1) * 4);
     S.chg = take(2 * BH * 4);
     S.neff = take(BH * 4);
@@ -398,7 +398,8 @@ ac_status do_cluster_k_cold(const Plan &P, const ac_params *p, const uint16_t *K
                             ac_clusters *k, ac_kstats *stats, void *ws, hipStream_t st) {
   const int BH = P.BH, L = P.L, D = P.D;
   Engine E{P, P.sk, ws, st};
-  std::vector<int> nU(BH, L), nC(BH, 0), done(BH, 0), F(BH, 0), stg(BH, 0), hn(BH), hm(BH), hc(BH);
+  std::vector<int> nU(BH, L), nC(BH, 0), done(BH, 0), F(BH, 0), stg(BH, 0), nmc(3 * (size_t)BH);
+  int *hn = nmc.data(), *hm = hn + BH, *hc = hn + 2 * BH;
   int *uidx[2] = {at<int>(ws, P.uidx0), at<int>(ws, P.uidx1)};
   int cur = 0;
   float *dist = at<float>(ws, P.dist);
@@ -416,9 +417,7 @@ ac_status do_cluster_k_cold(const Plan &P, const ac_params *p, const uint16_t *K
       nmaxpts = std::max(nmaxpts, hn[h]);
     }
     if (!active) break;
-    AC_HIP(hipMemcpyAsync(E.n(), hn.data(), BH * 4, hipMemcpyHostToDevice, st));
-    AC_HIP(hipMemcpyAsync(E.m(), hm.data(), BH * 4, hipMemcpyHostToDevice, st));
-    AC_HIP(hipMemcpyAsync(E.coff(), hc.data(), BH * 4, hipMemcpyHostToDevice, st));
+    AC_HIP(hipMemcpyAsync(E.n(), nmc.data(), 3 * (size_t)BH * 4, hipMemcpyHostToDevice, st));
     KmArgs a{K, (int64_t)L * D, t == 0 ? nullptr : uidx[cur], L, E.n(), E.m(), E.coff(), k->cent,
              (int64_t)k->ncap * D};
     int *lab = at<int>(ws, E.S.lab);
