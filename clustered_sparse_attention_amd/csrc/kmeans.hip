@@ -376,8 +376,8 @@ __global__ __launch_bounds__(256) void k_sort_gscan(SortArgs s) {
   s.grp[((int64_t)h * s.max_groups + g) * s.mcap + c] = run;
 }
 
-// Per head: scan each label over the groups, then the label totals; grp
-// ends up holding the first output position of (group, label).  With
+// Per head: each label's total over the groups, a scan of the label totals,
+// then grp is rewritten to the first output position of (group, label).  With
 // chunk_off set, the chunk counts of the centre update are scanned beside the
 // label totals.
 __global__ __launch_bounds__(1024) void k_sort_scan(SortArgs s) {
@@ -387,45 +387,69 @@ __global__ __launch_bounds__(1024) void k_sort_scan(SortArgs s) {
   const int nt = (n + SORT_TILE - 1) / SORT_TILE;
   const int ng = (nt + SORT_GROUP - 1) / SORT_GROUP;
   int *grp = s.grp + (int64_t)h * s.max_groups * s.mcap;
-  __shared__ int2 part[1024];
+  __shared__ int2 part[16];  // wave totals
   const int per = (m + 1023) / 1024;
   const int cb = min(m, (int)threadIdx.x * per), ce = min(m, cb + per);
+  // a label's group counts are read SCAN_BATCH at a time, so the loads of a
+  // batch are in flight together
+  constexpr int SCAN_BATCH = 8;
   int tot_local = 0, chunks_local = 0;
   for (int c = cb; c < ce; ++c) {
     int run = 0;
-    for (int g = 0; g < ng; ++g) {
-      int *q = grp + (int64_t)g * s.mcap + c;
-      const int v = *q;
-      *q = run;
-      run += v;
+    for (int g0 = 0; g0 < ng; g0 += SCAN_BATCH) {
+      int v[SCAN_BATCH];
+#pragma unroll
+      for (int j = 0; j < SCAN_BATCH; ++j) v[j] = g0 + j < ng ? grp[(int64_t)(g0 + j) * s.mcap + c] : 0;
+#pragma unroll
+      for (int j = 0; j < SCAN_BATCH; ++j) run += v[j];
     }
     seg[c] = run;  // count for now
     tot_local += run;
     chunks_local += (run + UPD_CHUNK - 1) / UPD_CHUNK;
   }
-  part[threadIdx.x] = make_int2(tot_local, chunks_local);
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int2 v = threadIdx.x >= off ? part[threadIdx.x - off] : make_int2(0, 0);
-    __syncthreads();
-    part[threadIdx.x].x += v.x;
-    part[threadIdx.x].y += v.y;
-    __syncthreads();
+  // exclusive scan of both counts over the threads: wave scans, then the
+  // wave totals through LDS (integer sums, so the order is immaterial)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int ix = tot_local, iy = chunks_local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_up(ix, o, 64), y = __shfl_up(iy, o, 64);
+    if (lane >= o) { ix += x; iy += y; }
   }
-  int run = part[threadIdx.x].x - tot_local;
-  int crun = part[threadIdx.x].y - chunks_local;
+  if (lane == 63) part[wave] = make_int2(ix, iy);
+  __syncthreads();
+  int ox = 0, oy = 0, ty = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const int2 t = part[w];
+    if (w < wave) { ox += t.x; oy += t.y; }
+    ty += t.y;
+  }
+  int run = ox + ix - tot_local;
+  int crun = oy + iy - chunks_local;
   int *co = s.chunk_off ? s.chunk_off + (int64_t)h * s.co_hs : nullptr;
   for (int c = cb; c < ce; ++c) {
     const int v = seg[c];
     seg[c] = run;
-    for (int g = 0; g < ng; ++g) grp[(int64_t)g * s.mcap + c] += run;
+    int pos = run;  // first output position of (group, label c)
+    for (int g0 = 0; g0 < ng; g0 += SCAN_BATCH) {
+      int w[SCAN_BATCH];
+#pragma unroll
+      for (int j = 0; j < SCAN_BATCH; ++j) w[j] = g0 + j < ng ? grp[(int64_t)(g0 + j) * s.mcap + c] : 0;
+#pragma unroll
+      for (int j = 0; j < SCAN_BATCH; ++j)
+        if (g0 + j < ng) {
+          grp[(int64_t)(g0 + j) * s.mcap + c] = pos;
+          pos += w[j];
+        }
+    }
     run += v;
     if (co) {
       co[c] = crun;
       crun += (v + UPD_CHUNK - 1) / UPD_CHUNK;
     }
   }
-  if (co && threadIdx.x == 1023) co[max(m, 0)] = part[1023].y;
+  if (co && threadIdx.x == 1023) co[max(m, 0)] = ty;
   for (int c = m + threadIdx.x; c <= s.segcap; c += 1024) seg[c] = max(n, 0);
   if (n <= 0)
     for (int c = threadIdx.x; c <= s.segcap; c += 1024) seg[c] = 0;
