@@ -8,7 +8,7 @@ namespace ac {
 
 constexpr int KPP_SMAX = 16384;  // most points a k-means++ subsample may hold
 constexpr int KPP_GRAM_MAX = 8192;  // subsamples up to this size seed from a distance matrix
-constexpr int SORT_TILE = 128;   // points per counting-sort tile (one wave)
+constexpr int SORT_TILE = 256;   // points per counting-sort tile (one wave)
 constexpr int SORT_GROUP = 32;   // tiles per group in the two-level scan over tiles
 constexpr int ATT_QT = 256;      // query rows per attention block at d = 128 (8 waves)
 constexpr int ATT_QT64 = 384;    // at d = 64: 12 waves, three per SIMD fit its registers
