@@ -598,36 +598,59 @@ __global__ __launch_bounds__(128) void k_update_final(KmArgs a, SortArgs s, cons
 
 // ---------------------------------------------------------------------------
 // Distance of each point of a stage to its own centre, ||x - c(x)|| (fp64
-// accumulation, stored fp32).  16 lanes per point, 16 points per block.
+// accumulation, stored fp32).  16 lanes per point; a block takes 16 * SD_PTS
+// points and issues the index, label, row and centre loads of all of them
+// before the arithmetic, so the two levels of dependent loads overlap.
+constexpr int SD_PTS = 4;
+
 template <int D>
 __global__ __launch_bounds__(256) void k_stage_dist(KmArgs a, const int *__restrict__ labels, int64_t lab_hs,
                                                     float *__restrict__ dist, int64_t dist_hs) {
   constexpr int PL = D / 16;
   typedef uint32_t pw_t __attribute__((ext_vector_type(PL / 2)));
+  typedef float pf_t __attribute__((ext_vector_type(PL)));
   const int h = blockIdx.y;
   const int n = a.n[h];
-  const int i = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int i0 = blockIdx.x * (16 * SD_PTS) + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
-  if (blockIdx.x * 16 >= n || a.m[h] <= 0) return;
-  double acc = 0.0;
-  if (i < n) {
-    const uint16_t *X = a.X + (int64_t)h * a.x_hs;
-    const int64_t row = a.idx ? (int64_t)a.idx[(int64_t)h * a.idx_hs + i] : (int64_t)i;
-    const int c = labels[(int64_t)h * lab_hs + i];
-    const float *cr = a.cent + (int64_t)h * a.cent_hs + (int64_t)(a.coff[h] + c) * D + sub * PL;
-    const pw_t xv = *(const pw_t *)(X + row * D + sub * PL);
+  if (blockIdx.x * (16 * SD_PTS) >= n || a.m[h] <= 0) return;
+  const uint16_t *X = a.X + (int64_t)h * a.x_hs;
+  const float *C = a.cent + (int64_t)h * a.cent_hs + (int64_t)a.coff[h] * D + sub * PL;
+  int64_t row[SD_PTS];
+  int c[SD_PTS];
 #pragma unroll
-    for (int q = 0; q < PL; ++q) {
-      const uint32_t w = xv[q >> 1];
-      const double df = (double)bf2f((uint16_t)((q & 1) ? (w >> 16) : (w & 0xFFFFu))) - (double)cr[q];
-      acc = fma(df, df, acc);
+  for (int j = 0; j < SD_PTS; ++j) {
+    const int i = i0 + 16 * j;
+    row[j] = i < n ? (a.idx ? (int64_t)a.idx[(int64_t)h * a.idx_hs + i] : (int64_t)i) : 0;
+    c[j] = i < n ? labels[(int64_t)h * lab_hs + i] : 0;
+  }
+  pw_t xv[SD_PTS];
+  pf_t cv[SD_PTS];
+#pragma unroll
+  for (int j = 0; j < SD_PTS; ++j) {
+    if (i0 + 16 * j < n) {
+      xv[j] = *(const pw_t *)(X + row[j] * D + sub * PL);
+      cv[j] = *(const pf_t *)(C + (int64_t)c[j] * D);
     }
   }
-  acc += __shfl_xor(acc, 1, 64);
-  acc += __shfl_xor(acc, 2, 64);
-  acc += __shfl_xor(acc, 4, 64);
-  acc += __shfl_xor(acc, 8, 64);
-  if (i < n && sub == 0) dist[(int64_t)h * dist_hs + i] = (float)sqrt(acc);
+#pragma unroll
+  for (int j = 0; j < SD_PTS; ++j) {
+    const int i = i0 + 16 * j;
+    double acc = 0.0;
+    if (i < n) {
+#pragma unroll
+      for (int q = 0; q < PL; ++q) {
+        const uint32_t w = xv[j][q >> 1];
+        const double df = (double)bf2f((uint16_t)((q & 1) ? (w >> 16) : (w & 0xFFFFu))) - (double)cv[j][q];
+        acc = fma(df, df, acc);
+      }
+    }
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    acc += __shfl_xor(acc, 4, 64);
+    acc += __shfl_xor(acc, 8, 64);
+    if (i < n && sub == 0) dist[(int64_t)h * dist_hs + i] = (float)sqrt(acc);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1016,8 +1039,8 @@ void launch_update(int D, const KmArgs &a, const SortArgs &s, const CentOps &op,
 
 void launch_stage_dist(int D, const KmArgs &a, int BH, int nmax_pts, const int *labels, int64_t lab_hs, float *dist,
                        int64_t dist_hs, hipStream_t st) {
-  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_stage_dist<DD>, g2((nmax_pts + 15) / 16, BH), dim3(256), 0, st, a, labels,
-                                      lab_hs, dist, dist_hs));
+  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_stage_dist<DD>, g2((nmax_pts + 16 * SD_PTS - 1) / (16 * SD_PTS), BH), dim3(256),
+                                      0, st, a, labels, lab_hs, dist, dist_hs));
 }
 
 void launch_tau(const float *dist, int64_t dist_hs, const int *n_arr, int BH, int nmax_pts, int rule, float param,
