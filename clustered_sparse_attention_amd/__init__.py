@@ -22,7 +22,8 @@ AC_SCORE_QUEST, AC_SCORE_MEAN = range(2)
 AC_SEL_TOPK, AC_SEL_DENSITY, AC_SEL_TOPP, AC_SEL_DENSE = range(4)
 AC_QUEST_MFMA, AC_QUEST_VALU = range(2)
 
-ENTRY_POINTS = ("ac_params_default", "ac_sizes", "ac_cluster_q", "ac_cluster_k", "ac_score_select",
+ENTRY_POINTS = ("ac_params_default", "ac_sizes", "ac_cluster_q", "ac_cluster_k", "ac_cluster_k_trace",
+                "ac_cluster_q_trace", "ac_score_select",
                 "ac_sparse_attn", "ac_tail_merge", "ac_score_tokens", "ac_interaction_matrix",
                 "ac_cluster_k_metric", "ac_layer", "ac_topp_schedule",
                 "ac_kmax_calibrate", "ac_step_params", "ac_status_str", "ac_last_error")
@@ -48,7 +49,7 @@ class Params(ctypes.Structure):
                 ("tau_param", ctypes.c_float), ("score_mode", ctypes.c_int32), ("sel_mode", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("sel_param", ctypes.c_float), ("compensate", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("init_sample", ctypes.c_int32), ("tail_block", ctypes.c_int32),
-                ("reserved0", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+                ("min_sparse_gflop", ctypes.c_int32), ("seed", ctypes.c_uint64)]
 
 
 class CClusters(ctypes.Structure):
@@ -59,6 +60,11 @@ class CClusters(ctypes.Structure):
 class CKStats(ctypes.Structure):
     _fields_ = [("kmax", P), ("kmin", P), ("kmean", P), ("vmean", P), ("fallback", P), ("tau", P), ("mse", P),
                 ("stages", P)]
+
+
+class CKTrace(ctypes.Structure):
+    _fields_ = [("max_stages", ctypes.c_int32), ("n", P), ("m", P), ("u", P), ("cent", P), ("labels", P),
+                ("dist", P)]
 
 
 class CSelection(ctypes.Structure):
@@ -102,6 +108,13 @@ def load() -> ctypes.CDLL:
     lib.ac_cluster_k.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), vp, vp, ctypes.POINTER(CState),
                                  ctypes.POINTER(CClusters), ctypes.POINTER(CKStats), vp, ctypes.c_size_t, vp]
     lib.ac_cluster_k.restype = st
+    lib.ac_cluster_k_trace.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), vp, vp,
+                                       ctypes.POINTER(CClusters), ctypes.POINTER(CKStats), ctypes.POINTER(CKTrace),
+                                       vp, ctypes.c_size_t, vp]
+    lib.ac_cluster_k_trace.restype = st
+    lib.ac_cluster_q_trace.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), vp, ctypes.POINTER(CClusters),
+                                       vp, vp, ctypes.c_size_t, vp]
+    lib.ac_cluster_q_trace.restype = st
     lib.ac_score_select.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), ctypes.POINTER(CClusters),
                                     ctypes.POINTER(CClusters), ctypes.POINTER(CKStats), ctypes.POINTER(CSelection),
                                     vp, ctypes.c_size_t, vp]
@@ -219,6 +232,25 @@ class KStats:
                        _ptr(self.tau), _ptr(self.mse), _ptr(self.stages))
 
 
+class KTrace:
+    """Device arrays of a key-clustering stage record (see ac_ktrace)."""
+
+    def __init__(self, BH: int, L: int, max_stages: int, iters: int, m0: int, d: int, device):
+        import torch
+        i32 = torch.int32
+        self.max_stages = max_stages
+        self.n = torch.zeros((BH, max_stages), dtype=i32, device=device)
+        self.m = torch.zeros((BH, max_stages), dtype=i32, device=device)
+        self.u = torch.full((BH, max_stages, L), -1, dtype=i32, device=device)
+        self.cent = torch.zeros((BH, max_stages, iters + 1, m0, d), dtype=torch.float32, device=device)
+        self.labels = torch.full((BH, max_stages, L), -1, dtype=i32, device=device)
+        self.dist = torch.zeros((BH, max_stages, L), dtype=torch.float32, device=device)
+
+    def c(self) -> CKTrace:
+        return CKTrace(self.max_stages, _ptr(self.n), _ptr(self.m), _ptr(self.u), _ptr(self.cent),
+                       _ptr(self.labels), _ptr(self.dist))
+
+
 class Selection:
     def __init__(self, BH: int, nq: int, ncap_k: int, device, score: bool = True):
         import torch
@@ -270,6 +302,18 @@ def ac_cluster_k(shape, params, K, V, warm: Optional[State], k_out: Clusters, st
     _check(load().ac_cluster_k(ctypes.byref(shape), ctypes.byref(params), _ptr(K), _ptr(V), wc,
                                ctypes.byref(k_out.c()), ctypes.byref(stats.c()), _ptr(ws), ws.numel(),
                                _stream(stream)))
+
+
+def ac_cluster_k_trace(shape, params, K, V, k_out: Clusters, stats: KStats, trace: KTrace, ws, stream=None):
+    _check(load().ac_cluster_k_trace(ctypes.byref(shape), ctypes.byref(params), _ptr(K), _ptr(V),
+                                     ctypes.byref(k_out.c()), ctypes.byref(stats.c()), ctypes.byref(trace.c()),
+                                     _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def ac_cluster_q_trace(shape, params, Q, q_out: Clusters, cent_trace, ws, stream=None):
+    """cent_trace: [BH, iters + 1, q_out.ncap, d] float32."""
+    _check(load().ac_cluster_q_trace(ctypes.byref(shape), ctypes.byref(params), _ptr(Q), ctypes.byref(q_out.c()),
+                                     _ptr(cent_trace), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def ac_score_select(shape, params, q: Clusters, k: Clusters, stats: KStats, sel: Selection, ws, stream=None):

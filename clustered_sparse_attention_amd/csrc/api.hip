@@ -58,6 +58,9 @@ ac_status check_shape(const ac_shape *s) {
   if (s->d != 64 && s->d != 128) return fail(AC_E_UNSUPPORTED, "d = %d: only 64 and 128 are supported", s->d);
   if ((int64_t)s->B * s->H > (1 << 20)) return fail(AC_E_SHAPE, "B*H too large");
   if ((int64_t)s->L > (1 << 26)) return fail(AC_E_SHAPE, "L too large");
+  // the attention's row gathers address one head's K and V with 32-bit byte offsets
+  if ((int64_t)s->L * s->d * 2 >= (int64_t)1 << 32)
+    return fail(AC_E_UNSUPPORTED, "L = %d: one head's rows (L * d * 2 bytes) must stay below 4 GiB", s->L);
   return AC_OK;
 }
 
@@ -82,7 +85,7 @@ ac_status check_params(const ac_shape *s, const ac_params *p) {
   if (!(p->scale >= 0.f) || !std::isfinite(p->scale)) return fail(AC_E_ARG, "scale must be finite and >= 0");
   if (p->init_sample < 0) return fail(AC_E_ARG, "init_sample must be >= 0");
   if (p->tail_block < 0) return fail(AC_E_ARG, "tail_block must be >= 0");
-  if (p->reserved0 != 0) return fail(AC_E_ARG, "reserved0 must be 0");
+  if (p->min_sparse_gflop < 0) return fail(AC_E_ARG, "min_sparse_gflop must be >= 0");
   const int64_t ncap = (int64_t)p->nmax - 1 + p->m0;
   if (ncap > SEL_MAXN) return fail(AC_E_UNSUPPORTED, "nmax - 1 + m0 = %lld exceeds %d key clusters", (long long)ncap, SEL_MAXN);
   const int64_t mmax = std::max<int64_t>(std::min<int64_t>(p->nq, s->L), std::min<int64_t>(p->m0, s->L));
@@ -250,6 +253,12 @@ ac_status check_device() {
 
 float attn_scale(const ac_params *p, int D) { return p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)D); }
 
+// Record of a k-means job's centres (see Engine::run): head stride hs, slot stride it.
+struct TraceCent {
+  float *p = nullptr;
+  int64_t hs = 0, it = 0;
+};
+
 // ---------------------------------------------------------------------------
 // the k-means engine: optional k-means++ seeding, iters Lloyd iterations,
 // and a final assignment into labels_out.
@@ -288,9 +297,14 @@ struct Engine {
   // mmax: bound on m over heads (grid size); npts: bound on n.
   // metric: NULL for Euclidean distances, else [BH, D, D] fp32: the assignment
   // minimises (x - c) M (x - c)^T (centre operands M c and c M c^T)
+  // tc (optional): record of the centres after seeding (slot 0) and after each
+  // Lloyd update (slot j), head stride tc.hs, slot stride tc.it
   ac_status run(const KmArgs &a, int mmax, int npts, bool seed_init, int iters, const ac_params *p, int role,
-                int stage, int *labels_out, const float *metric = nullptr) {
+                int stage, int *labels_out, const float *metric = nullptr, TraceCent tc = TraceCent()) {
     const int D = P.D;
+    auto trace = [&](int slot) {
+      if (tc.p) launch_trace_cent(D, a, P.BH, mmax, tc.p + slot * tc.it, tc.hs, st);
+    };
     if (seed_init) {
       if (S.kpp_smax <= KPP_GRAM_MAX)
         launch_kpp_gram(D, a, P.BH, S.kpp_smax, at<double>(ws, S.kpp_nx), at<double>(ws, S.kpp_G), p->init_sample,
@@ -299,6 +313,7 @@ struct Engine {
         launch_kpp(D, a, P.BH, at<double>(ws, S.d2buf), p->init_sample, p->seed, role, stage, st);
       AC_CHECK_LAUNCH();
     }
+    trace(0);
     CentOps op = ops();
     launch_cent_prep(D, a, op, P.BH, mmax, st);
     if (metric) launch_cent_prep_metric(D, a, op, metric, P.BH, mmax, st);
@@ -332,6 +347,7 @@ struct Engine {
       launch_sort(s, P.BH, npts, st);
       launch_update(D, al, s, op, P.BH, mmax, npts, at<double>(ws, S.upd_part), (int64_t)S.upd_items * D, st);
       if (metric) launch_cent_prep_metric(D, a, op, metric, P.BH, mmax, st);
+      trace(it + 1);
       AC_CHECK_LAUNCH();
     }
     if (iters > 0) {
@@ -347,7 +363,7 @@ struct Engine {
 
 // ---------------------------------------------------------------------------
 ac_status do_cluster_q(const Plan &P, const ac_params *p, const uint16_t *Q, const float *warm_cent,
-                       ac_clusters *q, void *ws, hipStream_t st) {
+                       ac_clusters *q, void *ws, hipStream_t st, float *cent_trace = nullptr) {
   const int BH = P.BH, L = P.L, D = P.D;
   Engine E{P, P.sq, ws, st};
   uint16_t *qhat = at<uint16_t>(ws, P.qhat);
@@ -365,7 +381,14 @@ ac_status do_cluster_q(const Plan &P, const ac_params *p, const uint16_t *Q, con
                             (size_t)P.nq * D * 4, hipMemcpyDeviceToDevice, st));
   }
   KmArgs a{qhat, (int64_t)L * D, nullptr, 0, E.n(), E.m(), E.coff(), q->cent, (int64_t)q->ncap * D};
-  AC_TRY(E.run(a, P.nq, L, warm_cent == nullptr, warm_cent ? p->iters_warm : p->iters, p, 0, 0, q->labels));
+  TraceCent tc;
+  if (cent_trace) {
+    tc.p = cent_trace;
+    tc.it = (int64_t)q->ncap * D;
+    tc.hs = (int64_t)(p->iters + 1) * tc.it;
+  }
+  AC_TRY(E.run(a, P.nq, L, warm_cent == nullptr, warm_cent ? p->iters_warm : p->iters, p, 0, 0, q->labels, nullptr,
+               tc));
   SortArgs s = E.sort_args(q->labels, q->perm, q->seg, q->ncap, P.nq);
   launch_sort(s, BH, L, st);
   launch_seg_mean(qn, q->perm, q->seg, L, q->ncap, q->ncl, q->rho, BH, st);
@@ -395,7 +418,8 @@ ac_status finish_keys(const Plan &P, const uint16_t *K, const uint16_t *V, ac_cl
 }
 
 ac_status do_cluster_k_cold(const Plan &P, const ac_params *p, const uint16_t *K, const uint16_t *V,
-                            ac_clusters *k, ac_kstats *stats, void *ws, hipStream_t st) {
+                            ac_clusters *k, ac_kstats *stats, void *ws, hipStream_t st,
+                            const ac_ktrace *tr = nullptr) {
   const int BH = P.BH, L = P.L, D = P.D;
   Engine E{P, P.sk, ws, st};
   std::vector<int> nU(BH, L), nC(BH, 0), done(BH, 0), F(BH, 0), stg(BH, 0), nmc(3 * (size_t)BH);
@@ -421,8 +445,23 @@ ac_status do_cluster_k_cold(const Plan &P, const ac_params *p, const uint16_t *K
     KmArgs a{K, (int64_t)L * D, t == 0 ? nullptr : uidx[cur], L, E.n(), E.m(), E.coff(), k->cent,
              (int64_t)k->ncap * D};
     int *lab = at<int>(ws, E.S.lab);
-    AC_TRY(E.run(a, mmax, nmaxpts, true, p->iters, p, 1, t, lab));
+    const bool rec = tr && t < tr->max_stages;
+    TraceCent tc;
+    if (rec && tr->cent) {
+      tc.it = (int64_t)p->m0 * D;
+      const int64_t stage_stride = (int64_t)(p->iters + 1) * tc.it;
+      tc.hs = (int64_t)tr->max_stages * stage_stride;
+      tc.p = tr->cent + t * stage_stride;
+    }
+    if (rec) launch_trace_nm(E.n(), E.m(), tr->n, tr->m, tr->max_stages, t, BH, st);
+    AC_TRY(E.run(a, mmax, nmaxpts, true, p->iters, p, 1, t, lab, nullptr, tc));
     launch_stage_dist(D, a, BH, nmaxpts, lab, L, dist, L, st);
+    if (rec && (tr->u || tr->labels || tr->dist)) {
+      const int64_t ohs = (int64_t)tr->max_stages * L, oo = (int64_t)t * L;
+      launch_trace_stage(E.n(), t == 0 ? nullptr : uidx[cur], L, lab, dist, L, tr->u ? tr->u + oo : nullptr,
+                         tr->labels ? tr->labels + oo : nullptr, tr->dist ? tr->dist + oo : nullptr, ohs, BH,
+                         nmaxpts, st);
+    }
     if (t == 0)
       launch_tau(dist, L, E.n(), BH, nmaxpts, p->tau_rule, p->tau_param, stats->tau, at<uint32_t>(ws, P.rstate),
                  at<uint32_t>(ws, P.rhist), st);
@@ -703,6 +742,35 @@ AC_API ac_status ac_cluster_k(const ac_shape *s, const ac_params *p, const uint1
   return do_cluster_k_cold(P, p, K, V, k_out, stats, ws, (hipStream_t)stream);
 }
 
+AC_API ac_status ac_cluster_k_trace(const ac_shape *s, const ac_params *p, const uint16_t *K, const uint16_t *V,
+                                    ac_clusters *k_out, ac_kstats *stats, const ac_ktrace *trace, void *ws,
+                                    size_t ws_bytes, ac_stream_t stream) {
+  AC_TRY(check_shape(s));
+  AC_TRY(check_params(s, p));
+  if (!K || !V) return fail(AC_E_ARG, "K or V is NULL");
+  if (!trace || trace->max_stages < 1) return fail(AC_E_ARG, "trace is NULL or max_stages < 1");
+  Plan P = make_plan(s, p);
+  AC_TRY(check_clusters(k_out, "key", P.ncapk, false));
+  if (k_out->ncap != P.ncapk) return fail(AC_E_ARG, "key clusters ncap must be %d", P.ncapk);
+  AC_TRY(check_kstats(stats));
+  AC_TRY(check_ws(P, ws, ws_bytes));
+  AC_TRY(check_device());
+  return do_cluster_k_cold(P, p, K, V, k_out, stats, ws, (hipStream_t)stream, trace);
+}
+
+AC_API ac_status ac_cluster_q_trace(const ac_shape *s, const ac_params *p, const uint16_t *Q, ac_clusters *q_out,
+                                    float *cent_trace, void *ws, size_t ws_bytes, ac_stream_t stream) {
+  AC_TRY(check_shape(s));
+  AC_TRY(check_params(s, p));
+  if (!Q || !cent_trace) return fail(AC_E_ARG, "Q or cent_trace is NULL");
+  Plan P = make_plan(s, p);
+  AC_TRY(check_clusters(q_out, "query", P.nq, true));
+  if (q_out->ncap != P.nq) return fail(AC_E_ARG, "query clusters ncap must be min(nq, L) = %d", P.nq);
+  AC_TRY(check_ws(P, ws, ws_bytes));
+  AC_TRY(check_device());
+  return do_cluster_q(P, p, Q, nullptr, q_out, ws, (hipStream_t)stream, cent_trace);
+}
+
 AC_API ac_status ac_score_select(const ac_shape *s, const ac_params *p, const ac_clusters *q, const ac_clusters *k,
                                  const ac_kstats *stats, ac_selection *sel, void *ws, size_t ws_bytes,
                                  ac_stream_t stream) {
@@ -869,7 +937,9 @@ AC_API ac_status ac_layer(const ac_shape *s, const ac_params *p, const uint16_t 
                at<uint8_t>(ws, P.fb), at<float>(ws, P.tau), at<float>(ws, P.mse), at<int>(ws, P.stages)};
   ac_selection sel{P.ncapk, at<int>(ws, P.sel_list), at<int>(ws, P.sel_n), at<uint32_t>(ws, P.sel_mask),
                    at<float>(ws, P.sel_score)};
-  if (p->sel_mode == AC_SEL_DENSE) {
+  const double dense_gflop = 4e-9 * (double)BH * (double)P.L * (double)P.L * (double)D;
+  const bool small = p->min_sparse_gflop > 0 && dense_gflop < (double)p->min_sparse_gflop;
+  if (p->sel_mode == AC_SEL_DENSE || small) {
     // dense attention only: no clustering, one query "cluster" of all tokens
     // per head, the state untouched (the next sparse call starts cold if it
     // is not valid)
@@ -877,7 +947,10 @@ AC_API ac_status ac_layer(const ac_shape *s, const ac_params *p, const uint16_t 
     launch_fill_i32(k.ncl, BH, 0, st);
     launch_fill_u8(ks.fallback, BH, 0, st);
     AC_CHECK_LAUNCH();
-    AC_TRY(do_attn(P, p, Q, K, V, &q, &k, &ks, &sel, O, nullptr, ws, st));
+    ac_params pd = *p;
+    pd.sel_mode = AC_SEL_DENSE;
+    pd.compensate = 0;
+    AC_TRY(do_attn(P, &pd, Q, K, V, &q, &k, &ks, &sel, O, nullptr, ws, st));
     if (host_stats) {
       AC_HIP(hipStreamSynchronize(st));
       for (int h = 0; h < BH; ++h) {

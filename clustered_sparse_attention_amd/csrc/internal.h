@@ -189,6 +189,11 @@ void launch_flag_removed(const float *dist, int64_t dist_hs, const int *n_arr, c
 void launch_compact_gather(const int *idx_old, int64_t idx_hs, const int *perm, int64_t perm_hs, const int *seg,
                            int64_t seg_hs, int *idx_new, int *n_new, int BH, int nmax_pts, hipStream_t st);
 void launch_kstats(int D, const KStatsArgs &s, int BH, hipStream_t st);
+// stage records of the traced entry points
+void launch_trace_cent(int D, const KmArgs &a, int BH, int mmax, float *dst, int64_t dst_hs, hipStream_t st);
+void launch_trace_stage(const int *n, const int *idx, int64_t idx_hs, const int *lab, const float *dist, int64_t hs,
+                        int *u_out, int *lab_out, float *dist_out, int64_t out_hs, int BH, int npts, hipStream_t st);
+void launch_trace_nm(const int *n, const int *m, int *n_out, int *m_out, int ld, int t, int BH, hipStream_t st);
 void launch_seg_mean(const float *val, const int *perm, const int *seg, int L, int ncap, const int *ncl, float *out,
                      int BH, hipStream_t st);
 void launch_fill_i32(int *p, int64_t n, int v, hipStream_t st);

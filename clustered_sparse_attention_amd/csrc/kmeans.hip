@@ -959,6 +959,38 @@ __global__ void k_set_m_min(int *__restrict__ m, const int *__restrict__ n, int 
 }
 
 // ---------------------------------------------------------------------------
+// Stage records of the traced entry points: copies only.
+// Centres of the job, m[h] rows from cent[h][coff[h]], into dst[h] (stride dst_hs).
+template <int D>
+__global__ __launch_bounds__(256) void k_trace_cent(KmArgs a, float *__restrict__ dst, int64_t dst_hs) {
+  const int h = blockIdx.y, c = blockIdx.x;
+  if (c >= a.m[h] || a.n[h] <= 0) return;
+  const float *src = a.cent + (int64_t)h * a.cent_hs + (int64_t)(a.coff[h] + c) * D;
+  for (int dd = threadIdx.x; dd < D; dd += 256) dst[(int64_t)h * dst_hs + (int64_t)c * D + dd] = src[dd];
+}
+// Point lists of a stage: key index, stage label and distance of the first n[h] points.
+__global__ void k_trace_stage(const int *__restrict__ n, const int *__restrict__ idx, int64_t idx_hs,
+                              const int *__restrict__ lab, const float *__restrict__ dist, int64_t hs,
+                              int *__restrict__ u_out, int *__restrict__ lab_out, float *__restrict__ dist_out,
+                              int64_t out_hs) {
+  const int h = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n[h]) return;
+  const int64_t o = (int64_t)h * out_hs + i;
+  if (u_out) u_out[o] = idx ? idx[(int64_t)h * idx_hs + i] : (int)i;
+  if (lab_out) lab_out[o] = lab[(int64_t)h * hs + i];
+  if (dist_out) dist_out[o] = dist[(int64_t)h * hs + i];
+}
+// n[h] and m[h] into column t of [BH, ld] tables.
+__global__ void k_trace_nm(const int *__restrict__ n, const int *__restrict__ m, int *__restrict__ n_out,
+                           int *__restrict__ m_out, int ld, int t, int BH) {
+  const int h = blockIdx.x * 256 + threadIdx.x;
+  if (h >= BH) return;
+  if (n_out) n_out[(int64_t)h * ld + t] = n[h];
+  if (m_out) m_out[(int64_t)h * ld + t] = m[h];
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 static inline dim3 g2(int64_t x, int y) { return dim3((unsigned)(x > 0 ? x : 1), (unsigned)y); }
 
@@ -1068,6 +1100,20 @@ void launch_compact_gather(const int *idx_old, int64_t idx_hs, const int *perm, 
                            int64_t seg_hs, int *idx_new, int *n_new, int BH, int nmax_pts, hipStream_t st) {
   hipLaunchKernelGGL(k_compact_gather, g2((nmax_pts + 255) / 256, BH), dim3(256), 0, st, idx_old, idx_hs, perm,
                      perm_hs, seg, seg_hs, idx_new, n_new);
+}
+
+void launch_trace_cent(int D, const KmArgs &a, int BH, int mmax, float *dst, int64_t dst_hs, hipStream_t st) {
+  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_trace_cent<DD>, g2(mmax, BH), dim3(256), 0, st, a, dst, dst_hs));
+}
+
+void launch_trace_stage(const int *n, const int *idx, int64_t idx_hs, const int *lab, const float *dist, int64_t hs,
+                        int *u_out, int *lab_out, float *dist_out, int64_t out_hs, int BH, int npts, hipStream_t st) {
+  hipLaunchKernelGGL(k_trace_stage, g2((npts + 255) / 256, BH), dim3(256), 0, st, n, idx, idx_hs, lab, dist, hs,
+                     u_out, lab_out, dist_out, out_hs);
+}
+
+void launch_trace_nm(const int *n, const int *m, int *n_out, int *m_out, int ld, int t, int BH, hipStream_t st) {
+  hipLaunchKernelGGL(k_trace_nm, dim3((BH + 255) / 256), dim3(256), 0, st, n, m, n_out, m_out, ld, t, BH);
 }
 
 void launch_kstats(int D, const KStatsArgs &s, int BH, hipStream_t st) {

@@ -28,6 +28,8 @@
  * Layout    Q, K, V, O are contiguous row-major [B, H, L, d] bfloat16, passed as uint16_t bit patterns.
  *           "BH" below is B*H; every per-head array is indexed by the flattened head b*H + h.
  *           d must be 64 or 128 (AC_E_UNSUPPORTED otherwise).  Self-attention: queries and keys share L.
+ *           One head's rows must stay below 4 GiB (L * d * 2 < 2^32: L <= 16,777,215 at d = 128),
+ *           else AC_E_UNSUPPORTED.
  * Pointers  Every array pointer is a DEVICE pointer owned by the caller, except the arrays inside
  *           ac_layer_stats, which are HOST pointers.  The library never allocates caller-visible
  *           memory, never frees, and keeps no pointer after a call returns.  Scratch memory is the
@@ -119,7 +121,11 @@ typedef struct ac_params {
                           0 = every point (8).  The subsample may hold at most 16384 points. */
   int32_t tail_block;  /* ac_layer only: > 0 applies ac_tail_merge with this query block before the
                           attention (iCATS tail merging); 0 = off (0) */
-  int32_t reserved0;   /* must be 0 */
+  int32_t min_sparse_gflop; /* ac_layer only: a layer whose dense attention work 4*B*H*L^2*d is below this
+                          many GFLOP runs dense (no clustering, the state untouched), since the sparse
+                          path has a fixed latency of ~1-2 ms on MI355X (Algorithm 1's stages, k-means++
+                          rounds, launches) that such a layer's dense attention does not reach;
+                          0 = always sparse (0) */
   uint64_t seed;       /* seed of the counter-based SplitMix64 stream of k-means++ (0) */
 } ac_params;
 
@@ -205,6 +211,36 @@ ac_status ac_cluster_q(const ac_shape *s, const ac_params *p, const uint16_t *Q,
 ac_status ac_cluster_k(const ac_shape *s, const ac_params *p, const uint16_t *K, const uint16_t *V,
                        const ac_state *warm, ac_clusters *k_out, ac_kstats *stats, void *ws,
                        size_t ws_bytes, ac_stream_t stream);
+
+/* Stage-by-stage record of a cold key clustering, so that every step of Algorithm 1 (AdaCluster
+ * §3.2.2) and of its k-means (k-means++ seeding, each Lloyd update, the stage's final assignment,
+ * the distances that set tau and the removal) can be recomputed from the previous step at any size.
+ * Device pointers owned by the caller; any array may be NULL to skip that record.  Stages
+ * t >= max_stages run as usual but are not recorded; entries of stages that do not run, and slots
+ * beyond n or m, are left as they were. */
+typedef struct ac_ktrace {
+  int32_t max_stages;
+  int32_t *n;      /* [BH, max_stages] |U_t|, the keys still unassigned when stage t starts */
+  int32_t *m;      /* [BH, max_stages] m_t, the centres of stage t */
+  int32_t *u;      /* [BH, max_stages, L] key index (0..L-1) of the i-th point of U_t, i < n */
+  float *cent;     /* [BH, max_stages, iters + 1, m0, d] stage centres (fp32): slot 0 after k-means++
+                      seeding, slot j after the j-th Lloyd update, rows c < m */
+  int32_t *labels; /* [BH, max_stages, L] stage centre (0..m-1) of the i-th point of U_t after the
+                      stage's final assignment */
+  float *dist;     /* [BH, max_stages, L] ||k - c|| of the i-th point of U_t to that centre */
+} ac_ktrace;
+
+/* ac_cluster_k (cold) with the stage record filled.  Same arguments, outputs and errors as a cold
+ * ac_cluster_k; trace must not be NULL and trace->max_stages must be >= 1.  For tests and
+ * diagnostics: the copies cost time. */
+ac_status ac_cluster_k_trace(const ac_shape *s, const ac_params *p, const uint16_t *K, const uint16_t *V,
+                             ac_clusters *k_out, ac_kstats *stats, const ac_ktrace *trace, void *ws,
+                             size_t ws_bytes, ac_stream_t stream);
+
+/* ac_cluster_q (cold) with the query centres recorded after k-means++ seeding (slot 0) and after each
+ * Lloyd update (slot j): cent_trace [BH, p->iters + 1, q_out->ncap, d] fp32, device memory. */
+ac_status ac_cluster_q_trace(const ac_shape *s, const ac_params *p, const uint16_t *Q, ac_clusters *q_out,
+                             float *cent_trace, void *ws, size_t ws_bytes, ac_stream_t stream);
 
 /* Scores of every (query cluster r, key cluster c) pair and the selection of key clusters for
  * each query cluster.  QUEST: S_rc = sum_d max(cq_r[d] kmax_c[d], cq_r[d] kmin_c[d]) (AdaCluster

@@ -34,6 +34,7 @@ def test_struct_sizes_match_c_layout():
     assert ctypes.sizeof(ac.CSelection) == 40
     assert ctypes.sizeof(ac.CState) == 48
     assert ctypes.sizeof(ac.CSchedule) == 24
+    assert ctypes.sizeof(ac.CKTrace) == 56
 
 
 def test_defaults_and_status_strings():
@@ -41,7 +42,7 @@ def test_defaults_and_status_strings():
     assert (p.nq, p.iters, p.m0, p.nmax, p.tau_rule, p.sel_mode) == (65, 10, 200, 1500, ac.AC_TAU_MEAN_X,
                                                                     ac.AC_SEL_DENSITY)
     assert abs(p.tau_param - 1.5) < 1e-7 and abs(p.sel_param - 0.15) < 1e-7
-    assert (p.tail_block, p.reserved0) == (0, 0)
+    assert (p.tail_block, p.min_sparse_gflop) == (0, 0)
     lib = ac.load()
     assert lib.ac_status_str(ac.AC_E_WORKSPACE) == b"workspace too small"
 
@@ -57,7 +58,8 @@ def test_sizes_validation():
             ac.ac_sizes(ac.Shape(*bad_shape), p)
         assert e.value.status == code
     for kw in [dict(nq=0), dict(tau_rule=9), dict(sel_mode=7), dict(sel_mode=ac.AC_SEL_DENSITY, sel_param=1.5),
-               dict(compensate=2), dict(tau_rule=ac.AC_TAU_PCTL, tau_param=0.0), dict(sel_mode=ac.AC_SEL_TOPK, topk=0)]:
+               dict(compensate=2), dict(tau_rule=ac.AC_TAU_PCTL, tau_param=0.0), dict(sel_mode=ac.AC_SEL_TOPK, topk=0),
+               dict(min_sparse_gflop=-1)]:
         with pytest.raises(ac.ACError) as e:
             ac.ac_sizes(ac.Shape(1, 2, 4096, 64), ac.params_default(**kw))
         assert e.value.status == ac.AC_E_ARG, kw
@@ -67,6 +69,12 @@ def test_sizes_validation():
     with pytest.raises(ac.ACError) as e:
         ac.ac_sizes(ac.Shape(1, 2, 100000, 64), ac.params_default(init_sample=0))
     assert e.value.status == ac.AC_E_UNSUPPORTED
+    # one head's rows must be addressable with 32-bit byte offsets
+    ac.ac_sizes(ac.Shape(1, 1, (1 << 24) - 1, 128), ac.params_default())
+    for L, d in ((1 << 24, 128), (1 << 25, 64)):
+        with pytest.raises(ac.ACError) as e:
+            ac.ac_sizes(ac.Shape(1, 1, L, d), ac.params_default())
+        assert e.value.status == ac.AC_E_UNSUPPORTED and b"4 GiB" in ac.load().ac_last_error()
 
 
 def _fake_clusters(ncap):
@@ -128,6 +136,14 @@ def test_entry_points_reject_bad_arguments_before_any_device_work():
                                    ctypes.byref(st), ws, wsb, None) == ac.AC_E_ARG
     assert lib.ac_cluster_k_metric(ctypes.byref(shape), ctypes.byref(p), 1 << 20, 1 << 20, 1 << 20,
                                    ctypes.byref(k_bad), ctypes.byref(st), ws, wsb, None) == ac.AC_E_ARG
+    # traced clustering: NULL trace, no stage to record
+    assert lib.ac_cluster_k_trace(ctypes.byref(shape), ctypes.byref(p), 1 << 20, 1 << 20, ctypes.byref(k),
+                                  ctypes.byref(st), None, ws, wsb, None) == ac.AC_E_ARG
+    tr0 = ac.CKTrace(0, 0, 0, 0, 0, 0, 0)
+    assert lib.ac_cluster_k_trace(ctypes.byref(shape), ctypes.byref(p), 1 << 20, 1 << 20, ctypes.byref(k),
+                                  ctypes.byref(st), ctypes.byref(tr0), ws, wsb, None) == ac.AC_E_ARG
+    assert lib.ac_cluster_q_trace(ctypes.byref(shape), ctypes.byref(p), 1 << 20, ctypes.byref(q), None, ws, wsb,
+                                  None) == ac.AC_E_ARG
     # NULL state
     assert lib.ac_layer(ctypes.byref(shape), ctypes.byref(p), 1 << 20, 1 << 20, 1 << 20, None, 1 << 20, None, ws, wsb,
                         None) == ac.AC_E_ARG
