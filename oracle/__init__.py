@@ -23,6 +23,9 @@ What it computes, step by step, in the order of the pages:
   compensation) -> ``attention``
 * The whole layer, cold and warm (AdaCluster §3.2.2 "Efficient
   initialization") -> ``layer.run_layer``
+* ClusterAttention's recursive split along principal components into
+  clusters of a preset power-of-two size (abstract; end of section 2)
+  -> ``pcasplit.pca_split``
 
 Where the pages leave a step open, the reading taken is stated in the
 docstring of the function that implements it.
@@ -35,4 +38,4 @@ policy and the number of warm iterations).  Those are "parity unpinned":
 they are checked only GPU-against-oracle.
 """
 from .numerics import Params, bf16_round, bf16_to_f64, uniform01, splitmix64_next  # noqa: F401
-from . import kmeans, multistage, stats, score, attention, layer  # noqa: F401
+from . import kmeans, multistage, stats, score, attention, layer, pcasplit  # noqa: F401
