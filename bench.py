@@ -64,7 +64,7 @@ def _abi(kw):
 class Layer:
     """Device buffers of one layer and the four entry points."""
 
-    def __init__(self, Qd, Kd, Vd, shape, params, tail_block=0, key_metric=False):
+    def __init__(self, Qd, Kd, Vd, shape, params, tail_block=0, key_metric=False, pca=None):
         import torch
         import clustered_sparse_attention_amd as ac
         self.ac = ac
@@ -90,6 +90,7 @@ class Layer:
         self.torch = torch
         self.side = torch.cuda.Stream()  # default priority
         self.key_metric = key_metric
+        self.pca = pca  # (query block, key block) of ClusterAttention's principal-component split, or None
         if key_metric:
             self.M = torch.empty((BH, d, d), dtype=torch.float32, device=dev)
 
@@ -109,6 +110,15 @@ class Layer:
             if ev: ev[3].record(main)
             ac.ac_interaction_matrix(self.shape, self.p, self.Q, self.q, self.M, self.ws)
             ac.ac_cluster_k_metric(self.shape, self.p, self.K, self.V, self.M, self.k, self.st, self.ws)
+            if ev: ev[1].record(main)
+            if ev: ev[4].record(main)
+        elif self.pca:
+            # the two sides share the workspace's split scratch: one after the other
+            if ev: ev[0].record(main)
+            if ev: ev[2].record(main)
+            ac.ac_cluster_q_pca(self.shape, self.p, self.Q, self.pca[0], self.q, self.ws)
+            if ev: ev[3].record(main)
+            ac.ac_cluster_k_pca(self.shape, self.p, self.K, self.V, self.pca[1], self.k, self.st, self.ws)
             if ev: ev[1].record(main)
             if ev: ev[4].record(main)
         else:
@@ -620,6 +630,9 @@ def main():
     ap.add_argument("--key-metric", type=int, default=0,
                     help="cluster the keys interaction-aware (iCATS, metric M_Q from the query clusters) into this "
                          "many clusters instead of Algorithm 1 (0 = off)")
+    ap.add_argument("--pca-split", default="",
+                    help="QB,KB: cluster queries and keys by ClusterAttention's principal-component split into "
+                         "clusters of QB and KB tokens (powers of two) instead of k-means / Algorithm 1")
     ap.add_argument("--no-baselines", action="store_true", help="skip dense baselines and the CPU oracle")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a plain copy of this many bytes")
@@ -673,15 +686,21 @@ def main():
     kw = workload_params(args.workload, args.variant, args.compensate)
     if args.key_metric:
         kw["m0"] = args.key_metric
+    pca = None
+    if args.pca_split:
+        pca = tuple(int(x) for x in args.pca_split.split(","))
+        # one query cluster per query block and a key capacity for every key cluster
+        kw["nq"] = -(-w.L // pca[0])
+        kw["nmax"] = max(kw["nmax"], -(-w.L // pca[1]) - kw["m0"] + 1)
     params = _abi(kw)
     layer = Layer(Qd, Kd, Vd, (w.B, w.H, w.L, w.d), params, tail_block=args.tail_block,
-                  key_metric=bool(args.key_metric))
+                  key_metric=bool(args.key_metric), pca=pca)
     if args.serial:
         layer.side = torch.cuda.current_stream()
 
     # the timed step is one ac_layer call (cold), except for the variants that
     # ac_layer does not run (interaction-aware keys) or a serial profile
-    use_layer = not args.key_metric and not args.serial
+    use_layer = not args.key_metric and not args.serial and not pca
     for _ in range(args.warmup):
         layer.layer_step() if use_layer else layer.step()
     torch.cuda.synchronize()
@@ -735,7 +754,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": (measured_traffic(args.workload, args.variant, args.compensate)
-                                 if not args.key_metric and not args.tail_block else None),
+                                 if not args.key_metric and not args.tail_block and not pca else None),
                      "kernel": "ac_sparse_attn: k_attn_rows + k_attn_prep + k_attn (block-sparse attention)",
                      "algorithmic_flops_per_launch": attn_flops, "avg_launch_ms": round(attn_ms, 4)},
         "phase_ms": {"cluster_q": round(float(phase_ms[0]), 3), "cluster_k": round(float(phase_ms[1]), 3),
@@ -745,8 +764,9 @@ def main():
         "_phase_note": ("phases from a separate pass of the entry points, the query clustering beside the key "
                         "clustering from the start; " if use_layer else "") +
                        "score_select includes ac_tail_merge when tail merging is on",
-        "key_clustering": "interaction-aware, %d clusters (iCATS)" % args.key_metric if args.key_metric
-                          else "Algorithm 1 (multi-stage)",
+        "key_clustering": ("interaction-aware, %d clusters (iCATS)" % args.key_metric if args.key_metric
+                           else "principal-component split, queries in clusters of %d, keys of %d "
+                                "(ClusterAttention)" % pca if pca else "Algorithm 1 (multi-stage)"),
         "tail_merge": None if not args.tail_block else dict(
             zip(("block", "query_blocks_before", "query_blocks_after"),
                 (args.tail_block,) + layer.query_blocks(args.tail_block))),

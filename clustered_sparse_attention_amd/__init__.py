@@ -23,7 +23,7 @@ AC_SEL_TOPK, AC_SEL_DENSITY, AC_SEL_TOPP, AC_SEL_DENSE = range(4)
 AC_QUEST_MFMA, AC_QUEST_VALU = range(2)
 
 ENTRY_POINTS = ("ac_params_default", "ac_sizes", "ac_cluster_q", "ac_cluster_k", "ac_cluster_k_trace",
-                "ac_cluster_q_trace", "ac_score_select",
+                "ac_cluster_q_trace", "ac_cluster_q_pca", "ac_cluster_k_pca", "ac_score_select",
                 "ac_sparse_attn", "ac_tail_merge", "ac_score_tokens", "ac_interaction_matrix",
                 "ac_cluster_k_metric", "ac_layer", "ac_topp_schedule",
                 "ac_kmax_calibrate", "ac_step_params", "ac_status_str", "ac_last_error")
@@ -65,6 +65,10 @@ class CKStats(ctypes.Structure):
 class CKTrace(ctypes.Structure):
     _fields_ = [("max_stages", ctypes.c_int32), ("n", P), ("m", P), ("u", P), ("cent", P), ("labels", P),
                 ("dist", P)]
+
+
+class CPcaTrace(ctypes.Structure):
+    _fields_ = [("dir", P), ("perm", P)]
 
 
 class CSelection(ctypes.Structure):
@@ -115,6 +119,13 @@ def load() -> ctypes.CDLL:
     lib.ac_cluster_q_trace.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), vp, ctypes.POINTER(CClusters),
                                        vp, vp, ctypes.c_size_t, vp]
     lib.ac_cluster_q_trace.restype = st
+    lib.ac_cluster_q_pca.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), vp, ctypes.c_int32,
+                                     ctypes.POINTER(CClusters), ctypes.POINTER(CPcaTrace), vp, ctypes.c_size_t, vp]
+    lib.ac_cluster_q_pca.restype = st
+    lib.ac_cluster_k_pca.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), vp, vp, ctypes.c_int32,
+                                     ctypes.POINTER(CClusters), ctypes.POINTER(CKStats), ctypes.POINTER(CPcaTrace), vp,
+                                     ctypes.c_size_t, vp]
+    lib.ac_cluster_k_pca.restype = st
     lib.ac_score_select.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), ctypes.POINTER(CClusters),
                                     ctypes.POINTER(CClusters), ctypes.POINTER(CKStats), ctypes.POINTER(CSelection),
                                     vp, ctypes.c_size_t, vp]
@@ -314,6 +325,34 @@ def ac_cluster_q_trace(shape, params, Q, q_out: Clusters, cent_trace, ws, stream
     """cent_trace: [BH, iters + 1, q_out.ncap, d] float32."""
     _check(load().ac_cluster_q_trace(ctypes.byref(shape), ctypes.byref(params), _ptr(Q), ctypes.byref(q_out.c()),
                                      _ptr(cent_trace), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+class PcaTrace:
+    """Device arrays of a principal-component split record (see ac_pca_trace)."""
+
+    def __init__(self, BH: int, L: int, block: int, levels: int, d: int, device):
+        import torch
+        nint = max(1, -(-L // block) - 1)
+        self.dir = torch.zeros((BH, nint, d), dtype=torch.float32, device=device)
+        self.perm = torch.full((BH, max(levels, 1), L), -1, dtype=torch.int32, device=device)
+
+    def c(self) -> CPcaTrace:
+        return CPcaTrace(_ptr(self.dir), _ptr(self.perm))
+
+
+def ac_cluster_q_pca(shape, params, Q, block: int, q_out: Clusters, ws, trace: Optional[PcaTrace] = None,
+                     stream=None):
+    tc = ctypes.byref(trace.c()) if trace is not None else None
+    _check(load().ac_cluster_q_pca(ctypes.byref(shape), ctypes.byref(params), _ptr(Q), int(block),
+                                   ctypes.byref(q_out.c()), tc, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def ac_cluster_k_pca(shape, params, K, V, block: int, k_out: Clusters, stats: KStats, ws,
+                     trace: Optional[PcaTrace] = None, stream=None):
+    tc = ctypes.byref(trace.c()) if trace is not None else None
+    _check(load().ac_cluster_k_pca(ctypes.byref(shape), ctypes.byref(params), _ptr(K), _ptr(V), int(block),
+                                   ctypes.byref(k_out.c()), ctypes.byref(stats.c()), tc, _ptr(ws), ws.numel(),
+                                   _stream(stream)))
 
 
 def ac_score_select(shape, params, q: Clusters, k: Clusters, stats: KStats, sel: Selection, ws, stream=None):

@@ -122,6 +122,8 @@ struct Plan {
   size_t tm_plan, m_labels, m_perm, m_seg, m_list, m_n, m_mask;
   // interaction matrix: raw query sums and counts per query cluster
   size_t qsum, qcnt;
+  // principal-component split: token scratch, projection keys, node table
+  size_t pca_tmp, pca_key, pca_nodes, pca_lvl;
 };
 
 // stride of the per-selection key row lists: whole key tiles
@@ -226,6 +228,10 @@ Plan make_plan(const ac_shape *s, const ac_params *p) {
   P.m_mask = take(BH * P.nq * (size_t)P.mwords * 4);
   P.qsum = take(BH * P.nq * D * 8);
   P.qcnt = take(BH * P.nq * 4);
+  P.pca_tmp = take(BH * L * 4);
+  P.pca_key = take(BH * L * 4);
+  P.pca_nodes = take((L / PCA_BLOCK_MIN + 2) * 8);  // at most ceil(L / b) - 1 internal nodes
+  P.pca_lvl = take(64 * 4);
   P.total = off + 256;  // slack for aligning the base pointer
   return P;
 }
@@ -519,6 +525,42 @@ ac_status do_cluster_k_warm(const Plan &P, const ac_params *p, const uint16_t *K
   return finish_keys(P, K, V, k, stats, ws, st, k->ncap);
 }
 
+// ClusterAttention's clustering of the rows X of every head by recursive
+// splits along principal directions into clusters of `block` rows; the
+// order, labels, segments, count and member-mean centres of `out`.
+ac_status do_pca_split(const Plan &P, const uint16_t *X, int block, ac_clusters *out, const ac_pca_trace *tr,
+                       void *ws, hipStream_t st) {
+  const int BH = P.BH, L = P.L, D = P.D;
+  const std::vector<int> counts = pca_level_counts(L, block);
+  int ninternal = 0;
+  for (int c : counts) ninternal += c;
+  PcaArgs a;
+  a.X = X;
+  a.perm = out->perm;
+  a.tmp = at<int>(ws, P.pca_tmp);
+  a.key = at<uint32_t>(ws, P.pca_key);
+  a.nodes = at<int2>(ws, P.pca_nodes);
+  a.lvl = at<int>(ws, P.pca_lvl);
+  a.dir = tr ? tr->dir : nullptr;
+  a.ndir = ninternal;
+  a.L = L;
+  a.block = block;
+  launch_pca_split(D, a, counts, BH, tr ? tr->perm : nullptr, st);
+  launch_pca_finish(out->perm, out->labels, out->seg, out->ncl, L, block, out->ncap, BH, st);
+  launch_seg_rowmean(D, X, out->perm, out->seg, out->ncl, L, out->ncap, out->cent, BH, st);
+  AC_CHECK_LAUNCH();
+  return AC_OK;
+}
+
+ac_status check_pca_block(const Plan &P, int block, int ncap) {
+  if (block < PCA_BLOCK_MIN || block > PCA_BLOCK_MAX || (block & (block - 1)) != 0)
+    return fail(AC_E_ARG, "block %d must be a power of two in [%d, %d]", block, PCA_BLOCK_MIN, PCA_BLOCK_MAX);
+  const int64_t nc = cdiv(P.L, block);
+  if (nc > ncap)
+    return fail(AC_E_ARG, "L / block = %lld clusters exceed the cluster capacity %d", (long long)nc, ncap);
+  return AC_OK;
+}
+
 // Interaction-aware keys: a fixed count m = min(m0, L) of k-means clusters,
 // Euclidean k-means++ seeding, Lloyd iterations and the final assignment
 // under the metric M, then the order and statistics as for the other keys.
@@ -769,6 +811,54 @@ AC_API ac_status ac_cluster_q_trace(const ac_shape *s, const ac_params *p, const
   AC_TRY(check_ws(P, ws, ws_bytes));
   AC_TRY(check_device());
   return do_cluster_q(P, p, Q, nullptr, q_out, ws, (hipStream_t)stream, cent_trace);
+}
+
+AC_API ac_status ac_cluster_q_pca(const ac_shape *s, const ac_params *p, const uint16_t *Q, int32_t block,
+                                  ac_clusters *q_out, const ac_pca_trace *trace, void *ws, size_t ws_bytes,
+                                  ac_stream_t stream) {
+  AC_TRY(check_shape(s));
+  AC_TRY(check_params(s, p));
+  if (!Q) return fail(AC_E_ARG, "Q is NULL");
+  Plan P = make_plan(s, p);
+  AC_TRY(check_clusters(q_out, "query", P.nq, true));
+  if (q_out->ncap != P.nq) return fail(AC_E_ARG, "query clusters ncap must be min(nq, L) = %d", P.nq);
+  AC_TRY(check_pca_block(P, block, q_out->ncap));
+  AC_TRY(check_ws(P, ws, ws_bytes));
+  AC_TRY(check_device());
+  hipStream_t st = (hipStream_t)stream;
+  uint16_t *qhat = at<uint16_t>(ws, P.qhat);
+  float *qn = at<float>(ws, P.qn);
+  launch_qnorm(P.D, Q, qhat, qn, (int64_t)P.BH * P.L, st);
+  AC_TRY(do_pca_split(P, qhat, block, q_out, trace, ws, st));
+  launch_seg_mean(qn, q_out->perm, q_out->seg, P.L, q_out->ncap, q_out->ncl, q_out->rho, P.BH, st);
+  AC_CHECK_LAUNCH();
+  return AC_OK;
+}
+
+AC_API ac_status ac_cluster_k_pca(const ac_shape *s, const ac_params *p, const uint16_t *K, const uint16_t *V,
+                                  int32_t block, ac_clusters *k_out, ac_kstats *stats, const ac_pca_trace *trace,
+                                  void *ws, size_t ws_bytes, ac_stream_t stream) {
+  AC_TRY(check_shape(s));
+  AC_TRY(check_params(s, p));
+  if (!K || !V) return fail(AC_E_ARG, "K or V is NULL");
+  Plan P = make_plan(s, p);
+  AC_TRY(check_clusters(k_out, "key", P.ncapk, false));
+  if (k_out->ncap != P.ncapk) return fail(AC_E_ARG, "key clusters ncap must be %d", P.ncapk);
+  AC_TRY(check_kstats(stats));
+  AC_TRY(check_pca_block(P, block, k_out->ncap));
+  AC_TRY(check_ws(P, ws, ws_bytes));
+  AC_TRY(check_device());
+  hipStream_t st = (hipStream_t)stream;
+  const int BH = P.BH;
+  AC_TRY(do_pca_split(P, K, block, k_out, trace, ws, st));
+  KStatsArgs ks{K, V, k_out->perm, k_out->seg, k_out->ncl, k_out->cent, stats->kmax, stats->kmin, stats->kmean,
+                stats->vmean, at<double>(ws, P.msepart), stats->mse, P.L, k_out->ncap};
+  launch_kstats(P.D, ks, BH, st);
+  launch_fill_u8(stats->fallback, BH, 0, st);
+  launch_fill_i32((int *)stats->tau, BH, 0, st);  // +0.0f: no distance threshold
+  launch_fill_i32(stats->stages, BH, (int)pca_level_counts(P.L, block).size(), st);
+  AC_CHECK_LAUNCH();
+  return AC_OK;
 }
 
 AC_API ac_status ac_score_select(const ac_shape *s, const ac_params *p, const ac_clusters *q, const ac_clusters *k,

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 namespace ac {
 
 constexpr int KPP_SMAX = 16384;  // most points a k-means++ subsample may hold
@@ -20,6 +22,7 @@ constexpr int ATT_KT = 64;       // keys per attention tile
 constexpr int SEL_MAXN = 4096;   // most key clusters the select kernel sorts
 constexpr int ASSIGN_RES_MAX = 224;  // most centres the LDS-resident assignment holds
 constexpr int UPD_CHUNK = 256;   // members per block in the centre update
+constexpr int KST_FIELDS = 8;    // ints of Algorithm 1's per-head state on the device
 
 enum { TAU_RULE_MEAN_X = 0, TAU_RULE_PCTL = 1, TAU_RULE_ABS = 2, TAU_RULE_INF = 3 };
 
@@ -155,6 +158,22 @@ struct TailArgs {
   int nq, ncapk, mwords, L, block;
 };
 
+// Recursive principal-component split (see pca.hip).
+constexpr int PCA_SMAX = 512;   // subsample points that set a node's direction
+constexpr int PCA_BLOCK_MIN = 16, PCA_BLOCK_MAX = 4096;  // cluster sizes (powers of two)
+constexpr int PCA_ITERS = 64;   // power iterations per node
+struct PcaArgs {
+  const uint16_t *X;  // [BH, L, D] rows to cluster
+  int *perm;          // [BH, L] token order, refined level by level
+  int *tmp;           // [BH, L] scratch: the node's tokens before its split
+  uint32_t *key;      // [BH, L] scratch: order-preserving projection keys
+  int2 *nodes;        // internal nodes (first position, count), levels in order
+  int *lvl;           // [levels + 1] first node of each level
+  float *dir;         // [BH, ndir, D] direction of each internal node, or NULL
+  int ndir;
+  int L, block;
+};
+
 // Per-token Quest scores (see quest.hip).
 struct TokQuestArgs {
   const uint16_t *Q;            // [BH, L, D] bf16 query rows
@@ -189,6 +208,10 @@ void launch_flag_removed(const float *dist, int64_t dist_hs, const int *n_arr, c
 void launch_compact_gather(const int *idx_old, int64_t idx_hs, const int *perm, int64_t perm_hs, const int *seg,
                            int64_t seg_hs, int *idx_new, int *n_new, int BH, int nmax_pts, hipStream_t st);
 void launch_kstats(int D, const KStatsArgs &s, int BH, hipStream_t st);
+// Algorithm 1's bookkeeping between stages on the device (state [BH, KST_FIELDS])
+void launch_stage_next(int *state, const int *nnew, int *n, int *m, int *coff, int t, int nmax, int m0, int L,
+                       int BH, hipStream_t st);
+void launch_stage_final(const int *state, int *ncl, uint8_t *fallback, int *stages, int BH, hipStream_t st);
 // stage records of the traced entry points
 void launch_trace_cent(int D, const KmArgs &a, int BH, int mmax, float *dst, int64_t dst_hs, hipStream_t st);
 void launch_trace_stage(const int *n, const int *idx, int64_t idx_hs, const int *lab, const float *dist, int64_t hs,
@@ -223,6 +246,15 @@ void launch_interaction_matrix(int D, const uint16_t *Q, const int *perm, const 
                                int nq, int nqcap, double *qsum, int *qcnt, float *M, int BH, hipStream_t st);
 void launch_cent_prep_metric(int D, const KmArgs &a, const CentOps &op, const float *M, int BH, int mmax,
                              hipStream_t st);
+
+// pca.hip
+std::vector<int> pca_level_counts(int n, int b);
+void launch_pca_split(int D, const PcaArgs &a, const std::vector<int> &counts, int BH, int *perm_trace,
+                      hipStream_t st);
+void launch_pca_finish(const int *perm, int *labels, int *seg, int *ncl, int L, int b, int segcap, int BH,
+                       hipStream_t st);
+void launch_seg_rowmean(int D, const uint16_t *X, const int *perm, const int *seg, const int *ncl, int L, int ncap,
+                        float *cent, int BH, hipStream_t st);
 
 // quest.hip (engine 0: MFMA, 1: vector ALU)
 void launch_token_quest(int D, const TokQuestArgs &a, int engine, int BH, hipStream_t st);

@@ -1,0 +1,462 @@
+// ClusterAttention's clustering for gfx950: recursive splits along the
+// leading principal direction into clusters of a preset power-of-two size b.
+//
+// A node of n > b points (a contiguous range of the head's token order) is
+// cut in two: the n_left = b * ceil(ceil(n / b) / 2) points with the
+// smallest projections onto the node's direction go left, the rest right,
+// each side keeping its token order.  The tree's shape depends only on n and
+// b, so every level is one launch over the internal nodes of that level
+// (one workgroup per node and head).  A workgroup:
+//   1. loads a strided subsample of s = min(n, PCA_SMAX) points into LDS,
+//      dimension-major, and centres it (bf16 of x - mean);
+//   2. forms the d x d covariance with 32x32x16 bf16 MFMA (fp32 sums);
+//   3. runs PCA_ITERS power iterations from the subsample row farthest from
+//      the mean and orients the result (largest component positive);
+//   4. projects every point of the node (fp32), radix-selects the n_left-th
+//      smallest (projection, position) key in four 8-bit passes, and writes
+//      the stable partition of the node's tokens.
+#include <utility>
+#include <vector>
+
+#include "common.h"
+#include "internal.h"
+
+namespace ac {
+
+constexpr int PCA_SP = PCA_SMAX + 8;  // LDS row stride (bf16) of the dimension-major subsample
+
+// Internal nodes of the split tree of n points, level by level, left to
+// right: nodes[k] = (first position, count); lvl[l] = first node of level l,
+// lvl[levels] = node count.  One thread: the tree has about n / b nodes.
+__global__ void k_pca_tree(int n, int b, int2 *__restrict__ nodes, int *__restrict__ lvl) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int head = 0, tail = 0, level = 0;
+  if (n > b) nodes[tail++] = make_int2(0, n);
+  while (head < tail) {
+    const int end = tail;
+    lvl[level++] = head;
+    for (; head < end; ++head) {
+      const int2 nd = nodes[head];
+      const int nb = (nd.y + b - 1) / b, nl = b * ((nb + 1) / 2), nr = nd.y - nl;
+      if (nl > b) nodes[tail++] = make_int2(nd.x, nl);
+      if (nr > b) nodes[tail++] = make_int2(nd.x + nl, nr);
+    }
+  }
+  lvl[level] = tail;
+}
+
+// Block-wide exclusive scan of two counters (512 threads = 8 waves); returns
+// the thread's exclusive prefix and writes the block totals.
+AC_DEV int2 block_scan2(int x, int y, int2 *sh, int2 &tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int ix = x, iy = y;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int a = __shfl_up(ix, o, 64), b = __shfl_up(iy, o, 64);
+    if (lane >= o) { ix += a; iy += b; }
+  }
+  if (lane == 63) sh[wave] = make_int2(ix, iy);
+  __syncthreads();
+  int ox = 0, oy = 0, tx = 0, ty = 0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const int2 t = sh[w];
+    if (w < wave) { ox += t.x; oy += t.y; }
+    tx += t.x;
+    ty += t.y;
+  }
+  __syncthreads();
+  tot = make_int2(tx, ty);
+  return make_int2(ox + ix - x, oy + iy - y);
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int count) {
+  constexpr int NT = 512;
+  const int h = blockIdx.y, node = first + (int)blockIdx.x;
+  if ((int)blockIdx.x >= count) return;
+  const int2 nd = a.nodes[node];
+  const int start = nd.x, n = nd.y, b = a.block;
+  const int nb = (n + b - 1) / b, nl = b * ((nb + 1) / 2);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint16_t *X = a.X + (int64_t)h * a.L * D;
+  int *perm = a.perm + (int64_t)h * a.L + start;
+  int *tmp = a.tmp + (int64_t)h * a.L + start;
+  uint32_t *key = a.key + (int64_t)h * a.L + start;
+
+  extern __shared__ __align__(16) unsigned char pca_lds[];
+  uint16_t *Y = reinterpret_cast<uint16_t *>(pca_lds);  // [D][PCA_SP] bf16, later C [D][D] fp32
+  float *C = reinterpret_cast<float *>(pca_lds);
+  __shared__ float mu[D], wbuf[2][D], nrm_part[2][8];
+  __shared__ uint32_t hist[256];
+  __shared__ float far_n[8];
+  __shared__ int far_j[8];
+  __shared__ int2 scan_sh[8];
+  __shared__ uint32_t sh_prefix, sh_rank;
+
+  // 1. strided subsample, dimension-major; columns beyond s are zero
+  const int s = min(n, PCA_SMAX);
+  const int spad = (s + 15) & ~15;
+  for (int q = tid; q < spad * (D / 8); q += NT) {
+    const int j = q / (D / 8), c = q % (D / 8);
+    uint16_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (j < s) {
+      const int t = perm[(int)(((int64_t)j * n) / s)];
+      *(u32x4_t *)v = *(const u32x4_t *)(X + (int64_t)t * D + c * 8);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) Y[(c * 8 + e) * PCA_SP + j] = v[e];
+  }
+  __syncthreads();
+  // mean of each dimension (four threads per dimension, fixed order)
+  {
+    const int i = tid >> 2, part = tid & 3;
+    float acc = 0.f;
+    if (i < D)
+      for (int j = part; j < s; j += 4) acc += bf2f(Y[i * PCA_SP + j]);
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    if (i < D && part == 0) mu[i] = acc / (float)s;
+  }
+  __syncthreads();
+  for (int q = tid; q < D * s; q += NT) {
+    const int i = q / s, j = q % s;
+    Y[i * PCA_SP + j] = f2bf(bf2f(Y[i * PCA_SP + j]) - mu[i]);
+  }
+  __syncthreads();
+  // start of the power iteration: the subsample row farthest from the mean
+  // (lowest position on ties), one thread per row
+  {
+    float nn = -1.f;
+    if (tid < s) {
+      nn = 0.f;
+      for (int i = 0; i < D; ++i) {
+        const float y = bf2f(Y[i * PCA_SP + tid]);
+        nn = fmaf(y, y, nn);
+      }
+    }
+    int bj = tid;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float on = __shfl_xor(nn, o, 64);
+      const int oj = __shfl_xor(bj, o, 64);
+      if (on > nn || (on == nn && oj < bj)) { nn = on; bj = oj; }
+    }
+    if (lane == 0) { far_n[wave] = nn; far_j[wave] = bj; }
+    __syncthreads();
+    if (wave == 0) {
+      float bn = lane < 8 ? far_n[lane] : -2.f;
+      int bjj = lane < 8 ? far_j[lane] : 0x7fffffff;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float on = __shfl_xor(bn, o, 64);
+        const int oj = __shfl_xor(bjj, o, 64);
+        if (on > bn || (on == bn && oj < bjj)) { bn = on; bjj = oj; }
+      }
+      // unnormalised start; the first iteration normalises (its norm is set here)
+      for (int i = lane; i < D; i += 64) wbuf[0][i] = bf2f(Y[i * PCA_SP + bjj]);
+      float sq = 0.f;
+      for (int i = lane; i < D; i += 64) sq = fmaf(wbuf[0][i], wbuf[0][i], sq);
+      sq = wave_sum(sq);
+      if (lane < 8) nrm_part[0][lane] = lane == 0 ? sq : 0.f;
+    }
+  }
+
+  // 2. covariance C = Y Y^T (unnormalised; only its direction matters), one
+  // 32x32 tile of C per wave and pass
+  constexpr int NTILE = (D / 32) * (D / 32);
+  constexpr int TPW = (NTILE + 7) / 8;
+  f32x16_t acc[TPW];
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) acc[k] = (f32x16_t){};
+  const int l32 = lane & 31, g = lane >> 5;
+  for (int k0 = 0; k0 < spad; k0 += 16) {
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int tile = wave + 8 * k;
+      if (tile < NTILE) {
+        const int I = tile / (D / 32), J = tile % (D / 32);
+        const bf16x8_t av = *(const bf16x8_t *)&Y[(I * 32 + l32) * PCA_SP + k0 + 8 * g];
+        const bf16x8_t bv = *(const bf16x8_t *)&Y[(J * 32 + l32) * PCA_SP + k0 + 8 * g];
+        acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[k], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();  // every read of Y is done before C overwrites it
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {
+    const int tile = wave + 8 * k;
+    if (tile < NTILE) {
+      const int I = tile / (D / 32), J = tile % (D / 32);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) C[(I * 32 + 8 * (r / 4) + 4 * g + (r % 4)) * D + J * 32 + l32] = acc[k][r];
+    }
+  }
+  __syncthreads();
+
+  // 3. power iteration (the start vector and its norm are in wbuf[0], nrm_part[0])
+  // w = C v: wave w owns outputs [D/8 * w, +D/8); lane (output o, part p)
+  constexpr int OPW = D / 8;           // outputs per wave
+  constexpr int PARTS = 64 / OPW;      // lanes per output
+  constexpr int KPP = D / PARTS;       // inputs per lane
+  const int oi = wave * OPW + lane % OPW, part = lane / OPW;
+  for (int it = 0; it < PCA_ITERS; ++it) {
+    const int cur = it & 1, nxt = cur ^ 1;
+    float nrm2 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) nrm2 += nrm_part[cur][w];
+    const float inv = nrm2 > 0.f ? 1.f / sqrtf(nrm2) : 0.f;
+    float acc1 = 0.f;
+    for (int k = part * KPP; k < (part + 1) * KPP; ++k) acc1 = fmaf(C[k * D + oi], wbuf[cur][k], acc1);
+#pragma unroll
+    for (int o = OPW; o < 64; o <<= 1) acc1 += __shfl_xor(acc1, o, 64);
+    const float w = acc1 * inv;
+    float sq = lane < OPW ? w * w : 0.f;
+    sq = wave_sum(sq);
+    if (lane < OPW) wbuf[nxt][oi] = w;
+    if (lane == 0) nrm_part[nxt][wave] = sq;
+    __syncthreads();
+  }
+  // normalise and orient: the component of largest magnitude is positive
+  if (wave == 0) {
+    float nrm2 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) nrm2 += nrm_part[PCA_ITERS & 1][w];
+    float best = -1.f, sgn = 1.f;
+    int bi = 0;
+    for (int i = lane; i < D; i += 64) {
+      const float v = wbuf[PCA_ITERS & 1][i];
+      if (fabsf(v) > best) { best = fabsf(v); bi = i; sgn = v < 0.f ? -1.f : 1.f; }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(best, o, 64);
+      const int oi2 = __shfl_xor(bi, o, 64);
+      const float os = __shfl_xor(sgn, o, 64);
+      if (ov > best || (ov == best && oi2 < bi)) { best = ov; bi = oi2; sgn = os; }
+    }
+    const bool zero = !(nrm2 > 0.f);
+    const float scale = zero ? 0.f : sgn / sqrtf(nrm2);
+    for (int i = lane; i < D; i += 64) {
+      const float v = zero ? (i == 0 ? 1.f : 0.f) : wbuf[PCA_ITERS & 1][i] * scale;
+      mu[i] = v;  // the direction (the mean is no longer needed)
+      if (a.dir) a.dir[((int64_t)h * a.ndir + node) * D + i] = v;
+    }
+  }
+  __syncthreads();
+
+  // 4. projections of every point, 16 lanes per point, four points in flight
+  {
+    constexpr int PL = D / 16;
+    typedef uint32_t pw_t __attribute__((ext_vector_type(PL / 2)));
+    const int grp = tid >> 4, sub = tid & 15;
+    float vv[PL];
+#pragma unroll
+    for (int k = 0; k < PL; ++k) vv[k] = mu[sub * PL + k];
+    for (int p0 = grp; p0 < n; p0 += 4 * (NT / 16)) {
+      int t[4];
+      pw_t xw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int p = p0 + j * (NT / 16);
+        t[j] = p < n ? perm[p] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xw[j] = *(const pw_t *)(X + (int64_t)t[j] * D + sub * PL);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float acc2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < PL; ++k) {
+          const uint32_t w = xw[j][k >> 1];
+          acc2 = fmaf(bf2f((uint16_t)((k & 1) ? (w >> 16) : (w & 0xFFFFu))), vv[k], acc2);
+        }
+        acc2 += __shfl_xor(acc2, 1, 64);
+        acc2 += __shfl_xor(acc2, 2, 64);
+        acc2 += __shfl_xor(acc2, 4, 64);
+        acc2 += __shfl_xor(acc2, 8, 64);
+        const int p = p0 + j * (NT / 16);
+        if (sub == 0 && p < n) {
+          key[p] = f2ord(acc2 + 0.f);  // -0 and +0 order alike
+          tmp[p] = t[j];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // radix select of the nl-th smallest key (1-based rank nl)
+  if (tid == 0) { sh_prefix = 0u; sh_rank = (uint32_t)nl; }
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int q = tid; q < 256; q += NT) hist[q] = 0u;
+    __syncthreads();
+    const uint32_t prefix = sh_prefix;
+    const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    for (int p = tid; p < n; p += NT) {
+      const uint32_t kv = key[p];
+      if ((kv & hmask) == prefix) atomicAdd(&hist[(kv >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t rk = sh_rank, run = 0;
+      int bin = 255;
+      for (int bb = 0; bb < 256; ++bb) {
+        if (run + hist[bb] >= rk) { bin = bb; break; }
+        run += hist[bb];
+      }
+      sh_prefix = prefix | ((uint32_t)bin << shift);
+      sh_rank = rk - run;
+    }
+    __syncthreads();
+  }
+  const uint32_t thr = sh_prefix;       // the nl-th smallest key
+  const int eq_left = (int)sh_rank;     // keys equal to thr that still go left, in position order
+
+  // stable partition: left = key < thr, or key == thr among the first eq_left such positions
+  int base_left = 0, base_eq = 0;
+  for (int c0 = 0; c0 < n; c0 += NT) {
+    const int p = c0 + tid;
+    const uint32_t kv = p < n ? key[p] : 0xFFFFFFFFu;
+    const bool valid = p < n;
+    const int lt = valid && kv < thr, eq = valid && kv == thr;
+    int2 tot;
+    const int2 pre = block_scan2(lt, eq, scan_sh, tot);
+    const bool left = lt || (eq && base_eq + pre.y < eq_left);
+    // left positions so far: strict ones plus the equal ones admitted
+    const int eq_admit_before = min(max(eq_left - base_eq, 0), pre.y);
+    const int left_before = base_left + pre.x + eq_admit_before;
+    if (valid) {
+      const int dst = left ? left_before : nl + (p - left_before);
+      perm[dst] = tmp[p];
+    }
+    const int eq_admit_chunk = min(max(eq_left - base_eq, 0), tot.y);
+    base_left += tot.x + eq_admit_chunk;
+    base_eq += tot.y;
+  }
+}
+
+// Labels, segments and cluster count after the last level: the clusters are
+// the consecutive runs of b positions (the last one ragged).
+__global__ void k_pca_finish(const int *__restrict__ perm, int *__restrict__ labels, int *__restrict__ seg,
+                             int *__restrict__ ncl, int L, int b, int segcap) {
+  const int h = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int nc = (L + b - 1) / b;
+  if (i < L) labels[(int64_t)h * L + perm[(int64_t)h * L + i]] = (int)(i / b);
+  if (i <= segcap) seg[(int64_t)h * (segcap + 1) + i] = (int)min((int64_t)L, i * b);
+  if (i == 0) ncl[h] = nc;
+}
+
+// Mean row of each cluster (fp64 sums in cluster order), stored fp32.
+template <int D>
+__global__ __launch_bounds__(256) void k_seg_rowmean(const uint16_t *__restrict__ X, const int *__restrict__ perm,
+                                                     const int *__restrict__ seg, const int *__restrict__ ncl, int L,
+                                                     int ncap, float *__restrict__ cent) {
+  constexpr int PL = D / 16;
+  typedef uint32_t pw_t __attribute__((ext_vector_type(PL / 2)));
+  const int h = blockIdx.y, c = blockIdx.x;
+  if (c >= ncap) return;
+  float *out = cent + ((int64_t)h * ncap + c) * D;
+  const int grp = threadIdx.x >> 4, sub = threadIdx.x & 15;
+  __shared__ double sh[16][D];
+  double acc[PL];
+#pragma unroll
+  for (int k = 0; k < PL; ++k) acc[k] = 0.0;
+  int beg = 0, end = 0;
+  if (c < ncl[h]) {
+    const int *sg = seg + (int64_t)h * (ncap + 1);
+    beg = sg[c];
+    end = sg[c + 1];
+  }
+  const uint16_t *Xh = X + (int64_t)h * L * D;
+  const int *ph = perm + (int64_t)h * L;
+  for (int p = beg + grp; p < end; p += 16) {
+    const pw_t xw = *(const pw_t *)(Xh + (int64_t)ph[p] * D + sub * PL);
+#pragma unroll
+    for (int k = 0; k < PL; ++k) acc[k] += (double)bf2f((uint16_t)((k & 1) ? (xw[k >> 1] >> 16) : (xw[k >> 1] & 0xFFFFu)));
+  }
+#pragma unroll
+  for (int k = 0; k < PL; ++k) sh[grp][sub * PL + k] = acc[k];
+  __syncthreads();
+  for (int dd = threadIdx.x; dd < D; dd += 256) {
+    double t = 0.0;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) t += sh[g][dd];
+    out[dd] = end > beg ? (float)(t / (double)(end - beg)) : 0.f;
+  }
+}
+
+// perm[h] = 0 .. L-1
+__global__ void k_iota_perm(int *__restrict__ perm, int L) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < L) perm[(int64_t)blockIdx.y * L + i] = (int)i;
+}
+// dst[h * dst_hs + i] = src[h * L + i]
+__global__ void k_copy_rows_i32(const int *__restrict__ src, int *__restrict__ dst, int L, int64_t dst_hs) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < L) dst[(int64_t)blockIdx.y * dst_hs + i] = src[(int64_t)blockIdx.y * L + i];
+}
+
+// host
+std::vector<int> pca_level_counts(int n, int b) {
+  std::vector<int> counts;
+  std::vector<std::pair<int, int>> cur, nxt;
+  if (n > b) cur.push_back({0, n});
+  while (!cur.empty()) {
+    counts.push_back((int)cur.size());
+    nxt.clear();
+    for (auto &nd : cur) {
+      const int nb = (nd.second + b - 1) / b, nl = b * ((nb + 1) / 2), nr = nd.second - nl;
+      if (nl > b) nxt.push_back({nd.first, nl});
+      if (nr > b) nxt.push_back({nd.first + nl, nr});
+    }
+    cur.swap(nxt);
+  }
+  return counts;
+}
+
+void launch_pca_split(int D, const PcaArgs &a, const std::vector<int> &counts, int BH, int *perm_trace,
+                      hipStream_t st) {
+  hipLaunchKernelGGL(k_pca_tree, dim3(1), dim3(1), 0, st, a.L, a.block, a.nodes, a.lvl);
+  hipLaunchKernelGGL(k_iota_perm, dim3((unsigned)((a.L + 255) / 256), (unsigned)BH), dim3(256), 0, st, a.perm, a.L);
+  const size_t lds = (size_t)D * PCA_SP * 2 > (size_t)D * D * 4 ? (size_t)D * PCA_SP * 2 : (size_t)D * D * 4;
+  // dynamic LDS above the default limit (a refusal shows up as a launch error)
+  static bool lds64 = hipFuncSetAttribute((const void *)k_pca_level<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                          64 * PCA_SP * 2) == hipSuccess;
+  static bool lds128 = hipFuncSetAttribute((const void *)k_pca_level<128>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 128 * PCA_SP * 2) == hipSuccess;
+  (void)lds64;
+  (void)lds128;
+  int first = 0;
+  for (size_t l = 0; l < counts.size(); ++l) {
+    if (D == 64)
+      hipLaunchKernelGGL(k_pca_level<64>, dim3((unsigned)counts[l], (unsigned)BH), dim3(512), lds, st, a, first,
+                         counts[l]);
+    else
+      hipLaunchKernelGGL(k_pca_level<128>, dim3((unsigned)counts[l], (unsigned)BH), dim3(512), lds, st, a, first,
+                         counts[l]);
+    if (perm_trace)
+      hipLaunchKernelGGL(k_copy_rows_i32, dim3((unsigned)((a.L + 255) / 256), (unsigned)BH), dim3(256), 0, st, a.perm,
+                         perm_trace + l * (int64_t)a.L, a.L, (int64_t)counts.size() * a.L);
+    first += counts[l];
+  }
+}
+
+void launch_pca_finish(const int *perm, int *labels, int *seg, int *ncl, int L, int b, int segcap, int BH,
+                       hipStream_t st) {
+  const int64_t n = std::max<int64_t>(L, (int64_t)segcap + 1);
+  hipLaunchKernelGGL(k_pca_finish, dim3((unsigned)((n + 255) / 256), (unsigned)BH), dim3(256), 0, st, perm, labels,
+                     seg, ncl, L, b, segcap);
+}
+
+void launch_seg_rowmean(int D, const uint16_t *X, const int *perm, const int *seg, const int *ncl, int L, int ncap,
+                        float *cent, int BH, hipStream_t st) {
+  if (D == 64)
+    hipLaunchKernelGGL(k_seg_rowmean<64>, dim3((unsigned)ncap, (unsigned)BH), dim3(256), 0, st, X, perm, seg, ncl, L,
+                       ncap, cent);
+  else
+    hipLaunchKernelGGL(k_seg_rowmean<128>, dim3((unsigned)ncap, (unsigned)BH), dim3(256), 0, st, X, perm, seg, ncl,
+                       L, ncap, cent);
+}
+
+}  // namespace ac

@@ -242,6 +242,40 @@ ac_status ac_cluster_k_trace(const ac_shape *s, const ac_params *p, const uint16
 ac_status ac_cluster_q_trace(const ac_shape *s, const ac_params *p, const uint16_t *Q, ac_clusters *q_out,
                              float *cent_trace, void *ws, size_t ws_bytes, ac_stream_t stream);
 
+/* ClusterAttention's clustering ("ClusterAttention: training-free acceleration of bidirectional
+ * attention": abstract, cluster sizes fixed to powers of two; end of section 2, recursive splits along
+ * principal components into clusters of a preset size; section 3.1, per head, keys and queries
+ * separately).  Per head, a node of n > block rows (initially all L) is cut in two by its leading
+ * principal direction: the block * ceil(ceil(n / block) / 2) rows with the smallest projections
+ * (ties: lower token index) go left, the rest right, each side keeping its token order; nodes of
+ * at most block rows are clusters.  So every cluster holds exactly `block` tokens except the last
+ * (L mod block when nonzero), clusters are numbered left to right, and each lists its tokens in
+ * ascending order.  The direction of a node is the leading eigenvector of the covariance of a strided
+ * subsample {floor(j n / s)} of s = min(n, 512) of its rows, centred and rounded to bf16 (the page's
+ * "approximate" projection), found by 64 power iterations from the subsample row farthest from the
+ * mean and oriented so that its component of largest magnitude is positive.  block: a power of two in
+ * [16, 4096] with ceil(L / block) <= the cluster capacity (AC_E_ARG otherwise).
+ *
+ * ac_cluster_q_pca clusters the normalised queries (bf16(q / ||q||), as ac_cluster_q): q_out gets
+ * labels, perm, seg, ncl = ceil(L / block), cent = member mean of the normalised queries, rho = member
+ * mean of ||q||; q_out->ncap = min(p->nq, L) must hold ceil(L / block) clusters.  ac_cluster_k_pca
+ * clusters the raw keys: k_out as ac_cluster_k's (cent = member mean) and the statistics of
+ * ac_cluster_k, with fallback 0, tau 0 and stages = the number of split levels.  The results feed
+ * ac_score_select and ac_sparse_attn; with block equal to the attention's query tile (256 rows at
+ * d = 128, 384 is not a power of two so 256 at d = 64 too) no query block is partial.
+ * trace (may be NULL): dir [BH, ceil(L / block) - 1, d] fp32, each internal node's direction, levels in
+ * order and left to right within a level; perm [BH, levels, L], the token order after each level. */
+typedef struct ac_pca_trace {
+  float *dir;
+  int32_t *perm;
+} ac_pca_trace;
+ac_status ac_cluster_q_pca(const ac_shape *s, const ac_params *p, const uint16_t *Q, int32_t block,
+                           ac_clusters *q_out, const ac_pca_trace *trace, void *ws, size_t ws_bytes,
+                           ac_stream_t stream);
+ac_status ac_cluster_k_pca(const ac_shape *s, const ac_params *p, const uint16_t *K, const uint16_t *V,
+                           int32_t block, ac_clusters *k_out, ac_kstats *stats, const ac_pca_trace *trace,
+                           void *ws, size_t ws_bytes, ac_stream_t stream);
+
 /* Scores of every (query cluster r, key cluster c) pair and the selection of key clusters for
  * each query cluster.  QUEST: S_rc = sum_d max(cq_r[d] kmax_c[d], cq_r[d] kmin_c[d]) (AdaCluster
  * eq. (1)), evaluated as the single product [cq+, cq-] . [kmax; kmin] on MFMA (the exact form of

@@ -35,6 +35,7 @@ def test_struct_sizes_match_c_layout():
     assert ctypes.sizeof(ac.CState) == 48
     assert ctypes.sizeof(ac.CSchedule) == 24
     assert ctypes.sizeof(ac.CKTrace) == 56
+    assert ctypes.sizeof(ac.CPcaTrace) == 16
 
 
 def test_defaults_and_status_strings():
@@ -144,6 +145,15 @@ def test_entry_points_reject_bad_arguments_before_any_device_work():
                                   ctypes.byref(st), ctypes.byref(tr0), ws, wsb, None) == ac.AC_E_ARG
     assert lib.ac_cluster_q_trace(ctypes.byref(shape), ctypes.byref(p), 1 << 20, ctypes.byref(q), None, ws, wsb,
                                   None) == ac.AC_E_ARG
+    # principal-component split: block not a power of two, too small, or more clusters than the capacity
+    for blk in (48, 8, 8192):
+        assert lib.ac_cluster_q_pca(ctypes.byref(shape), ctypes.byref(p), 1 << 20, blk, ctypes.byref(q), None, ws,
+                                    wsb, None) == ac.AC_E_ARG, blk
+    assert lib.ac_cluster_q_pca(ctypes.byref(shape), ctypes.byref(p), 1 << 20, 128, ctypes.byref(q), None, ws, wsb,
+                                None) == ac.AC_E_ARG  # 4096 / 128 = 32 clusters > nq = 16
+    assert b"capacity" in lib.ac_last_error()
+    assert lib.ac_cluster_k_pca(ctypes.byref(shape), ctypes.byref(p), 1 << 20, 1 << 20, 32, ctypes.byref(k),
+                                ctypes.byref(st), None, ws, wsb, None) == ac.AC_E_ARG  # 128 clusters > ncap 95
     # NULL state
     assert lib.ac_layer(ctypes.byref(shape), ctypes.byref(p), 1 << 20, 1 << 20, 1 << 20, None, 1 << 20, None, ws, wsb,
                         None) == ac.AC_E_ARG
