@@ -24,6 +24,7 @@ AC_QUEST_MFMA, AC_QUEST_VALU = range(2)
 
 ENTRY_POINTS = ("ac_params_default", "ac_sizes", "ac_cluster_q", "ac_cluster_k", "ac_cluster_k_trace",
                 "ac_cluster_q_trace", "ac_cluster_q_pca", "ac_cluster_k_pca", "ac_score_select",
+                "ac_score_select_noalloc",
                 "ac_sparse_attn", "ac_tail_merge", "ac_score_tokens", "ac_interaction_matrix",
                 "ac_cluster_k_metric", "ac_layer", "ac_topp_schedule",
                 "ac_kmax_calibrate", "ac_step_params", "ac_status_str", "ac_last_error")
@@ -130,6 +131,10 @@ def load() -> ctypes.CDLL:
                                     ctypes.POINTER(CClusters), ctypes.POINTER(CKStats), ctypes.POINTER(CSelection),
                                     vp, ctypes.c_size_t, vp]
     lib.ac_score_select.restype = st
+    lib.ac_score_select_noalloc.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), ctypes.POINTER(CClusters),
+                                            ctypes.POINTER(CClusters), ctypes.POINTER(CKStats),
+                                            ctypes.POINTER(CSelection), vp]
+    lib.ac_score_select_noalloc.restype = st
     lib.ac_sparse_attn.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Params), vp, vp, vp,
                                    ctypes.POINTER(CClusters), ctypes.POINTER(CClusters), ctypes.POINTER(CKStats),
                                    ctypes.POINTER(CSelection), vp, vp, vp, ctypes.c_size_t, vp]
@@ -359,6 +364,13 @@ def ac_score_select(shape, params, q: Clusters, k: Clusters, stats: KStats, sel:
     _check(load().ac_score_select(ctypes.byref(shape), ctypes.byref(params), ctypes.byref(q.c()),
                                   ctypes.byref(k.c()), ctypes.byref(stats.c()), ctypes.byref(sel.c()), _ptr(ws),
                                   ws.numel(), _stream(stream)))
+
+
+def ac_score_select_noalloc(shape, params, q: Clusters, k: Clusters, stats: KStats, sel: Selection, stream=None):
+    """ac_score_select with the library's fixed scratch array instead of a workspace."""
+    _check(load().ac_score_select_noalloc(ctypes.byref(shape), ctypes.byref(params), ctypes.byref(q.c()),
+                                          ctypes.byref(k.c()), ctypes.byref(stats.c()), ctypes.byref(sel.c()),
+                                          _stream(stream)))
 
 
 def ac_sparse_attn(shape, params, Q, K, V, q: Clusters, k: Clusters, stats: KStats, sel: Selection, O, lse=None,

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/ac.h"
@@ -588,10 +589,22 @@ ac_status do_cluster_k_metric(const Plan &P, const ac_params *p, const uint16_t 
   return AC_OK;
 }
 
+// Scratch of the scoring and selection: the GEMM operands, the score matrix
+// (when the caller passes none) and the selected token count of each row.
+struct SelScratch {
+  uint16_t *A, *Bm;
+  float *S;
+  int *seltok;
+};
+
+SelScratch sel_scratch_ws(const Plan &P, void *ws) {
+  return SelScratch{at<uint16_t>(ws, P.scoreA), at<uint16_t>(ws, P.scoreB), at<float>(ws, P.S), at<int>(ws, P.seltok)};
+}
+
 ac_status do_score_select(const Plan &P, const ac_params *p, const ac_clusters *q, const ac_clusters *k,
-                          const ac_kstats *stats, ac_selection *sel, void *ws, hipStream_t st) {
+                          const ac_kstats *stats, ac_selection *sel, const SelScratch &sc, hipStream_t st) {
   const int BH = P.BH, D = P.D;
-  float *S = sel->score ? sel->score : at<float>(ws, P.S);
+  float *S = sel->score ? sel->score : sc.S;
   ScoreArgs sa;
   sa.cq = q->cent;
   sa.nqcap = q->ncap;
@@ -603,8 +616,8 @@ ac_status do_score_select(const Plan &P, const ac_params *p, const ac_clusters *
   sa.ncl_k = k->ncl;
   sa.ncap = k->ncap;
   sa.mode = p->score_mode;
-  sa.A = at<uint16_t>(ws, P.scoreA);
-  sa.Bm = at<uint16_t>(ws, P.scoreB);
+  sa.A = sc.A;
+  sa.Bm = sc.Bm;
   sa.nq_pad = P.nq_pad;
   sa.ncap_pad = P.ncap_pad;
   sa.S = S;
@@ -629,7 +642,7 @@ ac_status do_score_select(const Plan &P, const ac_params *p, const ac_clusters *
   se.nsel = sel->n;
   se.mask = sel->mask;
   se.mwords = P.mwords;
-  se.seltok = at<int>(ws, P.seltok);
+  se.seltok = sc.seltok;
   launch_select(se, BH, st);
   AC_CHECK_LAUNCH();
   return AC_OK;
@@ -875,7 +888,80 @@ AC_API ac_status ac_score_select(const ac_shape *s, const ac_params *p, const ac
   AC_TRY(check_sel(sel, P.ncapk));
   AC_TRY(check_ws(P, ws, ws_bytes));
   AC_TRY(check_device());
-  return do_score_select(P, p, q, k, stats, sel, ws, (hipStream_t)stream);
+  return do_score_select(P, p, q, k, stats, sel, sel_scratch_ws(P, ws), (hipStream_t)stream);
+}
+
+namespace ac {
+namespace {
+// Scratch of ac_score_select_noalloc: a fixed array in device memory, one copy
+// per GPU the library runs on, held until the process ends.  Host code never
+// uses the array's name as an address: hipGetSymbolAddress gives each device's
+// copy, looked up once per device with that device current.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+ac_status scratch_address(unsigned char **out) {
+  static std::mutex mu;
+  static void *addr[64] = {};
+  int dev = 0;
+  AC_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(AC_E_DEVICE, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *ptr = nullptr;
+    AC_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr) return fail(AC_E_DEVICE, "hipGetSymbolAddress returned no address for the scratch array");
+    addr[dev] = ptr;
+  }
+  *out = static_cast<unsigned char *>(addr[dev]);
+  return AC_OK;
+}
+
+// Carve the scoring scratch from `base`; returns the bytes it needs.
+size_t sel_scratch_fixed(const Plan &P, bool need_S, unsigned char *base, SelScratch *sc) {
+  const size_t BH = P.BH, D = P.D;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + std::max<size_t>(bytes, 1));
+    return o;
+  };
+  const size_t a = take(BH * P.nq_pad * 6 * D * 2);
+  const size_t b = take(BH * P.ncap_pad * 6 * D * 2);
+  const size_t s = need_S ? take(BH * P.nq * (size_t)P.ncapk * 4) : 0;
+  const size_t t = take(BH * P.nq * 4);
+  if (sc && base)
+    *sc = SelScratch{reinterpret_cast<uint16_t *>(base + a), reinterpret_cast<uint16_t *>(base + b),
+                     need_S ? reinterpret_cast<float *>(base + s) : nullptr, reinterpret_cast<int *>(base + t)};
+  return off;
+}
+}  // namespace
+}  // namespace ac
+
+AC_API ac_status ac_score_select_noalloc(const ac_shape *s, const ac_params *p, const ac_clusters *q,
+                                         const ac_clusters *k, const ac_kstats *stats, ac_selection *sel,
+                                         ac_stream_t stream) {
+  AC_TRY(check_shape(s));
+  AC_TRY(check_params(s, p));
+  Plan P = make_plan(s, p);
+  AC_TRY(check_clusters(q, "query", P.nq, true));
+  if (q->ncap != P.nq) return fail(AC_E_ARG, "query clusters ncap must be min(nq, L) = %d", P.nq);
+  AC_TRY(check_clusters(k, "key", P.ncapk, false));
+  if (k->ncap != P.ncapk) return fail(AC_E_ARG, "key clusters ncap must be %d", P.ncapk);
+  AC_TRY(check_kstats(stats));
+  AC_TRY(check_sel(sel, P.ncapk));
+  const size_t need = sel_scratch_fixed(P, sel->score == nullptr, nullptr, nullptr);
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail(AC_E_UNSUPPORTED,
+                "ac_score_select_noalloc needs %zu bytes of scratch for this shape; its fixed array holds %zu "
+                "(use ac_score_select with a workspace, fewer heads per call, or pass sel->score)",
+                need, NOALLOC_SCRATCH_BYTES);
+  AC_TRY(check_device());
+  unsigned char *base = nullptr;
+  AC_TRY(scratch_address(&base));
+  SelScratch sc;
+  sel_scratch_fixed(P, sel->score == nullptr, base, &sc);
+  return do_score_select(P, p, q, k, stats, sel, sc, (hipStream_t)stream);
 }
 
 AC_API ac_status ac_sparse_attn(const ac_shape *s, const ac_params *p, const uint16_t *Q, const uint16_t *K,
@@ -1067,7 +1153,7 @@ AC_API ac_status ac_layer(const ac_shape *s, const ac_params *p, const uint16_t 
   AC_HIP(hipStreamWaitEvent(st, ss->join, 0));
   AC_TRY(sq);
   AC_TRY(sk);
-  AC_TRY(do_score_select(P, p, &q, &k, &ks, &sel, ws, st));
+  AC_TRY(do_score_select(P, p, &q, &k, &ks, &sel, sel_scratch_ws(P, ws), st));
   if (p->tail_block > 0) {
     ac_clusters qm{P.nq, at<int>(ws, P.m_labels), at<int>(ws, P.m_perm), at<int>(ws, P.m_seg), q.cent, q.ncl, q.rho};
     ac_selection sm{P.ncapk, at<int>(ws, P.m_list), at<int>(ws, P.m_n), at<uint32_t>(ws, P.m_mask), nullptr};

@@ -285,6 +285,19 @@ ac_status ac_score_select(const ac_shape *s, const ac_params *p, const ac_cluste
                           const ac_clusters *k, const ac_kstats *stats, ac_selection *sel, void *ws,
                           size_t ws_bytes, ac_stream_t stream);
 
+/* ac_score_select for callers that cannot allocate or pass a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same kernels and results,
+ * with the scratch (the GEMM operands of the scores, the score matrix when sel->score is NULL, and
+ * the token count of each selection) in a fixed 64 MiB array of device memory inside the library,
+ * one copy per GPU it runs on, kept until the process ends.  Allocates nothing.  Returns
+ * AC_E_UNSUPPORTED, before any device work, when the shape needs more scratch than the array holds
+ * (about 12 * d * BH * (ncap_k + nq + 32) bytes, plus BH * nq * ncap_k * 4 when sel->score is NULL:
+ * e.g. up to 20 heads with the default parameters at d = 128).  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (several streams or host threads) race, so order them. */
+ac_status ac_score_select_noalloc(const ac_shape *s, const ac_params *p, const ac_clusters *q,
+                                  const ac_clusters *k, const ac_kstats *stats, ac_selection *sel,
+                                  ac_stream_t stream);
+
 /* AdaCluster Algorithm 3 lines "K* <- K[Index], V* <- V[Index], Attention(Q, K*, V*)": every query
  * of query cluster r attends, with scale p->scale (0: 1/sqrt(d)), to the keys of the key clusters
  * selected for r, softmax-normalised over that set (ClusterAttention §1.2 eq. (2)).  With
