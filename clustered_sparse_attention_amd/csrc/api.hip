@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <vector>
 
@@ -125,6 +126,11 @@ struct Plan {
   size_t qsum, qcnt;
   // principal-component split: token scratch, projection keys, node table
   size_t pca_tmp, pca_key, pca_nodes, pca_lvl;
+  // cold key clustering: operands of every stage's centres at their global
+  // rows, the running nearest-centre score, per-stage centre counts and
+  // offsets for the merge launches, Algorithm 1's per-head state, all-L counts
+  size_t fops_hi, fops_lo, fops_norm, best, mtab, ctab, kst, nall;
+  int stage_slots;
 };
 
 // stride of the per-selection key row lists: whole key tiles
@@ -233,6 +239,16 @@ Plan make_plan(const ac_shape *s, const ac_params *p) {
   P.pca_key = take(BH * L * 4);
   P.pca_nodes = take((L / PCA_BLOCK_MIN + 2) * 8);  // at most ceil(L / b) - 1 internal nodes
   P.pca_lvl = take(64 * 4);
+  P.fops_hi = take(BH * P.ncapk * D * 2);
+  P.fops_lo = take(BH * P.ncapk * D * 2);
+  P.fops_norm = take(BH * P.ncapk * 4);
+  P.best = take(BH * L * 4);
+  // every stage but the last adds min(L, m0) centres, and none starts at nmax or beyond
+  P.stage_slots = (int)cdiv(p->nmax, std::max(1, std::min(p->m0, P.L))) + 2;
+  P.mtab = take((size_t)P.stage_slots * BH * 4);
+  P.ctab = take((size_t)P.stage_slots * BH * 4);
+  P.kst = take(BH * KST_FIELDS * 4);
+  P.nall = take(BH * 4);
   P.total = off + 256;  // slack for aligning the base pointer
   return P;
 }
@@ -306,20 +322,31 @@ struct Engine {
   // minimises (x - c) M (x - c)^T (centre operands M c and c M c^T)
   // tc (optional): record of the centres after seeding (slot 0) and after each
   // Lloyd update (slot j), head stride tc.hs, slot stride tc.it
+  // k-means++ seeding of the job's centres.  Its grids depend only on the
+  // engine's subsample cap, so it can be enqueued before the host knows the
+  // job's point counts (heads with n = 0 or m = 0 are idle).
+  ac_status seed(const KmArgs &a, const ac_params *p, int role, int stage) {
+    if (S.kpp_smax <= KPP_GRAM_MAX)
+      launch_kpp_gram(P.D, a, P.BH, S.kpp_smax, at<double>(ws, S.kpp_nx), at<double>(ws, S.kpp_G), p->init_sample,
+                      p->seed, role, stage, st);
+    else
+      launch_kpp(P.D, a, P.BH, at<double>(ws, S.d2buf), p->init_sample, p->seed, role, stage, st);
+    AC_CHECK_LAUNCH();
+    return AC_OK;
+  }
   ac_status run(const KmArgs &a, int mmax, int npts, bool seed_init, int iters, const ac_params *p, int role,
                 int stage, int *labels_out, const float *metric = nullptr, TraceCent tc = TraceCent()) {
+    if (seed_init) AC_TRY(seed(a, p, role, stage));
+    return lloyd(a, mmax, npts, iters, labels_out, metric, tc);
+  }
+  // iters Lloyd iterations from the job's current centres, then the final
+  // assignment into labels_out
+  ac_status lloyd(const KmArgs &a, int mmax, int npts, int iters, int *labels_out, const float *metric = nullptr,
+                  TraceCent tc = TraceCent()) {
     const int D = P.D;
     auto trace = [&](int slot) {
       if (tc.p) launch_trace_cent(D, a, P.BH, mmax, tc.p + slot * tc.it, tc.hs, st);
     };
-    if (seed_init) {
-      if (S.kpp_smax <= KPP_GRAM_MAX)
-        launch_kpp_gram(D, a, P.BH, S.kpp_smax, at<double>(ws, S.kpp_nx), at<double>(ws, S.kpp_G), p->init_sample,
-                        p->seed, role, stage, st);
-      else
-        launch_kpp(D, a, P.BH, at<double>(ws, S.d2buf), p->init_sample, p->seed, role, stage, st);
-      AC_CHECK_LAUNCH();
-    }
     trace(0);
     CentOps op = ops();
     launch_cent_prep(D, a, op, P.BH, mmax, st);
@@ -336,6 +363,8 @@ struct Engine {
     // still in the loop; the others keep the loop's last labels, which it
     // would repeat.
     int *chg = at<int>(ws, S.chg), *neff = at<int>(ws, S.neff);
+    // heads of few points: the counting sort and the update are one launch each
+    const bool small = npts <= SORT_SMALL_MAX && mmax <= SORT_SMALL_M;
     KmArgs al = a;
     if (iters > 0) {
       launch_copy_i32(a.n, neff, P.BH, st);
@@ -351,8 +380,13 @@ struct Engine {
       s.chg_zero = nxt;
       s.chunk_off = at<int>(ws, S.chunk_off);
       s.co_hs = S.mcap + 1;
-      launch_sort(s, P.BH, npts, st);
-      launch_update(D, al, s, op, P.BH, mmax, npts, at<double>(ws, S.upd_part), (int64_t)S.upd_items * D, st);
+      if (small) {
+        launch_sort_small(s, P.BH, st);
+        launch_update_small(D, al, s, op, P.BH, mmax, st);
+      } else {
+        launch_sort(s, P.BH, npts, st);
+        launch_update(D, al, s, op, P.BH, mmax, npts, at<double>(ws, S.upd_part), (int64_t)S.upd_items * D, st);
+      }
       if (metric) launch_cent_prep_metric(D, a, op, metric, P.BH, mmax, st);
       trace(it + 1);
       AC_CHECK_LAUNCH();
@@ -424,9 +458,11 @@ ac_status finish_keys(const Plan &P, const uint16_t *K, const uint16_t *V, ac_cl
   return AC_OK;
 }
 
-ac_status do_cluster_k_cold(const Plan &P, const ac_params *p, const uint16_t *K, const uint16_t *V,
-                            ac_clusters *k, ac_kstats *stats, void *ws, hipStream_t st,
-                            const ac_ktrace *tr = nullptr) {
+// Algorithm 1 with the stage loop on the host (centre counts above the
+// resident assignment's limit).
+ac_status do_cluster_k_cold_plain(const Plan &P, const ac_params *p, const uint16_t *K, const uint16_t *V,
+                                  ac_clusters *k, ac_kstats *stats, void *ws, hipStream_t st,
+                                  const ac_ktrace *tr) {
   const int BH = P.BH, L = P.L, D = P.D;
   Engine E{P, P.sk, ws, st};
   std::vector<int> nU(BH, L), nC(BH, 0), done(BH, 0), F(BH, 0), stg(BH, 0), nmc(3 * (size_t)BH);
@@ -504,6 +540,143 @@ ac_status do_cluster_k_cold(const Plan &P, const ac_params *p, const uint16_t *K
   AC_TRY(finish_keys(P, K, V, k, stats, ws, st, mmax));
   // the host vectors above must outlive the copies
   AC_HIP(hipStreamSynchronize(st));
+  return AC_OK;
+}
+
+ac_status aux_stream(int which, hipStream_t *out, hipEvent_t *fork, hipEvent_t *join);
+ac_status pinned_i32(int n, int **out);
+
+// Algorithm 1 (AdaCluster §3.2.2) with the per-head bookkeeping on the device.
+// Each stage: the Lloyd loop of its k-means (grids sized by the host from
+// the counts read one stage earlier), the distances, tau (first stage), the
+// removal flags and the stable compaction of U; then k_stage_next closes the
+// stage and opens the next one (centre count, fallback flag, n, m, offset).
+// The next stage's k-means++ seeding is enqueued at once (its grids do not
+// depend on the counts), and the host reads the new counts from pinned
+// memory behind it, so the GPU does not wait for the host at stage
+// boundaries.  The final nearest centre of every key over all stages is
+// computed stage by stage on an auxiliary stream as each stage's centres
+// are final (merge-mode assignment: strictly better only, so ties keep the
+// lowest centre index), beside the following stages.
+// after_first (optional) is called once the first stage is enqueued, before
+// the host first waits: ac_layer enqueues the query clustering there, so
+// that the key stream starts at once and the host's launch work for the
+// queries overlaps the first stage.
+ac_status do_cluster_k_cold(const Plan &P, const ac_params *p, const uint16_t *K, const uint16_t *V,
+                            ac_clusters *k, ac_kstats *stats, void *ws, hipStream_t st,
+                            const ac_ktrace *tr = nullptr,
+                            const std::function<ac_status()> &after_first = nullptr) {
+  const int BH = P.BH, L = P.L, D = P.D;
+  if (std::min(p->m0, L) > ASSIGN_RES_MAX) {
+    if (after_first) AC_TRY(after_first());
+    return do_cluster_k_cold_plain(P, p, K, V, k, stats, ws, st, tr);
+  }
+  Engine E{P, P.sk, ws, st};
+  int *uidx[2] = {at<int>(ws, P.uidx0), at<int>(ws, P.uidx1)};
+  int cur = 0;
+  float *dist = at<float>(ws, P.dist);
+  int *flag = at<int>(ws, P.flag);
+  int *kst = at<int>(ws, P.kst);
+  int *mtab = at<int>(ws, P.mtab), *ctab = at<int>(ws, P.ctab);
+  float *best = at<float>(ws, P.best);
+  CentOps fops{at<uint16_t>(ws, P.fops_hi), at<uint16_t>(ws, P.fops_lo), at<float>(ws, P.fops_norm), P.ncapk};
+  hipStream_t ax;
+  hipEvent_t ev_fork, ev_join;
+  AC_TRY(aux_stream(1, &ax, &ev_fork, &ev_join));
+  int *hnm = nullptr;  // pinned: n then m of the next stage
+  AC_TRY(pinned_i32(2 * BH, &hnm));
+  // the merge launches start from "no centre yet"
+  launch_fill_i32(at<int>(ws, P.nall), BH, L, st);
+  launch_fill_i32(reinterpret_cast<int *>(best), (int64_t)BH * L, (int)0xff800000u, st);  // -inf
+  launch_stage_next(kst, nullptr, E.n(), E.m(), E.coff(), 0, p->nmax, p->m0, L, BH, st);
+  AC_CHECK_LAUNCH();
+  int nmaxpts = L, mmax = std::min(p->m0, L);
+  auto args = [&](int t, int c) {
+    return KmArgs{K, (int64_t)L * D, t == 0 ? nullptr : uidx[c], L, E.n(), E.m(), E.coff(), k->cent,
+                  (int64_t)k->ncap * D};
+  };
+  AC_TRY(E.seed(args(0, cur), p, 1, 0));
+  for (int t = 0;; ++t) {
+    if (t >= P.stage_slots) return fail(AC_E_DEVICE, "Algorithm 1 ran more stages (%d) than it can", t);
+    KmArgs a = args(t, cur);
+    int *lab = at<int>(ws, E.S.lab);
+    const bool rec = tr && t < tr->max_stages;
+    TraceCent tc;
+    if (rec && tr->cent) {
+      tc.it = (int64_t)p->m0 * D;
+      const int64_t stage_stride = (int64_t)(p->iters + 1) * tc.it;
+      tc.hs = (int64_t)tr->max_stages * stage_stride;
+      tc.p = tr->cent + t * stage_stride;
+    }
+    if (rec) launch_trace_nm(E.n(), E.m(), tr->n, tr->m, tr->max_stages, t, BH, st);
+    AC_TRY(E.lloyd(a, mmax, nmaxpts, p->iters, lab, nullptr, tc));
+    // this stage's centres are final: their operands at global rows, and the
+    // merge into every key's nearest centre on the auxiliary stream
+    launch_copy_i32(E.m(), mtab + (int64_t)t * BH, BH, st);
+    launch_copy_i32(E.coff(), ctab + (int64_t)t * BH, BH, st);
+    launch_cent_prep(D, a, fops, BH, mmax, st, true);
+    AC_CHECK_LAUNCH();
+    const int mmax_t = mmax;
+    launch_stage_dist(D, a, BH, nmaxpts, lab, L, dist, L, st);
+    if (rec && (tr->u || tr->labels || tr->dist)) {
+      const int64_t ohs = (int64_t)tr->max_stages * L, oo = (int64_t)t * L;
+      launch_trace_stage(E.n(), t == 0 ? nullptr : uidx[cur], L, lab, dist, L, tr->u ? tr->u + oo : nullptr,
+                         tr->labels ? tr->labels + oo : nullptr, tr->dist ? tr->dist + oo : nullptr, ohs, BH,
+                         nmaxpts, st);
+    }
+    if (t == 0)
+      launch_tau(dist, L, E.n(), BH, nmaxpts, p->tau_rule, p->tau_param, stats->tau, at<uint32_t>(ws, P.rstate),
+                 at<uint32_t>(ws, P.rhist), st);
+    launch_flag_removed(dist, L, E.n(), stats->tau, flag, L, BH, nmaxpts, st);
+    // stable compaction: label 0 (kept) first
+    launch_fill_i32(E.m(), BH, 2, st);
+    SortArgs s = E.sort_args(flag, at<int>(ws, E.S.lperm), at<int>(ws, E.S.lseg), 1, 2);
+    if (nmaxpts <= SORT_SMALL_MAX) launch_sort_small(s, BH, st);
+    else launch_sort(s, BH, nmaxpts, st);
+    launch_compact_gather(t == 0 ? nullptr : uidx[cur], L, at<int>(ws, E.S.lperm), L, at<int>(ws, E.S.lseg), 2,
+                          uidx[cur ^ 1], at<int>(ws, P.hnew), BH, nmaxpts, st);
+    // close this stage, open the next; read its counts behind its seeding
+    launch_stage_next(kst, at<int>(ws, P.hnew), E.n(), E.m(), E.coff(), t + 1, p->nmax, p->m0, L, BH, st);
+    AC_CHECK_LAUNCH();
+    // the merge of this stage's centres runs beside the next stage's seeding
+    // (latency-bound, few CUs) rather than beside this stage's short tail
+    AC_HIP(hipEventRecord(ev_fork, st));
+    AC_HIP(hipStreamWaitEvent(ax, ev_fork, 0));
+    {
+      KmArgs am{K, (int64_t)L * D, nullptr, 0, at<int>(ws, P.nall), mtab + (int64_t)t * BH,
+                ctab + (int64_t)t * BH, k->cent, (int64_t)k->ncap * D};
+      launch_assign(D, am, fops, BH, mmax_t, L, k->labels, L, ax, nullptr, best);
+      AC_CHECK_LAUNCH();
+    }
+    AC_HIP(hipMemcpyAsync(hnm, E.n(), (size_t)BH * 4, hipMemcpyDeviceToHost, st));
+    AC_HIP(hipMemcpyAsync(hnm + BH, E.m(), (size_t)BH * 4, hipMemcpyDeviceToHost, st));
+    AC_HIP(hipEventRecord(ev_join, st));
+    cur ^= 1;
+    AC_TRY(E.seed(args(t + 1, cur), p, 1, t + 1));
+    if (t == 0 && after_first) AC_TRY(after_first());
+    AC_HIP(hipEventSynchronize(ev_join));
+    int active = 0;
+    nmaxpts = 0;
+    mmax = 0;
+    for (int h = 0; h < BH; ++h) {
+      if (hnm[h] > 0 && hnm[BH + h] > 0) ++active;
+      nmaxpts = std::max(nmaxpts, hnm[h]);
+      mmax = std::max(mmax, hnm[BH + h]);
+    }
+    if (!active) break;
+  }
+  launch_stage_final(kst, k->ncl, stats->fallback, stats->stages, BH, st);
+  // the last merge launch before the labels are sorted
+  AC_HIP(hipEventRecord(ev_join, ax));
+  AC_HIP(hipStreamWaitEvent(st, ev_join, 0));
+  SortArgs s = E.sort_args(k->labels, k->perm, k->seg, k->ncap, k->ncap);
+  launch_fill_i32(E.n(), BH, L, st);
+  launch_copy_i32(k->ncl, E.m(), BH, st);
+  launch_sort(s, BH, L, st);
+  KStatsArgs ks{K, V, k->perm, k->seg, k->ncl, k->cent, stats->kmax, stats->kmin, stats->kmean, stats->vmean,
+                at<double>(ws, P.msepart), stats->mse, L, k->ncap};
+  launch_kstats(D, ks, BH, st);
+  AC_CHECK_LAUNCH();
   return AC_OK;
 }
 
@@ -1075,6 +1248,48 @@ struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
 };
+// Auxiliary streams of the library (default priority), per device and host
+// thread, created on first use and kept until the process ends: 0 runs the
+// query clustering beside the key clustering (ac_layer), 1 the per-stage
+// merges of the final key assignment.
+ac_status aux_stream(int which, hipStream_t *out, hipEvent_t *fork, hipEvent_t *join) {
+  static thread_local SideStream tab[2][64];
+  int dev = 0;
+  AC_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64 || which < 0 || which > 1) return fail(AC_E_DEVICE, "device ordinal %d out of range", dev);
+  SideStream &x = tab[which][dev];
+  if (!x.s) {
+    AC_HIP(hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking));
+    AC_HIP(hipEventCreateWithFlags(&x.fork, hipEventDisableTiming));
+    AC_HIP(hipEventCreateWithFlags(&x.join, hipEventDisableTiming));
+  }
+  *out = x.s;
+  if (fork) *fork = x.fork;
+  if (join) *join = x.join;
+  return AC_OK;
+}
+
+// Pinned host staging for the stage counts, per device and host thread, grown
+// on demand and kept until the process ends.
+ac_status pinned_i32(int n, int **out) {
+  static thread_local int *buf[64] = {};
+  static thread_local int cap[64] = {};
+  int dev = 0;
+  AC_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(AC_E_DEVICE, "device ordinal %d out of range", dev);
+  if (cap[dev] < n) {
+    if (buf[dev]) AC_HIP(hipHostFree(buf[dev]));
+    buf[dev] = nullptr;
+    cap[dev] = 0;
+    void *p = nullptr;
+    AC_HIP(hipHostMalloc(&p, (size_t)n * 4, hipHostMallocDefault));
+    buf[dev] = static_cast<int *>(p);
+    cap[dev] = n;
+  }
+  *out = buf[dev];
+  return AC_OK;
+}
+
 ac_status side_stream(SideStream **out) {
   static thread_local SideStream tab[64];
   int dev = 0;
@@ -1146,13 +1361,19 @@ AC_API ac_status ac_layer(const ac_shape *s, const ac_params *p, const uint16_t 
   AC_TRY(side_stream(&ss));
   AC_HIP(hipEventRecord(ss->fork, st));
   AC_HIP(hipStreamWaitEvent(ss->s, ss->fork, 0));
-  const ac_status sq = do_cluster_q(P, p, Q, warm ? state->cent_q : nullptr, &q, ws, ss->s);
-  AC_HIP(hipEventRecord(ss->join, ss->s));
-  const ac_status sk = warm ? do_cluster_k_warm(P, p, K, V, state, &k, &ks, ws, st)
-                            : do_cluster_k_cold(P, p, K, V, &k, &ks, ws, st);
+  auto queries = [&]() -> ac_status {
+    AC_TRY(do_cluster_q(P, p, Q, warm ? state->cent_q : nullptr, &q, ws, ss->s));
+    AC_HIP(hipEventRecord(ss->join, ss->s));
+    return AC_OK;
+  };
+  if (warm) {
+    AC_TRY(queries());
+    AC_TRY(do_cluster_k_warm(P, p, K, V, state, &k, &ks, ws, st));
+  } else {
+    // the query clustering is enqueued once the first key stage is
+    AC_TRY(do_cluster_k_cold(P, p, K, V, &k, &ks, ws, st, nullptr, queries));
+  }
   AC_HIP(hipStreamWaitEvent(st, ss->join, 0));
-  AC_TRY(sq);
-  AC_TRY(sk);
   AC_TRY(do_score_select(P, p, &q, &k, &ks, &sel, sel_scratch_ws(P, ws), st));
   if (p->tail_block > 0) {
     ac_clusters qm{P.nq, at<int>(ws, P.m_labels), at<int>(ws, P.m_perm), at<int>(ws, P.m_seg), q.cent, q.ncl, q.rho};

@@ -23,6 +23,8 @@ constexpr int SEL_MAXN = 4096;   // most key clusters the select kernel sorts
 constexpr int ASSIGN_RES_MAX = 224;  // most centres the LDS-resident assignment holds
 constexpr int UPD_CHUNK = 256;   // members per block in the centre update
 constexpr int KST_FIELDS = 8;    // ints of Algorithm 1's per-head state on the device
+constexpr int SORT_SMALL_MAX = 2048;   // points per head up to which one block per head sorts (and updates)
+constexpr int SORT_SMALL_M = 256;      // labels that path handles
 
 enum { TAU_RULE_MEAN_X = 0, TAU_RULE_PCTL = 1, TAU_RULE_ABS = 2, TAU_RULE_INF = 3 };
 
@@ -191,14 +193,24 @@ void launch_kpp(int D, const KmArgs &a, int BH, double *d2buf, int init_sample, 
                 hipStream_t st);
 void launch_kpp_gram(int D, const KmArgs &a, int BH, int smax, double *nx, double *G, int init_sample, uint64_t seed,
                      int role, int stage, hipStream_t st);
-void launch_cent_prep(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, hipStream_t st);
+// at_coff: operand rows at the centres' global index coff[h] + c (merge-mode assignment)
+void launch_cent_prep(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, hipStream_t st,
+                      bool at_coff = false);
 // chg (nullable): per-head flag set to 1 when some point's label differs from
 // the one already in `labels` (the caller clears it)
+// best_io (nullable): merge mode of the resident kernel (mmax <= ASSIGN_RES_MAX):
+// the job's centres are one stage's, global index coff[h] + c with operands
+// at op row coff[h] + c, merged into the running nearest centre kept in
+// labels / best_io (scores x.c - |c|^2/2; -inf = none yet)
 void launch_assign(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, int nmax_pts, int *labels, int64_t lab_hs,
-                   hipStream_t st, int *chg = nullptr);
+                   hipStream_t st, int *chg = nullptr, float *best_io = nullptr);
 void launch_sort(const SortArgs &s, int BH, int nmax_pts, hipStream_t st);
 void launch_update(int D, const KmArgs &a, const SortArgs &s, const CentOps &op, int BH, int mmax, int npts,
                    double *partial, int64_t part_hs, hipStream_t st);
+// one launch each for heads of at most SORT_SMALL_MAX points and SORT_SMALL_M labels
+void launch_sort_small(const SortArgs &s, int BH, hipStream_t st);
+void launch_update_small(int D, const KmArgs &a, const SortArgs &s, const CentOps &op, int BH, int mmax,
+                         hipStream_t st);
 void launch_stage_dist(int D, const KmArgs &a, int BH, int nmax_pts, const int *labels, int64_t lab_hs, float *dist,
                        int64_t dist_hs, hipStream_t st);
 void launch_tau(const float *dist, int64_t dist_hs, const int *n_arr, int BH, int nmax_pts, int rule, float param,

@@ -50,15 +50,17 @@ __global__ __launch_bounds__(256) void k_qnorm(const uint16_t *__restrict__ Q, u
 // ---------------------------------------------------------------------------
 // Centre operands for the distance GEMM: hi = bf16(c), lo = bf16(c - hi),
 // and ||c||^2 (fp64 sum, stored fp32).  One wave per centre.
+// at_coff: operand rows at the centres' global index coff[h] + c instead of c.
 template <int D>
-__global__ __launch_bounds__(256) void k_cent_prep(KmArgs a, CentOps op) {
+__global__ __launch_bounds__(256) void k_cent_prep(KmArgs a, CentOps op, int at_coff) {
   const int h = blockIdx.y;
   const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (c >= a.m[h]) return;
   const float *cr = a.cent + (int64_t)h * a.cent_hs + (int64_t)(a.coff[h] + c) * D;
-  uint16_t *hi = op.hi + ((int64_t)h * op.cap + c) * D;
-  uint16_t *lo = op.lo + ((int64_t)h * op.cap + c) * D;
+  const int row = at_coff ? a.coff[h] + c : c;
+  uint16_t *hi = op.hi + ((int64_t)h * op.cap + row) * D;
+  uint16_t *lo = op.lo + ((int64_t)h * op.cap + row) * D;
   double ss = 0.0;
   for (int dd = lane; dd < D; dd += 64) {
     float v = cr[dd];
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(256) void k_cent_prep(KmArgs a, CentOps op) {
     ss += (double)v * (double)v;
   }
   ss = wave_sum(ss);
-  if (lane == 0) op.norm[(int64_t)h * op.cap + c] = (float)ss;
+  if (lane == 0) op.norm[(int64_t)h * op.cap + row] = (float)ss;
 }
 
 // ---------------------------------------------------------------------------
@@ -205,9 +207,19 @@ __global__ __launch_bounds__(256) void k_assign(KmArgs a, CentOps op, int *__res
 // wave at a time.  Blocks are sized to one per compute unit, so there is no
 // per-tile barrier and each wave's point loads overlap the other waves'
 // MFMA work.
+//
+// Merge mode (best != NULL): the launch scores one stage's centres (global
+// indices coff[h] + c, operands at op row coff[h] + c) against a running
+// nearest centre per point kept in labels / best from earlier launches, and
+// replaces it only for a strictly larger value, so that a sequence of such
+// launches over the stages in order gives the nearest centre over all of
+// them with ties to the lowest global index.  best[h][i] = -inf starts a
+// point afresh.
+
 template <int D, int NT>
 __global__ __launch_bounds__(NT) void k_assign_res(KmArgs a, CentOps op, int *__restrict__ labels, int64_t lab_hs,
-                                                   int BH, int mpmax, int *__restrict__ chg) {
+                                                   int BH, int mpmax, int *__restrict__ chg,
+                                                   float *__restrict__ best_io) {
   constexpr int KS = D / 32;
   constexpr int LDSROW = D + 8;
   constexpr int NW = NT / 64;
@@ -232,9 +244,10 @@ __global__ __launch_bounds__(NT) void k_assign_res(KmArgs a, CentOps op, int *__
     const int64_t r0 = max(lo, hb), r1 = min(hi, he);
     if (r0 < r1) {
       const int mp = (m + 15) & ~15;
-      const uint16_t *ghi = op.hi + (int64_t)h * op.cap * D;
-      const uint16_t *glo = op.lo + (int64_t)h * op.cap * D;
-      const float *gnorm = op.norm + (int64_t)h * op.cap;
+      const int cbase = best_io ? a.coff[h] : 0;  // merge mode: the stage's first global centre
+      const uint16_t *ghi = op.hi + ((int64_t)h * op.cap + cbase) * D;
+      const uint16_t *glo = op.lo + ((int64_t)h * op.cap + cbase) * D;
+      const float *gnorm = op.norm + (int64_t)h * op.cap + cbase;
       __syncthreads();  // previous head's centres no longer read
       for (int q = threadIdx.x; q < mp * (D / 8); q += NT) {
         const int r = q / (D / 8), cc = (q % (D / 8)) * 8;
@@ -277,6 +290,18 @@ __global__ __launch_bounds__(NT) void k_assign_res(KmArgs a, CentOps op, int *__
         int bidx[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) { best[rt] = -__builtin_inff(); bidx[rt] = 0x7fffffff; }
+        if (best_io) {
+          // the running nearest centre of earlier stages (lane group 0 holds it;
+          // the other groups start empty, so the reduction below keeps it on ties)
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            const int i = wbase + rt * 16 + l16;
+            if (g == 0 && i < n) {
+              best[rt] = best_io[(int64_t)h * lab_hs + i];
+              bidx[rt] = best[rt] == -__builtin_inff() ? 0x7fffffff : labels[(int64_t)h * lab_hs + i] - cbase;
+            }
+          }
+        }
 #pragma unroll 1
         for (int ct = 0; ct < mp / 16; ++ct) {
           const int c0 = ct * 16 + 4 * g;
@@ -312,9 +337,10 @@ __global__ __launch_bounds__(NT) void k_assign_res(KmArgs a, CentOps op, int *__
           }
           const int i = wbase + rt * 16 + l16;
           const bool wr = g == 0 && i < n;
-          const int nl = bi == 0x7fffffff ? 0 : bi;
+          const int nl = bi == 0x7fffffff ? 0 : bi + cbase;
           const bool changed = wr && chg != nullptr && old[rt] != nl;
           if (wr) labels[(int64_t)h * lab_hs + i] = nl;
+          if (wr && best_io) best_io[(int64_t)h * lab_hs + i] = bv;
           any_change |= __ballot(changed) != 0;
         }
       }
@@ -491,6 +517,178 @@ __global__ __launch_bounds__(64) void k_sort_scatter(SortArgs s) {
       if (below == 0) sh_base[lb] = basev + __popcll(same);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// The same stable counting sort for heads of at most SORT_SMALL_MAX points and
+// SORT_SMALL_M labels in one launch: one 1024-thread block per head builds the
+// label histogram in LDS, scans it, and scatters the points in chunks of 1024
+// (ranks among equal labels from one ballot per label bit within each wave,
+// then the earlier waves' counts of the chunk).  Same outputs as launch_sort,
+// including the Lloyd loop's fixed-point bookkeeping and the update's chunk
+// offsets.
+__global__ __launch_bounds__(1024) void k_sort_small(SortArgs s) {
+  constexpr int NT = 1024, NWV = NT / 64;
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = s.n[h], m = s.m[h];
+  __shared__ int hist[SORT_SMALL_M + 1];
+  __shared__ int wcnt[NWV][SORT_SMALL_M];
+  __shared__ int cur[SORT_SMALL_M];
+  __shared__ int conv;
+  if (tid == 0) {
+    conv = 0;
+    if (s.chg_zero != nullptr) {
+      // Lloyd loop: a head whose assignment changed no label leaves the loop
+      if (s.chg_cur != nullptr && s.chg_cur[h] == 0) { s.neff[h] = 0; conv = 1; }
+      s.chg_zero[h] = 0;
+    }
+  }
+  __syncthreads();
+  if (conv || n <= 0 || m <= 0) {
+    if (!conv) {
+      int *seg = s.seg + (int64_t)h * s.seg_hs;
+      for (int c = tid; c <= s.segcap; c += NT) seg[c] = 0;
+    }
+    return;
+  }
+  const int *lab = s.labels + (int64_t)h * s.lab_hs;
+  int *perm = s.perm + (int64_t)h * s.perm_hs;
+  int *seg = s.seg + (int64_t)h * s.seg_hs;
+  for (int c = tid; c < m; c += NT) hist[c] = 0;
+  for (int q = tid; q < NWV * SORT_SMALL_M; q += NT) (&wcnt[0][0])[q] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += NT) atomicAdd(&hist[lab[i]], 1);
+  __syncthreads();
+  if (wave == 0) {
+    // exclusive scan of the m counts (and of the update's chunk counts)
+    int run = 0, crun = 0;
+    int *co = s.chunk_off ? s.chunk_off + (int64_t)h * s.co_hs : nullptr;
+    for (int c0 = 0; c0 < m; c0 += 64) {
+      const int c = c0 + lane;
+      const int v = c < m ? hist[c] : 0;
+      const int ck = (v + UPD_CHUNK - 1) / UPD_CHUNK;
+      int iv = v, ic = ck;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int a = __shfl_up(iv, o, 64), b = __shfl_up(ic, o, 64);
+        if (lane >= o) { iv += a; ic += b; }
+      }
+      if (c < m) {
+        cur[c] = run + iv - v;
+        seg[c] = run + iv - v;
+        if (co) co[c] = crun + ic - ck;
+      }
+      run += __shfl(iv, 63, 64);
+      crun += __shfl(ic, 63, 64);
+    }
+    for (int c = m + lane; c <= s.segcap; c += 64) seg[c] = n;
+    if (co && lane == 0) co[m] = crun;
+  }
+  __syncthreads();
+  const int nb = m > 1 ? 32 - __builtin_clz((unsigned)(m - 1)) : 0;
+  for (int c0 = 0; c0 < n; c0 += NT) {
+    const int i = c0 + tid;
+    const bool valid = i < n;
+    const int lb = valid ? lab[i] : 0;
+    uint64_t same = __ballot(valid);
+    for (int bt = 0; bt < nb; ++bt) {
+      const bool bit = (lb >> bt) & 1;
+      const uint64_t bb = __ballot(bit);
+      same &= bit ? bb : ~bb;
+    }
+    const uint64_t below = same & ((1ull << lane) - 1ull);
+    if (valid && below == 0) wcnt[wave][lb] = __popcll(same);
+    __syncthreads();
+    if (valid) {
+      int base = cur[lb];
+      for (int w = 0; w < wave; ++w) base += wcnt[w][lb];
+      perm[base + __popcll(below)] = i;
+    }
+    __syncthreads();
+    for (int c = tid; c < m; c += NT) {
+      int t = 0;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) {
+        t += wcnt[w][c];
+        wcnt[w][c] = 0;
+      }
+      cur[c] += t;
+    }
+    __syncthreads();
+  }
+}
+
+// Lloyd update of heads sorted by k_sort_small: one block per (cluster,
+// head) sums its members in counting-sort order (fp64, 16 lanes per row,
+// fixed order), divides, and writes the centre's GEMM operands.  An empty
+// cluster keeps its centre.
+template <int D>
+__global__ __launch_bounds__(256) void k_update_small(KmArgs a, SortArgs s, CentOps op) {
+  constexpr int PL = D / 16;
+  typedef uint32_t pw_t __attribute__((ext_vector_type(PL / 2)));
+  const int h = blockIdx.y, c = blockIdx.x;
+  if (c >= a.m[h] || a.n[h] <= 0) return;
+  const int *seg = s.seg + (int64_t)h * s.seg_hs;
+  const int *perm = s.perm + (int64_t)h * s.perm_hs;
+  const int beg = seg[c], end = seg[c + 1];
+  const uint16_t *X = a.X + (int64_t)h * a.x_hs;
+  const int *idx = a.idx ? a.idx + (int64_t)h * a.idx_hs : nullptr;
+  const int grp = threadIdx.x >> 4, sub = threadIdx.x & 15;
+  double acc[PL];
+#pragma unroll
+  for (int k = 0; k < PL; ++k) acc[k] = 0.0;
+  for (int p0 = beg + grp; p0 < end; p0 += 64) {
+    int li[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) li[j] = (p0 + 16 * j < end) ? perm[p0 + 16 * j] : -1;
+    pw_t xv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (li[j] >= 0) {
+        const int64_t row = idx ? (int64_t)idx[li[j]] : (int64_t)li[j];
+        xv[j] = *(const pw_t *)(X + row * D + sub * PL);
+      } else {
+        xv[j] = (pw_t){};
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (li[j] < 0) break;
+#pragma unroll
+      for (int k = 0; k < PL; ++k) {
+        const uint32_t w = xv[j][k >> 1];
+        acc[k] += (double)bf2f((uint16_t)((k & 1) ? (w >> 16) : (w & 0xFFFFu)));
+      }
+    }
+  }
+  __shared__ double sh[16][D];
+  __shared__ double red[4];
+#pragma unroll
+  for (int k = 0; k < PL; ++k) sh[grp][sub * PL + k] = acc[k];
+  __syncthreads();
+  const int cnt = end - beg;
+  float *cr = a.cent + (int64_t)h * a.cent_hs + (int64_t)(a.coff[h] + c) * D;
+  double ss = 0.0;
+  for (int dd = threadIdx.x; dd < D; dd += 256) {
+    float v;
+    if (cnt > 0) {
+      double t = 0.0;
+#pragma unroll
+      for (int g = 0; g < 16; ++g) t += sh[g][dd];
+      v = (float)(t / (double)cnt);
+      cr[dd] = v;
+    } else {
+      v = cr[dd];
+    }
+    const uint16_t bh = f2bf(v);
+    op.hi[((int64_t)h * op.cap + c) * D + dd] = bh;
+    op.lo[((int64_t)h * op.cap + c) * D + dd] = f2bf(v - bf2f(bh));
+    ss += (double)v * (double)v;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) op.norm[(int64_t)h * op.cap + c] = (float)(red[0] + red[1] + red[2] + red[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -991,6 +1189,50 @@ __global__ void k_trace_nm(const int *__restrict__ n, const int *__restrict__ m,
 }
 
 // ---------------------------------------------------------------------------
+// Algorithm 1's per-head bookkeeping between stages (one thread per head).
+// st[h] = {|U|, centres so far, done, fallback, stages run, m and n of the
+// current stage}.  Stage 0 starts with U = all L keys.  Closing stage t - 1
+// (t > 0): the head adds that stage's m centres and keeps the nnew[h] keys
+// that stayed in U; a head whose U is empty is done.  Opening stage t: a head
+// that would start with nmax centres or more and keys left falls back and is
+// done.  Writes n, m (0 for heads that are done) and the first centre of
+// stage t.
+__global__ void k_stage_next(int *__restrict__ st, const int *__restrict__ nnew, int *__restrict__ n,
+                             int *__restrict__ m, int *__restrict__ coff, int t, int nmax, int m0, int L, int BH) {
+  const int h = blockIdx.x * 256 + threadIdx.x;
+  if (h >= BH) return;
+  int *x = st + (int64_t)h * KST_FIELDS;
+  int nU, nC, done, F, stg;
+  if (t == 0) {
+    nU = L; nC = 0; done = 0; F = 0; stg = 0;
+  } else {
+    nU = x[0]; nC = x[1]; done = x[2]; F = x[3]; stg = x[4];
+    if (!done) {
+      nC += x[5];
+      stg = t;
+      nU = x[6] > 0 ? nnew[h] : 0;
+      if (nU == 0) done = 1;
+    }
+  }
+  if (!done && nC >= nmax) { F = 1; done = 1; }
+  const int nn = done ? 0 : nU, mm = done ? 0 : min(nU, m0);
+  x[0] = nU; x[1] = nC; x[2] = done; x[3] = F; x[4] = stg; x[5] = mm; x[6] = nn;
+  n[h] = nn;
+  m[h] = mm;
+  coff[h] = nC;
+}
+// Outputs of Algorithm 1 from the state: centre count, fallback, stages.
+__global__ void k_stage_final(const int *__restrict__ st, int *__restrict__ ncl, uint8_t *__restrict__ fallback,
+                              int *__restrict__ stages, int BH) {
+  const int h = blockIdx.x * 256 + threadIdx.x;
+  if (h >= BH) return;
+  const int *x = st + (int64_t)h * KST_FIELDS;
+  ncl[h] = x[1];
+  fallback[h] = (uint8_t)x[3];
+  stages[h] = x[4];
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 static inline dim3 g2(int64_t x, int y) { return dim3((unsigned)(x > 0 ? x : 1), (unsigned)y); }
 
@@ -1005,8 +1247,9 @@ void launch_qnorm(int D, const uint16_t *Q, uint16_t *Qh, float *qn, int64_t row
   AC_D_DISPATCH(D, hipLaunchKernelGGL(k_qnorm<DD>, dim3((unsigned)blocks), dim3(256), 0, st, Q, Qh, qn, rows));
 }
 
-void launch_cent_prep(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, hipStream_t st) {
-  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_cent_prep<DD>, g2((mmax + 3) / 4, BH), dim3(256), 0, st, a, op));
+void launch_cent_prep(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, hipStream_t st, bool at_coff) {
+  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_cent_prep<DD>, g2((mmax + 3) / 4, BH), dim3(256), 0, st, a, op,
+                                      at_coff ? 1 : 0));
 }
 
 static int device_cus() {
@@ -1022,8 +1265,8 @@ static int device_cus() {
 }
 
 void launch_assign(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, int nmax_pts, int *labels,
-                   int64_t lab_hs, hipStream_t st, int *chg) {
-  if (mmax <= ASSIGN_RES_MAX) {
+                   int64_t lab_hs, hipStream_t st, int *chg, float *best_io) {
+  if (mmax <= ASSIGN_RES_MAX || best_io) {
     // 768 threads and LDS for this launch's centres only, one block per CU:
     // three waves a SIMD, so one wave's point loads hide behind two others'
     // MFMA work (two a SIMD measured 8% slower; four would spill registers)
@@ -1039,7 +1282,7 @@ void launch_assign(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, 
                            hipSuccess;
       (void)lds_ok;  // a refusal shows up as a launch error
       hipLaunchKernelGGL((k_assign_res<DD, NT>), dim3(blocks), dim3(NT), lds, st, a, op, labels, lab_hs, BH, mpmax,
-                         chg);
+                         chg, best_io);
     });
     return;
   }
@@ -1056,6 +1299,15 @@ void launch_sort(const SortArgs &s, int BH, int nmax_pts, hipStream_t st) {
                      st, s);
   hipLaunchKernelGGL(k_sort_scan, dim3(BH), dim3(1024), 0, st, s);
   hipLaunchKernelGGL(k_sort_scatter, g2(tiles, BH), dim3(64), sh, st, s);
+}
+
+void launch_sort_small(const SortArgs &s, int BH, hipStream_t st) {
+  hipLaunchKernelGGL(k_sort_small, dim3(BH), dim3(1024), 0, st, s);
+}
+
+void launch_update_small(int D, const KmArgs &a, const SortArgs &s, const CentOps &op, int BH, int mmax,
+                         hipStream_t st) {
+  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_update_small<DD>, g2(mmax, BH), dim3(256), 0, st, a, s, op));
 }
 
 void launch_update(int D, const KmArgs &a, const SortArgs &s, const CentOps &op, int BH, int mmax, int npts,
@@ -1114,6 +1366,15 @@ void launch_trace_stage(const int *n, const int *idx, int64_t idx_hs, const int 
 
 void launch_trace_nm(const int *n, const int *m, int *n_out, int *m_out, int ld, int t, int BH, hipStream_t st) {
   hipLaunchKernelGGL(k_trace_nm, dim3((BH + 255) / 256), dim3(256), 0, st, n, m, n_out, m_out, ld, t, BH);
+}
+
+void launch_stage_next(int *state, const int *nnew, int *n, int *m, int *coff, int t, int nmax, int m0, int L,
+                       int BH, hipStream_t st) {
+  hipLaunchKernelGGL(k_stage_next, dim3((BH + 255) / 256), dim3(256), 0, st, state, nnew, n, m, coff, t, nmax, m0, L,
+                     BH);
+}
+void launch_stage_final(const int *state, int *ncl, uint8_t *fallback, int *stages, int BH, hipStream_t st) {
+  hipLaunchKernelGGL(k_stage_final, dim3((BH + 255) / 256), dim3(256), 0, st, state, ncl, fallback, stages, BH);
 }
 
 void launch_kstats(int D, const KStatsArgs &s, int BH, hipStream_t st) {
