@@ -37,7 +37,10 @@ def workload_params(name: str, variant: str, compensate: int):
     elif name == "cogvideox":
         base.update(m0=200, nmax=1000, tau_rule=nm.AC_TAU_PCTL, tau_param=0.95, sel_mode=nm.AC_SEL_DENSITY, sel_param=0.10)
     elif name == "hunyuan":
-        base.update(m0=100, nmax=1500, tau_rule=nm.AC_TAU_MEAN_X, tau_param=1.5, sel_mode=nm.AC_SEL_TOPK, topk=64,
+        # AdaCluster's HunyuanVideo setting (Table 7): initial K 100, an absolute key
+        # threshold of 5.5, top-K 64.  A fixed threshold singles out the dispersed heads,
+        # whose keys stay farther than 5.5 from any centre until N_max stops the stages.
+        base.update(m0=100, nmax=1500, tau_rule=nm.AC_TAU_ABS, tau_param=5.5, sel_mode=nm.AC_SEL_TOPK, topk=64,
                     sel_param=0.0)
     elif name == "wan":
         base.update(m0=200, nmax=1500, tau_rule=nm.AC_TAU_MEAN_X, tau_param=1.5, sel_mode=nm.AC_SEL_DENSITY, sel_param=0.15)
@@ -50,6 +53,19 @@ def workload_params(name: str, variant: str, compensate: int):
     if variant == "dense":
         base.update(sel_mode=nm.AC_SEL_DENSE)
     return base
+
+
+def selection_name(kw) -> str:
+    """The selection rule of a parameter set, as the pages name it."""
+    import clustered_sparse_attention_amd as nm
+    mode = kw["sel_mode"]
+    if mode == nm.AC_SEL_TOPK:
+        return f"top-K {kw['topk']}"
+    if mode == nm.AC_SEL_DENSITY:
+        return f"top-K at {kw['sel_param']:.0%} density"
+    if mode == nm.AC_SEL_TOPP:
+        return f"top-p {kw['sel_param']}"
+    return "dense"
 
 
 def _abi(kw):
@@ -94,12 +110,13 @@ class Layer:
         if key_metric:
             self.M = torch.empty((BH, d, d), dtype=torch.float32, device=dev)
 
-    def step(self, ev=None):
+    def step(self, ev=None, warm=False):
         """One layer: the query clustering on a side stream beside the key
         clustering (the two use disjoint workspace scratch), then scoring,
         selection and attention.  ev: 7 timing events (start, key clustering
         done, query clustering start / done on the side stream, both joined,
-        selection done, attention done)."""
+        selection done, attention done).  warm: both clusterings start from
+        the state of the last ac_layer call (the warm entry points)."""
         ac, torch = self.ac, self.torch
         main = torch.cuda.current_stream()
         if self.key_metric:
@@ -125,9 +142,11 @@ class Layer:
             if ev: ev[0].record(main)
             self.side.wait_stream(main)
             if ev: ev[2].record(self.side)
-            ac.ac_cluster_q(self.shape, self.p, self.Q, None, self.q, self.ws, stream=self.side.cuda_stream)
+            ac.ac_cluster_q(self.shape, self.p, self.Q, self.state.cent_q if warm else None, self.q, self.ws,
+                            stream=self.side.cuda_stream)
             if ev: ev[3].record(self.side)
-            ac.ac_cluster_k(self.shape, self.p, self.K, self.V, None, self.k, self.st, self.ws)
+            ac.ac_cluster_k(self.shape, self.p, self.K, self.V, self.state if warm else None, self.k, self.st,
+                            self.ws)
             if ev: ev[1].record(main)
             main.wait_stream(self.side)
             if ev: ev[4].record(main)
@@ -138,15 +157,18 @@ class Layer:
         self.attn_only()
         if ev: ev[6].record(main)
 
-    def layer_step(self):
-        """One cold ac_layer call: the product's own orchestration (the query
+    def layer_step(self, warm=False):
+        """One ac_layer call: the product's own orchestration (the query
         clustering starts on a second stream after the first stage of the
-        key clustering); the state is reset so every step is cold."""
+        key clustering).  Cold: the state is reset so every step is cold.
+        Warm: the step starts from the state the previous call left (a later
+        denoising step)."""
         if not hasattr(self, "state"):
             B, H, L, d = self.shape.B, self.shape.H, self.shape.L, self.shape.d
             self.state = self.ac.State(B * H, min(self.p.nq, L), self.ncap, d, self.Q.device)
             self.O_layer = self.torch.empty_like(self.Q)
-        self.state.valid = 0
+        if not warm:
+            self.state.valid = 0
         self.ac.ac_layer(self.shape, self.p, self.Q, self.K, self.V, self.state, self.O_layer, self.ws)
 
     def attn_only(self):
@@ -189,10 +211,11 @@ def pairs_of(layer):
     return tot, per_head
 
 
-def cpu_baseline(w, Q, K, V, kw, max_rows=2048):
-    """The oracle, timed on this host on one head (full clustering, scoring,
-    selection, and attention for a seeded sample of query rows), extrapolated
-    to the whole layer."""
+def cpu_baseline(w, Q, K, V, kw, max_rows=0):
+    """The oracle, timed on this host on one complete head (clustering,
+    scoring, selection and the attention of every query row; max_rows > 0
+    limits the attention to a seeded sample of rows), extrapolated to the
+    layer's heads."""
     from oracle import numerics as nm, kmeans as okm, multistage as oms, stats as ost, score as osc
     from oracle import attention as oat
     import csa_inputs as gen
@@ -208,7 +231,7 @@ def cpu_baseline(w, Q, K, V, kw, max_rows=2048):
     S = osc.scores(p, qc["cent"], kst)
     sel = osc.select(S, kst["count"], qc["rho"], L, d, p)
     t1 = time.perf_counter()
-    rows = gen.row_sample(L, max_rows, 9004)
+    rows = gen.row_sample(L, max_rows, 9004) if 0 < max_rows < L else np.arange(L)
     Qx, Kx, Vx = (nm.bf16_to_f64(x) for x in (Qb, Kb, Vb))
     if kc["fallback"] or p.sel_mode == nm.SEL_DENSE:
         oat.dense_rows(Qx, Kx, Vx, rows, p.attn_scale(d))
@@ -222,10 +245,11 @@ def cpu_baseline(w, Q, K, V, kw, max_rows=2048):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
+    part = (f"all {L} query rows" if rows.size == L else
+            f"{rows.size} of {L} query rows, extrapolated x{L / rows.size:.1f} rows")
     return dict(value=w.dense_flops / layer_s / 1e12, unit="TFLOP/s (dense-equivalent)", cores=cores, kind="oracle",
-                sample=f"head 0 of {w.BH}: full clustering/scoring/selection ({t1 - t0:.1f} s) + attention for "
-                       f"{rows.size} of {L} query rows ({t2 - t1:.1f} s), extrapolated x{L / rows.size:.1f} rows "
-                       f"and x{w.BH} heads to {layer_s:.0f} s per layer",
+                sample=f"head 0 of {w.BH}, complete: clustering/scoring/selection ({t1 - t0:.1f} s) + attention for "
+                       f"{part} ({t2 - t1:.1f} s); the layer is x{w.BH} heads, {layer_s:.0f} s",
                 measured_s=round(t2 - t0, 2), layer_s_extrapolated=round(layer_s, 1))
 
 
@@ -633,6 +657,9 @@ def main():
     ap.add_argument("--pca-split", default="",
                     help="QB,KB: cluster queries and keys by ClusterAttention's principal-component split into "
                          "clusters of QB and KB tokens (powers of two) instead of k-means / Algorithm 1")
+    ap.add_argument("--warm", action="store_true",
+                    help="time the warm step instead: a cold ac_layer call fills the state, Q and K are perturbed "
+                         "by 2%%, and the timed ac_layer calls start from the state (a later denoising step)")
     ap.add_argument("--no-baselines", action="store_true", help="skip dense baselines and the CPU oracle")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a plain copy of this many bytes")
@@ -701,16 +728,25 @@ def main():
     # the timed step is one ac_layer call (cold), except for the variants that
     # ac_layer does not run (interaction-aware keys) or a serial profile
     use_layer = not args.key_metric and not args.serial and not pca
+    if args.warm and not use_layer:
+        raise SystemExit("--warm times ac_layer's warm step: not with --key-metric, --serial or --pca-split")
     for _ in range(args.warmup):
         layer.layer_step() if use_layer else layer.step()
     torch.cuda.synchronize()
+    if args.warm:
+        # the first step's state, then the next step's inputs: Q and K moved by 2 %
+        layer.layer_step()
+        Qd.copy_(dev(gen.perturb(Q, 1103)))
+        Kd.copy_(dev(gen.perturb(K, 1104)))
+        layer.layer_step(warm=True)
+        torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(args.steps):
-        layer.layer_step() if use_layer else layer.step(evs[s])
+        layer.layer_step(warm=args.warm) if use_layer else layer.step(evs[s])
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     ms_step = (t_end - t_start) * 1e3 / args.steps
@@ -721,7 +757,7 @@ def main():
     nph = min(args.steps, 3) if use_layer else args.steps
     if use_layer:
         for s in range(nph):
-            layer.step(evs[s])
+            layer.step(evs[s], warm=args.warm)
         torch.cuda.synchronize()
     pairs_ev = [(2, 3), (0, 1), (0, 4), (4, 5), (5, 6)]
     phase = np.array([[evs[s][a].elapsed_time(evs[s][b]) for a, b in pairs_ev] for s in range(nph)])
@@ -749,7 +785,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.description, "B": w.B, "H": w.H, "L": w.L, "d": w.d,
-                   "selection": args.variant, "compensate": args.compensate,
+                   "selection": selection_name(kw), "compensate": args.compensate,
                    "params": {k: (round(v, 6) if isinstance(v, float) else v) for k, v in kw.items()}},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -760,7 +796,8 @@ def main():
         "phase_ms": {"cluster_q": round(float(phase_ms[0]), 3), "cluster_k": round(float(phase_ms[1]), 3),
                      "clustering_q_beside_k": round(float(phase_ms[2]), 3),
                      "score_select": round(float(phase_ms[3]), 3), "sparse_attn": round(attn_ms, 3)},
-        "timed_step": "ac_layer (cold)" if use_layer else "entry points in ac_layer order",
+        "timed_step": ("ac_layer (warm: a later denoising step after a 2% perturbation of Q and K)" if args.warm
+                       else "ac_layer (cold)") if use_layer else "entry points in ac_layer order",
         "_phase_note": ("phases from a separate pass of the entry points, the query clustering beside the key "
                         "clustering from the start; " if use_layer else "") +
                        "score_select includes ac_tail_merge when tail merging is on",

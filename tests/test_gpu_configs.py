@@ -155,6 +155,10 @@ def test_config_full_size(name):
     if name == "long":
         # the widest heavy-tailed heads cannot be covered by N_max centres: several fall back
         assert 2 <= out["fallback"] <= 8
+    if name == "hunyuan":
+        # absolute threshold 5.5: the compact heads (sigma 0.15) finish below N_max, the
+        # dispersed ones (sigma 0.8 and 10% uniform outliers) keep every key and fall back
+        assert set(np.flatnonzero(np_(r.st.fallback)).tolist()) == set(range(12, 24))
 
 
 def test_hunyuan_warm_step():
@@ -177,6 +181,7 @@ def test_hunyuan_warm_step():
     state.tau.copy_(r.st.tau)
     state.valid = 1
     ncl0, fb0, tau0 = np_(r.k.ncl), np_(r.st.fallback), np_(r.st.tau)
+    assert set(np.flatnonzero(fb0).tolist()) == set(range(12, 24))  # the warm step covers fallback heads
     cent_q0, cent_k0 = np_(r.q.cent).astype(np.float64), np_(r.k.cent).astype(np.float64)
     Q2, K2 = gen.perturb(Q, 1103), gen.perturb(K, 1104)
     r2 = Run(Q2, K2, V, p)
