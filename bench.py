@@ -211,14 +211,13 @@ def pairs_of(layer):
     return tot, per_head
 
 
-def cpu_baseline(w, Q, K, V, kw, max_rows=0):
-    """The oracle, timed on this host on one complete head (clustering,
-    scoring, selection and the attention of every query row; max_rows > 0
-    limits the attention to a seeded sample of rows), extrapolated to the
-    layer's heads."""
+def cpu_baseline(w, Q, K, V, kw, budget_s=30.0):
+    """The oracle, timed on this host on head 0: clustering, scoring and
+    selection, then the attention of every query row in seeded chunks of
+    4096 while the time budget lasts.  When the budget ends first, the
+    attention time is extrapolated from the rows done (and said so)."""
     from oracle import numerics as nm, kmeans as okm, multistage as oms, stats as ost, score as osc
     from oracle import attention as oat
-    import csa_inputs as gen
     p = nm.Params(**{k: v for k, v in kw.items() if k in nm.Params.__dataclass_fields__})
     p.tau_param = float(np.float32(p.tau_param))
     p.sel_param = float(np.float32(p.sel_param))
@@ -231,26 +230,70 @@ def cpu_baseline(w, Q, K, V, kw, max_rows=0):
     S = osc.scores(p, qc["cent"], kst)
     sel = osc.select(S, kst["count"], qc["rho"], L, d, p)
     t1 = time.perf_counter()
-    rows = gen.row_sample(L, max_rows, 9004) if 0 < max_rows < L else np.arange(L)
+    order = np.random.default_rng(9004).permutation(L)
     Qx, Kx, Vx = (nm.bf16_to_f64(x) for x in (Qb, Kb, Vb))
-    if kc["fallback"] or p.sel_mode == nm.SEL_DENSE:
-        oat.dense_rows(Qx, Kx, Vx, rows, p.attn_scale(d))
-    else:
-        oat.sparse_rows(Qx, Kx, Vx, rows, qc["labels"], kc["labels"], sel, p.attn_scale(d), bool(p.compensate),
-                        kst["count"], kst["kmean"], kst["vmean"])
+    done = 0
+    while done < L and (done == 0 or time.perf_counter() - t0 < budget_s):
+        rows = np.sort(order[done:done + 4096])
+        if kc["fallback"] or p.sel_mode == nm.SEL_DENSE:
+            oat.dense_rows(Qx, Kx, Vx, rows, p.attn_scale(d))
+        else:
+            oat.sparse_rows(Qx, Kx, Vx, rows, qc["labels"], kc["labels"], sel, p.attn_scale(d),
+                            bool(p.compensate), kst["count"], kst["kmean"], kst["vmean"])
+        done += rows.size
     t2 = time.perf_counter()
-    per_head = (t1 - t0) + (t2 - t1) * (L / rows.size)
+    per_head = (t1 - t0) + (t2 - t1) * (L / done)
     layer_s = per_head * w.BH
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
-    part = (f"all {L} query rows" if rows.size == L else
-            f"{rows.size} of {L} query rows, extrapolated x{L / rows.size:.1f} rows")
+    part = (f"all {L} query rows" if done == L else
+            f"{done} of {L} query rows in the {budget_s:.0f} s budget, extrapolated x{L / done:.1f} rows")
     return dict(value=w.dense_flops / layer_s / 1e12, unit="TFLOP/s (dense-equivalent)", cores=cores, kind="oracle",
-                sample=f"head 0 of {w.BH}, complete: clustering/scoring/selection ({t1 - t0:.1f} s) + attention for "
+                sample=f"head 0 of {w.BH}: clustering/scoring/selection ({t1 - t0:.1f} s) + attention for "
                        f"{part} ({t2 - t1:.1f} s); the layer is x{w.BH} heads, {layer_s:.0f} s",
-                measured_s=round(t2 - t0, 2), layer_s_extrapolated=round(layer_s, 1))
+                complete_head=done == L, measured_s=round(t2 - t0, 2), layer_s_extrapolated=round(layer_s, 1))
+
+
+def peak_probe():
+    """Achievable peaks on this GPU, measured: a large bf16 GEMM through
+    torch (hipBLASLt) and a device-to-device copy of 4 GiB."""
+    import torch
+    out = {}
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    out["gemm_bf16"] = {"shape": [n, n, n], "ms": round(ms, 4), "tflops": round(2.0 * n ** 3 / ms / 1e9, 1),
+                        "frac_of_2500": round(2.0 * n ** 3 / ms / 1e9 / PEAK_BF16_TFLOPS, 3)}
+    del a, b
+    nbytes = 4 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = 2.0 * nbytes / ms / 1e6
+    out["copy"] = {"bytes": nbytes, "ms": round(ms, 3), "gbs_read_plus_write": round(gbs, 1),
+                   "frac_of_8000": round(gbs / PEAK_HBM_GBS, 3)}
+    print(json.dumps(out), flush=True)
 
 
 def sdpa_ms(Qd, Kd, Vd, reps=3):
@@ -359,14 +402,17 @@ def summarize(args):
         print(json.dumps(res))
         return
     if kind == "roofline":
-        # per-kernel roofline of the full-size launches of one layer step, from a
-        # kernel trace of `bench.py --serial` (entry points one after another)
-        src, out, wl, cmd = rest[0], rest[1], rest[2], " ".join(rest[3:])
+        # per-kernel roofline of one layer step's full-size launches, from a kernel
+        # trace of `bench.py --serial` (the entry points one after another) and
+        # that run's bench line (the attention's algorithmic flops)
+        src, bench_log, out, wl, cmd = rest[0], rest[1], rest[2], rest[3], " ".join(rest[4:])
         import csa_inputs as gen
         w = gen.get_workload(wl)
         kw = workload_params(wl, "density", 0)
         BH, L, d = w.BH, w.L, w.d
         nq, m0 = min(kw["nq"], L), min(kw["m0"], L)
+        line = [json.loads(x) for x in open(bench_log) if x.startswith("{")][-1]
+        attn_flops = line["roofline"]["algorithmic_flops_per_launch"]
         rows = list(csv.DictReader(open(src)))
         rows.sort(key=lambda r: int(r["Start_Timestamp"]))
         starts = [i for i, r in enumerate(rows) if "k_qnorm" in r["Kernel_Name"]]
@@ -375,50 +421,71 @@ def summarize(args):
         def dur(r):
             return (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
 
-        def nth(step, name, idx):
-            hits = [r for r in step if name in r["Kernel_Name"]]
-            return [hits[i] for i in idx if i < len(hits)]
+        def after_seed(step, name, which, count):
+            """The first `count` launches of `name` after the `which`-th seeding
+            of the step (0: the queries, 1: the keys' first stage): the Lloyd
+            iterations in which every head still takes part."""
+            seeds = [i for i, r in enumerate(step) if "k_kpp_seq" in r["Kernel_Name"]]
+            if len(seeds) <= which:
+                return []
+            hits = [r for r in step[seeds[which]:] if name in r["Kernel_Name"]]
+            return hits[:count]
+
+        def once(step, name):
+            return [r for r in step if name in r["Kernel_Name"]][:1]
 
         x_bytes = BH * L * d * 2.0
-        table = []  # (kernel, launches, what, work, unit, peak)
         pad = lambda m: (m + 15) // 16 * 16
-        # Lloyd launches in which every head still takes part: a head leaves the
-        # loop once an assignment changes none of its labels, so only iteration
-        # 0's update and sort, iterations 0 and 1's assignments and the final
-        # assignment are certain to cover all heads
+        hbm = lambda b: ("hbm", b, None)
+        # (label, launches picked per step, work, what)
         specs = [
-            ("k_qnorm", "k_qnorm", [0], "read Q + write q-hat (bf16) and norms", 2 * x_bytes + BH * L * 4, "hbm"),
-            ("k_assign_res, queries (n = L, m = %d)" % nq, "k_assign_res", [0, 1, 10],
-             "read X once (the argmin GEMM: %.2f TFLOP incl. hi/lo)" % (4.0 * BH * L * pad(nq) * d / 1e12),
-             x_bytes, "hbm"),
-            ("k_assign_res, key stage 1 (n = L, m = %d)" % m0, "k_assign_res", [11, 12, 21],
-             "bf16 MFMA, centres split hi + lo, m padded to 16", 4.0 * BH * L * pad(m0) * d, "mfma"),
-            ("k_update_partial, queries + key stage 1", "k_update_partial", [0, 10],
-             "gather X in cluster order (bf16) + perm", x_bytes + BH * L * 4, "hbm"),
-            ("k_sort_scatter, full-size", "k_sort_scatter", [0, 11], "read labels, write perm", BH * L * 8.0, "hbm"),
-            ("k_kstats", "k_kstats", [0], "read K and V in cluster order", 2 * x_bytes, "hbm"),
-            ("k_attn (density 0.15)", "k_attn<", [0], "see the bench line (algorithmic pairs x 4d)", None, "mfma"),
+            ("k_qnorm", lambda st: once(st, "k_qnorm"), hbm(2 * x_bytes + BH * L * 4),
+             "read Q, write q-hat (bf16) and norms"),
+            (f"k_assign_res, queries, iterations 0-1 (n = L, m = {nq})", lambda st: after_seed(st, "k_assign_res", 0, 2),
+             ("hbm+flop", x_bytes, 2.0 * BH * L * nq * d), "read X once; argmin GEMM"),
+            (f"k_assign_res, keys, stage 0, iterations 0-1 (n = L, m = {m0})",
+             lambda st: after_seed(st, "k_assign_res", 1, 2), ("hbm+flop", x_bytes, 2.0 * BH * L * m0 * d),
+             "read X once; argmin GEMM"),
+            ("k_update_partial, queries and key stage 0, iteration 0",
+             lambda st: after_seed(st, "k_update_partial", 0, 1) + after_seed(st, "k_update_partial", 1, 1),
+             hbm(x_bytes + BH * L * 4), "gather X in cluster order (bf16) + perm"),
+            ("k_sort_scatter, queries and key stage 0, iteration 0",
+             lambda st: after_seed(st, "k_sort_scatter", 0, 1) + after_seed(st, "k_sort_scatter", 1, 1),
+             hbm(BH * L * 8.0), "read labels, write perm"),
+            ("k_kstats", lambda st: once(st, "k_kstats"), hbm(2 * x_bytes + BH * L * 4),
+             "read K, V and labels in cluster order"),
+            ("k_attn", lambda st: once(st, "k_attn<"), ("flop", None, attn_flops),
+             "4 d x the algorithmic query-key pairs (padding and masked keys not counted)"),
         ]
-        peaks = {"hbm": (PEAK_HBM_GBS, "GB/s", 1e9), "mfma": (PEAK_BF16_TFLOPS, "TFLOP/s", 1e12)}
         lines = [f"# Per-kernel roofline, {w.description}", "", f"Command: `{cmd}`", "",
-                 "Full-size launches of the timed layer steps (the entry points run one after another; of the "
-                 "Lloyd loops only the launches in which every head takes part); work is algorithmic (what the "
-                 "step must move or compute), time is the kernel's own.", "",
-                 "| kernel | launches/step | work per launch | avg time | achieved | peak | fraction |",
-                 "|---|---:|---|---:|---:|---:|---:|"]
-        for label, name, idx, what, work, bound in specs:
-            ds = [dur(r) for st in steps for r in nth(st, name, idx)]
+                 "Full-size launches of the timed layer steps (the entry points one after another; of the Lloyd "
+                 "loops the iterations in which every head still takes part). Work is algorithmic: the bytes "
+                 "the step must move, or its flops without padding and without the low halves of the "
+                 "split centres; time is the kernel's own. Peaks: HBM 8000 GB/s, bf16 MFMA 2500 TFLOP/s "
+                 f"(dense). Attention: {line['layer']['density_pairs']:.4f} of the pairs, "
+                 f"{attn_flops / 1e12:.2f} TFLOP per call.", "",
+                 "| kernel | launches/step | avg time | algorithmic work | achieved | fraction of peak |",
+                 "|---|---:|---:|---|---|---:|"]
+        for label, pick, (bound, nbytes, flops), what in specs:
+            ds = [dur(r) for st in steps for r in pick(st)]
             if not ds:
                 continue
             t = float(np.mean(ds))
-            peak, unit, scale = peaks[bound]
-            if work is None:
-                lines.append(f"| {label} | {len(idx)} | {what} | {t * 1e3:.3f} ms | — | {peak:.0f} {unit} | — |")
-                continue
-            ach = work / t / scale
-            wtxt = f"{work / 1e9:.3f} GB" if bound == "hbm" else f"{work / 1e12:.3f} TFLOP"
-            lines.append(f"| {label} | {len(idx)} | {wtxt}: {what} | {t * 1e3:.3f} ms | {ach:.0f} {unit} | "
-                         f"{peak:.0f} {unit} | {ach / peak:.2f} |")
+            per = len(ds) / max(len(steps), 1)
+            parts, fracs = [], []
+            if nbytes is not None:
+                gbs = nbytes / t / 1e9
+                parts.append(f"{gbs:.0f} GB/s")
+                fracs.append(("HBM", gbs / PEAK_HBM_GBS))
+            if flops is not None:
+                tf = flops / t / 1e12
+                parts.append(f"{tf:.0f} TFLOP/s")
+                fracs.append(("MFMA", tf / PEAK_BF16_TFLOPS))
+            work = ", ".join(x for x in (f"{nbytes / 1e9:.3f} GB" if nbytes else "",
+                                         f"{flops / 1e12:.3f} TFLOP" if flops else "") if x)
+            frac = max(fracs, key=lambda f: f[1])
+            lines.append(f"| {label} | {per:g} | {t * 1e3:.3f} ms | {work}: {what} | {', '.join(parts)} | "
+                         f"{frac[1]:.2f} ({frac[0]}) |")
         open(out, "w").write("\n".join(lines) + "\n")
         print("\n".join(lines))
         return
@@ -663,6 +730,8 @@ def main():
     ap.add_argument("--no-baselines", action="store_true", help="skip dense baselines and the CPU oracle")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, help="only run a plain copy of this many bytes")
+    ap.add_argument("--peak-probe", action="store_true",
+                    help="only measure achievable peaks: a bf16 GEMM (torch) and a 4 GiB device copy")
     ap.add_argument("--summarize", nargs="+", help="write a profile summary from rocprofv3 output (no GPU)")
     ap.add_argument("--denoise", type=int, default=0,
                     help="only run this many denoising steps under the multi-step policy (dense warm-up, calibrated "
@@ -680,6 +749,9 @@ def main():
         return
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.peak_probe:
+        peak_probe()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (heads shard across GPUs by design "

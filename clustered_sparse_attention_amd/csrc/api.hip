@@ -130,6 +130,9 @@ struct Plan {
   // rows, the running nearest-centre score, per-stage centre counts and
   // offsets for the merge launches, Algorithm 1's per-head state, all-L counts
   size_t fops_hi, fops_lo, fops_norm, best, mtab, ctab, kst, nall;
+  // chunked key statistics: chunk and slot offsets, per-slot partials
+  size_t ks_co, ks_po, ks_psk, ks_psv, ks_pmx, ks_pmn, ks_pse;
+  int ks_slots;
   int stage_slots;
 };
 
@@ -192,6 +195,14 @@ Plan make_plan(const ac_shape *s, const ac_params *p) {
   P.rstate = take(BH * 2 * 4);
   P.rhist = take(BH * 256 * 4);
   P.msepart = take(BH * P.ncapk * 8);
+  P.ks_slots = kst_slots(P.L);
+  P.ks_co = take(BH * (P.ncapk + 1) * 4);
+  P.ks_po = take(BH * (P.ncapk + 1) * 4);
+  P.ks_psk = take(BH * (size_t)P.ks_slots * D * 8);
+  P.ks_psv = take(BH * (size_t)P.ks_slots * D * 8);
+  P.ks_pmx = take(BH * (size_t)P.ks_slots * D * 4);
+  P.ks_pmn = take(BH * (size_t)P.ks_slots * D * 4);
+  P.ks_pse = take(BH * (size_t)P.ks_slots * 8);
   P.scoreA = take(BH * P.nq_pad * 6 * D * 2);
   P.scoreB = take(BH * P.ncap_pad * 6 * D * 2);
   P.S = take(BH * P.nq * (size_t)P.ncapk * 4);
@@ -437,6 +448,23 @@ ac_status do_cluster_q(const Plan &P, const ac_params *p, const uint16_t *Q, con
   return AC_OK;
 }
 
+// Arguments of the key statistics of clusters k into stats, with their
+// workspace scratch.
+KStatsArgs kstats_args(const Plan &P, const uint16_t *K, const uint16_t *V, const ac_clusters *k, ac_kstats *stats,
+                       void *ws) {
+  KStatsArgs a{K, V, k->perm, k->seg, k->ncl, k->cent, stats->kmax, stats->kmin, stats->kmean, stats->vmean,
+               at<double>(ws, P.msepart), stats->mse, P.L, k->ncap};
+  a.co = at<int>(ws, P.ks_co);
+  a.po = at<int>(ws, P.ks_po);
+  a.psk = at<double>(ws, P.ks_psk);
+  a.psv = at<double>(ws, P.ks_psv);
+  a.pmx = at<float>(ws, P.ks_pmx);
+  a.pmn = at<float>(ws, P.ks_pmn);
+  a.pse = at<double>(ws, P.ks_pse);
+  a.pslots = P.ks_slots;
+  return a;
+}
+
 ac_status finish_keys(const Plan &P, const uint16_t *K, const uint16_t *V, ac_clusters *k, ac_kstats *stats,
                       void *ws, hipStream_t st, int mmax) {
   // final assignment of every key over all centres, counting sort, statistics
@@ -451,8 +479,7 @@ ac_status finish_keys(const Plan &P, const uint16_t *K, const uint16_t *V, ac_cl
   launch_assign(D, a, op, BH, mmax, L, k->labels, L, st);
   SortArgs s = E.sort_args(k->labels, k->perm, k->seg, k->ncap, mmax);
   launch_sort(s, BH, L, st);
-  KStatsArgs ks{K, V, k->perm, k->seg, k->ncl, k->cent, stats->kmax, stats->kmin, stats->kmean, stats->vmean,
-                at<double>(ws, P.msepart), stats->mse, L, k->ncap};
+  const KStatsArgs ks = kstats_args(P, K, V, k, stats, ws);
   launch_kstats(D, ks, BH, st);
   AC_CHECK_LAUNCH();
   return AC_OK;
@@ -673,8 +700,7 @@ ac_status do_cluster_k_cold(const Plan &P, const ac_params *p, const uint16_t *K
   launch_fill_i32(E.n(), BH, L, st);
   launch_copy_i32(k->ncl, E.m(), BH, st);
   launch_sort(s, BH, L, st);
-  KStatsArgs ks{K, V, k->perm, k->seg, k->ncl, k->cent, stats->kmax, stats->kmin, stats->kmean, stats->vmean,
-                at<double>(ws, P.msepart), stats->mse, L, k->ncap};
+  const KStatsArgs ks = kstats_args(P, K, V, k, stats, ws);
   launch_kstats(D, ks, BH, st);
   AC_CHECK_LAUNCH();
   return AC_OK;
@@ -755,8 +781,7 @@ ac_status do_cluster_k_metric(const Plan &P, const ac_params *p, const uint16_t 
   AC_TRY(E.run(a, m, L, true, p->iters, p, 1, 0, k->labels, M));
   SortArgs s = E.sort_args(k->labels, k->perm, k->seg, k->ncap, m);
   launch_sort(s, BH, L, st);
-  KStatsArgs ks{K, V, k->perm, k->seg, k->ncl, k->cent, stats->kmax, stats->kmin, stats->kmean, stats->vmean,
-                at<double>(ws, P.msepart), stats->mse, L, k->ncap};
+  const KStatsArgs ks = kstats_args(P, K, V, k, stats, ws);
   launch_kstats(D, ks, BH, st);
   AC_CHECK_LAUNCH();
   return AC_OK;
@@ -1037,8 +1062,7 @@ AC_API ac_status ac_cluster_k_pca(const ac_shape *s, const ac_params *p, const u
   hipStream_t st = (hipStream_t)stream;
   const int BH = P.BH;
   AC_TRY(do_pca_split(P, K, block, k_out, trace, ws, st));
-  KStatsArgs ks{K, V, k_out->perm, k_out->seg, k_out->ncl, k_out->cent, stats->kmax, stats->kmin, stats->kmean,
-                stats->vmean, at<double>(ws, P.msepart), stats->mse, P.L, k_out->ncap};
+  const KStatsArgs ks = kstats_args(P, K, V, k_out, stats, ws);
   launch_kstats(P.D, ks, BH, st);
   launch_fill_u8(stats->fallback, BH, 0, st);
   launch_fill_i32((int *)stats->tau, BH, 0, st);  // +0.0f: no distance threshold

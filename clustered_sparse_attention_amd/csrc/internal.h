@@ -86,7 +86,17 @@ struct KStatsArgs {
   double *msepart;        // [BH, ncap]
   float *mse;             // [BH]
   int L, ncap;
+  // scratch of the chunked statistics (kst_scratch): chunk and partial-slot
+  // offsets [BH, ncap + 1], per-slot partials [BH, pslots, D] and [BH, pslots]
+  int *co, *po;
+  double *psk, *psv;
+  float *pmx, *pmn;
+  double *pse;
+  int pslots;
 };
+constexpr int KST_CHUNK = 256;  // members per block of the key statistics
+// partial slots per head of the key statistics (fewer than 2 L / KST_CHUNK)
+inline int kst_slots(int L) { return 2 * ((L + KST_CHUNK - 1) / KST_CHUNK); }
 
 struct ScoreArgs {
   const float *cq;        // [BH, nqcap, D] query-cluster centres

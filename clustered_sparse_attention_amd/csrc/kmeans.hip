@@ -955,34 +955,77 @@ __global__ __launch_bounds__(256) void k_compact_gather(const int *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Statistics of the final key clusters, one block per (cluster, head):
-// count, fp64 means of K and V, per-dimension max / min of K (exact bf16),
-// and the cluster's share of sum ||k - c(k)||^2 (fp64).
+// Statistics of the final key clusters: count, fp64 means of K and V,
+// per-dimension max / min of K (exact bf16), and each cluster's share of
+// sum ||k - c(k)||^2 (fp64).  Clusters are cut into chunks of KST_CHUNK
+// members so that a large cluster spreads over many blocks: a cluster of one
+// chunk is finished by its block, a larger one leaves per-chunk partials that
+// a second kernel combines in chunk order (deterministic).
+//
+// Per head, from the segments: co[c] = chunks of clusters < c, and
+// po[c] = chunks of the multi-chunk clusters < c (their partial slots).  A
+// cluster of k >= 2 chunks holds more than (k - 1) KST_CHUNK >= k KST_CHUNK / 2
+// members, so the slots number fewer than 2 L / KST_CHUNK per head.
+__global__ __launch_bounds__(1024) void k_kst_chunks(KStatsArgs s) {
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ncl = s.ncl[h];
+  const int *seg = s.seg + (int64_t)h * (s.ncap + 1);
+  int *co = s.co + (int64_t)h * (s.ncap + 1);
+  int *po = s.po + (int64_t)h * (s.ncap + 1);
+  const int per = (ncl + 1023) / 1024;
+  const int c0 = min(ncl, tid * per), c1 = min(ncl, c0 + per);
+  int a = 0, b = 0;
+  for (int c = c0; c < c1; ++c) {
+    const int k = (seg[c + 1] - seg[c] + KST_CHUNK - 1) / KST_CHUNK;
+    a += k;
+    b += k >= 2 ? k : 0;
+  }
+  // exclusive block scan of (a, b)
+  int ia = a, ib = b;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int ya = __shfl_up(ia, o, 64), yb = __shfl_up(ib, o, 64);
+    if (lane >= o) { ia += ya; ib += yb; }
+  }
+  __shared__ int wa[16], wb[16];
+  if (lane == 63) { wa[wave] = ia; wb[wave] = ib; }
+  __syncthreads();
+  int oa = 0, ob = 0;
+  for (int w = 0; w < wave; ++w) { oa += wa[w]; ob += wb[w]; }
+  int ra = oa + ia - a, rb = ob + ib - b;
+  for (int c = c0; c < c1; ++c) {
+    const int k = (seg[c + 1] - seg[c] + KST_CHUNK - 1) / KST_CHUNK;
+    co[c] = ra;
+    po[c] = rb;
+    ra += k;
+    rb += k >= 2 ? k : 0;
+  }
+  if (tid == 1023) { co[ncl] = ra; po[ncl] = rb; }
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void k_kstats(KStatsArgs s) {
-  // one block per cluster: 16 row groups of 16 lanes (PL dims each), four
-  // member rows per group in flight; the groups of a wave combine with
-  // shuffles, the four waves through a small LDS table
+__global__ __launch_bounds__(256) void k_kstats_part(KStatsArgs s) {
+  // 16 row groups of 16 lanes (PL dims each), four member rows per group in
+  // flight; the groups of a wave combine with shuffles, the four waves
+  // through a small LDS table
   constexpr int PL = D / 16;  // dims per lane, 16 lanes per row
   typedef uint32_t pw_t __attribute__((ext_vector_type(PL / 2)));
-  const int h = blockIdx.y, c = blockIdx.x;
+  const int h = blockIdx.y, item = blockIdx.x;
   const int ncl = s.ncl[h];
+  const int *co = s.co + (int64_t)h * (s.ncap + 1);
+  if (ncl <= 0 || item >= co[ncl]) return;
+  int lo = 0, hi = ncl;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (co[mid] <= item) lo = mid; else hi = mid;
+  }
+  const int c = lo, j = item - co[c], nch = co[c + 1] - co[c];
   const int64_t cb = ((int64_t)h * s.ncap + c);
   const int grp = threadIdx.x >> 4, sub = threadIdx.x & 15;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (c >= ncl) {
-    if (c < s.ncap) {
-      for (int dd = threadIdx.x; dd < D; dd += 256) {
-        s.kmax[cb * D + dd] = 0; s.kmin[cb * D + dd] = 0;
-        s.kmean[cb * D + dd] = 0.f; s.vmean[cb * D + dd] = 0.f;
-      }
-      if (threadIdx.x == 0) s.msepart[cb] = 0.0;
-    }
-    return;
-  }
   const int *seg = s.seg + (int64_t)h * (s.ncap + 1);
   const int *perm = s.perm + (int64_t)h * s.L;
-  const int beg = seg[c], end = seg[c + 1];
+  const int beg = seg[c] + j * KST_CHUNK, end = min(seg[c + 1], beg + KST_CHUNK);
   const uint16_t *K = s.K + (int64_t)h * s.L * D;
   const uint16_t *V = s.V + (int64_t)h * s.L * D;
   const float *cent = s.cent + cb * D;
@@ -996,20 +1039,20 @@ __global__ __launch_bounds__(256) void k_kstats(KStatsArgs s) {
   for (int p0 = beg + grp; p0 < end; p0 += 64) {
     int64_t row[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) row[j] = (p0 + 16 * j < end) ? (int64_t)perm[p0 + 16 * j] : -1;
+    for (int jj = 0; jj < 4; ++jj) row[jj] = (p0 + 16 * jj < end) ? (int64_t)perm[p0 + 16 * jj] : -1;
     pw_t kw[4], vw[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t rr = row[j] >= 0 ? row[j] : row[0];
-      kw[j] = *(const pw_t *)(K + rr * D + sub * PL);
-      vw[j] = *(const pw_t *)(V + rr * D + sub * PL);
+    for (int jj = 0; jj < 4; ++jj) {
+      const int64_t rr = row[jj] >= 0 ? row[jj] : row[0];
+      kw[jj] = *(const pw_t *)(K + rr * D + sub * PL);
+      vw[jj] = *(const pw_t *)(V + rr * D + sub * PL);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (row[j] < 0) break;
+    for (int jj = 0; jj < 4; ++jj) {
+      if (row[jj] < 0) break;
 #pragma unroll
       for (int k = 0; k < PL; ++k) {
-        const uint32_t a1 = kw[j][k >> 1], b1 = vw[j][k >> 1];
+        const uint32_t a1 = kw[jj][k >> 1], b1 = vw[jj][k >> 1];
         const float kv = bf2f((uint16_t)((k & 1) ? (a1 >> 16) : (a1 & 0xFFFFu)));
         const float vv = bf2f((uint16_t)((k & 1) ? (b1 >> 16) : (b1 & 0xFFFFu)));
         sk[k] += (double)kv;
@@ -1048,29 +1091,78 @@ __global__ __launch_bounds__(256) void k_kstats(KStatsArgs s) {
   }
   if (lane == 0) she[wave] = se;
   __syncthreads();
-  const int cnt = end - beg;
+  // one chunk: the cluster's statistics; more: this chunk's partial slot
+  const int64_t slot = (int64_t)h * s.pslots + s.po[(int64_t)h * (s.ncap + 1) + c] + j;
+  const int cnt = seg[c + 1] - seg[c];
   if (threadIdx.x < D) {
     const int dd = threadIdx.x;
-    if (cnt > 0) {
-      double a = 0.0, b = 0.0;
-      float x = -__builtin_inff(), y = __builtin_inff();
+    double a = 0.0, b = 0.0;
+    float x = -__builtin_inff(), y = __builtin_inff();
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        a += shk[w][dd];
-        b += shv[w][dd];
-        x = fmaxf(x, shx[w][dd]);
-        y = fminf(y, shn[w][dd]);
-      }
+    for (int w = 0; w < 4; ++w) {
+      a += shk[w][dd];
+      b += shv[w][dd];
+      x = fmaxf(x, shx[w][dd]);
+      y = fminf(y, shn[w][dd]);
+    }
+    if (nch == 1) {
       s.kmean[cb * D + dd] = (float)(a / cnt);
       s.vmean[cb * D + dd] = (float)(b / cnt);
       s.kmax[cb * D + dd] = (uint16_t)(__float_as_uint(x) >> 16);
       s.kmin[cb * D + dd] = (uint16_t)(__float_as_uint(y) >> 16);
     } else {
-      s.kmean[cb * D + dd] = 0.f; s.vmean[cb * D + dd] = 0.f;
-      s.kmax[cb * D + dd] = 0; s.kmin[cb * D + dd] = 0;
+      s.psk[slot * D + dd] = a;
+      s.psv[slot * D + dd] = b;
+      s.pmx[slot * D + dd] = x;
+      s.pmn[slot * D + dd] = y;
     }
   }
-  if (threadIdx.x == 0) s.msepart[cb] = she[0] + she[1] + she[2] + she[3];
+  if (threadIdx.x == 0) {
+    const double e = she[0] + she[1] + she[2] + she[3];
+    if (nch == 1) s.msepart[cb] = e;
+    else s.pse[slot] = e;
+  }
+}
+
+// Clusters of several chunks, empty clusters and unused slots up to ncap.
+template <int D>
+__global__ __launch_bounds__(128) void k_kstats_fin(KStatsArgs s) {
+  const int h = blockIdx.y, c = blockIdx.x;
+  const int ncl = s.ncl[h];
+  const int64_t cb = ((int64_t)h * s.ncap + c);
+  const int *seg = s.seg + (int64_t)h * (s.ncap + 1);
+  const int cnt = c < ncl ? seg[c + 1] - seg[c] : 0;
+  const int *co = s.co + (int64_t)h * (s.ncap + 1);
+  const int nch = c < ncl ? co[c + 1] - co[c] : 0;
+  if (nch == 1) return;  // finished by its chunk
+  if (nch == 0) {
+    for (int dd = threadIdx.x; dd < D; dd += 128) {
+      s.kmax[cb * D + dd] = 0; s.kmin[cb * D + dd] = 0;
+      s.kmean[cb * D + dd] = 0.f; s.vmean[cb * D + dd] = 0.f;
+    }
+    if (threadIdx.x == 0) s.msepart[cb] = 0.0;
+    return;
+  }
+  const int64_t s0 = (int64_t)h * s.pslots + s.po[(int64_t)h * (s.ncap + 1) + c];
+  for (int dd = threadIdx.x; dd < D; dd += 128) {
+    double a = 0.0, b = 0.0;
+    float x = -__builtin_inff(), y = __builtin_inff();
+    for (int q = 0; q < nch; ++q) {
+      a += s.psk[(s0 + q) * D + dd];
+      b += s.psv[(s0 + q) * D + dd];
+      x = fmaxf(x, s.pmx[(s0 + q) * D + dd]);
+      y = fminf(y, s.pmn[(s0 + q) * D + dd]);
+    }
+    s.kmean[cb * D + dd] = (float)(a / cnt);
+    s.vmean[cb * D + dd] = (float)(b / cnt);
+    s.kmax[cb * D + dd] = (uint16_t)(__float_as_uint(x) >> 16);
+    s.kmin[cb * D + dd] = (uint16_t)(__float_as_uint(y) >> 16);
+  }
+  if (threadIdx.x == 0) {
+    double e = 0.0;
+    for (int q = 0; q < nch; ++q) e += s.pse[s0 + q];
+    s.msepart[cb] = e;
+  }
 }
 
 __global__ __launch_bounds__(256) void k_mse_reduce(const double *__restrict__ msepart, int ncap,
@@ -1378,7 +1470,10 @@ void launch_stage_final(const int *state, int *ncl, uint8_t *fallback, int *stag
 }
 
 void launch_kstats(int D, const KStatsArgs &s, int BH, hipStream_t st) {
-  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_kstats<DD>, g2(s.ncap, BH), dim3(256), 0, st, s));
+  hipLaunchKernelGGL(k_kst_chunks, dim3(BH), dim3(1024), 0, st, s);
+  const int items = (s.L + KST_CHUNK - 1) / KST_CHUNK + s.ncap;
+  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_kstats_part<DD>, g2(items, BH), dim3(256), 0, st, s));
+  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_kstats_fin<DD>, g2(s.ncap, BH), dim3(128), 0, st, s));
   hipLaunchKernelGGL(k_mse_reduce, dim3(BH), dim3(256), 0, st, s.msepart, s.ncap, s.ncl, s.L, s.mse);
 }
 
