@@ -434,6 +434,12 @@ def summarize(args):
         def once(step, name):
             return [r for r in step if name in r["Kernel_Name"]][:1]
 
+        def sum_of(step, names):
+            """The first launch of each kernel in names, as one launch of their summed duration."""
+            rs = [once(step, n)[0] for n in names if once(step, n)]
+            t = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rs)
+            return {"Start_Timestamp": "0", "End_Timestamp": str(t), "Kernel_Name": "+".join(names)}
+
         x_bytes = BH * L * d * 2.0
         pad = lambda m: (m + 15) // 16 * 16
         hbm = lambda b: ("hbm", b, None)
@@ -452,8 +458,9 @@ def summarize(args):
             ("k_sort_scatter, queries and key stage 0, iteration 0",
              lambda st: after_seed(st, "k_sort_scatter", 0, 1) + after_seed(st, "k_sort_scatter", 1, 1),
              hbm(BH * L * 8.0), "read labels, write perm"),
-            ("k_kstats", lambda st: once(st, "k_kstats"), hbm(2 * x_bytes + BH * L * 4),
-             "read K, V and labels in cluster order"),
+            ("k_kst_chunks + k_kstats_part + k_kstats_fin (one launch each)",
+             lambda st: [sum_of(st, ("k_kst_chunks", "k_kstats_part", "k_kstats_fin"))],
+             hbm(2 * x_bytes + BH * L * 4), "read K, V and labels in cluster order"),
             ("k_attn", lambda st: once(st, "k_attn<"), ("flop", None, attn_flops),
              "4 d x the algorithmic query-key pairs (padding and masked keys not counted)"),
         ]
@@ -488,6 +495,43 @@ def summarize(args):
                          f"{frac[1]:.2f} ({frac[0]}) |")
         open(out, "w").write("\n".join(lines) + "\n")
         print("\n".join(lines))
+        return
+    if kind == "configs":
+        # one table of bench lines: --summarize configs <out.md> <command> :: <log>...
+        out = rest[0]
+        k = rest.index("::")
+        cmd, logs = " ".join(rest[1:k]), rest[k + 1:]
+        lines = ["# Bench lines, all workloads (one MI355X)", "", f"Command: `{cmd}`", "",
+                 "A step is one `ac_layer` call on resident inputs (cold unless marked warm); the phase columns "
+                 "come from a separate untimed pass through the entry points, the query clustering on a second "
+                 "stream beside the key clustering (`both` is their wall time). Dense baselines: the library's "
+                 "own dense mode and torch SDPA (flash backend) on the same tensors.", "",
+                 "| workload | step | selection | layer ms | dense-equiv TFLOP/s | cluster_q / cluster_k / both (ms) | "
+                 "select ms | attention ms | attention / bf16 peak | pairs kept | fallback heads | key clusters | "
+                 "own dense ms | SDPA flash ms | vs best dense | CPU oracle |",
+                 "|---|---|---|---:|---:|---|---:|---:|---:|---:|---:|---|---:|---:|---:|---|"]
+        raw = []
+        for lg in logs:
+            ls = [x for x in open(lg) if x.startswith("{")]
+            if not ls:
+                continue
+            d = json.loads(ls[-1])
+            raw.append(ls[-1].strip())
+            ph, db, cb = d["phase_ms"], d.get("dense_baseline") or {}, d.get("cpu_baseline")
+            sel = d["config"]["selection"] + (" + compensation" if d["config"]["compensate"] else "")
+            warm = "warm" if "warm" in d["timed_step"] else "cold"
+            cpu = (f"{cb['value']:.3f} TFLOP/s, {cb['cores']} cores, "
+                   f"{'complete head' if cb.get('complete_head') else 'extrapolated'}") if cb else "—"
+            lines.append(
+                f"| {d['config']['workload']} | {warm} | {sel} | {d['ms_per_step']:.2f} | {d['value']:.0f} | "
+                f"{ph['cluster_q']:.2f} / {ph['cluster_k']:.2f} / {ph['clustering_q_beside_k']:.2f} | "
+                f"{ph['score_select']:.2f} | {ph['sparse_attn']:.2f} | {d['roofline']['frac']:.3f} | "
+                f"{d['layer']['density_pairs']:.3f} | {d['layer']['fallback_heads']} | "
+                f"{d['layer']['key_clusters_min_max'][0]}–{d['layer']['key_clusters_min_max'][1]} | "
+                f"{db.get('own_dense_attn_ms', float('nan')):.2f} | {db.get('sdpa_flash_ms') or float('nan'):.2f} | "
+                f"{db.get('speedup_layer_vs_best_dense', float('nan')):.2f}x | {cpu} |")
+        lines += ["", "Raw JSON lines:", "", "```"] + raw + ["```"]
+        open(out, "w").write("\n".join(lines) + "\n")
         return
     if kind == "quest":
         # per-token Quest engines: bench --quest-compare lines + kernel-trace durations
