@@ -32,10 +32,12 @@ docstring of the function that implements it.
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test in
 ``tests/test_oracle_*.py`` except the readings that no page fixes (the m_t
-rule for stages after the first, the percentile definition, the k-means++
-subsample and random stream, the top-p temperature, the empty-cluster
+rule for stages after the first, the k-means++ subsample and the order of
+its random stream, the choice of the top-p temperature, the empty-cluster
 policy and the number of warm iterations).  Those are "parity unpinned":
-they are checked only GPU-against-oracle.
+they are checked only GPU-against-oracle.  (The percentile definition is
+pinned to NumPy's inverted-CDF percentile, and the top-p mass to the
+attention mass of the kept clusters.)
 """
 from .numerics import Params, bf16_round, bf16_to_f64, uniform01, splitmix64_next  # noqa: F401
 from . import kmeans, multistage, stats, score, attention, layer, pcasplit  # noqa: F401

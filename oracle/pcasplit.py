@@ -10,8 +10,8 @@ cluster size be set freely, and the method fixes every cluster size to a
 power of two so that block-sparse attention costs about what dense attention
 costs per key-query interaction (abstract); it splits recursively along
 principal components to produce clusters of a preset size (end of section 2);
-the method section is cut off after "projecting the key or query set onto an
-approximate ...".  Readings taken here:
+the method section breaks off mid-sentence as it begins to describe an
+approximate projection of the key or query set.  Readings taken here:
 
 * A node of n > b points is cut in two by its leading principal direction:
   the points are ordered by their projection onto it (ties: lower token
@@ -21,8 +21,8 @@ approximate ...".  Readings taken here:
   depends only on n and b.
 * The direction is the leading right singular vector of the node's
   mean-centred points, taken on a strided subsample {floor(j n / s)} of
-  s = min(n, sample) points (the page's "approximate" projection; the
-  GPU approximates this vector by power iteration).  Its sign makes the
+  s = min(n, sample) points (the approximation the page mentions; the GPU
+  approximates this vector by power iteration).  Its sign makes the
   component of largest magnitude positive (lowest index among equal
   magnitudes).
 * Children keep their parent's token order (the split is a stable
