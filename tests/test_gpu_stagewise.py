@@ -155,17 +155,19 @@ def check_query_trace(r, qtr, Qb, p):
     return skipped
 
 
-@pytest.mark.parametrize("name,H,overrides", [
-    ("wan", 2, {}),                       # tau = 1.5 x mean; U_1 above the sort's one-group size
-    ("cogvideox", 2, {}),                 # d = 64, percentile tau by radix select over 70,200 distances
+@pytest.mark.parametrize("name,H,overrides,max_stages", [
+    ("wan", 2, {}, 12),                   # tau = 1.5 x mean; U_1 above the sort's one-group size
+    ("cogvideox", 2, {}, 12),             # d = 64, percentile tau by radix select over 70,200 distances
     # the widest Student-t heads of the long workload: Algorithm 1 falls back
-    ("long", 2, dict(key_sigma=(0.3, 0.3), key_outlier_scale=(0.70, 0.75))),
+    ("long", 2, dict(key_sigma=(0.3, 0.3), key_outlier_scale=(0.70, 0.75)), 12),
+    # absolute tau 5.5: a compact head finishes after 9 stages, a dispersed head with uniform
+    # outliers keeps every key and falls back when the 15th stage reaches N_max
+    ("hunyuan", 2, dict(key_sigma=(0.15, 0.8), outlier_heads=(1,)), 16),
 ])
-def test_full_length_stagewise_clustering(name, H, overrides):
+def test_full_length_stagewise_clustering(name, H, overrides, max_stages):
     w = gen.get_workload(name, H=H, **overrides)
     Q, K, V = gen.generate(w)
     p = workload_oracle_params(name)
-    max_stages = 12
     r, tr, qtr = _run_traced(Q, K, V, p, max_stages)
     s = check_key_trace(r, tr, K, p, max_stages)
     print(f"\n[{name}] stage sizes {s['stages']}, fallback {s['fallback']}, tie clusters {s['tie_clusters']}, "
@@ -173,6 +175,9 @@ def test_full_length_stagewise_clustering(name, H, overrides):
     assert len(s["stages"][0]) >= 2, "the workload should run several stages"
     if name == "long":
         assert any(s["fallback"]), "the widest heads should fall back"
+    if name == "hunyuan":
+        assert s["fallback"] == [0, 1], "the dispersed head, and only it, falls back"
+        assert len(s["stages"][1]) == 15, "the dispersed head runs every stage up to N_max"
     skipped = check_query_trace(r, qtr, Q, p)
     print(f"[{name}] query tie clusters {skipped}")
 
