@@ -15,6 +15,7 @@
 //   4. projects every point of the node (fp32), radix-selects the n_left-th
 //      smallest (projection, position) key in four 8-bit passes, and writes
 //      the stable partition of the node's tokens.
+#include <algorithm>
 #include <utility>
 #include <vector>
 
@@ -23,7 +24,7 @@
 
 namespace ac {
 
-constexpr int PCA_SP = PCA_SMAX + 8;  // LDS row stride (bf16) of the dimension-major subsample
+constexpr int PCA_SP = PCA_SMAX + 8;  // largest LDS row stride (bf16) of the dimension-major subsample
 
 // Internal nodes of the split tree of n points, level by level, left to
 // right: nodes[k] = (first position, count); lvl[l] = first node of level l,
@@ -70,8 +71,10 @@ AC_DEV int2 block_scan2(int x, int y, int2 *sh, int2 &tot) {
   return make_int2(ox + ix - x, oy + iy - y);
 }
 
+// sp: row stride (bf16) of the subsample in LDS, sized by the launch to the
+// level's largest node (the dynamic LDS holds max(D sp bf16, D D fp32))
 template <int D>
-__global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int count) {
+__global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int count, int sp) {
   constexpr int NT = 512;
   const int h = blockIdx.y, node = first + (int)blockIdx.x;
   if ((int)blockIdx.x >= count) return;
@@ -85,7 +88,7 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
   uint32_t *key = a.key + (int64_t)h * a.L + start;
 
   extern __shared__ __align__(16) unsigned char pca_lds[];
-  uint16_t *Y = reinterpret_cast<uint16_t *>(pca_lds);  // [D][PCA_SP] bf16, later C [D][D] fp32
+  uint16_t *Y = reinterpret_cast<uint16_t *>(pca_lds);  // [D][sp] bf16, later C [D][D] fp32
   float *C = reinterpret_cast<float *>(pca_lds);
   __shared__ float mu[D], wbuf[2][D], nrm_part[2][8];
   __shared__ uint32_t hist[256];
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
       *(u32x4_t *)v = *(const u32x4_t *)(X + (int64_t)t * D + c * 8);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) Y[(c * 8 + e) * PCA_SP + j] = v[e];
+    for (int e = 0; e < 8; ++e) Y[(c * 8 + e) * sp + j] = v[e];
   }
   __syncthreads();
   // mean of each dimension (four threads per dimension, fixed order)
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
     const int i = tid >> 2, part = tid & 3;
     float acc = 0.f;
     if (i < D)
-      for (int j = part; j < s; j += 4) acc += bf2f(Y[i * PCA_SP + j]);
+      for (int j = part; j < s; j += 4) acc += bf2f(Y[i * sp + j]);
     acc += __shfl_xor(acc, 1, 64);
     acc += __shfl_xor(acc, 2, 64);
     if (i < D && part == 0) mu[i] = acc / (float)s;
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
   __syncthreads();
   for (int q = tid; q < D * s; q += NT) {
     const int i = q / s, j = q % s;
-    Y[i * PCA_SP + j] = f2bf(bf2f(Y[i * PCA_SP + j]) - mu[i]);
+    Y[i * sp + j] = f2bf(bf2f(Y[i * sp + j]) - mu[i]);
   }
   __syncthreads();
   // start of the power iteration: the subsample row farthest from the mean
@@ -131,7 +134,7 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
     if (tid < s) {
       nn = 0.f;
       for (int i = 0; i < D; ++i) {
-        const float y = bf2f(Y[i * PCA_SP + tid]);
+        const float y = bf2f(Y[i * sp + tid]);
         nn = fmaf(y, y, nn);
       }
     }
@@ -154,7 +157,7 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
         if (on > bn || (on == bn && oj < bjj)) { bn = on; bjj = oj; }
       }
       // unnormalised start; the first iteration normalises (its norm is set here)
-      for (int i = lane; i < D; i += 64) wbuf[0][i] = bf2f(Y[i * PCA_SP + bjj]);
+      for (int i = lane; i < D; i += 64) wbuf[0][i] = bf2f(Y[i * sp + bjj]);
       float sq = 0.f;
       for (int i = lane; i < D; i += 64) sq = fmaf(wbuf[0][i], wbuf[0][i], sq);
       sq = wave_sum(sq);
@@ -176,8 +179,8 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
       const int tile = wave + 8 * k;
       if (tile < NTILE) {
         const int I = tile / (D / 32), J = tile % (D / 32);
-        const bf16x8_t av = *(const bf16x8_t *)&Y[(I * 32 + l32) * PCA_SP + k0 + 8 * g];
-        const bf16x8_t bv = *(const bf16x8_t *)&Y[(J * 32 + l32) * PCA_SP + k0 + 8 * g];
+        const bf16x8_t av = *(const bf16x8_t *)&Y[(I * 32 + l32) * sp + k0 + 8 * g];
+        const bf16x8_t bv = *(const bf16x8_t *)&Y[(J * 32 + l32) * sp + k0 + 8 * g];
         acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[k], 0, 0, 0);
       }
     }
@@ -419,7 +422,6 @@ void launch_pca_split(int D, const PcaArgs &a, const std::vector<int> &counts, i
                       hipStream_t st) {
   hipLaunchKernelGGL(k_pca_tree, dim3(1), dim3(1), 0, st, a.L, a.block, a.nodes, a.lvl);
   hipLaunchKernelGGL(k_iota_perm, dim3((unsigned)((a.L + 255) / 256), (unsigned)BH), dim3(256), 0, st, a.perm, a.L);
-  const size_t lds = (size_t)D * PCA_SP * 2 > (size_t)D * D * 4 ? (size_t)D * PCA_SP * 2 : (size_t)D * D * 4;
   // dynamic LDS above the default limit (a refusal shows up as a launch error)
   static bool lds64 = hipFuncSetAttribute((const void *)k_pca_level<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                           64 * PCA_SP * 2) == hipSuccess;
@@ -428,13 +430,21 @@ void launch_pca_split(int D, const PcaArgs &a, const std::vector<int> &counts, i
   (void)lds64;
   (void)lds128;
   int first = 0;
+  int nmax = a.L;  // largest node of the level: the left child is never the smaller one
   for (size_t l = 0; l < counts.size(); ++l) {
+    // the subsample of the level's largest node sets the LDS row stride, so that
+    // the deep levels (small nodes) fit two blocks a compute unit
+    const int spad = (std::min(nmax, PCA_SMAX) + 15) & ~15;
+    const int sp = spad + 8;
+    const size_t lds = std::max((size_t)D * sp * 2, (size_t)D * D * 4);
     if (D == 64)
       hipLaunchKernelGGL(k_pca_level<64>, dim3((unsigned)counts[l], (unsigned)BH), dim3(512), lds, st, a, first,
-                         counts[l]);
+                         counts[l], sp);
     else
       hipLaunchKernelGGL(k_pca_level<128>, dim3((unsigned)counts[l], (unsigned)BH), dim3(512), lds, st, a, first,
-                         counts[l]);
+                         counts[l], sp);
+    const int nb = (nmax + a.block - 1) / a.block;
+    nmax = a.block * ((nb + 1) / 2);
     if (perm_trace)
       hipLaunchKernelGGL(k_copy_rows_i32, dim3((unsigned)((a.L + 255) / 256), (unsigned)BH), dim3(256), 0, st, a.perm,
                          perm_trace + l * (int64_t)a.L, a.L, (int64_t)counts.size() * a.L);
