@@ -251,8 +251,8 @@ ac_status ac_cluster_q_trace(const ac_shape *s, const ac_params *p, const uint16
  * at most block rows are clusters.  So every cluster holds exactly `block` tokens except the last
  * (L mod block when nonzero), clusters are numbered left to right, and each lists its tokens in
  * ascending order.  The direction of a node is the leading eigenvector of the covariance of a strided
- * subsample {floor(j n / s)} of s = min(n, 512) of its rows, centred and rounded to bf16 (the page's
- * "approximate" projection), found by 64 power iterations from the subsample row farthest from the
+ * subsample {floor(j n / s)} of s = min(n, 512) of its rows, centred and rounded to bf16 (the
+ * approximation the page mentions), found by 64 power iterations from the subsample row farthest from the
  * mean and oriented so that its component of largest magnitude is positive.  block: a power of two in
  * [16, 4096] with ceil(L / block) <= the cluster capacity (AC_E_ARG otherwise).
  *
