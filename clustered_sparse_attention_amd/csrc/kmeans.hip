@@ -1004,10 +1004,9 @@ __global__ __launch_bounds__(1024) void k_kst_chunks(KStatsArgs s) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void k_kstats_part(KStatsArgs s) {
-  // 16 row groups of 16 lanes (PL dims each), four member rows per group in
-  // flight; the groups of a wave combine with shuffles, the four waves
-  // through a small LDS table
+__global__ __launch_bounds__(64) void k_kstats_part(KStatsArgs s) {
+  // one wave per chunk: 4 row groups of 16 lanes (PL dims each), four member
+  // rows per group in flight, the groups combined with shuffles
   constexpr int PL = D / 16;  // dims per lane, 16 lanes per row
   typedef uint32_t pw_t __attribute__((ext_vector_type(PL / 2)));
   const int h = blockIdx.y, item = blockIdx.x;
@@ -1022,7 +1021,6 @@ __global__ __launch_bounds__(256) void k_kstats_part(KStatsArgs s) {
   const int c = lo, j = item - co[c], nch = co[c + 1] - co[c];
   const int64_t cb = ((int64_t)h * s.ncap + c);
   const int grp = threadIdx.x >> 4, sub = threadIdx.x & 15;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int *seg = s.seg + (int64_t)h * (s.ncap + 1);
   const int *perm = s.perm + (int64_t)h * s.L;
   const int beg = seg[c] + j * KST_CHUNK, end = min(seg[c + 1], beg + KST_CHUNK);
@@ -1036,10 +1034,10 @@ __global__ __launch_bounds__(256) void k_kstats_part(KStatsArgs s) {
     sk[k] = 0.0; sv[k] = 0.0; mx[k] = -__builtin_inff(); mn[k] = __builtin_inff();
     cc[k] = cent[sub * PL + k];
   }
-  for (int p0 = beg + grp; p0 < end; p0 += 64) {
+  for (int p0 = beg + grp; p0 < end; p0 += 16) {
     int64_t row[4];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) row[jj] = (p0 + 16 * jj < end) ? (int64_t)perm[p0 + 16 * jj] : -1;
+    for (int jj = 0; jj < 4; ++jj) row[jj] = (p0 + 4 * jj < end) ? (int64_t)perm[p0 + 4 * jj] : -1;
     pw_t kw[4], vw[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
@@ -1064,7 +1062,7 @@ __global__ __launch_bounds__(256) void k_kstats_part(KStatsArgs s) {
       }
     }
   }
-  // the four row groups of a wave (lanes sub, sub + 16, sub + 32, sub + 48)
+  // the four row groups (lanes sub, sub + 16, sub + 32, sub + 48)
 #pragma unroll
   for (int o = 16; o < 64; o <<= 1) {
 #pragma unroll
@@ -1076,51 +1074,29 @@ __global__ __launch_bounds__(256) void k_kstats_part(KStatsArgs s) {
     }
   }
   se = wave_sum(se);
-  // then the four waves
-  __shared__ double shk[4][D], shv[4][D];
-  __shared__ float shx[4][D], shn[4][D];
-  __shared__ double she[4];
-  if (lane < 16) {
-#pragma unroll
-    for (int k = 0; k < PL; ++k) {
-      shk[wave][sub * PL + k] = sk[k];
-      shv[wave][sub * PL + k] = sv[k];
-      shx[wave][sub * PL + k] = mx[k];
-      shn[wave][sub * PL + k] = mn[k];
-    }
-  }
-  if (lane == 0) she[wave] = se;
-  __syncthreads();
   // one chunk: the cluster's statistics; more: this chunk's partial slot
   const int64_t slot = (int64_t)h * s.pslots + s.po[(int64_t)h * (s.ncap + 1) + c] + j;
   const int cnt = seg[c + 1] - seg[c];
-  if (threadIdx.x < D) {
-    const int dd = threadIdx.x;
-    double a = 0.0, b = 0.0;
-    float x = -__builtin_inff(), y = __builtin_inff();
+  if (grp == 0) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      a += shk[w][dd];
-      b += shv[w][dd];
-      x = fmaxf(x, shx[w][dd]);
-      y = fminf(y, shn[w][dd]);
-    }
-    if (nch == 1) {
-      s.kmean[cb * D + dd] = (float)(a / cnt);
-      s.vmean[cb * D + dd] = (float)(b / cnt);
-      s.kmax[cb * D + dd] = (uint16_t)(__float_as_uint(x) >> 16);
-      s.kmin[cb * D + dd] = (uint16_t)(__float_as_uint(y) >> 16);
-    } else {
-      s.psk[slot * D + dd] = a;
-      s.psv[slot * D + dd] = b;
-      s.pmx[slot * D + dd] = x;
-      s.pmn[slot * D + dd] = y;
+    for (int k = 0; k < PL; ++k) {
+      const int dd = sub * PL + k;
+      if (nch == 1) {
+        s.kmean[cb * D + dd] = (float)(sk[k] / cnt);
+        s.vmean[cb * D + dd] = (float)(sv[k] / cnt);
+        s.kmax[cb * D + dd] = (uint16_t)(__float_as_uint(mx[k]) >> 16);
+        s.kmin[cb * D + dd] = (uint16_t)(__float_as_uint(mn[k]) >> 16);
+      } else {
+        s.psk[slot * D + dd] = sk[k];
+        s.psv[slot * D + dd] = sv[k];
+        s.pmx[slot * D + dd] = mx[k];
+        s.pmn[slot * D + dd] = mn[k];
+      }
     }
   }
   if (threadIdx.x == 0) {
-    const double e = she[0] + she[1] + she[2] + she[3];
-    if (nch == 1) s.msepart[cb] = e;
-    else s.pse[slot] = e;
+    if (nch == 1) s.msepart[cb] = se;
+    else s.pse[slot] = se;
   }
 }
 
@@ -1472,7 +1448,7 @@ void launch_stage_final(const int *state, int *ncl, uint8_t *fallback, int *stag
 void launch_kstats(int D, const KStatsArgs &s, int BH, hipStream_t st) {
   hipLaunchKernelGGL(k_kst_chunks, dim3(BH), dim3(1024), 0, st, s);
   const int items = (s.L + KST_CHUNK - 1) / KST_CHUNK + s.ncap;
-  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_kstats_part<DD>, g2(items, BH), dim3(256), 0, st, s));
+  AC_D_DISPATCH(D, hipLaunchKernelGGL(k_kstats_part<DD>, g2(items, BH), dim3(64), 0, st, s));
   AC_D_DISPATCH(D, hipLaunchKernelGGL(k_kstats_fin<DD>, g2(s.ncap, BH), dim3(128), 0, st, s));
   hipLaunchKernelGGL(k_mse_reduce, dim3(BH), dim3(256), 0, st, s.msepart, s.ncap, s.ncl, s.L, s.mse);
 }
