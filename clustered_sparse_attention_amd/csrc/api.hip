@@ -465,18 +465,22 @@ KStatsArgs kstats_args(const Plan &P, const uint16_t *K, const uint16_t *V, cons
   return a;
 }
 
+// assign: with it, the final assignment of every key over all centres first
+// (without, k->labels already hold it)
 ac_status finish_keys(const Plan &P, const uint16_t *K, const uint16_t *V, ac_clusters *k, ac_kstats *stats,
-                      void *ws, hipStream_t st, int mmax) {
+                      void *ws, hipStream_t st, int mmax, bool assign = true) {
   // final assignment of every key over all centres, counting sort, statistics
   const int BH = P.BH, L = P.L, D = P.D;
   Engine E{P, P.sk, ws, st};
   launch_fill_i32(E.n(), BH, L, st);
   launch_copy_i32(k->ncl, E.m(), BH, st);
   launch_fill_i32(E.coff(), BH, 0, st);
-  KmArgs a{K, (int64_t)L * D, nullptr, 0, E.n(), E.m(), E.coff(), k->cent, (int64_t)k->ncap * D};
-  CentOps op = E.ops();
-  launch_cent_prep(D, a, op, BH, mmax, st);
-  launch_assign(D, a, op, BH, mmax, L, k->labels, L, st);
+  if (assign) {
+    KmArgs a{K, (int64_t)L * D, nullptr, 0, E.n(), E.m(), E.coff(), k->cent, (int64_t)k->ncap * D};
+    CentOps op = E.ops();
+    launch_cent_prep(D, a, op, BH, mmax, st);
+    launch_assign(D, a, op, BH, mmax, L, k->labels, L, st);
+  }
   SortArgs s = E.sort_args(k->labels, k->perm, k->seg, k->ncap, mmax);
   launch_sort(s, BH, L, st);
   const KStatsArgs ks = kstats_args(P, K, V, k, stats, ws);
@@ -721,8 +725,8 @@ ac_status do_cluster_k_warm(const Plan &P, const ac_params *p, const uint16_t *K
   AC_CHECK_LAUNCH();
   KmArgs a{K, (int64_t)L * D, nullptr, 0, E.n(), E.m(), E.coff(), k->cent, (int64_t)k->ncap * D};
   AC_TRY(E.run(a, k->ncap, L, false, p->iters_warm, p, 1, 0, k->labels));
-  // finish_keys repeats the final assignment; harmless and keeps one code path
-  return finish_keys(P, K, V, k, stats, ws, st, k->ncap);
+  // the loop ends with the final assignment: only the order and statistics remain
+  return finish_keys(P, K, V, k, stats, ws, st, k->ncap, false);
 }
 
 // ClusterAttention's clustering of the rows X of every head by recursive
