@@ -533,6 +533,42 @@ def summarize(args):
         lines += ["", "Raw JSON lines:", "", "```"] + raw + ["```"]
         open(out, "w").write("\n".join(lines) + "\n")
         return
+    if kind == "denoise":
+        # --summarize denoise <out.md> <command> :: <log>...  (bench.py --denoise lines)
+        out = rest[0]
+        k = rest.index("::")
+        cmd, logs = " ".join(rest[1:k]), rest[k + 1:]
+        runs = []
+        for lg in logs:
+            ls = [x for x in open(lg) if x.startswith("{")]
+            if ls:
+                runs.append(json.loads(ls[-1]))
+        w = runs[0]["workload"] if runs else ""
+        lines = [f"# Denoising runs under the multi-step policy, {w}", "", f"Commands: `{cmd}`", "",
+                 "Each step's Q and K are a 2% perturbation of the previous step's. k_max is calibrated on an "
+                 "uncapped first sparse step (untimed, target 15% of the heads); with N_max = k_max, Algorithm 1 "
+                 "lets a head fall back only when a stage would start with k_max centres and keys are left. "
+                 "Dense warm-up steps run the library's dense mode; the cold step runs Algorithm 1, the warm "
+                 "steps Lloyd iterations from the previous step's centres.", "",
+                 "| run | dense warm-up steps (ms) | cold step (ms) | warm steps, mean (ms) | total (ms) | "
+                 "own dense x steps (ms) | SDPA flash x steps (ms) | vs own dense | vs SDPA flash | k_max | "
+                 "heads dense |", "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+        for r in runs:
+            T = r["steps"]
+            dense = ", ".join(str(x["ms"]) for x in r["per_step"] if x["mode"] == "dense")
+            od, sd = r.get("own_dense_ms"), r.get("sdpa_flash_ms")
+            name = "SNR top-p" if r.get("topp_schedule") else "density 0.15"
+            lines.append(f"| {name} | {dense} | {r['cold_ms']} | {r['warm_ms_mean']} | {r['value']} | "
+                         f"{od * T:.1f} | {sd * T:.1f} | {od * T / r['value']:.2f}x | {sd * T / r['value']:.2f}x | "
+                         f"{r['kmax']} | {r['fallback_heads']} |")
+        for r in runs:
+            if r.get("topp_schedule"):
+                lines += ["", "Per step (top-p run): " + ", ".join(
+                    f"{x['step']}: {x['mode']} {x['ms']} ms" + (f" (p {x['sel_param']})" if "sel_param" in x else "")
+                    for x in r["per_step"])]
+        lines += ["", "Raw JSON lines:", "", "```"] + [json.dumps(r) for r in runs] + ["```"]
+        open(out, "w").write("\n".join(lines) + "\n")
+        return
     if kind == "quest":
         # per-token Quest engines: bench --quest-compare lines + kernel-trace durations
         src, lines_json, out, cmd = rest[0], rest[1], rest[2], " ".join(rest[3:])
