@@ -188,3 +188,32 @@ def test_pca_split_full_length(name):
     check_scores_selection(r, p)
     worst = check_attention_sampled(r, Q, K, V, p, rows_seed=9004, nrows=1024)
     print(f"\n[{name}] PCA split near ties {ties}; attention worst max-abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}")
+
+
+@pytest.mark.parametrize("L,d,bk", [(1793, 128, 512), (4396, 64, 4096), (768, 128, 256)])
+def test_key_statistics_at_chunk_boundaries(L, d, bk):
+    """The key statistics run in chunks of 256 members, one wave per chunk,
+    and combine the chunks of larger clusters in order.  The PCA split makes
+    clusters of exactly bk members (the last one L mod bk), so these cases
+    hold clusters of 512 (two full chunks), 257 (a full chunk and a single
+    member), 4096 (sixteen chunks), 300 and exactly 256 (one full chunk):
+    counts, means, max/min and MSE against the oracle on every cluster."""
+    from oracle import stats as ost
+    w = gen.get_workload("tiny", H=2, L=L, d=d)
+    Q, K, V = gen.generate(w)
+    p = oracle_params(nq=-(-L // 256), m0=32, nmax=max(64, -(-L // bk) + 1))
+    r, _, _ = _run_pca(Q, K, V, p, 256, bk, trace=False)
+    sizes = np.diff(np_(r.k.seg), axis=1)
+    for h in range(r.BH):
+        nk = int(np_(r.k.ncl)[h])
+        assert sizes[h, :nk].tolist() == ops.leaf_sizes(L, bk)
+        st = ost.key_stats(K.reshape(r.BH, L, d)[h], V.reshape(r.BH, L, d)[h], np_(r.k.labels)[h],
+                           np_(r.k.cent)[h, :nk].astype(np.float64))
+        assert np.array_equal(bf16_dev_to_f64(r.st.kmax)[h, :nk], st["kmax"])
+        assert np.array_equal(bf16_dev_to_f64(r.st.kmin)[h, :nk], st["kmin"])
+        scale = max(1.0, float(np.max(np.abs(st["kmean"]))))
+        assert np.max(np.abs(np_(r.st.kmean)[h, :nk] - st["kmean"])) <= 1e-5 * scale
+        assert np.max(np.abs(np_(r.st.vmean)[h, :nk] - st["vmean"])) <= 1e-5 * max(1.0, float(np.max(np.abs(st["vmean"]))))
+        assert abs(np_(r.st.mse)[h] - st["mse"]) <= 1e-4 * st["mse"]
+        # clusters beyond the count are zeroed
+        assert not np.any(np_(r.st.kmean)[h, nk:]) and not np.any(bf16_dev_to_f64(r.st.kmax)[h, nk:])
