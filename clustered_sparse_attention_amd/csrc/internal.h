@@ -249,7 +249,6 @@ void launch_copy_converged(const int *n, const int *neff, const int *src, int *d
                            hipStream_t st);
 void launch_copy_f32(const float *s, float *d, int64_t n, hipStream_t st);
 void launch_copy_u8(const uint8_t *s, uint8_t *d, int64_t n, hipStream_t st);
-void launch_set_m_min(int *m, const int *n, int v, int BH, hipStream_t st);
 
 // select.hip
 void launch_score(int D, const ScoreArgs &a, int BH, hipStream_t st);

@@ -1218,11 +1218,6 @@ __global__ void k_fill_u8(uint8_t *__restrict__ p, int64_t n, uint8_t v) {
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = v;
 }
-// m[h] = min(v, n[h]) clipped below at 0
-__global__ void k_set_m_min(int *__restrict__ m, const int *__restrict__ n, int v, int BH) {
-  int h = blockIdx.x * 256 + threadIdx.x;
-  if (h < BH) m[h] = max(0, min(v, n[h]));
-}
 
 // ---------------------------------------------------------------------------
 // Stage records of the traced entry points: copies only.
@@ -1482,9 +1477,6 @@ void launch_copy_f32(const float *s, float *d, int64_t n, hipStream_t st) {
 }
 void launch_copy_u8(const uint8_t *s, uint8_t *d, int64_t n, hipStream_t st) {
   if (n > 0) hipLaunchKernelGGL(k_copy_u8, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, s, d, n);
-}
-void launch_set_m_min(int *m, const int *n, int v, int BH, hipStream_t st) {
-  hipLaunchKernelGGL(k_set_m_min, dim3((BH + 255) / 256), dim3(256), 0, st, m, n, v, BH);
 }
 
 }  // namespace ac
