@@ -255,6 +255,11 @@ Plan make_plan(const ac_shape *s, const ac_params *p) {
   P.fops_norm = take(BH * P.ncapk * 4);
   P.best = take(BH * L * 4);
   // every stage but the last adds min(L, m0) centres, and none starts at nmax or beyond
+  // Stages of Algorithm 1: every stage but the last adds min(m0, L) centres.
+  // A stage on |U| <= m0 keys makes each its own centre (duplicates at
+  // distance 0 too), so with tau > 0 it removes them all and is the last;
+  // with tau = 0 nothing is ever removed and |U| stays L.  So at most
+  // ceil(nmax / min(m0, L)) stages start below the cap, plus the last one.
   P.stage_slots = (int)cdiv(p->nmax, std::max(1, std::min(p->m0, P.L))) + 2;
   P.mtab = take((size_t)P.stage_slots * BH * 4);
   P.ctab = take((size_t)P.stage_slots * BH * 4);
