@@ -130,13 +130,16 @@ class Layer:
             if ev: ev[1].record(main)
             if ev: ev[4].record(main)
         elif self.pca:
-            # the two sides share the workspace's split scratch: one after the other
+            # the query split on the side stream beside the key split (disjoint scratch)
             if ev: ev[0].record(main)
-            if ev: ev[2].record(main)
-            ac.ac_cluster_q_pca(self.shape, self.p, self.Q, self.pca[0], self.q, self.ws)
-            if ev: ev[3].record(main)
+            self.side.wait_stream(main)
+            if ev: ev[2].record(self.side)
+            ac.ac_cluster_q_pca(self.shape, self.p, self.Q, self.pca[0], self.q, self.ws,
+                                stream=self.side.cuda_stream)
+            if ev: ev[3].record(self.side)
             ac.ac_cluster_k_pca(self.shape, self.p, self.K, self.V, self.pca[1], self.k, self.st, self.ws)
             if ev: ev[1].record(main)
+            main.wait_stream(self.side)
             if ev: ev[4].record(main)
         else:
             if ev: ev[0].record(main)

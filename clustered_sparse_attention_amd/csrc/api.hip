@@ -125,7 +125,8 @@ struct Plan {
   // interaction matrix: raw query sums and counts per query cluster
   size_t qsum, qcnt;
   // principal-component split: token scratch, projection keys, node table
-  size_t pca_tmp, pca_key, pca_nodes, pca_lvl;
+  size_t pca_tmp, pca_key, pca_nodes, pca_lvl;          // key side
+  size_t pca_tmp_q, pca_key_q, pca_nodes_q, pca_lvl_q;  // query side (the two sides may overlap)
   // cold key clustering: operands of every stage's centres at their global
   // rows, the running nearest-centre score, per-stage centre counts and
   // offsets for the merge launches, Algorithm 1's per-head state, all-L counts
@@ -250,6 +251,10 @@ Plan make_plan(const ac_shape *s, const ac_params *p) {
   P.pca_key = take(BH * L * 4);
   P.pca_nodes = take((L / PCA_BLOCK_MIN + 2) * 8);  // at most ceil(L / b) - 1 internal nodes
   P.pca_lvl = take(64 * 4);
+  P.pca_tmp_q = take(BH * L * 4);
+  P.pca_key_q = take(BH * L * 4);
+  P.pca_nodes_q = take((L / PCA_BLOCK_MIN + 2) * 8);
+  P.pca_lvl_q = take(64 * 4);
   P.fops_hi = take(BH * P.ncapk * D * 2);
   P.fops_lo = take(BH * P.ncapk * D * 2);
   P.fops_norm = take(BH * P.ncapk * 4);
@@ -736,9 +741,10 @@ ac_status do_cluster_k_warm(const Plan &P, const ac_params *p, const uint16_t *K
 
 // ClusterAttention's clustering of the rows X of every head by recursive
 // splits along principal directions into clusters of `block` rows; the
-// order, labels, segments, count and member-mean centres of `out`.
+// order, labels, segments, count and member-mean centres of `out`.  The
+// query and the key side have scratch of their own, so the two may overlap.
 ac_status do_pca_split(const Plan &P, const uint16_t *X, int block, ac_clusters *out, const ac_pca_trace *tr,
-                       void *ws, hipStream_t st) {
+                       void *ws, hipStream_t st, bool query_side) {
   const int BH = P.BH, L = P.L, D = P.D;
   const std::vector<int> counts = pca_level_counts(L, block);
   int ninternal = 0;
@@ -746,10 +752,10 @@ ac_status do_pca_split(const Plan &P, const uint16_t *X, int block, ac_clusters 
   PcaArgs a;
   a.X = X;
   a.perm = out->perm;
-  a.tmp = at<int>(ws, P.pca_tmp);
-  a.key = at<uint32_t>(ws, P.pca_key);
-  a.nodes = at<int2>(ws, P.pca_nodes);
-  a.lvl = at<int>(ws, P.pca_lvl);
+  a.tmp = at<int>(ws, query_side ? P.pca_tmp_q : P.pca_tmp);
+  a.key = at<uint32_t>(ws, query_side ? P.pca_key_q : P.pca_key);
+  a.nodes = at<int2>(ws, query_side ? P.pca_nodes_q : P.pca_nodes);
+  a.lvl = at<int>(ws, query_side ? P.pca_lvl_q : P.pca_lvl);
   a.dir = tr ? tr->dir : nullptr;
   a.ndir = ninternal;
   a.L = L;
@@ -1049,7 +1055,7 @@ AC_API ac_status ac_cluster_q_pca(const ac_shape *s, const ac_params *p, const u
   uint16_t *qhat = at<uint16_t>(ws, P.qhat);
   float *qn = at<float>(ws, P.qn);
   launch_qnorm(P.D, Q, qhat, qn, (int64_t)P.BH * P.L, st);
-  AC_TRY(do_pca_split(P, qhat, block, q_out, trace, ws, st));
+  AC_TRY(do_pca_split(P, qhat, block, q_out, trace, ws, st, true));
   launch_seg_mean(qn, q_out->perm, q_out->seg, P.L, q_out->ncap, q_out->ncl, q_out->rho, P.BH, st);
   AC_CHECK_LAUNCH();
   return AC_OK;
@@ -1070,7 +1076,7 @@ AC_API ac_status ac_cluster_k_pca(const ac_shape *s, const ac_params *p, const u
   AC_TRY(check_device());
   hipStream_t st = (hipStream_t)stream;
   const int BH = P.BH;
-  AC_TRY(do_pca_split(P, K, block, k_out, trace, ws, st));
+  AC_TRY(do_pca_split(P, K, block, k_out, trace, ws, st, false));
   const KStatsArgs ks = kstats_args(P, K, V, k_out, stats, ws);
   launch_kstats(P.D, ks, BH, st);
   launch_fill_u8(stats->fallback, BH, 0, st);

@@ -71,6 +71,25 @@ AC_DEV int2 block_scan2(int x, int y, int2 *sh, int2 &tot) {
   return make_int2(ox + ix - x, oy + iy - y);
 }
 
+// DPP move of a float within rows of 16 lanes (controls: quad permutes
+// 0x00-0xFF, row mirror 0x140, half-row mirror 0x141); all lanes active
+template <int CTRL>
+AC_DEV float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// sum over each row of 16 lanes, left in every lane of the row: after each
+// step the groups of 2, 4, 8, 16 lanes hold equal values, so the mirrors
+// pair every lane with the other half of its group
+AC_DEV float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);   // quad: xor 1
+  v += dpp_f32<0x4E>(v);   // quad: xor 2
+  v += dpp_f32<0x141>(v);  // half-row mirror
+  v += dpp_f32<0x140>(v);  // row mirror
+  return v;
+}
+// the value lane l holds (uniform)
+AC_DEV float lane_f32(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
+
 // sp: row stride (bf16) of the subsample in LDS, sized by the launch to the
 // level's largest node (the dynamic LDS holds max(D sp bf16, D D fp32))
 template <int D>
@@ -90,41 +109,82 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
   extern __shared__ __align__(16) unsigned char pca_lds[];
   uint16_t *Y = reinterpret_cast<uint16_t *>(pca_lds);  // [D][sp] bf16, later C [D][D] fp32
   float *C = reinterpret_cast<float *>(pca_lds);
-  __shared__ float mu[D], wbuf[2][D], nrm_part[2][8];
-  __shared__ uint32_t hist[256];
+  __shared__ __align__(16) float mu[D];
+  __shared__ __align__(16) float wbuf[2][D];
+  __shared__ __align__(16) float nrm_part[2][8];
+  __shared__ __align__(16) uint32_t hist[256];
+  __shared__ int sidx[PCA_SMAX];
   __shared__ float far_n[8];
   __shared__ int far_j[8];
   __shared__ int2 scan_sh[8];
   __shared__ uint32_t sh_prefix, sh_rank;
 
-  // 1. strided subsample, dimension-major; columns beyond s are zero
+  // 1. strided subsample, dimension-major; columns beyond s are zero.  The
+  // tokens first (one 64-bit division each), then the rows: a lane gathers
+  // one 16-byte chunk of 8 consecutive subsample points (8 loads in flight)
+  // and writes it transposed as 8 rows of 8 columns; the lanes of a wave
+  // cover 8 chunks x 8 point groups, so that a 16-lane pass of a store spans
+  // two chunks of 8 groups and touches every LDS bank once
   const int s = min(n, PCA_SMAX);
   const int spad = (s + 15) & ~15;
-  for (int q = tid; q < spad * (D / 8); q += NT) {
-    const int j = q / (D / 8), c = q % (D / 8);
-    uint16_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (j < s) {
-      const int t = perm[(int)(((int64_t)j * n) / s)];
-      *(u32x4_t *)v = *(const u32x4_t *)(X + (int64_t)t * D + c * 8);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) Y[(c * 8 + e) * sp + j] = v[e];
-  }
+  for (int j = tid; j < s; j += NT) sidx[j] = perm[(int)(((int64_t)j * n) / s)];
   __syncthreads();
-  // mean of each dimension (four threads per dimension, fixed order)
   {
-    const int i = tid >> 2, part = tid & 3;
-    float acc = 0.f;
-    if (i < D)
-      for (int j = part; j < s; j += 4) acc += bf2f(Y[i * sp + j]);
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
-    if (i < D && part == 0) mu[i] = acc / (float)s;
+    constexpr int CW = D / 64;  // chunk octets per point (16-byte chunks: D / 8)
+    const int ngrp = spad / 8;
+    const int nitem = ((ngrp + 7) / 8) * CW;
+    for (int it = wave; it < nitem; it += NT / 64) {
+      const int c = (it % CW) * 8 + (lane >> 3), jg = (it / CW) * 8 + (lane & 7);
+      if (jg < ngrp) {
+        u32x4_t v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int j = 8 * jg + k;
+          v[k] = (u32x4_t){0u, 0u, 0u, 0u};
+          if (j < s) v[k] = *(const u32x4_t *)(X + (int64_t)sidx[j] * D + c * 8);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int sh = 16 * (e & 1);
+          u32x4_t o;
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            o[m] = ((v[2 * m][e >> 1] >> sh) & 0xFFFFu) | (((v[2 * m + 1][e >> 1] >> sh) & 0xFFFFu) << 16);
+          *(u32x4_t *)&Y[(c * 8 + e) * sp + 8 * jg] = o;
+        }
+      }
+    }
   }
   __syncthreads();
-  for (int q = tid; q < D * s; q += NT) {
-    const int i = q / s, j = q % s;
-    Y[i * sp + j] = f2bf(bf2f(Y[i * sp + j]) - mu[i]);
+  // mean of each dimension and centring of its s columns (the zero columns
+  // stay zero): one wave per dimension, groups of four columns a lane (spad
+  // is a multiple of 16, so a group never crosses it)
+  {
+    constexpr int GPL = PCA_SMAX / 256;  // column groups a lane
+    for (int i = wave; i < D; i += NT / 64) {
+      uint2 g[GPL];
+      float part = 0.f;
+#pragma unroll
+      for (int r = 0; r < GPL; ++r) {
+        const int j0 = 256 * r + 4 * lane;
+        g[r] = j0 < s ? *(const uint2 *)&Y[i * sp + j0] : make_uint2(0u, 0u);
+        part += (bf2f((uint16_t)(g[r].x & 0xFFFFu)) + bf2f((uint16_t)(g[r].x >> 16))) +
+                (bf2f((uint16_t)(g[r].y & 0xFFFFu)) + bf2f((uint16_t)(g[r].y >> 16)));
+      }
+      part = row16_sum(part);
+      const float m = ((lane_f32(part, 0) + lane_f32(part, 16)) + (lane_f32(part, 32) + lane_f32(part, 48))) / (float)s;
+#pragma unroll
+      for (int r = 0; r < GPL; ++r) {
+        const int j0 = 256 * r + 4 * lane;
+        if (j0 < s) {
+          uint32_t e[4] = {g[r].x & 0xFFFFu, g[r].x >> 16, g[r].y & 0xFFFFu, g[r].y >> 16};
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (j0 + k < s) e[k] = f2bf(bf2f((uint16_t)e[k]) - m);
+          *(uint2 *)&Y[i * sp + j0] = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+        }
+      }
+    }
   }
   __syncthreads();
   // start of the power iteration: the subsample row farthest from the mean
@@ -157,9 +217,12 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
         if (on > bn || (on == bn && oj < bjj)) { bn = on; bjj = oj; }
       }
       // unnormalised start; the first iteration normalises (its norm is set here)
-      for (int i = lane; i < D; i += 64) wbuf[0][i] = bf2f(Y[i * sp + bjj]);
       float sq = 0.f;
-      for (int i = lane; i < D; i += 64) sq = fmaf(wbuf[0][i], wbuf[0][i], sq);
+      for (int i = lane; i < D; i += 64) {
+        const float y = bf2f(Y[i * sp + bjj]);
+        wbuf[0][i] = y;
+        sq = fmaf(y, y, sq);
+      }
       sq = wave_sum(sq);
       if (lane < 8) nrm_part[0][lane] = lane == 0 ? sq : 0.f;
     }
@@ -197,27 +260,54 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
   }
   __syncthreads();
 
-  // 3. power iteration (the start vector and its norm are in wbuf[0], nrm_part[0])
-  // w = C v: wave w owns outputs [D/8 * w, +D/8); lane (output o, part p)
-  constexpr int OPW = D / 8;           // outputs per wave
-  constexpr int PARTS = 64 / OPW;      // lanes per output
-  constexpr int KPP = D / PARTS;       // inputs per lane
-  const int oi = wave * OPW + lane % OPW, part = lane / OPW;
+  // 3. power iteration (the start vector and its norm are in wbuf[0], nrm_part[0]).
+  // w = C v, normalised by the previous iterate's norm.  Wave w owns outputs
+  // [D/8 w, D/8 (w + 1)); row r (16 lanes) of the wave owns NA = D/32 of
+  // them, and lane l of the row the inputs 64 m + 4 l + t (m < D/64, t < 4),
+  // with those C entries in registers.  A step reads the iterate in D/64
+  // 16-byte loads a lane (one contiguous 256-byte span a row, the same for
+  // the four rows), sums over the row with DPP moves and over the rows with
+  // lane reads, and writes NA outputs and the wave's squared norm.
+  constexpr int NA = D / 32, NM = D / 64;
+  const int row = lane >> 4, l16 = lane & 15;
+  const int o0 = wave * (D / 8) + row * NA;
+  float cv[NM][4][NA];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int a2 = 0; a2 < NA; ++a2) cv[m][t][a2] = C[(64 * m + 4 * l16 + t) * D + o0 + a2];
   for (int it = 0; it < PCA_ITERS; ++it) {
     const int cur = it & 1, nxt = cur ^ 1;
-    float nrm2 = 0.f;
+    const float4 n0 = *(const float4 *)&nrm_part[cur][0], n1 = *(const float4 *)&nrm_part[cur][4];
+    const float nrm2 = ((n0.x + n0.y) + (n0.z + n0.w)) + ((n1.x + n1.y) + (n1.z + n1.w));
+    const float inv = nrm2 > 0.f ? rsqrtf(nrm2) : 0.f;  // only the direction matters
+    float acc[NA];
 #pragma unroll
-    for (int w = 0; w < 8; ++w) nrm2 += nrm_part[cur][w];
-    const float inv = nrm2 > 0.f ? 1.f / sqrtf(nrm2) : 0.f;
-    float acc1 = 0.f;
-    for (int k = part * KPP; k < (part + 1) * KPP; ++k) acc1 = fmaf(C[k * D + oi], wbuf[cur][k], acc1);
+    for (int a2 = 0; a2 < NA; ++a2) acc[a2] = 0.f;
 #pragma unroll
-    for (int o = OPW; o < 64; o <<= 1) acc1 += __shfl_xor(acc1, o, 64);
-    const float w = acc1 * inv;
-    float sq = lane < OPW ? w * w : 0.f;
-    sq = wave_sum(sq);
-    if (lane < OPW) wbuf[nxt][oi] = w;
-    if (lane == 0) nrm_part[nxt][wave] = sq;
+    for (int m = 0; m < NM; ++m) {
+      const float4 x = *(const float4 *)&wbuf[cur][64 * m + 4 * l16];
+#pragma unroll
+      for (int a2 = 0; a2 < NA; ++a2) {
+        acc[a2] = fmaf(cv[m][0][a2], x.x, acc[a2]);
+        acc[a2] = fmaf(cv[m][1][a2], x.y, acc[a2]);
+        acc[a2] = fmaf(cv[m][2][a2], x.z, acc[a2]);
+        acc[a2] = fmaf(cv[m][3][a2], x.w, acc[a2]);
+      }
+    }
+    float sq = 0.f;
+#pragma unroll
+    for (int a2 = 0; a2 < NA; ++a2) {
+      acc[a2] = row16_sum(acc[a2]) * inv;
+      sq = fmaf(acc[a2], acc[a2], sq);
+    }
+    const float tot = (lane_f32(sq, 0) + lane_f32(sq, 16)) + (lane_f32(sq, 32) + lane_f32(sq, 48));
+    if (l16 == 0)
+#pragma unroll
+      for (int a2 = 0; a2 < NA; ++a2) wbuf[nxt][o0 + a2] = acc[a2];
+    if (lane == 0) nrm_part[nxt][wave] = tot;
     __syncthreads();
   }
   // normalise and orient: the component of largest magnitude is positive
@@ -248,26 +338,27 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
   }
   __syncthreads();
 
-  // 4. projections of every point, 16 lanes per point, four points in flight
+  // 4. projections of every point, 16 lanes per point, PJ points in flight
   {
     constexpr int PL = D / 16;
+    constexpr int PJ = 8;
     typedef uint32_t pw_t __attribute__((ext_vector_type(PL / 2)));
     const int grp = tid >> 4, sub = tid & 15;
     float vv[PL];
 #pragma unroll
     for (int k = 0; k < PL; ++k) vv[k] = mu[sub * PL + k];
-    for (int p0 = grp; p0 < n; p0 += 4 * (NT / 16)) {
-      int t[4];
-      pw_t xw[4];
+    for (int p0 = grp; p0 < n; p0 += PJ * (NT / 16)) {
+      int t[PJ];
+      pw_t xw[PJ];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < PJ; ++j) {
         const int p = p0 + j * (NT / 16);
         t[j] = p < n ? perm[p] : 0;
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xw[j] = *(const pw_t *)(X + (int64_t)t[j] * D + sub * PL);
+      for (int j = 0; j < PJ; ++j) xw[j] = *(const pw_t *)(X + (int64_t)t[j] * D + sub * PL);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < PJ; ++j) {
         float acc2 = 0.f;
 #pragma unroll
         for (int k = 0; k < PL; ++k) {
@@ -300,15 +391,37 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
       if ((kv & hmask) == prefix) atomicAdd(&hist[(kv >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      uint32_t rk = sh_rank, run = 0;
-      int bin = 255;
-      for (int bb = 0; bb < 256; ++bb) {
-        if (run + hist[bb] >= rk) { bin = bb; break; }
-        run += hist[bb];
+    // the first bin whose running count reaches the rank: lane l holds bins
+    // 4l .. 4l+3, an inclusive scan over lanes finds the lane, the lane its bin
+    if (wave == 0) {
+      const uint4 hv = *(const uint4 *)&hist[4 * lane];
+      const uint32_t cnt = (hv.x + hv.y) + (hv.z + hv.w);
+      uint32_t inc = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += t;
       }
-      sh_prefix = prefix | ((uint32_t)bin << shift);
-      sh_rank = rk - run;
+      const uint32_t rk = sh_rank;
+      const uint64_t hit = __ballot(inc >= rk);
+      // the prefix's keys number at least rk, so some lane hits; were none to,
+      // the last bin is taken with every key counted, as a serial scan would
+      const int f = hit ? __ffsll((long long)hit) - 1 : 63;
+      if (lane == f) {
+        const uint32_t hh[4] = {hv.x, hv.y, hv.z, hv.w};
+        uint32_t run = inc - cnt;
+        int bin = 255;
+        if (hit) {
+          for (int bb = 0; bb < 4; ++bb) {
+            if (run + hh[bb] >= rk) { bin = 4 * lane + bb; break; }
+            run += hh[bb];
+          }
+        } else {
+          run = inc;
+        }
+        sh_prefix = prefix | ((uint32_t)bin << shift);
+        sh_rank = rk - run;
+      }
     }
     __syncthreads();
   }

@@ -39,9 +39,10 @@
  *           except: a cold ac_cluster_k / cold ac_layer waits on the stream once per stage of
  *           Algorithm 1 (it reads the size of the unassigned set), and ac_layer waits at its end when
  *           host_stats is not NULL.  Calls on different streams with different buffers are independent.
- *           ac_cluster_q and ac_cluster_k use disjoint parts of the workspace, so the two may run at
- *           the same time on two streams that share one workspace (every other pair of calls that
- *           share a workspace must be ordered).  ac_layer does so itself: it runs the query
+ *           The query clusterings (ac_cluster_q, ac_cluster_q_pca) and the key clusterings
+ *           (ac_cluster_k, ac_cluster_k_pca) use disjoint parts of the workspace, so a query and a key
+ *           clustering may run at the same time on two streams that share one workspace (every other
+ *           pair of calls that share a workspace must be ordered).  ac_layer does so itself: it runs the query
  *           clustering on a second stream of its own (created on first use, one per device and host
  *           thread, default priority, kept until the process ends) and joins it before returning
  *           control of `stream` to the caller's later work.

@@ -190,6 +190,51 @@ def test_pca_split_full_length(name):
     print(f"\n[{name}] PCA split near ties {ties}; attention worst max-abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}")
 
 
+def test_pca_query_and_key_sides_overlap():
+    """The query split and the key split have workspace scratch of their own:
+    run on two streams over one workspace, in either order of enqueueing,
+    every output equals that of the two calls one after the other, bit for
+    bit."""
+    import torch
+    import clustered_sparse_attention_amd as ac
+    w = gen.get_workload("wan", H=2)
+    Q, K, V = gen.generate(w)
+    bq, bk = 256, 64
+    L = w.L
+    p = oracle_params(nq=-(-L // bq), m0=200, nmax=-(-L // bk) + 1, sel_mode=nm.SEL_DENSITY, sel_param=0.15)
+    r = Run(Q, K, V, p)
+
+    def outputs():
+        q, k, st = r.q, r.k, r.st
+        return [t.clone() for t in (q.labels, q.perm, q.seg, q.cent, q.ncl, q.rho, k.labels, k.perm, k.seg, k.cent,
+                                    k.ncl, st.kmax, st.kmin, st.kmean, st.vmean, st.mse, st.stages)]
+
+    def clear():
+        for t in (r.q.labels, r.q.perm, r.q.seg, r.q.ncl, r.k.labels, r.k.perm, r.k.seg, r.k.ncl):
+            t.fill_(-7)
+        for t in (r.q.cent, r.q.rho, r.k.cent, r.st.kmean, r.st.vmean, r.st.mse):
+            t.fill_(-7.0)
+
+    main = torch.cuda.current_stream()
+    ac.ac_cluster_q_pca(r.shape, r.cp, r.Q, bq, r.q, r.ws)
+    ac.ac_cluster_k_pca(r.shape, r.cp, r.K, r.V, bk, r.k, r.st, r.ws)
+    torch.cuda.synchronize()
+    ref = outputs()
+    side = torch.cuda.Stream()  # default priority
+    for query_first in (True, False):
+        clear()
+        torch.cuda.synchronize()
+        side.wait_stream(main)
+        calls = [lambda: ac.ac_cluster_q_pca(r.shape, r.cp, r.Q, bq, r.q, r.ws, stream=side.cuda_stream),
+                 lambda: ac.ac_cluster_k_pca(r.shape, r.cp, r.K, r.V, bk, r.k, r.st, r.ws)]
+        for c in (calls if query_first else calls[::-1]):
+            c()
+        main.wait_stream(side)
+        torch.cuda.synchronize()
+        for i, (a_, b_) in enumerate(zip(ref, outputs())):
+            assert torch.equal(a_, b_), (query_first, i)
+
+
 @pytest.mark.parametrize("L,d,bk", [(1793, 128, 512), (4396, 64, 4096), (768, 128, 256)])
 def test_key_statistics_at_chunk_boundaries(L, d, bk):
     """The key statistics run in chunks of 256 members, one wave per chunk,
