@@ -10,9 +10,12 @@
 //   1. loads a strided subsample of s = min(n, PCA_SMAX) points into LDS,
 //      dimension-major, and centres it (bf16 of x - mean);
 //   2. forms the d x d covariance with 32x32x16 bf16 MFMA (fp32 sums);
-//   3. runs PCA_ITERS power iterations from the subsample row farthest from
-//      the mean and orients the result (largest component positive);
-//   4. projects every point of the node (fp32), radix-selects the n_left-th
+//   3. squares it PCA_SQUARINGS times on MFMA (split bf16, trace-normalised);
+//   4. runs the matching PCA_ITERS / 2^PCA_SQUARINGS power iterations from
+//      the subsample row farthest from the mean (the same direction as
+//      PCA_ITERS iterations with the covariance) and orients the result
+//      (largest component positive);
+//   5. projects every point of the node (fp32), radix-selects the n_left-th
 //      smallest (projection, position) key in four 8-bit passes, and writes
 //      the stable partition of the node's tokens.
 #include <algorithm>
@@ -25,6 +28,7 @@
 namespace ac {
 
 constexpr int PCA_SP = PCA_SMAX + 8;  // largest LDS row stride (bf16) of the dimension-major subsample
+constexpr int PCA_SQUARINGS = 3;      // the power iteration runs with C^8
 
 // Internal nodes of the split tree of n points, level by level, left to
 // right: nodes[k] = (first position, count); lvl[l] = first node of level l,
@@ -91,7 +95,9 @@ AC_DEV float row16_sum(float v) {
 AC_DEV float lane_f32(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
 
 // sp: row stride (bf16) of the subsample in LDS, sized by the launch to the
-// level's largest node (the dynamic LDS holds max(D sp bf16, D D fp32))
+// level's largest node (the dynamic LDS holds the larger of the subsample,
+// D sp bf16, and the split squares, 2 D (D + 8) bf16; the fp32 D x D matrix
+// fits in the latter)
 template <int D>
 __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int count, int sp) {
   constexpr int NT = 512;
@@ -118,6 +124,8 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
   __shared__ int far_j[8];
   __shared__ int2 scan_sh[8];
   __shared__ uint32_t sh_prefix, sh_rank;
+  __shared__ int sh_zero;  // 0, read where a value must not be hoisted out of a loop
+  if (tid == 0) sh_zero = 0;
 
   // 1. strided subsample, dimension-major; columns beyond s are zero.  The
   // tokens first (one 64-bit division each), then the rows: a lane gathers
@@ -248,20 +256,94 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
       }
     }
   }
-  __syncthreads();  // every read of Y is done before C overwrites it
+  // 3. A = C / tr(C), then PCA_SQUARINGS times A <- A A^T / tr(A A^T), so that
+  // A ends as C^(2^PCA_SQUARINGS) up to a positive factor; the power
+  // iteration then takes PCA_ITERS / 2^PCA_SQUARINGS steps with it, which in
+  // exact arithmetic is the same as PCA_ITERS steps with C.  The trace keeps
+  // the leading eigenvalue in [1/D, 1].  The products run on bf16 MFMA with A
+  // split into bf16 hi + lo (fp32 sums; the lo x lo term, below 2^-16 of an
+  // entry, is dropped).  LDS holds A_hi and A_lo row-major with rows of
+  // D + 8 bf16, so that the 16 rows of a 16-lane pass of the operand reads
+  // fall on distinct banks; the last A is written fp32 in the plain layout
+  // the power iteration reads.
+  constexpr int AP = D + 8;
+  uint16_t *Ahi = reinterpret_cast<uint16_t *>(pca_lds), *Alo = Ahi + D * AP;
+  auto aidx = [](int r, int c) { return r * AP + c; };
+#pragma unroll 1
+  for (int sq = 0; sq <= PCA_SQUARINGS; ++sq) {
+    if (sq > 0) {
 #pragma unroll
-  for (int k = 0; k < TPW; ++k) {
-    const int tile = wave + 8 * k;
-    if (tile < NTILE) {
-      const int I = tile / (D / 32), J = tile % (D / 32);
+      for (int k = 0; k < TPW; ++k) acc[k] = (f32x16_t){};
+#pragma unroll 1
+      for (int k0 = 0; k0 < D; k0 += 16) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) C[(I * 32 + 8 * (r / 4) + 4 * g + (r % 4)) * D + J * 32 + l32] = acc[k][r];
+        for (int k = 0; k < TPW; ++k) {
+          const int tile = wave + 8 * k;
+          if (tile < NTILE) {
+            const int I = tile / (D / 32), J = tile % (D / 32);
+            const int ia = aidx(I * 32 + l32, k0 + 8 * g), ib = aidx(J * 32 + l32, k0 + 8 * g);
+            const bf16x8_t ah = *(const bf16x8_t *)&Ahi[ia], al = *(const bf16x8_t *)&Alo[ia];
+            const bf16x8_t bh = *(const bf16x8_t *)&Ahi[ib], bl = *(const bf16x8_t *)&Alo[ib];
+            acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[k], 0, 0, 0);
+            acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[k], 0, 0, 0);
+            acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[k], 0, 0, 0);
+          }
+        }
+      }
     }
+    // the diagonal: in a tile with I == J, lane (l32, g) with g = bit 2 of
+    // l32 holds entry l32 in register 4 (l32 / 8) + l32 % 4
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int tile = wave + 8 * k;
+      if (tile < NTILE && tile / (D / 32) == tile % (D / 32) && g == ((l32 >> 2) & 1)) {
+        const int rr = 4 * (l32 >> 3) + (l32 & 3);
+        float dv = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (r == rr) dv = acc[k][r];
+        mu[(tile / (D / 32)) * 32 + l32] = dv;
+      }
+    }
+    __syncthreads();  // the diagonal is complete; every read of Y or of A is done
+    float tr = 0.f;
+#pragma unroll
+    for (int i = 0; i < D; i += 4) {
+      const float4 t4 = *(const float4 *)&mu[i];
+      tr += (t4.x + t4.y) + (t4.z + t4.w);
+    }
+    const float inv = tr > 0.f ? 1.f / tr : 0.f;
+    // entry r of a tile sits at a lane base plus a constant; the base goes
+    // through an LDS zero so that the 16 addresses are not kept in registers
+    // across the stages but folded into the stores' offsets
+    const int z = sh_zero;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int tile = wave + 8 * k;
+      if (tile < NTILE) {
+        const int I = tile / (D / 32), J = tile % (D / 32);
+        const int rb = I * 32 + 4 * g + z, cl = J * 32 + l32;
+        if (sq < PCA_SQUARINGS) {
+          uint16_t *ph = Ahi + aidx(rb, cl), *pl = Alo + aidx(rb, cl);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float v = acc[k][r] * inv;
+            const uint16_t hi = f2bf(v);
+            ph[(8 * (r / 4) + (r % 4)) * AP] = hi;
+            pl[(8 * (r / 4) + (r % 4)) * AP] = f2bf(v - bf2f(hi));
+          }
+        } else {
+          float *pc = C + rb * D + cl;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) pc[(8 * (r / 4) + (r % 4)) * D] = acc[k][r] * inv;
+        }
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
-  // 3. power iteration (the start vector and its norm are in wbuf[0], nrm_part[0]).
-  // w = C v, normalised by the previous iterate's norm.  Wave w owns outputs
+  // 4. power iteration (the start vector and its norm are in wbuf[0], nrm_part[0]).
+  // w = C v with C the last A, normalised by the previous iterate's norm.  Wave w owns outputs
   // [D/8 w, D/8 (w + 1)); row r (16 lanes) of the wave owns NA = D/32 of
   // them, and lane l of the row the inputs 64 m + 4 l + t (m < D/64, t < 4),
   // with those C entries in registers.  A step reads the iterate in D/64
@@ -278,7 +360,9 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int a2 = 0; a2 < NA; ++a2) cv[m][t][a2] = C[(64 * m + 4 * l16 + t) * D + o0 + a2];
-  for (int it = 0; it < PCA_ITERS; ++it) {
+  constexpr int NIT = PCA_ITERS >> PCA_SQUARINGS;
+  static_assert(NIT << PCA_SQUARINGS == PCA_ITERS, "the squarings must divide the power iterations");
+  for (int it = 0; it < NIT; ++it) {
     const int cur = it & 1, nxt = cur ^ 1;
     const float4 n0 = *(const float4 *)&nrm_part[cur][0], n1 = *(const float4 *)&nrm_part[cur][4];
     const float nrm2 = ((n0.x + n0.y) + (n0.z + n0.w)) + ((n1.x + n1.y) + (n1.z + n1.w));
@@ -314,11 +398,11 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
   if (wave == 0) {
     float nrm2 = 0.f;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) nrm2 += nrm_part[PCA_ITERS & 1][w];
+    for (int w = 0; w < 8; ++w) nrm2 += nrm_part[NIT & 1][w];
     float best = -1.f, sgn = 1.f;
     int bi = 0;
     for (int i = lane; i < D; i += 64) {
-      const float v = wbuf[PCA_ITERS & 1][i];
+      const float v = wbuf[NIT & 1][i];
       if (fabsf(v) > best) { best = fabsf(v); bi = i; sgn = v < 0.f ? -1.f : 1.f; }
     }
 #pragma unroll
@@ -331,14 +415,14 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
     const bool zero = !(nrm2 > 0.f);
     const float scale = zero ? 0.f : sgn / sqrtf(nrm2);
     for (int i = lane; i < D; i += 64) {
-      const float v = zero ? (i == 0 ? 1.f : 0.f) : wbuf[PCA_ITERS & 1][i] * scale;
+      const float v = zero ? (i == 0 ? 1.f : 0.f) : wbuf[NIT & 1][i] * scale;
       mu[i] = v;  // the direction (the mean is no longer needed)
       if (a.dir) a.dir[((int64_t)h * a.ndir + node) * D + i] = v;
     }
   }
   __syncthreads();
 
-  // 4. projections of every point, 16 lanes per point, PJ points in flight
+  // 5. projections of every point, 16 lanes per point, PJ points in flight
   {
     constexpr int PL = D / 16;
     constexpr int PJ = 8;
@@ -549,7 +633,7 @@ void launch_pca_split(int D, const PcaArgs &a, const std::vector<int> &counts, i
     // the deep levels (small nodes) fit two blocks a compute unit
     const int spad = (std::min(nmax, PCA_SMAX) + 15) & ~15;
     const int sp = spad + 8;
-    const size_t lds = std::max((size_t)D * sp * 2, (size_t)D * D * 4);
+    const size_t lds = std::max((size_t)D * sp * 2, (size_t)D * (D + 8) * 4);
     if (D == 64)
       hipLaunchKernelGGL(k_pca_level<64>, dim3((unsigned)counts[l], (unsigned)BH), dim3(512), lds, st, a, first,
                          counts[l], sp);

@@ -253,8 +253,9 @@ ac_status ac_cluster_q_trace(const ac_shape *s, const ac_params *p, const uint16
  * (L mod block when nonzero), clusters are numbered left to right, and each lists its tokens in
  * ascending order.  The direction of a node is the leading eigenvector of the covariance of a strided
  * subsample {floor(j n / s)} of s = min(n, 512) of its rows, centred and rounded to bf16 (the
- * approximation the page mentions), found by 64 power iterations from the subsample row farthest from the
- * mean and oriented so that its component of largest magnitude is positive.  block: a power of two in
+ * approximation the page mentions), found as the direction of 64 power iterations from the subsample row
+ * farthest from the mean (computed as 8 iterations with the covariance's eighth power) and oriented so
+ * that its component of largest magnitude is positive.  block: a power of two in
  * [16, 4096] with ceil(L / block) <= the cluster capacity (AC_E_ARG otherwise).
  *
  * ac_cluster_q_pca clusters the normalised queries (bf16(q / ||q||), as ac_cluster_q): q_out gets
