@@ -7,9 +7,10 @@
 // each side keeping its token order.  The tree's shape depends only on n and
 // b, so every level is one launch over the internal nodes of that level
 // (one workgroup per node and head).  A workgroup:
-//   1. loads a strided subsample of s = min(n, PCA_SMAX) points into LDS,
-//      dimension-major, and centres it (bf16 of x - mean);
-//   2. forms the d x d covariance with 32x32x16 bf16 MFMA (fp32 sums);
+//   1. takes a strided subsample of s = min(n, PCA_SMAX) points and its mean;
+//   2. forms the d x d covariance of the centred subsample (bf16 of x - mean)
+//      with 32x32x16 bf16 MFMA (fp32 sums), gathering PCA_CHUNK points into
+//      LDS at a time, and finds the point farthest from the mean;
 //   3. squares it PCA_SQUARINGS times on MFMA (split bf16, trace-normalised);
 //   4. runs the matching PCA_ITERS / 2^PCA_SQUARINGS power iterations from
 //      the subsample row farthest from the mean (the same direction as
@@ -27,8 +28,16 @@
 
 namespace ac {
 
-constexpr int PCA_SP = PCA_SMAX + 8;  // largest LDS row stride (bf16) of the dimension-major subsample
+constexpr int PCA_CHUNK = 256;         // subsample points in LDS at a time
+// dynamic LDS of a level: the larger of a chunk of the subsample (D x (chunk
+// width + 8) bf16) and the split squares (2 x D x (D + 8) bf16)
+constexpr int pca_lds_max(int D) {
+  return D * (PCA_CHUNK + 8) * 2 > D * (D + 8) * 4 ? D * (PCA_CHUNK + 8) * 2 : D * (D + 8) * 4;
+}
 constexpr int PCA_SQUARINGS = 3;      // the power iteration runs with C^8
+constexpr int PCA_PJ = 8;             // projection loads in flight per 16 lanes
+constexpr int PCA_PJ_BIG = 32;        // the same on levels whose largest node has PCA_BIG_NODE points or more
+constexpr int PCA_BIG_NODE = 16384;
 
 // Internal nodes of the split tree of n points, level by level, left to
 // right: nodes[k] = (first position, count); lvl[l] = first node of level l,
@@ -48,6 +57,73 @@ __global__ void k_pca_tree(int n, int b, int2 *__restrict__ nodes, int *__restri
     }
   }
   lvl[level] = tail;
+}
+
+// The same list built by one 1024-thread block, level by level: each level's
+// nodes sit in LDS (at most PCA_TREE_CAP), every thread takes a parent, and a
+// block scan of the internal-children counts places the children (left, then
+// right, parents in order), so the order is the one above.
+constexpr int PCA_TREE_CAP = 4096;
+__global__ __launch_bounds__(1024) void k_pca_tree_wide(int n, int b, int2 *__restrict__ nodes, int *__restrict__ lvl) {
+  __shared__ int2 buf[2][PCA_TREE_CAP];
+  __shared__ int wtot[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int cnt = n > b ? 1 : 0, base = 0, level = 0, cur = 0;
+  if (tid == 0 && cnt) {
+    buf[0][0] = make_int2(0, n);
+    nodes[0] = make_int2(0, n);
+  }
+  __syncthreads();
+  while (cnt > 0) {
+    if (tid == 0) lvl[level] = base;
+    int next = 0;
+    for (int c0 = 0; c0 < cnt; c0 += 1024) {
+      const int i = c0 + tid;
+      int2 nd = make_int2(0, 0);
+      int nl = 0, nr = 0, kids = 0;
+      if (i < cnt) {
+        nd = buf[cur][i];
+        const int nb = (nd.y + b - 1) / b;
+        nl = b * ((nb + 1) / 2);
+        nr = nd.y - nl;
+        kids = (nl > b) + (nr > b);
+      }
+      int inc = kids;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += t;
+      }
+      if (lane == 63) wtot[wave] = inc;
+      __syncthreads();
+      int off = 0, tot = 0;
+#pragma unroll
+      for (int w = 0; w < 16; ++w) {
+        const int t = wtot[w];
+        if (w < wave) off += t;
+        tot += t;
+      }
+      int o = next + off + inc - kids;
+      if (nl > b) {
+        const int2 c = make_int2(nd.x, nl);
+        buf[cur ^ 1][o] = c;
+        nodes[base + cnt + o] = c;
+        ++o;
+      }
+      if (nr > b) {
+        const int2 c = make_int2(nd.x + nl, nr);
+        buf[cur ^ 1][o] = c;
+        nodes[base + cnt + o] = c;
+      }
+      next += tot;
+      __syncthreads();
+    }
+    base += cnt;
+    cnt = next;
+    cur ^= 1;
+    ++level;
+  }
+  if (tid == 0) lvl[level] = base;
 }
 
 // Block-wide exclusive scan of two counters (512 threads = 8 waves); returns
@@ -98,7 +174,9 @@ AC_DEV float lane_f32(float v, int l) { return __int_as_float(__builtin_amdgcn_r
 // level's largest node (the dynamic LDS holds the larger of the subsample,
 // D sp bf16, and the split squares, 2 D (D + 8) bf16; the fp32 D x D matrix
 // fits in the latter)
-template <int D>
+// PJ: projection loads in flight per 16-lane group (more for the levels of
+// few, large nodes, where LDS already limits a compute unit to one block)
+template <int D, int PJ>
 __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int count, int sp) {
   constexpr int NT = 512;
   const int h = blockIdx.y, node = first + (int)blockIdx.x;
@@ -124,138 +202,164 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
   __shared__ int far_j[8];
   __shared__ int2 scan_sh[8];
   __shared__ uint32_t sh_prefix, sh_rank;
+  __shared__ float sh_best;  // squared distance of the start row from the mean
   __shared__ int sh_zero;  // 0, read where a value must not be hoisted out of a loop
   if (tid == 0) sh_zero = 0;
 
-  // 1. strided subsample, dimension-major; columns beyond s are zero.  The
-  // tokens first (one 64-bit division each), then the rows: a lane gathers
-  // one 16-byte chunk of 8 consecutive subsample points (8 loads in flight)
-  // and writes it transposed as 8 rows of 8 columns; the lanes of a wave
-  // cover 8 chunks x 8 point groups, so that a 16-lane pass of a store spans
-  // two chunks of 8 groups and touches every LDS bank once
+  // 1. the strided subsample's tokens (one 64-bit division each)
   const int s = min(n, PCA_SMAX);
-  const int spad = (s + 15) & ~15;
   for (int j = tid; j < s; j += NT) sidx[j] = perm[(int)(((int64_t)j * n) / s)];
+  if (tid == 0) sh_best = -1.f;
   __syncthreads();
+  // mean of each dimension over the subsample, from the rows in memory:
+  // thread (chunk c, point group pg) sums the 8 dimensions of chunk c over
+  // points pg, pg + PG, ... (8 loads in flight); the lanes of a wave with the
+  // same c, then the waves, are added in a fixed order
   {
-    constexpr int CW = D / 64;  // chunk octets per point (16-byte chunks: D / 8)
-    const int ngrp = spad / 8;
-    const int nitem = ((ngrp + 7) / 8) * CW;
-    for (int it = wave; it < nitem; it += NT / 64) {
-      const int c = (it % CW) * 8 + (lane >> 3), jg = (it / CW) * 8 + (lane & 7);
-      if (jg < ngrp) {
-        u32x4_t v[8];
+    constexpr int CPR = D / 8;    // 16-byte chunks per row
+    constexpr int PG = NT / CPR;  // point groups
+    const int c = tid % CPR, pg = tid / CPR;
+    float sum8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j0 = pg; j0 < s; j0 += 8 * PG) {
+      u32x4_t v[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int j = 8 * jg + k;
-          v[k] = (u32x4_t){0u, 0u, 0u, 0u};
-          if (j < s) v[k] = *(const u32x4_t *)(X + (int64_t)sidx[j] * D + c * 8);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int sh = 16 * (e & 1);
-          u32x4_t o;
-#pragma unroll
-          for (int m = 0; m < 4; ++m)
-            o[m] = ((v[2 * m][e >> 1] >> sh) & 0xFFFFu) | (((v[2 * m + 1][e >> 1] >> sh) & 0xFFFFu) << 16);
-          *(u32x4_t *)&Y[(c * 8 + e) * sp + 8 * jg] = o;
-        }
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u * PG;
+        v[u] = (u32x4_t){0u, 0u, 0u, 0u};
+        if (j < s) v[u] = *(const u32x4_t *)(X + (int64_t)sidx[j] * D + c * 8);
       }
-    }
-  }
-  __syncthreads();
-  // mean of each dimension and centring of its s columns (the zero columns
-  // stay zero): one wave per dimension, groups of four columns a lane (spad
-  // is a multiple of 16, so a group never crosses it)
-  {
-    constexpr int GPL = PCA_SMAX / 256;  // column groups a lane
-    for (int i = wave; i < D; i += NT / 64) {
-      uint2 g[GPL];
-      float part = 0.f;
 #pragma unroll
-      for (int r = 0; r < GPL; ++r) {
-        const int j0 = 256 * r + 4 * lane;
-        g[r] = j0 < s ? *(const uint2 *)&Y[i * sp + j0] : make_uint2(0u, 0u);
-        part += (bf2f((uint16_t)(g[r].x & 0xFFFFu)) + bf2f((uint16_t)(g[r].x >> 16))) +
-                (bf2f((uint16_t)(g[r].y & 0xFFFFu)) + bf2f((uint16_t)(g[r].y >> 16)));
-      }
-      part = row16_sum(part);
-      const float m = ((lane_f32(part, 0) + lane_f32(part, 16)) + (lane_f32(part, 32) + lane_f32(part, 48))) / (float)s;
+      for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int r = 0; r < GPL; ++r) {
-        const int j0 = 256 * r + 4 * lane;
-        if (j0 < s) {
-          uint32_t e[4] = {g[r].x & 0xFFFFu, g[r].x >> 16, g[r].y & 0xFFFFu, g[r].y >> 16};
+        for (int e = 0; e < 8; ++e) sum8[e] += bf2f((uint16_t)((e & 1) ? (v[u][e >> 1] >> 16) : (v[u][e >> 1] & 0xFFFFu)));
+    }
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-            if (j0 + k < s) e[k] = f2bf(bf2f((uint16_t)e[k]) - m);
-          *(uint2 *)&Y[i * sp + j0] = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
-        }
-      }
-    }
-  }
-  __syncthreads();
-  // start of the power iteration: the subsample row farthest from the mean
-  // (lowest position on ties), one thread per row
-  {
-    float nn = -1.f;
-    if (tid < s) {
-      nn = 0.f;
-      for (int i = 0; i < D; ++i) {
-        const float y = bf2f(Y[i * sp + tid]);
-        nn = fmaf(y, y, nn);
-      }
-    }
-    int bj = tid;
+    for (int o = CPR; o < 64; o <<= 1)
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float on = __shfl_xor(nn, o, 64);
-      const int oj = __shfl_xor(bj, o, 64);
-      if (on > nn || (on == nn && oj < bj)) { nn = on; bj = oj; }
-    }
-    if (lane == 0) { far_n[wave] = nn; far_j[wave] = bj; }
+      for (int e = 0; e < 8; ++e) sum8[e] += __shfl_xor(sum8[e], o, 64);
+    float *part = reinterpret_cast<float *>(pca_lds);  // [NT / 64][D], in the subsample's space
+    if (lane < CPR)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[wave * D + c * 8 + e] = sum8[e];
     __syncthreads();
-    if (wave == 0) {
-      float bn = lane < 8 ? far_n[lane] : -2.f;
-      int bjj = lane < 8 ? far_j[lane] : 0x7fffffff;
+    if (tid < D) {
+      float t = 0.f;
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float on = __shfl_xor(bn, o, 64);
-        const int oj = __shfl_xor(bjj, o, 64);
-        if (on > bn || (on == bn && oj < bjj)) { bn = on; bjj = oj; }
-      }
-      // unnormalised start; the first iteration normalises (its norm is set here)
-      float sq = 0.f;
-      for (int i = lane; i < D; i += 64) {
-        const float y = bf2f(Y[i * sp + bjj]);
-        wbuf[0][i] = y;
-        sq = fmaf(y, y, sq);
-      }
-      sq = wave_sum(sq);
-      if (lane < 8) nrm_part[0][lane] = lane == 0 ? sq : 0.f;
+      for (int w = 0; w < NT / 64; ++w) t += part[w * D + tid];
+      mu[tid] = t / (float)s;
     }
+    __syncthreads();
   }
 
-  // 2. covariance C = Y Y^T (unnormalised; only its direction matters), one
-  // 32x32 tile of C per wave and pass
+  // 2. covariance C = Y Y^T of the centred subsample Y (bf16 of x - mean;
+  // unnormalised, only its direction matters), over chunks of up to sp - 8
+  // points: a chunk is gathered centred into LDS, dimension-major (a lane
+  // takes one 16-byte chunk of 4 consecutive points and writes it as 8 rows
+  // of 4 columns; the 32 lanes of a store pass cover two chunks of 16 point
+  // groups, every bank once); its farthest point from the mean updates the
+  // start of the power iteration; then one 32x32 tile of C per wave and pass
+  // accumulates it on MFMA.
   constexpr int NTILE = (D / 32) * (D / 32);
   constexpr int TPW = (NTILE + 7) / 8;
   f32x16_t acc[TPW];
 #pragma unroll
   for (int k = 0; k < TPW; ++k) acc[k] = (f32x16_t){};
   const int l32 = lane & 31, g = lane >> 5;
-  for (int k0 = 0; k0 < spad; k0 += 16) {
+  const int chw = sp - 8;  // chunk width, a multiple of 16
+  for (int ch0 = 0; ch0 < s; ch0 += chw) {
+    const int cs = min(chw, s - ch0), cpad = (cs + 15) & ~15;
+    {
+      constexpr int CQ = D / 32;  // chunk quads per point (16-byte chunks: D / 8)
+      const int ngrp = cpad / 4;  // groups of 4 points
+      const int nitem = ((ngrp + 15) / 16) * CQ;
+      for (int it = wave; it < nitem; it += NT / 64) {
+        const int c = (it % CQ) * 4 + (lane >> 4), jq = (it / CQ) * 16 + (lane & 15);
+        if (jq < ngrp) {
+          u32x4_t v[4];
 #pragma unroll
-    for (int k = 0; k < TPW; ++k) {
-      const int tile = wave + 8 * k;
-      if (tile < NTILE) {
-        const int I = tile / (D / 32), J = tile % (D / 32);
-        const bf16x8_t av = *(const bf16x8_t *)&Y[(I * 32 + l32) * sp + k0 + 8 * g];
-        const bf16x8_t bv = *(const bf16x8_t *)&Y[(J * 32 + l32) * sp + k0 + 8 * g];
-        acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[k], 0, 0, 0);
+          for (int k = 0; k < 4; ++k) {
+            const int j = 4 * jq + k;
+            v[k] = (u32x4_t){0u, 0u, 0u, 0u};
+            if (j < cs) v[k] = *(const u32x4_t *)(X + (int64_t)sidx[ch0 + j] * D + c * 8);
+          }
+          const float4 m0 = *(const float4 *)&mu[c * 8], m1 = *(const float4 *)&mu[c * 8 + 4];
+          const float m8[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int sh = 16 * (e & 1);
+            uint32_t y[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const uint16_t xb = (uint16_t)((v[k][e >> 1] >> sh) & 0xFFFFu);
+              y[k] = 4 * jq + k < cs ? f2bf(bf2f(xb) - m8[e]) : 0u;  // the padding columns stay zero
+            }
+            *(uint2 *)&Y[(c * 8 + e) * sp + 4 * jq] = make_uint2(y[0] | (y[1] << 16), y[2] | (y[3] << 16));
+          }
+        }
       }
     }
+    __syncthreads();
+    // the chunk's point farthest from the mean (two threads a point, lowest
+    // position on ties); a strictly farther one than the earlier chunks'
+    // becomes the start (unnormalised; the first iteration normalises)
+    {
+      const int j = tid >> 1, half = tid & 1;
+      float nn = -1.f;
+      if (j < cs) {
+        nn = 0.f;
+#pragma unroll 8
+        for (int i = half * (D / 2); i < (half + 1) * (D / 2); ++i) {
+          const float y = bf2f(Y[i * sp + j]);
+          nn = fmaf(y, y, nn);
+        }
+      }
+      nn += dpp_f32<0xB1>(nn);  // the point's other half
+      int bj = ch0 + j;
+#pragma unroll
+      for (int o = 32; o > 1; o >>= 1) {
+        const float on = __shfl_xor(nn, o, 64);
+        const int oj = __shfl_xor(bj, o, 64);
+        if (on > nn || (on == nn && oj < bj)) { nn = on; bj = oj; }
+      }
+      if (lane == 0) { far_n[wave] = nn; far_j[wave] = bj; }
+      __syncthreads();
+      if (wave == 0) {
+        float bn = lane < 8 ? far_n[lane] : -2.f;
+        int bjj = lane < 8 ? far_j[lane] : 0x7fffffff;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          const float on = __shfl_xor(bn, o, 64);
+          const int oj = __shfl_xor(bjj, o, 64);
+          if (on > bn || (on == bn && oj < bjj)) { bn = on; bjj = oj; }
+        }
+        if (bn > sh_best) {
+          float sq = 0.f;
+          for (int i = lane; i < D; i += 64) {
+            const float y = bf2f(Y[i * sp + (bjj - ch0)]);
+            wbuf[0][i] = y;
+            sq = fmaf(y, y, sq);
+          }
+          sq = wave_sum(sq);
+          if (lane < 8) nrm_part[0][lane] = lane == 0 ? sq : 0.f;
+          if (lane == 0) sh_best = bn;
+        }
+      }
+    }
+    for (int k0 = 0; k0 < cpad; k0 += 16) {
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) {
+        const int tile = wave + 8 * k;
+        if (tile < NTILE) {
+          const int I = tile / (D / 32), J = tile % (D / 32);
+          const bf16x8_t av = *(const bf16x8_t *)&Y[(I * 32 + l32) * sp + k0 + 8 * g];
+          const bf16x8_t bv = *(const bf16x8_t *)&Y[(J * 32 + l32) * sp + k0 + 8 * g];
+          acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[k], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();  // every read of the chunk is done before the next one (or A) overwrites it
   }
+
   // 3. A = C / tr(C), then PCA_SQUARINGS times A <- A A^T / tr(A A^T), so that
   // A ends as C^(2^PCA_SQUARINGS) up to a positive factor; the power
   // iteration then takes PCA_ITERS / 2^PCA_SQUARINGS steps with it, which in
@@ -425,7 +529,6 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
   // 5. projections of every point, 16 lanes per point, PJ points in flight
   {
     constexpr int PL = D / 16;
-    constexpr int PJ = 8;
     typedef uint32_t pw_t __attribute__((ext_vector_type(PL / 2)));
     const int grp = tid >> 4, sub = tid & 15;
     float vv[PL];
@@ -449,10 +552,7 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
           const uint32_t w = xw[j][k >> 1];
           acc2 = fmaf(bf2f((uint16_t)((k & 1) ? (w >> 16) : (w & 0xFFFFu))), vv[k], acc2);
         }
-        acc2 += __shfl_xor(acc2, 1, 64);
-        acc2 += __shfl_xor(acc2, 2, 64);
-        acc2 += __shfl_xor(acc2, 4, 64);
-        acc2 += __shfl_xor(acc2, 8, 64);
+        acc2 = row16_sum(acc2);  // the 16 lanes of the point
         const int p = p0 + j * (NT / 16);
         if (sub == 0 && p < n) {
           key[p] = f2ord(acc2 + 0.f);  // -0 and +0 order alike
@@ -470,9 +570,13 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
     __syncthreads();
     const uint32_t prefix = sh_prefix;
     const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    for (int p = tid; p < n; p += NT) {
-      const uint32_t kv = key[p];
-      if ((kv & hmask) == prefix) atomicAdd(&hist[(kv >> shift) & 255u], 1u);
+    for (int p0 = tid; p0 < n; p0 += 8 * NT) {  // 8 loads in flight
+      uint32_t kv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) kv[u] = p0 + u * NT < n ? key[p0 + u * NT] : 0u;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (p0 + u * NT < n && (kv[u] & hmask) == prefix) atomicAdd(&hist[(kv[u] >> shift) & 255u], 1u);
     }
     __syncthreads();
     // the first bin whose running count reaches the rank: lane l holds bins
@@ -512,25 +616,42 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
   const uint32_t thr = sh_prefix;       // the nl-th smallest key
   const int eq_left = (int)sh_rank;     // keys equal to thr that still go left, in position order
 
-  // stable partition: left = key < thr, or key == thr among the first eq_left such positions
+  // stable partition: left = key < thr, or key == thr among the first eq_left
+  // such positions.  A round takes 4 NT positions, 4 consecutive a thread.
   int base_left = 0, base_eq = 0;
-  for (int c0 = 0; c0 < n; c0 += NT) {
-    const int p = c0 + tid;
-    const uint32_t kv = p < n ? key[p] : 0xFFFFFFFFu;
-    const bool valid = p < n;
-    const int lt = valid && kv < thr, eq = valid && kv == thr;
-    int2 tot;
-    const int2 pre = block_scan2(lt, eq, scan_sh, tot);
-    const bool left = lt || (eq && base_eq + pre.y < eq_left);
-    // left positions so far: strict ones plus the equal ones admitted
-    const int eq_admit_before = min(max(eq_left - base_eq, 0), pre.y);
-    const int left_before = base_left + pre.x + eq_admit_before;
-    if (valid) {
-      const int dst = left ? left_before : nl + (p - left_before);
-      perm[dst] = tmp[p];
+  for (int c0 = 0; c0 < n; c0 += 4 * NT) {
+    const int p0 = c0 + 4 * tid;
+    uint32_t kv[4];
+    int tv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      kv[u] = p0 + u < n ? key[p0 + u] : 0u;
+      tv[u] = p0 + u < n ? tmp[p0 + u] : 0;
     }
-    const int eq_admit_chunk = min(max(eq_left - base_eq, 0), tot.y);
-    base_left += tot.x + eq_admit_chunk;
+    int nlt = 0, neq = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (p0 + u < n) {
+        nlt += kv[u] < thr;
+        neq += kv[u] == thr;
+      }
+    int2 tot;
+    const int2 pre = block_scan2(nlt, neq, scan_sh, tot);
+    const int room = max(eq_left - base_eq, 0);  // equal keys still admitted left
+    int lt_run = pre.x, eq_run = pre.y;          // of this round, before the position
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = p0 + u;
+      if (p < n) {
+        const bool lt = kv[u] < thr, eq = kv[u] == thr;
+        const bool left = lt || (eq && eq_run < room);
+        const int left_before = base_left + lt_run + min(room, eq_run);
+        perm[left ? left_before : nl + (p - left_before)] = tv[u];
+        lt_run += lt;
+        eq_run += eq;
+      }
+    }
+    base_left += tot.x + min(room, tot.y);
     base_eq += tot.y;
   }
 }
@@ -617,29 +738,48 @@ std::vector<int> pca_level_counts(int n, int b) {
 
 void launch_pca_split(int D, const PcaArgs &a, const std::vector<int> &counts, int BH, int *perm_trace,
                       hipStream_t st) {
-  hipLaunchKernelGGL(k_pca_tree, dim3(1), dim3(1), 0, st, a.L, a.block, a.nodes, a.lvl);
+  const int widest = counts.empty() ? 0 : *std::max_element(counts.begin(), counts.end());
+  if (widest <= PCA_TREE_CAP)
+    hipLaunchKernelGGL(k_pca_tree_wide, dim3(1), dim3(1024), 0, st, a.L, a.block, a.nodes, a.lvl);
+  else
+    hipLaunchKernelGGL(k_pca_tree, dim3(1), dim3(1), 0, st, a.L, a.block, a.nodes, a.lvl);
   hipLaunchKernelGGL(k_iota_perm, dim3((unsigned)((a.L + 255) / 256), (unsigned)BH), dim3(256), 0, st, a.perm, a.L);
   // dynamic LDS above the default limit (a refusal shows up as a launch error)
-  static bool lds64 = hipFuncSetAttribute((const void *)k_pca_level<64>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                          64 * PCA_SP * 2) == hipSuccess;
-  static bool lds128 = hipFuncSetAttribute((const void *)k_pca_level<128>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 128 * PCA_SP * 2) == hipSuccess;
-  (void)lds64;
-  (void)lds128;
+  static bool lds_set = [] {
+    bool ok = true;
+    ok &= hipFuncSetAttribute((const void *)k_pca_level<64, PCA_PJ>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              pca_lds_max(64)) == hipSuccess;
+    ok &= hipFuncSetAttribute((const void *)k_pca_level<64, PCA_PJ_BIG>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, pca_lds_max(64)) == hipSuccess;
+    ok &= hipFuncSetAttribute((const void *)k_pca_level<128, PCA_PJ>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              pca_lds_max(128)) == hipSuccess;
+    ok &= hipFuncSetAttribute((const void *)k_pca_level<128, PCA_PJ_BIG>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, pca_lds_max(128)) == hipSuccess;
+    return ok;
+  }();
+  (void)lds_set;
   int first = 0;
   int nmax = a.L;  // largest node of the level: the left child is never the smaller one
   for (size_t l = 0; l < counts.size(); ++l) {
-    // the subsample of the level's largest node sets the LDS row stride, so that
-    // the deep levels (small nodes) fit two blocks a compute unit
-    const int spad = (std::min(nmax, PCA_SMAX) + 15) & ~15;
+    // a chunk of the subsample (at most PCA_CHUNK points) sets the LDS row
+    // stride; with the split squares the largest need is 69.6 KB at d = 128,
+    // so every level fits two blocks a compute unit
+    const int spad = (std::min(std::min(nmax, PCA_SMAX), PCA_CHUNK) + 15) & ~15;
     const int sp = spad + 8;
     const size_t lds = std::max((size_t)D * sp * 2, (size_t)D * (D + 8) * 4);
-    if (D == 64)
-      hipLaunchKernelGGL(k_pca_level<64>, dim3((unsigned)counts[l], (unsigned)BH), dim3(512), lds, st, a, first,
-                         counts[l], sp);
-    else
-      hipLaunchKernelGGL(k_pca_level<128>, dim3((unsigned)counts[l], (unsigned)BH), dim3(512), lds, st, a, first,
-                         counts[l], sp);
+    const dim3 grid((unsigned)counts[l], (unsigned)BH);
+    const bool big = nmax >= PCA_BIG_NODE;
+    if (D == 64) {
+      if (big)
+        hipLaunchKernelGGL((k_pca_level<64, PCA_PJ_BIG>), grid, dim3(512), lds, st, a, first, counts[l], sp);
+      else
+        hipLaunchKernelGGL((k_pca_level<64, PCA_PJ>), grid, dim3(512), lds, st, a, first, counts[l], sp);
+    } else {
+      if (big)
+        hipLaunchKernelGGL((k_pca_level<128, PCA_PJ_BIG>), grid, dim3(512), lds, st, a, first, counts[l], sp);
+      else
+        hipLaunchKernelGGL((k_pca_level<128, PCA_PJ>), grid, dim3(512), lds, st, a, first, counts[l], sp);
+    }
     const int nb = (nmax + a.block - 1) / a.block;
     nmax = a.block * ((nb + 1) / 2);
     if (perm_trace)
