@@ -15,6 +15,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -364,6 +365,7 @@ def summarize(args):
     --summarize stats <kernel_stats.csv> <out.md> <command...>
     --summarize traffic <fetch.csv> <write.csv> <copy_fetch.csv> <copy_write.csv> <copy_bytes>
                         <dispatches_per_call> <out.json> <command...>
+    --summarize pca <kernel_trace.csv> <out.md> <title> <command...>
     """
     import csv
     kind, rest = args[0], args[1:]
@@ -607,6 +609,51 @@ def summarize(args):
                          f"{r['mfma_hbm_gbs']} | {r['mfma_hbm_frac']} | {r['quest_valu_ms']} ({tv:.3f}) | "
                          f"{r['valu_tops']} | {r['valu_alu_frac']} | {r['speedup']}x | {r['fill_gbs']} |")
         open(out, "w").write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return
+    if kind == "pca":
+        # the principal-component split of the last layer step in a kernel trace of
+        # `bench.py --pca-split qb,kb`: per side (its own queue) the split tree,
+        # every level's launch and the finishing kernels, and the span of both
+        src, out, title, cmd = rest[0], rest[1], rest[2], " ".join(rest[3:])
+        rows = list(csv.DictReader(open(src)))
+        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+        sides = []
+        for q in sorted({r["Queue_Id"] for r in rows}):
+            qr = [r for r in rows if r["Queue_Id"] == q]
+            trees = [i for i, r in enumerate(qr) if "k_pca_tree" in r["Kernel_Name"]]
+            if not trees:
+                continue
+            t = trees[-1]
+            b = t - 1 if t > 0 and "k_qnorm" in qr[t - 1]["Kernel_Name"] else t
+            e = t
+            while e + 1 < len(qr) and not re.search(r"k_score_prep|k_pca_tree|k_qnorm", qr[e + 1]["Kernel_Name"]):
+                e += 1
+            seq = qr[b:e + 1]
+            key = any("k_kstats" in r["Kernel_Name"] for r in seq)
+            sides.append(("keys" if key else "queries", seq))
+        if not sides:
+            raise SystemExit("no principal-component split in the trace")
+        t0 = min(int(seq[0]["Start_Timestamp"]) for _, seq in sides)
+        t1 = max(int(seq[-1]["End_Timestamp"]) for _, seq in sides)
+        lines = [f"# Principal-component split, {title}", "", f"Command: `{cmd}`", "",
+                 "The last layer step of the trace; each side runs on its own queue (the two overlap). "
+                 f"Both sides together: {(t1 - t0) / 1e6:.3f} ms from the first launch to the last end.", ""]
+        for name, seq in sorted(sides):
+            span = (int(seq[-1]["End_Timestamp"]) - int(seq[0]["Start_Timestamp"])) / 1e6
+            lines += [f"## {name}: {span:.3f} ms", "", "| kernel | level | time | start |", "|---|---:|---:|---:|"]
+            lvl = 0
+            for r in seq:
+                kn = r["Kernel_Name"].replace("void ", "").split("(")[0]
+                d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                st = (int(r["Start_Timestamp"]) - t0) / 1e3
+                lv = ""
+                if "k_pca_level" in kn:
+                    lv = str(lvl)
+                    lvl += 1
+                lines.append(f"| {kn} | {lv} | {d:.1f} us | {st:.1f} us |")
+            lines.append("")
+        open(out, "w").write("\n".join(lines))
         print("\n".join(lines))
         return
     raise SystemExit(f"unknown summary kind {kind}")
