@@ -642,16 +642,20 @@ def summarize(args):
         for name, seq in sorted(sides):
             span = (int(seq[-1]["End_Timestamp"]) - int(seq[0]["Start_Timestamp"])) / 1e6
             lines += [f"## {name}: {span:.3f} ms", "", "| kernel | level | time | start |", "|---|---:|---:|---:|"]
-            lvl = 0
+            # a level of large nodes is three launches: its directions
+            # (k_pca_level), the projections (k_pca_project), its cuts (k_pca_level)
+            lvl, prev = -1, ""
             for r in seq:
                 kn = r["Kernel_Name"].replace("void ", "").split("(")[0]
                 d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
                 st = (int(r["Start_Timestamp"]) - t0) / 1e3
                 lv = ""
-                if "k_pca_level" in kn:
-                    lv = str(lvl)
+                if "k_pca_level" in kn and "k_pca_project" not in prev:
                     lvl += 1
+                if "k_pca_level" in kn or "k_pca_project" in kn:
+                    lv = str(lvl)
                 lines.append(f"| {kn} | {lv} | {d:.1f} us | {st:.1f} us |")
+                prev = kn
             lines.append("")
         open(out, "w").write("\n".join(lines))
         print("\n".join(lines))

@@ -125,8 +125,8 @@ struct Plan {
   // interaction matrix: raw query sums and counts per query cluster
   size_t qsum, qcnt;
   // principal-component split: token scratch, projection keys, node table
-  size_t pca_tmp, pca_key, pca_nodes, pca_lvl;          // key side
-  size_t pca_tmp_q, pca_key_q, pca_nodes_q, pca_lvl_q;  // query side (the two sides may overlap)
+  size_t pca_tmp, pca_key, pca_nodes, pca_lvl, pca_dbuf;            // key side
+  size_t pca_tmp_q, pca_key_q, pca_nodes_q, pca_lvl_q, pca_dbuf_q;  // query side (the two sides may overlap)
   // cold key clustering: operands of every stage's centres at their global
   // rows, the running nearest-centre score, per-stage centre counts and
   // offsets for the merge launches, Algorithm 1's per-head state, all-L counts
@@ -251,10 +251,12 @@ Plan make_plan(const ac_shape *s, const ac_params *p) {
   P.pca_key = take(BH * L * 4);
   P.pca_nodes = take((L / PCA_BLOCK_MIN + 2) * 8);  // at most ceil(L / b) - 1 internal nodes
   P.pca_lvl = take(64 * 4);
+  P.pca_dbuf = take(BH * (size_t)pca_dir_cap(L) * D * 4);
   P.pca_tmp_q = take(BH * L * 4);
   P.pca_key_q = take(BH * L * 4);
   P.pca_nodes_q = take((L / PCA_BLOCK_MIN + 2) * 8);
   P.pca_lvl_q = take(64 * 4);
+  P.pca_dbuf_q = take(BH * (size_t)pca_dir_cap(L) * D * 4);
   P.fops_hi = take(BH * P.ncapk * D * 2);
   P.fops_lo = take(BH * P.ncapk * D * 2);
   P.fops_norm = take(BH * P.ncapk * 4);
@@ -756,6 +758,7 @@ ac_status do_pca_split(const Plan &P, const uint16_t *X, int block, ac_clusters 
   a.key = at<uint32_t>(ws, query_side ? P.pca_key_q : P.pca_key);
   a.nodes = at<int2>(ws, query_side ? P.pca_nodes_q : P.pca_nodes);
   a.lvl = at<int>(ws, query_side ? P.pca_lvl_q : P.pca_lvl);
+  a.dbuf = at<float>(ws, query_side ? P.pca_dbuf_q : P.pca_dbuf);
   a.dir = tr ? tr->dir : nullptr;
   a.ndir = ninternal;
   a.L = L;

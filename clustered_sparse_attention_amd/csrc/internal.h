@@ -174,6 +174,11 @@ struct TailArgs {
 constexpr int PCA_SMAX = 512;   // subsample points that set a node's direction
 constexpr int PCA_BLOCK_MIN = 16, PCA_BLOCK_MAX = 4096;  // cluster sizes (powers of two)
 constexpr int PCA_ITERS = 64;   // power iterations per node
+// Levels whose largest node has PCA_BIG_NODE points or more run in three
+// launches: the directions (a block per node), the projections (a block per
+// PCA_PROJ_CHUNK points) and the cuts (a block per node).
+constexpr int PCA_BIG_NODE = 16384, PCA_PROJ_CHUNK = 4096;
+__host__ __device__ inline int pca_dir_cap(int L) { return L / 4096 + 2; }  // node slots a head for such a level
 struct PcaArgs {
   const uint16_t *X;  // [BH, L, D] rows to cluster
   int *perm;          // [BH, L] token order, refined level by level
@@ -183,6 +188,7 @@ struct PcaArgs {
   int *lvl;           // [levels + 1] first node of each level
   float *dir;         // [BH, ndir, D] direction of each internal node, or NULL
   int ndir;
+  float *dbuf;        // [BH, pca_dir_cap(L), D] directions of a level split in three launches
   int L, block;
 };
 

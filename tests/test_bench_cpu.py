@@ -118,11 +118,12 @@ def test_summarize_pca_takes_the_last_step_of_each_side(tmp_path):
     """Two queues, two layer steps: the table lists the last step's split tree,
     levels and finishing kernels per side, and the span covers both sides."""
     def step(t0):
-        key = [("ac::k_pca_tree_wide", 10_000), ("ac::k_iota_perm", 5_000)] + \
-              [("void ac::k_pca_level<128, 8>", 100_000 * (i + 1)) for i in range(3)] + \
+        key = [("ac::k_pca_tree_wide", 10_000), ("ac::k_iota_perm", 5_000), ("void ac::k_pca_level<128>", 40_000),
+               ("void ac::k_pca_project<128>", 30_000), ("void ac::k_pca_level<128>", 30_000)] + \
+              [("void ac::k_pca_level<128>", 100_000 * (i + 1)) for i in range(3)] + \
               [("ac::k_pca_finish", 20_000), ("void ac::k_kstats_part<128>", 300_000)]
         qry = [("void ac::k_qnorm<128>", 300_000), ("ac::k_pca_tree_wide", 9_000)] + \
-              [("void ac::k_pca_level<128, 8>", 50_000) for _ in range(2)] + [("ac::k_seg_mean", 40_000)]
+              [("void ac::k_pca_level<128>", 50_000) for _ in range(2)] + [("ac::k_seg_mean", 40_000)]
         out = []
         for q, seq, t in (("1", key, t0), ("2", qry, t0 + 7_000)):
             for name, dur in seq:
@@ -143,12 +144,15 @@ def test_summarize_pca_takes_the_last_step_of_each_side(tmp_path):
     assert "Command: `the cmd`" in text
     keys = text.split("## keys")[1].split("## queries")[0]
     qrys = text.split("## queries")[1]
-    assert [l.split("|")[2].strip() for l in keys.splitlines() if "k_pca_level" in l] == ["0", "1", "2"]
+    # level 0 in three launches (direction, projections, cut), then levels 1-3
+    lv = [(l.split("|")[1].strip(), l.split("|")[2].strip()) for l in keys.splitlines()
+          if "k_pca_level" in l or "k_pca_project" in l]
+    assert [x[1] for x in lv] == ["0", "0", "0", "1", "2", "3"] and lv[1][0] == "ac::k_pca_project<128>"
     assert "| 300.0 us |" in [l for l in keys.splitlines() if "k_pca_level" in l][-1]
     assert "k_kstats_part" in keys and "k_score_prep" not in keys
     assert "k_qnorm" in qrys and "k_seg_mean" in qrys and qrys.count("k_pca_level") == 2
-    # keys: 10 + 5 + 100 + 200 + 300 + 20 + 300 us and 6 gaps of 1 us, from t = 10,000,000 ns
-    assert keys.startswith(": 0.941 ms")
+    # keys: 10 + 5 + 40 + 30 + 30 + 100 + 200 + 300 + 20 + 300 us and 9 gaps of 1 us
+    assert keys.startswith(": 1.044 ms")
     # the last step only: every start within the second step's span
     starts = [float(l.split("|")[4].split()[0]) for l in text.splitlines() if l.startswith("| ac::") or l.startswith("| void")]
     assert min(starts) == 0.0 and max(starts) < 1000.0

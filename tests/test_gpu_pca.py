@@ -190,6 +190,35 @@ def test_pca_split_full_length(name):
     print(f"\n[{name}] PCA split near ties {ties}; attention worst max-abs {worst[0]:.3g} rel-L2 {worst[1]:.3g}")
 
 
+def test_pca_split_tree_wider_than_one_block_holds():
+    """261,144 queries in clusters of 16 (16,322 query clusters, which one
+    k-means++ point per cluster allows): the widest level holds more internal
+    nodes (8,130) than the one-block tree builder keeps in LDS (4,096), so the
+    split tree comes from the sequential builder.  Every split of the query
+    side against the oracle, then the exact cluster shape."""
+    L, d, bq, bk = 261144, 64, 16, 4096
+    counts = []
+    cur = [L]
+    while cur:
+        counts.append(len(cur))
+        nxt = []
+        for n in cur:
+            nl, nr = ops.split_sizes(n, bq)
+            nxt += [c for c in (nl, nr) if c > bq]
+        cur = nxt
+    assert max(counts) > 4096
+    w = gen.get_workload("tiny", H=1, L=L, d=d)
+    Q, K, V = gen.generate(w)
+    p = oracle_params(nq=-(-L // bq), m0=32, nmax=-(-L // bk) + 1, init_sample=1, sel_mode=nm.SEL_DENSITY,
+                      sel_param=0.2)
+    r, tq, _ = _run_pca(Q, K, V, p, bq, bk)
+    Xq = nm.bf16_to_f64(okm.normalize_queries(Q.reshape(r.BH, L, d)[0]))
+    ties = check_pca_trace(Xq, bq, np_(tq.dir)[0], np_(tq.perm)[0])
+    _check_clusters(Xq, bq, np_(r.q.labels)[0], np_(r.q.perm)[0], np_(r.q.seg)[0], int(np_(r.q.ncl)[0]),
+                    np_(r.q.cent)[0])
+    print(f"\nL={L} bq={bq}: {len(counts)} levels, widest {max(counts)}; split near ties {ties}")
+
+
 def test_pca_query_and_key_sides_overlap():
     """The query split and the key split have workspace scratch of their own:
     run on two streams over one workspace, in either order of enqueueing,
