@@ -6,7 +6,8 @@
 // smallest projections onto the node's direction go left, the rest right,
 // each side keeping its token order.  The tree's shape depends only on n and
 // b, so every level is one launch over the internal nodes of that level
-// (one workgroup per node and head).  A workgroup:
+// (one workgroup per node and head; a level of large nodes is three
+// launches, so that many workgroups share its projections).  A workgroup:
 //   1. takes a strided subsample of s = min(n, PCA_SMAX) points and its mean;
 //   2. forms the d x d covariance of the centred subsample (bf16 of x - mean)
 //      with 32x32x16 bf16 MFMA (fp32 sums), gathering PCA_CHUNK points into
@@ -168,10 +169,6 @@ AC_DEV float row16_sum(float v) {
 // the value lane l holds (uniform)
 AC_DEV float lane_f32(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
 
-// sp: row stride (bf16) of the subsample in LDS, sized by the launch to the
-// level's largest node (the dynamic LDS holds the larger of the subsample,
-// D sp bf16, and the split squares, 2 D (D + 8) bf16; the fp32 D x D matrix
-// fits in the latter)
 // Projections of the node's points [beg, end) onto the direction whose
 // entries sub*PL .. sub*PL + PL - 1 the lane holds in vv: 16 lanes a point
 // (lane sub takes those PL dimensions; the sum over the 16 lanes by DPP),
@@ -214,7 +211,11 @@ AC_DEV void pca_project(const uint16_t *X, const int *perm, int *tmp, uint32_t *
 
 // mode 0: the whole node; 1: its direction only, to a.dbuf; 2: the cut only,
 // from the projection keys k_pca_project wrote (a level of large nodes runs
-// modes 1, k_pca_project and 2, so that many blocks share its projections)
+// modes 1, k_pca_project and 2, so that many blocks share its projections).
+// sp: row stride (bf16) of a subsample chunk in LDS, its width + 8, set by
+// the launch from the level's largest node; the dynamic LDS holds the larger
+// of a chunk, D sp bf16, and the split squares, 2 D (D + 8) bf16 (the fp32
+// D x D matrix fits in the latter); mode 2 uses none of it.
 template <int D>
 __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int count, int sp, int mode) {
   constexpr int NT = 512;
@@ -262,29 +263,29 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
       float sum8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       for (int j0 = pg; j0 < s; j0 += 8 * PG) {
         u32x4_t v[8];
-  #pragma unroll
+#pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int j = j0 + u * PG;
           v[u] = (u32x4_t){0u, 0u, 0u, 0u};
           if (j < s) v[u] = *(const u32x4_t *)(X + (int64_t)sidx[j] * D + c * 8);
         }
-  #pragma unroll
+#pragma unroll
         for (int u = 0; u < 8; ++u)
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 8; ++e) sum8[e] += bf2f((uint16_t)((e & 1) ? (v[u][e >> 1] >> 16) : (v[u][e >> 1] & 0xFFFFu)));
       }
-  #pragma unroll
+#pragma unroll
       for (int o = CPR; o < 64; o <<= 1)
-  #pragma unroll
+#pragma unroll
         for (int e = 0; e < 8; ++e) sum8[e] += __shfl_xor(sum8[e], o, 64);
       float *part = reinterpret_cast<float *>(pca_lds);  // [NT / 64][D], in the subsample's space
       if (lane < CPR)
-  #pragma unroll
+#pragma unroll
         for (int e = 0; e < 8; ++e) part[wave * D + c * 8 + e] = sum8[e];
       __syncthreads();
       if (tid < D) {
         float t = 0.f;
-  #pragma unroll
+#pragma unroll
         for (int w = 0; w < NT / 64; ++w) t += part[w * D + tid];
         mu[tid] = t / (float)s;
       }
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
     constexpr int NTILE = (D / 32) * (D / 32);
     constexpr int TPW = (NTILE + 7) / 8;
     f32x16_t acc[TPW];
-  #pragma unroll
+#pragma unroll
     for (int k = 0; k < TPW; ++k) acc[k] = (f32x16_t){};
     const int l32 = lane & 31, g = lane >> 5;
     const int chw = sp - 8;  // chunk width, a multiple of 16
@@ -316,7 +317,7 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
           const int c = (it % CQ) * 4 + (lane >> 4), jq = (it / CQ) * 16 + (lane & 15);
           if (jq < ngrp) {
             u32x4_t v[4];
-  #pragma unroll
+#pragma unroll
             for (int k = 0; k < 4; ++k) {
               const int j = 4 * jq + k;
               v[k] = (u32x4_t){0u, 0u, 0u, 0u};
@@ -324,11 +325,11 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
             }
             const float4 m0 = *(const float4 *)&mu[c * 8], m1 = *(const float4 *)&mu[c * 8 + 4];
             const float m8[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-  #pragma unroll
+#pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int sh = 16 * (e & 1);
               uint32_t y[4];
-  #pragma unroll
+#pragma unroll
               for (int k = 0; k < 4; ++k) {
                 const uint16_t xb = (uint16_t)((v[k][e >> 1] >> sh) & 0xFFFFu);
                 y[k] = 4 * jq + k < cs ? f2bf(bf2f(xb) - m8[e]) : 0u;  // the padding columns stay zero
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
         float nn = -1.f;
         if (j < cs) {
           nn = 0.f;
-  #pragma unroll 8
+#pragma unroll 8
           for (int i = half * (D / 2); i < (half + 1) * (D / 2); ++i) {
             const float y = bf2f(Y[i * sp + j]);
             nn = fmaf(y, y, nn);
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
         }
         nn += dpp_f32<0xB1>(nn);  // the point's other half
         int bj = ch0 + j;
-  #pragma unroll
+#pragma unroll
         for (int o = 32; o > 1; o >>= 1) {
           const float on = __shfl_xor(nn, o, 64);
           const int oj = __shfl_xor(bj, o, 64);
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
         if (wave == 0) {
           float bn = lane < 8 ? far_n[lane] : -2.f;
           int bjj = lane < 8 ? far_j[lane] : 0x7fffffff;
-  #pragma unroll
+#pragma unroll
           for (int o = 32; o > 0; o >>= 1) {
             const float on = __shfl_xor(bn, o, 64);
             const int oj = __shfl_xor(bjj, o, 64);
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
         }
       }
       for (int k0 = 0; k0 < cpad; k0 += 16) {
-  #pragma unroll
+#pragma unroll
         for (int k = 0; k < TPW; ++k) {
           const int tile = wave + 8 * k;
           if (tile < NTILE) {
@@ -413,14 +414,14 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
     constexpr int AP = D + 8;
     uint16_t *Ahi = reinterpret_cast<uint16_t *>(pca_lds), *Alo = Ahi + D * AP;
     auto aidx = [](int r, int c) { return r * AP + c; };
-  #pragma unroll 1
+#pragma unroll 1
     for (int sq = 0; sq <= PCA_SQUARINGS; ++sq) {
       if (sq > 0) {
-  #pragma unroll
+#pragma unroll
         for (int k = 0; k < TPW; ++k) acc[k] = (f32x16_t){};
-  #pragma unroll 1
+#pragma unroll 1
         for (int k0 = 0; k0 < D; k0 += 16) {
-  #pragma unroll
+#pragma unroll
           for (int k = 0; k < TPW; ++k) {
             const int tile = wave + 8 * k;
             if (tile < NTILE) {
@@ -437,13 +438,13 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
       }
       // the diagonal: in a tile with I == J, lane (l32, g) with g = bit 2 of
       // l32 holds entry l32 in register 4 (l32 / 8) + l32 % 4
-  #pragma unroll
+#pragma unroll
       for (int k = 0; k < TPW; ++k) {
         const int tile = wave + 8 * k;
         if (tile < NTILE && tile / (D / 32) == tile % (D / 32) && g == ((l32 >> 2) & 1)) {
           const int rr = 4 * (l32 >> 3) + (l32 & 3);
           float dv = 0.f;
-  #pragma unroll
+#pragma unroll
           for (int r = 0; r < 16; ++r)
             if (r == rr) dv = acc[k][r];
           mu[(tile / (D / 32)) * 32 + l32] = dv;
@@ -451,7 +452,7 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
       }
       __syncthreads();  // the diagonal is complete; every read of Y or of A is done
       float tr = 0.f;
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < D; i += 4) {
         const float4 t4 = *(const float4 *)&mu[i];
         tr += (t4.x + t4.y) + (t4.z + t4.w);
@@ -461,7 +462,7 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
       // through an LDS zero so that the 16 addresses are not kept in registers
       // across the stages but folded into the stores' offsets
       const int z = sh_zero;
-  #pragma unroll
+#pragma unroll
       for (int k = 0; k < TPW; ++k) {
         const int tile = wave + 8 * k;
         if (tile < NTILE) {
@@ -469,7 +470,7 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
           const int rb = I * 32 + 4 * g + z, cl = J * 32 + l32;
           if (sq < PCA_SQUARINGS) {
             uint16_t *ph = Ahi + aidx(rb, cl), *pl = Alo + aidx(rb, cl);
-  #pragma unroll
+#pragma unroll
             for (int r = 0; r < 16; ++r) {
               const float v = acc[k][r] * inv;
               const uint16_t hi = f2bf(v);
@@ -478,7 +479,7 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
             }
           } else {
             float *pc = C + rb * D + cl;
-  #pragma unroll
+#pragma unroll
             for (int r = 0; r < 16; ++r) pc[(8 * (r / 4) + (r % 4)) * D] = acc[k][r] * inv;
           }
         }
@@ -498,11 +499,11 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
     const int row = lane >> 4, l16 = lane & 15;
     const int o0 = wave * (D / 8) + row * NA;
     float cv[NM][4][NA];
-  #pragma unroll
+#pragma unroll
     for (int m = 0; m < NM; ++m)
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < 4; ++t)
-  #pragma unroll
+#pragma unroll
         for (int a2 = 0; a2 < NA; ++a2) cv[m][t][a2] = C[(64 * m + 4 * l16 + t) * D + o0 + a2];
     constexpr int NIT = PCA_ITERS >> PCA_SQUARINGS;
     static_assert(NIT << PCA_SQUARINGS == PCA_ITERS, "the squarings must divide the power iterations");
@@ -512,12 +513,12 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
       const float nrm2 = ((n0.x + n0.y) + (n0.z + n0.w)) + ((n1.x + n1.y) + (n1.z + n1.w));
       const float inv = nrm2 > 0.f ? rsqrtf(nrm2) : 0.f;  // only the direction matters
       float acc[NA];
-  #pragma unroll
+#pragma unroll
       for (int a2 = 0; a2 < NA; ++a2) acc[a2] = 0.f;
-  #pragma unroll
+#pragma unroll
       for (int m = 0; m < NM; ++m) {
         const float4 x = *(const float4 *)&wbuf[cur][64 * m + 4 * l16];
-  #pragma unroll
+#pragma unroll
         for (int a2 = 0; a2 < NA; ++a2) {
           acc[a2] = fmaf(cv[m][0][a2], x.x, acc[a2]);
           acc[a2] = fmaf(cv[m][1][a2], x.y, acc[a2]);
@@ -526,14 +527,14 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
         }
       }
       float sq = 0.f;
-  #pragma unroll
+#pragma unroll
       for (int a2 = 0; a2 < NA; ++a2) {
         acc[a2] = row16_sum(acc[a2]) * inv;
         sq = fmaf(acc[a2], acc[a2], sq);
       }
       const float tot = (lane_f32(sq, 0) + lane_f32(sq, 16)) + (lane_f32(sq, 32) + lane_f32(sq, 48));
       if (l16 == 0)
-  #pragma unroll
+#pragma unroll
         for (int a2 = 0; a2 < NA; ++a2) wbuf[nxt][o0 + a2] = acc[a2];
       if (lane == 0) nrm_part[nxt][wave] = tot;
       __syncthreads();
@@ -541,7 +542,7 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
     // normalise and orient: the component of largest magnitude is positive
     if (wave == 0) {
       float nrm2 = 0.f;
-  #pragma unroll
+#pragma unroll
       for (int w = 0; w < 8; ++w) nrm2 += nrm_part[NIT & 1][w];
       float best = -1.f, sgn = 1.f;
       int bi = 0;
@@ -549,7 +550,7 @@ __global__ __launch_bounds__(512) void k_pca_level(PcaArgs a, int first, int cou
         const float v = wbuf[NIT & 1][i];
         if (fabsf(v) > best) { best = fabsf(v); bi = i; sgn = v < 0.f ? -1.f : 1.f; }
       }
-  #pragma unroll
+#pragma unroll
       for (int o = 32; o > 0; o >>= 1) {
         const float ov = __shfl_xor(best, o, 64);
         const int oi2 = __shfl_xor(bi, o, 64);
