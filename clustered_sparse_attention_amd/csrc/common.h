@@ -75,6 +75,30 @@ AC_DEV uint64_t stream_id(uint64_t bh, uint32_t role, uint32_t stage) {
   return ((bh & ((1ull << 44) - 1)) << 20) | ((uint64_t)(role & 0xF) << 16) | (stage & 0xFFFF);
 }
 
+// DPP moves within a wave.  Controls used: quad permutes 0x00-0xFF, row
+// mirror 0x140, half-row mirror 0x141.  Lanes that the row and bank masks
+// leave out get 0.
+template <int CTRL, int ROWS = 0xF, int BANKS = 0xF>
+AC_DEV uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, BANKS, false);
+}
+template <int CTRL, int ROWS = 0xF, int BANKS = 0xF>
+AC_DEV float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL, ROWS, BANKS>(__float_as_uint(v)));
+}
+// sum over each row of 16 lanes, left in every lane of the row: after each
+// step the groups of 2, 4, 8, 16 lanes hold equal values, so the mirrors
+// pair every lane with the other half of its group
+AC_DEV float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);   // quad: xor 1
+  v += dpp_f32<0x4E>(v);   // quad: xor 2
+  v += dpp_f32<0x141>(v);  // half-row mirror
+  v += dpp_f32<0x140>(v);  // row mirror
+  return v;
+}
+// the value lane l holds (uniform)
+AC_DEV float lane_f32(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
+
 template <typename T>
 AC_DEV T wave_sum(T v) {
 #pragma unroll

@@ -150,25 +150,6 @@ AC_DEV int2 block_scan2(int x, int y, int2 *sh, int2 &tot) {
   return make_int2(ox + ix - x, oy + iy - y);
 }
 
-// DPP move of a float within rows of 16 lanes (controls: quad permutes
-// 0x00-0xFF, row mirror 0x140, half-row mirror 0x141); all lanes active
-template <int CTRL>
-AC_DEV float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-// sum over each row of 16 lanes, left in every lane of the row: after each
-// step the groups of 2, 4, 8, 16 lanes hold equal values, so the mirrors
-// pair every lane with the other half of its group
-AC_DEV float row16_sum(float v) {
-  v += dpp_f32<0xB1>(v);   // quad: xor 1
-  v += dpp_f32<0x4E>(v);   // quad: xor 2
-  v += dpp_f32<0x141>(v);  // half-row mirror
-  v += dpp_f32<0x140>(v);  // row mirror
-  return v;
-}
-// the value lane l holds (uniform)
-AC_DEV float lane_f32(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
-
 // Projections of the node's points [beg, end) onto the direction whose
 // entries sub*PL .. sub*PL + PL - 1 the lane holds in vv: 16 lanes a point
 // (lane sub takes those PL dimensions; the sum over the 16 lanes by DPP),
