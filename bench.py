@@ -509,8 +509,11 @@ def summarize(args):
         lines = ["# Bench lines, all workloads (one MI355X)", "", f"Command: `{cmd}`", "",
                  "A step is one `ac_layer` call on resident inputs (cold unless marked warm); the phase columns "
                  "come from a separate untimed pass through the entry points, the query clustering on a second "
-                 "stream beside the key clustering (`both` is their wall time). Dense baselines: the library's "
-                 "own dense mode and torch SDPA (flash backend) on the same tensors.", "",
+                 "stream beside the key clustering (`both` is their wall time). Rows marked with the "
+                 "principal-component split time the entry points in `ac_layer`'s order instead (the query "
+                 "split beside the key split), with ClusterAttention's clustering in place of Algorithm 1's. "
+                 "Dense baselines: the library's own dense mode and torch SDPA (flash backend) on the same "
+                 "tensors.", "",
                  "| workload | step | selection | layer ms | dense-equiv TFLOP/s | cluster_q / cluster_k / both (ms) | "
                  "select ms | attention ms | attention / bf16 peak | pairs kept | fallback heads | key clusters | "
                  "own dense ms | SDPA flash ms | vs best dense | CPU oracle |",
@@ -525,6 +528,8 @@ def summarize(args):
             ph, db, cb = d["phase_ms"], d.get("dense_baseline") or {}, d.get("cpu_baseline")
             sel = d["config"]["selection"] + (" + compensation" if d["config"]["compensate"] else "")
             warm = "warm" if "warm" in d["timed_step"] else "cold"
+            if d.get("key_clustering", "").startswith("principal-component"):
+                warm += ", principal-component split " + "/".join(re.findall(r" of (\d+)", d["key_clustering"]))
             cpu = (f"{cb['value']:.3f} TFLOP/s, {cb['cores']} cores, "
                    f"{'complete head' if cb.get('complete_head') else 'extrapolated'}") if cb else "—"
             lines.append(

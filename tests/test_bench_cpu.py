@@ -63,6 +63,18 @@ def test_summarize_configs_table(tmp_path):
     assert "Command: `the command`" in text
 
 
+def test_summarize_configs_marks_the_principal_component_rows(tmp_path):
+    d = json.loads(_bench_line(29.4, cpu=False))
+    d["timed_step"] = "entry points in ac_layer order"
+    d["key_clustering"] = "principal-component split, queries in clusters of 256, keys of 64 (ClusterAttention)"
+    lg = tmp_path / "p.log"
+    lg.write_text(json.dumps(d) + "\n")
+    out = tmp_path / "t.md"
+    bench.summarize(["configs", str(out), "cmd", "::", str(lg)])
+    row = [l for l in out.read_text().splitlines() if l.startswith("| Wan2.1")][0]
+    assert "| cold, principal-component split 256/64 |" in row and "| 29.40 |" in row
+
+
 def test_summarize_denoise_table(tmp_path):
     steps = [{"step": 0, "mode": "dense", "ms": 116.0}, {"step": 1, "mode": "cold", "ms": 38.0, "sel_param": 0.15},
              {"step": 2, "mode": "warm", "ms": 30.0, "sel_param": 0.15}]
