@@ -58,32 +58,50 @@ __global__ __launch_bounds__(256) void k_score_prep_b(ScoreArgs a) {
   }
 }
 
-// S[r, c] = A[r] . B[c] with 16x16x32 MFMA, one wave per 16x16 tile.
+// S[r, c] = A[r] . B[c] with 16x16x32 MFMA.  A wave computes a 32 x 32 block
+// (2 x 2 tiles of 16 x 16: each A and B fragment it loads feeds two
+// products), four waves a 32 x 128 block.
 template <int D>
 __global__ __launch_bounds__(256) void k_score_gemm(ScoreArgs a) {
   constexpr int KD = 6 * D;
   const int h = blockIdx.z;
-  const int rt = blockIdx.y;
-  const int ct = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int r0 = blockIdx.y * 32;
+  const int c0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 32;
   const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
-  if (ct * 16 >= a.ncap_pad) return;
-  const uint16_t *Ar = a.A + ((int64_t)h * a.nq_pad + rt * 16 + l16) * KD;
-  const uint16_t *Br = a.Bm + ((int64_t)h * a.ncap_pad + ct * 16 + l16) * KD;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  if (c0 >= a.ncap_pad || r0 >= a.nq_pad) return;
+  // a row or column tile beyond the padded extent reads row 0 and is not stored
+  const bool rv1 = r0 + 16 < a.nq_pad, cv1 = c0 + 16 < a.ncap_pad;
+  const uint16_t *A0 = a.A + ((int64_t)h * a.nq_pad + r0 + l16) * KD;
+  const uint16_t *A1 = a.A + ((int64_t)h * a.nq_pad + (rv1 ? r0 + 16 : 0) + l16) * KD;
+  const uint16_t *B0 = a.Bm + ((int64_t)h * a.ncap_pad + c0 + l16) * KD;
+  const uint16_t *B1 = a.Bm + ((int64_t)h * a.ncap_pad + (cv1 ? c0 + 16 : 0) + l16) * KD;
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
   for (int ks = 0; ks < KD / 32; ++ks) {
-    bf16x8_t af = *(const bf16x8_t *)&Ar[ks * 32 + g * 8];
-    bf16x8_t bf = *(const bf16x8_t *)&Br[ks * 32 + g * 8];
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc, 0, 0, 0);
+    const bf16x8_t a0 = *(const bf16x8_t *)&A0[ks * 32 + g * 8], a1 = *(const bf16x8_t *)&A1[ks * 32 + g * 8];
+    const bf16x8_t b0 = *(const bf16x8_t *)&B0[ks * 32 + g * 8], b1 = *(const bf16x8_t *)&B1[ks * 32 + g * 8];
+    acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[0][0], 0, 0, 0);
+    acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b1, acc[0][1], 0, 0, 0);
+    acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b0, acc[1][0], 0, 0, 0);
+    acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[1][1], 0, 0, 0);
   }
-  const int c = ct * 16 + l16;
-  if (c >= a.ncap) return;
   const int *seg = a.seg_k + (int64_t)h * (a.ncap + 1);
-  const bool live = c < a.ncl_k[h] && seg[c + 1] > seg[c];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = rt * 16 + g * 4 + j;
-    if (r < a.nq) a.S[((int64_t)h * a.nqcap + r) * a.ncap + c] = live ? acc[j] : -__builtin_inff();
+  for (int j = 0; j < 2; ++j) {
+    const int c = c0 + 16 * j + l16;
+    if (c >= a.ncap) continue;
+    const bool live = c < a.ncl_k[h] && seg[c + 1] > seg[c];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = r0 + 16 * i + g * 4 + q;
+        if (r < a.nq) a.S[((int64_t)h * a.nqcap + r) * a.ncap + c] = live ? acc[i][j][q] : -__builtin_inff();
+      }
   }
 }
 
@@ -135,13 +153,12 @@ __global__ __launch_bounds__(256) void k_select(SelectArgs a) {
   // bitonic sort, ascending
   for (int k = 2; k <= P; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < P; i += 256) {
-        int ixj = i ^ j;
-        if (ixj > i) {
-          unsigned long long x = keys[i], y = keys[ixj];
-          bool up = (i & k) == 0;
-          if ((x > y) == up) { keys[i] = y; keys[ixj] = x; }
-        }
+      // compare-exchange pair q: i has bit j clear, partner i + j
+      for (int q = tid; q < P / 2; q += 256) {
+        const int i = 2 * q - (q & (j - 1)), ixj = i + j;
+        unsigned long long x = keys[i], y = keys[ixj];
+        bool up = (i & k) == 0;
+        if ((x > y) == up) { keys[i] = y; keys[ixj] = x; }
       }
       __syncthreads();
     }
@@ -234,11 +251,11 @@ void launch_score(int D, const ScoreArgs &a, int BH, hipStream_t st) {
   if (D == 64) {
     hipLaunchKernelGGL(k_score_prep_a<64>, dim3(a.nq_pad, BH), dim3(256), 0, st, a);
     hipLaunchKernelGGL(k_score_prep_b<64>, dim3(a.ncap_pad, BH), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_score_gemm<64>, dim3((a.ncap_pad / 16 + 3) / 4, a.nq_pad / 16, BH), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_score_gemm<64>, dim3((a.ncap_pad / 32 + 4) / 4, (a.nq_pad + 31) / 32, BH), dim3(256), 0, st, a);
   } else {
     hipLaunchKernelGGL(k_score_prep_a<128>, dim3(a.nq_pad, BH), dim3(256), 0, st, a);
     hipLaunchKernelGGL(k_score_prep_b<128>, dim3(a.ncap_pad, BH), dim3(256), 0, st, a);
-    hipLaunchKernelGGL(k_score_gemm<128>, dim3((a.ncap_pad / 16 + 3) / 4, a.nq_pad / 16, BH), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_score_gemm<128>, dim3((a.ncap_pad / 32 + 4) / 4, (a.nq_pad + 31) / 32, BH), dim3(256), 0, st, a);
   }
 }
 
