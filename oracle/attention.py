@@ -10,6 +10,9 @@ import numpy as np
 from .numerics import bf16_to_f64
 
 
+ROW_CHUNK = 512  # query rows whose logits against every key are held at once
+
+
 def softmax_attend(logits: np.ndarray, values: np.ndarray):
     """o = sum_j softmax(logits)_j v_j per row; also the natural-log
     normaliser lse = log sum_j exp(logits_j)."""
@@ -43,27 +46,47 @@ def sparse_rows(Q, K, V, rows, q_labels, k_labels, selection, scale, compensate=
     rows = np.asarray(rows)
     O = np.zeros((rows.size, Q.shape[1]))
     lse = np.zeros(rows.size)
+    for c0 in range(0, rows.size, ROW_CHUNK):
+        O[c0:c0 + ROW_CHUNK], lse[c0:c0 + ROW_CHUNK] = _sparse_rows_chunk(
+            Q, K, V, rows[c0:c0 + ROW_CHUNK], q_labels, k_labels, selection, scale, compensate, count, kmean, vmean)
+    return O, lse
+
+
+def _sparse_rows_chunk(Q, K, V, rows, q_labels, k_labels, selection, scale, compensate, count, kmean, vmean):
+    """sparse_rows for one chunk of rows.  The softmax of a row runs over
+    its selected keys alone: their logits are read out of the row's product
+    with every key, and every other key gets weight zero in the product with
+    all of V (the same sums as over a gathered K[Index], V[Index], without
+    copying those rows)."""
+    S = (Q[rows] @ K.T) * scale
+    W = np.zeros_like(S)
+    num = np.zeros((rows.size, V.shape[1]))
+    den = np.zeros(rows.size)
+    mxs = np.zeros(rows.size)
     rq = q_labels[rows]
     for r in np.unique(rq):
         sel = np.asarray(selection[r], dtype=np.int64)
-        keymask = np.isin(k_labels, sel)
-        kidx = np.nonzero(keymask)[0]
+        keys = np.nonzero(np.isin(k_labels, sel))[0]
         at = np.nonzero(rq == r)[0]
-        q = Q[rows[at]]
-        logits = (q @ K[kidx].T) * scale
-        vals = V[kidx]
+        z = S[np.ix_(at, keys)]
+        zs = [z]
         if compensate:
-            m = count.shape[0]
-            excl = np.ones(m, dtype=bool)
+            excl = np.ones(count.shape[0], dtype=bool)
             excl[sel] = False
             excl &= count > 0
             ex = np.nonzero(excl)[0]
-            if ex.size:
-                pl = (q @ kmean[ex].T) * scale + np.log(count[ex].astype(np.float64))[None, :]
-                logits = np.concatenate([logits, pl], axis=1)
-                vals = np.concatenate([vals, vmean[ex]], axis=0)
-        O[at], lse[at] = softmax_attend(logits, vals)
-    return O, lse
+            pl = (Q[rows[at]] @ kmean[ex].T) * scale + np.log(count[ex].astype(np.float64))[None, :]
+            zs.append(pl)
+        mx = np.max(np.concatenate(zs, axis=1), axis=1, keepdims=True)
+        W[np.ix_(at, keys)] = np.exp(z - mx)
+        if compensate and ex.size:
+            wp = np.exp(pl - mx)
+            num[at] = wp @ vmean[ex]
+            den[at] = np.sum(wp, axis=1)
+        mxs[at] = mx[:, 0]
+    num += W @ V
+    den += np.sum(W, axis=1)
+    return num / den[:, None], mxs + np.log(den)
 
 
 def subset_output(Q, K, V, row, subset, scale):
