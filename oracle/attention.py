@@ -10,7 +10,7 @@ import numpy as np
 from .numerics import bf16_to_f64
 
 
-ROW_CHUNK = 512  # query rows whose logits against every key are held at once
+FEW_ROWS = 16  # rows of a query cluster up to which a large selection skips the gather
 
 
 def softmax_attend(logits: np.ndarray, values: np.ndarray):
@@ -46,47 +46,45 @@ def sparse_rows(Q, K, V, rows, q_labels, k_labels, selection, scale, compensate=
     rows = np.asarray(rows)
     O = np.zeros((rows.size, Q.shape[1]))
     lse = np.zeros(rows.size)
-    for c0 in range(0, rows.size, ROW_CHUNK):
-        O[c0:c0 + ROW_CHUNK], lse[c0:c0 + ROW_CHUNK] = _sparse_rows_chunk(
-            Q, K, V, rows[c0:c0 + ROW_CHUNK], q_labels, k_labels, selection, scale, compensate, count, kmean, vmean)
-    return O, lse
-
-
-def _sparse_rows_chunk(Q, K, V, rows, q_labels, k_labels, selection, scale, compensate, count, kmean, vmean):
-    """sparse_rows for one chunk of rows.  The softmax of a row runs over
-    its selected keys alone: their logits are read out of the row's product
-    with every key, and every other key gets weight zero in the product with
-    all of V (the same sums as over a gathered K[Index], V[Index], without
-    copying those rows)."""
-    S = (Q[rows] @ K.T) * scale
-    W = np.zeros_like(S)
-    num = np.zeros((rows.size, V.shape[1]))
-    den = np.zeros(rows.size)
-    mxs = np.zeros(rows.size)
     rq = q_labels[rows]
     for r in np.unique(rq):
         sel = np.asarray(selection[r], dtype=np.int64)
         keys = np.nonzero(np.isin(k_labels, sel))[0]
         at = np.nonzero(rq == r)[0]
-        z = S[np.ix_(at, keys)]
+        q = Q[rows[at]]
+        # The softmax runs over the selected keys alone.  K[Index] and
+        # V[Index] are gathered, except for a cluster with few rows here whose
+        # selection holds more than a quarter of the keys: its logits are read
+        # out of the product with every key, and every other key gets weight
+        # zero in the product with all of V.  The sums are the same either
+        # way, up to their order.
+        few = at.size <= FEW_ROWS and 4 * keys.size > K.shape[0]
+        z = ((q @ K.T) * scale)[:, keys] if few else (q @ K[keys].T) * scale
         zs = [z]
         if compensate:
-            excl = np.ones(count.shape[0], dtype=bool)
+            m = count.shape[0]
+            excl = np.ones(m, dtype=bool)
             excl[sel] = False
             excl &= count > 0
             ex = np.nonzero(excl)[0]
-            pl = (Q[rows[at]] @ kmean[ex].T) * scale + np.log(count[ex].astype(np.float64))[None, :]
+            pl = (q @ kmean[ex].T) * scale + np.log(count[ex].astype(np.float64))[None, :]
             zs.append(pl)
         mx = np.max(np.concatenate(zs, axis=1), axis=1, keepdims=True)
-        W[np.ix_(at, keys)] = np.exp(z - mx)
+        w = np.exp(z - mx)
+        if few:
+            wf = np.zeros((at.size, K.shape[0]))
+            wf[:, keys] = w
+            num = wf @ V
+        else:
+            num = w @ V[keys]
+        den = np.sum(w, axis=1)
         if compensate and ex.size:
             wp = np.exp(pl - mx)
-            num[at] = wp @ vmean[ex]
-            den[at] = np.sum(wp, axis=1)
-        mxs[at] = mx[:, 0]
-    num += W @ V
-    den += np.sum(W, axis=1)
-    return num / den[:, None], mxs + np.log(den)
+            num += wp @ vmean[ex]
+            den += np.sum(wp, axis=1)
+        O[at] = num / den[:, None]
+        lse[at] = mx[:, 0] + np.log(den)
+    return O, lse
 
 
 def subset_output(Q, K, V, row, subset, scale):

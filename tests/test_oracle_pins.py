@@ -479,11 +479,17 @@ def _toy_layer(seed, L=300, d=16, nk=12, nq=4):
     return Q, K, V, kl, ql
 
 
-def test_all_selected_equals_dense():
+# every row (each query cluster gathers its selected keys) and a sparse
+# sample (few rows a cluster: logits of every key, unselected ones at weight 0)
+ROW_SETS = [np.arange(300), np.arange(3, 300, 37)]
+
+
+@pytest.mark.parametrize("rows", ROW_SETS, ids=["all-rows", "sampled-rows"])
+def test_all_selected_equals_dense(rows):
     Q, K, V, kl, ql = _toy_layer(26)
     sel = [np.arange(12)] * 4
-    O, lse = oat.sparse_rows(Q, K, V, np.arange(300), ql, kl, sel, 0.25)
-    Od, lsed = oat.dense_rows(Q, K, V, np.arange(300), 0.25)
+    O, lse = oat.sparse_rows(Q, K, V, rows, ql, kl, sel, 0.25)
+    Od, lsed = oat.dense_rows(Q, K, V, rows, 0.25)
     assert np.allclose(O, Od, atol=1e-12) and np.allclose(lse, lsed, atol=1e-12)
 
 
@@ -504,7 +510,8 @@ def test_error_identity_eq4():
         assert np.allclose(Os[0], oS, atol=1e-13)
 
 
-def test_compensation_identity_eq5():
+@pytest.mark.parametrize("rows", ROW_SETS, ids=["all-rows", "sampled-rows"])
+def test_compensation_identity_eq5(rows):
     """ClusterAttention §1.2 eq. (5), with ||c|| read as the cluster size:
     o - o_hat_S = (1/d_hat_S) sum_c n_c (delta_c (vbar_c - o) + Cov_c(w, v)),
     with delta_c >= 0 (Jensen) and d_hat_S <= 1."""
@@ -514,8 +521,10 @@ def test_compensation_identity_eq5():
     kmean = np.stack([K[kl == c].mean(0) for c in range(12)])
     vmean = np.stack([V[kl == c].mean(0) for c in range(12)])
     sel = [np.array([0, 3, 5]), np.array([1]), np.array([2, 4, 6, 7]), np.array([11])]
-    Oc, _ = oat.sparse_rows(Q, K, V, np.arange(300), ql, kl, sel, scale, True, cnt, kmean, vmean)
-    for row in range(0, 300, 37):
+    Oc, _ = oat.sparse_rows(Q, K, V, rows, ql, kl, sel, scale, True, cnt, kmean, vmean)
+    for i, row in enumerate(rows):
+        if i % 9:
+            continue
         z = (Q[row] @ K.T) * scale
         Z = np.exp(z).sum()
         w = np.exp(z) / Z
@@ -533,10 +542,11 @@ def test_compensation_identity_eq5():
             rhs += cnt[c] * (delta * (vmean[c] - o) + cov)
             dhat += cnt[c] * what
         assert dhat <= 1 + 1e-12
-        assert np.allclose(o - Oc[row], rhs / dhat, atol=1e-12)
+        assert np.allclose(o - Oc[i], rhs / dhat, atol=1e-12)
 
 
-def test_singletons_compensation_is_dense():
+@pytest.mark.parametrize("rows", [np.arange(60), np.arange(1, 60, 7)], ids=["all-rows", "sampled-rows"])
+def test_singletons_compensation_is_dense(rows):
     """All clusters of size one: each pseudo-key is the key itself with weight
     ln 1 = 0, so sparse attention with compensation equals dense attention
     for any selection."""
@@ -546,8 +556,8 @@ def test_singletons_compensation_is_dense():
     ql = r.integers(0, 3, 60)
     sel = [np.array([1, 5]), np.array([7]), np.arange(30)]
     cnt = np.ones(60, int)
-    O, _ = oat.sparse_rows(Q, K, V, np.arange(60), ql, kl, sel, 0.3, True, cnt, K, V)
-    Od, _ = oat.dense_rows(Q, K, V, np.arange(60), 0.3)
+    O, _ = oat.sparse_rows(Q, K, V, rows, ql, kl, sel, 0.3, True, cnt, K, V)
+    Od, _ = oat.dense_rows(Q, K, V, rows, 0.3)
     assert np.allclose(O, Od, atol=1e-12)
 
 
