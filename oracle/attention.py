@@ -10,9 +10,6 @@ import numpy as np
 from .numerics import bf16_to_f64
 
 
-FEW_ROWS = 16  # rows of a query cluster up to which a large selection skips the gather
-
-
 def softmax_attend(logits: np.ndarray, values: np.ndarray):
     """o = sum_j softmax(logits)_j v_j per row; also the natural-log
     normaliser lse = log sum_j exp(logits_j)."""
@@ -49,41 +46,23 @@ def sparse_rows(Q, K, V, rows, q_labels, k_labels, selection, scale, compensate=
     rq = q_labels[rows]
     for r in np.unique(rq):
         sel = np.asarray(selection[r], dtype=np.int64)
-        keys = np.nonzero(np.isin(k_labels, sel))[0]
+        keymask = np.isin(k_labels, sel)
+        kidx = np.nonzero(keymask)[0]
         at = np.nonzero(rq == r)[0]
         q = Q[rows[at]]
-        # The softmax runs over the selected keys alone.  K[Index] and
-        # V[Index] are gathered, except for a cluster with few rows here whose
-        # selection holds more than a quarter of the keys: its logits are read
-        # out of the product with every key, and every other key gets weight
-        # zero in the product with all of V.  The sums are the same either
-        # way, up to their order.
-        few = at.size <= FEW_ROWS and 4 * keys.size > K.shape[0]
-        z = ((q @ K.T) * scale)[:, keys] if few else (q @ K[keys].T) * scale
-        zs = [z]
+        logits = (q @ K[kidx].T) * scale
+        vals = V[kidx]
         if compensate:
             m = count.shape[0]
             excl = np.ones(m, dtype=bool)
             excl[sel] = False
             excl &= count > 0
             ex = np.nonzero(excl)[0]
-            pl = (q @ kmean[ex].T) * scale + np.log(count[ex].astype(np.float64))[None, :]
-            zs.append(pl)
-        mx = np.max(np.concatenate(zs, axis=1), axis=1, keepdims=True)
-        w = np.exp(z - mx)
-        if few:
-            wf = np.zeros((at.size, K.shape[0]))
-            wf[:, keys] = w
-            num = wf @ V
-        else:
-            num = w @ V[keys]
-        den = np.sum(w, axis=1)
-        if compensate and ex.size:
-            wp = np.exp(pl - mx)
-            num += wp @ vmean[ex]
-            den += np.sum(wp, axis=1)
-        O[at] = num / den[:, None]
-        lse[at] = mx[:, 0] + np.log(den)
+            if ex.size:
+                pl = (q @ kmean[ex].T) * scale + np.log(count[ex].astype(np.float64))[None, :]
+                logits = np.concatenate([logits, pl], axis=1)
+                vals = np.concatenate([vals, vmean[ex]], axis=0)
+        O[at], lse[at] = softmax_attend(logits, vals)
     return O, lse
 
 

@@ -52,11 +52,12 @@ def interaction_matrix(Qbits: np.ndarray, labels: np.ndarray, nq: int) -> np.nda
 
 def metric_sq_dist(X: np.ndarray, C: np.ndarray, M: np.ndarray, chunk: int = 256) -> np.ndarray:
     """(x_i - c_j) M (x_i - c_j)^T for all pairs, the quadratic form as
-    written (differences first), in row chunks."""
+    written (differences first: each difference times M, then its dot
+    product with the difference), in row chunks."""
     out = np.empty((X.shape[0], C.shape[0]))
     for s in range(0, X.shape[0], chunk):
         diff = X[s:s + chunk, None, :] - C[None, :, :]
-        out[s:s + chunk] = np.einsum("ijk,kl,ijl->ij", diff, M, diff)
+        out[s:s + chunk] = np.sum((diff @ M) * diff, axis=2)
     return out
 
 
