@@ -246,10 +246,26 @@ def check_scores_selection(r: "Run", p: nm.Params):
     return ties
 
 
-def check_attention_sampled(r: "Run", Qb, Kb, Vb, p: nm.Params, rows_seed: int, nrows: int = 2048, q=None, sel=None):
+def cluster_rows(labels: np.ndarray, nclusters: int, per: int, seed: int) -> np.ndarray:
+    """Seeded sample of query rows taken cluster by cluster: ``nclusters``
+    distinct non-empty query clusters, up to ``per`` rows of each, ascending."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cand = np.unique(labels)
+    pick = rng.choice(cand, size=min(nclusters, cand.size), replace=False)
+    rows = [rng.choice(np.flatnonzero(labels == c), size=min(per, int(np.sum(labels == c))), replace=False)
+            for c in pick]
+    return np.sort(np.concatenate(rows))
+
+
+def check_attention_sampled(r: "Run", Qb, Kb, Vb, p: nm.Params, rows_seed: int, nrows: int = 2048, q=None, sel=None,
+                            clusters: int = 0):
     """Attention of a seeded sample of query rows per head against the fp64
     oracle given the GPU's clusters and selection (q / sel: other query
-    clusters and selection than the Run's, e.g. tail-merged ones)."""
+    clusters and selection than the Run's, e.g. tail-merged ones).  The
+    sample is nrows rows drawn from the whole head, or with clusters > 0
+    nrows / clusters rows from each of that many query clusters of the head
+    (the oracle gathers a query cluster's selected keys once for all its
+    sampled rows, which matters when selections keep most keys)."""
     from oracle import stats as ost
     from oracle import attention as oat
     B, H, L, d = Qb.shape
@@ -260,19 +276,23 @@ def check_attention_sampled(r: "Run", Qb, Kb, Vb, p: nm.Params, rows_seed: int, 
     sel_ = r.sel if sel is None else sel
     qlab, klab, ncl, fb = np_(q.labels), np_(r.k.labels), np_(r.k.ncl), np_(r.st.fallback)
     lst, n = np_(sel_.list), np_(sel_.n)
-    rows = gen.row_sample(L, nrows, rows_seed)
+    head_rows = gen.row_sample(L, nrows, rows_seed)
     worst = (0.0, 0.0)
     for h in range(BH):
+        rows = cluster_rows(qlab[h], clusters, nrows // clusters, rows_seed + h) if clusters else head_rows
         Qx, Kx, Vx = (nm.bf16_to_f64(x[h]) for x in (Qf, Kf, Vf))
         if fb[h] or p.sel_mode == nm.SEL_DENSE:
             Oo = np.concatenate([oat.dense_rows(Qx, Kx, Vx, rows[i:i + 256], p.attn_scale(d))[0]
                                  for i in range(0, rows.size, 256)])
         else:
             nk = int(ncl[h])
-            st = ost.key_stats(Kf[h], Vf[h], klab[h], np.zeros((nk, d)))
+            cnt = kmean = vmean = None
+            if p.compensate:
+                st = ost.key_stats(Kf[h], Vf[h], klab[h], np.zeros((nk, d)))
+                cnt, kmean, vmean = st["count"], st["kmean"], st["vmean"]
             sel = [lst[h, q, :n[h, q]] for q in range(r.nq)]
             Oo, _ = oat.sparse_rows(Qx, Kx, Vx, rows, qlab[h], klab[h], sel, p.attn_scale(d), bool(p.compensate),
-                                    st["count"], st["kmean"], st["vmean"])
+                                    cnt, kmean, vmean)
         mx, rl2 = attn_error(O[h][rows], Oo)
         assert mx <= ATTN_MAX_ABS and rl2 <= ATTN_REL_L2, (h, mx, rl2)
         worst = (max(worst[0], mx), max(worst[1], rl2))
