@@ -315,7 +315,7 @@ def sdpa_ms(Qd, Kd, Vd, reps=3):
             e1.record()
             torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
-    except Exception as e:  # backend not available on this build
+    except Exception as e:  # backend not available in this torch
         print(f"[bench] sdpa flash backend unavailable: {e}", file=sys.stderr)
         return None
 
@@ -893,7 +893,7 @@ def main():
         peak_probe()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (heads shard across GPUs by design "
+        print("bench.py measures one GPU: the library has no multi-GPU path (heads shard across GPUs by design "
               "only); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

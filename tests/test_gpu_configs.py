@@ -1,8 +1,8 @@
 """GPU parity at the full sizes of the four large workloads, in the launch
 configuration bench.py times: every stage of every head checked against the
 oracle recomputing it from the GPU's previous stage; attention on a seeded
-sample of 2048 query rows per head (512 rows from 16 query clusters per head
-for top-p selections, which keep most keys)."""
+sample of 2048 query rows per head (for top-p selections, which keep most
+keys, 128 rows from each of 16 seeded query clusters per head)."""
 import numpy as np
 import pytest
 
@@ -15,8 +15,9 @@ pytestmark = pytest.mark.gpu
 
 ROW_SEED = {"cogvideox": 9002, "hunyuan": 9003, "wan": 9004, "long": 9005}
 # top-p 0.9 keeps most keys of every query cluster here: its attention is
-# checked on 32 rows from each of 16 seeded query clusters per head
-LARGE_SELECTION_SAMPLE = {"topp": dict(nrows=512, clusters=16)}
+# checked on 128 rows from each of 16 seeded query clusters per head (2048
+# rows, each sampled cluster's keys gathered once)
+LARGE_SELECTION_SAMPLE = {"topp": dict(nrows=2048, clusters=16)}
 
 
 @pytest.fixture(scope="module")
