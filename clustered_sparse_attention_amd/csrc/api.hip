@@ -58,7 +58,8 @@ ac_status check_shape(const ac_shape *s) {
   if (s->B <= 0 || s->H <= 0 || s->L <= 0 || s->d <= 0)
     return fail(AC_E_SHAPE, "B, H, L, d must be positive (got %d %d %d %d)", s->B, s->H, s->L, s->d);
   if (s->d != 64 && s->d != 128) return fail(AC_E_UNSUPPORTED, "d = %d: only 64 and 128 are supported", s->d);
-  if ((int64_t)s->B * s->H > (1 << 20)) return fail(AC_E_SHAPE, "B*H too large");
+  // kernels launch a row of workgroups per head: the grid's y extent is B*H
+  if ((int64_t)s->B * s->H > 65535) return fail(AC_E_SHAPE, "B*H = %lld: at most 65,535 heads", (long long)s->B * s->H);
   if ((int64_t)s->L > (1 << 26)) return fail(AC_E_SHAPE, "L too large");
   // the attention's row gathers address one head's K and V with 32-bit byte offsets
   if ((int64_t)s->L * s->d * 2 >= (int64_t)1 << 32)

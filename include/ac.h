@@ -29,7 +29,8 @@
  *           "BH" below is B*H; every per-head array is indexed by the flattened head b*H + h.
  *           d must be 64 or 128 (AC_E_UNSUPPORTED otherwise).  Self-attention: queries and keys share L.
  *           One head's rows must stay below 4 GiB (L * d * 2 < 2^32: L <= 16,777,215 at d = 128),
- *           else AC_E_UNSUPPORTED.
+ *           else AC_E_UNSUPPORTED.  B*H <= 65,535 (kernels run a row of workgroups per head), else
+ *           AC_E_SHAPE.
  * Pointers  Every array pointer is a DEVICE pointer owned by the caller, except the arrays inside
  *           ac_layer_stats, which are HOST pointers.  The library never allocates caller-visible
  *           memory, never frees, and keeps no pointer after a call returns.  Scratch memory is the

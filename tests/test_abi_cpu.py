@@ -54,10 +54,11 @@ def test_sizes_validation():
     assert ncap == 1699 and ws > 40 * 75600 * 128 * 2
     for bad_shape, code in [((1, 2, 4096, 96), ac.AC_E_UNSUPPORTED), ((0, 2, 4096, 64), ac.AC_E_SHAPE),
                             ((1, 2, -5, 64), ac.AC_E_SHAPE), ((1, 2, 0, 64), ac.AC_E_SHAPE),
-                            ((1, 0, 4096, 64), ac.AC_E_SHAPE)]:
+                            ((1, 0, 4096, 64), ac.AC_E_SHAPE), ((2, 32768, 64, 64), ac.AC_E_SHAPE)]:
         with pytest.raises(ac.ACError) as e:
             ac.ac_sizes(ac.Shape(*bad_shape), p)
         assert e.value.status == code
+    ac.ac_sizes(ac.Shape(1, 65535, 64, 64), p)  # the most heads a call takes
     for kw in [dict(nq=0), dict(tau_rule=9), dict(sel_mode=7), dict(sel_mode=ac.AC_SEL_DENSITY, sel_param=1.5),
                dict(compensate=2), dict(tau_rule=ac.AC_TAU_PCTL, tau_param=0.0), dict(sel_mode=ac.AC_SEL_TOPK, topk=0),
                dict(min_sparse_gflop=-1)]:
