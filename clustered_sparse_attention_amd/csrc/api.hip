@@ -349,12 +349,16 @@ struct Engine {
   // k-means++ seeding of the job's centres.  Its grids depend only on the
   // engine's subsample cap, so it can be enqueued before the host knows the
   // job's point counts (heads with n = 0 or m = 0 are idle).
-  ac_status seed(const KmArgs &a, const ac_params *p, int role, int stage) {
-    if (S.kpp_smax <= KPP_GRAM_MAX)
-      launch_kpp_gram(P.D, a, P.BH, S.kpp_smax, at<double>(ws, S.kpp_nx), at<double>(ws, S.kpp_G), p->init_sample,
-                      p->seed, role, stage, st);
-    else
+  // rounds (nullable): recorded on st where the wide launches end and only
+  // the sequential rounds, one block per head, remain
+  ac_status seed(const KmArgs &a, const ac_params *p, int role, int stage, hipEvent_t rounds = nullptr) {
+    if (S.kpp_smax <= KPP_GRAM_MAX) {
+      AC_HIP(launch_kpp_gram(P.D, a, P.BH, S.kpp_smax, at<double>(ws, S.kpp_nx), at<double>(ws, S.kpp_G),
+                             p->init_sample, p->seed, role, stage, st, rounds));
+    } else {
+      if (rounds) AC_HIP(hipEventRecord(rounds, st));
       launch_kpp(P.D, a, P.BH, at<double>(ws, S.d2buf), p->init_sample, p->seed, role, stage, st);
+    }
     AC_CHECK_LAUNCH();
     return AC_OK;
   }
@@ -682,21 +686,24 @@ ac_status do_cluster_k_cold(const Plan &P, const ac_params *p, const uint16_t *K
     // close this stage, open the next; read its counts behind its seeding
     launch_stage_next(kst, at<int>(ws, P.hnew), E.n(), E.m(), E.coff(), t + 1, p->nmax, p->m0, L, BH, st);
     AC_CHECK_LAUNCH();
-    // the merge of this stage's centres runs beside the next stage's seeding
-    // (latency-bound, few CUs) rather than beside this stage's short tail
-    AC_HIP(hipEventRecord(ev_fork, st));
-    AC_HIP(hipStreamWaitEvent(ax, ev_fork, 0));
-    {
-      KmArgs am{K, (int64_t)L * D, nullptr, 0, at<int>(ws, P.nall), mtab + (int64_t)t * BH,
-                ctab + (int64_t)t * BH, k->cent, (int64_t)k->ncap * D};
-      launch_assign(D, am, fops, BH, mmax_t, L, k->labels, L, ax, nullptr, best);
-      AC_CHECK_LAUNCH();
-    }
     AC_HIP(hipMemcpyAsync(hnm, E.n(), (size_t)BH * 4, hipMemcpyDeviceToHost, st));
     AC_HIP(hipMemcpyAsync(hnm + BH, E.m(), (size_t)BH * 4, hipMemcpyDeviceToHost, st));
     AC_HIP(hipEventRecord(ev_join, st));
     cur ^= 1;
-    AC_TRY(E.seed(args(t + 1, cur), p, 1, t + 1));
+    AC_TRY(E.seed(args(t + 1, cur), p, 1, t + 1, ev_fork));
+    // The merge of this stage's centres runs beside the next stage's
+    // sequential seeding rounds, which keep one compute unit per head busy
+    // and leave the rest idle.  It starts after the seeding's distance matrix
+    // (a grid over every compute unit that it would otherwise hold up), and
+    // its resident grid leaves those compute units to the rounds, so none of
+    // its blocks waits behind them.
+    AC_HIP(hipStreamWaitEvent(ax, ev_fork, 0));
+    {
+      KmArgs am{K, (int64_t)L * D, nullptr, 0, at<int>(ws, P.nall), mtab + (int64_t)t * BH,
+                ctab + (int64_t)t * BH, k->cent, (int64_t)k->ncap * D};
+      launch_assign(D, am, fops, BH, mmax_t, L, k->labels, L, ax, nullptr, best, BH);
+      AC_CHECK_LAUNCH();
+    }
     if (t == 0 && after_first) AC_TRY(after_first());
     AC_HIP(hipEventSynchronize(ev_join));
     int active = 0;

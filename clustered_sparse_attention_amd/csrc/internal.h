@@ -207,8 +207,11 @@ struct TokQuestArgs {
 void launch_qnorm(int D, const uint16_t *Q, uint16_t *Qh, float *qn, int64_t rows, hipStream_t st);
 void launch_kpp(int D, const KmArgs &a, int BH, double *d2buf, int init_sample, uint64_t seed, int role, int stage,
                 hipStream_t st);
-void launch_kpp_gram(int D, const KmArgs &a, int BH, int smax, double *nx, double *G, int init_sample, uint64_t seed,
-                     int role, int stage, hipStream_t st);
+// after_gram (nullable): recorded on st once the distance matrix is enqueued,
+// before the m sequential rounds (one block per head) that read it; returns
+// that record's status
+hipError_t launch_kpp_gram(int D, const KmArgs &a, int BH, int smax, double *nx, double *G, int init_sample,
+                           uint64_t seed, int role, int stage, hipStream_t st, hipEvent_t after_gram = nullptr);
 // at_coff: operand rows at the centres' global index coff[h] + c (merge-mode assignment)
 void launch_cent_prep(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, hipStream_t st,
                       bool at_coff = false);
@@ -218,8 +221,11 @@ void launch_cent_prep(int D, const KmArgs &a, const CentOps &op, int BH, int mma
 // the job's centres are one stage's, global index coff[h] + c with operands
 // at op row coff[h] + c, merged into the running nearest centre kept in
 // labels / best_io (scores x.c - |c|^2/2; -inf = none yet)
+// spare_cus: compute units to leave to work running beside this launch, if at
+// most a quarter of the device (the resident kernel's grid is one block per
+// remaining compute unit)
 void launch_assign(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, int nmax_pts, int *labels, int64_t lab_hs,
-                   hipStream_t st, int *chg = nullptr, float *best_io = nullptr);
+                   hipStream_t st, int *chg = nullptr, float *best_io = nullptr, int spare_cus = 0);
 void launch_sort(const SortArgs &s, int BH, int nmax_pts, hipStream_t st);
 void launch_update(int D, const KmArgs &a, const SortArgs &s, const CentOps &op, int BH, int mmax, int npts,
                    double *partial, int64_t part_hs, hipStream_t st);

@@ -1328,7 +1328,7 @@ static int device_cus() {
 }
 
 void launch_assign(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, int nmax_pts, int *labels,
-                   int64_t lab_hs, hipStream_t st, int *chg, float *best_io) {
+                   int64_t lab_hs, hipStream_t st, int *chg, float *best_io, int spare_cus) {
   if (mmax <= ASSIGN_RES_MAX || best_io) {
     // 768 threads and LDS for this launch's centres only, one block per CU:
     // three waves a SIMD, so one wave's point loads hide behind two others'
@@ -1337,7 +1337,9 @@ void launch_assign(int D, const KmArgs &a, const CentOps &op, int BH, int mmax, 
     const int mpmax = (mmax + 15) & ~15;
     const size_t lds = (size_t)mpmax * (D + 8) * 2 * 2 + (size_t)mpmax * 4;
     const int64_t subs = (int64_t)BH * ((nmax_pts + 63) / 64);
-    const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(device_cus(), (subs + NT / 64 - 1) / (NT / 64)));
+    const int all = device_cus();
+    const int cus = spare_cus > 0 && spare_cus <= all / 4 ? all - spare_cus : all;
+    const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>(cus, (subs + NT / 64 - 1) / (NT / 64)));
     AC_D_DISPATCH(D, {
       static bool lds_ok = hipFuncSetAttribute((const void *)k_assign_res<DD, NT>,
                                                hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -394,18 +394,22 @@ void launch_kpp(int D, const KmArgs &a, int BH, double *d2buf, int init_sample, 
     hipLaunchKernelGGL(k_kpp<128>, dim3(BH), dim3(KPP_THREADS), 0, st, a, d2buf, init_sample, seed, role, stage);
 }
 
-void launch_kpp_gram(int D, const KmArgs &a, int BH, int smax, double *nx, double *G, int init_sample, uint64_t seed,
-                     int role, int stage, hipStream_t st) {
+hipError_t launch_kpp_gram(int D, const KmArgs &a, int BH, int smax, double *nx, double *G, int init_sample,
+                           uint64_t seed, int role, int stage, hipStream_t st, hipEvent_t after_gram) {
   const int nt = (smax + 63) / 64;
   if (D == 64) {
     hipLaunchKernelGGL(k_kpp_norms<64>, dim3((smax + 15) / 16, BH), dim3(64), 0, st, a, init_sample, nx, smax);
     hipLaunchKernelGGL(k_kpp_gram<64>, dim3(nt * nt, BH), dim3(256), 0, st, a, init_sample, nx, G, smax);
-    hipLaunchKernelGGL(k_kpp_seq<64>, dim3(BH), dim3(KPP_SEQ_THREADS), 0, st, a, G, smax, init_sample, seed, role, stage);
   } else {
     hipLaunchKernelGGL(k_kpp_norms<128>, dim3((smax + 15) / 16, BH), dim3(64), 0, st, a, init_sample, nx, smax);
     hipLaunchKernelGGL(k_kpp_gram<128>, dim3(nt * nt, BH), dim3(256), 0, st, a, init_sample, nx, G, smax);
-    hipLaunchKernelGGL(k_kpp_seq<128>, dim3(BH), dim3(KPP_SEQ_THREADS), 0, st, a, G, smax, init_sample, seed, role, stage);
   }
+  const hipError_t ev = after_gram ? hipEventRecord(after_gram, st) : hipSuccess;
+  if (D == 64)
+    hipLaunchKernelGGL(k_kpp_seq<64>, dim3(BH), dim3(KPP_SEQ_THREADS), 0, st, a, G, smax, init_sample, seed, role, stage);
+  else
+    hipLaunchKernelGGL(k_kpp_seq<128>, dim3(BH), dim3(KPP_SEQ_THREADS), 0, st, a, G, smax, init_sample, seed, role, stage);
+  return ev;
 }
 
 }  // namespace ac
