@@ -1416,12 +1416,15 @@ AC_API ac_status ac_layer(const ac_shape *s, const ac_params *p, const uint16_t 
     AC_HIP(hipEventRecord(ss->join, ss->s));
     return AC_OK;
   };
+  // the value means feed only the compensation's pseudo-keys: without it the
+  // key statistics do not read V
+  const uint16_t *Vs = p->compensate ? V : nullptr;
   if (warm) {
     AC_TRY(queries());
-    AC_TRY(do_cluster_k_warm(P, p, K, V, state, &k, &ks, ws, st));
+    AC_TRY(do_cluster_k_warm(P, p, K, Vs, state, &k, &ks, ws, st));
   } else {
     // the query clustering is enqueued once the first key stage is
-    AC_TRY(do_cluster_k_cold(P, p, K, V, &k, &ks, ws, st, nullptr, queries));
+    AC_TRY(do_cluster_k_cold(P, p, K, Vs, &k, &ks, ws, st, nullptr, queries));
   }
   AC_HIP(hipStreamWaitEvent(st, ss->join, 0));
   AC_TRY(do_score_select(P, p, &q, &k, &ks, &sel, sel_scratch_ws(P, ws), st));

@@ -77,7 +77,7 @@ struct SortArgs {
 };
 
 struct KStatsArgs {
-  const uint16_t *K, *V;  // [BH, L, D]
+  const uint16_t *K, *V;  // [BH, L, D]; V NULL: no value means (vmean left as it is)
   const int *perm, *seg;  // [BH, L], [BH, ncap + 1]
   const int *ncl;         // [BH]
   const float *cent;      // [BH, ncap, D]

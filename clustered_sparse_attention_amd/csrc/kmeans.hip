@@ -1025,7 +1025,8 @@ __global__ __launch_bounds__(64) void k_kstats_part(KStatsArgs s) {
   const int *perm = s.perm + (int64_t)h * s.L;
   const int beg = seg[c] + j * KST_CHUNK, end = min(seg[c + 1], beg + KST_CHUNK);
   const uint16_t *K = s.K + (int64_t)h * s.L * D;
-  const uint16_t *V = s.V + (int64_t)h * s.L * D;
+  const bool wv = s.V != nullptr;  // value means wanted
+  const uint16_t *V = wv ? s.V + (int64_t)h * s.L * D : nullptr;
   const float *cent = s.cent + cb * D;
   double sk[PL], sv[PL], se = 0.0;
   float mx[PL], mn[PL], cc[PL];
@@ -1043,7 +1044,8 @@ __global__ __launch_bounds__(64) void k_kstats_part(KStatsArgs s) {
     for (int jj = 0; jj < 4; ++jj) {
       const int64_t rr = row[jj] >= 0 ? row[jj] : row[0];
       kw[jj] = *(const pw_t *)(K + rr * D + sub * PL);
-      vw[jj] = *(const pw_t *)(V + rr * D + sub * PL);
+      if (wv) vw[jj] = *(const pw_t *)(V + rr * D + sub * PL);
+      else vw[jj] = (pw_t){};
     }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
@@ -1083,12 +1085,12 @@ __global__ __launch_bounds__(64) void k_kstats_part(KStatsArgs s) {
       const int dd = sub * PL + k;
       if (nch == 1) {
         s.kmean[cb * D + dd] = (float)(sk[k] / cnt);
-        s.vmean[cb * D + dd] = (float)(sv[k] / cnt);
+        if (wv) s.vmean[cb * D + dd] = (float)(sv[k] / cnt);
         s.kmax[cb * D + dd] = (uint16_t)(__float_as_uint(mx[k]) >> 16);
         s.kmin[cb * D + dd] = (uint16_t)(__float_as_uint(mn[k]) >> 16);
       } else {
         s.psk[slot * D + dd] = sk[k];
-        s.psv[slot * D + dd] = sv[k];
+        if (wv) s.psv[slot * D + dd] = sv[k];
         s.pmx[slot * D + dd] = mx[k];
         s.pmn[slot * D + dd] = mn[k];
       }
@@ -1114,7 +1116,8 @@ __global__ __launch_bounds__(128) void k_kstats_fin(KStatsArgs s) {
   if (nch == 0) {
     for (int dd = threadIdx.x; dd < D; dd += 128) {
       s.kmax[cb * D + dd] = 0; s.kmin[cb * D + dd] = 0;
-      s.kmean[cb * D + dd] = 0.f; s.vmean[cb * D + dd] = 0.f;
+      s.kmean[cb * D + dd] = 0.f;
+      if (s.V) s.vmean[cb * D + dd] = 0.f;
     }
     if (threadIdx.x == 0) s.msepart[cb] = 0.0;
     return;
@@ -1125,12 +1128,12 @@ __global__ __launch_bounds__(128) void k_kstats_fin(KStatsArgs s) {
     float x = -__builtin_inff(), y = __builtin_inff();
     for (int q = 0; q < nch; ++q) {
       a += s.psk[(s0 + q) * D + dd];
-      b += s.psv[(s0 + q) * D + dd];
+      if (s.V) b += s.psv[(s0 + q) * D + dd];
       x = fmaxf(x, s.pmx[(s0 + q) * D + dd]);
       y = fminf(y, s.pmn[(s0 + q) * D + dd]);
     }
     s.kmean[cb * D + dd] = (float)(a / cnt);
-    s.vmean[cb * D + dd] = (float)(b / cnt);
+    if (s.V) s.vmean[cb * D + dd] = (float)(b / cnt);
     s.kmax[cb * D + dd] = (uint16_t)(__float_as_uint(x) >> 16);
     s.kmin[cb * D + dd] = (uint16_t)(__float_as_uint(y) >> 16);
   }
