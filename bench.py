@@ -502,11 +502,15 @@ def summarize(args):
         print("\n".join(lines))
         return
     if kind == "configs":
-        # one table of bench lines: --summarize configs <out.md> <command> :: <log>...
+        # one table of bench lines: --summarize configs <out.md> [title=<title>] <command> :: <log>...
         out = rest[0]
         k = rest.index("::")
+        title = "Bench lines, all workloads (one MI355X)"
+        if rest[1].startswith("title="):
+            title, rest = rest[1][len("title="):], rest[:1] + rest[2:]
+            k -= 1
         cmd, logs = " ".join(rest[1:k]), rest[k + 1:]
-        lines = ["# Bench lines, all workloads (one MI355X)", "", f"Command: `{cmd}`", "",
+        lines = [f"# {title}", "", f"Command: `{cmd}`", "",
                  "A step is one `ac_layer` call on resident inputs (cold unless marked warm); the phase columns "
                  "come from a separate untimed pass through the entry points, the query clustering on a second "
                  "stream beside the key clustering (`both` is their wall time). Rows marked with the "
@@ -852,6 +856,8 @@ def main():
     ap.add_argument("--variant", default="density", choices=["density", "topp", "dense"])
     ap.add_argument("--compensate", type=int, default=0)
     ap.add_argument("--heads", type=int, default=0, help="run only this many heads (0 = all)")
+    ap.add_argument("--seq-len", type=int, default=0,
+                    help="tokens per head instead of the workload's own (0 = the workload's; same data recipe)")
     ap.add_argument("--serial", action="store_true",
                     help="run the query clustering on the main stream too (for per-kernel profiles)")
     ap.add_argument("--tail-block", type=int, default=0,
@@ -909,9 +915,12 @@ def main():
         return
 
 
-    w = gen.get_workload(args.workload)
+    over = {}
     if args.heads:
-        w = gen.get_workload(args.workload, H=args.heads)
+        over["H"] = args.heads
+    if args.seq_len:
+        over["L"] = args.seq_len
+    w = gen.get_workload(args.workload, **over)
     t0 = time.perf_counter()
     Q, K, V = gen.generate(w)
     print(f"[bench] generated {w.name} B={w.B} H={w.H} L={w.L} d={w.d} in {time.perf_counter() - t0:.1f} s",

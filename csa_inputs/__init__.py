@@ -22,6 +22,7 @@ labels, query noise, query norms, V.
 from __future__ import annotations
 
 import dataclasses
+import re
 import math
 import os
 from concurrent.futures import ThreadPoolExecutor
@@ -114,6 +115,10 @@ def get_workload(name: str, **overrides) -> Workload:
                 overrides["key_outlier_scale"] = tuple(sc)
             overrides.setdefault("outlier_heads", tuple(h for h in w.outlier_heads if h < H))
         w = dataclasses.replace(w, **overrides)
+        # the description names the shape: keep it in step with overridden sizes
+        desc = re.sub(r"\bH=\d+", f"H={w.H}", w.description)
+        desc = re.sub(r"\bL=\d+", f"L={w.L}", desc)
+        w = dataclasses.replace(w, description=desc)
     return w
 
 

@@ -49,6 +49,15 @@ def _bench_line(ms, workload="Wan2.1-14B-like H=40 L=75600 d=128", warm=False, c
     return json.dumps(line)
 
 
+def test_overridden_shapes_are_named_in_the_description():
+    """A bench line run with --heads or --seq-len names the shape it ran."""
+    import csa_inputs as gen
+    w = gen.get_workload("wan", H=5, L=18900)
+    assert (w.H, w.L) == (5, 18900) and "H=5 L=18900 d=128" in w.description
+    assert gen.get_workload("wan").description.endswith("H=40 L=75600 d=128")
+    assert "H=2 L=180000" in gen.get_workload("long", H=2).description
+
+
 def test_summarize_configs_table(tmp_path):
     a, b = tmp_path / "a.log", tmp_path / "b.log"
     a.write_text("[bench] noise\n" + _bench_line(36.0) + "\n")
@@ -61,6 +70,11 @@ def test_summarize_configs_table(tmp_path):
     assert "| cold |" in rows[0] and "| 36.00 |" in rows[0] and "3.33x" in rows[0] and "complete head" in rows[0]
     assert "| warm |" in rows[1] and "4.53x" in rows[1] and rows[1].endswith("| — |")
     assert "Command: `the command`" in text
+    assert text.startswith("# Bench lines, all workloads")
+    bench.summarize(["configs", str(out), "title=Sequence sweep", "cmd", "::", str(a)])
+    text = out.read_text()
+    assert text.startswith("# Sequence sweep\n") and "Command: `cmd`" in text
+    assert len([l for l in text.splitlines() if l.startswith("| Wan2.1")]) == 1
 
 
 def test_summarize_configs_marks_the_principal_component_rows(tmp_path):
