@@ -76,8 +76,10 @@ AC_DEV uint64_t stream_id(uint64_t bh, uint32_t role, uint32_t stage) {
 }
 
 // DPP moves within a wave.  Controls used: quad permutes 0x00-0xFF, row
-// mirror 0x140, half-row mirror 0x141.  Lanes that the row and bank masks
-// leave out get 0.
+// shifts right 0x111-0x11F, wave shift right by one 0x138, row mirror 0x140,
+// half-row mirror 0x141, row broadcasts of lanes 15 and 31 0x142 / 0x143.
+// Lanes that the row and bank masks leave out, or whose source lane lies
+// outside the row (or wave), get 0.
 template <int CTRL, int ROWS = 0xF, int BANKS = 0xF>
 AC_DEV uint32_t dpp_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, BANKS, false);
@@ -96,6 +98,28 @@ AC_DEV float row16_sum(float v) {
   v += dpp_f32<0x140>(v);  // row mirror
   return v;
 }
+// fp64 through the same moves, one 32-bit half at a time (both halves from
+// the same source lane, or both 0)
+template <int CTRL, int ROWS = 0xF, int BANKS = 0xF>
+AC_DEV double dpp_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = dpp_u32<CTRL, ROWS, BANKS>((uint32_t)b), hi = dpp_u32<CTRL, ROWS, BANKS>((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// inclusive prefix sum over the 64 lanes: within each row of 16 by row
+// shifts of 1, 2, 4, 8, then row 0's total into row 1 and row 2's into row 3
+// (row broadcast of lane 15), then lane 31's total into rows 2 and 3
+AC_DEV double wave_incl_scan(double v) {
+  v += dpp_f64<0x111>(v);
+  v += dpp_f64<0x112>(v);
+  v += dpp_f64<0x114>(v);
+  v += dpp_f64<0x118>(v);
+  v += dpp_f64<0x142, 0xA>(v);
+  v += dpp_f64<0x143, 0xC>(v);
+  return v;
+}
+// the previous lane's value (0 in lane 0), bit for bit: a wave shift by one
+AC_DEV double wave_prev(double v) { return dpp_f64<0x138>(v); }
 // the value lane l holds (uniform)
 AC_DEV float lane_f32(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
 

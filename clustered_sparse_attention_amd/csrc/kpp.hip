@@ -340,13 +340,10 @@ __global__ __launch_bounds__(KPP_SEQ_THREADS) void k_kpp_seq(KmArgs a, const dou
 #pragma unroll
     for (int e = 0; e < KPP_SEQ_CS; ++e)
       if (e < ne) loc += d2[e];
-    double inc = loc;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const double y = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += y;
-    }
-    const double prev = __shfl_up(inc, 1, 64);  // the previous lane's inclusive sum, bit for bit
+    // wave scan on DPP moves (the LDS permutes of a shuffle scan, two per
+    // fp64 step, each waited for, were a sixth of a round)
+    const double inc = wave_incl_scan(loc);
+    const double prev = wave_prev(inc);  // the previous lane's inclusive sum, bit for bit
     if (lane == 63) sh_wt[wave] = inc;
     if (tid == 0) sh_pick[t & 1] = -1;
     __syncthreads();
