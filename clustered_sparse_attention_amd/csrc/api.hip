@@ -605,7 +605,8 @@ ac_status pinned_i32(int n, int **out);
 // boundaries.  The final nearest centre of every key over all stages is
 // computed stage by stage on an auxiliary stream as each stage's centres
 // are final (merge-mode assignment: strictly better only, so ties keep the
-// lowest centre index), beside the following stages.
+// lowest centre index), each merge beside the next stage's sequential
+// seeding rounds.
 // after_first (optional) is called once the first stage is enqueued, before
 // the host first waits: ac_layer enqueues the query clustering there, so
 // that the key stream starts at once and the host's launch work for the
