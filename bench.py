@@ -320,13 +320,19 @@ def sdpa_ms(Qd, Kd, Vd, reps=3):
         return None
 
 
-ATTN_SRC = os.path.join(ROOT, "clustered_sparse_attention_amd", "csrc", "attn.hip")
+ATTN_SRCS = [os.path.join(ROOT, "clustered_sparse_attention_amd", "csrc", f)
+             for f in ("attn.hip", "common.h", "internal.h")]
 TRAFFIC = os.path.join(ROOT, "profiles", "k_attn_wan_traffic.json")
 
 
 def attn_source_hash() -> str:
+    """SHA-256 of the sources the attention kernels compile from (attn.hip and
+    the two headers it includes)."""
     import hashlib
-    return hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for path in ATTN_SRCS:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str, variant: str, compensate: int):
