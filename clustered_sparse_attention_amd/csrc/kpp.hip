@@ -340,8 +340,8 @@ __global__ __launch_bounds__(KPP_SEQ_THREADS) void k_kpp_seq(KmArgs a, const dou
 #pragma unroll
     for (int e = 0; e < KPP_SEQ_CS; ++e)
       if (e < ne) loc += d2[e];
-    // wave scan on DPP moves (the LDS permutes of a shuffle scan, two per
-    // fp64 step, each waited for, were a sixth of a round)
+    // wave scan on DPP moves: a shuffle scan costs two LDS permutes per fp64
+    // step, each waited for, about a sixth of a round
     const double inc = wave_incl_scan(loc);
     const double prev = wave_prev(inc);  // the previous lane's inclusive sum, bit for bit
     if (lane == 63) sh_wt[wave] = inc;
