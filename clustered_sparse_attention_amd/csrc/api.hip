@@ -314,6 +314,9 @@ struct Engine {
   const Scratch &S;
   void *ws;
   hipStream_t st;
+  // compute units the resident assignment leaves to work beside it (the key
+  // clustering's one-block-per-head launches when the queries run beside it)
+  int spare = 0;
   int *n() { return at<int>(ws, S.hn); }
   int *m() { return at<int>(ws, S.hm); }
   int *coff() { return at<int>(ws, S.hcoff); }
@@ -400,7 +403,7 @@ struct Engine {
     }
     for (int it = 0; it < iters; ++it) {
       int *cur = chg + (it & 1) * P.BH, *nxt = chg + ((it + 1) & 1) * P.BH;
-      launch_assign(D, al, op, P.BH, mmax, npts, lab, P.L, st, it > 0 ? cur : nullptr);
+      launch_assign(D, al, op, P.BH, mmax, npts, lab, P.L, st, it > 0 ? cur : nullptr, nullptr, spare);
       SortArgs s = sort_args(lab, at<int>(ws, S.lperm), at<int>(ws, S.lseg), S.mcap, mmax);
       s.n = neff;
       s.neff = neff;
@@ -420,10 +423,10 @@ struct Engine {
       AC_CHECK_LAUNCH();
     }
     if (iters > 0) {
-      launch_assign(D, al, op, P.BH, mmax, npts, labels_out, P.L, st);
+      launch_assign(D, al, op, P.BH, mmax, npts, labels_out, P.L, st, nullptr, nullptr, spare);
       launch_copy_converged(a.n, neff, lab, labels_out, P.L, npts, P.BH, st);
     } else {
-      launch_assign(D, a, op, P.BH, mmax, npts, labels_out, P.L, st);
+      launch_assign(D, a, op, P.BH, mmax, npts, labels_out, P.L, st, nullptr, nullptr, spare);
     }
     AC_CHECK_LAUNCH();
     return AC_OK;
@@ -431,10 +434,16 @@ struct Engine {
 };
 
 // ---------------------------------------------------------------------------
+// beside_keys: the key clustering runs at the same time on another stream;
+// the query assignment's resident grid then leaves one compute unit per head
+// to the key side's one-block-per-head launches (seeding rounds, label scans),
+// which otherwise wait until the assignment ends.
 ac_status do_cluster_q(const Plan &P, const ac_params *p, const uint16_t *Q, const float *warm_cent,
-                       ac_clusters *q, void *ws, hipStream_t st, float *cent_trace = nullptr) {
+                       ac_clusters *q, void *ws, hipStream_t st, float *cent_trace = nullptr,
+                       bool beside_keys = false) {
   const int BH = P.BH, L = P.L, D = P.D;
   Engine E{P, P.sq, ws, st};
+  E.spare = beside_keys ? BH : 0;
   uint16_t *qhat = at<uint16_t>(ws, P.qhat);
   float *qn = at<float>(ws, P.qn);
   launch_qnorm(D, Q, qhat, qn, (int64_t)BH * L, st);
@@ -1413,7 +1422,7 @@ AC_API ac_status ac_layer(const ac_shape *s, const ac_params *p, const uint16_t 
   AC_HIP(hipEventRecord(ss->fork, st));
   AC_HIP(hipStreamWaitEvent(ss->s, ss->fork, 0));
   auto queries = [&]() -> ac_status {
-    AC_TRY(do_cluster_q(P, p, Q, warm ? state->cent_q : nullptr, &q, ws, ss->s));
+    AC_TRY(do_cluster_q(P, p, Q, warm ? state->cent_q : nullptr, &q, ws, ss->s, nullptr, true));
     AC_HIP(hipEventRecord(ss->join, ss->s));
     return AC_OK;
   };
