@@ -59,6 +59,36 @@ def test_wan_selection_and_attention(wan_run, variant, compensate):
           f"rel-L2 {worst[1]:.3g}")
 
 
+def test_wan_layer_equals_entry_points(wan_run):
+    """ac_layer, the call bench.py times (the query clustering beside the key
+    clustering on a second stream, each stage's merge beside the next stage's
+    seeding, statistics without the value rows when compensation is off), on
+    the full Wan2.1-shaped layer: the same output, bit for bit, as the entry
+    points one after another, whose every stage the tests above check against
+    the oracle; and the same per-head cluster counts, flags, thresholds and
+    stage counts."""
+    import torch
+    import clustered_sparse_attention_amd as ac
+    from abi_helpers import abi_params
+    w, Q, K, V, r = wan_run
+    p = workload_oracle_params("wan", "density", 0)
+    r.p, r.cp = p, abi_params(p)
+    r.score_select()
+    r.attn()
+    ws = ac.workspace(r.ws_bytes, torch.device("cuda"))
+    state = ac.State(r.BH, r.nq, r.ncap_k, r.d, torch.device("cuda"))
+    O = torch.empty_like(r.Q)
+    hs = ac.ac_layer(r.shape, r.cp, r.Q, r.K, r.V, state, O, ws, host_stats=True)
+    torch.cuda.synchronize()
+    assert torch.equal(O, r.O)
+    assert np.array_equal(hs["ncl_k"], np_(r.k.ncl)) and np.array_equal(hs["stages"], np_(r.st.stages))
+    assert np.array_equal(hs["fallback"], np_(r.st.fallback)) and np.array_equal(hs["tau"], np_(r.st.tau))
+    assert torch.equal(state.cent_q, r.q.cent)
+    ck, ck0, ncl = np_(state.cent_k), np_(r.k.cent), np_(r.k.ncl)
+    assert all(np.array_equal(ck[h, :ncl[h]], ck0[h, :ncl[h]]) for h in range(r.BH))  # slots past N_k are unused
+    del ws
+
+
 @pytest.mark.parametrize("variant", ["density", "topp"])
 def test_wan_tail_merge(wan_run, variant):
     """iCATS tail merging at full size: the merged clusters and selections of
