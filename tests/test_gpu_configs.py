@@ -89,6 +89,44 @@ def test_wan_layer_equals_entry_points(wan_run):
     del ws
 
 
+def test_wan_warm_layer_equals_entry_points(wan_run):
+    """ac_layer's warm step (bench.py --warm: a cold call fills the state, then
+    Q and K move by 2 %) on the full Wan2.1-shaped layer: bit-identical output
+    and carried centres to the warm entry points from the same state."""
+    import torch
+    import clustered_sparse_attention_amd as ac
+    from abi_helpers import abi_params, to_dev
+    w, Q, K, V, r = wan_run
+    p = workload_oracle_params("wan", "density", 0)
+    cp = abi_params(p)
+    dev = torch.device("cuda")
+    ws = ac.workspace(r.ws_bytes, dev)
+    state = ac.State(r.BH, r.nq, r.ncap_k, r.d, dev)
+    O = torch.empty_like(r.Q)
+    ac.ac_layer(r.shape, cp, r.Q, r.K, r.V, state, O, ws)
+    torch.cuda.synchronize()
+    assert state.valid == 1
+    start = ac.State(r.BH, r.nq, r.ncap_k, r.d, dev)
+    for name in ("cent_q", "cent_k", "ncl_k", "fallback", "tau"):
+        getattr(start, name).copy_(getattr(state, name))
+    start.valid = 1
+    Q2, K2 = to_dev(gen.perturb(Q, 1103)), to_dev(gen.perturb(K, 1104))
+    Ow = torch.empty_like(r.Q)
+    ac.ac_layer(r.shape, cp, Q2, K2, r.V, state, Ow, ws)
+    r2 = Run(gen.perturb(Q, 1103), gen.perturb(K, 1104), V, p)
+    r2.cluster_q(warm_cent=start.cent_q)
+    r2.cluster_k(warm=start)
+    r2.score_select()
+    r2.attn()
+    torch.cuda.synchronize()
+    assert torch.equal(Ow, r2.O)
+    assert torch.equal(state.cent_q, r2.q.cent)
+    ck, ck0, ncl = np_(state.cent_k), np_(r2.k.cent), np_(r2.k.ncl)
+    assert np.array_equal(np_(state.ncl_k), ncl)
+    assert all(np.array_equal(ck[h, :ncl[h]], ck0[h, :ncl[h]]) for h in range(r.BH))
+    del ws, r2
+
+
 @pytest.mark.parametrize("variant", ["density", "topp"])
 def test_wan_tail_merge(wan_run, variant):
     """iCATS tail merging at full size: the merged clusters and selections of
